@@ -1,0 +1,263 @@
+/*
+ * libgradcomp — per-step gradient compression for data-parallel training on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   [AdaComp] "AdaComp: Adaptive Residual Gradient Compression for
+ *             Data-Parallel Distributed Training" (Chen et al.), the review's
+ *             "Proposed method" list and Abstract.
+ *   [DGC]     "Deep Gradient Compression: Reducing the Communication Bandwidth
+ *             for Distributed Training" (Lin et al.), §3.1–§3.3, §5 and
+ *             Appendices A, C, D.
+ *   [DCD]     "Communication Compression for Decentralized Training"
+ *             (Tang et al.), DCD-PSGD steps 1–3 and the signal-to-noise
+ *             parameter alpha of the compression operator.
+ *   [SlimDP]  "Slim-DP: A Light Communication Data Parallelism for DNN",
+ *             experimental setup (Quant-DP baseline: random quantization with
+ *             buckets of 512).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every buffer argument typed as a pointer to float / uint32_t / uint8_t /
+ *    uint64_t / void is a DEVICE pointer owned by the caller.  Structs and
+ *    arrays documented as "host" are read during the call and not retained.
+ *  - A learner's model is one flat fp32 buffer of n_total elements.  Each
+ *    layer tensor is a segment of it (gc_segment).  State buffers (AdaComp
+ *    residual R, DGC momentum U and accumulator V) use the same flat layout.
+ *  - Argument errors are detected on the host before anything is enqueued; on
+ *    error no device buffer has been touched.  Errors are returned as negative
+ *    gc_status codes; gc_last_error() gives a thread-local message.
+ *  - Hot calls enqueue kernels on `stream` and return without synchronising.
+ *    Counts and messages land in device memory.
+ *  - Hot calls never allocate device memory, with one exception: the first
+ *    call that uses a plan on a device uploads the plan's tables to that
+ *    device (one hipMalloc + one synchronous copy per plan and device).
+ *  - Results are bitwise deterministic: every floating-point operation is a
+ *    single correctly rounded IEEE operation in a fixed order (no FMA
+ *    contraction), and every reduction that feeds a decision uses a fixed
+ *    pairwise tree (see gc_dgc_step and gc_adacomp_compress).
+ *  - Inputs must be finite.  NaN or Inf gives unspecified selections but never
+ *    an out-of-bounds access.
+ *  - Input, state and output buffers must not alias each other (except
+ *    x_out == x in gc_dcd_compress).
+ *  - Calls on different streams are independent as long as they use
+ *    different workspaces and outputs.
+ */
+#ifndef GRADCOMP_H
+#define GRADCOMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+typedef int gc_status;
+#define GC_OK          0
+#define GC_EINVAL     -1   /* malformed argument (null pointer, bad range)   */
+#define GC_ECAPACITY  -2   /* output or workspace capacity too small         */
+#define GC_ERANGE     -3   /* size outside the supported range (n >= 2^32)   */
+#define GC_EHIP       -4   /* a HIP runtime call failed                      */
+#define GC_ENOTSUP    -5   /* valid but unsupported parameter combination    */
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char *gc_last_error(void);
+/* Library version string, e.g. "libgradcomp 0.1.0". */
+const char *gc_version(void);
+
+/* ------------------------------------------------------------------ layout */
+/*
+ * One layer tensor inside the flat buffer (host struct).
+ * Both methods act on each layer on its own: [AdaComp] applies the scheme
+ * layer by layer; [DGC] §3.1 thresholds each gradient tensor.
+ *   offset  : index of the segment's first element in the flat buffer.
+ *   length  : number of elements n_s (>= 1).
+ *   bin_len : AdaComp bin length L_T (>= 1, <= GC_MAX_BIN_LEN); bins restart
+ *             at the segment start and the last bin may be partial.
+ *   k       : DGC top-k count (1 <= k <= length).  gc_topk_count() gives the
+ *             0.1%-density value ceil(n_s/1000) used by [DGC] §3.3/§4.
+ */
+typedef struct gc_segment {
+    uint64_t offset;
+    uint32_t length;
+    uint32_t bin_len;
+    uint32_t k;
+    uint32_t reserved;   /* must be 0 */
+} gc_segment;
+
+#define GC_MAX_BIN_LEN   4096u
+#define GC_MAX_MESSAGES  64
+
+/* Opaque, immutable plan: validated segment table + device tables. */
+typedef struct gc_plan gc_plan;
+
+/*
+ * Validate a segment table and build a plan.  Host only: touches no device.
+ *   segs[nseg] (host) must be ascending by offset, non-overlapping, and lie in
+ *   [0, n_total); n_total must be < 2^32 (indices are u32).  Gaps between
+ *   segments are allowed and are never read or written.
+ * Returns GC_EINVAL (bad table), GC_ERANGE (n_total >= 2^32), GC_ENOTSUP
+ * (bin_len > GC_MAX_BIN_LEN).  *out is set only on GC_OK.
+ */
+gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total,
+                         gc_plan **out);
+void      gc_plan_destroy(gc_plan *plan);
+int       gc_plan_num_segments(const gc_plan *plan);
+uint64_t  gc_plan_num_elements(const gc_plan *plan);
+/* Sum over segments of k (the DGC message size). */
+uint64_t  gc_plan_total_k(const gc_plan *plan);
+/* Sum over segments of ceil(length/bin_len) (AdaComp bin count). */
+uint64_t  gc_plan_total_bins(const gc_plan *plan);
+/* ceil(n / 1000), the per-tensor count at 99.9% sparsity. */
+uint32_t  gc_topk_count(uint32_t n);
+
+#define GC_OP_DGC      1
+#define GC_OP_ADACOMP  2
+#define GC_OP_PACK     3
+#define GC_OP_DECODE   4
+/* Device workspace bytes a hot call with this plan needs (0 if none). */
+size_t gc_plan_workspace_bytes(const gc_plan *plan, int op);
+
+/* ----------------------------------------------------------------- message */
+/*
+ * Sparse message (host struct whose members are device pointers).
+ *   idx[cap]        : flat element indices, ascending within the message
+ *                     (segments in plan order, ascending inside a segment).
+ *   val[cap]        : value to add at idx — V_i for DGC, +-scale_s for AdaComp.
+ *   seg_off[nseg+1] : entries of segment s are [seg_off[s], seg_off[s+1]);
+ *                     seg_off[nseg] is the message's entry count.
+ *   seg_scale[nseg] : AdaComp layer scale per segment (unused by DGC; may be
+ *                     NULL there).
+ *   cap             : capacity of idx/val in entries.
+ */
+typedef struct gc_sparse {
+    uint32_t *idx;
+    float    *val;
+    uint32_t *seg_off;
+    float    *seg_scale;
+    uint64_t  cap;
+} gc_sparse;
+
+/* --------------------------------------------------------------- AdaComp */
+/*
+ * One AdaComp step for one learner ([AdaComp] "Proposed method", Abstract):
+ *   a1  G_i = fl32(R_i + dW_i)                                (residual + new gradient)
+ *   a2  g_max(b) = max_{i in b} |G_i|   over bins of bin_len  (exact; max is order-free)
+ *   a3  sel_i  <=>  g_max(b) > 0  and  fl32(scale_factor * |G_i|) >= g_max(b)
+ *       (the bin's own max always qualifies when scale_factor >= 1; 2.0 is the
+ *        empirical factor the page gives)
+ *   a4  scale_s = fl32( PSUM64(g_max over the segment's bins) / nbins_s )
+ *       (mean of the bin maxima across the whole layer)
+ *   a5  q_i = copysign(scale_s, G_i) if selected, else 0;  R_i <- fl32(G_i - q_i)
+ *   a6  out: per segment, ascending idx with val = q_i; out->seg_scale[s] = scale_s.
+ * PSUM64(x_0..x_{m-1}) converts each term to double, pads with +0.0 to the
+ * next power of two and adds as a perfect binary tree in index order.
+ *   dW  [n_total] in,  R [n_total] in/out,  out: cap >= n_total (worst case).
+ *   ws  : at least gc_plan_workspace_bytes(plan, GC_OP_ADACOMP) bytes.
+ * Errors: GC_EINVAL (null pointer, scale_factor not finite or < 1),
+ *         GC_ECAPACITY (out->cap < n_total or ws too small).
+ */
+gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R,
+                              float scale_factor, gc_sparse *out,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------- DGC */
+/*
+ * One DGC step for one learner, vanilla momentum ([DGC] §3.1–§3.3, App. C, D):
+ *   a7  local clipping (App. C), only if thr_G > 0:
+ *         thr = fl32(thr_G / sqrt(num_nodes))            (in double)
+ *         S_s = PSUM64(G_i^2 over the segment)            (squares exact in double)
+ *         c_s = fl32(thr / sqrt(S_s)) if sqrt(S_s) > thr else 1
+ *       G'_i = fl32(c_s * G_i)
+ *   a8  momentum correction (§3.2):  U_i <- fl32(fl32(momentum*U_i) + G'_i)
+ *                                    V_i <- fl32(V_i + U_i)
+ *   a9  exact top-k (§3.1, §5): key_i = bits(V_i) & 0x7FFFFFFF; the k_s entries
+ *       first in the order (key descending, index ascending) are sent.
+ *   a10 momentum factor masking (§3.3): at sent indices V_i <- +0, U_i <- +0.
+ *   out: per segment exactly k_s entries, ascending idx, val = V_i before masking.
+ *   G [n_total] in;  U, V [n_total] in/out;  out->cap >= gc_plan_total_k(plan).
+ *   0 <= momentum < 1;  num_nodes >= 1;  thr_G <= 0 disables clipping.
+ * Errors: GC_EINVAL, GC_ECAPACITY (out->cap or ws too small).
+ */
+gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, float *V,
+                      float momentum, float thr_G, int num_nodes,
+                      gc_sparse *out, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------ pack */
+/*
+ * Byte-exact run-length encoding of a message ([DGC] §3.1: 32-bit values and
+ * 16-bit zero-run lengths).  Little-endian; every block 4-byte aligned.
+ *   stream header : u32 'GCP1', u32 kind, u32 nseg, u32 0
+ *   DGC block     : u32 'DGC1', u32 n_s, u32 E, u32 k_s,
+ *                   u16 run[E] (+ one u16 0 if E is odd), f32 val[E]
+ *   AdaComp block : u32 'ADC1', u32 n_s, u32 E, f32 scale_s,
+ *                   u16 code[E] (+ one u16 0 if E is odd);
+ *                   code = sign << 15 | run  (sign 1 = negative)
+ * A run counts the unsent elements since the previous entry of the segment
+ * (from the segment start for the first).  A run >= MAX is split: emit an
+ * escape (run MAX; DGC value +0.0f), subtract MAX, repeat.  MAX is 65535 for
+ * DGC and 32767 for AdaComp; E counts entries plus escapes.
+ *   in       : a message produced for this plan (device counts are read).
+ *   out      : device byte buffer of out_cap >= gc_pack_bound(plan, kind).
+ *   out_bytes: device u64, receives the stream length.
+ * Errors: GC_EINVAL (bad kind / null), GC_ECAPACITY (out_cap or ws too small).
+ */
+#define GC_KIND_DGC      1
+#define GC_KIND_ADACOMP  2
+uint64_t  gc_pack_bound(const gc_plan *plan, int kind);
+gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
+                  uint8_t *out, uint64_t out_cap, uint64_t *out_bytes,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode */
+/*
+ * Decompress-and-aggregate K messages into a dense update ([DGC] App. A: the
+ * nodes' gradients are summed; [AdaComp]: the learners' compressed gradients
+ * are averaged).  For every element i of the plan's segments:
+ *   S_i = +0.0f, then S_i = fl32(S_i + v_{k,i}) for k = 0..K-1 in array order
+ *         over the messages that hold i;
+ *   r_i = fl32(S_i / K) (GC_AVG) or S_i (GC_SUM);
+ *   dense_i = r_i (accumulate == 0) or fl32(dense_i + r_i) (accumulate != 0).
+ *   msgs (host array of K <= GC_MAX_MESSAGES): messages for this plan with
+ *   indices inside segments and ascending.  dense [n_total] out (in/out if
+ *   accumulate).  Elements in gaps between segments are not touched.
+ * Errors: GC_EINVAL (K out of range, bad mode, null), GC_ECAPACITY (ws).
+ */
+#define GC_SUM  0
+#define GC_AVG  1
+gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_sparse *msgs,
+                                   int K, float *dense, int mode,
+                                   int accumulate, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------- DCD */
+/*
+ * Compressed model difference with random quantization ([DCD] DCD-PSGD step 2;
+ * [SlimDP] Quant-DP: buckets of 512; 8-bit and 4-bit precisions).
+ *   z_i = fl32(x_half_i - x_i); buckets of `bucket` elements over [0, n).
+ *   s_b = max |z_i| in bucket b -> scales[b].
+ *   L = 2^(bits-1) - 1.  If s_b == 0 every code is 0 and C_i = 0.  Otherwise
+ *     inv = fl32(L / s_b); y = min(L, fl32(|z_i| * inv)); l0 = floor(y);
+ *     f = y - l0; r = word (i mod 4) of Philox4x32-10(key = (seed lo, seed hi),
+ *     counter = (lo(i/4), hi(i/4), lo(step), hi(step))); u = (r >> 8) * 2^-24;
+ *     l = l0 + (u < f); C_i = +-fl32(l * fl32(s_b / L)) with the sign of z_i.
+ *   code_i = l == 0 ? 0 : (sign << (bits-1)) | l.  4-bit codes are packed two
+ *   per byte, even index in the low nibble; 8-bit codes one per byte.
+ *   x_out_i = fl32(x_i + C_i)  (x_out may equal x: step 2's local update).
+ *   scales [ceil(n/bucket)], codes [ceil(n*bits/8)] out.
+ * Errors: GC_EINVAL (bits not 4 or 8, bucket 0, null), GC_ENOTSUP
+ *         (bucket > 4096 or not a multiple of 2), GC_ERANGE (n >= 2^32).
+ */
+gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
+                          uint64_t n, int bits, uint32_t bucket, uint64_t seed,
+                          uint64_t step, float *scales, uint8_t *codes,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GRADCOMP_H */

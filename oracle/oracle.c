@@ -1,0 +1,494 @@
+/*
+ * Oracle for libgradcomp — TEST INFRASTRUCTURE ONLY (see oracle.h).
+ *
+ * Plain loops in the order the pages describe the steps.  Library routines
+ * used as steps: qsort (ordering for top-k), sqrt, copysignf, floorf.
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ------------------------------------------------------------ pairwise sum */
+/* Node [lo, lo+len) of the perfect binary tree over the zero-padded terms.
+ * A node that lies wholly in the padding is a sum of +0.0 terms, i.e. +0.0. */
+static double psum_node(const double *x, uint64_t m, uint64_t lo, uint64_t len)
+{
+    if (lo >= m) return 0.0;
+    if (len == 1) return x[lo];
+    uint64_t h = len / 2;
+    double left = psum_node(x, m, lo, h);
+    double right = psum_node(x, m, lo + h, h);
+    return left + right;
+}
+
+double orc_psum64(const double *x, uint64_t m)
+{
+    if (m == 0) return 0.0;
+    uint64_t M = 1;
+    while (M < m) M <<= 1;
+    return psum_node(x, m, 0, M);
+}
+
+/* ----------------------------------------------------------------- AdaComp */
+/*
+ * AdaComp (Chen et al.), "Proposed method":
+ *  - the layer's residual plus the new gradient is split into fixed-size bins
+ *    of L_T and each bin's max magnitude marks its important entries;
+ *  - inside a bin, the max and its neighbours that pass an adaptive threshold
+ *    (a scale factor, empirically 2x) are selected;
+ *  - selected entries are quantized to sign times one layer-wide scale, the
+ *    mean of the bins' |g_max|;
+ *  - what is not sent stays in the residual (residual gradient compression,
+ *    Abstract); layers are treated independently.
+ */
+static void adacomp_segment(const orc_seg *sg, const float *dW, float *R,
+                            float s, uint32_t *idx, float *val,
+                            uint32_t *count, float *scale_out, float *gmax_out)
+{
+    const uint64_t base = sg->offset;
+    const uint32_t n = sg->length, L = sg->bin_len;
+    const uint32_t nb = (n + L - 1) / L;
+    float *G = (float *)malloc(sizeof(float) * (size_t)n);
+    float *gmax = (float *)malloc(sizeof(float) * (size_t)nb);
+    double *gm64 = (double *)malloc(sizeof(double) * (size_t)nb);
+
+    /* residual + gradient */
+    for (uint32_t i = 0; i < n; ++i) G[i] = R[base + i] + dW[base + i];
+
+    /* bin maxima; bins restart at the segment start, the last may be short */
+    for (uint32_t b = 0; b < nb; ++b) {
+        float mx = 0.0f;
+        uint32_t lo = b * L, hi = lo + L < n ? lo + L : n;
+        for (uint32_t i = lo; i < hi; ++i) {
+            float a = fabsf(G[i]);
+            if (a > mx) mx = a;
+        }
+        gmax[b] = mx;
+        gm64[b] = (double)mx;
+    }
+
+    /* layer scale: mean of the bin maxima over the whole layer */
+    double total = orc_psum64(gm64, nb);
+    float scale = (float)(total / (double)nb);
+
+    /* selection, quantization, new residual */
+    uint32_t c = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        float g = G[i];
+        float gm = gmax[i / L];
+        float t = s * fabsf(g);
+        if (gm > 0.0f && t >= gm) {
+            float q = copysignf(scale, g);
+            R[base + i] = g - q;
+            idx[c] = (uint32_t)(base + i);
+            val[c] = q;
+            ++c;
+        } else {
+            R[base + i] = g;
+        }
+    }
+    *count = c;
+    *scale_out = scale;
+    if (gmax_out) memcpy(gmax_out, gmax, sizeof(float) * (size_t)nb);
+    free(G);
+    free(gmax);
+    free(gm64);
+}
+
+void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
+                 float scale_factor, uint32_t *out_idx, float *out_val,
+                 uint32_t *seg_off, float *seg_scale, float *gmax_out)
+{
+    /* segment s may emit up to n_s entries; stage each at its own offset */
+    uint64_t *stage_at = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nseg + 1));
+    uint64_t *bin_at = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nseg + 1));
+    stage_at[0] = 0;
+    bin_at[0] = 0;
+    for (int s = 0; s < nseg; ++s) {
+        stage_at[s + 1] = stage_at[s] + segs[s].length;
+        bin_at[s + 1] = bin_at[s] + (segs[s].length + segs[s].bin_len - 1) / segs[s].bin_len;
+    }
+    uint64_t ntot = stage_at[nseg];
+    uint32_t *sidx = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(ntot ? ntot : 1));
+    float *sval = (float *)malloc(sizeof(float) * (size_t)(ntot ? ntot : 1));
+    uint32_t *cnt = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nseg ? nseg : 1));
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < nseg; ++s)
+        adacomp_segment(&segs[s], dW, R, scale_factor, sidx + stage_at[s],
+                        sval + stage_at[s], &cnt[s], &seg_scale[s],
+                        gmax_out ? gmax_out + bin_at[s] : NULL);
+
+    uint32_t pos = 0;
+    for (int s = 0; s < nseg; ++s) {
+        seg_off[s] = pos;
+        memcpy(out_idx + pos, sidx + stage_at[s], sizeof(uint32_t) * cnt[s]);
+        memcpy(out_val + pos, sval + stage_at[s], sizeof(float) * cnt[s]);
+        pos += cnt[s];
+    }
+    seg_off[nseg] = pos;
+    free(stage_at);
+    free(bin_at);
+    free(sidx);
+    free(sval);
+    free(cnt);
+}
+
+/* --------------------------------------------------------------------- DGC */
+typedef struct keyed {
+    uint32_t key;
+    uint32_t pos;
+} keyed;
+
+/* order: larger key first; equal keys by smaller position */
+static int by_key_desc_pos_asc(const void *a, const void *b)
+{
+    const keyed *x = (const keyed *)a, *y = (const keyed *)b;
+    if (x->key != y->key) return x->key > y->key ? -1 : 1;
+    if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+    return 0;
+}
+
+static int u32_asc(const void *a, const void *b)
+{
+    uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+static uint32_t abs_bits(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    return u & 0x7FFFFFFFu;
+}
+
+/*
+ * Deep Gradient Compression (Lin et al.), vanilla-momentum variant, per
+ * gradient tensor:
+ *  - App. C: the current gradient is clipped by its L2 norm before it is
+ *    added to the accumulation; the node's threshold is thr_G * N^-1/2;
+ *  - §3.2 / App. B, D: momentum correction accumulates the momentum-adjusted
+ *    gradient (U <- m U + G) into V (V <- V + U) before sparsification;
+ *  - §3.1 / §5: only the largest entries of V (top 0.1%) are sent, the rest
+ *    keep accumulating locally;
+ *  - §3.3: momentum factor masking clears U (and V) where entries were sent.
+ */
+static void dgc_segment(const orc_seg *sg, const float *Gin, float *U, float *V,
+                        float m, float thr_G, int N, uint32_t *idx, float *val,
+                        float *clip)
+{
+    const uint64_t base = sg->offset;
+    const uint32_t n = sg->length, k = sg->k;
+
+    float c = 1.0f;
+    if (thr_G > 0.0f) {
+        float thr = (float)((double)thr_G / sqrt((double)N));
+        double *sq = (double *)malloc(sizeof(double) * (size_t)n);
+        for (uint32_t i = 0; i < n; ++i) {
+            double g = (double)Gin[base + i];
+            sq[i] = g * g; /* exact: a 24-bit mantissa squared fits in 53 bits */
+        }
+        double norm = sqrt(orc_psum64(sq, n));
+        free(sq);
+        if (norm > (double)thr) c = (float)((double)thr / norm);
+    }
+    *clip = c;
+
+    for (uint32_t i = 0; i < n; ++i) {
+        float g = c * Gin[base + i];
+        float u = m * U[base + i];
+        u = u + g;
+        U[base + i] = u;
+        V[base + i] = V[base + i] + u;
+    }
+
+    keyed *order = (keyed *)malloc(sizeof(keyed) * (size_t)n);
+    for (uint32_t i = 0; i < n; ++i) {
+        order[i].key = abs_bits(V[base + i]);
+        order[i].pos = i;
+    }
+    qsort(order, n, sizeof(keyed), by_key_desc_pos_asc);
+
+    uint32_t *chosen = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)k);
+    for (uint32_t j = 0; j < k; ++j) chosen[j] = order[j].pos;
+    qsort(chosen, k, sizeof(uint32_t), u32_asc);
+    for (uint32_t j = 0; j < k; ++j) {
+        uint64_t e = base + chosen[j];
+        idx[j] = (uint32_t)e;
+        val[j] = V[e];
+        V[e] = 0.0f;
+        U[e] = 0.0f;
+    }
+    free(chosen);
+    free(order);
+}
+
+void orc_dgc(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
+             float momentum, float thr_G, int num_nodes, uint32_t *out_idx,
+             float *out_val, uint32_t *seg_off, float *clip_out)
+{
+    uint32_t pos = 0;
+    for (int s = 0; s < nseg; ++s) {
+        seg_off[s] = pos;
+        pos += segs[s].k;
+    }
+    seg_off[nseg] = pos;
+    float *clip = (float *)malloc(sizeof(float) * (size_t)(nseg ? nseg : 1));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < nseg; ++s)
+        dgc_segment(&segs[s], G, U, V, momentum, thr_G, num_nodes,
+                    out_idx + seg_off[s], out_val + seg_off[s], &clip[s]);
+    if (clip_out) memcpy(clip_out, clip, sizeof(float) * (size_t)nseg);
+    free(clip);
+}
+
+/* -------------------------------------------------------------------- pack */
+/*
+ * DGC §3.1: the encoder stores 32-bit values and 16-bit zero-run lengths.
+ * Layout (little-endian, 4-byte aligned blocks) as documented with gc_pack.
+ */
+static void put_u32(uint8_t *p, uint32_t v)
+{
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+    p[2] = (uint8_t)(v >> 16);
+    p[3] = (uint8_t)(v >> 24);
+}
+
+static void put_u16(uint8_t *p, uint16_t v)
+{
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+}
+
+static void put_f32(uint8_t *p, float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    put_u32(p, u);
+}
+
+#define ORC_MAGIC(a, b, c, d) \
+    ((uint32_t)(a) | (uint32_t)(b) << 8 | (uint32_t)(c) << 16 | (uint32_t)(d) << 24)
+
+uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
+                  const uint32_t *idx, const float *val,
+                  const uint32_t *seg_off, const float *seg_scale,
+                  uint8_t *out, uint64_t cap)
+{
+    const uint32_t MAX = kind == 1 ? 65535u : 32767u;
+    /* first pass: the stream length */
+    uint64_t total = 16;
+    for (int s = 0; s < nseg; ++s) {
+        uint64_t E = 0, p = 0;
+        for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
+            uint64_t rel = idx[j] - segs[s].offset;
+            uint64_t gap = rel - p;
+            E += gap / MAX + 1;
+            p = rel + 1;
+        }
+        total += 16 + 2 * E + 2 * (E % 2) + (kind == 1 ? 4 * E : 0);
+    }
+    if (total > cap) return 0;
+
+    uint8_t *w = out;
+    put_u32(w, ORC_MAGIC('G', 'C', 'P', '1'));
+    put_u32(w + 4, (uint32_t)kind);
+    put_u32(w + 8, (uint32_t)nseg);
+    put_u32(w + 12, 0);
+    w += 16;
+    for (int s = 0; s < nseg; ++s) {
+        /* count entries + escapes again for the header */
+        uint64_t E = 0, p = 0;
+        for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
+            uint64_t rel = idx[j] - segs[s].offset;
+            E += (rel - p) / MAX + 1;
+            p = rel + 1;
+        }
+        uint32_t cnt = seg_off[s + 1] - seg_off[s];
+        put_u32(w, kind == 1 ? ORC_MAGIC('D', 'G', 'C', '1') : ORC_MAGIC('A', 'D', 'C', '1'));
+        put_u32(w + 4, segs[s].length);
+        put_u32(w + 8, (uint32_t)E);
+        if (kind == 1)
+            put_u32(w + 12, cnt);
+        else
+            put_f32(w + 12, seg_scale[s]);
+        uint8_t *runs = w + 16;
+        uint8_t *vals = runs + 2 * E + 2 * (E % 2);
+        uint64_t e = 0;
+        p = 0;
+        for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
+            uint64_t rel = idx[j] - segs[s].offset;
+            uint64_t gap = rel - p;
+            while (gap >= MAX) { /* escape: skip MAX positions, carry nothing */
+                put_u16(runs + 2 * e, (uint16_t)MAX);
+                if (kind == 1) put_f32(vals + 4 * e, 0.0f);
+                ++e;
+                gap -= MAX;
+            }
+            if (kind == 1) {
+                put_u16(runs + 2 * e, (uint16_t)gap);
+                put_f32(vals + 4 * e, val[j]);
+            } else {
+                uint16_t sign = signbit(val[j]) ? 0x8000u : 0u;
+                put_u16(runs + 2 * e, (uint16_t)(sign | gap));
+            }
+            ++e;
+            p = rel + 1;
+        }
+        if (E % 2) put_u16(runs + 2 * E, 0);
+        w = vals + (kind == 1 ? 4 * E : 0);
+    }
+    return (uint64_t)(w - out);
+}
+
+/* ------------------------------------------------------------------ decode */
+/*
+ * DGC App. A: the nodes' gradients are summed; AdaComp: the learners'
+ * compressed gradients are averaged.  Messages are added in array order.
+ */
+void orc_decode(const orc_seg *segs, int nseg, int K,
+                const uint32_t *const *idx, const float *const *val,
+                const uint64_t *count, float *dense, int mode, int accumulate)
+{
+    uint64_t n = 0;
+    for (int s = 0; s < nseg; ++s) {
+        uint64_t end = segs[s].offset + segs[s].length;
+        if (end > n) n = end;
+    }
+    float *S = (float *)calloc(n ? n : 1, sizeof(float)); /* all +0.0f */
+    for (int k = 0; k < K; ++k)
+        for (uint64_t j = 0; j < count[k]; ++j) S[idx[k][j]] = S[idx[k][j]] + val[k][j];
+    for (int s = 0; s < nseg; ++s) {
+        for (uint32_t i = 0; i < segs[s].length; ++i) {
+            uint64_t e = segs[s].offset + i;
+            float r = mode == 1 ? S[e] / (float)K : S[e];
+            dense[e] = accumulate ? dense[e] + r : r;
+        }
+    }
+    free(S);
+}
+
+/* -------------------------------------------------------------- Philox4x32 */
+/*
+ * Philox4x32-10, from Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+ * as easy as 1, 2, 3" (SC'11): ten rounds of two 32x32->64 multiplies with the
+ * round key added (Weyl sequence) between rounds.
+ */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        uint64_t p0 = (uint64_t)M0 * c0;
+        uint64_t p1 = (uint64_t)M1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* --------------------------------------------------------------------- DCD */
+/*
+ * DCD-PSGD (Tang et al.) step 2: z = x_{t+1/2} - x_t, x_{t+1} = x_t + C(z);
+ * C is random quantization (the page allows random quantization or random
+ * sparsification) in buckets (Slim-DP's Quant-DP setting uses buckets of 512)
+ * at 8 or 4 bits, with unbiased stochastic rounding to a uniform grid whose
+ * top level is the bucket's max magnitude.
+ */
+void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
+             int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+             float *scales, uint8_t *codes)
+{
+    const uint32_t L = (1u << (bits - 1)) - 1u;
+    const float Lf = (float)L;
+    const uint64_t nb = (n + bucket - 1) / bucket;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    if (bits == 4) memset(codes, 0, (size_t)((n + 1) / 2));
+
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < (int64_t)nb; ++b) {
+        uint64_t lo = (uint64_t)b * bucket;
+        uint64_t hi = lo + bucket < n ? lo + bucket : n;
+        float sb = 0.0f;
+        for (uint64_t i = lo; i < hi; ++i) {
+            float z = x_half[i] - x[i];
+            float a = fabsf(z);
+            if (a > sb) sb = a;
+        }
+        scales[b] = sb;
+        float inv = sb > 0.0f ? Lf / sb : 0.0f;
+        float stepq = sb > 0.0f ? sb / Lf : 0.0f;
+        for (uint64_t i = lo; i < hi; ++i) {
+            float z = x_half[i] - x[i];
+            uint32_t level = 0;
+            if (sb > 0.0f) {
+                float y = fabsf(z) * inv;
+                if (y > Lf) y = Lf;
+                float l0 = floorf(y);
+                float f = y - l0;
+                uint64_t q = i / 4;
+                uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)step,
+                                   (uint32_t)(step >> 32)};
+                uint32_t r[4];
+                orc_philox4x32_10(ctr, key, r);
+                float u = (float)(r[i % 4] >> 8) * 0x1p-24f;
+                level = (uint32_t)l0 + (u < f ? 1u : 0u);
+            }
+            float C = 0.0f;
+            uint32_t code = 0;
+            if (level > 0) {
+                float mag = (float)level * stepq;
+                C = signbit(z) ? -mag : mag;
+                code = (signbit(z) ? 1u << (bits - 1) : 0u) | level;
+            }
+            x_out[i] = x[i] + C;
+            if (bits == 8) {
+                codes[i] = (uint8_t)code;
+            } else {
+                /* buckets hold an even number of elements, so a byte never
+                 * straddles two buckets (or two threads) */
+                codes[i / 2] |= (uint8_t)(code << (4 * (i % 2)));
+            }
+        }
+    }
+}

@@ -1,0 +1,73 @@
+/*
+ * Oracle for libgradcomp — TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU definition of every result the
+ * compression path computes.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may build, load or call it; the product path
+ * never does.  It shares no code, header, table or helper with the HIP path.
+ *
+ * Arithmetic: gradients and states are fp32 (the DGC encoder carries 32-bit
+ * values; residuals and momenta live in the same fp32 layout), so every
+ * elementwise step is one correctly rounded fp32 IEEE operation, in the order
+ * written, with no contraction (built with -ffp-contract=off).  Reductions are
+ * in fp64 through orc_psum64's fixed pairwise tree.
+ *
+ * Parity pins: every function is pinned by tests that do not re-run it (hand
+ * derived golden values, closed forms, invariants, brute force on tiny
+ * inputs, published known-answer vectors).  See tests/test_oracle_*.py.
+ */
+#ifndef GC_ORACLE_H
+#define GC_ORACLE_H
+#include <stdint.h>
+
+typedef struct orc_seg {
+    uint64_t offset;
+    uint32_t length;
+    uint32_t bin_len;
+    uint32_t k;
+    uint32_t pad;
+} orc_seg;
+
+/* Number of threads the OpenMP runtime uses (1 when built without OpenMP). */
+int orc_num_threads(void);
+void orc_set_num_threads(int n);
+
+/* Pairwise sum in fp64: pad x[0..m) with +0.0 to the next power of two and
+ * add as a perfect binary tree in index order. */
+double orc_psum64(const double *x, uint64_t m);
+
+/* AdaComp step on every segment (see oracle.c for the steps).
+ * gmax_out (optional) receives all bin maxima, segments in order. */
+void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
+                 float scale_factor, uint32_t *out_idx, float *out_val,
+                 uint32_t *seg_off, float *seg_scale, float *gmax_out);
+
+/* DGC step (vanilla momentum) on every segment.  clip_out (optional)
+ * receives the per-segment clip coefficient. */
+void orc_dgc(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
+             float momentum, float thr_G, int num_nodes, uint32_t *out_idx,
+             float *out_val, uint32_t *seg_off, float *clip_out);
+
+/* Run-length packing.  kind 1 = DGC, 2 = AdaComp.  Returns bytes written,
+ * or 0 if cap is too small. */
+uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
+                  const uint32_t *idx, const float *val,
+                  const uint32_t *seg_off, const float *seg_scale,
+                  uint8_t *out, uint64_t cap);
+
+/* Decompress-aggregate K messages (idx[k], val[k], count[k]) into dense.
+ * mode 0 = sum, 1 = average; accumulate != 0 adds into dense. */
+void orc_decode(const orc_seg *segs, int nseg, int K,
+                const uint32_t *const *idx, const float *const *val,
+                const uint64_t *count, float *dense, int mode, int accumulate);
+
+/* Philox4x32-10 block: out = philox(ctr, key). */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
+                       uint32_t out[4]);
+
+/* DCD difference + random quantization on a flat buffer. */
+void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
+             int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+             float *scales, uint8_t *codes);
+
+#endif
