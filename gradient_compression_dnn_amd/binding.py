@@ -1,0 +1,248 @@
+"""ctypes binding of libgradcomp: the C-ABI calls under the same names.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+GC_OK, GC_EINVAL, GC_ECAPACITY, GC_ERANGE, GC_EHIP, GC_ENOTSUP = 0, -1, -2, -3, -4, -5
+GC_OP_DGC, GC_OP_ADACOMP, GC_OP_PACK, GC_OP_DECODE = 1, 2, 3, 4
+GC_KIND_DGC, GC_KIND_ADACOMP = 1, 2
+GC_SUM, GC_AVG = 0, 1
+GC_MAX_BIN_LEN = 4096
+GC_MAX_MESSAGES = 64
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgradcomp.so")
+
+
+class GCError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libgradcomp status {status}: {msg}")
+        self.status = status
+
+
+class gc_segment(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("length", ctypes.c_uint32),
+                ("bin_len", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+class gc_sparse(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("seg_off", ctypes.c_void_p), ("seg_scale", ctypes.c_void_p),
+                ("cap", ctypes.c_uint64)]
+
+
+_lib = None
+
+# every symbol the header declares, with (restype, argtypes)
+_P = ctypes.c_void_p
+_SIGS = {
+    "gc_last_error": (ctypes.c_char_p, []),
+    "gc_version": (ctypes.c_char_p, []),
+    "gc_plan_create": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_uint64, _P]),
+    "gc_plan_destroy": (None, [_P]),
+    "gc_plan_num_segments": (ctypes.c_int, [_P]),
+    "gc_plan_num_elements": (ctypes.c_uint64, [_P]),
+    "gc_plan_total_k": (ctypes.c_uint64, [_P]),
+    "gc_plan_total_bins": (ctypes.c_uint64, [_P]),
+    "gc_topk_count": (ctypes.c_uint32, [ctypes.c_uint32]),
+    "gc_plan_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int]),
+    "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "gc_dgc_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                   _P, _P, ctypes.c_size_t, _P]),
+    "gc_pack_bound": (ctypes.c_uint64, [_P, ctypes.c_int]),
+    "gc_pack": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_uint64, _P, _P, ctypes.c_size_t, _P]),
+    "gc_decompress_accumulate": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
+                                                _P, ctypes.c_size_t, _P]),
+    "gc_dcd_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
+                                       ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
+}
+
+
+def load():
+    """Load libgradcomp.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(status: int):
+    if status != GC_OK:
+        raise GCError(status, load().gc_last_error().decode())
+
+
+def gc_version() -> str:
+    return load().gc_version().decode()
+
+
+def gc_last_error() -> str:
+    return load().gc_last_error().decode()
+
+
+def gc_topk_count(n: int) -> int:
+    return int(load().gc_topk_count(int(n)))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _f32(t: torch.Tensor, n: int, name: str):
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name}: need a contiguous CUDA float32 tensor of >= {n} elements")
+    return _ptr(t)
+
+
+# ---------------------------------------------------------------- plans
+class Plan:
+    """A validated segment table (gc_plan)."""
+
+    def __init__(self, table, n_total: int | None = None):
+        t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+        self.table = t
+        self.n_total = int(n_total if n_total is not None else (t[-1, 0] + t[-1, 1] if len(t) else 0))
+        arr = (gc_segment * max(len(t), 1))()
+        for i, (o, n, lt, k) in enumerate(t):
+            arr[i] = gc_segment(int(o), int(n), int(lt), int(k), 0)
+        h = ctypes.c_void_p()
+        _check(load().gc_plan_create(arr, len(t), self.n_total, ctypes.byref(h)))
+        self.handle = h
+        self.nseg = len(t)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.gc_plan_destroy(h)
+            self.handle = None
+
+    @property
+    def total_k(self) -> int:
+        return int(load().gc_plan_total_k(self.handle))
+
+    @property
+    def total_bins(self) -> int:
+        return int(load().gc_plan_total_bins(self.handle))
+
+    def workspace_bytes(self, op: int) -> int:
+        return int(load().gc_plan_workspace_bytes(self.handle, op))
+
+    def workspace(self, op: int, device="cuda") -> torch.Tensor:
+        return torch.empty(max(self.workspace_bytes(op), 1), dtype=torch.uint8, device=device)
+
+    def pack_bound(self, kind: int) -> int:
+        return int(load().gc_pack_bound(self.handle, kind))
+
+
+def gc_plan_create(table, n_total=None) -> Plan:
+    return Plan(table, n_total)
+
+
+def gc_plan_workspace_bytes(plan: Plan, op: int) -> int:
+    return plan.workspace_bytes(op)
+
+
+def gc_pack_bound(plan: Plan, kind: int) -> int:
+    return plan.pack_bound(kind)
+
+
+@dataclass
+class Sparse:
+    """A message: device tensors idx (int32 holding u32), val, seg_off, seg_scale."""
+    idx: torch.Tensor
+    val: torch.Tensor
+    seg_off: torch.Tensor
+    seg_scale: torch.Tensor
+    cap: int
+
+    @staticmethod
+    def empty(plan: Plan, cap: int, device="cuda") -> "Sparse":
+        return Sparse(torch.zeros(max(cap, 1), dtype=torch.int32, device=device),
+                      torch.zeros(max(cap, 1), dtype=torch.float32, device=device),
+                      torch.zeros(plan.nseg + 1, dtype=torch.int32, device=device),
+                      torch.zeros(max(plan.nseg, 1), dtype=torch.float32, device=device), cap)
+
+    def struct(self) -> gc_sparse:
+        return gc_sparse(self.idx.data_ptr(), self.val.data_ptr(), self.seg_off.data_ptr(),
+                         self.seg_scale.data_ptr(), self.cap)
+
+    def count(self) -> int:
+        return int(self.seg_off[-1].item())
+
+    def host(self):
+        """(idx u32, val f32, seg_off u32, seg_scale f32) as NumPy arrays."""
+        n = self.count()
+        return (self.idx[:n].cpu().numpy().view(np.uint32), self.val[:n].cpu().numpy(),
+                self.seg_off.cpu().numpy().view(np.uint32), self.seg_scale.cpu().numpy())
+
+
+# -------------------------------------------------------------- hot calls
+def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws: torch.Tensor):
+    n = plan.n_total
+    msg = out.struct()
+    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"),
+                                      float(scale_factor), ctypes.byref(msg), _ptr(ws), ws.numel(),
+                                      _stream(R)))
+
+
+def gc_dgc_step(plan: Plan, G, U, V, momentum: float, thr_G: float, num_nodes: int, out: Sparse,
+                ws: torch.Tensor):
+    n = plan.n_total
+    msg = out.struct()
+    _check(load().gc_dgc_step(plan.handle, _f32(G, n, "G"), _f32(U, n, "U"), _f32(V, n, "V"),
+                              float(momentum), float(thr_G), int(num_nodes), ctypes.byref(msg),
+                              _ptr(ws), ws.numel(), _stream(V)))
+
+
+def gc_pack(plan: Plan, kind: int, msg: Sparse, out: torch.Tensor, out_bytes: torch.Tensor,
+            ws: torch.Tensor):
+    if out.dtype != torch.uint8 or out_bytes.dtype != torch.int64:
+        raise ValueError("gc_pack: out must be uint8 and out_bytes int64 (holding u64)")
+    m = msg.struct()
+    _check(load().gc_pack(plan.handle, int(kind), ctypes.byref(m), _ptr(out), out.numel(),
+                          _ptr(out_bytes), _ptr(ws), ws.numel(), _stream(out)))
+
+
+def gc_decompress_accumulate(plan: Plan, msgs, dense, mode: int, accumulate: bool,
+                             ws: torch.Tensor):
+    K = len(msgs)
+    arr = (gc_sparse * max(K, 1))(*[m.struct() for m in msgs])
+    _check(load().gc_decompress_accumulate(plan.handle, arr, K, _f32(dense, plan.n_total, "dense"),
+                                           int(mode), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                           _stream(dense)))
+
+
+def gc_dcd_compress(x, x_half, x_out, bits: int, bucket: int, seed: int, step: int,
+                    scales: torch.Tensor, codes: torch.Tensor):
+    n = x.numel()
+    nb = (n + bucket - 1) // bucket
+    if scales.numel() < nb or codes.numel() < (n * bits + 7) // 8 or codes.dtype != torch.uint8:
+        raise ValueError("gc_dcd_compress: scales or codes too small")
+    _check(load().gc_dcd_compress(_f32(x, n, "x"), _f32(x_half, n, "x_half"), _f32(x_out, n, "x_out"),
+                                  n, int(bits), int(bucket), int(seed) & (2 ** 64 - 1),
+                                  int(step) & (2 ** 64 - 1), _f32(scales, nb, "scales"), _ptr(codes),
+                                  _stream(x_out)))

@@ -1,0 +1,201 @@
+// Compressed model difference with random quantization.
+// "Communication Compression for Decentralized Training" (Tang et al.),
+// DCD-PSGD step 2: z = x_{t+1/2} - x_t and x_{t+1} = x_t + C(z), with C a
+// random quantization.  Buckets of 512 and 8-bit codes are the Quant-DP
+// setting in "Slim-DP" (experimental setup); the DCD page also runs 4 bits.
+//
+// One workgroup per 4096 elements; thread t of row j owns the 4 consecutive
+// elements [base + 1024 j + 4 t, +4), which share one Philox4x32-10 block
+// (counter = element / 4), so every random word is drawn exactly once.
+// Bucket maxima: per-thread max of 4, butterfly max over the lanes of a
+// bucket inside a wave, LDS max across waves.
+#include <cmath>
+
+#include "gc_internal.hpp"
+
+namespace gc {
+
+namespace {
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products, the
+// key advanced by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+    constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hi0 = __umulhi(kM0, c.x), lo0 = kM0 * c.x;
+        const uint32_t hi1 = __umulhi(kM1, c.z), lo1 = kM1 * c.z;
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        k0 += kW0;
+        k1 += kW1;
+    }
+    return c;
+}
+
+constexpr int kRows = kChunk / (4 * kBlock);  // 4 rows of 1024 elements
+
+template <bool kAligned>
+__global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may alias xo
+                                                     const float *__restrict__ xh, float *xo,
+                                                     uint64_t n, int bits, int blog2,
+                                                     uint32_t k0, uint32_t k1, uint64_t step,
+                                                     float *__restrict__ scales,
+                                                     uint8_t *__restrict__ codes) {
+    const uint64_t base = uint64_t(blockIdx.x) * kChunk;
+    const uint32_t bucket = 1u << blog2;
+    const int lanes_per_bucket = bucket >= 4 * kWave ? kWave : int(bucket / 4);
+    __shared__ uint32_t smax[kChunk / 4];  // up to 1024 buckets of 4
+    const uint32_t nbk = kChunk >> blog2;
+    for (uint32_t b = threadIdx.x; b < nbk; b += kBlock) smax[b] = 0u;
+    float xv[kRows][4], zv[kRows][4];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        const uint64_t i0 = base + uint64_t(j) * (4 * kBlock) + 4u * threadIdx.x;
+        if (kAligned && i0 + 3 < n) {
+            float4 a = *reinterpret_cast<const float4 *>(x + i0);
+            float4 h = *reinterpret_cast<const float4 *>(xh + i0);
+            xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
+            zv[j][0] = h.x - a.x; zv[j][1] = h.y - a.y; zv[j][2] = h.z - a.z; zv[j][3] = h.w - a.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xv[j][u] = 0.0f;
+                zv[j][u] = 0.0f;
+                if (i0 + u < n) {
+                    xv[j][u] = x[i0 + u];
+                    zv[j][u] = xh[i0 + u] - xv[j][u];
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t a = dev_f2u(zv[j][u]) & 0x7FFFFFFFu;
+            m = a > m ? a : m;
+        }
+        for (int d = 1; d < lanes_per_bucket; d <<= 1) {
+            uint32_t o = __shfl_xor(m, d, kWave);
+            m = m > o ? m : o;
+        }
+        const uint32_t e0 = uint32_t(j) * (4 * kBlock) + 4u * threadIdx.x;
+        if ((lane_id() & (lanes_per_bucket - 1)) == 0) atomicMax(&smax[e0 >> blog2], m);
+    }
+    __syncthreads();
+    const uint32_t L = (1u << (bits - 1)) - 1u;
+    const float Lf = static_cast<float>(L);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        const uint32_t e0 = uint32_t(j) * (4 * kBlock) + 4u * threadIdx.x;
+        const uint64_t i0 = base + e0;
+        if (i0 >= n) continue;
+        const float sb = dev_u2f(smax[e0 >> blog2]);
+        const uint64_t q = i0 >> 2;
+        const uint4 r = philox4x32_10(make_uint4(uint32_t(q), uint32_t(q >> 32), uint32_t(step),
+                                                 uint32_t(step >> 32)),
+                                      k0, k1);
+        const uint32_t words[4] = {r.x, r.y, r.z, r.w};
+        uint32_t code[4];
+        float out[4];
+        const float inv = sb > 0.0f ? Lf / sb : 0.0f;
+        const float stepq = sb > 0.0f ? sb / Lf : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t level = 0;
+            const float z = zv[j][u];
+            if (sb > 0.0f) {
+                float y = fabsf(z) * inv;
+                if (y > Lf) y = Lf;
+                const float l0 = floorf(y);
+                const float f = y - l0;
+                const float uu = static_cast<float>(words[u] >> 8) * 0x1p-24f;
+                level = static_cast<uint32_t>(l0) + (uu < f ? 1u : 0u);
+            }
+            float C = 0.0f;
+            code[u] = 0;
+            if (level > 0) {
+                const float mag = static_cast<float>(level) * stepq;
+                const bool neg = dev_f2u(z) >> 31;
+                C = neg ? -mag : mag;
+                code[u] = (neg ? 1u << (bits - 1) : 0u) | level;
+            }
+            out[u] = xv[j][u] + C;
+        }
+        if (kAligned && i0 + 3 < n) {
+            *reinterpret_cast<float4 *>(xo + i0) = make_float4(out[0], out[1], out[2], out[3]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u < n) xo[i0 + u] = out[u];
+        }
+        if (bits == 8) {
+            if (i0 + 3 < n) {
+                *reinterpret_cast<uint32_t *>(codes + i0) =
+                    code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i0 + u < n) codes[i0 + u] = static_cast<uint8_t>(code[u]);
+            }
+        } else {
+            const uint32_t b0 = code[0] | code[1] << 4, b1 = code[2] | code[3] << 4;
+            if (i0 + 3 < n) {
+                *reinterpret_cast<uint16_t *>(codes + i0 / 2) = static_cast<uint16_t>(b0 | b1 << 8);
+            } else {
+                // the stream ends inside this group: only bytes holding a
+                // real element exist; missing high nibbles stay zero
+                codes[i0 / 2] = static_cast<uint8_t>(i0 + 1 < n ? b0 : code[0]);
+                if (i0 + 2 < n) codes[i0 / 2 + 1] = static_cast<uint8_t>(i0 + 3 < n ? b1 : code[2]);
+            }
+        }
+    }
+    const uint64_t b_first = base >> blog2;
+    const uint64_t nb_total = (n + bucket - 1) >> blog2;
+    for (uint32_t b = threadIdx.x; b < nbk; b += kBlock)
+        if (b_first + b < nb_total) scales[b_first + b] = dev_u2f(smax[b]);
+}
+
+}  // namespace
+
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out, uint64_t n,
+                                     int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+                                     float *scales, uint8_t *codes, hipStream_t stream) {
+    clear_error();
+    if (!x || !x_half || !x_out || !scales || !codes)
+        return set_error(GC_EINVAL, "gc_dcd_compress: buffers must be non-null");
+    if (bits != 4 && bits != 8) return set_error(GC_EINVAL, "gc_dcd_compress: bits must be 4 or 8");
+    if (bucket == 0) return set_error(GC_EINVAL, "gc_dcd_compress: bucket must be >= 1");
+    if (bucket < 4 || bucket > uint32_t(kChunk) || (bucket & (bucket - 1)))
+        return set_error(GC_ENOTSUP, "gc_dcd_compress: bucket must be a power of two in [4, 4096]");
+    if (n >= (uint64_t(1) << 32)) return set_error(GC_ERANGE, "gc_dcd_compress: n must be < 2^32");
+    if (reinterpret_cast<uintptr_t>(codes) % 4)
+        return set_error(GC_EINVAL, "gc_dcd_compress: codes must be 4-byte aligned");
+    if (x_half == x_out && x_half != x)
+        return set_error(GC_EINVAL, "gc_dcd_compress: x_out may alias x only");
+    if (n == 0) return GC_OK;
+    int blog2 = 0;
+    while ((1u << blog2) < bucket) ++blog2;
+    const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(x_half) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(x_out) % 16 == 0);
+    const unsigned grid = grid_1d(n, kChunk);
+    const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+    if (aligned)
+        dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+                                                      scales, codes);
+    else
+        dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+                                                       scales, codes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_dcd_compress launch");
+    return GC_OK;
+}

@@ -1,0 +1,314 @@
+// Internal definitions shared by the libgradcomp translation units:
+// plan tables, workspace layouts, error state and block-level device
+// primitives for gfx950 (wave64, 256-thread workgroups).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gradcomp.h"
+
+namespace gc {
+
+// ------------------------------------------------------------ launch shape
+constexpr int kBlock = 256;            // threads per workgroup (4 waves)
+constexpr int kWave = 64;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kEPT = 16;               // elements per thread in dense passes
+constexpr int kChunk = kBlock * kEPT;  // 4096 elements per workgroup tile
+constexpr int kChunkLog2 = 12;
+
+// Radix-select digits over the 31-bit magnitude key: 11 + 11 + 9 bits.
+constexpr int kDigit1Bits = 11, kDigit2Bits = 11, kDigit3Bits = 9;
+constexpr int kHist1 = 1 << kDigit1Bits;
+constexpr int kHist2 = 1 << kDigit2Bits;
+constexpr int kHist3 = 1 << kDigit3Bits;
+
+// ------------------------------------------------------------ plan tables
+// One segment as the kernels see it.  DGC chunks are aligned kChunk-element
+// tiles from the segment start (so pairwise-tree nodes line up with them);
+// AdaComp chunks hold a whole number of bins.
+struct SegDev {
+    uint64_t off;        // first element in the flat buffer
+    uint32_t len;        // n_s
+    uint32_t bin_len;    // L_T
+    uint32_t k;          // top-k count
+    uint32_t nbins;      // ceil(len / bin_len)
+    uint32_t dchunk0;    // first DGC chunk
+    uint32_t dnchunk;    // DGC chunks in this segment
+    uint32_t achunk0;    // first AdaComp chunk
+    uint32_t anchunk;    // AdaComp chunks in this segment
+    uint32_t achunk_len; // elements per AdaComp chunk (multiple of bin_len)
+    uint32_t bin0;       // first bin of the segment in the plan-wide bin array
+    uint32_t kbase;      // first message slot of the segment in a DGC message
+    uint32_t pad;
+};
+
+struct PlanDev {
+    const SegDev *seg;          // [nseg]
+    const uint32_t *dchunk_seg; // [ndchunk]
+    const uint32_t *achunk_seg; // [nachunk]
+    const uint64_t *seg_start;  // [nseg] offsets, for searching an index
+    int nseg;
+    uint32_t ndchunk;
+    uint32_t nachunk;
+    uint64_t n_total;
+};
+
+}  // namespace gc
+
+struct gc_plan {
+    int nseg = 0;
+    uint64_t n_total = 0;
+    uint64_t total_k = 0;
+    uint64_t total_bins = 0;
+    uint32_t ndchunk = 0;
+    uint32_t nachunk = 0;
+    std::vector<gc::SegDev> seg;
+    std::vector<uint32_t> dchunk_seg;
+    std::vector<uint32_t> achunk_seg;
+    std::vector<uint64_t> seg_start;
+    // device copies, one per device, uploaded on first use
+    std::mutex mu;
+    std::vector<std::pair<int, void *>> dev_blob;
+};
+
+namespace gc {
+
+// --------------------------------------------------------------- errors
+gc_status set_error(gc_status code, const std::string &msg);
+gc_status hip_error(hipError_t e, const char *what);
+void clear_error();
+
+// Device tables of a plan on the current device (uploads on first use).
+gc_status plan_device(const gc_plan *plan, PlanDev *out);
+
+// Workspace bytes per operation (each op's translation unit lays out its own).
+size_t dgc_workspace_bytes(const gc_plan *plan);
+size_t adacomp_workspace_bytes(const gc_plan *plan);
+size_t pack_workspace_bytes(const gc_plan *plan);
+size_t decode_workspace_bytes(const gc_plan *plan);
+
+// --------------------------------------------------------------- workspace
+// Bump allocator over the caller's workspace; every region 256-byte aligned.
+struct WsCursor {
+    uintptr_t base;
+    size_t used = 0;
+    explicit WsCursor(void *p) : base(reinterpret_cast<uintptr_t>(p)) {}
+    template <class T>
+    T *take(size_t count) {
+        used = (used + 255) & ~size_t(255);
+        T *p = reinterpret_cast<T *>(base + used);
+        used += sizeof(T) * count;
+        return p;
+    }
+};
+
+inline unsigned grid_1d(uint64_t n, unsigned per_block) {
+    return static_cast<unsigned>((n + per_block - 1) / per_block);
+}
+
+// Fill u32 words with zero (used instead of hipMemsetAsync so the library's
+// enqueued work stays plain kernels).
+void zero_words(uint32_t *p, size_t words, hipStream_t s);
+
+inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// ===================================================================== device
+#if defined(__HIPCC__)
+
+__device__ __forceinline__ uint32_t dev_f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float dev_u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Number of set bits of a wave mask below this lane.
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+// Exclusive scan of one value per thread, in thread order, over the
+// workgroup.  Returns the exclusive prefix; *total receives the sum.
+template <class T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *total) {
+    __shared__ T wsum[kWaves];
+    T x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T y = __shfl_up(x, d, kWave);
+        if (lane_id() >= d) x += y;
+    }
+    if (lane_id() == kWave - 1) wsum[wave_id()] = x;
+    __syncthreads();
+    T before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        T s = wsum[w];
+        if (w < wave_id()) before += s;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return before + x - v;
+}
+
+// Ordered compaction of kEPT flags per thread, where element (j, t) has rank
+// j * kBlock + t in index order.  pos[j] receives the output slot of flagged
+// elements; returns the number of flagged elements in the block.
+template <int EPT>
+__device__ __forceinline__ uint32_t block_compact(const bool (&flag)[EPT], uint32_t (&pos)[EPT]) {
+    __shared__ uint32_t cnt[EPT * kWaves];
+    __shared__ uint32_t tot;
+    uint32_t rank[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        uint64_t m = __ballot(flag[j]);
+        rank[j] = lane_rank(m);
+        if (lane_id() == 0) cnt[j * kWaves + wave_id()] = static_cast<uint32_t>(__popcll(m));
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        // one wave scans the EPT*kWaves (<= 64) counters in (j, wave) order
+        uint32_t v = threadIdx.x < EPT * kWaves ? cnt[threadIdx.x] : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            uint32_t y = __shfl_up(x, d, kWave);
+            if (lane_id() >= d) x += y;
+        }
+        if (threadIdx.x < EPT * kWaves) cnt[threadIdx.x] = x - v;
+        if (threadIdx.x == kWave - 1) tot = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) pos[j] = cnt[j * kWaves + wave_id()] + rank[j];
+    uint32_t t = tot;
+    __syncthreads();
+    return t;
+}
+
+// Perfect binary tree sum of one double per thread, leaves in thread order.
+// Butterfly adds are bit-identical on both lanes because IEEE addition is
+// commutative, so every lane ends with the wave's subtree sum.
+__device__ __forceinline__ double block_tree_sum(double v) {
+    __shared__ double ws[kWaves];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v = v + __shfl_xor(v, d, kWave);
+    if (lane_id() == 0) ws[wave_id()] = v;
+    __syncthreads();
+    double r = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    __syncthreads();
+    return r;
+}
+
+// Canonical pairwise sum of x[0..m) (zero-padded to a power of two) by one
+// workgroup.  load(i) returns term i as double for i < m.  Thread t sums an
+// aligned sub-block of B = max(1, M/kBlock) leaves sequentially with the
+// binary-counter stack (which forms exactly the perfect subtree), then the
+// 256 subtree sums are combined by block_tree_sum.  Sub-blocks past m are
+// +0.0 subtrees, and adding +0.0 to a non-negative value is exact, so the
+// result equals the tree over M leaves.
+constexpr int kTreeDepth = 26;  // sub-blocks of up to 2^25 leaves per thread
+
+template <class Load>
+__device__ double block_pairwise_sum(uint64_t m, Load load) {
+    uint64_t M = 1;
+    while (M < m) M <<= 1;
+    uint64_t B = M > kBlock ? M / kBlock : 1;
+    uint64_t lo = static_cast<uint64_t>(threadIdx.x) * B;
+    double stack[kTreeDepth];
+    double carry = 0.0;
+    for (uint64_t i = 0; i < B; ++i) {
+        uint64_t g = lo + i;
+        carry = g < m ? load(g) : 0.0;
+        bool done = false;
+#pragma unroll
+        for (int l = 0; l < kTreeDepth; ++l) {
+            if (!done) {
+                if ((i >> l) & 1) {
+                    carry = stack[l] + carry;
+                } else {
+                    stack[l] = carry;
+                    done = true;
+                }
+            }
+        }
+    }
+    // after B (a power of two) leaves the full subtree sum is the last carry
+    return block_tree_sum(carry);
+}
+
+// Given NB bucket counts (read through `count(b)`), and 1 <= k <= total, find
+// the bucket d holding the k-th largest element: sum_{b>d} < k <= sum_{b>=d}.
+// Returns d and writes sum_{b>d} to *above.  Called by the whole workgroup.
+template <int NB, class Count>
+__device__ uint32_t block_find_bucket(uint32_t k, Count count, uint32_t *above) {
+    constexpr int per = NB / kBlock;
+    static_assert(per >= 1 && NB % kBlock == 0, "bucket count");
+    __shared__ uint32_t res_d, res_above;
+    if (threadIdx.x == 0) {
+        res_d = 0;
+        res_above = 0;
+    }
+    uint32_t c[per];
+    uint32_t tsum = 0;
+    // thread t owns buckets NB-1-t*per down to NB-(t+1)*per (descending)
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = count(NB - 1 - threadIdx.x * per - i);
+        tsum += c[i];
+    }
+    uint32_t total;
+    uint32_t pre = block_exclusive_scan(tsum, &total);
+    if (pre < k && pre + tsum >= k) {
+        uint32_t cum = pre;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            if (cum + c[i] >= k) {
+                res_d = NB - 1 - threadIdx.x * per - i;
+                res_above = cum;
+                break;
+            }
+            cum += c[i];
+        }
+    }
+    __syncthreads();
+    *above = res_above;
+    uint32_t d = res_d;
+    __syncthreads();
+    return d;
+}
+
+// Last-workgroup detection: every workgroup of a group calls this once after
+// its global writes; exactly one (the last to arrive) gets true, and after
+// the acquire fence it sees all the others' writes.
+__device__ __forceinline__ bool block_arrive_last(uint32_t *ticket, uint32_t expected) {
+    __shared__ bool last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        uint32_t prev = atomicAdd(ticket, 1u);
+        last = (prev == expected - 1);
+    }
+    __syncthreads();
+    bool l = last;
+    if (l) __threadfence();
+    return l;
+}
+
+// Read a value written by other workgroups of the same launch, bypassing
+// the non-coherent vector L1.
+template <class T>
+__device__ __forceinline__ T load_coherent(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+#endif  // __HIPCC__
+
+}  // namespace gc

@@ -1,0 +1,215 @@
+// Host side of libgradcomp: error state, segment-plan validation and tables,
+// device upload of the tables, workspace sizing.
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "gc_internal.hpp"
+
+namespace gc {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+gc_status set_error(gc_status code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+gc_status hip_error(hipError_t e, const char *what) {
+    return set_error(GC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void clear_error() { g_last_error.clear(); }
+
+__global__ void zero_words_kernel(uint32_t *p, size_t words) {
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (; i < words; i += stride) p[i] = 0u;
+}
+
+void zero_words(uint32_t *p, size_t words, hipStream_t s) {
+    if (words == 0) return;
+    unsigned grid = static_cast<unsigned>(std::min<size_t>((words + kBlock - 1) / kBlock, 2048));
+    zero_words_kernel<<<grid, kBlock, 0, s>>>(p, words);
+}
+
+// Layout of the per-device table blob.
+struct BlobLayout {
+    size_t seg, dchunk, achunk, start, total;
+};
+
+static BlobLayout blob_layout(const gc_plan *p) {
+    BlobLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        o = (o + 255) & ~size_t(255);
+        size_t at = o;
+        o += bytes;
+        return at;
+    };
+    L.seg = take(sizeof(SegDev) * p->seg.size());
+    L.dchunk = take(sizeof(uint32_t) * p->dchunk_seg.size());
+    L.achunk = take(sizeof(uint32_t) * p->achunk_seg.size());
+    L.start = take(sizeof(uint64_t) * p->seg_start.size());
+    L.total = std::max<size_t>(o, 256);
+    return L;
+}
+
+gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
+    gc_plan *plan = const_cast<gc_plan *>(cplan);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_error(e, "hipGetDevice");
+    BlobLayout L = blob_layout(plan);
+    void *blob = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(plan->mu);
+        for (auto &pr : plan->dev_blob)
+            if (pr.first == dev) blob = pr.second;
+        if (!blob) {
+            e = hipMalloc(&blob, L.total);
+            if (e != hipSuccess) return hip_error(e, "hipMalloc(plan tables)");
+            std::vector<uint8_t> host(L.total, 0);
+            std::memcpy(host.data() + L.seg, plan->seg.data(), sizeof(SegDev) * plan->seg.size());
+            std::memcpy(host.data() + L.dchunk, plan->dchunk_seg.data(),
+                        sizeof(uint32_t) * plan->dchunk_seg.size());
+            std::memcpy(host.data() + L.achunk, plan->achunk_seg.data(),
+                        sizeof(uint32_t) * plan->achunk_seg.size());
+            std::memcpy(host.data() + L.start, plan->seg_start.data(),
+                        sizeof(uint64_t) * plan->seg_start.size());
+            e = hipMemcpy(blob, host.data(), L.total, hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                (void)hipFree(blob);
+                return hip_error(e, "hipMemcpy(plan tables)");
+            }
+            plan->dev_blob.emplace_back(dev, blob);
+        }
+    }
+    auto *b = static_cast<uint8_t *>(blob);
+    out->seg = reinterpret_cast<const SegDev *>(b + L.seg);
+    out->dchunk_seg = reinterpret_cast<const uint32_t *>(b + L.dchunk);
+    out->achunk_seg = reinterpret_cast<const uint32_t *>(b + L.achunk);
+    out->seg_start = reinterpret_cast<const uint64_t *>(b + L.start);
+    out->nseg = plan->nseg;
+    out->ndchunk = plan->ndchunk;
+    out->nachunk = plan->nachunk;
+    out->n_total = plan->n_total;
+    return GC_OK;
+}
+
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+const char *gc_last_error(void) { return g_last_error.c_str(); }
+
+const char *gc_version(void) { return "libgradcomp 0.1.0 (gfx950)"; }
+
+uint32_t gc_topk_count(uint32_t n) {
+    uint64_t k = (static_cast<uint64_t>(n) + 999) / 1000;
+    return static_cast<uint32_t>(k < 1 ? 1 : k);
+}
+
+gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_plan **out) {
+    clear_error();
+    if (!out) return set_error(GC_EINVAL, "gc_plan_create: out is null");
+    if (nseg < 1) return set_error(GC_EINVAL, "gc_plan_create: nseg must be >= 1");
+    if (!segs) return set_error(GC_EINVAL, "gc_plan_create: segs is null");
+    if (n_total >= (uint64_t(1) << 32))
+        return set_error(GC_ERANGE, "gc_plan_create: n_total must be < 2^32 (u32 indices)");
+    uint64_t prev_end = 0, total_k = 0, total_bins = 0;
+    uint64_t ndchunk = 0, nachunk = 0;
+    for (int s = 0; s < nseg; ++s) {
+        const gc_segment &g = segs[s];
+        std::string at = "gc_plan_create: segment " + std::to_string(s) + ": ";
+        if (g.reserved != 0) return set_error(GC_EINVAL, at + "reserved field must be 0");
+        if (g.length < 1) return set_error(GC_EINVAL, at + "length must be >= 1");
+        if (g.offset < prev_end)
+            return set_error(GC_EINVAL, at + "segments must be ascending and non-overlapping");
+        if (g.offset + g.length > n_total)
+            return set_error(GC_EINVAL, at + "segment extends past n_total");
+        if (g.bin_len < 1) return set_error(GC_EINVAL, at + "bin_len must be >= 1");
+        if (g.bin_len > GC_MAX_BIN_LEN)
+            return set_error(GC_ENOTSUP, at + "bin_len above GC_MAX_BIN_LEN");
+        if (g.k < 1 || g.k > g.length) return set_error(GC_EINVAL, at + "k must be in [1, length]");
+        prev_end = g.offset + g.length;
+        total_k += g.k;
+        total_bins += (g.length + g.bin_len - 1) / g.bin_len;
+        ndchunk += (g.length + kChunk - 1) / kChunk;
+        uint32_t per = (kChunk / g.bin_len) * g.bin_len;  // whole bins per AdaComp chunk
+        nachunk += (g.length + per - 1) / per;
+    }
+    if (ndchunk >= (uint64_t(1) << 31) || nachunk >= (uint64_t(1) << 31))
+        return set_error(GC_ERANGE, "gc_plan_create: too many chunks");
+
+    gc_plan *p = new (std::nothrow) gc_plan;
+    if (!p) return set_error(GC_EINVAL, "gc_plan_create: out of host memory");
+    p->nseg = nseg;
+    p->n_total = n_total;
+    p->total_k = total_k;
+    p->total_bins = total_bins;
+    p->seg.resize(nseg);
+    p->seg_start.resize(nseg);
+    p->dchunk_seg.reserve(ndchunk);
+    p->achunk_seg.reserve(nachunk);
+    uint32_t bin0 = 0, kbase = 0;
+    for (int s = 0; s < nseg; ++s) {
+        const gc_segment &g = segs[s];
+        SegDev d{};
+        d.off = g.offset;
+        d.len = g.length;
+        d.bin_len = g.bin_len;
+        d.k = g.k;
+        d.nbins = (g.length + g.bin_len - 1) / g.bin_len;
+        d.dchunk0 = static_cast<uint32_t>(p->dchunk_seg.size());
+        d.dnchunk = (g.length + kChunk - 1) / kChunk;
+        d.achunk_len = (kChunk / g.bin_len) * g.bin_len;
+        d.achunk0 = static_cast<uint32_t>(p->achunk_seg.size());
+        d.anchunk = (g.length + d.achunk_len - 1) / d.achunk_len;
+        d.bin0 = bin0;
+        d.kbase = kbase;
+        bin0 += d.nbins;
+        kbase += g.k;
+        for (uint32_t c = 0; c < d.dnchunk; ++c) p->dchunk_seg.push_back(static_cast<uint32_t>(s));
+        for (uint32_t c = 0; c < d.anchunk; ++c) p->achunk_seg.push_back(static_cast<uint32_t>(s));
+        p->seg[s] = d;
+        p->seg_start[s] = g.offset;
+    }
+    p->ndchunk = static_cast<uint32_t>(p->dchunk_seg.size());
+    p->nachunk = static_cast<uint32_t>(p->achunk_seg.size());
+    *out = p;
+    return GC_OK;
+}
+
+void gc_plan_destroy(gc_plan *plan) {
+    if (!plan) return;
+    int cur = 0;
+    bool have = hipGetDevice(&cur) == hipSuccess;
+    for (auto &pr : plan->dev_blob) {
+        if (hipSetDevice(pr.first) == hipSuccess) (void)hipFree(pr.second);
+    }
+    if (have) (void)hipSetDevice(cur);
+    delete plan;
+}
+
+int gc_plan_num_segments(const gc_plan *plan) { return plan ? plan->nseg : 0; }
+uint64_t gc_plan_num_elements(const gc_plan *plan) { return plan ? plan->n_total : 0; }
+uint64_t gc_plan_total_k(const gc_plan *plan) { return plan ? plan->total_k : 0; }
+uint64_t gc_plan_total_bins(const gc_plan *plan) { return plan ? plan->total_bins : 0; }
+
+size_t gc_plan_workspace_bytes(const gc_plan *plan, int op) {
+    if (!plan) return 0;
+    switch (op) {
+        case GC_OP_DGC: return dgc_workspace_bytes(plan);
+        case GC_OP_ADACOMP: return adacomp_workspace_bytes(plan);
+        case GC_OP_PACK: return pack_workspace_bytes(plan);
+        case GC_OP_DECODE: return decode_workspace_bytes(plan);
+        default: return 0;
+    }
+}
+
+}  // extern "C"

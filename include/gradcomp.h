@@ -249,8 +249,10 @@ gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_sparse *msgs,
  *   per byte, even index in the low nibble; 8-bit codes one per byte.
  *   x_out_i = fl32(x_i + C_i)  (x_out may equal x: step 2's local update).
  *   scales [ceil(n/bucket)], codes [ceil(n*bits/8)] out.
- * Errors: GC_EINVAL (bits not 4 or 8, bucket 0, null), GC_ENOTSUP
- *         (bucket > 4096 or not a multiple of 2), GC_ERANGE (n >= 2^32).
+ *   codes must be 4-byte aligned.
+ * Errors: GC_EINVAL (bits not 4 or 8, bucket 0, null, misaligned codes),
+ *         GC_ENOTSUP (bucket not a power of two in [4, 4096]),
+ *         GC_ERANGE (n >= 2^32).
  */
 gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
                           uint64_t n, int bits, uint32_t bucket, uint64_t seed,

@@ -1,0 +1,94 @@
+"""Host-only checks of the C ABI: the library loads here (no GPU), exports
+every function the header declares, and validates plans on the host."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gradcomp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    declared = header_functions()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.exported_symbols()) == declared
+
+
+def test_version_and_topk_count():
+    assert "libgradcomp" in B.gc_version()
+    assert B.gc_topk_count(1) == 1
+    assert B.gc_topk_count(1000) == 1
+    assert B.gc_topk_count(1001) == 2
+    assert B.gc_topk_count(1 << 20) == 1049
+
+
+def _create(rows, n_total):
+    lib = B.load()
+    arr = (B.gc_segment * max(len(rows), 1))()
+    for i, r in enumerate(rows):
+        arr[i] = B.gc_segment(*r)
+    h = ctypes.c_void_p()
+    st = lib.gc_plan_create(arr, len(rows), n_total, ctypes.byref(h))
+    if st == 0:
+        lib.gc_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("rows,n_total,code", [
+    ([], 10, B.GC_EINVAL),                                   # no segments
+    ([(0, 0, 1, 1, 0)], 10, B.GC_EINVAL),                    # empty segment
+    ([(0, 5, 1, 1, 0), (4, 5, 1, 1, 0)], 10, B.GC_EINVAL),   # overlap
+    ([(5, 5, 1, 1, 0), (0, 5, 1, 1, 0)], 10, B.GC_EINVAL),   # not ascending
+    ([(0, 11, 1, 1, 0)], 10, B.GC_EINVAL),                   # past n_total
+    ([(0, 5, 0, 1, 0)], 10, B.GC_EINVAL),                    # bin_len 0
+    ([(0, 5, 1, 0, 0)], 10, B.GC_EINVAL),                    # k 0
+    ([(0, 5, 1, 6, 0)], 10, B.GC_EINVAL),                    # k > length
+    ([(0, 5, 1, 1, 7)], 10, B.GC_EINVAL),                    # reserved != 0
+    ([(0, 5, 4097, 1, 0)], 10, B.GC_ENOTSUP),                # bin_len too large
+    ([(0, 5, 1, 1, 0)], 1 << 32, B.GC_ERANGE),               # indices are u32
+    ([(0, 5, 1, 5, 0), (7, 3, 2, 1, 0)], 10, B.GC_OK),       # gap allowed
+])
+def test_plan_validation(rows, n_total, code):
+    assert _create(rows, n_total) == code
+    if code != B.GC_OK:
+        assert B.gc_last_error() != ""
+
+
+def test_plan_queries_and_workspace_on_workloads():
+    for name in ("fc1m", "resnet50", "deepspeech"):
+        w = W.make_config(name)
+        p = B.Plan(w.table, w.n_total)
+        t = w.table
+        assert p.total_k == int(t[:, 3].sum())
+        assert p.total_bins == int(((t[:, 1] + t[:, 2] - 1) // t[:, 2]).sum())
+        for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK, B.GC_OP_DECODE):
+            assert p.workspace_bytes(op) > 0
+        # staging needs 8 bytes per element at most, plus small tables
+        assert p.workspace_bytes(B.GC_OP_DGC) < 9 * w.n_total + (64 << 20)
+        # the pack bound covers the format's closed form at k entries per segment
+        E = t[:, 3]
+        assert p.pack_bound(B.GC_KIND_DGC) >= 16 + int(np.sum(16 + 6 * E + 2 * (E % 2)))
+        del p
+
+
+def test_hot_calls_reject_null_plan_without_touching_a_device():
+    lib = B.load()
+    assert lib.gc_dgc_step(None, None, None, None, 0.9, 0.0, 1, None, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_adacomp_compress(None, None, None, 2.0, None, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_pack(None, 1, None, None, 0, None, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_decompress_accumulate(None, None, 1, None, 1, 0, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_dcd_compress(None, None, None, 10, 4, 512, 0, 0, None, None, None) == B.GC_EINVAL

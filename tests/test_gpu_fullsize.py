@@ -1,0 +1,118 @@
+"""GPU parity at the workloads' full sizes, through the same library calls the
+benchmark times: every output compared with the oracle element by element
+(the oracle finishes these in seconds)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, dcd, same_bits, say, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+
+def check_dgc(hp, t, G, U, V, m, thr, N, tag):
+    say(f"{tag}: oracle")
+    Uo, Vo, idx, val, off, clip = oracle.dgc(t, G, U, V, m, thr, N)
+    say(f"{tag}: hip")
+    Ug, Vg, gidx, gval, goff = hp.dgc(G, U, V, m, thr, N)
+    assert np.array_equal(goff, off), tag
+    assert np.array_equal(gidx, idx), tag
+    assert same_bits(gval, val), ulp_report(gval, val)
+    assert same_bits(Ug, Uo), ulp_report(Ug, Uo)
+    assert same_bits(Vg, Vo), ulp_report(Vg, Vo)
+    return Uo, Vo, (idx, val, off), clip
+
+
+def check_ada(hp, t, dW, R, tag, sf=2.0):
+    say(f"{tag}: oracle")
+    Ro, idx, val, off, scale, _ = oracle.adacomp(t, dW, R, sf)
+    say(f"{tag}: hip")
+    Rg, gidx, gval, goff, gscale = hp.adacomp(dW, R, sf)
+    assert np.array_equal(goff, off), tag
+    assert same_bits(gscale, scale), ulp_report(gscale, scale)
+    assert np.array_equal(gidx, idx), tag
+    assert same_bits(gval, val), ulp_report(gval, val)
+    assert same_bits(Rg, Ro), ulp_report(Rg, Ro)
+    return Ro, (idx, val, off, scale)
+
+
+def test_fc1m_dgc_and_adacomp():
+    w = W.make_config("fc1m")
+    hp = HipPath(w.table, w.n_total)
+    g = W.gradient(w, 0)
+    z = np.zeros(w.n_total, np.float32)
+    check_dgc(hp, w.table, g, z, z, 0.9, 0.0, 1, "fc1m dgc")
+    check_ada(hp, w.table, g, z, "fc1m adacomp")
+
+
+def test_resnet50_dgc_two_steps():
+    w = W.make_config("resnet50")
+    hp = HipPath(w.table, w.n_total)
+    U = np.zeros(w.n_total, np.float32)
+    V = U.copy()
+    for step in range(2):
+        g = W.gradient(w, step)
+        U, V, _, clip = check_dgc(hp, w.table, g, U, V, 0.9, 1.0, 1, f"resnet50 dgc step {step}")
+
+
+def test_lstm_adacomp_two_steps():
+    w = W.make_config("lstm_lm")
+    hp = HipPath(w.table, w.n_total)
+    R = np.zeros(w.n_total, np.float32)
+    for step in range(2):
+        R, _ = check_ada(hp, w.table, W.gradient(w, step), R, f"lstm adacomp step {step}")
+
+
+def test_resnet50x8_learners_and_average():
+    w = W.make_config("resnet50x8")
+    per = w.params["learner_len"]
+    single = W.make_config("resnet50")
+    t = single.table
+    hp = HipPath(t, per)
+    g_all = W.gradient(w, 0)
+    z = np.zeros(per, np.float32)
+    host_msgs, dev_msgs = [], []
+    for j in range(8):
+        g = g_all[j * per:(j + 1) * per]
+        say(f"resnet50x8 learner {j}")
+        Uo, Vo, idx, val, off, _ = oracle.dgc(t, g, z, z, 0.9, 1.0, 8)
+        Ud, Vd, msg = hp.dgc(g, z.copy(), z.copy(), 0.9, 1.0, 8, tensors=True)
+        gidx, gval, goff, _ = msg.host()
+        assert np.array_equal(gidx, idx) and same_bits(gval, val)
+        assert same_bits(Ud.cpu().numpy(), Uo) and same_bits(Vd.cpu().numpy(), Vo)
+        host_msgs.append((idx, val))
+        dev_msgs.append(msg)
+    say("resnet50x8 decode average")
+    want = oracle.decode(t, per, host_msgs, mode=1)
+    got = hp.decode(dev_msgs, B.GC_AVG)
+    assert same_bits(got, want), ulp_report(got, want)
+
+
+def test_deepspeech_dgc_adacomp_pack_dcd():
+    w = W.make_config("deepspeech")
+    t = w.table
+    n = w.n_total
+    hp = HipPath(t, n)
+    g = W.gradient(w, 0)
+    z = np.zeros(n, np.float32)
+    Uo, Vo, (idx, val, off), clip = check_dgc(hp, t, g, z, z, 0.9, 1.0, 1, "deepspeech dgc")
+    assert np.any(clip < 1), "the large GRU input matrices exceed the clip norm"
+    say("deepspeech dgc pack")
+    _, _, msg = hp.dgc(g, z.copy(), z.copy(), 0.9, 1.0, 1, tensors=True)
+    want = oracle.pack(1, t, idx, val, off, np.zeros(len(t), np.float32))
+    assert hp.pack(B.GC_KIND_DGC, msg) == want
+    assert 0.70e6 < len(want) < 0.76e6
+    Ro, (aidx, aval, aoff, ascale) = check_ada(hp, t, g, z, "deepspeech adacomp")
+    say("deepspeech adacomp pack")
+    _, amsg = hp.adacomp(g, z.copy(), tensors=True)
+    assert hp.pack(B.GC_KIND_ADACOMP, amsg) == oracle.pack(2, t, aidx, aval, aoff, ascale)
+    say("deepspeech dcd")
+    x = W.dcd_model(w)
+    xh = W.dcd_half_step(x, g)
+    xo, sc, codes = oracle.dcd(x, xh, 4, 512, 0x5EED, 0)
+    gx, gsc, gcodes, tail = dcd(x, xh, 4, 512, 0x5EED, 0, inplace=True)
+    assert same_bits(gsc, sc) and np.array_equal(gcodes, codes) and same_bits(gx, xo)
+    assert np.all(tail == 0)

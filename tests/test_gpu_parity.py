@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs that span several 4096-element tiles, ragged tails,
+odd segment offsets, gaps, ties, zero blocks and denormals.  Selections,
+counts and bytes must match exactly; fp32 states are compared bit for bit
+(stronger than the 1e-6 relative bar, which the design does not need)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, dcd, same_bits, say, sparse_from_host, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+BIG_LENGTHS = (1, 2, 63, 64, 65, 4095, 4096, 4097, 12289, 50000)
+
+
+def mixed_table(rng, nseg, bin_lens=(1, 7, 50, 64, 500, 4096), per_mille=(1, 10, 100, 1000),
+                big=True):
+    lengths, bls, ks, gaps = [], [], [], []
+    for i in range(nseg):
+        if big and i == 0:
+            n = int(rng.integers(100_000, 300_000))
+        elif rng.random() < 0.4:
+            n = int(rng.choice(BIG_LENGTHS))
+        else:
+            n = int(rng.integers(1, 20000))
+        lengths.append(n)
+        bls.append(int(rng.choice(bin_lens)))
+        ks.append(min(n, W.topk_count(n, int(rng.choice(per_mille)))))
+        gaps.append(int(rng.integers(0, 7)))
+    order = rng.permutation(nseg)
+    return W.make_table([lengths[i] for i in order], [bls[i] for i in order],
+                        [ks[i] for i in order], [gaps[i] for i in order])
+
+
+# ---------------------------------------------------------------------- DGC
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
+def test_dgc_parity_multistep(seed, kind):
+    rng = np.random.default_rng(100 + seed)
+    t = mixed_table(rng, int(rng.integers(1, 14)))
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    U = W.random_values(rng, n, kind)
+    V = W.random_values(rng, n, kind)
+    Ug, Vg = U.copy(), V.copy()
+    clip_cfg = [(0.0, 1), (1e-3 if kind != "denormal" else 1e-41, 1 + seed % 4), (1.0, 8)][seed % 3]
+    for step in range(3):
+        G = W.random_values(rng, n, kind)
+        say(f"dgc seed={seed} kind={kind} nseg={len(t)} n={n} step={step} clip={clip_cfg}")
+        U, V, idx, val, off, _ = oracle.dgc(t, G, U, V, 0.9, clip_cfg[0], clip_cfg[1])
+        Ug, Vg, gidx, gval, goff = hp.dgc(G, Ug, Vg, 0.9, clip_cfg[0], clip_cfg[1])
+        assert np.array_equal(goff, off), "segment offsets"
+        assert np.array_equal(gidx, idx), "selected indices"
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Ug, U), ulp_report(Ug, U)
+        assert same_bits(Vg, V), ulp_report(Vg, V)
+
+
+@pytest.mark.parametrize("kind", ["const", "ties", "zeros"])
+def test_dgc_all_ties_and_k_equals_n(kind):
+    rng = np.random.default_rng(7)
+    lengths = [4097, 9000, 1, 64, 20000]
+    t = W.make_table(lengths, [1] * 5, [4097, 4500, 1, 63, 19999])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    G = W.random_values(rng, n, kind)
+    z = np.zeros(n, np.float32)
+    say(f"dgc ties kind={kind}")
+    U, V, idx, val, off, _ = oracle.dgc(t, G, z, z, 0.5, 0.0, 1)
+    Ug, Vg, gidx, gval, goff = hp.dgc(G, z.copy(), z.copy(), 0.5, 0.0, 1)
+    assert np.array_equal(gidx, idx) and np.array_equal(goff, off)
+    assert same_bits(gval, val) and same_bits(Ug, U) and same_bits(Vg, V)
+
+
+def test_dgc_clip_active_and_deterministic():
+    rng = np.random.default_rng(55)
+    t = mixed_table(rng, 8)
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    G = (W.random_values(rng, n, "normal") * np.float32(1000)).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    say("dgc clip active")
+    U, V, idx, val, off, clip = oracle.dgc(t, G, z, z, 0.9, 0.5, 3)
+    assert np.all(clip < 1)
+    runs = [hp.dgc(G, z.copy(), z.copy(), 0.9, 0.5, 3) for _ in range(2)]
+    for Ug, Vg, gidx, gval, goff in runs:
+        assert np.array_equal(gidx, idx)
+        assert same_bits(gval, val) and same_bits(Ug, U) and same_bits(Vg, V)
+
+
+# ------------------------------------------------------------------ AdaComp
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
+def test_adacomp_parity_multistep(seed, kind):
+    rng = np.random.default_rng(200 + seed)
+    t = mixed_table(rng, int(rng.integers(1, 14)))
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    R = W.random_values(rng, n, kind)
+    Rg = R.copy()
+    sf = [2.0, 1.0, 3.5][seed % 3]
+    for step in range(3):
+        dW = W.random_values(rng, n, kind)
+        say(f"adacomp seed={seed} kind={kind} nseg={len(t)} n={n} step={step} sf={sf}")
+        R, idx, val, off, scale, _ = oracle.adacomp(t, dW, R, sf)
+        Rg, gidx, gval, goff, gscale = hp.adacomp(dW, Rg, sf)
+        assert np.array_equal(goff, off), "segment offsets"
+        assert same_bits(gscale, scale), ulp_report(gscale, scale)
+        assert np.array_equal(gidx, idx), "selected indices"
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Rg, R), ulp_report(Rg, R)
+
+
+def test_adacomp_constant_and_single_bin():
+    t = W.make_table([5000, 300, 8192], [50, 4096, 1], [1, 1, 1])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    dW = np.full(n, -0.125, np.float32)
+    z = np.zeros(n, np.float32)
+    say("adacomp constant")
+    R, idx, val, off, scale, _ = oracle.adacomp(t, dW, z)
+    Rg, gidx, gval, goff, gscale = hp.adacomp(dW, z.copy())
+    assert np.array_equal(gidx, idx) and same_bits(Rg, R) and same_bits(gscale, scale)
+    assert gidx.size == n and np.all(Rg == 0)
+
+
+# --------------------------------------------------------------------- pack
+@pytest.mark.parametrize("kind", [B.GC_KIND_DGC, B.GC_KIND_ADACOMP])
+@pytest.mark.parametrize("seed", range(3))
+def test_pack_bytes_match_oracle(kind, seed):
+    rng = np.random.default_rng(300 + seed)
+    lengths = [200_000, 70_000, 1, 5, 33_000, 4096, 131_071]
+    t = W.make_table(lengths, [50, 500, 1, 7, 64, 4096, 50],
+                     [max(1, n // 1000) for n in lengths], [0, 3, 0, 1, 2, 0, 5])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    g = W.random_values(rng, n)
+    g[rng.random(n) < (0.9995 if kind == B.GC_KIND_ADACOMP else 0.0)] = 0.0
+    z = np.zeros(n, np.float32)
+    say(f"pack kind={kind} seed={seed}")
+    if kind == B.GC_KIND_DGC:
+        _, _, msg = hp.dgc(g, z.copy(), z.copy(), 0.9, 0.0, 1, tensors=True)
+        _, _, idx, val, off, _ = oracle.dgc(t, g, z, z, 0.9, 0.0, 1)
+        sc = np.zeros(len(t), np.float32)
+    else:
+        _, msg = hp.adacomp(g, z.copy(), tensors=True)
+        _, idx, val, off, sc, _ = oracle.adacomp(t, g, z)
+    got = hp.pack(kind, msg)
+    want = oracle.pack(kind, t, idx, val, off, sc)
+    assert len(got) == len(want)
+    assert got == want
+
+
+def test_pack_escapes_and_empty_segments():
+    # hand-placed entries: long gaps (escapes), an empty AdaComp segment
+    t = W.make_table([300_000, 10, 70_000], [50, 1, 500], [3, 1, 1])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    for kind in (B.GC_KIND_DGC, B.GC_KIND_ADACOMP):
+        if kind == B.GC_KIND_DGC:
+            idx = np.array([0, 65535 * 2 + 7, 299_999, 300_004, 300_010 + 69_999], np.uint32)
+            off = np.array([0, 3, 4, 5], np.uint32)
+        else:
+            idx = np.array([32767, 32767 * 3 + 1, 299_000, 300_010 + 40_000], np.uint32)
+            off = np.array([0, 3, 3, 4], np.uint32)
+        val = np.array([0.5, -1.0, 2.0, -0.25, 1.5][:len(idx)], np.float32)
+        sc = np.array([0.5, 0.0, 0.25], np.float32)
+        if kind == B.GC_KIND_ADACOMP:
+            val = np.where(val < 0, -1, 1).astype(np.float32) * sc[[0, 0, 0, 2]]
+        say(f"pack escapes kind={kind}")
+        msg = sparse_from_host(hp.plan, idx, val, off, sc)
+        assert hp.pack(kind, msg) == oracle.pack(kind, t, idx, val, off, sc)
+
+
+# ------------------------------------------------------------------- decode
+@pytest.mark.parametrize("K", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("mode", [B.GC_SUM, B.GC_AVG])
+def test_decode_parity(K, mode):
+    rng = np.random.default_rng(400 + K)
+    t = mixed_table(rng, 6, big=True)
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    msgs, host = [], []
+    for k in range(K):
+        parts, offs, pos = [], [0], 0
+        for o, ln, _, _ in t:
+            m = int(rng.integers(0, min(ln, 3000) + 1))
+            sel = np.sort(rng.choice(ln, m, replace=False)) + o
+            parts.append(sel)
+            pos += m
+            offs.append(pos)
+        idx = np.concatenate(parts).astype(np.uint32)
+        val = W.random_values(rng, idx.size, "laplace")
+        host.append((idx, val))
+        msgs.append(sparse_from_host(hp.plan, idx, val, offs))
+    dense0 = W.random_values(rng, n)
+    for acc in (False, True):
+        say(f"decode K={K} mode={mode} acc={acc}")
+        want = oracle.decode(t, n, host, mode=mode, dense=dense0 if acc else None)
+        got = hp.decode(msgs, mode, dense0 if acc else None)
+        if not acc:
+            # gaps between segments are not touched: zero in both
+            pass
+        assert same_bits(got, want), ulp_report(got, want)
+
+
+# ---------------------------------------------------------------------- DCD
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 511, 512, 513, 4096, 4097, 100_003])
+@pytest.mark.parametrize("bits_", [4, 8])
+@pytest.mark.parametrize("bucket", [4, 64, 512, 4096])
+def test_dcd_parity(n, bits_, bucket):
+    rng = np.random.default_rng(n * 7 + bits_ + bucket)
+    x = rng.normal(0, 0.05, n).astype(np.float32)
+    g = rng.normal(0, 1e-3, n).astype(np.float32)
+    if n > 1024:
+        g[512:1024] = 0.0
+    xh = W.dcd_half_step(x, g)
+    seed, step = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40))
+    say(f"dcd n={n} bits={bits_} bucket={bucket}")
+    xo, sc, codes = oracle.dcd(x, xh, bits_, bucket, seed, step)
+    for offset, inplace in ((0, False), (1, False), (0, True), (3, True)):
+        gx, gsc, gcodes, tail = dcd(x, xh, bits_, bucket, seed, step, offset, inplace)
+        assert same_bits(gsc, sc), ulp_report(gsc, sc)
+        assert np.array_equal(gcodes, codes)
+        assert same_bits(gx, xo), ulp_report(gx, xo)
+        assert np.all(tail == 0), "wrote past the codes buffer"
+
+
+# ------------------------------------------------------------------- errors
+def test_hot_call_errors_leave_buffers_untouched():
+    t = W.make_table([5000, 300], [50, 50], [5, 1])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    rng = np.random.default_rng(1)
+    G = torch.from_numpy(W.random_values(rng, n)).cuda()
+    U = torch.from_numpy(W.random_values(rng, n)).cuda()
+    V = U.clone()
+    U0, V0 = U.clone(), V.clone()
+    small = B.Sparse.empty(hp.plan, hp.plan.total_k - 1, "cuda")
+    with pytest.raises(B.GCError) as e:
+        B.gc_dgc_step(hp.plan, G, U, V, 0.9, 0.0, 1, small, hp.workspace(B.GC_OP_DGC))
+    assert e.value.status == B.GC_ECAPACITY
+    ok = B.Sparse.empty(hp.plan, hp.plan.total_k, "cuda")
+    tiny_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.GCError) as e:
+        B.gc_dgc_step(hp.plan, G, U, V, 0.9, 0.0, 1, ok, tiny_ws)
+    assert e.value.status == B.GC_ECAPACITY
+    with pytest.raises(B.GCError) as e:
+        B.gc_dgc_step(hp.plan, G, U, V, 1.5, 0.0, 1, ok, hp.workspace(B.GC_OP_DGC))
+    assert e.value.status == B.GC_EINVAL
+    with pytest.raises(B.GCError) as e:
+        B.gc_adacomp_compress(hp.plan, G, U, 0.5, B.Sparse.empty(hp.plan, n, "cuda"),
+                              hp.workspace(B.GC_OP_ADACOMP))
+    assert e.value.status == B.GC_EINVAL
+    with pytest.raises(B.GCError) as e:
+        B.gc_decompress_accumulate(hp.plan, [ok] * 65, V, B.GC_AVG, False,
+                                   hp.workspace(B.GC_OP_DECODE))
+    assert e.value.status == B.GC_EINVAL
+    x = torch.zeros(100, device="cuda")
+    with pytest.raises(B.GCError) as e:
+        B.gc_dcd_compress(x, x.clone(), x, 4, 500, 0, 0, torch.zeros(1, device="cuda"),
+                          torch.zeros(64, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == B.GC_ENOTSUP
+    torch.cuda.synchronize()
+    assert torch.equal(U, U0) and torch.equal(V, V0)
