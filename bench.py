@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the gradient-compression hot path on one MI355X.
+
+A step is one pass of the whole path over one DeepSpeech-scale fp32 gradient
+(121,893,373 elements in 68 tensors, inputs resident in HBM):
+  DGC step (clip at 1.0, momentum 0.9, exact top 0.1%, masking) + pack,
+  AdaComp step (L_T = 500, factor 2) + pack,
+  decompress-average of each message,
+  DCD 4-bit random quantization of the model difference (buckets of 512).
+value = fp32 gradient bytes compressed per second (two compressions of
+4 * n bytes per step).  One JSON line is printed.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+# Algorithmic bytes per launch of each kernel at this workload: what the
+# method itself must move (reads + writes of dense data, plus message bytes
+# where the kernel's job is the message).
+def algorithmic_bytes(n: int, nbins: int, k_total: int, ada_entries: int, bucket: int = 512):
+    return {
+        "dgc_update": 20 * n,                 # read G, U, V; write U, V
+        "dgc_norm": 4 * n,                    # read G
+        "dgc_stage": 4 * n,                   # read V
+        "ada_max": 8 * n,                     # read R, dW
+        "ada_apply": 12 * n + 8 * ada_entries,  # read R, dW; write R; message
+        "dcd": 12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket),  # x, x_half, x_out, codes, scales
+        "decode": 4 * n,                      # dense write (K=1)
+        "dgc_emit": 8 * k_total + 8 * k_total,  # message out + masking writes
+    }
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources, to tie stored counter readings to a build."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gradient_compression_dnn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the counters were taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_deepspeech.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != digest:
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 4):
+    """The oracle, as it stands, over a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from gradient_compression_dnn_amd import workloads as W
+
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_num_threads(threads)
+    names = [nm for nm, _ in W.deepspeech_shapes()]
+    sel = [i for i, nm in enumerate(names) if nm.split(".")[0] in ("gru1", "gru2", "gru3", "gru4")]
+    sub = w.table[sel].copy()
+    lo, hi = int(sub[0, 0]), int(sub[-1, 0] + sub[-1, 1])
+    sub[:, 0] -= lo
+    n = hi - lo
+    U = np.zeros(n, np.float32)
+    V = np.zeros(n, np.float32)
+    R = np.zeros(n, np.float32)
+    x = x0[lo:hi].copy()
+    done, t_total = 0, 0.0
+    while done < max_steps and (t_total < steps_min_s or done == 0):
+        g = grads[done % len(grads)][lo:hi]
+        xh = W.dcd_half_step(x, g)
+        t0 = time.perf_counter()
+        U, V, idx, val, off, _ = oracle.dgc(sub, g, U, V, 0.9, 1.0, 1)
+        oracle.pack(1, sub, idx, val, off)
+        R, ai, av, ao, asc, _ = oracle.adacomp(sub, g, R, 2.0)
+        oracle.pack(2, sub, ai, av, ao, asc)
+        oracle.decode(sub, n, [(idx, val)], mode=1)
+        oracle.decode(sub, n, [(ai, av)], mode=1)
+        oracle.dcd(x, xh, 4, 512, 0x5EED, done)
+        t_total += time.perf_counter() - t0
+        done += 1
+    gbs = 2 * 4 * n * done / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} full step(s) (DGC+pack, AdaComp+pack, 2 decodes, DCD) over the "
+                      f"32 GRU tensors of layers 1-4 ({n:,} of {w.n_total:,} elements), "
+                      f"{t_total:.1f} s on {threads} host threads"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--grads", type=int, default=2, help="distinct seeded gradients cycled over steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (for counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU: the compression step is per learner and needs no "
+              f"collective here; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from gradient_compression_dnn_amd import binding as B
+    from gradient_compression_dnn_amd import workloads as W
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    w = W.make_config("deepspeech")
+    n = w.n_total
+    plan = B.Plan(w.table, n)
+    log(f"workload deepspeech: {w.nseg} tensors, {n:,} elements; generating {args.grads} gradients")
+    grads = [W.gradient(w, t) for t in range(args.grads)]
+    x0 = W.dcd_model(w)
+
+    G = [torch.from_numpy(g).to(dev) for g in grads]
+    X = torch.from_numpy(x0).to(dev)
+    XH = [X - 0.1 * g for g in G]  # synthetic x_{t+1/2}, prepared outside the timed region
+    U = torch.zeros(n, dtype=torch.float32, device=dev)
+    V = torch.zeros_like(U)
+    R = torch.zeros_like(U)
+    XO = torch.zeros_like(U)
+    dmsg = B.Sparse.empty(plan, plan.total_k, dev)
+    amsg = B.Sparse.empty(plan, n, dev)
+    dbuf = torch.zeros(plan.pack_bound(B.GC_KIND_DGC), dtype=torch.uint8, device=dev)
+    abuf = torch.zeros(plan.pack_bound(B.GC_KIND_ADACOMP), dtype=torch.uint8, device=dev)
+    dn = torch.zeros(1, dtype=torch.int64, device=dev)
+    an = torch.zeros(1, dtype=torch.int64, device=dev)
+    ddense = torch.zeros_like(U)
+    adense = torch.zeros_like(U)
+    bucket = 512
+    scales = torch.zeros((n + bucket - 1) // bucket, dtype=torch.float32, device=dev)
+    codes = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=dev)
+    ws = {op: plan.workspace(op, dev) for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK,
+                                                 B.GC_OP_DECODE)}
+
+    def step(t):
+        g = G[t % len(G)]
+        B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC])
+        B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK])
+        B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP])
+        B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK])
+        B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE])
+        B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE])
+        B.gc_dcd_compress(X, XH[t % len(XH)], XO, 4, bucket, 0x5EED, t, scales, codes)
+
+    # warm-up, then one instrumented step to find the dominant kernel
+    log(f"warmup {args.warmup} step(s)")
+    for t in range(args.warmup):
+        step(t)
+    B.gc_timing_enable("*")
+    step(args.warmup)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for kname in B.KERNELS:
+        ms, cnt = B.gc_timing_take(kname)
+        if cnt:
+            per_kernel[kname] = (ms, cnt)
+    dominant = max(per_kernel, key=lambda k: per_kernel[k][0])
+    log("kernel times (ms/step): " + ", ".join(
+        f"{k} {v[0]:.3f}" for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1][0])))
+
+    # timed region: only the dominant kernel is bracketed by events
+    B.gc_timing_enable(dominant)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} step(s)")
+    t_start.record()
+    for t in range(args.steps):
+        step(args.warmup + 1 + t)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    dom_ms, dom_cnt = B.gc_timing_take(dominant)
+    B.gc_timing_enable(None)
+    ms_per_step = total_ms / args.steps
+
+    # a per-kernel breakdown from one more instrumented step (not the timed one)
+    B.gc_timing_enable("*")
+    step(args.warmup + 1 + args.steps)
+    torch.cuda.synchronize()
+    breakdown = {}
+    for kname in B.KERNELS:
+        ms, cnt = B.gc_timing_take(kname)
+        if cnt:
+            breakdown[kname] = round(ms * 1000.0, 2)  # microseconds in one step
+    B.gc_timing_enable(None)
+
+    if args.copy_calibration:
+        a = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ada_entries = amsg.count()
+    nbins = plan.total_bins
+    alg = algorithmic_bytes(n, nbins, plan.total_k, ada_entries, bucket)
+    dom_avg_s = dom_ms / dom_cnt / 1000.0
+    digest = source_digest()
+    roof = None
+    if dominant in alg:
+        ach = alg[dominant] / dom_avg_s / 1e9
+        traffic = stored_traffic(dominant, digest)
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dominant, "avg_us": round(dom_avg_s * 1e6, 2), "launches": dom_cnt,
+                "algorithmic_bytes_per_launch": alg[dominant]}
+    kernel_frac = {}
+    for k, us in breakdown.items():
+        if k in alg and us > 0:
+            kernel_frac[k] = round(alg[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+
+    value = 2 * 4 * n / (ms_per_step / 1000.0) / 1e9
+    # the method's own bytes for the whole step: DGC 20 B/elt, AdaComp 12, DCD 12.5 + scales,
+    # two dense decodes 4 each, plus the messages read and written
+    step_bytes = (alg["dgc_update"] + 12 * n + alg["dcd"] + 2 * alg["decode"]
+                  + alg["dgc_emit"] + 8 * ada_entries + int(dn.item()) + int(an.item()))
+    result = {
+        "metric": "GB/s of fp32 gradient compressed per step (+% HBM peak), DGC & AdaComp",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "deepspeech: 121,893,373 fp32 gradient elements in 68 tensors "
+                               "(5 conv + 7 bidirectional GRU, hidden 800 + FC), log-normal "
+                               "per-tensor scales",
+                   "step": "DGC(m=0.9, clip 1.0, top 0.1%, masking)+pack, AdaComp(L_T=500, x2)+pack, "
+                           "2x decompress-average (K=1), DCD 4-bit bucket 512",
+                   "parallelism": "single GPU (one learner)"},
+        "step_alg_bytes": step_bytes,
+        "step_alg_hbm_frac": round(step_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "kernel_us_per_step": breakdown,
+        "kernel_alg_hbm_frac": kernel_frac,
+        "messages": {"dgc_entries": plan.total_k, "adacomp_entries": ada_entries,
+                     "dgc_packed_bytes": int(dn.item()), "adacomp_packed_bytes": int(an.item())},
+        "source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, grads, x0)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -65,7 +65,33 @@ _SIGS = {
                                                 _P, ctypes.c_size_t, _P]),
     "gc_dcd_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
+    "gc_timing_enable": (ctypes.c_int, [ctypes.c_char_p]),
+    "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
 }
+
+KERNELS = ("dgc_norm", "dgc_prep", "dgc_update", "dgc_select", "dgc_stage", "dgc_refine",
+           "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
+           "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd")
+
+
+def gc_timing_enable(kernels) -> None:
+    """Bracket launches of the named kernels with HIP events ("*" = all,
+    None or "" = off)."""
+    if kernels is None:
+        arg = None
+    elif isinstance(kernels, str):
+        arg = kernels.encode()
+    else:
+        arg = ",".join(kernels).encode()
+    _check(load().gc_timing_enable(arg))
+
+
+def gc_timing_take(kernel: str):
+    """(total milliseconds, launches) recorded for a kernel since the last take."""
+    ms = ctypes.c_double()
+    n = ctypes.c_uint64()
+    _check(load().gc_timing_take(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def load():

@@ -3,17 +3,21 @@
 // "AdaComp: Adaptive Residual Gradient Compression for Data-Parallel
 // Distributed Training" (Chen et al.), "Proposed method" and Abstract.
 //
-// Launch sequence:
-//   zero    tickets and per-segment totals
-//   pass    one workgroup per chunk of whole bins: G = R + dW, bin maxima by a
-//           segmented wave reduction and LDS max, selection, R <- G for every
-//           element, selected (idx, G) staged in index order at the chunk's
-//           own offset, bin maxima written out
-//   scale   one workgroup per segment: pairwise fp64 sum of its bin maxima ->
-//           layer scale; chunk prefix sums; the last segment scans the
-//           segment totals into the message's seg_off
-//   emit    selected entries: q = copysign(scale, G), R <- fl(G - q), message
-//           (idx, q) in index order
+// Launch sequence (the layer scale needs every bin of the layer, so the
+// residual is finished in a second pass instead of being patched in place;
+// both passes stream whole 16-byte-aligned lines):
+//   max     one workgroup per chunk of whole bins: G = R + dW, bin maxima by
+//           in-lane runs and LDS max, count of selected entries (selection
+//           needs only the bin's max); reads R and dW, writes nothing dense
+//   binsum  one workgroup per aligned group of 4096 bins: its node of the
+//           layer's pairwise fp64 tree over the bin maxima
+//   scale   one workgroup per segment: the rest of the tree -> layer scale;
+//           prefix sums of the chunk counts
+//   offsets one workgroup: segment totals -> the message's seg_off
+//   apply   one workgroup per chunk, last chunk first (its inputs were read
+//           last and may still sit in the Infinity Cache): G again, selection
+//           against the stored bin maxima, R <- G - copysign(scale, G) or G,
+//           message (idx, +-scale) in index order at its final slot
 #include <cmath>
 
 #include "gc_internal.hpp"
@@ -23,27 +27,20 @@ namespace gc {
 namespace {
 
 struct AdaWs {
-    uint32_t *zeroed;
-    size_t zero_words;
-    uint32_t *ticket, *seg_total;
+    uint32_t *seg_total;
     float *gmax;
+    double *bpartial;
     uint32_t *ccount, *cpre;
-    uint32_t *sidx;
-    float *sval;
 };
 
 AdaWs ada_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
     AdaWs w{};
-    w.zero_words = 64 + size_t(p->nseg);
-    w.zeroed = c.take<uint32_t>(w.zero_words);
-    w.ticket = w.zeroed;
-    w.seg_total = w.zeroed + 64;
+    w.seg_total = c.take<uint32_t>(p->nseg);
     w.gmax = c.take<float>(p->total_bins);
+    w.bpartial = c.take<double>(p->nbgroup);
     w.ccount = c.take<uint32_t>(p->nachunk);
     w.cpre = c.take<uint32_t>(p->nachunk);
-    w.sidx = c.take<uint32_t>(p->n_total);
-    w.sval = c.take<float>(p->n_total);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -77,9 +74,28 @@ __device__ __forceinline__ uint32_t div_small(uint32_t e, uint32_t L, float invL
     return q;
 }
 
-__global__ __launch_bounds__(kBlock) void ada_pass_kernel(PlanDev P, const float *__restrict__ dW,
-                                                          float *__restrict__ R, float sf,
-                                                          AdaWs w) {
+// G = R + dW for the chunk in the 4-wide layout, with each element's bin.
+__device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const float *dW, float invL,
+                                        float (&g)[kRows][4], uint32_t (&bin)[kRows][4]) {
+    const float *rp = R + a.lo;
+    const float *dp = dW + a.lo;
+    const bool vec = is_aligned16(rp) && is_aligned16(dp);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        float r[4], d[4];
+        load4(rp, row_elem(j), a.cnt, vec, r);
+        load4(dp, row_elem(j), a.cnt, vec, d);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g[j][q] = r[q] + d[q];
+            bin[j][q] = div_small(row_elem(j) + q, a.seg.bin_len, invL);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float *__restrict__ dW,
+                                                         const float *__restrict__ R, float sf,
+                                                         AdaWs w) {
     const uint32_t c = blockIdx.x;
     const AChunk a = achunk_info(P, c);
     const uint32_t L = a.seg.bin_len;
@@ -87,69 +103,91 @@ __global__ __launch_bounds__(kBlock) void ada_pass_kernel(PlanDev P, const float
     const uint32_t nb = (a.cnt + L - 1) / L;
     __shared__ uint32_t gm[kChunk];
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = 0u;
-    float g[kEPT];
-    uint32_t bin[kEPT];
+    float g[kRows][4];
+    uint32_t bin[kRows][4];
+    chunk_G(a, R, dW, invL, g, bin);
+    __syncthreads();
+    // bin maxima of |G| (as bit patterns, which order like the values)
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        float r = 0.0f, d = 0.0f;
-        if (e < a.cnt) {
-            r = R[a.lo + e];
-            d = dW[a.lo + e];
+    for (int j = 0; j < kRows; ++j) {
+        const uint32_t e0 = row_elem(j);
+        uint32_t mag[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mag[q] = e0 + q < a.cnt ? (dev_f2u(g[j][q]) & 0x7FFFFFFFu) : 0u;
+        const uint32_t b_first = __shfl(bin[j][0], 0, kWave);
+        const uint32_t b_last = __shfl(bin[j][3], kWave - 1, kWave);
+        const uint32_t row0 = e0 - 4u * lane_id();
+        if (b_first == b_last) {
+            // the wave's 256 elements of this row share one bin
+            uint32_t m = max(max(mag[0], mag[1]), max(mag[2], mag[3]));
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, d, kWave)));
+            if (lane_id() == 0 && row0 < a.cnt) atomicMax(&gm[b_first], m);
+        } else {
+            // runs of equal bins inside the lane, one LDS max per run
+            uint32_t cur = bin[j][0], mv = mag[0];
+            bool live = e0 < a.cnt;
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                if (bin[j][q] == cur) {
+                    mv = max(mv, mag[q]);
+                } else {
+                    if (live) atomicMax(&gm[cur], mv);
+                    cur = bin[j][q];
+                    mv = mag[q];
+                    live = e0 + q < a.cnt;
+                }
+            }
+            if (live) atomicMax(&gm[cur], mv);
         }
-        g[j] = r + d;
-        bin[j] = div_small(e, L, invL);
     }
     __syncthreads();
-    const int lane = lane_id();
+    uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        uint32_t row0 = e - lane;  // element of lane 0 in this wave row
-        uint32_t v = e < a.cnt ? (dev_f2u(g[j]) & 0x7FFFFFFFu) : 0u;
-        // last lane of this wave row that lies in the same bin
-        uint32_t bin_last = (bin[j] + 1) * L - 1;
-        uint32_t run_last = bin_last - row0 < uint32_t(kWave) ? bin_last - row0 : uint32_t(kWave - 1);
+    for (int j = 0; j < kRows; ++j) {
+        const uint32_t e0 = row_elem(j);
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            uint32_t o = __shfl_down(v, d, kWave);
-            if (uint32_t(lane + d) <= run_last) v = v > o ? v : o;
-        }
-        bool head = lane == 0 || e == bin[j] * L;
-        if (head && e < a.cnt) atomicMax(&gm[bin[j]], v);
-    }
-    __syncthreads();
-    bool flag[kEPT];
-    uint32_t pos[kEPT];
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        float gmx = dev_u2f(gm[bin[j] < nb ? bin[j] : 0]);
-        float t = sf * fabsf(g[j]);
-        flag[j] = e < a.cnt && gmx > 0.0f && t >= gmx;
-        if (e < a.cnt) R[a.lo + e] = g[j];
-    }
-    uint32_t total = block_compact<kEPT>(flag, pos);
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        if (flag[j]) {
-            uint32_t e = j * kBlock + threadIdx.x;
-            w.sidx[a.lo + pos[j]] = static_cast<uint32_t>(a.lo + e);
-            w.sval[a.lo + pos[j]] = g[j];
+        for (int q = 0; q < 4; ++q) {
+            const bool in = e0 + q < a.cnt;
+            const float gmx = dev_u2f(gm[in ? bin[j][q] : 0u]);
+            const float t = sf * fabsf(g[j][q]);
+            mine += (in && gmx > 0.0f && t >= gmx) ? 1u : 0u;
         }
     }
+    uint32_t total;
+    (void)block_exclusive_scan(mine, &total);
     float *gout = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gout[b] = dev_u2f(gm[b]);
     if (threadIdx.x == 0) w.ccount[c] = total;
 }
 
+// Level 1 of the layer scale's pairwise sum: one workgroup per aligned group
+// of 4096 bins of a segment (a node of the segment's tree); thread t holds
+// the 16-leaf subtree of bins [16 t, 16 t + 16) of the group.
+__global__ __launch_bounds__(kBlock) void ada_binsum_kernel(PlanDev P, AdaWs w) {
+    const uint32_t grp = blockIdx.x;
+    const uint32_t s = P.bgroup_seg[grp];
+    const SegDev seg = P.seg[s];
+    const uint32_t b0 = (grp - seg.bgroup0) * kBinGroup + threadIdx.x * (kBinGroup / kBlock);
+    const float *gm = w.gmax + seg.bin0;
+    double a[kBinGroup / kBlock];
+#pragma unroll
+    for (uint32_t i = 0; i < kBinGroup / kBlock; ++i)
+        a[i] = b0 + i < seg.nbins ? static_cast<double>(gm[b0 + i]) : 0.0;
+#pragma unroll
+    for (uint32_t h = 1; h < kBinGroup / kBlock; h <<= 1)
+#pragma unroll
+        for (uint32_t i = 0; i < kBinGroup / kBlock; i += 2 * h) a[i] = a[i] + a[i + h];
+    const double sum = block_tree_sum(a[0]);
+    if (threadIdx.x == 0) w.bpartial[grp] = sum;
+}
+
 __global__ __launch_bounds__(kBlock) void ada_scale_kernel(PlanDev P, AdaWs w,
-                                                           uint32_t *__restrict__ seg_off,
                                                            float *__restrict__ seg_scale) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
-    const float *gm = w.gmax + seg.bin0;
-    double S = block_pairwise_sum(seg.nbins, [&](uint64_t b) { return static_cast<double>(gm[b]); });
+    const double *part = w.bpartial + seg.bgroup0;
+    double S = block_pairwise_sum(seg.nbgroup, [&](uint64_t i) { return part[i]; });
     if (threadIdx.x == 0) seg_scale[s] = static_cast<float>(S / static_cast<double>(seg.nbins));
     uint32_t before = 0;
     for (uint32_t r = 0; r < seg.anchunk; r += kBlock) {
@@ -162,38 +200,72 @@ __global__ __launch_bounds__(kBlock) void ada_scale_kernel(PlanDev P, AdaWs w,
         before += tot;
     }
     if (threadIdx.x == 0) w.seg_total[s] = before;
-    if (block_arrive_last(&w.ticket[0], static_cast<uint32_t>(P.nseg))) {
-        uint32_t run = 0;
-        for (int r = 0; r < P.nseg; r += kBlock) {
-            bool in = r + int(threadIdx.x) < P.nseg;
-            uint32_t v = in ? load_coherent(w.seg_total + r + threadIdx.x) : 0u;
-            uint32_t tot;
-            uint32_t pre = block_exclusive_scan(v, &tot);
-            if (in) seg_off[r + threadIdx.x] = run + pre;
-            run += tot;
-        }
-        if (threadIdx.x == 0) seg_off[P.nseg] = run;
-    }
 }
 
-__global__ __launch_bounds__(kBlock) void ada_emit_kernel(PlanDev P, float *__restrict__ R, AdaWs w,
-                                                          const uint32_t *__restrict__ seg_off,
-                                                          const float *__restrict__ seg_scale,
-                                                          uint32_t *__restrict__ out_idx,
-                                                          float *__restrict__ out_val) {
-    const uint32_t c = blockIdx.x;
+__global__ __launch_bounds__(kBlock) void ada_offsets_kernel(int nseg, AdaWs w,
+                                                             uint32_t *__restrict__ seg_off) {
+    uint32_t run = 0;
+    for (int r = 0; r < nseg; r += kBlock) {
+        bool in = r + int(threadIdx.x) < nseg;
+        uint32_t v = in ? w.seg_total[r + threadIdx.x] : 0u;
+        uint32_t tot;
+        uint32_t pre = block_exclusive_scan(v, &tot);
+        if (in) seg_off[r + threadIdx.x] = run + pre;
+        run += tot;
+    }
+    if (threadIdx.x == 0) seg_off[nseg] = run;
+}
+
+__global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const float *__restrict__ dW,
+                                                           float *__restrict__ R, float sf, AdaWs w,
+                                                           const uint32_t *__restrict__ seg_off,
+                                                           const float *__restrict__ seg_scale,
+                                                           uint32_t *__restrict__ out_idx,
+                                                           float *__restrict__ out_val) {
+    const uint32_t c = P.nachunk - 1 - blockIdx.x;
     const AChunk a = achunk_info(P, c);
-    const uint32_t n = w.ccount[c];
-    if (n == 0) return;
+    const uint32_t L = a.seg.bin_len;
+    const float invL = 1.0f / static_cast<float>(L);
+    const uint32_t nb = (a.cnt + L - 1) / L;
+    __shared__ float gm[kChunk];
+    const float *gin = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
+    for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = gin[b];
+    float g[kRows][4];
+    uint32_t bin[kRows][4];
+    chunk_G(a, R, dW, invL, g, bin);
     const float scale = seg_scale[a.s];
     const uint32_t base = seg_off[a.s] + w.cpre[c];
-    for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
-        uint32_t id = w.sidx[a.lo + i];
-        float g = w.sval[a.lo + i];
-        float q = copysignf(scale, g);
-        R[id] = g - q;
-        out_idx[base + i] = id;
-        out_val[base + i] = q;
+    const uint32_t count = w.ccount[c];  // slots reserved for this chunk by ada_max
+    __syncthreads();
+    bool flag[kRows][4];
+    uint32_t pos[kRows][4];
+    float *rp = R + a.lo;
+    const bool vec = is_aligned16(rp) && is_aligned16(dW + a.lo);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        const uint32_t e0 = row_elem(j);
+        float r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool in = e0 + q < a.cnt;
+            const float gmx = gm[in ? bin[j][q] : 0u];
+            const float t = sf * fabsf(g[j][q]);
+            flag[j][q] = in && gmx > 0.0f && t >= gmx;
+            const float qv = copysignf(scale, g[j][q]);
+            r[q] = flag[j][q] ? g[j][q] - qv : g[j][q];
+        }
+        store4(rp, e0, a.cnt, vec, r);
+    }
+    (void)block_compact4(flag, pos);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (flag[j][q] && pos[j][q] < count) {
+                out_idx[base + pos[j][q]] = static_cast<uint32_t>(a.lo + row_elem(j) + q);
+                out_val[base + pos[j][q]] = copysignf(scale, g[j][q]);
+            }
+        }
     }
 }
 
@@ -232,11 +304,12 @@ extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, f
     gc_status st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     AdaWs w = ada_layout(plan, ws, nullptr);
-    zero_words(w.zeroed, w.zero_words, stream);
-    ada_pass_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w);
-    ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_off, out->seg_scale);
-    ada_emit_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, R, w, out->seg_off, out->seg_scale,
-                                                          out->idx, out->val);
+    GC_LAUNCH("ada_max", stream, ada_max_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w));
+    GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale));
+    GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
+    GC_LAUNCH("ada_apply", stream, ada_apply_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
+        P, dW, R, scale_factor, w, out->seg_off, out->seg_scale, out->idx, out->val));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_adacomp_compress launch");
     return GC_OK;

@@ -34,8 +34,6 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-constexpr int kRows = kChunk / (4 * kBlock);  // 4 rows of 1024 elements
-
 template <bool kAligned>
 __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may alias xo
                                                      const float *__restrict__ xh, float *xo,
@@ -190,11 +188,11 @@ extern "C" gc_status gc_dcd_compress(const float *x, const float *x_half, float 
     const unsigned grid = grid_1d(n, kChunk);
     const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
     if (aligned)
-        dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
-                                                      scales, codes);
+        GC_LAUNCH("dcd", stream, dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+                                                      scales, codes));
     else
-        dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
-                                                       scales, codes);
+        GC_LAUNCH("dcd", stream, dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+                                                       scales, codes));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dcd_compress launch");
     return GC_OK;

@@ -43,29 +43,67 @@ DecWs dec_layout(const gc_plan *p, void *base, size_t *bytes) {
     return w;
 }
 
-// Chunk holding flat index i (clamped into the plan for malformed input).
-__device__ __forceinline__ uint32_t chunk_of(const PlanDev &P, uint32_t i) {
+// Segment holding flat index i (the last segment starting at or before it).
+__device__ __forceinline__ int segment_of(const PlanDev &P, uint32_t i) {
     int lo = 0, hi = P.nseg - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) / 2;
         if (P.seg_start[mid] <= i) lo = mid;
         else hi = mid - 1;
     }
-    const SegDev s = P.seg[lo];
-    uint64_t rel = i >= s.off ? (i - s.off) >> kChunkLog2 : 0;
-    if (rel >= s.dnchunk) rel = s.dnchunk - 1;
-    return s.dchunk0 + static_cast<uint32_t>(rel);
+    return lo;
 }
+
+// Walks ascending indices forward through the segments, keeping the current
+// segment's bounds in registers.  Out-of-range or descending indices are
+// clamped into the plan (malformed input stays in bounds).
+struct SegCursor {
+    const PlanDev *P;
+    int s;
+    uint64_t off, next;
+    uint32_t dchunk0, dnchunk;
+    __device__ void load(int seg) {
+        s = seg;
+        const SegDev d = P->seg[s];
+        off = d.off;
+        dchunk0 = d.dchunk0;
+        dnchunk = d.dnchunk;
+        next = s + 1 < P->nseg ? P->seg_start[s + 1] : ~uint64_t(0);
+    }
+    __device__ uint32_t chunk(uint32_t i) {
+        if (i >= next) {
+            int t = s;
+            while (t + 1 < P->nseg && P->seg_start[t + 1] <= i) ++t;
+            load(t);
+        }
+        uint64_t rel = i >= off ? (i - off) >> kChunkLog2 : 0;
+        if (rel >= dnchunk) rel = dnchunk - 1;
+        return dchunk0 + static_cast<uint32_t>(rel);
+    }
+};
+
+constexpr uint32_t kRun = 8;          // entries per thread and pass
+constexpr uint32_t kSparseChunk = 32;  // up to this many entries: no LDS accumulator
 
 __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTable m, DecWs w) {
     const int k = blockIdx.y;
     const uint32_t n = msg_count(m, k);
     const uint32_t *idx = m.idx[k];
     uint32_t *start = w.start + size_t(k) * (P.ndchunk + 1);
-    for (uint32_t j = blockIdx.x * kBlock + threadIdx.x; j <= n; j += gridDim.x * kBlock) {
-        uint32_t cj = j < n ? chunk_of(P, idx[j]) : P.ndchunk;
-        int64_t cp = j > 0 ? int64_t(chunk_of(P, idx[j - 1])) : -1;
-        for (int64_t c = cp + 1; c <= int64_t(cj); ++c) start[c] = j;
+    const uint64_t stride = uint64_t(gridDim.x) * kBlock * kRun;
+    for (uint64_t base = (uint64_t(blockIdx.x) * kBlock + threadIdx.x) * kRun; base <= n;
+         base += stride) {
+        SegCursor cur;
+        cur.P = &P;
+        cur.load(segment_of(P, base > 0 ? idx[base - 1] : (n > 0 ? idx[0] : 0u)));
+        int64_t cp = base > 0 ? int64_t(cur.chunk(idx[base - 1])) : -1;
+        for (uint32_t q = 0; q < kRun; ++q) {
+            const uint64_t j = base + q;
+            if (j > n) break;
+            const int64_t cj = j < n ? int64_t(cur.chunk(idx[j])) : int64_t(P.ndchunk);
+            for (int64_t c = cp + 1; c <= cj; ++c) start[c] = static_cast<uint32_t>(j);
+            if (cj > cp) cp = cj;
+        }
     }
 }
 
@@ -79,32 +117,89 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
     const uint64_t lo = seg.off + (uint64_t(pos) << kChunkLog2);
     const uint32_t rem = seg.len - (pos << kChunkLog2);
     const uint32_t cnt = rem < uint32_t(kChunk) ? rem : uint32_t(kChunk);
+    float *dp = dense + lo;
+    const bool vec = is_aligned16(dp);
+    __shared__ uint32_t range[2 * GC_MAX_MESSAGES];
     __shared__ float acc[kChunk];
-    for (int e = threadIdx.x; e < kChunk; e += kBlock) acc[e] = 0.0f;
-    __syncthreads();
-    for (int k = 0; k < K; ++k) {
+    bool mine = false;
+    if (threadIdx.x < uint32_t(K)) {
+        const int k = threadIdx.x;
         const uint32_t n = msg_count(m, k);
         const uint32_t *st = w.start + size_t(k) * (P.ndchunk + 1);
-        uint32_t a = min(st[c], n);
-        uint32_t b = min(max(st[c + 1], a), n);
-        const uint32_t *idx = m.idx[k];
-        const float *val = m.val[k];
-        for (uint32_t i = a + threadIdx.x; i < b; i += kBlock) {
-            uint64_t r = uint64_t(idx[i]) - lo;
-            if (idx[i] >= lo && r < cnt) acc[r] = acc[r] + val[i];
-        }
-        __syncthreads();
+        const uint32_t a = min(st[c], n);
+        const uint32_t b = min(max(st[c + 1], a), n);
+        range[2 * k] = a;
+        range[2 * k + 1] = b;
+        mine = b > a;
     }
+    const bool any = __syncthreads_or(mine);
+    __shared__ uint32_t total_entries;
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int k = 0; k < K; ++k) t += range[2 * k + 1] - range[2 * k];
+        total_entries = t;
+    }
+    __syncthreads();
     const float fk = static_cast<float>(K);
+    float v[kRows][4];
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        if (e < cnt) {
-            float v = acc[e];
-            if (avg) v = v / fk;
-            if (accumulate) v = dense[lo + e] + v;
-            dense[lo + e] = v;
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[j][q] = 0.0f;
+    if (any && total_entries <= kSparseChunk) {
+        // few entries: every thread scans them all (broadcast loads), in
+        // message order, and adds those that fall on its own elements
+        for (int k = 0; k < K; ++k) {
+            const uint32_t a = range[2 * k], b = range[2 * k + 1];
+            for (uint32_t i = a; i < b; ++i) {
+                const uint32_t id = m.idx[k][i];
+                const uint64_t r = uint64_t(id) - lo;
+                if (id < lo || r >= cnt) continue;
+                const uint32_t e = static_cast<uint32_t>(r);
+                const uint32_t j = e >> 10, q = e & 3u;
+                if (((e >> 2) & (kBlock - 1)) == threadIdx.x) {
+                    const float x = m.val[k][i];
+#pragma unroll
+                    for (int jj = 0; jj < kRows; ++jj)
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq)
+                            if (uint32_t(jj) == j && uint32_t(qq) == q) v[jj][qq] = v[jj][qq] + x;
+                }
+            }
         }
+    } else if (any) {
+        for (int e = threadIdx.x; e < kChunk; e += kBlock) acc[e] = 0.0f;
+        __syncthreads();
+        for (int k = 0; k < K; ++k) {
+            const uint32_t a = range[2 * k], b = range[2 * k + 1];
+            const uint32_t *idx = m.idx[k];
+            const float *val = m.val[k];
+            for (uint32_t i = a + threadIdx.x; i < b; i += kBlock) {
+                const uint32_t id = idx[i];
+                const uint64_t r = uint64_t(id) - lo;
+                if (id >= lo && r < cnt) acc[r] = acc[r] + val[i];
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kRows; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[j][q] = acc[row_elem(j) + q];
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        const uint32_t e0 = row_elem(j);
+        if (avg) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[j][q] = v[j][q] / fk;
+        }
+        if (accumulate) {
+            float d[4];
+            load4(dp, e0, cnt, vec, d);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[j][q] = d[q] + v[j][q];
+        }
+        store4(dp, e0, cnt, vec, v[j]);
     }
 }
 
@@ -151,10 +246,11 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     DecWs w = dec_layout(plan, ws, nullptr);
     uint64_t max_entries = 0;
     for (int k = 0; k < K; ++k) max_entries = std::max<uint64_t>(max_entries, msgs[k].cap);
-    unsigned gx = static_cast<unsigned>(std::min<uint64_t>((max_entries + kBlock) / kBlock + 1, 1024));
-    decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w);
-    decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
-                                                        accumulate != 0);
+    unsigned gx = static_cast<unsigned>(
+        std::min<uint64_t>((max_entries + kBlock * kRun) / (kBlock * kRun) + 1, 1024));
+    GC_LAUNCH("decode_index", stream, decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w));
+    GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
+                                                        accumulate != 0));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_decompress_accumulate launch");
     return GC_OK;

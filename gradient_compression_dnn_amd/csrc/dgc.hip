@@ -2,20 +2,25 @@
 // radix select on |V| bit patterns, ordered compaction, momentum factor
 // masking.  "Deep Gradient Compression" (Lin et al.), §3.1–§3.3, App. C, D.
 //
-// Launch sequence (one workgroup per 4096-element chunk of a segment):
-//   zero          histograms and tickets
-//   norm          (clip only) pairwise fp64 sum of G^2 per chunk; the last
-//                 chunk of a segment finishes the tree and the clip factor
-//   update        U <- fl(fl(m U) + fl(c G)); V <- fl(V + U); LDS histogram of
-//                 key >> 20; the last chunk of a segment finds digit 1
-//   stage         re-read V, keep entries whose digit 1 is at or above the
-//                 k-th largest's (ordered, at the chunk's own offset); histogram
-//                 digit 2 of the boundary bucket; last chunk finds digit 2
-//   refine        digit-3 histogram over staged boundary entries; last chunk
-//                 fixes the threshold key T and the tie count
-//   count         per chunk: keys > T and keys == T; last chunk scans the
-//                 segment's chunks into output slots and ties to take
-//   emit          write (idx, V) in index order, then zero U and V there
+// Launch sequence.  Chunk kernels run one workgroup per 4096-element chunk of
+// a segment; segment kernels one workgroup per segment.  Chunk kernels hand
+// results to segment kernels through global memory at kernel boundaries only
+// (no cross-workgroup fences, which on gfx950 write back the XCD's L2).
+//   norm    (chunk, clip only) pairwise fp64 sum of G^2 over the chunk
+//   prep    (segment) clear the segment's histograms; finish the pairwise
+//           tree over the chunk sums and set the clip factor
+//   update  (chunk) U <- fl(fl(m U) + fl(c G)); V <- fl(V + U); LDS histogram
+//           of digit 1 (key >> 20), flushed with global atomics
+//   select1 (segment) digit 1 of the k-th largest key
+//   stage   (chunk) re-read V; keep entries with digit 1 at or above it, in
+//           index order at the chunk's own offset; histogram digit 2 of the
+//           boundary bucket
+//   select2 (segment) digit 2
+//   refine  (chunk) histogram digit 3 of staged entries in the boundary bucket
+//   select3 (segment) threshold key T, count above it, ties to send
+//   count   (chunk) staged keys > T and == T
+//   scan    (segment) message slot and tie quota of every chunk
+//   emit    (chunk) write (idx, V) in index order, then zero U and V there
 #include <cmath>
 
 #include "gc_internal.hpp"
@@ -29,12 +34,8 @@ struct SegState {
     uint32_t d1, above1, d2, above2, T, gt, need_eq;
 };
 
-enum { kTicketNorm, kTicketUpdate, kTicketStage, kTicketRefine, kTicketCount, kTickets };
-
 struct DgcWs {
-    uint32_t *zeroed;   // start of the region cleared every call
-    size_t zero_words;
-    uint32_t *hist1, *hist2, *hist3, *ticket;
+    uint32_t *hist1, *hist2, *hist3;
     SegState *st;
     double *partial;
     uint32_t *ccount, *cgt, *ceq, *cout, *ctake;
@@ -45,13 +46,9 @@ struct DgcWs {
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
     DgcWs w{};
-    size_t per_seg = size_t(kHist1) + kHist2 + kHist3 + kTickets;
-    w.zero_words = per_seg * p->nseg;
-    w.zeroed = c.take<uint32_t>(w.zero_words);
-    w.hist1 = w.zeroed;
-    w.hist2 = w.hist1 + size_t(kHist1) * p->nseg;
-    w.hist3 = w.hist2 + size_t(kHist2) * p->nseg;
-    w.ticket = w.hist3 + size_t(kHist3) * p->nseg;
+    w.hist1 = c.take<uint32_t>(size_t(kHist1) * p->nseg);
+    w.hist2 = c.take<uint32_t>(size_t(kHist2) * p->nseg);
+    w.hist3 = c.take<uint32_t>(size_t(kHist3) * p->nseg);
     w.st = c.take<SegState>(p->nseg);
     w.partial = c.take<double>(p->ndchunk);
     w.ccount = c.take<uint32_t>(p->ndchunk);
@@ -85,91 +82,189 @@ __device__ __forceinline__ ChunkInfo chunk_info(const PlanDev &P, uint32_t c) {
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return dev_f2u(v) & 0x7FFFFFFFu; }
 
+// Persistent dense kernels: workgroup b walks chunks [first, last), a
+// contiguous range, so consecutive chunks mostly share a segment.
+__device__ __forceinline__ void chunk_range(uint32_t nchunk, uint32_t *first, uint32_t *last) {
+    const uint32_t per = (nchunk + gridDim.x - 1) / gridDim.x;
+    *first = blockIdx.x * per;
+    *last = min(*first + per, nchunk);
+}
+
 // ------------------------------------------------------------------ norm
+// Lane l of wave w holds elements [1024 j + 256 w + 4 l, +4) of row j: its
+// (x0^2 + x1^2) + (x2^2 + x3^2) is a level-2 node of the pairwise tree.  The
+// lane nodes go to LDS in index order; thread t then owns the 4 consecutive
+// level-2 nodes [4 t, 4 t + 4) (a 16-element subtree), and the 256 thread
+// sums are combined by block_tree_sum into the chunk's level-12 node.
 __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float *__restrict__ G,
-                                                          DgcWs w, float thr) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
-    __shared__ float tile[kChunk];
+                                                          DgcWs w) {
+    uint32_t c0, c1;
+    chunk_range(P.ndchunk, &c0, &c1);
+    __shared__ double node[kChunk / 4];  // level-2 nodes of the chunk, in order
+    float cur[kRows][4], nxt[kRows][4];
+    ChunkInfo ci;
+    bool vec = false;
+    if (c0 < c1) {
+        ci = chunk_info(P, c0);
+        vec = is_aligned16(G + ci.lo);
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        tile[e] = e < ci.cnt ? G[ci.lo + e] : 0.0f;
+        for (int j = 0; j < kRows; ++j) load4(G + ci.lo, row_elem(j), ci.cnt, vec, cur[j]);
     }
-    __syncthreads();
-    // leaves [16t, 16t+16) of the chunk: a perfect 16-leaf subtree per thread
-    double a[kEPT];
+    for (uint32_t c = c0; c < c1; ++c) {
+        ChunkInfo cn;
+        bool vn = false;
+        if (c + 1 < c1) {
+            cn = chunk_info(P, c + 1);
+            vn = is_aligned16(G + cn.lo);
 #pragma unroll
-    for (int i = 0; i < kEPT; ++i) {
-        double x = static_cast<double>(tile[threadIdx.x * kEPT + i]);
-        a[i] = x * x;
-    }
+            for (int j = 0; j < kRows; ++j) load4(G + cn.lo, row_elem(j), cn.cnt, vn, nxt[j]);
+        }
 #pragma unroll
-    for (int w2 = 1; w2 < kEPT; w2 <<= 1)
+        for (int j = 0; j < kRows; ++j) {
+            double a[4];
 #pragma unroll
-        for (int i = 0; i < kEPT; i += 2 * w2) a[i] = a[i] + a[i + w2];
-    double chunk_sum = block_tree_sum(a[0]);
-    if (threadIdx.x == 0) w.partial[c] = chunk_sum;
-    if (block_arrive_last(&w.ticket[ci.s * kTickets + kTicketNorm], ci.seg.dnchunk)) {
-        const double *part = w.partial + ci.seg.dchunk0;
-        double S = block_pairwise_sum(ci.seg.dnchunk,
-                                      [&](uint64_t g) { return load_coherent(part + g); });
-        if (threadIdx.x == 0) {
-            double norm = sqrt(S);
-            float cl = 1.0f;
-            if (norm > static_cast<double>(thr)) cl = static_cast<float>(static_cast<double>(thr) / norm);
-            w.st[ci.s].clip = cl;
+            for (int q = 0; q < 4; ++q) {
+                double x = static_cast<double>(cur[j][q]);
+                a[q] = x * x;
+            }
+            node[j * kBlock + threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
+        }
+        __syncthreads();
+        // four consecutive level-2 nodes: the 16-element level-4 node of thread t
+        const double t0 = node[4 * threadIdx.x] + node[4 * threadIdx.x + 1];
+        const double t1 = node[4 * threadIdx.x + 2] + node[4 * threadIdx.x + 3];
+        double t[1] = {t0 + t1};
+        const double chunk_sum = block_tree_sum(t[0]);
+        if (threadIdx.x == 0) w.partial[c] = chunk_sum;
+        if (c + 1 < c1) {
+            ci = cn;
+#pragma unroll
+            for (int j = 0; j < kRows; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[j][q] = nxt[j][q];
         }
     }
 }
 
+// ------------------------------------------------------------------ prep
+__global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, int use_clip,
+                                                          float thr) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    uint32_t *h = w.hist1 + size_t(s) * kHist1;
+    for (int i = threadIdx.x; i < kHist1; i += kBlock) h[i] = 0u;
+    h = w.hist2 + size_t(s) * kHist2;
+    for (int i = threadIdx.x; i < kHist2; i += kBlock) h[i] = 0u;
+    h = w.hist3 + size_t(s) * kHist3;
+    for (int i = threadIdx.x; i < kHist3; i += kBlock) h[i] = 0u;
+    float cl = 1.0f;
+    if (use_clip) {
+        const double *part = w.partial + seg.dchunk0;
+        double S = block_pairwise_sum(seg.dnchunk, [&](uint64_t g) { return part[g]; });
+        double norm = sqrt(S);
+        if (norm > static_cast<double>(thr)) cl = static_cast<float>(static_cast<double>(thr) / norm);
+    }
+    if (threadIdx.x == 0) w.st[s].clip = cl;
+}
+
 // ---------------------------------------------------------------- update
+// The digit-1 histogram lives in LDS across the workgroup's chunks and is
+// flushed to the segment's global histogram only when the segment changes.
 __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const float *__restrict__ G,
                                                             float *__restrict__ U,
-                                                            float *__restrict__ V, float m,
-                                                            int use_clip, DgcWs w) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
+                                                            float *__restrict__ V, float m, DgcWs w) {
+    uint32_t c0, c1;
+    chunk_range(P.ndchunk, &c0, &c1);
     __shared__ uint32_t hist[kHist1];
     for (int i = threadIdx.x; i < kHist1; i += kBlock) hist[i] = 0u;
-    const float clip = use_clip ? w.st[ci.s].clip : 1.0f;
-    float g[kEPT], u[kEPT], v[kEPT];
+    if (c0 >= c1) return;
+    float g[kRows][4], u[kRows][4], v[kRows][4];
+    ChunkInfo ci = chunk_info(P, c0);
+    bool vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        if (e < ci.cnt) {
-            g[j] = G[ci.lo + e];
-            u[j] = U[ci.lo + e];
-            v[j] = V[ci.lo + e];
-        }
+    for (int j = 0; j < kRows; ++j) {
+        load4(G + ci.lo, row_elem(j), ci.cnt, vec, g[j]);
+        load4(U + ci.lo, row_elem(j), ci.cnt, vec, u[j]);
+        load4(V + ci.lo, row_elem(j), ci.cnt, vec, v[j]);
     }
     __syncthreads();
+    for (uint32_t c = c0; c < c1; ++c) {
+        const float clip = w.st[ci.s].clip;
+        float *up = U + ci.lo;
+        float *vp = V + ci.lo;
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        if (e < ci.cnt) {
-            float gc = clip * g[j];
-            float un = m * u[j];
-            un = un + gc;
-            float vn = v[j] + un;
-            U[ci.lo + e] = un;
-            V[ci.lo + e] = vn;
-            atomicAdd(&hist[mag_key(vn) >> (kDigit2Bits + kDigit3Bits)], 1u);
+        for (int j = 0; j < kRows; ++j) {
+            const uint32_t e0 = row_elem(j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float gc = clip * g[j][q];
+                float un = m * u[j][q];
+                un = un + gc;
+                float vn = v[j][q] + un;
+                u[j][q] = un;
+                v[j][q] = vn;
+                if (e0 + q < ci.cnt) atomicAdd(&hist[mag_key(vn) >> (kDigit2Bits + kDigit3Bits)], 1u);
+            }
+            store4(up, e0, ci.cnt, vec, u[j]);
+            store4(vp, e0, ci.cnt, vec, v[j]);
+        }
+        const uint32_t s_done = ci.s;
+        const bool more = c + 1 < c1;
+        if (more) {
+            ci = chunk_info(P, c + 1);
+            vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) {
+                load4(G + ci.lo, row_elem(j), ci.cnt, vec, g[j]);
+                load4(U + ci.lo, row_elem(j), ci.cnt, vec, u[j]);
+                load4(V + ci.lo, row_elem(j), ci.cnt, vec, v[j]);
+            }
+        }
+        if (!more || ci.s != s_done) {
+            __syncthreads();
+            uint32_t *h1 = w.hist1 + size_t(s_done) * kHist1;
+            for (int i = threadIdx.x; i < kHist1; i += kBlock) {
+                const uint32_t n = hist[i];
+                if (n) {
+                    atomicAdd(&h1[i], n);
+                    hist[i] = 0u;
+                }
+            }
+            __syncthreads();
         }
     }
-    __syncthreads();
-    uint32_t *h1 = w.hist1 + size_t(ci.s) * kHist1;
-    for (int i = threadIdx.x; i < kHist1; i += kBlock) {
-        uint32_t n = hist[i];
-        if (n) atomicAdd(&h1[i], n);
-    }
-    if (block_arrive_last(&w.ticket[ci.s * kTickets + kTicketUpdate], ci.seg.dnchunk)) {
-        uint32_t above;
-        uint32_t d1 = block_find_bucket<kHist1>(
-            ci.seg.k, [&](int b) { return load_coherent(h1 + b); }, &above);
+}
+
+// --------------------------------------------------------------- selects
+// Level 1..3 of the radix select for one segment.
+template <int kLevel>
+__global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    SegState st = w.st[s];
+    uint32_t above;
+    if (kLevel == 1) {
+        const uint32_t *h = w.hist1 + size_t(s) * kHist1;
+        uint32_t d = block_find_bucket<kHist1>(seg.k, [&](int b) { return h[b]; }, &above);
         if (threadIdx.x == 0) {
-            w.st[ci.s].d1 = d1;
-            w.st[ci.s].above1 = above;
+            w.st[s].d1 = d;
+            w.st[s].above1 = above;
+        }
+    } else if (kLevel == 2) {
+        const uint32_t *h = w.hist2 + size_t(s) * kHist2;
+        uint32_t d = block_find_bucket<kHist2>(seg.k - st.above1, [&](int b) { return h[b]; }, &above);
+        if (threadIdx.x == 0) {
+            w.st[s].d2 = d;
+            w.st[s].above2 = st.above1 + above;
+        }
+    } else {
+        const uint32_t *h = w.hist3 + size_t(s) * kHist3;
+        uint32_t d = block_find_bucket<kHist3>(seg.k - st.above2, [&](int b) { return h[b]; }, &above);
+        if (threadIdx.x == 0) {
+            uint32_t gt = st.above2 + above;
+            w.st[s].T = (((st.d1 << kDigit2Bits) | st.d2) << kDigit3Bits) | d;
+            w.st[s].gt = gt;
+            w.st[s].need_eq = seg.k - gt;
         }
     }
 }
@@ -177,40 +272,55 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
 // ----------------------------------------------------------------- stage
 __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const float *__restrict__ V,
                                                            DgcWs w) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
-    const uint32_t d1 = w.st[ci.s].d1;
-    uint32_t *h2 = w.hist2 + size_t(ci.s) * kHist2;
-    float v[kEPT];
-    bool flag[kEPT];
-    uint32_t pos[kEPT];
+    uint32_t c0, c1;
+    chunk_range(P.ndchunk, &c0, &c1);
+    if (c0 >= c1) return;
+    float v[kRows][4], nv[kRows][4];
+    ChunkInfo ci = chunk_info(P, c0);
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t e = j * kBlock + threadIdx.x;
-        v[j] = e < ci.cnt ? V[ci.lo + e] : 0.0f;
-        uint32_t key = mag_key(v[j]);
-        uint32_t dig1 = key >> (kDigit2Bits + kDigit3Bits);
-        flag[j] = e < ci.cnt && dig1 >= d1;
-        if (e < ci.cnt && dig1 == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
-    }
-    uint32_t total = block_compact<kEPT>(flag, pos);
+    for (int j = 0; j < kRows; ++j) load4(V + ci.lo, row_elem(j), ci.cnt, is_aligned16(V + ci.lo), v[j]);
+    for (uint32_t c = c0; c < c1; ++c) {
+        ChunkInfo cn;
+        const bool more = c + 1 < c1;
+        if (more) {
+            cn = chunk_info(P, c + 1);
+            const bool vn = is_aligned16(V + cn.lo);
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        if (flag[j]) {
-            uint32_t e = j * kBlock + threadIdx.x;
-            w.sidx[ci.lo + pos[j]] = static_cast<uint32_t>(ci.lo + e);
-            w.sval[ci.lo + pos[j]] = v[j];
+            for (int j = 0; j < kRows; ++j) load4(V + cn.lo, row_elem(j), cn.cnt, vn, nv[j]);
         }
-    }
-    if (threadIdx.x == 0) w.ccount[c] = total;
-    if (block_arrive_last(&w.ticket[ci.s * kTickets + kTicketStage], ci.seg.dnchunk)) {
-        const uint32_t need = ci.seg.k - w.st[ci.s].above1;
-        uint32_t above;
-        uint32_t d2 = block_find_bucket<kHist2>(
-            need, [&](int b) { return load_coherent(h2 + b); }, &above);
-        if (threadIdx.x == 0) {
-            w.st[ci.s].d2 = d2;
-            w.st[ci.s].above2 = w.st[ci.s].above1 + above;
+        const uint32_t d1 = w.st[ci.s].d1;
+        uint32_t *h2 = w.hist2 + size_t(ci.s) * kHist2;
+        bool flag[kRows][4];
+        uint32_t pos[kRows][4];
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool in = row_elem(j) + q < ci.cnt;
+                const uint32_t key = mag_key(v[j][q]);
+                const uint32_t dig1 = key >> (kDigit2Bits + kDigit3Bits);
+                flag[j][q] = in && dig1 >= d1;
+                if (in && dig1 == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            }
+        }
+        const uint32_t total = block_compact4(flag, pos);
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (flag[j][q]) {
+                    w.sidx[ci.lo + pos[j][q]] = static_cast<uint32_t>(ci.lo + row_elem(j) + q);
+                    w.sval[ci.lo + pos[j][q]] = v[j][q];
+                }
+            }
+        }
+        if (threadIdx.x == 0) w.ccount[c] = total;
+        if (more) {
+            ci = cn;
+#pragma unroll
+            for (int j = 0; j < kRows; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[j][q] = nv[j][q];
         }
     }
 }
@@ -220,33 +330,33 @@ __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) 
     const uint32_t c = blockIdx.x;
     const ChunkInfo ci = chunk_info(P, c);
     const uint32_t n = w.ccount[c];
+    if (n == 0) return;
     const uint32_t prefix = (w.st[ci.s].d1 << kDigit2Bits) | w.st[ci.s].d2;
     uint32_t *h3 = w.hist3 + size_t(ci.s) * kHist3;
     for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
         uint32_t key = mag_key(w.sval[ci.lo + i]);
         if ((key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
     }
-    if (block_arrive_last(&w.ticket[ci.s * kTickets + kTicketRefine], ci.seg.dnchunk)) {
-        const uint32_t need = ci.seg.k - w.st[ci.s].above2;
-        uint32_t above;
-        uint32_t d3 = block_find_bucket<kHist3>(
-            need, [&](int b) { return load_coherent(h3 + b); }, &above);
-        if (threadIdx.x == 0) {
-            uint32_t gt = w.st[ci.s].above2 + above;
-            w.st[ci.s].T = (prefix << kDigit3Bits) | d3;
-            w.st[ci.s].gt = gt;
-            w.st[ci.s].need_eq = ci.seg.k - gt;
-        }
-    }
 }
 
 // ----------------------------------------------------------------- count
-__global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w,
-                                                           uint32_t *__restrict__ seg_off) {
+__global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w) {
     const uint32_t c = blockIdx.x;
     const ChunkInfo ci = chunk_info(P, c);
     const uint32_t n = w.ccount[c];
     const uint32_t T = w.st[ci.s].T;
+    if (n <= uint32_t(kWave)) {
+        if (wave_id() != 0) return;
+        const bool in = uint32_t(lane_id()) < n;
+        const uint32_t key = in ? mag_key(w.sval[ci.lo + lane_id()]) : 0u;
+        const uint32_t tgt = static_cast<uint32_t>(__popcll(__ballot(in && key > T)));
+        const uint32_t teq = static_cast<uint32_t>(__popcll(__ballot(in && key == T)));
+        if (lane_id() == 0) {
+            w.cgt[c] = tgt;
+            w.ceq[c] = teq;
+        }
+        return;
+    }
     uint32_t ngt = 0, neq = 0;
     for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
         uint32_t key = mag_key(w.sval[ci.lo + i]);
@@ -260,33 +370,39 @@ __global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w,
         w.cgt[c] = tgt;
         w.ceq[c] = teq;
     }
-    if (block_arrive_last(&w.ticket[ci.s * kTickets + kTicketCount], ci.seg.dnchunk)) {
-        // scan the segment's chunks in order: ties go to the lowest indices
-        const uint32_t need_eq = w.st[ci.s].need_eq;
-        uint32_t eq_before = 0, sel_before = 0;
-        for (uint32_t r = 0; r < ci.seg.dnchunk; r += kBlock) {
-            uint32_t cc = ci.seg.dchunk0 + r + threadIdx.x;
-            bool in = r + threadIdx.x < ci.seg.dnchunk;
-            uint32_t eq = in ? load_coherent(w.ceq + cc) : 0u;
-            uint32_t gt = in ? load_coherent(w.cgt + cc) : 0u;
-            uint32_t eq_tot;
-            uint32_t eq_pre = eq_before + block_exclusive_scan(eq, &eq_tot);
-            uint32_t take = 0;
-            if (need_eq > eq_pre) take = min(need_eq - eq_pre, eq);
-            uint32_t sel = gt + take;
-            uint32_t sel_tot;
-            uint32_t sel_pre = sel_before + block_exclusive_scan(sel, &sel_tot);
-            if (in) {
-                w.ctake[cc] = take;
-                w.cout[cc] = ci.seg.kbase + sel_pre;
-            }
-            eq_before += eq_tot;
-            sel_before += sel_tot;
+}
+
+// ------------------------------------------------------------------ scan
+// Ties at the threshold go to the lowest indices: scan the segment's chunks
+// in order for the tie quota and the message slot of each chunk.
+__global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
+                                                          uint32_t *__restrict__ seg_off) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    const uint32_t need_eq = w.st[s].need_eq;
+    uint32_t eq_before = 0, sel_before = 0;
+    for (uint32_t r = 0; r < seg.dnchunk; r += kBlock) {
+        uint32_t cc = seg.dchunk0 + r + threadIdx.x;
+        bool in = r + threadIdx.x < seg.dnchunk;
+        uint32_t eq = in ? w.ceq[cc] : 0u;
+        uint32_t gt = in ? w.cgt[cc] : 0u;
+        uint32_t eq_tot;
+        uint32_t eq_pre = eq_before + block_exclusive_scan(eq, &eq_tot);
+        uint32_t take = 0;
+        if (need_eq > eq_pre) take = min(need_eq - eq_pre, eq);
+        uint32_t sel = gt + take;
+        uint32_t sel_tot;
+        uint32_t sel_pre = sel_before + block_exclusive_scan(sel, &sel_tot);
+        if (in) {
+            w.ctake[cc] = take;
+            w.cout[cc] = seg.kbase + sel_pre;
         }
-        if (threadIdx.x == 0) {
-            seg_off[ci.s] = ci.seg.kbase;
-            if (ci.s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = ci.seg.kbase + ci.seg.k;
-        }
+        eq_before += eq_tot;
+        sel_before += sel_tot;
+    }
+    if (threadIdx.x == 0) {
+        seg_off[s] = seg.kbase;
+        if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = seg.kbase + seg.k;
     }
 }
 
@@ -302,6 +418,27 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__re
     const uint32_t T = w.st[ci.s].T;
     const uint32_t take = w.ctake[c];
     const uint32_t base = w.cout[c];
+    // a segment owns message slots [kbase, kbase + k): never write past them
+    const uint32_t limit = ci.seg.kbase + ci.seg.k;
+    if (n <= uint32_t(kWave)) {
+        // one wave: ranks straight from ballots, no barriers
+        if (wave_id() != 0) return;
+        const uint32_t i = lane_id();
+        const bool in = i < n;
+        const uint32_t id = in ? w.sidx[ci.lo + i] : 0u;
+        const float val = in ? w.sval[ci.lo + i] : 0.0f;
+        const uint32_t key = mag_key(val);
+        const bool eq = in && key == T;
+        const bool sel = (in && key > T) || (eq && lane_rank(__ballot(eq)) < take);
+        const uint32_t p = base + lane_rank(__ballot(sel));
+        if (sel && p < limit) {
+            out_idx[p] = id;
+            out_val[p] = val;
+            V[id] = 0.0f;
+            U[id] = 0.0f;
+        }
+        return;
+    }
     bool eqf[kEPT], self[kEPT];
     uint32_t eqpos[kEPT], pos[kEPT];
     uint32_t id[kEPT];
@@ -320,8 +457,6 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__re
 #pragma unroll
     for (int j = 0; j < kEPT; ++j) self[j] = self[j] || (eqf[j] && eqpos[j] < take);
     (void)block_compact<kEPT>(self, pos);
-    // a segment owns message slots [kbase, kbase + k): never write past them
-    const uint32_t limit = ci.seg.kbase + ci.seg.k;
 #pragma unroll
     for (int j = 0; j < kEPT; ++j) {
         if (self[j] && base + pos[j] < limit) {
@@ -374,13 +509,19 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     const float thr = clip ? static_cast<float>(static_cast<double>(thr_G) /
                                                 std::sqrt(static_cast<double>(num_nodes)))
                            : 0.0f;
-    zero_words(w.zeroed, w.zero_words, stream);
-    if (clip) dgc_norm_kernel<<<grid, kBlock, 0, stream>>>(P, G, w, thr);
-    dgc_update_kernel<<<grid, kBlock, 0, stream>>>(P, G, U, V, momentum, clip ? 1 : 0, w);
-    dgc_stage_kernel<<<grid, kBlock, 0, stream>>>(P, V, w);
-    dgc_refine_kernel<<<grid, kBlock, 0, stream>>>(P, w);
-    dgc_count_kernel<<<grid, kBlock, 0, stream>>>(P, w, out->seg_off);
-    dgc_emit_kernel<<<grid, kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val);
+    const unsigned segs = static_cast<unsigned>(plan->nseg);
+    const unsigned pgrid = persistent_grid(plan->ndchunk);
+    if (clip) GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<pgrid, kBlock, 0, stream>>>(P, G, w));
+    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
+    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<<<pgrid, kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<pgrid, kBlock, 0, stream>>>(P, V, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
+    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<grid, kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dgc_step launch");
     return GC_OK;

@@ -45,17 +45,24 @@ struct SegDev {
     uint32_t achunk_len; // elements per AdaComp chunk (multiple of bin_len)
     uint32_t bin0;       // first bin of the segment in the plan-wide bin array
     uint32_t kbase;      // first message slot of the segment in a DGC message
+    uint32_t bgroup0;    // first 4096-bin group of the segment (AdaComp scale sum)
+    uint32_t nbgroup;    // 4096-bin groups in the segment
     uint32_t pad;
 };
+
+constexpr int kBinGroupLog2 = 12;  // bins per group of the scale's pairwise tree
+constexpr uint32_t kBinGroup = 1u << kBinGroupLog2;
 
 struct PlanDev {
     const SegDev *seg;          // [nseg]
     const uint32_t *dchunk_seg; // [ndchunk]
     const uint32_t *achunk_seg; // [nachunk]
     const uint64_t *seg_start;  // [nseg] offsets, for searching an index
+    const uint32_t *bgroup_seg; // [nbgroup] segment of each bin group
     int nseg;
     uint32_t ndchunk;
     uint32_t nachunk;
+    uint32_t nbgroup;
     uint64_t n_total;
 };
 
@@ -68,10 +75,12 @@ struct gc_plan {
     uint64_t total_bins = 0;
     uint32_t ndchunk = 0;
     uint32_t nachunk = 0;
+    uint32_t nbgroup = 0;
     std::vector<gc::SegDev> seg;
     std::vector<uint32_t> dchunk_seg;
     std::vector<uint32_t> achunk_seg;
     std::vector<uint64_t> seg_start;
+    std::vector<uint32_t> bgroup_seg;
     // device copies, one per device, uploaded on first use
     std::mutex mu;
     std::vector<std::pair<int, void *>> dev_blob;
@@ -112,9 +121,34 @@ inline unsigned grid_1d(uint64_t n, unsigned per_block) {
     return static_cast<unsigned>((n + per_block - 1) / per_block);
 }
 
-// Fill u32 words with zero (used instead of hipMemsetAsync so the library's
-// enqueued work stays plain kernels).
-void zero_words(uint32_t *p, size_t words, hipStream_t s);
+// Workgroups for a persistent dense pass: enough to fill every CU of an
+// MI355X (256 CUs x 8 resident 256-thread workgroups), never more than the
+// work items.
+constexpr unsigned kPersistentBlocks = 256 * 8;
+inline unsigned persistent_grid(uint64_t items) {
+    return static_cast<unsigned>(items < kPersistentBlocks ? (items ? items : 1) : kPersistentBlocks);
+}
+
+// Kernel timing (see gc_timing_enable): returns an event to record before
+// the launch (or nullptr when the kernel is not selected) and records the
+// closing event after it.
+hipEvent_t timing_begin(const char *kernel, hipStream_t s);
+void timing_end(const char *kernel, hipEvent_t start, hipStream_t s);
+
+struct TimedLaunch {
+    const char *name;
+    hipStream_t stream;
+    hipEvent_t start;
+    TimedLaunch(const char *n, hipStream_t s) : name(n), stream(s), start(timing_begin(n, s)) {}
+    ~TimedLaunch() {
+        if (start) timing_end(name, start, stream);
+    }
+};
+#define GC_LAUNCH(name, stream, ...)                  \
+    do {                                              \
+        ::gc::TimedLaunch gc_timed_launch_(name, stream); \
+        __VA_ARGS__;                                  \
+    } while (0)
 
 inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
@@ -188,6 +222,92 @@ __device__ __forceinline__ uint32_t block_compact(const bool (&flag)[EPT], uint3
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < EPT; ++j) pos[j] = cnt[j * kWaves + wave_id()] + rank[j];
+    uint32_t t = tot;
+    __syncthreads();
+    return t;
+}
+
+// ------------------------------------------------------ 4-wide lane layout
+// Dense chunk kernels give every lane 4 consecutive elements per row:
+// element e = row * 1024 + 4 * threadIdx.x + u (u = 0..3), rows 0..3, so a
+// 4096-element chunk is 4 rows.  When the chunk starts on a 16-byte boundary
+// the four elements move as one float4; otherwise (or at a ragged tail) each
+// element is accessed on its own.
+constexpr int kRows = kChunk / (4 * kBlock);
+
+__device__ __forceinline__ uint32_t row_elem(int row) { return row * (4 * kBlock) + 4u * threadIdx.x; }
+
+__device__ __forceinline__ bool is_aligned16(const void *p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+__device__ __forceinline__ void load4(const float *p, uint32_t e0, uint32_t cnt, bool vec,
+                                      float (&v)[4]) {
+    if (vec && e0 + 4 <= cnt) {
+        float4 t = *reinterpret_cast<const float4 *>(p + e0);
+        v[0] = t.x;
+        v[1] = t.y;
+        v[2] = t.z;
+        v[3] = t.w;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = e0 + u < cnt ? p[e0 + u] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void store4(float *p, uint32_t e0, uint32_t cnt, bool vec,
+                                       const float (&v)[4]) {
+    if (vec && e0 + 4 <= cnt) {
+        *reinterpret_cast<float4 *>(p + e0) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (e0 + u < cnt) p[e0 + u] = v[u];
+    }
+}
+
+// Ordered compaction in the 4-wide layout: element (row, u) of thread t has
+// rank row * 1024 + 4 t + u.  pos receives the output slot of flagged
+// elements; returns the block's flagged count.
+__device__ __forceinline__ uint32_t block_compact4(const bool (&flag)[kRows][4],
+                                                   uint32_t (&pos)[kRows][4]) {
+    __shared__ uint32_t cnt[kRows * kWaves];
+    __shared__ uint32_t tot;
+    uint32_t rank[kRows][4];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint64_t m = __ballot(flag[j][u]);
+            before += lane_rank(m);
+            total += static_cast<uint32_t>(__popcll(m));
+        }
+        uint32_t within = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            rank[j][u] = before + within;
+            within += flag[j][u] ? 1u : 0u;
+        }
+        if (lane_id() == 0) cnt[j * kWaves + wave_id()] = total;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        uint32_t v = threadIdx.x < kRows * kWaves ? cnt[threadIdx.x] : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            uint32_t y = __shfl_up(x, d, kWave);
+            if (lane_id() >= d) x += y;
+        }
+        if (threadIdx.x < kRows * kWaves) cnt[threadIdx.x] = x - v;
+        if (threadIdx.x == kWave - 1) tot = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pos[j][u] = cnt[j * kWaves + wave_id()] + rank[j][u];
     uint32_t t = tot;
     __syncthreads();
     return t;
@@ -283,30 +403,6 @@ __device__ uint32_t block_find_bucket(uint32_t k, Count count, uint32_t *above) 
     uint32_t d = res_d;
     __syncthreads();
     return d;
-}
-
-// Last-workgroup detection: every workgroup of a group calls this once after
-// its global writes; exactly one (the last to arrive) gets true, and after
-// the acquire fence it sees all the others' writes.
-__device__ __forceinline__ bool block_arrive_last(uint32_t *ticket, uint32_t expected) {
-    __shared__ bool last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        uint32_t prev = atomicAdd(ticket, 1u);
-        last = (prev == expected - 1);
-    }
-    __syncthreads();
-    bool l = last;
-    if (l) __threadfence();
-    return l;
-}
-
-// Read a value written by other workgroups of the same launch, bypassing
-// the non-coherent vector L1.
-template <class T>
-__device__ __forceinline__ T load_coherent(const T *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 #endif  // __HIPCC__

@@ -149,18 +149,25 @@ __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind
                                                              uint8_t *__restrict__ out,
                                                              uint64_t *__restrict__ out_bytes, PackWs w) {
     const uint32_t ntiles = w.tile_base[P.nseg];
-    uint32_t run = 0;
-    for (uint32_t r = 0; r < ntiles; r += kBlock) {
-        uint32_t t = r + threadIdx.x;
-        uint32_t v = t < ntiles ? w.tile_esc[t] : 0u;
-        uint32_t tot;
-        uint32_t pre = block_exclusive_scan(v, &tot);
-        if (t < ntiles) w.tile_esc[t] = run + pre;
-        run += tot;
+    {
+        // exclusive scan of the tiles' escape counts: thread t owns a
+        // contiguous run of tiles, then one workgroup scan of the run sums
+        const uint32_t per = (ntiles + kBlock - 1) / kBlock;
+        const uint32_t t0 = threadIdx.x * per;
+        const uint32_t t1 = min(t0 + per, ntiles);
+        uint32_t sum = 0;
+        for (uint32_t t = t0; t < t1; ++t) sum += w.tile_esc[t];
+        uint32_t all;
+        uint32_t run = block_exclusive_scan(sum, &all);
+        for (uint32_t t = t0; t < t1; ++t) {
+            const uint32_t e = w.tile_esc[t];
+            w.tile_esc[t] = run;
+            run += e;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) w.tile_esc[ntiles] = all;
+        __syncthreads();
     }
-    __syncthreads();
-    if (threadIdx.x == 0) w.tile_esc[ntiles] = run;
-    __syncthreads();
     uint64_t byte_run = 16;
     const bool dgc = kind == GC_KIND_DGC;
     for (int r = 0; r < P.nseg; r += kBlock) {
@@ -309,12 +316,12 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
     const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, 2048));
     const uint64_t cap = in->cap;
-    pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w);
-    pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w);
-    pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
-                                                 out_bytes, w);
-    pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->idx, in->val, in->seg_off, MAX,
-                                                   out, w);
+    GC_LAUNCH("pack_tiles", stream, pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w));
+    GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
+    GC_LAUNCH("pack_layout", stream, pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
+                                                 out_bytes, w));
+    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->idx, in->val, in->seg_off, MAX,
+                                                   out, w));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_pack launch");
     return GC_OK;

@@ -23,21 +23,9 @@ gc_status hip_error(hipError_t e, const char *what) {
 
 void clear_error() { g_last_error.clear(); }
 
-__global__ void zero_words_kernel(uint32_t *p, size_t words) {
-    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (; i < words; i += stride) p[i] = 0u;
-}
-
-void zero_words(uint32_t *p, size_t words, hipStream_t s) {
-    if (words == 0) return;
-    unsigned grid = static_cast<unsigned>(std::min<size_t>((words + kBlock - 1) / kBlock, 2048));
-    zero_words_kernel<<<grid, kBlock, 0, s>>>(p, words);
-}
-
 // Layout of the per-device table blob.
 struct BlobLayout {
-    size_t seg, dchunk, achunk, start, total;
+    size_t seg, dchunk, achunk, start, bgroup, total;
 };
 
 static BlobLayout blob_layout(const gc_plan *p) {
@@ -53,6 +41,7 @@ static BlobLayout blob_layout(const gc_plan *p) {
     L.dchunk = take(sizeof(uint32_t) * p->dchunk_seg.size());
     L.achunk = take(sizeof(uint32_t) * p->achunk_seg.size());
     L.start = take(sizeof(uint64_t) * p->seg_start.size());
+    L.bgroup = take(sizeof(uint32_t) * p->bgroup_seg.size());
     L.total = std::max<size_t>(o, 256);
     return L;
 }
@@ -79,6 +68,8 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
                         sizeof(uint32_t) * plan->achunk_seg.size());
             std::memcpy(host.data() + L.start, plan->seg_start.data(),
                         sizeof(uint64_t) * plan->seg_start.size());
+            std::memcpy(host.data() + L.bgroup, plan->bgroup_seg.data(),
+                        sizeof(uint32_t) * plan->bgroup_seg.size());
             e = hipMemcpy(blob, host.data(), L.total, hipMemcpyHostToDevice);
             if (e != hipSuccess) {
                 (void)hipFree(blob);
@@ -92,7 +83,9 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
     out->dchunk_seg = reinterpret_cast<const uint32_t *>(b + L.dchunk);
     out->achunk_seg = reinterpret_cast<const uint32_t *>(b + L.achunk);
     out->seg_start = reinterpret_cast<const uint64_t *>(b + L.start);
+    out->bgroup_seg = reinterpret_cast<const uint32_t *>(b + L.bgroup);
     out->nseg = plan->nseg;
+    out->nbgroup = plan->nbgroup;
     out->ndchunk = plan->ndchunk;
     out->nachunk = plan->nachunk;
     out->n_total = plan->n_total;
@@ -172,6 +165,9 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         d.anchunk = (g.length + d.achunk_len - 1) / d.achunk_len;
         d.bin0 = bin0;
         d.kbase = kbase;
+        d.bgroup0 = static_cast<uint32_t>(p->bgroup_seg.size());
+        d.nbgroup = (d.nbins + kBinGroup - 1) / kBinGroup;
+        for (uint32_t g2 = 0; g2 < d.nbgroup; ++g2) p->bgroup_seg.push_back(static_cast<uint32_t>(s));
         bin0 += d.nbins;
         kbase += g.k;
         for (uint32_t c = 0; c < d.dnchunk; ++c) p->dchunk_seg.push_back(static_cast<uint32_t>(s));
@@ -181,6 +177,7 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     }
     p->ndchunk = static_cast<uint32_t>(p->dchunk_seg.size());
     p->nachunk = static_cast<uint32_t>(p->achunk_seg.size());
+    p->nbgroup = static_cast<uint32_t>(p->bgroup_seg.size());
     *out = p;
     return GC_OK;
 }

@@ -259,6 +259,25 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
                           uint64_t step, float *scales, uint8_t *codes,
                           hipStream_t stream);
 
+/* ----------------------------------------------------------- measurement */
+/*
+ * Kernel timing for measurement tools (off by default).  While enabled, each
+ * launch of a selected kernel is bracketed by a pair of HIP events recorded
+ * on the caller's stream; nothing else changes.
+ *   kernels : comma-separated kernel names ("dgc_update,ada_apply"), "*" for
+ *             all, NULL or "" to disable.  Names: dgc_norm, dgc_prep,
+ *             dgc_update, dgc_select, dgc_stage, dgc_refine, dgc_count,
+ *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
+ *             ada_apply,
+ *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,
+ *             decode, dcd.
+ * gc_timing_take waits for the recorded events of one kernel and returns the
+ * summed duration in milliseconds and the number of launches, then forgets
+ * them.  Host-thread safe; not for use while a stream is being captured.
+ */
+gc_status gc_timing_enable(const char *kernels);
+gc_status gc_timing_take(const char *kernel, double *total_ms, uint64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif
