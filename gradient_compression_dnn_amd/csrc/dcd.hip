@@ -17,6 +17,14 @@ namespace gc {
 
 namespace {
 
+// Full 64-bit product of two u32 in one VALU op (v_mad_u64_u32 with a zero
+// addend); on gfx950 this is faster than the separate low and high multiplies.
+__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) {
+    uint64_t r, carry;
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "v"(b));
+    return r;
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products, the
 // key advanced by the Weyl constants between rounds.
@@ -25,9 +33,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t hi0 = __umulhi(kM0, c.x), lo0 = kM0 * c.x;
-        const uint32_t hi1 = __umulhi(kM1, c.z), lo1 = kM1 * c.z;
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        const uint64_t p0 = mul_wide(kM0, c.x);
+        const uint64_t p1 = mul_wide(kM1, c.z);
+        c = make_uint4(uint32_t(p1 >> 32) ^ c.y ^ k0, uint32_t(p1), uint32_t(p0 >> 32) ^ c.w ^ k1,
+                       uint32_t(p0));
         k0 += kW0;
         k1 += kW1;
     }
@@ -37,20 +46,21 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 template <bool kAligned>
 __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may alias xo
                                                      const float *__restrict__ xh, float *xo,
-                                                     uint64_t n, int bits, int blog2,
+                                                     uint32_t n, int bits, int blog2,
                                                      uint32_t k0, uint32_t k1, uint64_t step,
                                                      float *__restrict__ scales,
                                                      uint8_t *__restrict__ codes) {
-    const uint64_t base = uint64_t(blockIdx.x) * kChunk;
+    const uint32_t base = blockIdx.x * uint32_t(kChunk);
     const uint32_t bucket = 1u << blog2;
     const int lanes_per_bucket = bucket >= 4 * kWave ? kWave : int(bucket / 4);
     __shared__ uint32_t smax[kChunk / 4];  // up to 1024 buckets of 4
+    __shared__ float sinv[kChunk / 4], sstep[kChunk / 4];
     const uint32_t nbk = kChunk >> blog2;
     for (uint32_t b = threadIdx.x; b < nbk; b += kBlock) smax[b] = 0u;
     float xv[kRows][4], zv[kRows][4];
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
-        const uint64_t i0 = base + uint64_t(j) * (4 * kBlock) + 4u * threadIdx.x;
+        const uint32_t i0 = base + row_elem(j);
         if (kAligned && i0 + 3 < n) {
             float4 a = *reinterpret_cast<const float4 *>(x + i0);
             float4 h = *reinterpret_cast<const float4 *>(xh + i0);
@@ -81,27 +91,32 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
             uint32_t o = __shfl_xor(m, d, kWave);
             m = m > o ? m : o;
         }
-        const uint32_t e0 = uint32_t(j) * (4 * kBlock) + 4u * threadIdx.x;
-        if ((lane_id() & (lanes_per_bucket - 1)) == 0) atomicMax(&smax[e0 >> blog2], m);
+        if ((lane_id() & (lanes_per_bucket - 1)) == 0) atomicMax(&smax[row_elem(j) >> blog2], m);
     }
     __syncthreads();
     const uint32_t L = (1u << (bits - 1)) - 1u;
     const float Lf = static_cast<float>(L);
+    // per bucket: inv = fl(L / s_b), step = fl(s_b / L), once
+    for (uint32_t b = threadIdx.x; b < nbk; b += kBlock) {
+        const float sb = dev_u2f(smax[b]);
+        sinv[b] = sb > 0.0f ? Lf / sb : 0.0f;
+        sstep[b] = sb > 0.0f ? sb / Lf : 0.0f;
+    }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
-        const uint32_t e0 = uint32_t(j) * (4 * kBlock) + 4u * threadIdx.x;
-        const uint64_t i0 = base + e0;
+        const uint32_t e0 = row_elem(j);
+        const uint32_t i0 = base + e0;
         if (i0 >= n) continue;
-        const float sb = dev_u2f(smax[e0 >> blog2]);
-        const uint64_t q = i0 >> 2;
-        const uint4 r = philox4x32_10(make_uint4(uint32_t(q), uint32_t(q >> 32), uint32_t(step),
-                                                 uint32_t(step >> 32)),
-                                      k0, k1);
+        const uint32_t bk = e0 >> blog2;
+        const float sb = dev_u2f(smax[bk]);
+        const float inv = sinv[bk];
+        const float stepq = sstep[bk];
+        const uint32_t q = i0 >> 2;
+        const uint4 r = philox4x32_10(make_uint4(q, 0u, uint32_t(step), uint32_t(step >> 32)), k0, k1);
         const uint32_t words[4] = {r.x, r.y, r.z, r.w};
         uint32_t code[4];
         float out[4];
-        const float inv = sb > 0.0f ? Lf / sb : 0.0f;
-        const float stepq = sb > 0.0f ? sb / Lf : 0.0f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint32_t level = 0;
@@ -152,8 +167,8 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
             }
         }
     }
-    const uint64_t b_first = base >> blog2;
-    const uint64_t nb_total = (n + bucket - 1) >> blog2;
+    const uint32_t b_first = base >> blog2;
+    const uint32_t nb_total = static_cast<uint32_t>((uint64_t(n) + bucket - 1) >> blog2);
     for (uint32_t b = threadIdx.x; b < nbk; b += kBlock)
         if (b_first + b < nb_total) scales[b_first + b] = dev_u2f(smax[b]);
 }
@@ -174,7 +189,8 @@ extern "C" gc_status gc_dcd_compress(const float *x, const float *x_half, float 
     if (bucket == 0) return set_error(GC_EINVAL, "gc_dcd_compress: bucket must be >= 1");
     if (bucket < 4 || bucket > uint32_t(kChunk) || (bucket & (bucket - 1)))
         return set_error(GC_ENOTSUP, "gc_dcd_compress: bucket must be a power of two in [4, 4096]");
-    if (n >= (uint64_t(1) << 32)) return set_error(GC_ERANGE, "gc_dcd_compress: n must be < 2^32");
+    if (n > (uint64_t(1) << 32) - 2 * uint64_t(kChunk))
+        return set_error(GC_ERANGE, "gc_dcd_compress: n must be <= 2^32 - 8192");
     if (reinterpret_cast<uintptr_t>(codes) % 4)
         return set_error(GC_EINVAL, "gc_dcd_compress: codes must be 4-byte aligned");
     if (x_half == x_out && x_half != x)
@@ -188,10 +204,10 @@ extern "C" gc_status gc_dcd_compress(const float *x, const float *x_half, float 
     const unsigned grid = grid_1d(n, kChunk);
     const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
     if (aligned)
-        GC_LAUNCH("dcd", stream, dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+        GC_LAUNCH("dcd", stream, dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, static_cast<uint32_t>(n), bits, blog2, k0, k1, step,
                                                       scales, codes));
     else
-        GC_LAUNCH("dcd", stream, dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, n, bits, blog2, k0, k1, step,
+        GC_LAUNCH("dcd", stream, dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, static_cast<uint32_t>(n), bits, blog2, k0, k1, step,
                                                        scales, codes));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dcd_compress launch");

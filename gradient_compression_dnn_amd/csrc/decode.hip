@@ -43,37 +43,42 @@ DecWs dec_layout(const gc_plan *p, void *base, size_t *bytes) {
     return w;
 }
 
-// Segment holding flat index i (the last segment starting at or before it).
-__device__ __forceinline__ int segment_of(const PlanDev &P, uint32_t i) {
-    int lo = 0, hi = P.nseg - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) / 2;
-        if (P.seg_start[mid] <= i) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
+// Walks ascending flat indices forward through the segments, keeping the
+// current segment's bounds in registers; the table of segment starts is read
+// from LDS when it fits.  Out-of-range or descending indices are clamped
+// into the plan (malformed input stays in bounds).
+constexpr int kLdsSegs = 4096;
 
-// Walks ascending indices forward through the segments, keeping the current
-// segment's bounds in registers.  Out-of-range or descending indices are
-// clamped into the plan (malformed input stays in bounds).
 struct SegCursor {
     const PlanDev *P;
+    const uint32_t *start;  // segment starts (LDS copy or plan table)
     int s;
     uint64_t off, next;
     uint32_t dchunk0, dnchunk;
+    __device__ uint64_t seg_start(int i) const {
+        return start ? uint64_t(start[i]) : P->seg_start[i];
+    }
     __device__ void load(int seg) {
         s = seg;
         const SegDev d = P->seg[s];
         off = d.off;
         dchunk0 = d.dchunk0;
         dnchunk = d.dnchunk;
-        next = s + 1 < P->nseg ? P->seg_start[s + 1] : ~uint64_t(0);
+        next = s + 1 < P->nseg ? seg_start(s + 1) : ~uint64_t(0);
+    }
+    __device__ void find(uint32_t i) {
+        int lo = 0, hi = P->nseg - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) / 2;
+            if (seg_start(mid) <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        load(lo);
     }
     __device__ uint32_t chunk(uint32_t i) {
         if (i >= next) {
             int t = s;
-            while (t + 1 < P->nseg && P->seg_start[t + 1] <= i) ++t;
+            while (t + 1 < P->nseg && seg_start(t + 1) <= i) ++t;
             load(t);
         }
         uint64_t rel = i >= off ? (i - off) >> kChunkLog2 : 0;
@@ -82,31 +87,59 @@ struct SegCursor {
     }
 };
 
-constexpr uint32_t kRun = 8;          // entries per thread and pass
+constexpr uint32_t kRun = 8;           // entries per thread in the index pass
 constexpr uint32_t kSparseChunk = 32;  // up to this many entries: no LDS accumulator
 
+// start[k][c] = first entry of message k at or after chunk c: entry j writes
+// it for every chunk after its predecessor's chunk and up to its own.
 __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTable m, DecWs w) {
     const int k = blockIdx.y;
     const uint32_t n = msg_count(m, k);
+    const uint64_t base = (uint64_t(blockIdx.x) * kBlock + threadIdx.x) * kRun;
+    if (uint64_t(blockIdx.x) * kBlock * kRun > n) return;
+    __shared__ uint32_t starts[kLdsSegs];
+    const bool in_lds = P.nseg <= kLdsSegs;
+    if (in_lds) {
+        for (int i = threadIdx.x; i < P.nseg; i += kBlock) starts[i] = static_cast<uint32_t>(P.seg_start[i]);
+        __syncthreads();
+    }
+    if (base > n) return;
     const uint32_t *idx = m.idx[k];
     uint32_t *start = w.start + size_t(k) * (P.ndchunk + 1);
-    const uint64_t stride = uint64_t(gridDim.x) * kBlock * kRun;
-    for (uint64_t base = (uint64_t(blockIdx.x) * kBlock + threadIdx.x) * kRun; base <= n;
-         base += stride) {
-        SegCursor cur;
-        cur.P = &P;
-        cur.load(segment_of(P, base > 0 ? idx[base - 1] : (n > 0 ? idx[0] : 0u)));
-        int64_t cp = base > 0 ? int64_t(cur.chunk(idx[base - 1])) : -1;
-        for (uint32_t q = 0; q < kRun; ++q) {
-            const uint64_t j = base + q;
-            if (j > n) break;
-            const int64_t cj = j < n ? int64_t(cur.chunk(idx[j])) : int64_t(P.ndchunk);
+    // all of this thread's indices (and its predecessor's) in flight at once
+    uint32_t id[kRun + 1];
+#pragma unroll
+    for (uint32_t q = 0; q <= kRun; ++q) {
+        const uint64_t j = base + q;  // slot q holds entry j - 1
+        id[q] = (j >= 1 && j - 1 < n) ? idx[j - 1] : 0u;
+    }
+    SegCursor cur;
+    cur.P = &P;
+    cur.start = in_lds ? starts : nullptr;
+    cur.find(base > 0 ? id[0] : (n > 0 ? idx[0] : 0u));
+    int64_t cp = base > 0 ? int64_t(cur.chunk(id[0])) : -1;
+#pragma unroll
+    for (uint32_t q = 0; q < kRun; ++q) {
+        const uint64_t j = base + q;
+        if (j <= n) {
+            const int64_t cj = j < n ? int64_t(cur.chunk(id[q + 1])) : int64_t(P.ndchunk);
             for (int64_t c = cp + 1; c <= cj; ++c) start[c] = static_cast<uint32_t>(j);
             if (cj > cp) cp = cj;
         }
     }
 }
 
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// One workgroup per output chunk.  Lane k (< K) of every wave loads message
+// k's entry range for the chunk, so every wave sees the same entry total and
+// picks the same path without a workgroup vote.  The average divides by K;
+// for K a power of two that is the same real number as multiplying by 1/K,
+// so the exact product is used (identical correctly rounded result).
 __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, int K, DecWs w,
                                                         float *__restrict__ dense, int avg,
                                                         int accumulate) {
@@ -119,62 +152,49 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
     const uint32_t cnt = rem < uint32_t(kChunk) ? rem : uint32_t(kChunk);
     float *dp = dense + lo;
     const bool vec = is_aligned16(dp);
-    __shared__ uint32_t range[2 * GC_MAX_MESSAGES];
     __shared__ float acc[kChunk];
-    bool mine = false;
-    if (threadIdx.x < uint32_t(K)) {
-        const int k = threadIdx.x;
-        const uint32_t n = msg_count(m, k);
-        const uint32_t *st = w.start + size_t(k) * (P.ndchunk + 1);
-        const uint32_t a = min(st[c], n);
-        const uint32_t b = min(max(st[c + 1], a), n);
-        range[2 * k] = a;
-        range[2 * k + 1] = b;
-        mine = b > a;
+    const int lane = lane_id();
+    uint32_t a = 0, b = 0;
+    if (lane < K) {
+        const uint32_t nk = msg_count(m, lane);
+        const uint32_t *st = w.start + size_t(lane) * (P.ndchunk + 1);
+        a = min(st[c], nk);
+        b = min(max(st[c + 1], a), nk);
     }
-    const bool any = __syncthreads_or(mine);
-    __shared__ uint32_t total_entries;
-    if (threadIdx.x == 0) {
-        uint32_t t = 0;
-        for (int k = 0; k < K; ++k) t += range[2 * k + 1] - range[2 * k];
-        total_entries = t;
-    }
-    __syncthreads();
-    const float fk = static_cast<float>(K);
+    const uint32_t total = wave_sum(b - a);  // identical in every wave
     float v[kRows][4];
 #pragma unroll
     for (int j = 0; j < kRows; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[j][q] = 0.0f;
-    if (any && total_entries <= kSparseChunk) {
-        // few entries: every thread scans them all (broadcast loads), in
+    if (total != 0 && total <= kSparseChunk) {
+        // few entries: every thread reads them all (broadcast loads), in
         // message order, and adds those that fall on its own elements
         for (int k = 0; k < K; ++k) {
-            const uint32_t a = range[2 * k], b = range[2 * k + 1];
-            for (uint32_t i = a; i < b; ++i) {
+            const uint32_t ak = __shfl(a, k, kWave), bk = __shfl(b, k, kWave);
+            for (uint32_t i = ak; i < bk; ++i) {
                 const uint32_t id = m.idx[k][i];
                 const uint64_t r = uint64_t(id) - lo;
                 if (id < lo || r >= cnt) continue;
                 const uint32_t e = static_cast<uint32_t>(r);
+                if (((e >> 2) & (kBlock - 1)) != threadIdx.x) continue;
+                const float x = m.val[k][i];
                 const uint32_t j = e >> 10, q = e & 3u;
-                if (((e >> 2) & (kBlock - 1)) == threadIdx.x) {
-                    const float x = m.val[k][i];
 #pragma unroll
-                    for (int jj = 0; jj < kRows; ++jj)
+                for (int jj = 0; jj < kRows; ++jj)
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq)
-                            if (uint32_t(jj) == j && uint32_t(qq) == q) v[jj][qq] = v[jj][qq] + x;
-                }
+                    for (int qq = 0; qq < 4; ++qq)
+                        if (uint32_t(jj) == j && uint32_t(qq) == q) v[jj][qq] = v[jj][qq] + x;
             }
         }
-    } else if (any) {
+    } else if (total != 0) {
         for (int e = threadIdx.x; e < kChunk; e += kBlock) acc[e] = 0.0f;
         __syncthreads();
         for (int k = 0; k < K; ++k) {
-            const uint32_t a = range[2 * k], b = range[2 * k + 1];
+            const uint32_t ak = __shfl(a, k, kWave), bk = __shfl(b, k, kWave);
             const uint32_t *idx = m.idx[k];
             const float *val = m.val[k];
-            for (uint32_t i = a + threadIdx.x; i < b; i += kBlock) {
+            for (uint32_t i = ak + threadIdx.x; i < bk; i += kBlock) {
                 const uint32_t id = idx[i];
                 const uint64_t r = uint64_t(id) - lo;
                 if (id >= lo && r < cnt) acc[r] = acc[r] + val[i];
@@ -186,12 +206,15 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[j][q] = acc[row_elem(j) + q];
     }
+    const bool pow2 = (K & (K - 1)) == 0;
+    const float fk = static_cast<float>(K);
+    const float inv = 1.0f / fk;  // exact for a power of two
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
         const uint32_t e0 = row_elem(j);
-        if (avg) {
+        if (avg && K > 1) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[j][q] = v[j][q] / fk;
+            for (int q = 0; q < 4; ++q) v[j][q] = pow2 ? v[j][q] * inv : v[j][q] / fk;
         }
         if (accumulate) {
             float d[4];
@@ -246,8 +269,8 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     DecWs w = dec_layout(plan, ws, nullptr);
     uint64_t max_entries = 0;
     for (int k = 0; k < K; ++k) max_entries = std::max<uint64_t>(max_entries, msgs[k].cap);
-    unsigned gx = static_cast<unsigned>(
-        std::min<uint64_t>((max_entries + kBlock * kRun) / (kBlock * kRun) + 1, 1024));
+    // one pass: enough workgroups for the largest capacity (extra ones exit)
+    unsigned gx = static_cast<unsigned>((max_entries + kBlock * kRun) / (kBlock * kRun) + 1);
     GC_LAUNCH("decode_index", stream, decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w));
     GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
                                                         accumulate != 0));

@@ -82,6 +82,27 @@ __device__ __forceinline__ ChunkInfo chunk_info(const PlanDev &P, uint32_t c) {
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return dev_f2u(v) & 0x7FFFFFFFu; }
 
+// Chunk geometry with the segment record cached across consecutive chunks
+// (a persistent workgroup's chunks mostly share a segment).
+struct ChunkWalker {
+    uint32_t s = 0;
+    SegDev seg{};
+    __device__ ChunkInfo at(const PlanDev &P, uint32_t c) {
+        if (c < seg.dchunk0 || c >= seg.dchunk0 + seg.dnchunk) {
+            s = P.dchunk_seg[c];
+            seg = P.seg[s];
+        }
+        ChunkInfo ci;
+        ci.s = s;
+        ci.seg = seg;
+        const uint32_t pos = c - seg.dchunk0;
+        ci.lo = seg.off + (uint64_t(pos) << kChunkLog2);
+        const uint32_t rem = seg.len - (pos << kChunkLog2);
+        ci.cnt = rem < uint32_t(kChunk) ? rem : uint32_t(kChunk);
+        return ci;
+    }
+};
+
 // Persistent dense kernels: workgroup b walks chunks [first, last), a
 // contiguous range, so consecutive chunks mostly share a segment.
 __device__ __forceinline__ void chunk_range(uint32_t nchunk, uint32_t *first, uint32_t *last) {
@@ -102,10 +123,11 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
     chunk_range(P.ndchunk, &c0, &c1);
     __shared__ double node[kChunk / 4];  // level-2 nodes of the chunk, in order
     float cur[kRows][4], nxt[kRows][4];
+    ChunkWalker walk;
     ChunkInfo ci;
     bool vec = false;
     if (c0 < c1) {
-        ci = chunk_info(P, c0);
+        ci = walk.at(P, c0);
         vec = is_aligned16(G + ci.lo);
 #pragma unroll
         for (int j = 0; j < kRows; ++j) load4(G + ci.lo, row_elem(j), ci.cnt, vec, cur[j]);
@@ -114,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
         ChunkInfo cn;
         bool vn = false;
         if (c + 1 < c1) {
-            cn = chunk_info(P, c + 1);
+            cn = walk.at(P, c + 1);
             vn = is_aligned16(G + cn.lo);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) load4(G + cn.lo, row_elem(j), cn.cnt, vn, nxt[j]);
@@ -179,7 +201,8 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
     for (int i = threadIdx.x; i < kHist1; i += kBlock) hist[i] = 0u;
     if (c0 >= c1) return;
     float g[kRows][4], u[kRows][4], v[kRows][4];
-    ChunkInfo ci = chunk_info(P, c0);
+    ChunkWalker walk;
+    ChunkInfo ci = walk.at(P, c0);
     bool vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
@@ -211,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
         const uint32_t s_done = ci.s;
         const bool more = c + 1 < c1;
         if (more) {
-            ci = chunk_info(P, c + 1);
+            ci = walk.at(P, c + 1);
             vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) {
@@ -270,59 +293,57 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
 }
 
 // ----------------------------------------------------------------- stage
+// One wave per chunk: lane l holds elements [256 r + 4 l, +4) for rows
+// r = 0..15, so 16 KB of V is in flight per wave and the ordered compaction
+// needs only ballots (rank = running count + lanes below + within lane); no
+// LDS, no workgroup barrier.
+constexpr int kWaveRows = kChunk / (4 * kWave);
+
 __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const float *__restrict__ V,
                                                            DgcWs w) {
-    uint32_t c0, c1;
-    chunk_range(P.ndchunk, &c0, &c1);
-    if (c0 >= c1) return;
-    float v[kRows][4], nv[kRows][4];
-    ChunkInfo ci = chunk_info(P, c0);
+    const uint32_t c = blockIdx.x * kWaves + wave_id();
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t lo = rec.x, cnt = rec.y, s = rec.z;
+    const float *vp = V + lo;
+    const bool vec = is_aligned16(vp);
+    const int lane = lane_id();
+    float v[kWaveRows][4];
 #pragma unroll
-    for (int j = 0; j < kRows; ++j) load4(V + ci.lo, row_elem(j), ci.cnt, is_aligned16(V + ci.lo), v[j]);
-    for (uint32_t c = c0; c < c1; ++c) {
-        ChunkInfo cn;
-        const bool more = c + 1 < c1;
-        if (more) {
-            cn = chunk_info(P, c + 1);
-            const bool vn = is_aligned16(V + cn.lo);
+    for (int r = 0; r < kWaveRows; ++r) load4(vp, r * (4 * kWave) + 4u * lane, cnt, vec, v[r]);
+    const uint32_t d1 = w.st[s].d1;
+    uint32_t *h2 = w.hist2 + size_t(s) * kHist2;
+    uint32_t run = 0;  // wave-uniform count of entries staged so far
 #pragma unroll
-            for (int j = 0; j < kRows; ++j) load4(V + cn.lo, row_elem(j), cn.cnt, vn, nv[j]);
+    for (int r = 0; r < kWaveRows; ++r) {
+        const uint32_t e0 = r * (4 * kWave) + 4u * lane;
+        bool flag[4];
+        uint32_t before = 0, row_total = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool in = e0 + q < cnt;
+            const uint32_t key = mag_key(v[r][q]);
+            const uint32_t dig1 = key >> (kDigit2Bits + kDigit3Bits);
+            flag[q] = in && dig1 >= d1;
+            if (in && dig1 == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            const uint64_t m = __ballot(flag[q]);
+            before += lane_rank(m);
+            row_total += static_cast<uint32_t>(__popcll(m));
         }
-        const uint32_t d1 = w.st[ci.s].d1;
-        uint32_t *h2 = w.hist2 + size_t(ci.s) * kHist2;
-        bool flag[kRows][4];
-        uint32_t pos[kRows][4];
-#pragma unroll
-        for (int j = 0; j < kRows; ++j) {
+        if (row_total) {
+            uint32_t slot = lo + run + before;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const bool in = row_elem(j) + q < ci.cnt;
-                const uint32_t key = mag_key(v[j][q]);
-                const uint32_t dig1 = key >> (kDigit2Bits + kDigit3Bits);
-                flag[j][q] = in && dig1 >= d1;
-                if (in && dig1 == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
-            }
-        }
-        const uint32_t total = block_compact4(flag, pos);
-#pragma unroll
-        for (int j = 0; j < kRows; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (flag[j][q]) {
-                    w.sidx[ci.lo + pos[j][q]] = static_cast<uint32_t>(ci.lo + row_elem(j) + q);
-                    w.sval[ci.lo + pos[j][q]] = v[j][q];
+                if (flag[q]) {
+                    w.sidx[slot] = lo + e0 + q;
+                    w.sval[slot] = v[r][q];
+                    ++slot;
                 }
             }
         }
-        if (threadIdx.x == 0) w.ccount[c] = total;
-        if (more) {
-            ci = cn;
-#pragma unroll
-            for (int j = 0; j < kRows; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[j][q] = nv[j][q];
-        }
+        run += row_total;
     }
+    if (lane == 0) w.ccount[c] = run;
 }
 
 // ---------------------------------------------------------------- refine
@@ -515,7 +536,7 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<<<pgrid, kBlock, 0, stream>>>(P, G, U, V, momentum, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<pgrid, kBlock, 0, stream>>>(P, V, w));
+    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, V, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w));

@@ -53,8 +53,16 @@ struct SegDev {
 constexpr int kBinGroupLog2 = 12;  // bins per group of the scale's pairwise tree
 constexpr uint32_t kBinGroup = 1u << kBinGroupLog2;
 
+// One chunk of a segment, fetched with a single 16-byte load:
+//   x = first flat element, y = elements, z = segment, w = aux (AdaComp:
+//   first bin of the chunk in the plan-wide bin array; DGC: chunk number
+//   inside the segment).
+using ChunkRec = uint4;
+
 struct PlanDev {
     const SegDev *seg;          // [nseg]
+    const ChunkRec *dchunk_rec; // [ndchunk]
+    const ChunkRec *achunk_rec; // [nachunk]
     const uint32_t *dchunk_seg; // [ndchunk]
     const uint32_t *achunk_seg; // [nachunk]
     const uint64_t *seg_start;  // [nseg] offsets, for searching an index
@@ -81,6 +89,8 @@ struct gc_plan {
     std::vector<uint32_t> achunk_seg;
     std::vector<uint64_t> seg_start;
     std::vector<uint32_t> bgroup_seg;
+    std::vector<gc::ChunkRec> dchunk_rec;
+    std::vector<gc::ChunkRec> achunk_rec;
     // device copies, one per device, uploaded on first use
     std::mutex mu;
     std::vector<std::pair<int, void *>> dev_blob;

@@ -3,11 +3,11 @@
 // zero-run lengths; AdaComp messages carry only a sign per entry plus one
 // layer scale, so their 16-bit code holds the sign in bit 15.
 //
-// Entries of a segment are processed in tiles of 1024.  A run longer than
-// the code can hold is split with escapes; an entry's slot in its block is
-// its rank in the segment plus the escapes emitted before it, so the escape
-// counts are scanned per tile (count), across tiles (layout) and inside a
-// tile (write).
+// Entries of a segment are processed in tiles of 4096 (16 per thread).  A run longer than the code can hold is split with escapes; an
+// entry's slot in its block is its rank in the segment plus the escapes
+// emitted before it.  Escapes are rare (a gap of 32767+ unsent elements), so
+// the count pass adds per-segment totals with integer atomics, and the write
+// pass scans escape counts only in segments and tiles that have any.
 #include <algorithm>
 
 #include "gc_internal.hpp"
@@ -16,12 +16,13 @@ namespace gc {
 
 namespace {
 
-constexpr uint32_t kTile = 1024;
+constexpr uint32_t kTile = 4096;
 constexpr uint32_t kPerThread = kTile / kBlock;
 
 struct PackWs {
     uint32_t *tile_base;  // [nseg + 1] first tile of each segment
-    uint32_t *tile_esc;   // [max_tiles] escapes per tile, then exclusive prefix
+    uint32_t *tile_esc;   // [max_tiles] escapes per tile
+    uint32_t *seg_esc;    // [nseg] escapes per segment
     uint64_t *blk_off;    // [nseg] byte offset of each block
     uint32_t *seg_E;      // [nseg]
     size_t max_tiles;
@@ -35,6 +36,7 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.max_tiles = tiles + 1;
     w.tile_base = c.take<uint32_t>(p->nseg + 1);
     w.tile_esc = c.take<uint32_t>(w.max_tiles + 1);
+    w.seg_esc = c.take<uint32_t>(p->nseg);
     w.blk_off = c.take<uint64_t>(p->nseg);
     w.seg_E = c.take<uint32_t>(p->nseg);
     if (bytes) *bytes = c.used + 256;
@@ -103,71 +105,78 @@ __global__ __launch_bounds__(kBlock) void pack_tiles_kernel(PlanDev P, int kind,
         if (s < nseg) v = (seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap) + kTile - 1) / kTile;
         uint32_t tot;
         uint32_t pre = block_exclusive_scan(v, &tot);
-        if (s < nseg) w.tile_base[s] = run + pre;
+        if (s < nseg) {
+            w.tile_base[s] = run + pre;
+            w.seg_esc[s] = 0u;
+        }
         run += tot;
     }
     if (threadIdx.x == 0) w.tile_base[nseg] = run;
 }
 
-__device__ __forceinline__ uint32_t tile_segment(const uint32_t *tile_base, int nseg, uint32_t t) {
-    // last s with tile_base[s] <= t
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) / 2;
-        if (tile_base[mid] <= t) lo = mid;
-        else hi = mid - 1;
+// Segment of tile t: the last s with tile_base[s] <= t.  Workgroups copy the
+// table to LDS once when it fits, so the searches cost no global round trips.
+constexpr int kLdsSegs = 4096;
+
+struct TileTable {
+    const uint32_t *tb;
+    int nseg;
+    __device__ void init(const uint32_t *tile_base, int n, uint32_t *lds) {
+        nseg = n;
+        if (n <= kLdsSegs) {
+            for (int i = threadIdx.x; i < n; i += kBlock) lds[i] = tile_base[i];
+            __syncthreads();
+            tb = lds;
+        } else {
+            tb = tile_base;
+        }
     }
-    return static_cast<uint32_t>(lo);
-}
+    __device__ uint32_t segment(uint32_t t) const {
+        int lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) / 2;
+            if (tb[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        return static_cast<uint32_t>(lo);
+    }
+};
 
 __global__ __launch_bounds__(kBlock) void pack_count_kernel(PlanDev P, int kind,
                                                             const uint32_t *__restrict__ idx,
                                                             const uint32_t *__restrict__ seg_off,
                                                             uint64_t cap, uint32_t MAX, PackWs w) {
     const uint32_t ntiles = w.tile_base[P.nseg];
+    if (blockIdx.x >= ntiles) return;
+    __shared__ uint32_t lds[kLdsSegs];
+    TileTable table;
+    table.init(w.tile_base, P.nseg, lds);
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const EntryCtx x = entry_ctx(P, seg_off, kind, cap, tile_segment(w.tile_base, P.nseg, t));
-        uint32_t j0 = x.first + (t - w.tile_base[x.s]) * kTile;
-        uint32_t esc = 0;
+    const EntryCtx x = entry_ctx(P, seg_off, kind, cap, table.segment(t));
+    const uint32_t j0 = x.first + (t - w.tile_base[x.s]) * kTile;
+    uint32_t esc = 0;
 #pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            uint32_t j = j0 + i * kBlock + threadIdx.x;
-            uint32_t gap;
-            if (j < x.end) esc += entry_escapes(idx, x, j, MAX, &gap);
-        }
-        uint32_t tot;
-        (void)block_exclusive_scan(esc, &tot);
-        if (threadIdx.x == 0) w.tile_esc[t] = tot;
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t j = j0 + i * kBlock + threadIdx.x;
+        uint32_t gap;
+        if (j < x.end) esc += entry_escapes(idx, x, j, MAX, &gap);
+    }
+    uint32_t tot;
+    (void)block_exclusive_scan(esc, &tot);
+    if (threadIdx.x == 0) {
+        w.tile_esc[t] = tot;
+        if (tot) atomicAdd(&w.seg_esc[x.s], tot);
+    }
     }
 }
 
-// One workgroup: scan escapes over all tiles, size every block, write the
+// One workgroup: size every block from its entries and escapes, write the
 // stream header, block headers and pads, and the stream length.
 __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind, uint64_t cap, uint32_t MAX,
                                                              const uint32_t *__restrict__ seg_off,
                                                              const float *__restrict__ seg_scale,
                                                              uint8_t *__restrict__ out,
                                                              uint64_t *__restrict__ out_bytes, PackWs w) {
-    const uint32_t ntiles = w.tile_base[P.nseg];
-    {
-        // exclusive scan of the tiles' escape counts: thread t owns a
-        // contiguous run of tiles, then one workgroup scan of the run sums
-        const uint32_t per = (ntiles + kBlock - 1) / kBlock;
-        const uint32_t t0 = threadIdx.x * per;
-        const uint32_t t1 = min(t0 + per, ntiles);
-        uint32_t sum = 0;
-        for (uint32_t t = t0; t < t1; ++t) sum += w.tile_esc[t];
-        uint32_t all;
-        uint32_t run = block_exclusive_scan(sum, &all);
-        for (uint32_t t = t0; t < t1; ++t) {
-            const uint32_t e = w.tile_esc[t];
-            w.tile_esc[t] = run;
-            run += e;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) w.tile_esc[ntiles] = all;
-        __syncthreads();
-    }
     uint64_t byte_run = 16;
     const bool dgc = kind == GC_KIND_DGC;
     for (int r = 0; r < P.nseg; r += kBlock) {
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind
             const SegDev sg = P.seg[s];
             const uint32_t maxe = seg_max_entries(sg, kind);
             cnt = seg_entries(seg_off, s, maxe, cap);
-            uint32_t esc = w.tile_esc[w.tile_base[s + 1]] - w.tile_esc[w.tile_base[s]];
+            uint32_t esc = w.seg_esc[s];
             // never more slots than gc_pack_bound reserves for the segment
             uint64_t cap_e = uint64_t(maxe) + sg.len / MAX + 1;
             uint64_t e64 = uint64_t(cnt) + esc;
@@ -217,51 +226,83 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
                                                             uint32_t MAX, uint8_t *__restrict__ out,
                                                             PackWs w) {
     const uint32_t ntiles = w.tile_base[P.nseg];
+    if (blockIdx.x >= ntiles) return;
     const bool dgc = kind == GC_KIND_DGC;
+    __shared__ uint32_t lds[kLdsSegs];
+    TileTable table;
+    table.init(w.tile_base, P.nseg, lds);
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const EntryCtx x = entry_ctx(P, seg_off, kind, cap, tile_segment(w.tile_base, P.nseg, t));
-        const uint32_t j0 = x.first + (t - w.tile_base[x.s]) * kTile;
-        const uint32_t esc_base = w.tile_esc[t] - w.tile_esc[w.tile_base[x.s]];
-        const uint32_t E = w.seg_E[x.s];
-        uint8_t *blk = out + w.blk_off[x.s];
-        uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
-        float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
-        // entries in index order: thread-contiguous groups keep the scan simple
-        uint32_t esc[kPerThread], gap[kPerThread];
-        uint32_t mine = 0;
+    const EntryCtx x = entry_ctx(P, seg_off, kind, cap, table.segment(t));
+    const uint32_t tile0 = w.tile_base[x.s];
+    const uint32_t j0 = x.first + (t - tile0) * kTile;
+    const uint32_t E = w.seg_E[x.s];
+    uint8_t *blk = out + w.blk_off[x.s];
+    uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
+    float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
+    // escapes emitted before this tile in its segment
+    uint32_t esc_base = 0;
+    if (w.seg_esc[x.s] != 0) {
+        uint32_t part = 0;
+        for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
+        uint32_t all;
+        (void)block_exclusive_scan(part, &all);
+        esc_base = all;
+    }
+    if (w.tile_esc[t] == 0) {
+        // no escape in this tile: entry j goes to slot (j - first) + esc_base
 #pragma unroll
         for (uint32_t i = 0; i < kPerThread; ++i) {
-            uint32_t j = j0 + threadIdx.x * kPerThread + i;
-            esc[i] = 0;
-            gap[i] = 0;
-            if (j < x.end) esc[i] = entry_escapes(idx, x, j, MAX, &gap[i]);
-            mine += esc[i];
-        }
-        uint32_t tot;
-        uint32_t pre = block_exclusive_scan(mine, &tot);
-        uint32_t before = esc_base + pre;
-#pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            uint32_t j = j0 + threadIdx.x * kPerThread + i;
+            const uint32_t j = j0 + i * kBlock + threadIdx.x;
             if (j >= x.end) continue;
-            uint32_t slot = (j - x.first) + before;
-            uint32_t g = gap[i];
-            for (uint32_t q = 0; q < esc[i] && slot < E; ++q) {
-                runs[slot] = static_cast<uint16_t>(MAX);
-                if (dgc) vals[slot] = 0.0f;
-                ++slot;
-                g -= MAX;
-            }
+            const uint32_t slot = (j - x.first) + esc_base;
             if (slot >= E) continue;  // only for malformed messages
+            uint32_t gap;
+            (void)entry_escapes(idx, x, j, MAX, &gap);
             if (dgc) {
-                runs[slot] = static_cast<uint16_t>(g);
+                runs[slot] = static_cast<uint16_t>(gap);
                 vals[slot] = val[j];
             } else {
-                uint16_t sign = (dev_f2u(val[j]) >> 31) ? 0x8000u : 0u;
-                runs[slot] = static_cast<uint16_t>(sign | g);
+                const uint16_t sign = (dev_f2u(val[j]) >> 31) ? 0x8000u : 0u;
+                runs[slot] = static_cast<uint16_t>(sign | gap);
             }
-            before += esc[i];
         }
+        continue;
+    }
+    // tile with escapes: thread-contiguous entries and an in-tile scan
+    uint32_t esc[kPerThread], gap[kPerThread];
+    uint32_t mine = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t j = j0 + threadIdx.x * kPerThread + i;
+        esc[i] = 0;
+        gap[i] = 0;
+        if (j < x.end) esc[i] = entry_escapes(idx, x, j, MAX, &gap[i]);
+        mine += esc[i];
+    }
+    uint32_t tot;
+    uint32_t before = esc_base + block_exclusive_scan(mine, &tot);
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t j = j0 + threadIdx.x * kPerThread + i;
+        if (j >= x.end) continue;
+        uint32_t slot = (j - x.first) + before;
+        uint32_t g = gap[i];
+        for (uint32_t q = 0; q < esc[i] && slot < E; ++q) {
+            runs[slot] = static_cast<uint16_t>(MAX);
+            if (dgc) vals[slot] = 0.0f;
+            ++slot;
+            g -= MAX;
+        }
+        if (slot >= E) continue;  // only for malformed messages
+        if (dgc) {
+            runs[slot] = static_cast<uint16_t>(g);
+            vals[slot] = val[j];
+        } else {
+            const uint16_t sign = (dev_f2u(val[j]) >> 31) ? 0x8000u : 0u;
+            runs[slot] = static_cast<uint16_t>(sign | g);
+        }
+        before += esc[i];
+    }
     }
 }
 
@@ -314,7 +355,7 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     if (st != GC_OK) return st;
     PackWs w = pack_layout(plan, ws, nullptr);
     const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
-    const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, 2048));
+    const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kPersistentBlocks));
     const uint64_t cap = in->cap;
     GC_LAUNCH("pack_tiles", stream, pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w));
     GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));

@@ -25,7 +25,7 @@ void clear_error() { g_last_error.clear(); }
 
 // Layout of the per-device table blob.
 struct BlobLayout {
-    size_t seg, dchunk, achunk, start, bgroup, total;
+    size_t seg, dchunk, achunk, start, bgroup, drec, arec, total;
 };
 
 static BlobLayout blob_layout(const gc_plan *p) {
@@ -42,6 +42,8 @@ static BlobLayout blob_layout(const gc_plan *p) {
     L.achunk = take(sizeof(uint32_t) * p->achunk_seg.size());
     L.start = take(sizeof(uint64_t) * p->seg_start.size());
     L.bgroup = take(sizeof(uint32_t) * p->bgroup_seg.size());
+    L.drec = take(sizeof(ChunkRec) * p->dchunk_rec.size());
+    L.arec = take(sizeof(ChunkRec) * p->achunk_rec.size());
     L.total = std::max<size_t>(o, 256);
     return L;
 }
@@ -70,6 +72,10 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
                         sizeof(uint64_t) * plan->seg_start.size());
             std::memcpy(host.data() + L.bgroup, plan->bgroup_seg.data(),
                         sizeof(uint32_t) * plan->bgroup_seg.size());
+            std::memcpy(host.data() + L.drec, plan->dchunk_rec.data(),
+                        sizeof(ChunkRec) * plan->dchunk_rec.size());
+            std::memcpy(host.data() + L.arec, plan->achunk_rec.data(),
+                        sizeof(ChunkRec) * plan->achunk_rec.size());
             e = hipMemcpy(blob, host.data(), L.total, hipMemcpyHostToDevice);
             if (e != hipSuccess) {
                 (void)hipFree(blob);
@@ -84,6 +90,8 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
     out->achunk_seg = reinterpret_cast<const uint32_t *>(b + L.achunk);
     out->seg_start = reinterpret_cast<const uint64_t *>(b + L.start);
     out->bgroup_seg = reinterpret_cast<const uint32_t *>(b + L.bgroup);
+    out->dchunk_rec = reinterpret_cast<const ChunkRec *>(b + L.drec);
+    out->achunk_rec = reinterpret_cast<const ChunkRec *>(b + L.arec);
     out->nseg = plan->nseg;
     out->nbgroup = plan->nbgroup;
     out->ndchunk = plan->ndchunk;
@@ -170,8 +178,21 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         for (uint32_t g2 = 0; g2 < d.nbgroup; ++g2) p->bgroup_seg.push_back(static_cast<uint32_t>(s));
         bin0 += d.nbins;
         kbase += g.k;
-        for (uint32_t c = 0; c < d.dnchunk; ++c) p->dchunk_seg.push_back(static_cast<uint32_t>(s));
-        for (uint32_t c = 0; c < d.anchunk; ++c) p->achunk_seg.push_back(static_cast<uint32_t>(s));
+        for (uint32_t c = 0; c < d.dnchunk; ++c) {
+            p->dchunk_seg.push_back(static_cast<uint32_t>(s));
+            const uint32_t first = c * uint32_t(kChunk);
+            const uint32_t cnt = std::min<uint32_t>(uint32_t(kChunk), g.length - first);
+            p->dchunk_rec.push_back(make_uint4(static_cast<uint32_t>(g.offset + first), cnt,
+                                               static_cast<uint32_t>(s), c));
+        }
+        for (uint32_t c = 0; c < d.anchunk; ++c) {
+            p->achunk_seg.push_back(static_cast<uint32_t>(s));
+            const uint32_t first = c * d.achunk_len;
+            const uint32_t cnt = std::min<uint32_t>(d.achunk_len, g.length - first);
+            p->achunk_rec.push_back(make_uint4(static_cast<uint32_t>(g.offset + first), cnt,
+                                               static_cast<uint32_t>(s),
+                                               d.bin0 + c * (d.achunk_len / g.bin_len)));
+        }
         p->seg[s] = d;
         p->seg_start[s] = g.offset;
     }

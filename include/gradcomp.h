@@ -252,7 +252,7 @@ gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_sparse *msgs,
  *   codes must be 4-byte aligned.
  * Errors: GC_EINVAL (bits not 4 or 8, bucket 0, null, misaligned codes),
  *         GC_ENOTSUP (bucket not a power of two in [4, 4096]),
- *         GC_ERANGE (n >= 2^32).
+ *         GC_ERANGE (n > 2^32 - 8192).
  */
 gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
                           uint64_t n, int bits, uint32_t bucket, uint64_t seed,
