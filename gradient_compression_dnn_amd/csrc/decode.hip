@@ -90,12 +90,17 @@ struct SegCursor {
 constexpr uint32_t kRun = 8;           // entries per thread in the index pass
 constexpr uint32_t kSparseChunk = 32;  // up to this many entries: no LDS accumulator
 
-// start[k][c] = first entry of message k at or after chunk c: entry j writes
-// it for every chunk after its predecessor's chunk and up to its own.
+// start[k][c] = first entry of message k at or after chunk c: entry j (0..n)
+// writes it for every chunk c with chunk(idx[j-1]) < c <= chunk(idx[j]),
+// taking chunk(idx[-1]) = -1 and chunk(idx[n]) = ndchunk.  Those intervals
+// cover 0..ndchunk whatever the order of the indices, so every start[k][c] is
+// written, with a value in [0, count_k].  The grid is
+// bounded and strides over the entries, since the host sizes it from the
+// capacity, not from the (device-resident) count.
 __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTable m, DecWs w) {
     const int k = blockIdx.y;
     const uint32_t n = msg_count(m, k);
-    const uint64_t base = (uint64_t(blockIdx.x) * kBlock + threadIdx.x) * kRun;
+    const uint64_t stride = uint64_t(gridDim.x) * kBlock * kRun;
     if (uint64_t(blockIdx.x) * kBlock * kRun > n) return;
     __shared__ uint32_t starts[kLdsSegs];
     const bool in_lds = P.nseg <= kLdsSegs;
@@ -103,28 +108,36 @@ __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTabl
         for (int i = threadIdx.x; i < P.nseg; i += kBlock) starts[i] = static_cast<uint32_t>(P.seg_start[i]);
         __syncthreads();
     }
-    if (base > n) return;
     const uint32_t *idx = m.idx[k];
     uint32_t *start = w.start + size_t(k) * (P.ndchunk + 1);
-    // all of this thread's indices (and its predecessor's) in flight at once
-    uint32_t id[kRun + 1];
-#pragma unroll
-    for (uint32_t q = 0; q <= kRun; ++q) {
-        const uint64_t j = base + q;  // slot q holds entry j - 1
-        id[q] = (j >= 1 && j - 1 < n) ? idx[j - 1] : 0u;
+    if (n == 0) {  // no entries (only workgroup 0 is left): every chunk starts at 0
+        for (uint32_t c = threadIdx.x; c <= P.ndchunk; c += kBlock) start[c] = 0u;
+        return;
     }
-    SegCursor cur;
-    cur.P = &P;
-    cur.start = in_lds ? starts : nullptr;
-    cur.find(base > 0 ? id[0] : (n > 0 ? idx[0] : 0u));
-    int64_t cp = base > 0 ? int64_t(cur.chunk(id[0])) : -1;
+    SegCursor walk;
+    walk.P = &P;
+    walk.start = in_lds ? starts : nullptr;
+    // entries j = base + q * kBlock (q < kRun) per thread: coalesced loads of
+    // idx[j] and idx[j - 1], all issued before the walk; a thread's indices
+    // ascend, so one cursor walks forward through the segments
+    for (uint64_t base = uint64_t(blockIdx.x) * kBlock * kRun + threadIdx.x; base <= n; base += stride) {
+        uint32_t cur[kRun], prv[kRun];
+        const uint64_t last = n - 1;
 #pragma unroll
-    for (uint32_t q = 0; q < kRun; ++q) {
-        const uint64_t j = base + q;
-        if (j <= n) {
-            const int64_t cj = j < n ? int64_t(cur.chunk(id[q + 1])) : int64_t(P.ndchunk);
+        for (uint32_t q = 0; q < kRun; ++q) {
+            const uint64_t j = base + uint64_t(q) * kBlock;
+            const uint64_t jp = j > 0 ? j - 1 : 0;
+            cur[q] = idx[j < last ? j : last];
+            prv[q] = idx[jp < last ? jp : last];
+        }
+        walk.find(base > 0 ? prv[0] : cur[0]);
+#pragma unroll
+        for (uint32_t q = 0; q < kRun; ++q) {
+            const uint64_t j = base + uint64_t(q) * kBlock;
+            if (j > n) break;
+            const int64_t cp = j > 0 ? int64_t(walk.chunk(prv[q])) : -1;
+            const int64_t cj = j < n ? int64_t(walk.chunk(cur[q])) : int64_t(P.ndchunk);
             for (int64_t c = cp + 1; c <= cj; ++c) start[c] = static_cast<uint32_t>(j);
-            if (cj > cp) cp = cj;
         }
     }
 }
@@ -143,23 +156,21 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, int K, DecWs w,
                                                         float *__restrict__ dense, int avg,
                                                         int accumulate) {
+    // the chunk record and the entry ranges depend on c alone: one round trip
     const uint32_t c = blockIdx.x;
-    const uint32_t s = P.dchunk_seg[c];
-    const SegDev seg = P.seg[s];
-    const uint32_t pos = c - seg.dchunk0;
-    const uint64_t lo = seg.off + (uint64_t(pos) << kChunkLog2);
-    const uint32_t rem = seg.len - (pos << kChunkLog2);
-    const uint32_t cnt = rem < uint32_t(kChunk) ? rem : uint32_t(kChunk);
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint64_t lo = rec.x;
+    const uint32_t cnt = rec.y;
     float *dp = dense + lo;
     const bool vec = is_aligned16(dp);
     __shared__ float acc[kChunk];
     const int lane = lane_id();
     uint32_t a = 0, b = 0;
     if (lane < K) {
-        const uint32_t nk = msg_count(m, lane);
+        // the index pass wrote every start[lane][0..ndchunk] within [0, count]
         const uint32_t *st = w.start + size_t(lane) * (P.ndchunk + 1);
-        a = min(st[c], nk);
-        b = min(max(st[c + 1], a), nk);
+        a = st[c];
+        b = max(st[c + 1], a);
     }
     const uint32_t total = wave_sum(b - a);  // identical in every wave
     float v[kRows][4];
@@ -168,36 +179,76 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[j][q] = 0.0f;
     if (total != 0 && total <= kSparseChunk) {
-        // few entries: every thread reads them all (broadcast loads), in
-        // message order, and adds those that fall on its own elements
-        for (int k = 0; k < K; ++k) {
-            const uint32_t ak = __shfl(a, k, kWave), bk = __shfl(b, k, kWave);
-            for (uint32_t i = ak; i < bk; ++i) {
-                const uint32_t id = m.idx[k][i];
-                const uint64_t r = uint64_t(id) - lo;
-                if (id < lo || r >= cnt) continue;
-                const uint32_t e = static_cast<uint32_t>(r);
-                if (((e >> 2) & (kBlock - 1)) != threadIdx.x) continue;
-                const float x = m.val[k][i];
-                const uint32_t j = e >> 10, q = e & 3u;
+        // few entries: lane l of every wave loads the l-th entry of the
+        // chunk (messages in order, entries ascending within a message) in a
+        // single round trip; then every thread walks them in that order and
+        // adds those that fall on its own elements
+        const uint32_t cntk = b - a;
+        uint32_t pre = cntk;  // inclusive scan over the message lanes
 #pragma unroll
-                for (int jj = 0; jj < kRows; ++jj)
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq)
-                        if (uint32_t(jj) == j && uint32_t(qq) == q) v[jj][qq] = v[jj][qq] + x;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t o = __shfl_up(pre, d, kWave);
+            if (lane >= d) pre += o;
+        }
+        pre -= cntk;
+        // message q holds chunk entries [pre_q, pre_q + cnt_q); every lane
+        // takes part in the shuffles, then lanes below the total load
+        int k = 0;
+        uint32_t base = 0, first = 0;
+        for (int q = 0; q < K; ++q) {
+            const uint32_t pq = __shfl(pre, q, kWave), cq = __shfl(cntk, q, kWave);
+            const uint32_t aq = __shfl(a, q, kWave);
+            if (uint32_t(lane) >= pq && uint32_t(lane) < pq + cq) {
+                k = q;
+                base = pq;
+                first = aq;
             }
+        }
+        uint32_t my_id = 0;
+        float my_x = 0.0f;
+        if (uint32_t(lane) < total) {
+            const uint32_t i = first + (uint32_t(lane) - base);
+            my_id = m.idx[k][i];
+            my_x = m.val[k][i];
+        }
+        for (uint32_t l = 0; l < total; ++l) {
+            const uint32_t id = __shfl(my_id, int(l), kWave);
+            const float x = __shfl(my_x, int(l), kWave);
+            const uint64_t r = uint64_t(id) - lo;
+            if (id < lo || r >= cnt) continue;
+            const uint32_t e = static_cast<uint32_t>(r);
+            if (((e >> 2) & (kBlock - 1)) != threadIdx.x) continue;
+            const uint32_t j = e >> 10, q = e & 3u;
+#pragma unroll
+            for (int jj = 0; jj < kRows; ++jj)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    if (uint32_t(jj) == j && uint32_t(qq) == q) v[jj][qq] = v[jj][qq] + x;
         }
     } else if (total != 0) {
         for (int e = threadIdx.x; e < kChunk; e += kBlock) acc[e] = 0.0f;
         __syncthreads();
+        constexpr uint32_t kBatch = 4;  // entries per thread with loads in flight together
         for (int k = 0; k < K; ++k) {
             const uint32_t ak = __shfl(a, k, kWave), bk = __shfl(b, k, kWave);
             const uint32_t *idx = m.idx[k];
             const float *val = m.val[k];
-            for (uint32_t i = ak + threadIdx.x; i < bk; i += kBlock) {
-                const uint32_t id = idx[i];
-                const uint64_t r = uint64_t(id) - lo;
-                if (id >= lo && r < cnt) acc[r] = acc[r] + val[i];
+            for (uint64_t i0 = ak; i0 < bk; i0 += kBatch * kBlock) {
+                uint32_t id[kBatch];
+                float x[kBatch];
+#pragma unroll
+                for (uint32_t u = 0; u < kBatch; ++u) {
+                    const uint64_t i = uint64_t(i0) + u * kBlock + threadIdx.x;
+                    const uint32_t ic = i < bk ? static_cast<uint32_t>(i) : bk - 1;
+                    id[u] = idx[ic];
+                    x[u] = val[ic];
+                }
+#pragma unroll
+                for (uint32_t u = 0; u < kBatch; ++u) {
+                    const uint64_t r = uint64_t(id[u]) - lo;
+                    if (uint64_t(i0) + u * kBlock + threadIdx.x < bk && id[u] >= lo && r < cnt)
+                        acc[r] = acc[r] + x[u];
+                }
             }
             __syncthreads();
         }
@@ -270,7 +321,9 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     uint64_t max_entries = 0;
     for (int k = 0; k < K; ++k) max_entries = std::max<uint64_t>(max_entries, msgs[k].cap);
     // one pass: enough workgroups for the largest capacity (extra ones exit)
-    unsigned gx = static_cast<unsigned>((max_entries + kBlock * kRun) / (kBlock * kRun) + 1);
+    const uint64_t need_x = (max_entries + kBlock * kRun) / (kBlock * kRun) + 1;
+    const uint64_t cap_x = std::max<uint64_t>(64, uint64_t(kPersistentBlocks) / uint64_t(K));
+    unsigned gx = static_cast<unsigned>(std::min(need_x, cap_x));
     GC_LAUNCH("decode_index", stream, decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w));
     GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
                                                         accumulate != 0));

@@ -82,15 +82,30 @@ __device__ __forceinline__ EntryCtx entry_ctx(const PlanDev &P, const uint32_t *
     return x;
 }
 
-// Escapes before entry j: floor(gap / MAX), gap = unsent elements since the
-// previous entry.  Out-of-order or out-of-segment indices count as gap 0.
-__device__ __forceinline__ uint32_t entry_escapes(const uint32_t *idx, const EntryCtx &x, uint32_t j,
-                                                  uint32_t MAX, uint32_t *gap_out) {
-    uint64_t rel = idx[j] >= x.off ? uint64_t(idx[j]) - x.off : uint64_t(x.len);
-    uint64_t prev_next = j > x.first ? (idx[j - 1] >= x.off ? uint64_t(idx[j - 1]) - x.off + 1 : 0) : 0;
-    uint32_t gap = (rel < x.len && rel >= prev_next) ? static_cast<uint32_t>(rel - prev_next) : 0u;
-    *gap_out = gap;
-    return gap / MAX;
+// Gap before entry j (unsent elements since the previous entry) from the
+// loaded indices cur = idx[j] and prv = idx[j - 1]; out-of-order or
+// out-of-segment indices count as gap 0.  Escapes before the entry are
+// floor(gap / MAX).
+__device__ __forceinline__ uint32_t entry_gap(const EntryCtx &x, uint32_t j, uint32_t cur, uint32_t prv) {
+    const uint64_t rel = cur >= x.off ? uint64_t(cur) - x.off : uint64_t(x.len);
+    const uint64_t prev_next = j > x.first ? (prv >= x.off ? uint64_t(prv) - x.off + 1 : 0) : 0;
+    return (rel < x.len && rel >= prev_next) ? static_cast<uint32_t>(rel - prev_next) : 0u;
+}
+
+// Loads idx[j] and idx[j - 1] for entries j = j0 + i * stride of one tile,
+// all issued before any is used: addresses are clamped into the segment's
+// entries (which the tile's existence makes non-empty), so no load sits
+// behind a branch.
+template <uint32_t N>
+__device__ __forceinline__ void load_ids(const uint32_t *__restrict__ idx, const EntryCtx &x, uint32_t j0,
+                                         uint32_t stride, uint32_t (&cur)[N], uint32_t (&prv)[N]) {
+    const uint32_t last = x.end > x.first ? x.end - 1 : x.first;
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i) {
+        const uint32_t j = min(j0 + i * stride, last);
+        cur[i] = idx[j];
+        prv[i] = idx[j > x.first ? j - 1 : j];
+    }
 }
 
 // One workgroup: tile counts per segment -> tile_base.
@@ -154,12 +169,13 @@ __global__ __launch_bounds__(kBlock) void pack_count_kernel(PlanDev P, int kind,
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const EntryCtx x = entry_ctx(P, seg_off, kind, cap, table.segment(t));
     const uint32_t j0 = x.first + (t - w.tile_base[x.s]) * kTile;
+    uint32_t cur[kPerThread], prv[kPerThread];
+    load_ids(idx, x, j0 + threadIdx.x, kBlock, cur, prv);
     uint32_t esc = 0;
 #pragma unroll
     for (uint32_t i = 0; i < kPerThread; ++i) {
         const uint32_t j = j0 + i * kBlock + threadIdx.x;
-        uint32_t gap;
-        if (j < x.end) esc += entry_escapes(idx, x, j, MAX, &gap);
+        if (j < x.end) esc += entry_gap(x, j, cur[i], prv[i]) / MAX;
     }
     uint32_t tot;
     (void)block_exclusive_scan(esc, &tot);
@@ -250,19 +266,23 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
     }
     if (w.tile_esc[t] == 0) {
         // no escape in this tile: entry j goes to slot (j - first) + esc_base
+        uint32_t cur[kPerThread], prv[kPerThread];
+        load_ids(idx, x, j0 + threadIdx.x, kBlock, cur, prv);
+        float v[kPerThread];
+        const uint32_t last = x.end > x.first ? x.end - 1 : x.first;
+#pragma unroll
+        for (uint32_t i = 0; i < kPerThread; ++i) v[i] = val[min(j0 + i * kBlock + threadIdx.x, last)];
 #pragma unroll
         for (uint32_t i = 0; i < kPerThread; ++i) {
             const uint32_t j = j0 + i * kBlock + threadIdx.x;
-            if (j >= x.end) continue;
             const uint32_t slot = (j - x.first) + esc_base;
-            if (slot >= E) continue;  // only for malformed messages
-            uint32_t gap;
-            (void)entry_escapes(idx, x, j, MAX, &gap);
+            if (j >= x.end || slot >= E) continue;  // slot >= E only for malformed messages
+            const uint32_t gap = entry_gap(x, j, cur[i], prv[i]);
             if (dgc) {
                 runs[slot] = static_cast<uint16_t>(gap);
-                vals[slot] = val[j];
+                vals[slot] = v[i];
             } else {
-                const uint16_t sign = (dev_f2u(val[j]) >> 31) ? 0x8000u : 0u;
+                const uint16_t sign = (dev_f2u(v[i]) >> 31) ? 0x8000u : 0u;
                 runs[slot] = static_cast<uint16_t>(sign | gap);
             }
         }
@@ -270,15 +290,19 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
     }
     // tile with escapes: thread-contiguous entries and an in-tile scan
     uint32_t esc[kPerThread], gap[kPerThread];
+    {
+        uint32_t cur[kPerThread], prv[kPerThread];
+        load_ids(idx, x, j0 + threadIdx.x * kPerThread, 1u, cur, prv);
+#pragma unroll
+        for (uint32_t i = 0; i < kPerThread; ++i) {
+            const uint32_t j = j0 + threadIdx.x * kPerThread + i;
+            gap[i] = j < x.end ? entry_gap(x, j, cur[i], prv[i]) : 0u;
+            esc[i] = gap[i] / MAX;
+        }
+    }
     uint32_t mine = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < kPerThread; ++i) {
-        const uint32_t j = j0 + threadIdx.x * kPerThread + i;
-        esc[i] = 0;
-        gap[i] = 0;
-        if (j < x.end) esc[i] = entry_escapes(idx, x, j, MAX, &gap[i]);
-        mine += esc[i];
-    }
+    for (uint32_t i = 0; i < kPerThread; ++i) mine += esc[i];
     uint32_t tot;
     uint32_t before = esc_base + block_exclusive_scan(mine, &tot);
 #pragma unroll

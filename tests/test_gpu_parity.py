@@ -208,6 +208,46 @@ def test_decode_parity(K, mode):
         assert same_bits(got, want), ulp_report(got, want)
 
 
+@pytest.mark.parametrize("K", [1, 3, 8])
+def test_decode_chunk_entry_counts(K):
+    """Chunks holding 0, 1, 31, 32, 33 and a few hundred entries in total over
+    K messages (a chunk is 4096 elements of a segment): both accumulation
+    strategies of the decoder, and messages empty in a chunk, sum in message
+    order bit-exactly."""
+    rng = np.random.default_rng(700 + K)
+    t = W.make_table([4096 * 7 + 1000, 4096 * 2 + 5, 77], [50, 50, 7], [10, 10, 1])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    totals = [0, 1, 31, 32, 33, 400, 32, 2, 9, 0, 64]  # per chunk, in chunk order
+    chunks = []
+    for o, ln, _, _ in t:
+        for c0 in range(0, ln, 4096):
+            chunks.append((o + c0, min(4096, ln - c0)))
+    per_msg = [[] for _ in range(K)]
+    for ci, (lo, cnt) in enumerate(chunks):
+        tot = min(totals[ci % len(totals)], cnt * K)
+        # split tot over the messages (some get none), each a set of distinct positions
+        cuts = np.sort(rng.integers(0, tot + 1, K - 1)) if K > 1 else np.array([], np.int64)
+        sizes = np.diff(np.concatenate([[0], cuts, [tot]])).astype(int)
+        for k in range(K):
+            m = min(int(sizes[k]), cnt)
+            per_msg[k].append(np.sort(rng.choice(cnt, m, replace=False)) + lo)
+    msgs, host = [], []
+    for k in range(K):
+        idx = np.concatenate(per_msg[k]).astype(np.uint32) if per_msg[k] else np.zeros(0, np.uint32)
+        offs = [int(np.searchsorted(idx, o)) for o, _, _, _ in t] + [idx.size]
+        val = W.random_values(rng, idx.size, "laplace")
+        host.append((idx, val))
+        msgs.append(sparse_from_host(hp.plan, idx, val, offs))
+    dense0 = W.random_values(rng, n)
+    for mode in (B.GC_SUM, B.GC_AVG):
+        for acc in (False, True):
+            say(f"decode chunk counts K={K} mode={mode} acc={acc}")
+            want = oracle.decode(t, n, host, mode=mode, dense=dense0 if acc else None)
+            got = hp.decode(msgs, mode, dense0 if acc else None)
+            assert same_bits(got, want), ulp_report(got, want)
+
+
 # ---------------------------------------------------------------------- DCD
 @pytest.mark.parametrize("n", [1, 3, 4, 5, 511, 512, 513, 4096, 4097, 100_003])
 @pytest.mark.parametrize("bits_", [4, 8])
