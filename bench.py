@@ -33,11 +33,10 @@ def algorithmic_bytes(n: int, nbins: int, k_total: int, ada_entries: int, bucket
     return {
         "dgc_update": 20 * n,                 # read G, U, V; write U, V
         "dgc_norm": 4 * n,                    # read G
-        "dgc_stage": 4 * n,                   # read V
         "ada_max": 8 * n,                     # read R, dW
         "ada_apply": 12 * n + 8 * ada_entries,  # read R, dW; write R; message
         "dcd": 12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket),  # x, x_half, x_out, codes, scales
-        "decode": 4 * n,                      # dense write (K=1)
+        "decode": 4 * n + 4 * (k_total + ada_entries),  # dense write; the two messages, per launch
         "dgc_emit": 8 * k_total + 8 * k_total,  # message out + masking writes
     }
 

@@ -69,7 +69,7 @@ _SIGS = {
     "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
 }
 
-KERNELS = ("dgc_norm", "dgc_prep", "dgc_update", "dgc_select", "dgc_stage", "dgc_refine",
+KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_update", "dgc_select", "dgc_stage", "dgc_refine",
            "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd")
 

@@ -77,14 +77,12 @@ __device__ __forceinline__ uint32_t div_small(uint32_t e, uint32_t L, float invL
 // G = R + dW for the chunk in the 4-wide layout, with each element's bin.
 __device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const float *dW, float invL,
                                         float (&g)[kRows][4], uint32_t (&bin)[kRows][4]) {
-    const float *rp = R + a.lo;
-    const float *dp = dW + a.lo;
-    const bool vec = is_aligned16(rp) && is_aligned16(dp);
+    const BufRsrc rr = chunk_buf(R + a.lo, a.cnt), rd = chunk_buf(dW + a.lo, a.cnt);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
         float r[4], d[4];
-        load4(rp, row_elem(j), a.cnt, vec, r);
-        load4(dp, row_elem(j), a.cnt, vec, d);
+        load4(rr, row_elem(j), r);
+        load4(rd, row_elem(j), d);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             g[j][q] = r[q] + d[q];
@@ -239,8 +237,7 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
     __syncthreads();
     bool flag[kRows][4];
     uint32_t pos[kRows][4];
-    float *rp = R + a.lo;
-    const bool vec = is_aligned16(rp) && is_aligned16(dW + a.lo);
+    const BufRsrc rr = chunk_buf(R + a.lo, a.cnt);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
         const uint32_t e0 = row_elem(j);
@@ -254,7 +251,7 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
             const float qv = copysignf(scale, g[j][q]);
             r[q] = flag[j][q] ? g[j][q] - qv : g[j][q];
         }
-        store4(rp, e0, a.cnt, vec, r);
+        store4(rr, e0, r);
     }
     (void)block_compact4(flag, pos);
 #pragma unroll

@@ -161,8 +161,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
     const ChunkRec rec = P.dchunk_rec[c];
     const uint64_t lo = rec.x;
     const uint32_t cnt = rec.y;
-    float *dp = dense + lo;
-    const bool vec = is_aligned16(dp);
+    const BufRsrc rd = chunk_buf(dense + lo, cnt);
     __shared__ float acc[kChunk];
     const int lane = lane_id();
     uint32_t a = 0, b = 0;
@@ -269,11 +268,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
         }
         if (accumulate) {
             float d[4];
-            load4(dp, e0, cnt, vec, d);
+            load4(rd, e0, d);
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[j][q] = d[q] + v[j][q];
         }
-        store4(dp, e0, cnt, vec, v[j]);
+        store4(rd, e0, v[j]);
     }
 }
 

@@ -2,25 +2,34 @@
 // radix select on |V| bit patterns, ordered compaction, momentum factor
 // masking.  "Deep Gradient Compression" (Lin et al.), §3.1–§3.3, App. C, D.
 //
-// Launch sequence.  Chunk kernels run one workgroup per 4096-element chunk of
-// a segment; segment kernels one workgroup per segment.  Chunk kernels hand
-// results to segment kernels through global memory at kernel boundaries only
-// (no cross-workgroup fences, which on gfx950 write back the XCD's L2).
+// Launch sequence.  Chunk kernels run one workgroup (or one wave) per
+// 4096-element chunk of a segment; segment kernels one workgroup per segment.
+// Chunk kernels hand results to segment kernels through global memory at
+// kernel boundaries only (no cross-workgroup fences, which on gfx950 write
+// back the XCD's L2).
 //   norm    (chunk, clip only) pairwise fp64 sum of G^2 over the chunk
 //   prep    (segment) clear the segment's histograms; finish the pairwise
 //           tree over the chunk sums and set the clip factor
+//   sample  (chunk) V' = V + (m U + c G) for 32 contiguous elements of the
+//           chunk; histogram of their digit 1 (key >> 20)
+//   bound   (segment) from the sample, a digit L1 that the k-th largest key
+//           almost surely reaches (the DGC paper estimates its threshold
+//           from a sample of the gradient, §3.1 / App. D)
 //   update  (chunk) U <- fl(fl(m U) + fl(c G)); V <- fl(V + U); LDS histogram
-//           of digit 1 (key >> 20), flushed with global atomics
-//   select1 (segment) digit 1 of the k-th largest key
-//   stage   (chunk) re-read V; keep entries with digit 1 at or above it, in
-//           index order at the chunk's own offset; histogram digit 2 of the
-//           boundary bucket
+//           of digit 1, flushed with global atomics; entries with digit 1 at
+//           or above L1 staged in index order at the chunk's own offset
+//   select1 (segment) digit 1 of the k-th largest key, d1; if d1 < L1 the
+//           staging missed candidates and the segment is re-staged
+//   stage   (chunk) histogram digit 2 of the staged entries in the boundary
+//           bucket; for a re-staged segment, re-read V and stage digit 1 >= d1
 //   select2 (segment) digit 2
 //   refine  (chunk) histogram digit 3 of staged entries in the boundary bucket
 //   select3 (segment) threshold key T, count above it, ties to send
 //   count   (chunk) staged keys > T and == T
 //   scan    (segment) message slot and tie quota of every chunk
 //   emit    (chunk) write (idx, V) in index order, then zero U and V there
+// Staged entries below d1 are never counted or sent (their keys are below T),
+// so the looser staging changes no result.
 #include <cmath>
 
 #include "gc_internal.hpp"
@@ -32,7 +41,28 @@ namespace {
 struct SegState {
     float clip;
     uint32_t d1, above1, d2, above2, T, gt, need_eq;
+    uint32_t L1;    // staging bound on digit 1 from the sample
+    uint32_t redo;  // d1 < L1: re-stage the segment from V
 };
+
+// Sample of a segment: in every stride-th chunk (at most kSampleChunks
+// chunks), kSamples contiguous elements starting at a per-chunk offset
+// (spread over the chunk so that strided tensor layouts are not always
+// sampled at the same columns).
+constexpr uint32_t kSamples = 32;
+constexpr uint32_t kSampleChunks = 512;
+__device__ __forceinline__ uint32_t sample_offset(uint32_t c, uint32_t cnt) {
+    return cnt == uint32_t(kChunk) ? 128u * ((c * 13u) & 31u) : 0u;
+}
+__device__ __forceinline__ uint32_t sample_stride(uint32_t dnchunk) {
+    return (dnchunk + kSampleChunks - 1) / kSampleChunks;
+}
+
+// Digit-1 and digit-2 histograms are kept in kHistRep replicas per segment,
+// picked by workgroup (update) or chunk (stage): concurrent global atomics on
+// one address serialize, and a large segment is covered by hundreds of
+// workgroups.  The select kernels add the replicas.
+constexpr uint32_t kHistRep = 16;
 
 struct DgcWs {
     uint32_t *hist1, *hist2, *hist3;
@@ -41,13 +71,14 @@ struct DgcWs {
     uint32_t *ccount, *cgt, *ceq, *cout, *ctake;
     uint32_t *sidx;
     float *sval;
+    uint16_t *skey;  // [ndchunk][kSamples] digit 1 of the sampled V'
 };
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
     DgcWs w{};
-    w.hist1 = c.take<uint32_t>(size_t(kHist1) * p->nseg);
-    w.hist2 = c.take<uint32_t>(size_t(kHist2) * p->nseg);
+    w.hist1 = c.take<uint32_t>(size_t(kHist1) * kHistRep * p->nseg);
+    w.hist2 = c.take<uint32_t>(size_t(kHist2) * kHistRep * p->nseg);
     w.hist3 = c.take<uint32_t>(size_t(kHist3) * p->nseg);
     w.st = c.take<SegState>(p->nseg);
     w.partial = c.take<double>(p->ndchunk);
@@ -58,6 +89,7 @@ DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.ctake = c.take<uint32_t>(p->ndchunk);
     w.sidx = c.take<uint32_t>(p->n_total);
     w.sval = c.take<float>(p->n_total);
+    w.skey = c.take<uint16_t>(size_t(p->ndchunk) * kSamples);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -125,21 +157,19 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
     float cur[kRows][4], nxt[kRows][4];
     ChunkWalker walk;
     ChunkInfo ci;
-    bool vec = false;
     if (c0 < c1) {
         ci = walk.at(P, c0);
-        vec = is_aligned16(G + ci.lo);
+        const BufRsrc rg = chunk_buf(G + ci.lo, ci.cnt);
 #pragma unroll
-        for (int j = 0; j < kRows; ++j) load4(G + ci.lo, row_elem(j), ci.cnt, vec, cur[j]);
+        for (int j = 0; j < kRows; ++j) load4(rg, row_elem(j), cur[j]);
     }
     for (uint32_t c = c0; c < c1; ++c) {
         ChunkInfo cn;
-        bool vn = false;
         if (c + 1 < c1) {
             cn = walk.at(P, c + 1);
-            vn = is_aligned16(G + cn.lo);
+            const BufRsrc rn = chunk_buf(G + cn.lo, cn.cnt);
 #pragma unroll
-            for (int j = 0; j < kRows; ++j) load4(G + cn.lo, row_elem(j), cn.cnt, vn, nxt[j]);
+            for (int j = 0; j < kRows; ++j) load4(rn, row_elem(j), nxt[j]);
         }
 #pragma unroll
         for (int j = 0; j < kRows; ++j) {
@@ -173,11 +203,11 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
                                                           float thr) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
-    uint32_t *h = w.hist1 + size_t(s) * kHist1;
-    for (int i = threadIdx.x; i < kHist1; i += kBlock) h[i] = 0u;
-    h = w.hist2 + size_t(s) * kHist2;
-    for (int i = threadIdx.x; i < kHist2; i += kBlock) h[i] = 0u;
-    h = w.hist3 + size_t(s) * kHist3;
+    uint4 *h4 = reinterpret_cast<uint4 *>(w.hist1 + size_t(s) * kHistRep * kHist1);
+    for (int i = threadIdx.x; i < int(kHistRep * kHist1 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+    h4 = reinterpret_cast<uint4 *>(w.hist2 + size_t(s) * kHistRep * kHist2);
+    for (int i = threadIdx.x; i < int(kHistRep * kHist2 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t *h = w.hist3 + size_t(s) * kHist3;
     for (int i = threadIdx.x; i < kHist3; i += kBlock) h[i] = 0u;
     float cl = 1.0f;
     if (use_clip) {
@@ -189,35 +219,119 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
     if (threadIdx.x == 0) w.st[s].clip = cl;
 }
 
+// ---------------------------------------------------------------- sample
+// Half a wave per chunk: in a sampled chunk, lane l < min(32, cnt) computes
+// V' of element sample_offset + l with the update's own arithmetic and
+// records its digit 1 (plain stores: no atomics).
+__global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const float *__restrict__ G,
+                                                            const float *__restrict__ U,
+                                                            const float *__restrict__ V, float m,
+                                                            DgcWs w) {
+    const uint32_t c = (blockIdx.x * kWaves + wave_id()) * 2u + (uint32_t(lane_id()) >> 5);
+    const uint32_t l = lane_id() & 31;
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t cnt = rec.y;
+    const SegDev seg = P.seg[rec.z];
+    if ((c - seg.dchunk0) % sample_stride(seg.dnchunk) != 0 || l >= min(kSamples, cnt)) return;
+    const uint64_t e = uint64_t(rec.x) + sample_offset(c, cnt) + l;
+    const float clip = w.st[rec.z].clip;
+    const float gc = clip * G[e];
+    float un = m * U[e];
+    un = un + gc;
+    const float vn = V[e] + un;
+    w.skey[size_t(c) * kSamples + l] = static_cast<uint16_t>(mag_key(vn) >> (kDigit2Bits + kDigit3Bits));
+}
+
+// ----------------------------------------------------------------- bound
+// Of S samples, about E = S k / n fall in the segment's top k (a binomial
+// count).  L1 is the digit-1 bucket of the (E + 4 sqrt(E) + 16)-th largest
+// sample, or 0 (stage everything) when the sample is too small for that.
+// A sampled chunk's 32 keys are 64 contiguous bytes: thread i loads 16-byte
+// piece i (piece 4 j + p of sampled chunk j), at most 8 per thread, all in
+// flight together, into an LDS histogram.
+__global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    __shared__ uint32_t h[kHist1];
+    for (int i = threadIdx.x; i < kHist1; i += kBlock) h[i] = 0u;
+    const uint32_t stride = sample_stride(seg.dnchunk);
+    const uint32_t nsc = (seg.dnchunk + stride - 1) / stride;  // sampled chunks
+    const uint32_t last = (nsc - 1) * stride;                   // last sampled chunk
+    const uint32_t last_cnt = min(seg.len - last * uint32_t(kChunk), uint32_t(kChunk));
+    const uint32_t last_ns = min(kSamples, last_cnt);
+    const uint32_t total = (nsc - 1) * kSamples + last_ns;
+    constexpr uint32_t kPer = kSampleChunks * 4 / kBlock;
+    uint4 piece[kPer];
+#pragma unroll
+    for (uint32_t u = 0; u < kPer; ++u) {
+        const uint32_t i = min(u * kBlock + threadIdx.x, nsc * 4 - 1);
+        const uint32_t c = seg.dchunk0 + (i >> 2) * stride;
+        piece[u] = *reinterpret_cast<const uint4 *>(w.skey + size_t(c) * kSamples + (i & 3) * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t u = 0; u < kPer; ++u) {
+        const uint32_t i = u * kBlock + threadIdx.x;
+        if (i >= nsc * 4) continue;
+        const uint32_t lim = (i >> 2) == nsc - 1 ? last_ns : kSamples;  // keys of the chunk
+        const uint32_t words[4] = {piece[u].x, piece[u].y, piece[u].z, piece[u].w};
+#pragma unroll
+        for (uint32_t q = 0; q < 8; ++q) {
+            const uint32_t l = (i & 3) * 8 + q;
+            if (l < lim) atomicAdd(&h[(words[q >> 1] >> (16 * (q & 1))) & 0xFFFFu], 1u);
+        }
+    }
+    __syncthreads();
+    const double E = double(total) * double(seg.k) / double(seg.len);
+    const double target = E + 4.0 * sqrt(E) + 16.0;
+    uint32_t L1 = 0;
+    if (target < double(total)) {
+        uint32_t above;
+        L1 = block_find_bucket<kHist1>(static_cast<uint32_t>(target), [&](int b) { return h[b]; }, &above);
+    }
+    if (threadIdx.x == 0) w.st[s].L1 = L1;
+}
+
 // ---------------------------------------------------------------- update
 // The digit-1 histogram lives in LDS across the workgroup's chunks and is
 // flushed to the segment's global histogram only when the segment changes.
+// Staging: in row j, wave w holds elements [1024 j + 256 w, +256) of the
+// chunk (lane-major, 4 per lane), so an entry's rank in the chunk is the
+// staged count of the (row, wave) pieces before its own, plus the ballot
+// ranks of lower lanes, plus its own earlier flags.  The piece counts go
+// through a double-buffered LDS table with one barrier per chunk.
 __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const float *__restrict__ G,
                                                             float *__restrict__ U,
                                                             float *__restrict__ V, float m, DgcWs w) {
     uint32_t c0, c1;
     chunk_range(P.ndchunk, &c0, &c1);
     __shared__ uint32_t hist[kHist1];
+    __shared__ uint32_t piece[2][kRows * kWaves];
     for (int i = threadIdx.x; i < kHist1; i += kBlock) hist[i] = 0u;
     if (c0 >= c1) return;
     float g[kRows][4], u[kRows][4], v[kRows][4];
     ChunkWalker walk;
     ChunkInfo ci = walk.at(P, c0);
-    bool vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
+    BufRsrc rg = chunk_buf(G + ci.lo, ci.cnt), ru = chunk_buf(U + ci.lo, ci.cnt), rv = chunk_buf(V + ci.lo, ci.cnt);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
-        load4(G + ci.lo, row_elem(j), ci.cnt, vec, g[j]);
-        load4(U + ci.lo, row_elem(j), ci.cnt, vec, u[j]);
-        load4(V + ci.lo, row_elem(j), ci.cnt, vec, v[j]);
+        load4(rg, row_elem(j), g[j]);
+        load4(ru, row_elem(j), u[j]);
+        load4(rv, row_elem(j), v[j]);
     }
     __syncthreads();
+    const int lane = lane_id(), wave = wave_id();
     for (uint32_t c = c0; c < c1; ++c) {
         const float clip = w.st[ci.s].clip;
-        float *up = U + ci.lo;
-        float *vp = V + ci.lo;
+        const uint32_t L1 = w.st[ci.s].L1;
+        uint32_t flags[kRows], before[kRows];
 #pragma unroll
         for (int j = 0; j < kRows; ++j) {
             const uint32_t e0 = row_elem(j);
+            flags[j] = 0;
+            before[j] = 0;
+            uint32_t piece_total = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float gc = clip * g[j][q];
@@ -226,26 +340,63 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
                 float vn = v[j][q] + un;
                 u[j][q] = un;
                 v[j][q] = vn;
-                if (e0 + q < ci.cnt) atomicAdd(&hist[mag_key(vn) >> (kDigit2Bits + kDigit3Bits)], 1u);
+                const bool in = e0 + q < ci.cnt;
+                const uint32_t d = mag_key(vn) >> (kDigit2Bits + kDigit3Bits);
+                if (in) atomicAdd(&hist[d], 1u);
+                const bool f = in && d >= L1;
+                flags[j] |= uint32_t(f) << q;
+                const uint64_t bm = __ballot(f);
+                before[j] += lane_rank(bm);
+                piece_total += static_cast<uint32_t>(__popcll(bm));
             }
-            store4(up, e0, ci.cnt, vec, u[j]);
-            store4(vp, e0, ci.cnt, vec, v[j]);
+            if (lane == 0) piece[(c - c0) & 1][j * kWaves + wave] = piece_total;
+            store4(ru, e0, u[j]);
+            store4(rv, e0, v[j]);
+        }
+        __syncthreads();
+        {
+            const uint32_t *pc = piece[(c - c0) & 1];
+            uint32_t run = 0, base[kRows];
+#pragma unroll
+            for (int j = 0; j < kRows; ++j)
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    if (ww == wave) base[j] = run;
+                    run += pc[j * kWaves + ww];
+                }
+            if (threadIdx.x == 0) w.ccount[c] = run;
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) {
+                if (!flags[j]) continue;
+                uint32_t slot = static_cast<uint32_t>(ci.lo) + base[j] + before[j];
+                const uint32_t e0 = static_cast<uint32_t>(ci.lo) + row_elem(j);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if ((flags[j] >> q) & 1u) {
+                        w.sidx[slot] = e0 + q;
+                        w.sval[slot] = v[j][q];
+                        ++slot;
+                    }
+                }
+            }
         }
         const uint32_t s_done = ci.s;
         const bool more = c + 1 < c1;
         if (more) {
             ci = walk.at(P, c + 1);
-            vec = is_aligned16(G + ci.lo) && is_aligned16(U + ci.lo) && is_aligned16(V + ci.lo);
+            rg = chunk_buf(G + ci.lo, ci.cnt);
+            ru = chunk_buf(U + ci.lo, ci.cnt);
+            rv = chunk_buf(V + ci.lo, ci.cnt);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) {
-                load4(G + ci.lo, row_elem(j), ci.cnt, vec, g[j]);
-                load4(U + ci.lo, row_elem(j), ci.cnt, vec, u[j]);
-                load4(V + ci.lo, row_elem(j), ci.cnt, vec, v[j]);
+                load4(rg, row_elem(j), g[j]);
+                load4(ru, row_elem(j), u[j]);
+                load4(rv, row_elem(j), v[j]);
             }
         }
         if (!more || ci.s != s_done) {
             __syncthreads();
-            uint32_t *h1 = w.hist1 + size_t(s_done) * kHist1;
+            uint32_t *h1 = w.hist1 + (size_t(s_done) * kHistRep + blockIdx.x % kHistRep) * kHist1;
             for (int i = threadIdx.x; i < kHist1; i += kBlock) {
                 const uint32_t n = hist[i];
                 if (n) {
@@ -259,6 +410,14 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
 }
 
 // --------------------------------------------------------------- selects
+template <int NB>
+__device__ __forceinline__ uint32_t replica_sum(const uint32_t *h, int b) {
+    uint32_t t = 0;
+#pragma unroll
+    for (uint32_t r = 0; r < kHistRep; ++r) t += h[r * NB + b];
+    return t;
+}
+
 // Level 1..3 of the radix select for one segment.
 template <int kLevel>
 __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) {
@@ -267,15 +426,17 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
     SegState st = w.st[s];
     uint32_t above;
     if (kLevel == 1) {
-        const uint32_t *h = w.hist1 + size_t(s) * kHist1;
-        uint32_t d = block_find_bucket<kHist1>(seg.k, [&](int b) { return h[b]; }, &above);
+        const uint32_t *h = w.hist1 + size_t(s) * kHistRep * kHist1;
+        uint32_t d = block_find_bucket<kHist1>(seg.k, [&](int b) { return replica_sum<kHist1>(h, b); }, &above);
         if (threadIdx.x == 0) {
             w.st[s].d1 = d;
             w.st[s].above1 = above;
+            w.st[s].redo = d < st.L1 ? 1u : 0u;
         }
     } else if (kLevel == 2) {
-        const uint32_t *h = w.hist2 + size_t(s) * kHist2;
-        uint32_t d = block_find_bucket<kHist2>(seg.k - st.above1, [&](int b) { return h[b]; }, &above);
+        const uint32_t *h = w.hist2 + size_t(s) * kHistRep * kHist2;
+        uint32_t d = block_find_bucket<kHist2>(seg.k - st.above1, [&](int b) { return replica_sum<kHist2>(h, b); },
+                                               &above);
         if (threadIdx.x == 0) {
             w.st[s].d2 = d;
             w.st[s].above2 = st.above1 + above;
@@ -293,10 +454,12 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
 }
 
 // ----------------------------------------------------------------- stage
-// One wave per chunk: lane l holds elements [256 r + 4 l, +4) for rows
-// r = 0..15, so 16 KB of V is in flight per wave and the ordered compaction
-// needs only ballots (rank = running count + lanes below + within lane); no
-// LDS, no workgroup barrier.
+// One wave per chunk.  Normally the update staged every candidate: the wave
+// histograms digit 2 of the staged entries whose digit 1 is d1.  In a
+// re-staged segment it re-reads V instead: lane l holds elements
+// [256 r + 4 l, +4) for rows r = 0..15, so 16 KB of V is in flight per wave
+// and the ordered compaction needs only ballots (rank = running count +
+// lanes below + within lane); no LDS, no workgroup barrier.
 constexpr int kWaveRows = kChunk / (4 * kWave);
 
 __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const float *__restrict__ V,
@@ -305,14 +468,27 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const floa
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
     const uint32_t lo = rec.x, cnt = rec.y, s = rec.z;
-    const float *vp = V + lo;
-    const bool vec = is_aligned16(vp);
+    const uint32_t d1 = w.st[s].d1;
+    const uint32_t redo = w.st[s].redo;
+    uint32_t *h2 = w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2;
     const int lane = lane_id();
+    if (!redo) {
+        const uint32_t n = min(w.ccount[c], cnt);
+        for (uint32_t i0 = 0; i0 < n; i0 += 4 * kWave) {
+            uint32_t key[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) key[q] = mag_key(w.sval[lo + min(i0 + q * kWave + lane, n - 1)]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + q * kWave + lane < n && (key[q] >> (kDigit2Bits + kDigit3Bits)) == d1)
+                    atomicAdd(&h2[(key[q] >> kDigit3Bits) & (kHist2 - 1)], 1u);
+        }
+        return;
+    }
+    const BufRsrc rv = chunk_buf(V + lo, cnt);
     float v[kWaveRows][4];
 #pragma unroll
-    for (int r = 0; r < kWaveRows; ++r) load4(vp, r * (4 * kWave) + 4u * lane, cnt, vec, v[r]);
-    const uint32_t d1 = w.st[s].d1;
-    uint32_t *h2 = w.hist2 + size_t(s) * kHist2;
+    for (int r = 0; r < kWaveRows; ++r) load4(rv, r * (4 * kWave) + 4u * lane, v[r]);
     uint32_t run = 0;  // wave-uniform count of entries staged so far
 #pragma unroll
     for (int r = 0; r < kWaveRows; ++r) {
@@ -531,10 +707,12 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
                                                 std::sqrt(static_cast<double>(num_nodes)))
                            : 0.0f;
     const unsigned segs = static_cast<unsigned>(plan->nseg);
-    const unsigned pgrid = persistent_grid(plan->ndchunk);
-    if (clip) GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<pgrid, kBlock, 0, stream>>>(P, G, w));
+    if (clip)
+        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, G, w));
     GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
-    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<<<pgrid, kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<<<persistent_grid(dgc_update_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, V, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w));

@@ -131,12 +131,18 @@ inline unsigned grid_1d(uint64_t n, unsigned per_block) {
     return static_cast<unsigned>((n + per_block - 1) / per_block);
 }
 
-// Workgroups for a persistent dense pass: enough to fill every CU of an
-// MI355X (256 CUs x 8 resident 256-thread workgroups), never more than the
-// work items.
+// Upper bound on the workgroups of a persistent pass (256 CUs x 8 resident
+// 256-thread workgroups at full occupancy).
 constexpr unsigned kPersistentBlocks = 256 * 8;
-inline unsigned persistent_grid(uint64_t items) {
-    return static_cast<unsigned>(items < kPersistentBlocks ? (items ? items : 1) : kPersistentBlocks);
+
+// Workgroups of a persistent pass of `kernel` (256 threads, no dynamic LDS):
+// as many as are resident at once on the current device, given the kernel's
+// registers and LDS, so that every workgroup starts in the first round;
+// never more than the work items, never fewer than 1.
+unsigned resident_grid(const void *kernel, uint64_t items);
+template <class K>
+unsigned persistent_grid(K *kernel, uint64_t items) {
+    return resident_grid(reinterpret_cast<const void *>(kernel), items);
 }
 
 // Kernel timing (see gc_timing_enable): returns an event to record before
@@ -247,33 +253,35 @@ constexpr int kRows = kChunk / (4 * kBlock);
 
 __device__ __forceinline__ uint32_t row_elem(int row) { return row * (4 * kBlock) + 4u * threadIdx.x; }
 
-__device__ __forceinline__ bool is_aligned16(const void *p) {
-    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+// Chunk access through a raw buffer resource that covers exactly the chunk,
+// [p, p + cnt): the hardware checks each dword against that range, so loads
+// past cnt return 0 and stores past it are dropped.  Every lane then issues
+// one 16-byte access with no branch (divergent load paths into the same
+// registers would force waits that serialize a prefetch), p needs only dword
+// alignment, and the base lives in scalar registers.  The resource must be
+// wave-uniform: p and cnt depend on the chunk only.
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit data format, gfx9 resource word 3
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ BufRsrc chunk_buf(const float *p, uint32_t cnt) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), static_cast<short>(0),
+                                             static_cast<int>(cnt * 4u), kBufWord3);
 }
 
-__device__ __forceinline__ void load4(const float *p, uint32_t e0, uint32_t cnt, bool vec,
-                                      float (&v)[4]) {
-    if (vec && e0 + 4 <= cnt) {
-        float4 t = *reinterpret_cast<const float4 *>(p + e0);
-        v[0] = t.x;
-        v[1] = t.y;
-        v[2] = t.z;
-        v[3] = t.w;
-    } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = e0 + u < cnt ? p[e0 + u] : 0.0f;
-    }
+// Elements [e0, e0 + 4) of the chunk; 0 past its end.
+__device__ __forceinline__ void load4(BufRsrc r, uint32_t e0, float (&v)[4]) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(e0 * 4u), 0, 0);
+    v[0] = dev_u2f(t.x);
+    v[1] = dev_u2f(t.y);
+    v[2] = dev_u2f(t.z);
+    v[3] = dev_u2f(t.w);
 }
 
-__device__ __forceinline__ void store4(float *p, uint32_t e0, uint32_t cnt, bool vec,
-                                       const float (&v)[4]) {
-    if (vec && e0 + 4 <= cnt) {
-        *reinterpret_cast<float4 *>(p + e0) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (e0 + u < cnt) p[e0 + u] = v[u];
-    }
+// Writes elements [e0, e0 + 4) of the chunk; those past its end are dropped.
+__device__ __forceinline__ void store4(BufRsrc r, uint32_t e0, const float (&v)[4]) {
+    const u32x4 t = {dev_f2u(v[0]), dev_f2u(v[1]), dev_f2u(v[2]), dev_f2u(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, static_cast<int>(e0 * 4u), 0, 0);
 }
 
 // Ordered compaction in the 4-wide layout: element (row, u) of thread t has

@@ -2,7 +2,9 @@
 // device upload of the tables, workspace sizing.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "gc_internal.hpp"
 
@@ -22,6 +24,36 @@ gc_status hip_error(hipError_t e, const char *what) {
 }
 
 void clear_error() { g_last_error.clear(); }
+
+unsigned resident_grid(const void *kernel, uint64_t items) {
+    struct Entry {
+        const void *kernel;
+        int device;
+        unsigned blocks;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    unsigned blocks = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (e.kernel == kernel && e.device == dev) blocks = e.blocks;
+    }
+    if (blocks == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        blocks = std::min<unsigned>(kPersistentBlocks, unsigned(per_cu) * unsigned(cus));
+        std::lock_guard<std::mutex> lock(mu);
+        cache.push_back({kernel, dev, blocks});
+    }
+    return static_cast<unsigned>(items < blocks ? (items ? items : 1) : blocks);
+}
 
 // Layout of the per-device table blob.
 struct BlobLayout {

@@ -266,7 +266,8 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
  * on the caller's stream; nothing else changes.
  *   kernels : comma-separated kernel names ("dgc_update,ada_apply"), "*" for
  *             all, NULL or "" to disable.  Names: dgc_norm, dgc_prep,
- *             dgc_update, dgc_select, dgc_stage, dgc_refine, dgc_count,
+ *             dgc_sample, dgc_bound, dgc_update, dgc_select, dgc_stage,
+ *             dgc_refine, dgc_count,
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
  *             ada_apply,
  *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,

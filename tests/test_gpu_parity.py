@@ -92,6 +92,49 @@ def test_dgc_clip_active_and_deterministic():
         assert same_bits(gval, val) and same_bits(Ug, U) and same_bits(Vg, V)
 
 
+def _dgc_sample_positions(t):
+    """Flat positions the library samples to bound the top-k digit: per
+    4096-element chunk c (numbered over all segments in order), 32
+    contiguous elements at 128 * ((13 c) mod 32) in a full chunk, else the
+    chunk's first min(32, cnt)."""
+    pos, c = [], 0
+    for o, ln, _, _ in t:
+        for c0 in range(0, ln, 4096):
+            cnt = min(4096, ln - c0)
+            off = 128 * ((13 * c) % 32) if cnt == 4096 else 0
+            pos.extend(range(o + c0 + off, o + c0 + off + min(32, cnt)))
+            c += 1
+    return np.array(pos, np.int64)
+
+
+@pytest.mark.parametrize("layout", ["sampled_large", "sampled_large_ties"])
+def test_dgc_sample_bound_fallback(layout):
+    """Adversarial input for the sampled staging bound: the sampled elements
+    hold the largest values, spread over many octaves, so the sample's upper
+    quantile lies far above the true k-th largest value and the segment must
+    be re-staged from V.  Results stay bit-exact against the oracle, and a
+    second segment with ordinary values is unaffected."""
+    rng = np.random.default_rng(91)
+    t = W.make_table([3000, 4096 * 16 + 123, 50000], [50, 50, 50], [3, 200, 50])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    V = (rng.standard_normal(n) * 1e-20).astype(np.float32)
+    pos = _dgc_sample_positions(t)
+    o1, l1 = int(t[1][0]), int(t[1][1])
+    inseg = pos[(pos >= o1) & (pos < o1 + l1)]
+    mags = np.float32(2.0) ** (-(np.arange(inseg.size) / 4.0)).astype(np.float32)
+    if layout == "sampled_large_ties":
+        mags[150:260] = mags[150]  # a tie run across the k-th position
+    V[inseg] = (mags * np.where(rng.random(inseg.size) < 0.5, -1, 1)).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    G = (rng.standard_normal(n) * 1e-30).astype(np.float32)
+    say(f"dgc sample fallback {layout}")
+    U, Vo, idx, val, off, _ = oracle.dgc(t, G, z, V, 0.9, 0.0, 1)
+    Ug, Vg, gidx, gval, goff = hp.dgc(G, z.copy(), V.copy(), 0.9, 0.0, 1)
+    assert np.array_equal(goff, off) and np.array_equal(gidx, idx)
+    assert same_bits(gval, val) and same_bits(Ug, U) and same_bits(Vg, Vo)
+
+
 # ------------------------------------------------------------------ AdaComp
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
