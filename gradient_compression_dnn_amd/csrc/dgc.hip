@@ -12,13 +12,14 @@
 //           tree over the chunk sums and set the clip factor
 //   sample  (chunk) V' = V + (m U + c G) for 32 contiguous elements of the
 //           chunk; histogram of their digit 1 (key >> 20)
-//   bound   (segment) from the sample, a digit L1 that the k-th largest key
+//   bound   (segment) from the sample, a key Lkey that the k-th largest key
 //           almost surely reaches (the DGC paper estimates its threshold
 //           from a sample of the gradient, §3.1 / App. D)
 //   update  (chunk) U <- fl(fl(m U) + fl(c G)); V <- fl(V + U); LDS histogram
-//           of digit 1, flushed with global atomics; entries with digit 1 at
-//           or above L1 staged in index order at the chunk's own offset
-//   select1 (segment) digit 1 of the k-th largest key, d1; if d1 < L1 the
+//           of digit 1, flushed with global atomics; entries with key at or
+//           above Lkey staged in index order at the chunk's own offset
+//   select1 (segment) digit 1 of the k-th largest key, d1; if fewer than k
+//           entries were staged, the k-th largest key is below Lkey, the
 //           staging missed candidates and the segment is re-staged
 //   stage   (chunk) histogram digit 2 of the staged entries in the boundary
 //           bucket; for a re-staged segment, re-read V and stage digit 1 >= d1
@@ -41,8 +42,8 @@ namespace {
 struct SegState {
     float clip;
     uint32_t d1, above1, d2, above2, T, gt, need_eq;
-    uint32_t L1;    // staging bound on digit 1 from the sample
-    uint32_t redo;  // d1 < L1: re-stage the segment from V
+    uint32_t Lkey;  // staging bound on the key, from the sample
+    uint32_t redo;  // fewer than k staged: re-stage the segment from V
 };
 
 // Sample of a segment: in every stride-th chunk (at most kSampleChunks
@@ -63,6 +64,7 @@ __device__ __forceinline__ uint32_t sample_stride(uint32_t dnchunk) {
 // one address serialize, and a large segment is covered by hundreds of
 // workgroups.  The select kernels add the replicas.
 constexpr uint32_t kHistRep = 16;
+static_assert(kHist1 == kHist2, "the sample bound reuses one LDS histogram for digits 1 and 2");
 
 struct DgcWs {
     uint32_t *hist1, *hist2, *hist3;
@@ -71,7 +73,7 @@ struct DgcWs {
     uint32_t *ccount, *cgt, *ceq, *cout, *ctake;
     uint32_t *sidx;
     float *sval;
-    uint16_t *skey;  // [ndchunk][kSamples] digit 1 of the sampled V'
+    uint32_t *skey;  // [ndchunk][kSamples] key of the sampled V'
 };
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
@@ -89,7 +91,7 @@ DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.ctake = c.take<uint32_t>(p->ndchunk);
     w.sidx = c.take<uint32_t>(p->n_total);
     w.sval = c.take<float>(p->n_total);
-    w.skey = c.take<uint16_t>(size_t(p->ndchunk) * kSamples);
+    w.skey = c.take<uint32_t>(size_t(p->ndchunk) * kSamples);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
 // ---------------------------------------------------------------- sample
 // Half a wave per chunk: in a sampled chunk, lane l < min(32, cnt) computes
 // V' of element sample_offset + l with the update's own arithmetic and
-// records its digit 1 (plain stores: no atomics).
+// records its key (plain stores: no atomics).
 __global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const float *__restrict__ G,
                                                             const float *__restrict__ U,
                                                             const float *__restrict__ V, float m,
@@ -240,57 +242,72 @@ __global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const flo
     float un = m * U[e];
     un = un + gc;
     const float vn = V[e] + un;
-    w.skey[size_t(c) * kSamples + l] = static_cast<uint16_t>(mag_key(vn) >> (kDigit2Bits + kDigit3Bits));
+    w.skey[size_t(c) * kSamples + l] = mag_key(vn);
 }
 
 // ----------------------------------------------------------------- bound
 // Of S samples, about E = S k / n fall in the segment's top k (a binomial
-// count).  L1 is the digit-1 bucket of the (E + 4 sqrt(E) + 16)-th largest
-// sample, or 0 (stage everything) when the sample is too small for that.
-// A sampled chunk's 32 keys are 64 contiguous bytes: thread i loads 16-byte
-// piece i (piece 4 j + p of sampled chunk j), at most 8 per thread, all in
-// flight together, into an LDS histogram.
+// count).  Lkey is the (E + 4 sqrt(E) + 16)-th largest sample key, rounded
+// down to its 22-bit prefix (digits 1 and 2), or 0 (stage everything) when
+// the sample is too small for that.  A sampled chunk's 32 keys are 128
+// contiguous bytes: thread i loads 16-byte pieces i, i + 256, ... (piece
+// 8 j + p of sampled chunk j), at most 16 per thread, all in flight
+// together, and keeps them for the two LDS histogram passes.
 __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     __shared__ uint32_t h[kHist1];
-    for (int i = threadIdx.x; i < kHist1; i += kBlock) h[i] = 0u;
     const uint32_t stride = sample_stride(seg.dnchunk);
     const uint32_t nsc = (seg.dnchunk + stride - 1) / stride;  // sampled chunks
     const uint32_t last = (nsc - 1) * stride;                   // last sampled chunk
     const uint32_t last_cnt = min(seg.len - last * uint32_t(kChunk), uint32_t(kChunk));
     const uint32_t last_ns = min(kSamples, last_cnt);
     const uint32_t total = (nsc - 1) * kSamples + last_ns;
-    constexpr uint32_t kPer = kSampleChunks * 4 / kBlock;
+    const double E = double(total) * double(seg.k) / double(seg.len);
+    const double target = E + 4.0 * sqrt(E) + 16.0;
+    if (!(target < double(total))) {  // uniform: too few samples, stage everything
+        if (threadIdx.x == 0) w.st[s].Lkey = 0u;
+        return;
+    }
+    constexpr uint32_t kPer = kSampleChunks * (kSamples / 4) / kBlock;
+    const uint32_t npiece = nsc * (kSamples / 4);
     uint4 piece[kPer];
 #pragma unroll
     for (uint32_t u = 0; u < kPer; ++u) {
-        const uint32_t i = min(u * kBlock + threadIdx.x, nsc * 4 - 1);
-        const uint32_t c = seg.dchunk0 + (i >> 2) * stride;
-        piece[u] = *reinterpret_cast<const uint4 *>(w.skey + size_t(c) * kSamples + (i & 3) * 8);
+        const uint32_t i = min(u * kBlock + threadIdx.x, npiece - 1);
+        const uint32_t c = seg.dchunk0 + (i / (kSamples / 4)) * stride;
+        piece[u] = *reinterpret_cast<const uint4 *>(w.skey + size_t(c) * kSamples + (i % (kSamples / 4)) * 4);
     }
-    __syncthreads();
-#pragma unroll
-    for (uint32_t u = 0; u < kPer; ++u) {
+    // key q of piece u, or none (past the samples)
+    auto key_of = [&](uint32_t u, uint32_t q, uint32_t *key) {
         const uint32_t i = u * kBlock + threadIdx.x;
-        if (i >= nsc * 4) continue;
-        const uint32_t lim = (i >> 2) == nsc - 1 ? last_ns : kSamples;  // keys of the chunk
-        const uint32_t words[4] = {piece[u].x, piece[u].y, piece[u].z, piece[u].w};
+        const uint32_t lim = i / (kSamples / 4) == nsc - 1 ? last_ns : kSamples;
+        const uint32_t l = (i % (kSamples / 4)) * 4 + q;
+        *key = q == 0 ? piece[u].x : q == 1 ? piece[u].y : q == 2 ? piece[u].z : piece[u].w;
+        return i < npiece && l < lim;
+    };
+    uint32_t rank = static_cast<uint32_t>(target), prefix = 0;
+    for (int level = 0; level < 2; ++level) {
+        for (int i = threadIdx.x; i < kHist1; i += kBlock) h[i] = 0u;
+        __syncthreads();
 #pragma unroll
-        for (uint32_t q = 0; q < 8; ++q) {
-            const uint32_t l = (i & 3) * 8 + q;
-            if (l < lim) atomicAdd(&h[(words[q >> 1] >> (16 * (q & 1))) & 0xFFFFu], 1u);
-        }
-    }
-    __syncthreads();
-    const double E = double(total) * double(seg.k) / double(seg.len);
-    const double target = E + 4.0 * sqrt(E) + 16.0;
-    uint32_t L1 = 0;
-    if (target < double(total)) {
+        for (uint32_t u = 0; u < kPer; ++u)
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                uint32_t key;
+                if (!key_of(u, q, &key)) continue;
+                const uint32_t d1 = key >> (kDigit2Bits + kDigit3Bits);
+                if (level == 0) atomicAdd(&h[d1], 1u);
+                else if (d1 == prefix) atomicAdd(&h[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            }
+        __syncthreads();
         uint32_t above;
-        L1 = block_find_bucket<kHist1>(static_cast<uint32_t>(target), [&](int b) { return h[b]; }, &above);
+        const uint32_t d = block_find_bucket<kHist1>(rank, [&](int b) { return h[b]; }, &above);
+        rank -= above;
+        prefix = level == 0 ? d : ((prefix << kDigit2Bits) | d);
+        __syncthreads();
     }
-    if (threadIdx.x == 0) w.st[s].L1 = L1;
+    if (threadIdx.x == 0) w.st[s].Lkey = prefix << kDigit3Bits;
 }
 
 // ---------------------------------------------------------------- update
@@ -324,7 +341,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
     const int lane = lane_id(), wave = wave_id();
     for (uint32_t c = c0; c < c1; ++c) {
         const float clip = w.st[ci.s].clip;
-        const uint32_t L1 = w.st[ci.s].L1;
+        const uint32_t Lkey = w.st[ci.s].Lkey;
         uint32_t flags[kRows], before[kRows];
 #pragma unroll
         for (int j = 0; j < kRows; ++j) {
@@ -343,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
                 const bool in = e0 + q < ci.cnt;
                 const uint32_t d = mag_key(vn) >> (kDigit2Bits + kDigit3Bits);
                 if (in) atomicAdd(&hist[d], 1u);
-                const bool f = in && d >= L1;
+                const bool f = in && mag_key(vn) >= Lkey;
                 flags[j] |= uint32_t(f) << q;
                 const uint64_t bm = __ballot(f);
                 before[j] += lane_rank(bm);
@@ -428,10 +445,23 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
     if (kLevel == 1) {
         const uint32_t *h = w.hist1 + size_t(s) * kHistRep * kHist1;
         uint32_t d = block_find_bucket<kHist1>(seg.k, [&](int b) { return replica_sum<kHist1>(h, b); }, &above);
+        // entries the update staged in the segment (all keys >= Lkey)
+        uint32_t staged = 0;
+        for (uint32_t i0 = 0; i0 < seg.dnchunk; i0 += 8 * kBlock) {
+            uint32_t n[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                n[u] = w.ccount[seg.dchunk0 + min(i0 + u * kBlock + threadIdx.x, seg.dnchunk - 1)];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                if (i0 + u * kBlock + threadIdx.x < seg.dnchunk) staged += n[u];
+        }
+        uint32_t staged_total;
+        (void)block_exclusive_scan(staged, &staged_total);
         if (threadIdx.x == 0) {
             w.st[s].d1 = d;
             w.st[s].above1 = above;
-            w.st[s].redo = d < st.L1 ? 1u : 0u;
+            w.st[s].redo = staged_total < seg.k ? 1u : 0u;
         }
     } else if (kLevel == 2) {
         const uint32_t *h = w.hist2 + size_t(s) * kHistRep * kHist2;
