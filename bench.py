@@ -33,8 +33,8 @@ def algorithmic_bytes(n: int, nbins: int, k_total: int, ada_entries: int, bucket
     return {
         "dgc_update": 20 * n,                 # read G, U, V; write U, V
         "dgc_norm": 4 * n,                    # read G
-        "ada_max": 8 * n,                     # read R, dW
-        "ada_apply": 12 * n + 8 * ada_entries,  # read R, dW; write R; message
+        "ada_fold": 12 * n,                   # read R, dW; write R (deferred residual: one pass)
+        "ada_emit": 8 * ada_entries,          # message
         "dcd": 12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket),  # x, x_half, x_out, codes, scales
         "decode": 4 * n + 4 * (k_total + ada_entries),  # dense write; the two messages, per launch
         "dgc_emit": 8 * k_total + 8 * k_total,  # message out + masking writes
@@ -148,6 +148,7 @@ def main(argv=None):
     U = torch.zeros(n, dtype=torch.float32, device=dev)
     V = torch.zeros_like(U)
     R = torch.zeros_like(U)
+    astate = plan.adacomp_state(dev)  # deferred residual: (R, astate) is the learner's residual
     XO = torch.zeros_like(U)
     dmsg = B.Sparse.empty(plan, plan.total_k, dev)
     amsg = B.Sparse.empty(plan, n, dev)
@@ -167,7 +168,7 @@ def main(argv=None):
         g = G[t % len(G)]
         B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC])
         B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK])
-        B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP])
+        B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=astate)
         B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK])
         B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE])
         B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE])

@@ -56,7 +56,10 @@ _SIGS = {
     "gc_plan_total_bins": (ctypes.c_uint64, [_P]),
     "gc_topk_count": (ctypes.c_uint32, [ctypes.c_uint32]),
     "gc_plan_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int]),
-    "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.c_float, _P, _P,
+                                           ctypes.c_size_t, _P]),
+    "gc_adacomp_state_bytes": (ctypes.c_size_t, [_P]),
+    "gc_adacomp_residual": (ctypes.c_int, [_P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gc_dgc_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]),
     "gc_pack_bound": (ctypes.c_uint64, [_P, ctypes.c_int]),
@@ -71,6 +74,7 @@ _SIGS = {
 
 KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_update", "dgc_select", "dgc_stage", "dgc_refine",
            "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
+           "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd")
 
 
@@ -183,6 +187,15 @@ class Plan:
     def pack_bound(self, kind: int) -> int:
         return int(load().gc_pack_bound(self.handle, kind))
 
+    @property
+    def adacomp_state_bytes(self) -> int:
+        return int(load().gc_adacomp_state_bytes(self.handle))
+
+    def adacomp_state(self, device="cuda") -> torch.Tensor:
+        """A zero-filled deferred-residual state for one learner (torch
+        allocations are 256-byte aligned)."""
+        return torch.zeros(max(self.adacomp_state_bytes, 1), dtype=torch.uint8, device=device)
+
 
 def gc_plan_create(table, n_total=None) -> Plan:
     return Plan(table, n_total)
@@ -227,12 +240,26 @@ class Sparse:
 
 
 # -------------------------------------------------------------- hot calls
-def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws: torch.Tensor):
+def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws: torch.Tensor,
+                        state: torch.Tensor | None = None):
+    """state None: R is the exact residual.  state (Plan.adacomp_state()):
+    deferred mode, the residual is (R, state)."""
     n = plan.n_total
     msg = out.struct()
-    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"),
-                                      float(scale_factor), ctypes.byref(msg), _ptr(ws), ws.numel(),
-                                      _stream(R)))
+    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _ptr(state),
+                                      state.numel() if state is not None else 0, float(scale_factor),
+                                      ctypes.byref(msg), _ptr(ws), ws.numel(), _stream(R)))
+
+
+def gc_adacomp_state_bytes(plan: Plan) -> int:
+    return plan.adacomp_state_bytes
+
+
+def gc_adacomp_residual(plan: Plan, R, state: torch.Tensor | None, R_out):
+    n = plan.n_total
+    _check(load().gc_adacomp_residual(plan.handle, _f32(R, n, "R"), _ptr(state),
+                                      state.numel() if state is not None else 0,
+                                      _f32(R_out, n, "R_out"), _stream(R_out)))
 
 
 def gc_dgc_step(plan: Plan, G, U, V, momentum: float, thr_G: float, num_nodes: int, out: Sparse,

@@ -31,7 +31,25 @@ struct AdaWs {
     float *gmax;
     double *bpartial;
     uint32_t *ccount, *cpre;
+    uint16_t *sign;  // [nachunk][kBlock] deferred mode: sign bits of this step's G
 };
+
+// Deferred-residual state of one learner (caller-owned, zero before the
+// first step).  Thread t of chunk c holds 16 elements, (row j, q) at bit
+// 4 j + q of word c * kBlock + t.
+struct AdaState {
+    uint16_t *sel;  // [nachunk][kBlock] entries sent in the last step
+    float *scale;   // [nseg] layer scales of the last step
+};
+
+AdaState ada_state_layout(const gc_plan *p, void *base, size_t *bytes) {
+    WsCursor c(base);
+    AdaState st{};
+    st.sel = c.take<uint16_t>(size_t(p->nachunk) * kBlock);
+    st.scale = c.take<float>(p->nseg);
+    if (bytes) *bytes = c.used;
+    return st;
+}
 
 AdaWs ada_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
@@ -41,6 +59,7 @@ AdaWs ada_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.bpartial = c.take<double>(p->nbgroup);
     w.ccount = c.take<uint32_t>(p->nachunk);
     w.cpre = c.take<uint32_t>(p->nachunk);
+    w.sign = c.take<uint16_t>(size_t(p->nachunk) * kBlock);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -91,21 +110,10 @@ __device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const f
     }
 }
 
-__global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float *__restrict__ dW,
-                                                         const float *__restrict__ R, float sf,
-                                                         AdaWs w) {
-    const uint32_t c = blockIdx.x;
-    const AChunk a = achunk_info(P, c);
-    const uint32_t L = a.seg.bin_len;
-    const float invL = 1.0f / static_cast<float>(L);
-    const uint32_t nb = (a.cnt + L - 1) / L;
-    __shared__ uint32_t gm[kChunk];
-    for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = 0u;
-    float g[kRows][4];
-    uint32_t bin[kRows][4];
-    chunk_G(a, R, dW, invL, g, bin);
-    __syncthreads();
-    // bin maxima of |G| (as bit patterns, which order like the values)
+// Bin maxima of |G| over the chunk into the LDS array gm (zeroed by the
+// caller, then a barrier), as bit patterns, which order like the values.
+__device__ __forceinline__ void chunk_bin_max(const AChunk &a, const float (&g)[kRows][4],
+                                              const uint32_t (&bin)[kRows][4], uint32_t *gm) {
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
         const uint32_t e0 = row_elem(j);
@@ -139,19 +147,39 @@ __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float 
             if (live) atomicMax(&gm[cur], mv);
         }
     }
+}
+
+// Selection against the bin maxima: element (row j, q) is sent when its
+// bin's max is positive and fl(sf |G|) reaches it.
+__device__ __forceinline__ bool selected(const AChunk &a, uint32_t e, float gq, uint32_t b, float sf,
+                                         const uint32_t *gm) {
+    const bool in = e < a.cnt;
+    const float gmx = dev_u2f(gm[in ? b : 0u]);
+    const float t = sf * fabsf(gq);
+    return in && gmx > 0.0f && t >= gmx;
+}
+
+__global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float *__restrict__ dW,
+                                                         const float *__restrict__ R, float sf,
+                                                         AdaWs w) {
+    const uint32_t c = blockIdx.x;
+    const AChunk a = achunk_info(P, c);
+    const uint32_t L = a.seg.bin_len;
+    const float invL = 1.0f / static_cast<float>(L);
+    const uint32_t nb = (a.cnt + L - 1) / L;
+    __shared__ uint32_t gm[kChunk];
+    for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = 0u;
+    float g[kRows][4];
+    uint32_t bin[kRows][4];
+    chunk_G(a, R, dW, invL, g, bin);
+    __syncthreads();
+    chunk_bin_max(a, g, bin, gm);
     __syncthreads();
     uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < kRows; ++j) {
-        const uint32_t e0 = row_elem(j);
+    for (int j = 0; j < kRows; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool in = e0 + q < a.cnt;
-            const float gmx = dev_u2f(gm[in ? bin[j][q] : 0u]);
-            const float t = sf * fabsf(g[j][q]);
-            mine += (in && gmx > 0.0f && t >= gmx) ? 1u : 0u;
-        }
-    }
+        for (int q = 0; q < 4; ++q) mine += selected(a, row_elem(j) + q, g[j][q], bin[j][q], sf, gm) ? 1u : 0u;
     uint32_t total;
     (void)block_exclusive_scan(mine, &total);
     float *gout = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
@@ -181,12 +209,17 @@ __global__ __launch_bounds__(kBlock) void ada_binsum_kernel(PlanDev P, AdaWs w) 
 }
 
 __global__ __launch_bounds__(kBlock) void ada_scale_kernel(PlanDev P, AdaWs w,
-                                                           float *__restrict__ seg_scale) {
+                                                           float *__restrict__ seg_scale,
+                                                           float *__restrict__ state_scale) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     const double *part = w.bpartial + seg.bgroup0;
     double S = block_pairwise_sum(seg.nbgroup, [&](uint64_t i) { return part[i]; });
-    if (threadIdx.x == 0) seg_scale[s] = static_cast<float>(S / static_cast<double>(seg.nbins));
+    if (threadIdx.x == 0) {
+        const float scale = static_cast<float>(S / static_cast<double>(seg.nbins));
+        seg_scale[s] = scale;
+        if (state_scale) state_scale[s] = scale;
+    }
     uint32_t before = 0;
     for (uint32_t r = 0; r < seg.anchunk; r += kBlock) {
         bool in = r + threadIdx.x < seg.anchunk;
@@ -266,6 +299,123 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
     }
 }
 
+// ---------------------------------------------------------- deferred mode
+// The residual of an entry sent in step t is fl(G - copysign(scale_t, G)).
+// In deferred mode R keeps G after the call and the state keeps which
+// entries were sent and scale_t; the next call (or gc_adacomp_residual)
+// applies exactly that expression to R before anything else reads it.  One
+// dense pass then reads R and dW once and writes R once:
+//   fold   one workgroup per chunk: R' = pending correction of R, G = R' + dW,
+//          R <- G; bin maxima; selection bits (state) and sign bits
+//          (workspace); count of selected entries
+//   (binsum, scale, offsets as in the exact mode; scale also records scale_t)
+//   emit   one workgroup per chunk: message (idx, copysign(scale, G)) from the
+//          bits, in index order at its final slot
+
+// R' for the element at bit `bit` of the thread's word.
+__device__ __forceinline__ float pending(float r, uint32_t held, int bit, float pscale) {
+    return ((held >> bit) & 1u) ? r - copysignf(pscale, r) : r;
+}
+
+__global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float *__restrict__ dW,
+                                                          float *__restrict__ R, float sf, AdaWs w,
+                                                          AdaState S) {
+    const uint32_t c = blockIdx.x;
+    const AChunk a = achunk_info(P, c);
+    const uint32_t L = a.seg.bin_len;
+    const float invL = 1.0f / static_cast<float>(L);
+    const uint32_t nb = (a.cnt + L - 1) / L;
+    __shared__ uint32_t gm[kChunk];
+    for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = 0u;
+    const BufRsrc rr = chunk_buf(R + a.lo, a.cnt), rd = chunk_buf(dW + a.lo, a.cnt);
+    const size_t word = size_t(c) * kBlock + threadIdx.x;
+    const uint32_t held = S.sel[word];
+    const float pscale = S.scale[a.s];
+    float g[kRows][4];
+    uint32_t bin[kRows][4];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        float r[4], d[4];
+        load4(rr, row_elem(j), r);
+        load4(rd, row_elem(j), d);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g[j][q] = pending(r[q], held, 4 * j + q, pscale) + d[q];
+            bin[j][q] = div_small(row_elem(j) + q, L, invL);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) store4(rr, row_elem(j), g[j]);
+    __syncthreads();
+    chunk_bin_max(a, g, bin, gm);
+    __syncthreads();
+    uint32_t bits = 0, signs = 0, mine = 0;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool f = selected(a, row_elem(j) + q, g[j][q], bin[j][q], sf, gm);
+            bits |= uint32_t(f) << (4 * j + q);
+            signs |= (dev_f2u(g[j][q]) >> 31) << (4 * j + q);
+            mine += f ? 1u : 0u;
+        }
+    S.sel[word] = static_cast<uint16_t>(bits);
+    w.sign[word] = static_cast<uint16_t>(signs);
+    uint32_t total;
+    (void)block_exclusive_scan(mine, &total);
+    float *gout = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
+    for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gout[b] = dev_u2f(gm[b]);
+    if (threadIdx.x == 0) w.ccount[c] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void ada_emit_kernel(PlanDev P, AdaWs w, AdaState S,
+                                                          const uint32_t *__restrict__ seg_off,
+                                                          const float *__restrict__ seg_scale,
+                                                          uint32_t *__restrict__ out_idx,
+                                                          float *__restrict__ out_val) {
+    const uint32_t c = blockIdx.x;
+    const AChunk a = achunk_info(P, c);
+    const size_t word = size_t(c) * kBlock + threadIdx.x;
+    const uint32_t bits = S.sel[word], signs = w.sign[word];
+    const float scale = seg_scale[a.s];
+    const uint32_t base = seg_off[a.s] + w.cpre[c];
+    const uint32_t count = w.ccount[c];
+    bool flag[kRows][4];
+    uint32_t pos[kRows][4];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) flag[j][q] = (bits >> (4 * j + q)) & 1u;
+    (void)block_compact4(flag, pos);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (flag[j][q] && pos[j][q] < count) {
+                out_idx[base + pos[j][q]] = static_cast<uint32_t>(a.lo + row_elem(j) + q);
+                out_val[base + pos[j][q]] = copysignf(scale, ((signs >> (4 * j + q)) & 1u) ? -1.0f : 1.0f);
+            }
+        }
+}
+
+// R_out <- the exact residual held by (R, state), segment elements only.
+__global__ __launch_bounds__(kBlock) void ada_residual_kernel(PlanDev P, const float *__restrict__ R,
+                                                              AdaState S, float *__restrict__ R_out) {
+    const uint32_t c = blockIdx.x;
+    const AChunk a = achunk_info(P, c);
+    const BufRsrc rr = chunk_buf(R + a.lo, a.cnt), ro = chunk_buf(R_out + a.lo, a.cnt);
+    const uint32_t held = S.sel[size_t(c) * kBlock + threadIdx.x];
+    const float pscale = S.scale[a.s];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        float r[4];
+        load4(rr, row_elem(j), r);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = pending(r[q], held, 4 * j + q, pscale);
+        store4(ro, row_elem(j), r);
+    }
+}
+
 }  // namespace
 
 size_t adacomp_workspace_bytes(const gc_plan *plan) {
@@ -278,9 +428,16 @@ size_t adacomp_workspace_bytes(const gc_plan *plan) {
 
 using namespace gc;
 
-extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R,
-                                         float scale_factor, gc_sparse *out, void *ws,
-                                         size_t ws_bytes, hipStream_t stream) {
+extern "C" size_t gc_adacomp_state_bytes(const gc_plan *plan) {
+    if (!plan) return 0;
+    size_t b = 0;
+    (void)ada_state_layout(plan, nullptr, &b);
+    return b;
+}
+
+extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, void *state,
+                                         size_t state_bytes, float scale_factor, gc_sparse *out,
+                                         void *ws, size_t ws_bytes, hipStream_t stream) {
     clear_error();
     if (!plan) return set_error(GC_EINVAL, "gc_adacomp_compress: plan is null");
     if (!dW || !R) return set_error(GC_EINVAL, "gc_adacomp_compress: dW and R must be non-null");
@@ -297,17 +454,59 @@ extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, f
                          "gc_adacomp_compress: workspace smaller than gc_plan_workspace_bytes");
     if (reinterpret_cast<uintptr_t>(ws) % 256)
         return set_error(GC_EINVAL, "gc_adacomp_compress: workspace must be 256-byte aligned");
+    if (state && state_bytes < gc_adacomp_state_bytes(plan))
+        return set_error(GC_ECAPACITY, "gc_adacomp_compress: state smaller than gc_adacomp_state_bytes");
+    if (state && reinterpret_cast<uintptr_t>(state) % 256)
+        return set_error(GC_EINVAL, "gc_adacomp_compress: state must be 256-byte aligned");
     PlanDev P;
     gc_status st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     AdaWs w = ada_layout(plan, ws, nullptr);
-    GC_LAUNCH("ada_max", stream, ada_max_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w));
-    GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale));
-    GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
-    GC_LAUNCH("ada_apply", stream, ada_apply_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
-        P, dW, R, scale_factor, w, out->seg_off, out->seg_scale, out->idx, out->val));
+    if (state) {
+        const AdaState S = ada_state_layout(plan, state, nullptr);
+        GC_LAUNCH("ada_fold", stream, ada_fold_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w, S));
+        GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
+        GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale, S.scale));
+        GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
+        GC_LAUNCH("ada_emit", stream, ada_emit_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
+            P, w, S, out->seg_off, out->seg_scale, out->idx, out->val));
+    } else {
+        GC_LAUNCH("ada_max", stream, ada_max_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w));
+        GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
+        GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale, nullptr));
+        GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
+        GC_LAUNCH("ada_apply", stream, ada_apply_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
+            P, dW, R, scale_factor, w, out->seg_off, out->seg_scale, out->idx, out->val));
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_adacomp_compress launch");
+    return GC_OK;
+}
+
+extern "C" gc_status gc_adacomp_residual(const gc_plan *plan, const float *R, const void *state,
+                                         size_t state_bytes, float *R_out, hipStream_t stream) {
+    clear_error();
+    if (!plan) return set_error(GC_EINVAL, "gc_adacomp_residual: plan is null");
+    if (!R || !R_out) return set_error(GC_EINVAL, "gc_adacomp_residual: R and R_out must be non-null");
+    const uint64_t bytes = plan->n_total * sizeof(float);
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(R), o0 = reinterpret_cast<uintptr_t>(R_out);
+    if (bytes && r0 < o0 + bytes && o0 < r0 + bytes)
+        return set_error(GC_EINVAL, "gc_adacomp_residual: R_out must not overlap R");
+    if (state && state_bytes < gc_adacomp_state_bytes(plan))
+        return set_error(GC_ECAPACITY, "gc_adacomp_residual: state smaller than gc_adacomp_state_bytes");
+    if (state && reinterpret_cast<uintptr_t>(state) % 256)
+        return set_error(GC_EINVAL, "gc_adacomp_residual: state must be 256-byte aligned");
+    PlanDev P;
+    gc_status st = plan_device(plan, &P);
+    if (st != GC_OK) return st;
+    // elements outside every segment carry over unchanged
+    hipError_t e = hipMemcpyAsync(R_out, R, bytes, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_error(e, "gc_adacomp_residual copy");
+    if (state) {
+        const AdaState S = ada_state_layout(plan, const_cast<void *>(state), nullptr);
+        GC_LAUNCH("ada_residual", stream, ada_residual_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, R, S, R_out));
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_adacomp_residual launch");
     return GC_OK;
 }

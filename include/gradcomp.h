@@ -155,14 +155,40 @@ typedef struct gc_sparse {
  *   a6  out: per segment, ascending idx with val = q_i; out->seg_scale[s] = scale_s.
  * PSUM64(x_0..x_{m-1}) converts each term to double, pads with +0.0 to the
  * next power of two and adds as a perfect binary tree in index order.
+ *
+ * Residual storage.  A learner's residual is the pair (R, state):
+ *   state == NULL : R holds the exact residual before and after the call.
+ *   state != NULL : deferred mode.  `state` is a caller-owned, 256-byte
+ *     aligned device buffer of at least gc_adacomp_state_bytes(plan) bytes,
+ *     zero-filled before the learner's first step and used with this plan
+ *     only.  After a call, R holds G and the state records which entries the
+ *     call sent and the layer scales; the residual of such an entry is
+ *     fl32(R_i - copysign(scale_s, R_i)) (step a5, exactly), which the next
+ *     call applies before a1.  R and dW then cross HBM once per step instead
+ *     of twice.  Messages are identical in both modes; gc_adacomp_residual()
+ *     gives the exact residual of (R, state).
  *   dW  [n_total] in,  R [n_total] in/out,  out: cap >= n_total (worst case).
  *   ws  : at least gc_plan_workspace_bytes(plan, GC_OP_ADACOMP) bytes.
- * Errors: GC_EINVAL (null pointer, scale_factor not finite or < 1),
- *         GC_ECAPACITY (out->cap < n_total or ws too small).
+ * Errors: GC_EINVAL (null pointer, scale_factor not finite or < 1, state
+ *         not 256-byte aligned), GC_ECAPACITY (out->cap < n_total, ws or
+ *         state too small).
  */
-gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R,
-                              float scale_factor, gc_sparse *out,
+gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, void *state,
+                              size_t state_bytes, float scale_factor, gc_sparse *out,
                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of one learner's deferred-residual state for this plan (0 if plan
+ * is NULL). */
+size_t gc_adacomp_state_bytes(const gc_plan *plan);
+
+/* R_out[n_total] <- the exact residual held by (R, state): elements outside
+ * every segment are copied, in-segment elements sent in the last deferred
+ * step get fl32(R_i - copysign(scale_s, R_i)).  state == NULL copies R.
+ * R_out must not overlap R; R and state are not modified.
+ * Errors: GC_EINVAL (null R or R_out, overlap, misaligned state),
+ *         GC_ECAPACITY (state smaller than gc_adacomp_state_bytes). */
+gc_status gc_adacomp_residual(const gc_plan *plan, const float *R, const void *state,
+                              size_t state_bytes, float *R_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------- DGC */
 /*
@@ -269,7 +295,7 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
  *             dgc_sample, dgc_bound, dgc_update, dgc_select, dgc_stage,
  *             dgc_refine, dgc_count,
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
- *             ada_apply,
+ *             ada_apply, ada_fold, ada_emit, ada_residual,
  *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,
  *             decode, dcd.
  * gc_timing_take waits for the recorded events of one kernel and returns the

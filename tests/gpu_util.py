@@ -62,12 +62,22 @@ class HipPath:
         idx, val, off, _ = out.host()
         return Ud.cpu().numpy(), Vd.cpu().numpy(), idx, val, off
 
-    def adacomp(self, dW, R, scale_factor=2.0, tensors=False):
+    def adacomp(self, dW, R, scale_factor=2.0, tensors=False, state=None):
+        """One AdaComp call; with `state` (a deferred-residual state tensor) the
+        returned R is the exact residual, materialized by gc_adacomp_residual,
+        while the device R keeps the deferred form."""
         dWd = dW if torch.is_tensor(dW) else to_dev(dW)
         Rd = R if torch.is_tensor(R) else to_dev(R)
         out = B.Sparse.empty(self.plan, self.n, dev())
-        B.gc_adacomp_compress(self.plan, dWd, Rd, scale_factor, out, self.workspace(B.GC_OP_ADACOMP))
+        B.gc_adacomp_compress(self.plan, dWd, Rd, scale_factor, out, self.workspace(B.GC_OP_ADACOMP),
+                              state=state)
         torch.cuda.synchronize()
+        if state is not None and not tensors:
+            exact = torch.empty_like(Rd)
+            B.gc_adacomp_residual(self.plan, Rd, state, exact)
+            torch.cuda.synchronize()
+            idx, val, off, scale = out.host()
+            return exact.cpu().numpy(), idx, val, off, scale[:self.plan.nseg]
         if tensors:
             return Rd, out
         idx, val, off, scale = out.host()

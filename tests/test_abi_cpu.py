@@ -79,6 +79,9 @@ def test_plan_queries_and_workspace_on_workloads():
             assert p.workspace_bytes(op) > 0
         # staging needs 8 bytes per element at most, plus small tables
         assert p.workspace_bytes(B.GC_OP_DGC) < 9 * w.n_total + (64 << 20)
+        # deferred AdaComp state: one selection bit per element slot, plus the scales
+        assert p.adacomp_state_bytes >= w.n_total // 8
+        assert p.adacomp_state_bytes < w.n_total // 8 + (4 << 20)
         # the pack bound covers the format's closed form at k entries per segment
         E = t[:, 3]
         assert p.pack_bound(B.GC_KIND_DGC) >= 16 + int(np.sum(16 + 6 * E + 2 * (E % 2)))
@@ -88,7 +91,9 @@ def test_plan_queries_and_workspace_on_workloads():
 def test_hot_calls_reject_null_plan_without_touching_a_device():
     lib = B.load()
     assert lib.gc_dgc_step(None, None, None, None, 0.9, 0.0, 1, None, None, 0, None) == B.GC_EINVAL
-    assert lib.gc_adacomp_compress(None, None, None, 2.0, None, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_adacomp_compress(None, None, None, None, 0, 2.0, None, None, 0, None) == B.GC_EINVAL
+    assert lib.gc_adacomp_residual(None, None, None, 0, None, None) == B.GC_EINVAL
+    assert lib.gc_adacomp_state_bytes(None) == 0
     assert lib.gc_pack(None, 1, None, None, 0, None, None, 0, None) == B.GC_EINVAL
     assert lib.gc_decompress_accumulate(None, None, 1, None, 1, 0, None, 0, None) == B.GC_EINVAL
     assert lib.gc_dcd_compress(None, None, None, 10, 4, 512, 0, 0, None, None, None) == B.GC_EINVAL

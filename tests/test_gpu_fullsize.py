@@ -116,3 +116,27 @@ def test_deepspeech_dgc_adacomp_pack_dcd():
     gx, gsc, gcodes, tail = dcd(x, xh, 4, 512, 0x5EED, 0, inplace=True)
     assert same_bits(gsc, sc) and np.array_equal(gcodes, codes) and same_bits(gx, xo)
     assert np.all(tail == 0)
+
+
+def test_deepspeech_adacomp_deferred_two_steps():
+    """The benchmark's AdaComp configuration: deferred residual, two steps on
+    the full 122M-element layout; messages and the materialized residual
+    against the oracle's exact residual."""
+    w = W.make_config("deepspeech")
+    t, n = w.table, w.n_total
+    hp = HipPath(t, n)
+    state = hp.plan.adacomp_state()
+    Rd = torch.zeros(n, dtype=torch.float32, device="cuda")
+    R = np.zeros(n, np.float32)
+    for step in range(2):
+        g = W.gradient(w, step)
+        tag = f"deepspeech adacomp deferred step {step}"
+        say(f"{tag}: oracle")
+        R, idx, val, off, scale, _ = oracle.adacomp(t, g, R, 2.0)
+        say(f"{tag}: hip")
+        Rg, gidx, gval, goff, gscale = hp.adacomp(g, Rd, 2.0, state=state)
+        assert np.array_equal(goff, off), tag
+        assert same_bits(gscale, scale), ulp_report(gscale, scale)
+        assert np.array_equal(gidx, idx), tag
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Rg, R), ulp_report(Rg, R)

@@ -10,7 +10,7 @@ import torch
 import oracle
 from gradient_compression_dnn_amd import binding as B
 from gradient_compression_dnn_amd import workloads as W
-from tests.gpu_util import HipPath, dcd, same_bits, say, sparse_from_host, ulp_report
+from tests.gpu_util import HipPath, dcd, same_bits, say, sparse_from_host, to_dev, ulp_report
 
 pytestmark = pytest.mark.gpu
 
@@ -169,6 +169,66 @@ def test_adacomp_constant_and_single_bin():
     Rg, gidx, gval, goff, gscale = hp.adacomp(dW, z.copy())
     assert np.array_equal(gidx, idx) and same_bits(Rg, R) and same_bits(gscale, scale)
     assert gidx.size == n and np.all(Rg == 0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
+def test_adacomp_deferred_multistep(seed, kind):
+    """Deferred residual mode: the device R holds G and the state the pending
+    corrections; every step's message and the materialized residual match the
+    oracle's exact residual bit for bit."""
+    rng = np.random.default_rng(300 + seed)
+    t = mixed_table(rng, int(rng.integers(1, 14)))
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    R = W.random_values(rng, n, kind)
+    Rd = to_dev(R)
+    state = hp.plan.adacomp_state()
+    sf = [2.0, 1.0, 3.5, 2.0][seed]
+    for step in range(4):
+        dW = W.random_values(rng, n, kind)
+        say(f"adacomp deferred seed={seed} kind={kind} nseg={len(t)} n={n} step={step} sf={sf}")
+        R, idx, val, off, scale, _ = oracle.adacomp(t, dW, R, sf)
+        Rg, gidx, gval, goff, gscale = hp.adacomp(dW, Rd, sf, state=state)
+        assert np.array_equal(goff, off), "segment offsets"
+        assert same_bits(gscale, scale), ulp_report(gscale, scale)
+        assert np.array_equal(gidx, idx), "selected indices"
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Rg, R), ulp_report(Rg, R)
+
+
+def test_adacomp_deferred_state_checks():
+    t = W.make_table([5000, 300], [50, 50], [5, 1])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    rng = np.random.default_rng(3)
+    dW, R = to_dev(W.random_values(rng, n)), to_dev(W.random_values(rng, n))
+    R0 = R.clone()
+    out = B.Sparse.empty(hp.plan, n, "cuda")
+    ws = hp.workspace(B.GC_OP_ADACOMP)
+    say("adacomp deferred state checks")
+    small = torch.zeros(hp.plan.adacomp_state_bytes - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.GCError) as e:
+        B.gc_adacomp_compress(hp.plan, dW, R, 2.0, out, ws, state=small)
+    assert e.value.status == B.GC_ECAPACITY
+    big = torch.zeros(hp.plan.adacomp_state_bytes + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.GCError) as e:
+        B.gc_adacomp_compress(hp.plan, dW, R, 2.0, out, ws, state=big[4:])
+    assert e.value.status == B.GC_EINVAL
+    with pytest.raises(B.GCError) as e:
+        B.gc_adacomp_residual(hp.plan, R, None, R)
+    assert e.value.status == B.GC_EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(R, R0), "a rejected call wrote R"
+    # without a state the residual is a copy; with a fresh (zero) state as well
+    cp = torch.empty_like(R)
+    B.gc_adacomp_residual(hp.plan, R, None, cp)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, R)
+    cp.zero_()
+    B.gc_adacomp_residual(hp.plan, R, hp.plan.adacomp_state(), cp)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, R)
 
 
 # --------------------------------------------------------------------- pack
