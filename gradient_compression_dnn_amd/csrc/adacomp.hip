@@ -64,23 +64,25 @@ AdaWs ada_layout(const gc_plan *p, void *base, size_t *bytes) {
     return w;
 }
 
+// A chunk from its 16-byte record, so the chunk's data loads can go out
+// after one round trip; the bin length comes from the segment record, which
+// is fetched alongside.
 struct AChunk {
     uint32_t s;
-    SegDev seg;
-    uint32_t pos;  // chunk number inside the segment
-    uint64_t lo;   // first flat element
-    uint32_t cnt;  // elements
+    uint64_t lo;         // first flat element
+    uint32_t cnt;        // elements
+    uint32_t bin_first;  // first bin of the chunk in the plan-wide bin array
+    uint32_t L;          // bin length
 };
 
 __device__ __forceinline__ AChunk achunk_info(const PlanDev &P, uint32_t c) {
+    const ChunkRec rec = P.achunk_rec[c];
     AChunk a;
-    a.s = P.achunk_seg[c];
-    a.seg = P.seg[a.s];
-    a.pos = c - a.seg.achunk0;
-    uint32_t first = a.pos * a.seg.achunk_len;
-    a.lo = a.seg.off + first;
-    uint32_t rem = a.seg.len - first;
-    a.cnt = rem < a.seg.achunk_len ? rem : a.seg.achunk_len;
+    a.lo = rec.x;
+    a.cnt = rec.y;
+    a.s = rec.z;
+    a.bin_first = rec.w;
+    a.L = P.seg[a.s].bin_len;
     return a;
 }
 
@@ -105,7 +107,7 @@ __device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const f
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             g[j][q] = r[q] + d[q];
-            bin[j][q] = div_small(row_elem(j) + q, a.seg.bin_len, invL);
+            bin[j][q] = div_small(row_elem(j) + q, a.L, invL);
         }
     }
 }
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float 
                                                          AdaWs w) {
     const uint32_t c = blockIdx.x;
     const AChunk a = achunk_info(P, c);
-    const uint32_t L = a.seg.bin_len;
+    const uint32_t L = a.L;
     const float invL = 1.0f / static_cast<float>(L);
     const uint32_t nb = (a.cnt + L - 1) / L;
     __shared__ uint32_t gm[kChunk];
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float 
         for (int q = 0; q < 4; ++q) mine += selected(a, row_elem(j) + q, g[j][q], bin[j][q], sf, gm) ? 1u : 0u;
     uint32_t total;
     (void)block_exclusive_scan(mine, &total);
-    float *gout = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
+    float *gout = w.gmax + a.bin_first;
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gout[b] = dev_u2f(gm[b]);
     if (threadIdx.x == 0) w.ccount[c] = total;
 }
@@ -220,14 +222,31 @@ __global__ __launch_bounds__(kBlock) void ada_scale_kernel(PlanDev P, AdaWs w,
         seg_scale[s] = scale;
         if (state_scale) state_scale[s] = scale;
     }
+    // chunk prefixes: thread t owns a contiguous run of up to kScanRun
+    // chunks (loads in flight together); one block scan per round
+    constexpr uint32_t kScanRun = 32;
+    const uint32_t *cc = w.ccount + seg.achunk0;
     uint32_t before = 0;
-    for (uint32_t r = 0; r < seg.anchunk; r += kBlock) {
-        bool in = r + threadIdx.x < seg.anchunk;
-        uint32_t cc = seg.achunk0 + r + threadIdx.x;
-        uint32_t v = in ? w.ccount[cc] : 0u;
+    for (uint32_t r0 = 0; r0 < seg.anchunk; r0 += kBlock * kScanRun) {
+        const uint32_t nr = min(seg.anchunk - r0, kBlock * kScanRun);
+        const uint32_t per = (nr + kBlock - 1) / kBlock;
+        const uint32_t t0 = r0 + threadIdx.x * per;
+        const uint32_t t1 = min(t0 + per, r0 + nr);
+        uint32_t v[kScanRun];
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u) v[u] = cc[min(t0 + u, r0 + nr - 1)];
+        uint32_t sum = 0;
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u)
+            if (t0 + u < t1) sum += v[u];
         uint32_t tot;
-        uint32_t pre = block_exclusive_scan(v, &tot);
-        if (in) w.cpre[cc] = before + pre;
+        uint32_t run = before + block_exclusive_scan(sum, &tot);
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u) {
+            if (t0 + u >= t1) break;
+            w.cpre[seg.achunk0 + t0 + u] = run;
+            run += v[u];
+        }
         before += tot;
     }
     if (threadIdx.x == 0) w.seg_total[s] = before;
@@ -255,11 +274,11 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
                                                            float *__restrict__ out_val) {
     const uint32_t c = P.nachunk - 1 - blockIdx.x;
     const AChunk a = achunk_info(P, c);
-    const uint32_t L = a.seg.bin_len;
+    const uint32_t L = a.L;
     const float invL = 1.0f / static_cast<float>(L);
     const uint32_t nb = (a.cnt + L - 1) / L;
     __shared__ float gm[kChunk];
-    const float *gin = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
+    const float *gin = w.gmax + a.bin_first;
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = gin[b];
     float g[kRows][4];
     uint32_t bin[kRows][4];
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float
                                                           AdaState S) {
     const uint32_t c = blockIdx.x;
     const AChunk a = achunk_info(P, c);
-    const uint32_t L = a.seg.bin_len;
+    const uint32_t L = a.L;
     const float invL = 1.0f / static_cast<float>(L);
     const uint32_t nb = (a.cnt + L - 1) / L;
     __shared__ uint32_t gm[kChunk];
@@ -363,9 +382,22 @@ __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float
     w.sign[word] = static_cast<uint16_t>(signs);
     uint32_t total;
     (void)block_exclusive_scan(mine, &total);
-    float *gout = w.gmax + a.seg.bin0 + a.pos * (a.seg.achunk_len / L);
+    float *gout = w.gmax + a.bin_first;
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gout[b] = dev_u2f(gm[b]);
     if (threadIdx.x == 0) w.ccount[c] = total;
+}
+
+// Thread t takes the 16 consecutive elements [16 t, 16 t + 16) of the chunk.
+// In the fold's layout element 1024 j + 4 t' + q is bit 4 j + q of word t',
+// so they are the 4-bit groups at 4 j (j = t / 64) of the four words
+// 4 (t mod 64) .. + 3: one 8-byte load each for the selection and sign bits.
+// One block scan orders the chunk's entries; they are staged in LDS as
+// (element | sign << 15) and written out with coalesced stores.
+__device__ __forceinline__ uint32_t gather16(uint64_t words, uint32_t j) {
+    uint32_t v = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) v |= static_cast<uint32_t>((words >> (16 * k + 4 * j)) & 0xFu) << (4 * k);
+    return v;
 }
 
 __global__ __launch_bounds__(kBlock) void ada_emit_kernel(PlanDev P, AdaWs w, AdaState S,
@@ -374,28 +406,29 @@ __global__ __launch_bounds__(kBlock) void ada_emit_kernel(PlanDev P, AdaWs w, Ad
                                                           uint32_t *__restrict__ out_idx,
                                                           float *__restrict__ out_val) {
     const uint32_t c = blockIdx.x;
-    const AChunk a = achunk_info(P, c);
-    const size_t word = size_t(c) * kBlock + threadIdx.x;
-    const uint32_t bits = S.sel[word], signs = w.sign[word];
-    const float scale = seg_scale[a.s];
-    const uint32_t base = seg_off[a.s] + w.cpre[c];
+    const ChunkRec rec = P.achunk_rec[c];
+    const uint32_t s = rec.z;
+    const size_t w4 = size_t(c) * kBlock + 4 * (threadIdx.x & (kWave - 1));
+    const uint64_t selw = *reinterpret_cast<const uint64_t *>(S.sel + w4);
+    const uint64_t sgnw = *reinterpret_cast<const uint64_t *>(w.sign + w4);
+    const uint32_t j = threadIdx.x / kWave;
+    const uint32_t bits = gather16(selw, j), signs = gather16(sgnw, j);
+    const float scale = seg_scale[s];
+    const uint32_t base = seg_off[s] + w.cpre[c];
     const uint32_t count = w.ccount[c];
-    bool flag[kRows][4];
-    uint32_t pos[kRows][4];
+    __shared__ uint16_t ent[kChunk];
+    uint32_t total;
+    uint32_t slot = block_exclusive_scan(static_cast<uint32_t>(__popc(bits)), &total);
 #pragma unroll
-    for (int j = 0; j < kRows; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) flag[j][q] = (bits >> (4 * j + q)) & 1u;
-    (void)block_compact4(flag, pos);
-#pragma unroll
-    for (int j = 0; j < kRows; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (flag[j][q] && pos[j][q] < count) {
-                out_idx[base + pos[j][q]] = static_cast<uint32_t>(a.lo + row_elem(j) + q);
-                out_val[base + pos[j][q]] = copysignf(scale, ((signs >> (4 * j + q)) & 1u) ? -1.0f : 1.0f);
-            }
-        }
+    for (uint32_t i = 0; i < 16; ++i)
+        if ((bits >> i) & 1u) ent[slot++] = static_cast<uint16_t>((16 * threadIdx.x + i) | (((signs >> i) & 1u) << 15));
+    __syncthreads();
+    const uint32_t n = min(total, count);  // equal unless the inputs were tampered with
+    for (uint32_t k = threadIdx.x; k < n; k += kBlock) {
+        const uint32_t v = ent[k];
+        out_idx[base + k] = static_cast<uint32_t>(rec.x + (v & 0x7FFFu));
+        out_val[base + k] = copysignf(scale, (v >> 15) ? -1.0f : 1.0f);
+    }
 }
 
 // R_out <- the exact residual held by (R, state), segment elements only.

@@ -103,14 +103,15 @@ struct ChunkInfo {
     uint32_t cnt;  // elements in the chunk
 };
 
+// From the chunk's 16-byte record (one round trip for lo, cnt and the
+// segment); the segment record follows.
 __device__ __forceinline__ ChunkInfo chunk_info(const PlanDev &P, uint32_t c) {
+    const ChunkRec rec = P.dchunk_rec[c];
     ChunkInfo ci;
-    ci.s = P.dchunk_seg[c];
+    ci.lo = rec.x;
+    ci.cnt = rec.y;
+    ci.s = rec.z;
     ci.seg = P.seg[ci.s];
-    uint32_t pos = c - ci.seg.dchunk0;
-    ci.lo = ci.seg.off + (uint64_t(pos) << kChunkLog2);
-    uint32_t rem = ci.seg.len - (pos << kChunkLog2);
-    ci.cnt = rem < uint32_t(kChunk) ? rem : uint32_t(kChunk);
     return ci;
 }
 
@@ -601,28 +602,53 @@ __global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w) {
 
 // ------------------------------------------------------------------ scan
 // Ties at the threshold go to the lowest indices: scan the segment's chunks
-// in order for the tie quota and the message slot of each chunk.
+// in order for the tie quota and the message slot of each chunk.  Thread t
+// owns a contiguous run of chunks (loads batched), so one round of two block
+// scans covers up to kBlock * kScanRun chunks.  The ties taken in a run are a
+// greedy prefix fill of the quota, so a run's total is known from its tie
+// prefix alone: min(max(need - before, 0), run ties).
+constexpr uint32_t kScanRun = 32;
+
 __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
                                                           uint32_t *__restrict__ seg_off) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     const uint32_t need_eq = w.st[s].need_eq;
+    const uint32_t *ceq = w.ceq + seg.dchunk0, *cgt = w.cgt + seg.dchunk0;
     uint32_t eq_before = 0, sel_before = 0;
-    for (uint32_t r = 0; r < seg.dnchunk; r += kBlock) {
-        uint32_t cc = seg.dchunk0 + r + threadIdx.x;
-        bool in = r + threadIdx.x < seg.dnchunk;
-        uint32_t eq = in ? w.ceq[cc] : 0u;
-        uint32_t gt = in ? w.cgt[cc] : 0u;
+    for (uint32_t r0 = 0; r0 < seg.dnchunk; r0 += kBlock * kScanRun) {
+        const uint32_t nr = min(seg.dnchunk - r0, kBlock * kScanRun);
+        const uint32_t per = (nr + kBlock - 1) / kBlock;
+        const uint32_t t0 = r0 + threadIdx.x * per;
+        const uint32_t t1 = min(t0 + per, r0 + nr);
+        uint32_t e[kScanRun], g[kScanRun];  // the run, all loads in flight together
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u) {
+            const uint32_t i = min(t0 + u, r0 + nr - 1);
+            e[u] = ceq[i];
+            g[u] = cgt[i];
+        }
+        uint32_t eq_sum = 0, gt_sum = 0;
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u)
+            if (t0 + u < t1) {
+                eq_sum += e[u];
+                gt_sum += g[u];
+            }
         uint32_t eq_tot;
-        uint32_t eq_pre = eq_before + block_exclusive_scan(eq, &eq_tot);
-        uint32_t take = 0;
-        if (need_eq > eq_pre) take = min(need_eq - eq_pre, eq);
-        uint32_t sel = gt + take;
+        const uint32_t eq_pre = eq_before + block_exclusive_scan(eq_sum, &eq_tot);
+        const uint32_t take_run = need_eq > eq_pre ? min(need_eq - eq_pre, eq_sum) : 0u;
         uint32_t sel_tot;
-        uint32_t sel_pre = sel_before + block_exclusive_scan(sel, &sel_tot);
-        if (in) {
-            w.ctake[cc] = take;
-            w.cout[cc] = seg.kbase + sel_pre;
+        const uint32_t sel_pre = sel_before + block_exclusive_scan(gt_sum + take_run, &sel_tot);
+        uint32_t eq_run = eq_pre, sel_run = sel_pre;
+#pragma unroll
+        for (uint32_t u = 0; u < kScanRun; ++u) {
+            if (t0 + u >= t1) break;
+            const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e[u]) : 0u;
+            w.ctake[seg.dchunk0 + t0 + u] = take;
+            w.cout[seg.dchunk0 + t0 + u] = seg.kbase + sel_run;
+            eq_run += e[u];
+            sel_run += g[u] + take;
         }
         eq_before += eq_tot;
         sel_before += sel_tot;

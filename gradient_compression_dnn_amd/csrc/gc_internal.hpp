@@ -362,18 +362,32 @@ __device__ double block_pairwise_sum(uint64_t m, Load load) {
     uint64_t lo = static_cast<uint64_t>(threadIdx.x) * B;
     double stack[kTreeDepth];
     double carry = 0.0;
-    for (uint64_t i = 0; i < B; ++i) {
-        uint64_t g = lo + i;
-        carry = g < m ? load(g) : 0.0;
-        bool done = false;
+    // leaves are loaded 8 at a time (clamped index, then selected) so that a
+    // batch is in flight together; m >= 1
+    constexpr uint64_t kBatch = 8;
+    for (uint64_t i0 = 0; i0 < B; i0 += kBatch) {
+        double leaf[kBatch];
 #pragma unroll
-        for (int l = 0; l < kTreeDepth; ++l) {
-            if (!done) {
-                if ((i >> l) & 1) {
-                    carry = stack[l] + carry;
-                } else {
-                    stack[l] = carry;
-                    done = true;
+        for (uint64_t u = 0; u < kBatch; ++u) {
+            const uint64_t g = lo + i0 + u;
+            const double v = load(g < m ? g : m - 1);
+            leaf[u] = g < m ? v : 0.0;
+        }
+#pragma unroll
+        for (uint64_t u = 0; u < kBatch; ++u) {
+            const uint64_t i = i0 + u;
+            if (i >= B) break;
+            carry = leaf[u];
+            bool done = false;
+#pragma unroll
+            for (int l = 0; l < kTreeDepth; ++l) {
+                if (!done) {
+                    if ((i >> l) & 1) {
+                        carry = stack[l] + carry;
+                    } else {
+                        stack[l] = carry;
+                        done = true;
+                    }
                 }
             }
         }

@@ -140,3 +140,16 @@ def test_deepspeech_adacomp_deferred_two_steps():
         assert np.array_equal(gidx, idx), tag
         assert same_bits(gval, val), ulp_report(gval, val)
         assert same_bits(Rg, R), ulp_report(Rg, R)
+
+
+def test_segment_beyond_one_scan_round():
+    """One 36M-element layer: more than 8192 DGC and AdaComp chunks, so the
+    per-segment chunk scans take a second round."""
+    n = 36_000_000
+    t = W.make_table([n], [50], [W.topk_count(n)])
+    hp = HipPath(t, n)
+    rng = np.random.default_rng(77)
+    g = W.random_values(rng, n, "laplace")
+    z = np.zeros(n, np.float32)
+    check_dgc(hp, t, g, z, z, 0.9, 0.0, 1, "36M dgc")
+    check_ada(hp, t, g, z, "36M adacomp")
