@@ -43,7 +43,6 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-template <bool kAligned>
 __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may alias xo
                                                      const float *__restrict__ xh, float *xo,
                                                      uint32_t n, int bits, int blog2,
@@ -58,25 +57,17 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
     const uint32_t nbk = kChunk >> blog2;
     for (uint32_t b = threadIdx.x; b < nbk; b += kBlock) smax[b] = 0u;
     float xv[kRows][4], zv[kRows][4];
+    // dense arrays through chunk-bounded buffer resources: branch-free tail,
+    // any dword alignment, non-temporal
+    const uint32_t cnt = min(n - base, uint32_t(kChunk));
+    const BufRsrc rx = chunk_buf(x + base, cnt), rh = chunk_buf(xh + base, cnt), ro = chunk_buf(xo + base, cnt);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
-        const uint32_t i0 = base + row_elem(j);
-        if (kAligned && i0 + 3 < n) {
-            float4 a = *reinterpret_cast<const float4 *>(x + i0);
-            float4 h = *reinterpret_cast<const float4 *>(xh + i0);
-            xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
-            zv[j][0] = h.x - a.x; zv[j][1] = h.y - a.y; zv[j][2] = h.z - a.z; zv[j][3] = h.w - a.w;
-        } else {
+        float h[4];
+        load4(rx, row_elem(j), xv[j]);
+        load4(rh, row_elem(j), h);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xv[j][u] = 0.0f;
-                zv[j][u] = 0.0f;
-                if (i0 + u < n) {
-                    xv[j][u] = x[i0 + u];
-                    zv[j][u] = xh[i0 + u] - xv[j][u];
-                }
-            }
-        }
+        for (int u = 0; u < 4; ++u) zv[j][u] = h[u] - xv[j][u];
     }
     __syncthreads();
 #pragma unroll
@@ -139,17 +130,11 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
             }
             out[u] = xv[j][u] + C;
         }
-        if (kAligned && i0 + 3 < n) {
-            *reinterpret_cast<float4 *>(xo + i0) = make_float4(out[0], out[1], out[2], out[3]);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (i0 + u < n) xo[i0 + u] = out[u];
-        }
+        store4(ro, e0, out);
         if (bits == 8) {
             if (i0 + 3 < n) {
-                *reinterpret_cast<uint32_t *>(codes + i0) =
-                    code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
+                __builtin_nontemporal_store(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                                            reinterpret_cast<uint32_t *>(codes + i0));
             } else {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
@@ -158,7 +143,8 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
         } else {
             const uint32_t b0 = code[0] | code[1] << 4, b1 = code[2] | code[3] << 4;
             if (i0 + 3 < n) {
-                *reinterpret_cast<uint16_t *>(codes + i0 / 2) = static_cast<uint16_t>(b0 | b1 << 8);
+                __builtin_nontemporal_store(static_cast<uint16_t>(b0 | b1 << 8),
+                                            reinterpret_cast<uint16_t *>(codes + i0 / 2));
             } else {
                 // the stream ends inside this group: only bytes holding a
                 // real element exist; missing high nibbles stay zero
@@ -198,17 +184,10 @@ extern "C" gc_status gc_dcd_compress(const float *x, const float *x_half, float 
     if (n == 0) return GC_OK;
     int blog2 = 0;
     while ((1u << blog2) < bucket) ++blog2;
-    const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(x_half) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(x_out) % 16 == 0);
     const unsigned grid = grid_1d(n, kChunk);
     const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
-    if (aligned)
-        GC_LAUNCH("dcd", stream, dcd_kernel<true><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, static_cast<uint32_t>(n), bits, blog2, k0, k1, step,
-                                                      scales, codes));
-    else
-        GC_LAUNCH("dcd", stream, dcd_kernel<false><<<grid, kBlock, 0, stream>>>(x, x_half, x_out, static_cast<uint32_t>(n), bits, blog2, k0, k1, step,
-                                                       scales, codes));
+    GC_LAUNCH("dcd", stream, dcd_kernel<<<grid, kBlock, 0, stream>>>(x, x_half, x_out, static_cast<uint32_t>(n), bits,
+                                                                    blog2, k0, k1, step, scales, codes));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dcd_compress launch");
     return GC_OK;

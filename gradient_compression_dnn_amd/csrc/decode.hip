@@ -321,7 +321,7 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     for (int k = 0; k < K; ++k) max_entries = std::max<uint64_t>(max_entries, msgs[k].cap);
     // one pass: enough workgroups for the largest capacity (extra ones exit)
     const uint64_t need_x = (max_entries + kBlock * kRun) / (kBlock * kRun) + 1;
-    const uint64_t cap_x = std::max<uint64_t>(64, uint64_t(kPersistentBlocks) / uint64_t(K));
+    const uint64_t cap_x = std::max<uint64_t>(64, uint64_t(16384) / uint64_t(K));
     unsigned gx = static_cast<unsigned>(std::min(need_x, cap_x));
     GC_LAUNCH("decode_index", stream, decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w));
     GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,

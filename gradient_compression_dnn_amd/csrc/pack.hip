@@ -380,11 +380,17 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     PackWs w = pack_layout(plan, ws, nullptr);
     const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
     const uint64_t cap = in->cap;
+    // one tile per workgroup up to kTileGrid tiles (each tile is a chain of
+    // dependent loads, so tiles run side by side rather than in sequence);
+    // the grid follows the capacity, and workgroups past the actual tile
+    // count exit at once
+    constexpr size_t kTileGrid = 8192;
+    const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kTileGrid));
     GC_LAUNCH("pack_tiles", stream, pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w));
-    GC_LAUNCH("pack_count", stream, pack_count_kernel<<<persistent_grid(pack_count_kernel, w.max_tiles), kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
+    GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
     GC_LAUNCH("pack_layout", stream, pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
                                                  out_bytes, w));
-    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<persistent_grid(pack_write_kernel, w.max_tiles), kBlock, 0, stream>>>(P, kind, cap, in->idx, in->val, in->seg_off, MAX,
+    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->idx, in->val, in->seg_off, MAX,
                                                    out, w));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_pack launch");
