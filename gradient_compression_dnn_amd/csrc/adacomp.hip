@@ -426,8 +426,10 @@ __global__ __launch_bounds__(kBlock) void ada_emit_kernel(PlanDev P, AdaWs w, Ad
     const uint32_t n = min(total, count);  // equal unless the inputs were tampered with
     for (uint32_t k = threadIdx.x; k < n; k += kBlock) {
         const uint32_t v = ent[k];
-        out_idx[base + k] = static_cast<uint32_t>(rec.x + (v & 0x7FFFu));
-        out_val[base + k] = copysignf(scale, (v >> 15) ? -1.0f : 1.0f);
+        // non-temporal stores: measured faster over the whole step, although pack
+        // and decode read the message next
+        __builtin_nontemporal_store(static_cast<uint32_t>(rec.x + (v & 0x7FFFu)), out_idx + base + k);
+        __builtin_nontemporal_store(copysignf(scale, (v >> 15) ? -1.0f : 1.0f), out_val + base + k);
     }
 }
 

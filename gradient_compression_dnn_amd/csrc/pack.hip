@@ -278,12 +278,13 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
             const uint32_t slot = (j - x.first) + esc_base;
             if (j >= x.end || slot >= E) continue;  // slot >= E only for malformed messages
             const uint32_t gap = entry_gap(x, j, cur[i], prv[i]);
+            // the packed stream is not read again here: non-temporal stores
             if (dgc) {
-                runs[slot] = static_cast<uint16_t>(gap);
-                vals[slot] = v[i];
+                __builtin_nontemporal_store(static_cast<uint16_t>(gap), runs + slot);
+                __builtin_nontemporal_store(v[i], vals + slot);
             } else {
                 const uint16_t sign = (dev_f2u(v[i]) >> 31) ? 0x8000u : 0u;
-                runs[slot] = static_cast<uint16_t>(sign | gap);
+                __builtin_nontemporal_store(static_cast<uint16_t>(sign | gap), runs + slot);
             }
         }
         continue;
