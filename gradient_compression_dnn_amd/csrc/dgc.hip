@@ -103,18 +103,6 @@ struct ChunkInfo {
     uint32_t cnt;  // elements in the chunk
 };
 
-// From the chunk's 16-byte record (one round trip for lo, cnt and the
-// segment); the segment record follows.
-__device__ __forceinline__ ChunkInfo chunk_info(const PlanDev &P, uint32_t c) {
-    const ChunkRec rec = P.dchunk_rec[c];
-    ChunkInfo ci;
-    ci.lo = rec.x;
-    ci.cnt = rec.y;
-    ci.s = rec.z;
-    ci.seg = P.seg[ci.s];
-    return ci;
-}
-
 __device__ __forceinline__ uint32_t mag_key(float v) { return dev_f2u(v) & 0x7FFFFFFFu; }
 
 // Chunk geometry with the segment record cached across consecutive chunks
@@ -553,50 +541,46 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const floa
     if (lane == 0) w.ccount[c] = run;
 }
 
-// ---------------------------------------------------------------- refine
+// ------------------------------------------------- refine, count (waves)
+// The candidate kernels run one wave per chunk (four chunks per workgroup):
+// a chunk holds a few staged entries, read 64 at a time from clamped indices.
+__device__ __forceinline__ uint32_t staged_count(const DgcWs &w, uint32_t c, uint32_t cnt) {
+    return min(w.ccount[c], cnt);
+}
+
 __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
-    const uint32_t n = w.ccount[c];
+    const uint32_t c = blockIdx.x * kWaves + wave_id();
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t lo = rec.x, s = rec.z;
+    const uint32_t n = staged_count(w, c, rec.y);
     if (n == 0) return;
-    const uint32_t prefix = (w.st[ci.s].d1 << kDigit2Bits) | w.st[ci.s].d2;
-    uint32_t *h3 = w.hist3 + size_t(ci.s) * kHist3;
-    for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
-        uint32_t key = mag_key(w.sval[ci.lo + i]);
-        if ((key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
+    const uint32_t prefix = (w.st[s].d1 << kDigit2Bits) | w.st[s].d2;
+    uint32_t *h3 = w.hist3 + size_t(s) * kHist3;
+    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+        const uint32_t i = i0 + lane_id();
+        const uint32_t key = mag_key(w.sval[lo + min(i, n - 1)]);
+        if (i < n && (key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
     }
 }
 
-// ----------------------------------------------------------------- count
 __global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
-    const uint32_t n = w.ccount[c];
-    const uint32_t T = w.st[ci.s].T;
-    if (n <= uint32_t(kWave)) {
-        if (wave_id() != 0) return;
-        const bool in = uint32_t(lane_id()) < n;
-        const uint32_t key = in ? mag_key(w.sval[ci.lo + lane_id()]) : 0u;
-        const uint32_t tgt = static_cast<uint32_t>(__popcll(__ballot(in && key > T)));
-        const uint32_t teq = static_cast<uint32_t>(__popcll(__ballot(in && key == T)));
-        if (lane_id() == 0) {
-            w.cgt[c] = tgt;
-            w.ceq[c] = teq;
-        }
-        return;
-    }
+    const uint32_t c = blockIdx.x * kWaves + wave_id();
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t lo = rec.x;
+    const uint32_t n = staged_count(w, c, rec.y);
+    const uint32_t T = w.st[rec.z].T;
     uint32_t ngt = 0, neq = 0;
-    for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
-        uint32_t key = mag_key(w.sval[ci.lo + i]);
-        ngt += key > T;
-        neq += key == T;
+    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+        const uint32_t i = i0 + lane_id();
+        const uint32_t key = mag_key(w.sval[lo + min(i, n - 1)]);
+        ngt += static_cast<uint32_t>(__popcll(__ballot(i < n && key > T)));
+        neq += static_cast<uint32_t>(__popcll(__ballot(i < n && key == T)));
     }
-    uint32_t tgt, teq;
-    (void)block_exclusive_scan(ngt, &tgt);
-    (void)block_exclusive_scan(neq, &teq);
-    if (threadIdx.x == 0) {
-        w.cgt[c] = tgt;
-        w.ceq[c] = teq;
+    if (lane_id() == 0) {
+        w.cgt[c] = ngt;
+        w.ceq[c] = neq;
     }
 }
 
@@ -660,64 +644,45 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
 }
 
 // ------------------------------------------------------------------ emit
+// One wave per chunk: staged entries in index order, 64 at a time; ties at T
+// are taken in index order up to the chunk's quota; ranks from ballots.
 __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__restrict__ U,
                                                           float *__restrict__ V, DgcWs w,
                                                           uint32_t *__restrict__ out_idx,
                                                           float *__restrict__ out_val) {
-    const uint32_t c = blockIdx.x;
-    const ChunkInfo ci = chunk_info(P, c);
-    const uint32_t n = w.ccount[c];
+    const uint32_t c = blockIdx.x * kWaves + wave_id();
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t lo = rec.x, s = rec.z;
+    const uint32_t n = staged_count(w, c, rec.y);
     if (n == 0) return;
-    const uint32_t T = w.st[ci.s].T;
+    const uint32_t T = w.st[s].T;
     const uint32_t take = w.ctake[c];
     const uint32_t base = w.cout[c];
+    const SegDev seg = P.seg[s];
     // a segment owns message slots [kbase, kbase + k): never write past them
-    const uint32_t limit = ci.seg.kbase + ci.seg.k;
-    if (n <= uint32_t(kWave)) {
-        // one wave: ranks straight from ballots, no barriers
-        if (wave_id() != 0) return;
-        const uint32_t i = lane_id();
-        const bool in = i < n;
-        const uint32_t id = in ? w.sidx[ci.lo + i] : 0u;
-        const float val = in ? w.sval[ci.lo + i] : 0.0f;
+    const uint32_t limit = seg.kbase + seg.k;
+    uint32_t eq_run = 0, sel_run = 0;
+    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+        const uint32_t i = i0 + lane_id();
+        const uint32_t ic = lo + min(i, n - 1);
+        const uint32_t id = w.sidx[ic];
+        const float val = w.sval[ic];
         const uint32_t key = mag_key(val);
+        const bool in = i < n;
         const bool eq = in && key == T;
-        const bool sel = (in && key > T) || (eq && lane_rank(__ballot(eq)) < take);
-        const uint32_t p = base + lane_rank(__ballot(sel));
+        const uint64_t eqm = __ballot(eq);
+        const bool sel = (in && key > T) || (eq && eq_run + lane_rank(eqm) < take);
+        const uint64_t selm = __ballot(sel);
+        const uint32_t p = base + sel_run + lane_rank(selm);
         if (sel && p < limit) {
             out_idx[p] = id;
             out_val[p] = val;
             V[id] = 0.0f;
             U[id] = 0.0f;
         }
-        return;
-    }
-    bool eqf[kEPT], self[kEPT];
-    uint32_t eqpos[kEPT], pos[kEPT];
-    uint32_t id[kEPT];
-    float val[kEPT];
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        uint32_t i = j * kBlock + threadIdx.x;
-        bool in = i < n;
-        id[j] = in ? w.sidx[ci.lo + i] : 0u;
-        val[j] = in ? w.sval[ci.lo + i] : 0.0f;
-        uint32_t key = mag_key(val[j]);
-        eqf[j] = in && key == T;
-        self[j] = in && key > T;
-    }
-    (void)block_compact<kEPT>(eqf, eqpos);
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) self[j] = self[j] || (eqf[j] && eqpos[j] < take);
-    (void)block_compact<kEPT>(self, pos);
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        if (self[j] && base + pos[j] < limit) {
-            out_idx[base + pos[j]] = id[j];
-            out_val[base + pos[j]] = val[j];
-            V[id[j]] = 0.0f;
-            U[id[j]] = 0.0f;
-        }
+        eq_run += static_cast<uint32_t>(__popcll(eqm));
+        sel_run += static_cast<uint32_t>(__popcll(selm));
     }
 }
 
@@ -757,7 +722,6 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     gc_status st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     DgcWs w = dgc_layout(plan, ws, nullptr);
-    const unsigned grid = plan->ndchunk;
     const bool clip = thr_G > 0.0f;
     const float thr = clip ? static_cast<float>(static_cast<double>(thr_G) /
                                                 std::sqrt(static_cast<double>(num_nodes)))
@@ -772,11 +736,11 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, V, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
-    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<grid, kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
+    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dgc_step launch");
     return GC_OK;
