@@ -66,7 +66,7 @@ def stored_traffic(kernel: str, digest: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 4):
+def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
     """The oracle, as it stands, over a bounded sample of the same workload."""
     import numpy as np
 
