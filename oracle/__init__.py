@@ -33,6 +33,13 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+class _DgcOpts(ctypes.Structure):
+    _fields_ = [("momentum", ctypes.c_float), ("thr_G", ctypes.c_float),
+                ("num_nodes", ctypes.c_int), ("nesterov", ctypes.c_int),
+                ("sampled", ctypes.c_int), ("sample_period", ctypes.c_uint32),
+                ("over", ctypes.c_uint32), ("pad", ctypes.c_uint32)]
+
+
 class _Seg(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_uint64), ("length", ctypes.c_uint32),
                 ("bin_len", ctypes.c_uint32), ("k", ctypes.c_uint32),
@@ -54,6 +61,7 @@ def lib():
         L.orc_adacomp.argtypes = [P, ctypes.c_int, P, P, ctypes.c_float, P, P, P, P, P]
         L.orc_dgc.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_float, ctypes.c_float,
                               ctypes.c_int, P, P, P, P]
+        L.orc_dgc_ex.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P]
         L.orc_pack.restype = ctypes.c_uint64
         L.orc_pack.argtypes = [ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, ctypes.c_uint64]
         L.orc_decode.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
@@ -130,6 +138,30 @@ def dgc(table, G, U, V, momentum=0.9, thr_G=0.0, num_nodes=1):
     lib().orc_dgc(_segs(t), len(t), _ptr(G), _ptr(U), _ptr(V), float(momentum), float(thr_G),
                   int(num_nodes), _ptr(idx), _ptr(val), _ptr(seg_off), _ptr(clip))
     return U, V, idx[:ktot].copy(), val[:ktot].copy(), seg_off, clip[:len(t)]
+
+
+def dgc_ex(table, G, U, V, momentum=0.9, thr_G=0.0, num_nodes=1, nesterov=False,
+           sampled=False, sample_period=100, over=2):
+    """One DGC step with the momentum kind and selection mode chosen.
+    Returns (U_new, V_new, idx, val, seg_off, clip); the message is compact."""
+    t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+    G = _f32(G)
+    U = _f32(U, copy=True)
+    V = _f32(V, copy=True)
+    if sampled:
+        cap = int(np.minimum(t[:, 1], int(over) * t[:, 3]).sum()) if len(t) else 0
+    else:
+        cap = int(t[:, 3].sum()) if len(t) else 0
+    idx = np.zeros(max(cap, 1), np.uint32)
+    val = np.zeros(max(cap, 1), np.float32)
+    seg_off = np.zeros(len(t) + 1, np.uint32)
+    clip = np.zeros(max(len(t), 1), np.float32)
+    o = _DgcOpts(float(momentum), float(thr_G), int(num_nodes), int(bool(nesterov)),
+                 int(bool(sampled)), int(sample_period), int(over), 0)
+    lib().orc_dgc_ex(_segs(t), len(t), _ptr(G), _ptr(U), _ptr(V), ctypes.byref(o), _ptr(idx),
+                     _ptr(val), _ptr(seg_off), _ptr(clip))
+    m = int(seg_off[-1])
+    return U, V, idx[:m].copy(), val[:m].copy(), seg_off, clip[:len(t)]
 
 
 def pack(kind, table, idx, val, seg_off, seg_scale=None, cap=None) -> bytes:

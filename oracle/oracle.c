@@ -187,26 +187,39 @@ static uint32_t abs_bits(float v)
 }
 
 /*
- * Deep Gradient Compression (Lin et al.), vanilla-momentum variant, per
- * gradient tensor:
+ * Deep Gradient Compression (Lin et al.), per gradient tensor:
  *  - App. C: the current gradient is clipped by its L2 norm before it is
  *    added to the accumulation; the node's threshold is thr_G * N^-1/2;
  *  - §3.2 / App. B, D: momentum correction accumulates the momentum-adjusted
- *    gradient (U <- m U + G) into V (V <- V + U) before sparsification;
+ *    gradient into V before sparsification.  Vanilla momentum (Alg. 3):
+ *    U <- m U + G, V <- V + U.  Nesterov momentum (Alg. 4, App. B): the
+ *    conventional Nesterov step direction is m U + G with U <- m U + G, and
+ *    it is that direction which is accumulated: V <- V + (m U + G);
  *  - §3.1 / §5: only the largest entries of V (top 0.1%) are sent, the rest
  *    keep accumulating locally;
+ *  - §5 / §6 (sampled selection): the threshold is estimated from a sample of
+ *    the entries, and when the estimate passes far more entries than the
+ *    target, the exact threshold is taken among those already selected
+ *    (hierarchical selection);
  *  - §3.3: momentum factor masking clears U (and V) where entries were sent.
  */
+static uint32_t sample_block_offset(uint32_t w, uint32_t P)
+{
+    uint32_t h = w * 2654435769u; /* Fibonacci hashing of the window index, mod 2^32 */
+    return 32u * (h % P);
+}
+
 static void dgc_segment(const orc_seg *sg, const float *Gin, float *U, float *V,
-                        float m, float thr_G, int N, uint32_t *idx, float *val,
-                        float *clip)
+                        const orc_dgc_opts *o, uint32_t *idx, float *val,
+                        uint32_t *count, float *clip)
 {
     const uint64_t base = sg->offset;
     const uint32_t n = sg->length, k = sg->k;
+    const float m = o->momentum;
 
     float c = 1.0f;
-    if (thr_G > 0.0f) {
-        float thr = (float)((double)thr_G / sqrt((double)N));
+    if (o->thr_G > 0.0f) {
+        float thr = (float)((double)o->thr_G / sqrt((double)o->num_nodes));
         double *sq = (double *)malloc(sizeof(double) * (size_t)n);
         for (uint32_t i = 0; i < n; ++i) {
             double g = (double)Gin[base + i];
@@ -223,7 +236,13 @@ static void dgc_segment(const orc_seg *sg, const float *Gin, float *U, float *V,
         float u = m * U[base + i];
         u = u + g;
         U[base + i] = u;
-        V[base + i] = V[base + i] + u;
+        if (o->nesterov) {
+            float d = m * u;
+            d = d + g;
+            V[base + i] = V[base + i] + d;
+        } else {
+            V[base + i] = V[base + i] + u;
+        }
     }
 
     keyed *order = (keyed *)malloc(sizeof(keyed) * (size_t)n);
@@ -233,37 +252,97 @@ static void dgc_segment(const orc_seg *sg, const float *Gin, float *U, float *V,
     }
     qsort(order, n, sizeof(keyed), by_key_desc_pos_asc);
 
-    uint32_t *chosen = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)k);
-    for (uint32_t j = 0; j < k; ++j) chosen[j] = order[j].pos;
-    qsort(chosen, k, sizeof(uint32_t), u32_asc);
-    for (uint32_t j = 0; j < k; ++j) {
+    /* how many of the ordered entries are sent */
+    uint32_t nsend = k;
+    if (o->sampled) {
+        const uint32_t P = o->sample_period;
+        const uint64_t win = 32ull * P;
+        const uint64_t nwin = (n + win - 1) / win;
+        uint32_t *skeys = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nwin * 32));
+        uint64_t S = 0;
+        for (uint64_t w = 0; w < nwin; ++w) {
+            uint64_t p0 = w * win + sample_block_offset((uint32_t)w, P);
+            for (uint32_t l = 0; l < 32; ++l)
+                if (p0 + l < n) skeys[S++] = abs_bits(V[base + p0 + l]);
+        }
+        /* the r-th largest sample key, r = ceil(S k / n): the sample's
+         * estimate of the k-th largest key of the whole tensor */
+        uint64_t r = (S * k + n - 1) / n;
+        qsort(skeys, (size_t)S, sizeof(uint32_t), u32_asc);
+        uint32_t thr = skeys[S - r];
+        free(skeys);
+        uint32_t passed = 0; /* entries at or above the estimate */
+        while (passed < n && order[passed].key >= thr) ++passed;
+        uint64_t budget = (uint64_t)o->over * k;
+        if (budget > n) budget = n;
+        nsend = passed <= budget ? passed : k; /* else: exact top-k among them */
+    }
+
+    uint32_t *chosen = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nsend ? nsend : 1));
+    for (uint32_t j = 0; j < nsend; ++j) chosen[j] = order[j].pos;
+    qsort(chosen, nsend, sizeof(uint32_t), u32_asc);
+    for (uint32_t j = 0; j < nsend; ++j) {
         uint64_t e = base + chosen[j];
         idx[j] = (uint32_t)e;
         val[j] = V[e];
         V[e] = 0.0f;
         U[e] = 0.0f;
     }
+    *count = nsend;
     free(chosen);
     free(order);
+}
+
+void orc_dgc_ex(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
+                const orc_dgc_opts *opts, uint32_t *out_idx, float *out_val,
+                uint32_t *seg_off, float *clip_out)
+{
+    /* segment s stages its entries at its own slot range, at most
+     * min(n_s, over k_s) of them (k_s in exact mode) */
+    uint64_t *slot = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nseg + 1));
+    slot[0] = 0;
+    for (int s = 0; s < nseg; ++s) {
+        uint64_t cap = segs[s].k;
+        if (opts->sampled) {
+            cap = (uint64_t)opts->over * segs[s].k;
+            if (cap > segs[s].length) cap = segs[s].length;
+        }
+        slot[s + 1] = slot[s] + cap;
+    }
+    uint64_t tot = slot[nseg];
+    uint32_t *sidx = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(tot ? tot : 1));
+    float *sval = (float *)malloc(sizeof(float) * (size_t)(tot ? tot : 1));
+    uint32_t *cnt = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nseg ? nseg : 1));
+    float *clip = (float *)malloc(sizeof(float) * (size_t)(nseg ? nseg : 1));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < nseg; ++s)
+        dgc_segment(&segs[s], G, U, V, opts, sidx + slot[s], sval + slot[s], &cnt[s], &clip[s]);
+    uint32_t pos = 0;
+    for (int s = 0; s < nseg; ++s) {
+        seg_off[s] = pos;
+        memcpy(out_idx + pos, sidx + slot[s], sizeof(uint32_t) * cnt[s]);
+        memcpy(out_val + pos, sval + slot[s], sizeof(float) * cnt[s]);
+        pos += cnt[s];
+    }
+    seg_off[nseg] = pos;
+    if (clip_out) memcpy(clip_out, clip, sizeof(float) * (size_t)nseg);
+    free(slot);
+    free(sidx);
+    free(sval);
+    free(cnt);
+    free(clip);
 }
 
 void orc_dgc(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
              float momentum, float thr_G, int num_nodes, uint32_t *out_idx,
              float *out_val, uint32_t *seg_off, float *clip_out)
 {
-    uint32_t pos = 0;
-    for (int s = 0; s < nseg; ++s) {
-        seg_off[s] = pos;
-        pos += segs[s].k;
-    }
-    seg_off[nseg] = pos;
-    float *clip = (float *)malloc(sizeof(float) * (size_t)(nseg ? nseg : 1));
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int s = 0; s < nseg; ++s)
-        dgc_segment(&segs[s], G, U, V, momentum, thr_G, num_nodes,
-                    out_idx + seg_off[s], out_val + seg_off[s], &clip[s]);
-    if (clip_out) memcpy(clip_out, clip, sizeof(float) * (size_t)nseg);
-    free(clip);
+    orc_dgc_opts o;
+    memset(&o, 0, sizeof o);
+    o.momentum = momentum;
+    o.thr_G = thr_G;
+    o.num_nodes = num_nodes;
+    orc_dgc_ex(segs, nseg, G, U, V, &o, out_idx, out_val, seg_off, clip_out);
 }
 
 /* -------------------------------------------------------------------- pack */

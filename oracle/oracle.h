@@ -42,8 +42,28 @@ void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
                  float scale_factor, uint32_t *out_idx, float *out_val,
                  uint32_t *seg_off, float *seg_scale, float *gmax_out);
 
-/* DGC step (vanilla momentum) on every segment.  clip_out (optional)
- * receives the per-segment clip coefficient. */
+/* DGC options.  nesterov: 0 vanilla momentum (Alg. 3), 1 Nesterov (Alg. 4).
+ * sampled: 0 exact top-k; 1 threshold estimated from a sample of one
+ * 32-element block per window of 32*sample_period elements, with the exact
+ * top-k taken instead when more than over*k entries pass it. */
+typedef struct orc_dgc_opts {
+    float momentum;
+    float thr_G;
+    int num_nodes;
+    int nesterov;
+    int sampled;
+    uint32_t sample_period;
+    uint32_t over;
+    uint32_t pad;
+} orc_dgc_opts;
+
+/* DGC step on every segment; the message is compact (seg_off[nseg] entries).
+ * clip_out (optional) receives the per-segment clip coefficient. */
+void orc_dgc_ex(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
+                const orc_dgc_opts *opts, uint32_t *out_idx, float *out_val,
+                uint32_t *seg_off, float *clip_out);
+
+/* DGC step, vanilla momentum, exact top-k. */
 void orc_dgc(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
              float momentum, float thr_G, int num_nodes, uint32_t *out_idx,
              float *out_val, uint32_t *seg_off, float *clip_out);
