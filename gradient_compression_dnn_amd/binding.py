@@ -17,6 +17,8 @@ GC_OK, GC_EINVAL, GC_ECAPACITY, GC_ERANGE, GC_EHIP, GC_ENOTSUP = 0, -1, -2, -3, 
 GC_OP_DGC, GC_OP_ADACOMP, GC_OP_PACK, GC_OP_DECODE = 1, 2, 3, 4
 GC_KIND_DGC, GC_KIND_ADACOMP = 1, 2
 GC_SUM, GC_AVG = 0, 1
+GC_MOMENTUM_VANILLA, GC_MOMENTUM_NESTEROV = 0, 1
+GC_SELECT_EXACT, GC_SELECT_SAMPLED = 0, 1
 GC_MAX_BIN_LEN = 4096
 GC_MAX_MESSAGES = 64
 
@@ -41,6 +43,13 @@ class gc_sparse(ctypes.Structure):
                 ("cap", ctypes.c_uint64)]
 
 
+class gc_dgc_options(ctypes.Structure):
+    _fields_ = [("momentum", ctypes.c_float), ("thr_G", ctypes.c_float),
+                ("num_nodes", ctypes.c_int), ("momentum_kind", ctypes.c_int),
+                ("select", ctypes.c_int), ("sample_period", ctypes.c_uint32),
+                ("over", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 _lib = None
 
 # every symbol the header declares, with (restype, argtypes)
@@ -62,6 +71,8 @@ _SIGS = {
     "gc_adacomp_residual": (ctypes.c_int, [_P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gc_dgc_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]),
+    "gc_dgc_message_cap": (ctypes.c_uint64, [_P, _P]),
+    "gc_dgc_step_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gc_pack_bound": (ctypes.c_uint64, [_P, ctypes.c_int]),
     "gc_pack": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_uint64, _P, _P, ctypes.c_size_t, _P]),
     "gc_decompress_accumulate": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
@@ -72,8 +83,8 @@ _SIGS = {
     "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
 }
 
-KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_update", "dgc_select", "dgc_stage", "dgc_refine",
-           "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
+KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
+           "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd")
 
@@ -269,6 +280,25 @@ def gc_dgc_step(plan: Plan, G, U, V, momentum: float, thr_G: float, num_nodes: i
     _check(load().gc_dgc_step(plan.handle, _f32(G, n, "G"), _f32(U, n, "U"), _f32(V, n, "V"),
                               float(momentum), float(thr_G), int(num_nodes), ctypes.byref(msg),
                               _ptr(ws), ws.numel(), _stream(V)))
+
+
+def dgc_options(momentum: float, thr_G: float = 0.0, num_nodes: int = 1, nesterov: bool = False,
+                sampled: bool = False, sample_period: int = 100, over: int = 2) -> gc_dgc_options:
+    return gc_dgc_options(float(momentum), float(thr_G), int(num_nodes),
+                          GC_MOMENTUM_NESTEROV if nesterov else GC_MOMENTUM_VANILLA,
+                          GC_SELECT_SAMPLED if sampled else GC_SELECT_EXACT,
+                          int(sample_period), int(over), 0)
+
+
+def gc_dgc_message_cap(plan: Plan, opt: gc_dgc_options) -> int:
+    return int(load().gc_dgc_message_cap(plan.handle, ctypes.byref(opt)))
+
+
+def gc_dgc_step_ex(plan: Plan, G, U, V, opt: gc_dgc_options, out: Sparse, ws: torch.Tensor):
+    n = plan.n_total
+    msg = out.struct()
+    _check(load().gc_dgc_step_ex(plan.handle, _f32(G, n, "G"), _f32(U, n, "U"), _f32(V, n, "V"),
+                                 ctypes.byref(opt), ctypes.byref(msg), _ptr(ws), ws.numel(), _stream(V)))
 
 
 def gc_pack(plan: Plan, kind: int, msg: Sparse, out: torch.Tensor, out_bytes: torch.Tensor,

@@ -1,6 +1,8 @@
-// DGC step on gfx950: local clipping, momentum correction, exact top-k by
-// radix select on |V| bit patterns, ordered compaction, momentum factor
-// masking.  "Deep Gradient Compression" (Lin et al.), §3.1–§3.3, App. C, D.
+// DGC step on gfx950: local clipping, momentum correction (vanilla or
+// Nesterov), top-k by radix select on |V| bit patterns (exact, or from a
+// sampled threshold with a hierarchical exact fallback), ordered compaction,
+// momentum factor masking.  "Deep Gradient Compression" (Lin et al.),
+// §3.1–§3.3, §5, §6, App. B, C, D.
 //
 // Launch sequence.  Chunk kernels run one workgroup (or one wave) per
 // 4096-element chunk of a segment; segment kernels one workgroup per segment.
@@ -31,6 +33,18 @@
 //   emit    (chunk) write (idx, V) in index order, then zero U and V there
 // Staged entries below d1 are never counted or sent (their keys are below T),
 // so the looser staging changes no result.
+//
+// Sampled selection replaces sample + bound by
+//   ssample (chunk) V' at the sample positions (one 32-entry block per window
+//           of 32 P entries), keys stored at the segment's staging offset
+//   squant  (segment) the estimate: the r-th largest sample key,
+//           r = ceil(S k / n), by a three-digit LDS radix select
+// and the update stages exactly the keys at or above the estimate.  select1
+// then sends all of them when they fit the budget min(n, over k) ("all"
+// segments skip stage, refine and the later selects), and otherwise takes
+// the exact top-k among them through the normal path.  sbase (one
+// workgroup) lays the segments' variable-size outputs end to end.
+#include <algorithm>
 #include <cmath>
 
 #include "gc_internal.hpp"
@@ -44,7 +58,28 @@ struct SegState {
     uint32_t d1, above1, d2, above2, T, gt, need_eq;
     uint32_t Lkey;  // staging bound on the key, from the sample
     uint32_t redo;  // fewer than k staged: re-stage the segment from V
+    uint32_t all;   // sampled selection: every staged entry is sent
+    uint32_t sent;  // entries the segment sends
+    uint32_t base;  // first message slot of the segment
 };
+
+// Momentum correction (§3.2; App. B and D).  Vanilla: U <- m U + G',
+// V <- V + U.  Nesterov: U <- m U + G', V <- V + (m U + G') with the updated U,
+// the Nesterov step direction accumulated in place of being applied.  One
+// rounding per operation, in this order.
+template <bool kNest>
+__device__ __forceinline__ void momentum_update(float m, float gc, float &u, float &v) {
+    float un = m * u;
+    un = un + gc;
+    u = un;
+    if (kNest) {
+        float d = m * un;
+        d = d + gc;
+        v = v + d;
+    } else {
+        v = v + un;
+    }
+}
 
 // Sample of a segment: in every stride-th chunk (at most kSampleChunks
 // chunks), kSamples contiguous elements starting at a per-chunk offset
@@ -214,6 +249,7 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
 // Half a wave per chunk: in a sampled chunk, lane l < min(32, cnt) computes
 // V' of element sample_offset + l with the update's own arithmetic and
 // records its key (plain stores: no atomics).
+template <bool kNest>
 __global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const float *__restrict__ G,
                                                             const float *__restrict__ U,
                                                             const float *__restrict__ V, float m,
@@ -228,10 +264,97 @@ __global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const flo
     const uint64_t e = uint64_t(rec.x) + sample_offset(c, cnt) + l;
     const float clip = w.st[rec.z].clip;
     const float gc = clip * G[e];
-    float un = m * U[e];
-    un = un + gc;
-    const float vn = V[e] + un;
+    float un = U[e], vn = V[e];
+    momentum_update<kNest>(m, gc, un, vn);
     w.skey[size_t(c) * kSamples + l] = mag_key(vn);
+}
+
+// --------------------------------------------------------------- ssample
+// Sampled selection's sample: window w of a segment covers entries
+// [32 P w, 32 P (w + 1)); its block is the 32 entries from
+// 32 P w + sample_block_offset(w, P), those past the segment end excluded.
+// Only the last window can be cut, so the keys of sample j = 32 w + l form
+// the contiguous range [0, S) at the segment's staging offset (j never
+// exceeds the sampled position, so it stays inside the segment).  One wave
+// per chunk, half a wave per window whose block starts in the chunk.
+__device__ __forceinline__ uint32_t sample_block_offset(uint32_t w, uint32_t period) {
+    return 32u * ((w * 2654435769u) % period);  // Fibonacci hash of the window, mod 2^32
+}
+
+template <bool kNest>
+__global__ __launch_bounds__(kBlock) void dgc_ssample_kernel(PlanDev P, const float *__restrict__ G,
+                                                             const float *__restrict__ U,
+                                                             const float *__restrict__ V, float m,
+                                                             uint32_t period, DgcWs w) {
+    const uint32_t c = blockIdx.x * kWaves + wave_id();
+    if (c >= P.ndchunk) return;
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t cnt = rec.y, s = rec.z;
+    const SegDev seg = P.seg[s];
+    const uint64_t win = 32ull * period;
+    const uint64_t pos0 = uint64_t(rec.w) << kChunkLog2, pos1 = pos0 + cnt;
+    const uint64_t w0 = pos0 / win, w1 = (pos1 - 1) / win;
+    const float clip = w.st[s].clip;
+    const uint32_t l = lane_id() & 31;
+    for (uint64_t wb = w0; wb <= w1; wb += 2) {
+        const uint64_t wi = wb + (uint32_t(lane_id()) >> 5);
+        if (wi > w1) continue;
+        const uint64_t start = wi * win + sample_block_offset(static_cast<uint32_t>(wi), period);
+        const uint64_t p = start + l;
+        if (start < pos0 || start >= pos1 || p >= seg.len) continue;
+        const uint64_t e = seg.off + p;
+        const float gc = clip * G[e];
+        float un = U[e], vn = V[e];
+        momentum_update<kNest>(m, gc, un, vn);
+        w.sidx[seg.off + wi * 32 + l] = mag_key(vn);
+    }
+}
+
+// ---------------------------------------------------------------- squant
+// The estimate of the k-th largest key: the r-th largest of the S sample
+// keys, r = ceil(S k / n) (u64 arithmetic), by radix select over the 11, 11
+// and 9-bit digits with an LDS histogram per digit (keys re-read from
+// global memory each level; they are L2-resident after the first).
+__global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t period, DgcWs w) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    const uint64_t win = 32ull * period;
+    const uint64_t nwin = (seg.len + win - 1) / win;
+    const uint64_t wl = nwin - 1;
+    const uint64_t last_start = wl * win + sample_block_offset(static_cast<uint32_t>(wl), period);
+    const uint64_t last_ns = last_start < seg.len ? min<uint64_t>(32, seg.len - last_start) : 0;
+    const uint32_t S = static_cast<uint32_t>(wl * 32 + last_ns);
+    uint32_t rank = static_cast<uint32_t>((uint64_t(S) * seg.k + seg.len - 1) / seg.len);
+    const uint32_t *keys = w.sidx + seg.off;
+    __shared__ uint32_t h[kHist1];
+    uint32_t prefix = 0;
+    for (int level = 0; level < 3; ++level) {
+        const int nb = level == 2 ? kHist3 : kHist1;
+        const int shift = level == 0 ? kDigit2Bits + kDigit3Bits : level == 1 ? kDigit3Bits : 0;
+        const int pshift = level == 1 ? kDigit2Bits + kDigit3Bits : kDigit3Bits;  // prefix bits below
+        for (int i = threadIdx.x; i < nb; i += kBlock) h[i] = 0u;
+        __syncthreads();
+        constexpr uint32_t kB = 8;
+        for (uint32_t j0 = 0; j0 < S; j0 += kB * kBlock) {
+            uint32_t key[kB];
+#pragma unroll
+            for (uint32_t u = 0; u < kB; ++u) key[u] = keys[min(j0 + u * kBlock + threadIdx.x, S - 1)];
+#pragma unroll
+            for (uint32_t u = 0; u < kB; ++u) {
+                if (j0 + u * kBlock + threadIdx.x >= S) continue;
+                if (level > 0 && (key[u] >> pshift) != prefix) continue;
+                atomicAdd(&h[(key[u] >> shift) & uint32_t(nb - 1)], 1u);
+            }
+        }
+        __syncthreads();
+        uint32_t above, d;
+        if (level == 2) d = block_find_bucket<kHist3>(rank, [&](int b) { return h[b]; }, &above);
+        else d = block_find_bucket<kHist1>(rank, [&](int b) { return h[b]; }, &above);
+        rank -= above;
+        prefix = level == 0 ? d : level == 1 ? ((prefix << kDigit2Bits) | d) : ((prefix << kDigit3Bits) | d);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) w.st[s].Lkey = prefix;
 }
 
 // ----------------------------------------------------------------- bound
@@ -307,6 +430,7 @@ __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
 // staged count of the (row, wave) pieces before its own, plus the ballot
 // ranks of lower lanes, plus its own earlier flags.  The piece counts go
 // through a double-buffered LDS table with one barrier per chunk.
+template <bool kNest>
 __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const float *__restrict__ G,
                                                             float *__restrict__ U,
                                                             float *__restrict__ V, float m, DgcWs w) {
@@ -340,12 +464,9 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
             uint32_t piece_total = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float gc = clip * g[j][q];
-                float un = m * u[j][q];
-                un = un + gc;
-                float vn = v[j][q] + un;
-                u[j][q] = un;
-                v[j][q] = vn;
+                const float gc = clip * g[j][q];
+                momentum_update<kNest>(m, gc, u[j][q], v[j][q]);
+                const float vn = v[j][q];
                 const bool in = e0 + q < ci.cnt;
                 const uint32_t d = mag_key(vn) >> (kDigit2Bits + kDigit3Bits);
                 if (in) atomicAdd(&hist[d], 1u);
@@ -424,9 +545,11 @@ __device__ __forceinline__ uint32_t replica_sum(const uint32_t *h, int b) {
     return t;
 }
 
-// Level 1..3 of the radix select for one segment.
+// Level 1..3 of the radix select for one segment.  Level 1 also settles the
+// segment's output: in sampled selection (budget > 0) a segment whose staged
+// entries (every key at or above the estimate) fit the budget sends them all.
 template <int kLevel>
-__global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) {
+__global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, uint32_t over) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     SegState st = w.st[s];
@@ -450,9 +573,25 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
         if (threadIdx.x == 0) {
             w.st[s].d1 = d;
             w.st[s].above1 = above;
-            w.st[s].redo = staged_total < seg.k ? 1u : 0u;
+            w.st[s].redo = 0u;
+            w.st[s].all = 0u;
+            w.st[s].sent = seg.k;
+            w.st[s].base = seg.kbase;
+            if (over == 0) {
+                w.st[s].redo = staged_total < seg.k ? 1u : 0u;
+            } else {
+                const uint64_t budget = min<uint64_t>(seg.len, uint64_t(over) * seg.k);
+                if (staged_total <= budget) {
+                    w.st[s].all = 1u;
+                    w.st[s].sent = staged_total;
+                    w.st[s].T = st.Lkey;  // every staged key is >= the estimate
+                    w.st[s].gt = 0u;
+                    w.st[s].need_eq = 0xFFFFFFFFu;
+                }
+            }
         }
     } else if (kLevel == 2) {
+        if (st.all) return;
         const uint32_t *h = w.hist2 + size_t(s) * kHistRep * kHist2;
         uint32_t d = block_find_bucket<kHist2>(seg.k - st.above1, [&](int b) { return replica_sum<kHist2>(h, b); },
                                                &above);
@@ -461,6 +600,7 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
             w.st[s].above2 = st.above1 + above;
         }
     } else {
+        if (st.all) return;
         const uint32_t *h = w.hist3 + size_t(s) * kHist3;
         uint32_t d = block_find_bucket<kHist3>(seg.k - st.above2, [&](int b) { return h[b]; }, &above);
         if (threadIdx.x == 0) {
@@ -469,6 +609,21 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w) 
             w.st[s].gt = gt;
             w.st[s].need_eq = seg.k - gt;
         }
+    }
+}
+
+// ----------------------------------------------------------------- sbase
+// Sampled selection: segments send variable counts, laid end to end in
+// segment order.
+__global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w) {
+    uint32_t run = 0;
+    for (int s0 = 0; s0 < P.nseg; s0 += kBlock) {
+        const int s = s0 + int(threadIdx.x);
+        const uint32_t v = s < P.nseg ? w.st[s].sent : 0u;
+        uint32_t tot;
+        const uint32_t pre = block_exclusive_scan(v, &tot);
+        if (s < P.nseg) w.st[s].base = run + pre;
+        run += tot;
     }
 }
 
@@ -487,6 +642,7 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const floa
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
     const uint32_t lo = rec.x, cnt = rec.y, s = rec.z;
+    if (w.st[s].all) return;
     const uint32_t d1 = w.st[s].d1;
     const uint32_t redo = w.st[s].redo;
     uint32_t *h2 = w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2;
@@ -554,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) 
     const ChunkRec rec = P.dchunk_rec[c];
     const uint32_t lo = rec.x, s = rec.z;
     const uint32_t n = staged_count(w, c, rec.y);
-    if (n == 0) return;
+    if (n == 0 || w.st[s].all) return;
     const uint32_t prefix = (w.st[s].d1 << kDigit2Bits) | w.st[s].d2;
     uint32_t *h3 = w.hist3 + size_t(s) * kHist3;
     for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
@@ -598,6 +754,7 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     const uint32_t need_eq = w.st[s].need_eq;
+    const uint32_t base = w.st[s].base;
     const uint32_t *ceq = w.ceq + seg.dchunk0, *cgt = w.cgt + seg.dchunk0;
     uint32_t eq_before = 0, sel_before = 0;
     for (uint32_t r0 = 0; r0 < seg.dnchunk; r0 += kBlock * kScanRun) {
@@ -630,7 +787,7 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
             if (t0 + u >= t1) break;
             const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e[u]) : 0u;
             w.ctake[seg.dchunk0 + t0 + u] = take;
-            w.cout[seg.dchunk0 + t0 + u] = seg.kbase + sel_run;
+            w.cout[seg.dchunk0 + t0 + u] = base + sel_run;
             eq_run += e[u];
             sel_run += g[u] + take;
         }
@@ -638,8 +795,8 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
         sel_before += sel_tot;
     }
     if (threadIdx.x == 0) {
-        seg_off[s] = seg.kbase;
-        if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = seg.kbase + seg.k;
+        seg_off[s] = base;
+        if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = base + w.st[s].sent;
     }
 }
 
@@ -659,9 +816,8 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__re
     const uint32_t T = w.st[s].T;
     const uint32_t take = w.ctake[c];
     const uint32_t base = w.cout[c];
-    const SegDev seg = P.seg[s];
-    // a segment owns message slots [kbase, kbase + k): never write past them
-    const uint32_t limit = seg.kbase + seg.k;
+    // a segment owns message slots [base, base + sent): never write past them
+    const uint32_t limit = w.st[s].base + w.st[s].sent;
     uint32_t eq_run = 0, sel_run = 0;
     for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
         const uint32_t i = i0 + lane_id();
@@ -698,21 +854,49 @@ size_t dgc_workspace_bytes(const gc_plan *plan) {
 
 using namespace gc;
 
-extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, float *V,
-                                 float momentum, float thr_G, int num_nodes, gc_sparse *out,
-                                 void *ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+// Entries a message of this plan and selection holds at most.
+uint64_t dgc_capacity(const gc_plan *plan, int select, uint32_t over) {
+    if (select != GC_SELECT_SAMPLED) return plan->total_k;
+    uint64_t cap = 0;
+    for (const SegDev &d : plan->seg) cap += std::min<uint64_t>(d.len, uint64_t(over) * d.k);
+    return cap;
+}
+}  // namespace
+
+extern "C" uint64_t gc_dgc_message_cap(const gc_plan *plan, const gc_dgc_options *opt) {
+    if (!plan) return 0;
+    if (!opt || opt->select != GC_SELECT_SAMPLED) return plan->total_k;
+    return dgc_capacity(plan, GC_SELECT_SAMPLED, opt->over);
+}
+
+extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V,
+                                    const gc_dgc_options *opt, gc_sparse *out, void *ws,
+                                    size_t ws_bytes, hipStream_t stream) {
     clear_error();
     if (!plan) return set_error(GC_EINVAL, "gc_dgc_step: plan is null");
+    if (!opt) return set_error(GC_EINVAL, "gc_dgc_step: options are null");
     if (!G || !U || !V) return set_error(GC_EINVAL, "gc_dgc_step: G, U and V must be non-null");
     if (!out || !out->idx || !out->val || !out->seg_off)
         return set_error(GC_EINVAL, "gc_dgc_step: out, out->idx, out->val, out->seg_off must be non-null");
+    const float momentum = opt->momentum, thr_G = opt->thr_G;
+    const int num_nodes = opt->num_nodes;
     if (!(momentum >= 0.0f && momentum < 1.0f))
         return set_error(GC_EINVAL, "gc_dgc_step: momentum must be in [0, 1)");
     if (std::isnan(thr_G) || std::isinf(thr_G))
         return set_error(GC_EINVAL, "gc_dgc_step: thr_G must be finite");
     if (num_nodes < 1) return set_error(GC_EINVAL, "gc_dgc_step: num_nodes must be >= 1");
-    if (out->cap < plan->total_k)
-        return set_error(GC_ECAPACITY, "gc_dgc_step: out->cap below the plan's total k");
+    if (opt->momentum_kind != GC_MOMENTUM_VANILLA && opt->momentum_kind != GC_MOMENTUM_NESTEROV)
+        return set_error(GC_EINVAL, "gc_dgc_step: momentum_kind must be GC_MOMENTUM_VANILLA or GC_MOMENTUM_NESTEROV");
+    if (opt->select != GC_SELECT_EXACT && opt->select != GC_SELECT_SAMPLED)
+        return set_error(GC_EINVAL, "gc_dgc_step: select must be GC_SELECT_EXACT or GC_SELECT_SAMPLED");
+    const bool sampled = opt->select == GC_SELECT_SAMPLED;
+    if (sampled && opt->sample_period < 1)
+        return set_error(GC_EINVAL, "gc_dgc_step: sample_period must be >= 1");
+    if (sampled && opt->over < 1) return set_error(GC_EINVAL, "gc_dgc_step: over must be >= 1");
+    if (opt->reserved != 0) return set_error(GC_EINVAL, "gc_dgc_step: reserved must be 0");
+    if (out->cap < dgc_capacity(plan, opt->select, opt->over))
+        return set_error(GC_ECAPACITY, "gc_dgc_step: out->cap below gc_dgc_message_cap");
     size_t need = dgc_workspace_bytes(plan);
     if (!ws || ws_bytes < need)
         return set_error(GC_ECAPACITY, "gc_dgc_step: workspace smaller than gc_plan_workspace_bytes");
@@ -723,25 +907,55 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     if (st != GC_OK) return st;
     DgcWs w = dgc_layout(plan, ws, nullptr);
     const bool clip = thr_G > 0.0f;
+    const bool nest = opt->momentum_kind == GC_MOMENTUM_NESTEROV;
     const float thr = clip ? static_cast<float>(static_cast<double>(thr_G) /
                                                 std::sqrt(static_cast<double>(num_nodes)))
                            : 0.0f;
+    const uint32_t over = sampled ? opt->over : 0u;
     const unsigned segs = static_cast<unsigned>(plan->nseg);
+    const unsigned wave_grid = grid_1d(plan->ndchunk, kWaves);
     if (clip)
         GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, G, w));
     GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
-    GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
-    GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<<<persistent_grid(dgc_update_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, V, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, w));
+    if (sampled) {
+        if (nest)
+            GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<true><<<wave_grid, kBlock, 0, stream>>>(P, G, U, V, momentum, opt->sample_period, w));
+        else
+            GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<false><<<wave_grid, kBlock, 0, stream>>>(P, G, U, V, momentum, opt->sample_period, w));
+        GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, opt->sample_period, w));
+    } else {
+        if (nest)
+            GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<true><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+        else
+            GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<false><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+        GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
+    }
+    if (nest)
+        GC_LAUNCH("dgc_update", stream, dgc_update_kernel<true><<<persistent_grid(dgc_update_kernel<true>, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    else
+        GC_LAUNCH("dgc_update", stream, dgc_update_kernel<false><<<persistent_grid(dgc_update_kernel<false>, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, over));
+    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<wave_grid, kBlock, 0, stream>>>(P, V, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, over));
+    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, over));
+    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
-    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
+    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<wave_grid, kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dgc_step launch");
     return GC_OK;
+}
+
+extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, float *V,
+                                 float momentum, float thr_G, int num_nodes, gc_sparse *out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream) {
+    gc_dgc_options o{};
+    o.momentum = momentum;
+    o.thr_G = thr_G;
+    o.num_nodes = num_nodes;
+    o.momentum_kind = GC_MOMENTUM_VANILLA;
+    o.select = GC_SELECT_EXACT;
+    return gc_dgc_step_ex(plan, G, U, V, &o, out, ws, ws_bytes, stream);
 }

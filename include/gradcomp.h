@@ -7,8 +7,8 @@
  *             Data-Parallel Distributed Training" (Chen et al.), the review's
  *             "Proposed method" list and Abstract.
  *   [DGC]     "Deep Gradient Compression: Reducing the Communication Bandwidth
- *             for Distributed Training" (Lin et al.), §3.1–§3.3, §5 and
- *             Appendices A, C, D.
+ *             for Distributed Training" (Lin et al.), §3.1–§3.3, §5, §6 and
+ *             Appendices A–D.
  *   [DCD]     "Communication Compression for Decentralized Training"
  *             (Tang et al.), DCD-PSGD steps 1–3 and the signal-to-noise
  *             parameter alpha of the compression operator.
@@ -213,6 +213,61 @@ gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, float *V,
                       gc_sparse *out, void *ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/*
+ * DGC step with the momentum kind and the selection mode chosen.
+ * gc_dgc_step(plan, G, U, V, m, thr_G, N, ...) is this call with
+ * {m, thr_G, N, GC_MOMENTUM_VANILLA, GC_SELECT_EXACT}.
+ *
+ * Momentum correction ([DGC] §3.2, App. B, App. D):
+ *   GC_MOMENTUM_VANILLA  (Alg. 3)  U_i <- fl32(fl32(m*U_i) + G'_i);  V_i <- fl32(V_i + U_i)
+ *   GC_MOMENTUM_NESTEROV (Alg. 4)  U_i <- fl32(fl32(m*U_i) + G'_i);
+ *                                  V_i <- fl32(V_i + fl32(fl32(m*U_i) + G'_i))  (updated U_i)
+ *   Nesterov SGD steps along m*U + G with U <- m*U + G; momentum correction
+ *   accumulates that step direction in V instead of applying it.  Clipping
+ *   (a7) and masking (a10) are as in gc_dgc_step.
+ *
+ * Selection ([DGC] §3.1, §5, §6):
+ *   GC_SELECT_EXACT    exactly k_s entries per segment, as in gc_dgc_step.
+ *   GC_SELECT_SAMPLED  the threshold is estimated from a sample and, when it
+ *     lets through far more entries than k_s, the exact top-k is taken among
+ *     those (hierarchical selection).  Per segment of n entries:
+ *       sample: window w = 0, 1, ... covers entries [32*P*w, 32*P*(w+1)) of
+ *         the segment; its block is the 32 entries starting at
+ *         32*P*w + 32*((w * 2654435769 mod 2^32) mod P), those at or past n
+ *         excluded (P = sample_period: 1/P of the entries; the page samples
+ *         0.1% to 1%, P = 1000 to 100).  S = number of sampled entries.
+ *       estimate: thr = the r-th largest key among the sampled entries'
+ *         keys (of V after a8), r = ceil(S * k_s / n).
+ *       C = #{ i : key_i >= thr }.  If C <= min(n, over * k_s), those C
+ *         entries are sent; otherwise the exact top k_s (as GC_SELECT_EXACT).
+ *     Segments' entries are laid end to end: seg_off[s+1] - seg_off[s] is
+ *     the segment's count.  The call's cost grows with S (small P is slow).
+ *   out->cap >= gc_dgc_message_cap(plan, opt).
+ * Errors: as gc_dgc_step; GC_EINVAL also for an unknown momentum_kind or
+ *         select, sample_period or over < 1 in sampled mode, reserved != 0.
+ */
+#define GC_MOMENTUM_VANILLA   0
+#define GC_MOMENTUM_NESTEROV  1
+#define GC_SELECT_EXACT       0
+#define GC_SELECT_SAMPLED     1
+typedef struct gc_dgc_options {
+    float    momentum;       /* 0 <= m < 1                                   */
+    float    thr_G;          /* clip threshold of the whole job; <= 0: none  */
+    int      num_nodes;      /* N >= 1                                       */
+    int      momentum_kind;  /* GC_MOMENTUM_*                                */
+    int      select;         /* GC_SELECT_*                                  */
+    uint32_t sample_period;  /* GC_SELECT_SAMPLED: P >= 1                    */
+    uint32_t over;           /* GC_SELECT_SAMPLED: budget factor >= 1        */
+    uint32_t reserved;       /* must be 0                                    */
+} gc_dgc_options;
+
+/* Entries a message needs for these options: sum of k_s (exact), or sum of
+ * min(n_s, over * k_s) (sampled).  0 if plan is NULL. */
+uint64_t  gc_dgc_message_cap(const gc_plan *plan, const gc_dgc_options *opt);
+gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V,
+                         const gc_dgc_options *opt, gc_sparse *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ pack */
 /*
  * Byte-exact run-length encoding of a message ([DGC] §3.1: 32-bit values and
@@ -292,8 +347,8 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
  * on the caller's stream; nothing else changes.
  *   kernels : comma-separated kernel names ("dgc_update,ada_apply"), "*" for
  *             all, NULL or "" to disable.  Names: dgc_norm, dgc_prep,
- *             dgc_sample, dgc_bound, dgc_update, dgc_select, dgc_stage,
- *             dgc_refine, dgc_count,
+ *             dgc_sample, dgc_bound, dgc_ssample, dgc_squant, dgc_update,
+ *             dgc_select, dgc_stage, dgc_refine, dgc_sbase, dgc_count,
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
  *             ada_apply, ada_fold, ada_emit, ada_residual,
  *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,

@@ -62,6 +62,17 @@ class HipPath:
         idx, val, off, _ = out.host()
         return Ud.cpu().numpy(), Vd.cpu().numpy(), idx, val, off
 
+    def dgc_ex(self, G, U, V, opt, tensors=False):
+        """gc_dgc_step_ex with a gc_dgc_options struct (binding.dgc_options)."""
+        Gd, Ud, Vd = (x if torch.is_tensor(x) else to_dev(x) for x in (G, U, V))
+        out = B.Sparse.empty(self.plan, B.gc_dgc_message_cap(self.plan, opt), dev())
+        B.gc_dgc_step_ex(self.plan, Gd, Ud, Vd, opt, out, self.workspace(B.GC_OP_DGC))
+        torch.cuda.synchronize()
+        if tensors:
+            return Ud, Vd, out
+        idx, val, off, _ = out.host()
+        return Ud.cpu().numpy(), Vd.cpu().numpy(), idx, val, off
+
     def adacomp(self, dW, R, scale_factor=2.0, tensors=False, state=None):
         """One AdaComp call; with `state` (a deferred-residual state tensor) the
         returned R is the exact residual, materialized by gc_adacomp_residual,

@@ -97,3 +97,16 @@ def test_hot_calls_reject_null_plan_without_touching_a_device():
     assert lib.gc_pack(None, 1, None, None, 0, None, None, 0, None) == B.GC_EINVAL
     assert lib.gc_decompress_accumulate(None, None, 1, None, 1, 0, None, 0, None) == B.GC_EINVAL
     assert lib.gc_dcd_compress(None, None, None, 10, 4, 512, 0, 0, None, None, None) == B.GC_EINVAL
+
+
+def test_dgc_ex_host_checks_and_message_cap():
+    lib = B.load()
+    assert lib.gc_dgc_step_ex(None, None, None, None, None, None, None, 0, None) == B.GC_EINVAL
+    t = W.make_table([5000, 100, 7], [1, 1, 1], [5, 1, 3])
+    p = B.Plan(t)
+    exact = B.dgc_options(0.9)
+    assert B.gc_dgc_message_cap(p, exact) == 9
+    # sampled: sum of min(n_s, over * k_s)
+    assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=2)) == 10 + 2 + 6
+    assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=3)) == 15 + 3 + 7
+    assert lib.gc_dgc_message_cap(None, None) == 0
