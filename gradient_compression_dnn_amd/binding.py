@@ -21,6 +21,7 @@ GC_MOMENTUM_VANILLA, GC_MOMENTUM_NESTEROV = 0, 1
 GC_SELECT_EXACT, GC_SELECT_SAMPLED = 0, 1
 GC_MAX_BIN_LEN = 4096
 GC_MAX_MESSAGES = 64
+GC_MAX_REPLICAS = 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgradcomp.so")
 
@@ -79,6 +80,12 @@ _SIGS = {
                                                 _P, ctypes.c_size_t, _P]),
     "gc_dcd_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
+    "gc_dcd_decode": (ctypes.c_int, [_P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32, _P, _P]),
+    "gc_dcd_mix": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_float, _P, ctypes.c_uint64, _P]),
+    "gc_ecd_compress": (ctypes.c_int, [_P, _P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                       ctypes.c_uint32, ctypes.c_uint64, _P, _P, _P]),
+    "gc_ecd_update": (ctypes.c_int, [_P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
+                                     ctypes.c_uint64, _P, _P]),
     "gc_timing_enable": (ctypes.c_int, [ctypes.c_char_p]),
     "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
 }
@@ -86,7 +93,8 @@ _SIGS = {
 KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
-           "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd")
+           "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd",
+           "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update")
 
 
 def gc_timing_enable(kernels) -> None:
@@ -329,3 +337,42 @@ def gc_dcd_compress(x, x_half, x_out, bits: int, bucket: int, seed: int, step: i
                                   n, int(bits), int(bucket), int(seed) & (2 ** 64 - 1),
                                   int(step) & (2 ** 64 - 1), _f32(scales, nb, "scales"), _ptr(codes),
                                   _stream(x_out)))
+
+
+def _codes_check(n: int, bits: int, bucket: int, scales: torch.Tensor, codes: torch.Tensor, fn: str):
+    nb = (n + bucket - 1) // bucket
+    if scales.numel() < nb or codes.numel() < (n * bits + 7) // 8 or codes.dtype != torch.uint8:
+        raise ValueError(f"{fn}: scales or codes too small")
+    return nb
+
+
+def gc_dcd_decode(scales: torch.Tensor, codes: torch.Tensor, x_hat, bits: int, bucket: int):
+    n = x_hat.numel()
+    nb = _codes_check(n, bits, bucket, scales, codes, "gc_dcd_decode")
+    _check(load().gc_dcd_decode(_f32(scales, nb, "scales"), _ptr(codes), n, int(bits), int(bucket),
+                                _f32(x_hat, n, "x_hat"), _stream(x_hat)))
+
+
+def gc_dcd_mix(replicas, weights, grad, lr: float, x_half):
+    n = x_half.numel()
+    K = len(replicas)
+    reps = (ctypes.c_void_p * max(K, 1))(*[_f32(r, n, "replica").value for r in replicas])
+    w = (ctypes.c_float * max(K, 1))(*[float(v) for v in weights])
+    _check(load().gc_dcd_mix(reps, w, K, _f32(grad, n, "grad"), float(lr), _f32(x_half, n, "x_half"), n,
+                             _stream(x_half)))
+
+
+def gc_ecd_compress(x_prev, x, t: int, bits: int, bucket: int, seed: int, scales: torch.Tensor,
+                    codes: torch.Tensor):
+    n = x.numel()
+    nb = _codes_check(n, bits, bucket, scales, codes, "gc_ecd_compress")
+    _check(load().gc_ecd_compress(_f32(x_prev, n, "x_prev"), _f32(x, n, "x"), n, int(t), int(bits),
+                                  int(bucket), int(seed) & (2 ** 64 - 1), _f32(scales, nb, "scales"),
+                                  _ptr(codes), _stream(x)))
+
+
+def gc_ecd_update(scales: torch.Tensor, codes: torch.Tensor, x_tilde, t: int, bits: int, bucket: int):
+    n = x_tilde.numel()
+    nb = _codes_check(n, bits, bucket, scales, codes, "gc_ecd_update")
+    _check(load().gc_ecd_update(_f32(scales, nb, "scales"), _ptr(codes), n, int(bits), int(bucket), int(t),
+                                _f32(x_tilde, n, "x_tilde"), _stream(x_tilde)))

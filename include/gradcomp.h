@@ -10,8 +10,9 @@
  *             for Distributed Training" (Lin et al.), §3.1–§3.3, §5, §6 and
  *             Appendices A–D.
  *   [DCD]     "Communication Compression for Decentralized Training"
- *             (Tang et al.), DCD-PSGD steps 1–3 and the signal-to-noise
- *             parameter alpha of the compression operator.
+ *             (Tang et al.), DCD-PSGD steps 1–3, the signal-to-noise
+ *             parameter alpha of the compression operator, and ECD-PSGD's
+ *             extrapolation and estimate (Eqs. 3 and 4).
  *   [SlimDP]  "Slim-DP: A Light Communication Data Parallelism for DNN",
  *             experimental setup (Quant-DP baseline: random quantization with
  *             buckets of 512).
@@ -340,6 +341,62 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
                           uint64_t step, float *scales, uint8_t *codes,
                           hipStream_t stream);
 
+/*
+ * DCD-PSGD step 3 ([DCD] step 3): a neighbour's replica advances by the
+ * received compressed difference, x_hat_i <- fl32(x_hat_i + C_i), with C_i
+ * decoded from the stream gc_dcd_compress wrote:
+ *   code_i = codes[i] (8 bits) or nibble i%2 of codes[i/2] (4 bits, even i in
+ *   the low nibble); level = code & L, L = 2^(bits-1) - 1; sign = bit bits-1;
+ *   C_i = level == 0 ? 0 : +-fl32(level * fl32(scales[i/bucket] / L)).
+ * Applied to a copy of x_t this reproduces gc_dcd_compress's x_out bit for
+ * bit, so every replica stays equal to its node's model.
+ *   scales [ceil(n/bucket)], codes [ceil(n*bits/8)] in (codes 4-byte aligned);
+ *   x_hat [n] in/out.
+ * Errors: GC_EINVAL (null, bits not 4 or 8, bucket 0, misaligned codes),
+ *         GC_ENOTSUP (bucket not a power of two in [4, 4096]),
+ *         GC_ERANGE (n > 2^32 - 8192).
+ */
+gc_status gc_dcd_decode(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                        uint32_t bucket, float *x_hat, hipStream_t stream);
+
+/*
+ * DCD-PSGD step 1 ([DCD] step 1): the weighted average of the replicas (the
+ * node's own model among them) and a stochastic gradient step:
+ *   S_i = +0, then S_i = fl32(S_i + fl32(weights[j] * replicas[j][i])) for
+ *         j = 0..K-1 in array order;
+ *   x_half_i = fl32(S_i - fl32(lr * grad_i)).
+ *   replicas (host array of K device pointers, 1 <= K <= GC_MAX_REPLICAS),
+ *   weights (host array of K: row i of the mixing matrix W), grad [n] in,
+ *   x_half [n] out (must not alias grad or a replica).
+ * Errors: GC_EINVAL (null, K out of range, aliasing), GC_ERANGE (n > 2^32 - 8192).
+ */
+#define GC_MAX_REPLICAS 16
+gc_status gc_dcd_mix(const float *const *replicas, const float *weights, int K,
+                     const float *grad, float lr, float *x_half, uint64_t n,
+                     hipStream_t stream);
+
+/*
+ * ECD-PSGD sender ([DCD] ECD-PSGD, Eq. 3): the extrapolated value
+ *   z_i = fl32(fl32(a * x_prev_i) + fl32(b * x_i)),  a = fl32(1 - t/2), b = fl32(t/2)
+ * (coefficients formed in double), quantized exactly as gc_dcd_compress
+ * quantizes z (same code layout and scales) with Philox step = t.
+ *   x_prev = x_{t-1}, x = x_t [n] in; t >= 1; scales, codes out.
+ * Errors: as gc_dcd_decode; GC_EINVAL also for t = 0.
+ */
+gc_status gc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint64_t t,
+                          int bits, uint32_t bucket, uint64_t seed, float *scales,
+                          uint8_t *codes, hipStream_t stream);
+
+/*
+ * ECD-PSGD receiver ([DCD] ECD-PSGD, Eq. 4): the estimate of a neighbour's
+ * model, x_tilde_i <- fl32(fl32(c1 * x_tilde_i) + fl32(c2 * C_i)) with
+ * c1 = fl32(1 - 2/t), c2 = fl32(2/t) (formed in double), C_i decoded as in
+ * gc_dcd_decode.  t >= 1.
+ * Errors: as gc_dcd_decode; GC_EINVAL also for t = 0.
+ */
+gc_status gc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                        uint32_t bucket, uint64_t t, float *x_tilde, hipStream_t stream);
+
 /* ----------------------------------------------------------- measurement */
 /*
  * Kernel timing for measurement tools (off by default).  While enabled, each
@@ -352,7 +409,7 @@ gc_status gc_dcd_compress(const float *x, const float *x_half, float *x_out,
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
  *             ada_apply, ada_fold, ada_emit, ada_residual,
  *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,
- *             decode, dcd.
+ *             decode, dcd, dcd_decode, dcd_mix, ecd_compress, ecd_update.
  * gc_timing_take waits for the recorded events of one kernel and returns the
  * summed duration in milliseconds and the number of launches, then forgets
  * them.  Host-thread safe; not for use while a stream is being captured.

@@ -69,6 +69,12 @@ def lib():
         L.orc_philox4x32_10.argtypes = [P, P, P]
         L.orc_dcd.argtypes = [P, P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                               ctypes.c_uint64, ctypes.c_uint64, P, P]
+        L.orc_dcd_decode.argtypes = [P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32, P]
+        L.orc_dcd_mix.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, P, ctypes.c_uint64]
+        L.orc_ecd_compress.argtypes = [P, P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                       ctypes.c_uint32, ctypes.c_uint64, P, P]
+        L.orc_ecd_update.argtypes = [P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
+                                     ctypes.c_uint64, P]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -219,3 +225,45 @@ def dcd(x, x_half, bits=4, bucket=512, seed=0, step=0):
     lib().orc_dcd(_ptr(x), _ptr(xh), _ptr(xo), n, int(bits), int(bucket), int(seed) & (2**64 - 1),
                   int(step) & (2**64 - 1), _ptr(scales), _ptr(codes))
     return xo, scales[:(n + bucket - 1) // bucket], codes[:(n * bits + 7) // 8]
+
+
+def dcd_decode(scales, codes, x_hat, bits=4, bucket=512):
+    """DCD-PSGD step 3 on a copy of x_hat: x_hat + C(z)."""
+    xh = _f32(x_hat, copy=True)
+    sc = _f32(scales)
+    cd = np.ascontiguousarray(codes, dtype=np.uint8)
+    lib().orc_dcd_decode(_ptr(sc), _ptr(cd), xh.size, int(bits), int(bucket), _ptr(xh))
+    return xh
+
+
+def dcd_mix(replicas, weights, grad, lr):
+    """DCD-PSGD step 1: sum_j weights[j] * replicas[j] (in order) - lr * grad."""
+    reps = [_f32(r) for r in replicas]
+    K = len(reps)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    g = _f32(grad)
+    out = np.empty(g.size, np.float32)
+    rp = (ctypes.c_void_p * max(K, 1))(*[r.ctypes.data for r in reps])
+    lib().orc_dcd_mix(K, rp, _ptr(w), _ptr(g), float(lr), _ptr(out), g.size)
+    return out
+
+
+def ecd_compress(x_prev, x, t, bits=4, bucket=512, seed=0):
+    """ECD-PSGD Eq. (3): (scales, codes) of C((1 - t/2) x_prev + (t/2) x)."""
+    xp = _f32(x_prev)
+    xx = _f32(x)
+    n = xx.size
+    scales = np.zeros(max((n + bucket - 1) // bucket, 1), np.float32)
+    codes = np.zeros(max((n * bits + 7) // 8, 1), np.uint8)
+    lib().orc_ecd_compress(_ptr(xp), _ptr(xx), n, int(t), int(bits), int(bucket),
+                           int(seed) & (2**64 - 1), _ptr(scales), _ptr(codes))
+    return scales[:(n + bucket - 1) // bucket], codes[:(n * bits + 7) // 8]
+
+
+def ecd_update(scales, codes, x_tilde, t, bits=4, bucket=512):
+    """ECD-PSGD Eq. (4) on a copy of x_tilde."""
+    xt = _f32(x_tilde, copy=True)
+    sc = _f32(scales)
+    cd = np.ascontiguousarray(codes, dtype=np.uint8)
+    lib().orc_ecd_update(_ptr(sc), _ptr(cd), xt.size, int(bits), int(bucket), int(t), _ptr(xt))
+    return xt

@@ -508,15 +508,14 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
 
 /* --------------------------------------------------------------------- DCD */
 /*
- * DCD-PSGD (Tang et al.) step 2: z = x_{t+1/2} - x_t, x_{t+1} = x_t + C(z);
- * C is random quantization (the page allows random quantization or random
- * sparsification) in buckets (Slim-DP's Quant-DP setting uses buckets of 512)
- * at 8 or 4 bits, with unbiased stochastic rounding to a uniform grid whose
- * top level is the bucket's max magnitude.
+ * Random quantization C(z) of a flat vector (the compression operator of
+ * DCD-PSGD and ECD-PSGD; the page allows random quantization or random
+ * sparsification; Slim-DP's Quant-DP setting uses buckets of 512) at 8 or 4
+ * bits: unbiased stochastic rounding to a uniform grid whose top level is the
+ * bucket's max magnitude.  C_out[i] receives C(z)_i.
  */
-void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
-             int bits, uint32_t bucket, uint64_t seed, uint64_t step,
-             float *scales, uint8_t *codes)
+static void quantize(const float *z, uint64_t n, int bits, uint32_t bucket, uint64_t seed,
+                     uint64_t step, float *scales, uint8_t *codes, float *C_out)
 {
     const uint32_t L = (1u << (bits - 1)) - 1u;
     const float Lf = (float)L;
@@ -530,18 +529,16 @@ void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
         uint64_t hi = lo + bucket < n ? lo + bucket : n;
         float sb = 0.0f;
         for (uint64_t i = lo; i < hi; ++i) {
-            float z = x_half[i] - x[i];
-            float a = fabsf(z);
+            float a = fabsf(z[i]);
             if (a > sb) sb = a;
         }
         scales[b] = sb;
         float inv = sb > 0.0f ? Lf / sb : 0.0f;
         float stepq = sb > 0.0f ? sb / Lf : 0.0f;
         for (uint64_t i = lo; i < hi; ++i) {
-            float z = x_half[i] - x[i];
             uint32_t level = 0;
             if (sb > 0.0f) {
-                float y = fabsf(z) * inv;
+                float y = fabsf(z[i]) * inv;
                 if (y > Lf) y = Lf;
                 float l0 = floorf(y);
                 float f = y - l0;
@@ -557,10 +554,10 @@ void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
             uint32_t code = 0;
             if (level > 0) {
                 float mag = (float)level * stepq;
-                C = signbit(z) ? -mag : mag;
-                code = (signbit(z) ? 1u << (bits - 1) : 0u) | level;
+                C = signbit(z[i]) ? -mag : mag;
+                code = (signbit(z[i]) ? 1u << (bits - 1) : 0u) | level;
             }
-            x_out[i] = x[i] + C;
+            C_out[i] = C;
             if (bits == 8) {
                 codes[i] = (uint8_t)code;
             } else {
@@ -569,5 +566,100 @@ void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
                 codes[i / 2] |= (uint8_t)(code << (4 * (i % 2)));
             }
         }
+    }
+}
+
+/* C(z)_i from the transmitted codes and bucket scales: the inverse of
+ * quantize's encoding (level, sign; value level * fl(s_b / L)). */
+static float dequantize(const float *scales, const uint8_t *codes, uint64_t i, int bits,
+                        uint32_t bucket)
+{
+    const uint32_t L = (1u << (bits - 1)) - 1u;
+    uint32_t code = bits == 8 ? codes[i] : (uint32_t)(codes[i / 2] >> (4 * (i % 2))) & 0xFu;
+    uint32_t level = code & L;
+    if (level == 0) return 0.0f;
+    float sb = scales[i / bucket];
+    float stepq = sb / (float)L;
+    float mag = (float)level * stepq;
+    return (code >> (bits - 1)) ? -mag : mag;
+}
+
+/*
+ * DCD-PSGD (Tang et al.) step 2: z = x_{t+1/2} - x_t, x_{t+1} = x_t + C(z).
+ */
+void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
+             int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+             float *scales, uint8_t *codes)
+{
+    float *z = (float *)calloc(n ? n : 1, sizeof(float));
+    float *C = (float *)calloc(n ? n : 1, sizeof(float));
+    for (uint64_t i = 0; i < n; ++i) z[i] = x_half[i] - x[i];
+    quantize(z, n, bits, bucket, seed, step, scales, codes, C);
+    for (uint64_t i = 0; i < n; ++i) x_out[i] = x[i] + C[i];
+    free(z);
+    free(C);
+}
+
+/*
+ * DCD-PSGD step 3: a neighbour's replica advances by the received C(z):
+ * x_hat <- x_hat + C(z).
+ */
+void orc_dcd_decode(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                    uint32_t bucket, float *x_hat)
+{
+    for (uint64_t i = 0; i < n; ++i) x_hat[i] = x_hat[i] + dequantize(scales, codes, i, bits, bucket);
+}
+
+/*
+ * DCD-PSGD step 1: x_{t+1/2} = sum_j W_ij x_hat_j - gamma * grad, the weighted
+ * terms added in the order given, from +0.
+ */
+void orc_dcd_mix(int K, const float *const *replicas, const float *weights, const float *grad,
+                 float lr, float *x_half, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; ++i) {
+        float s = 0.0f;
+        for (int j = 0; j < K; ++j) {
+            float term = weights[j] * replicas[j][i];
+            s = s + term;
+        }
+        float g = lr * grad[i];
+        x_half[i] = s - g;
+    }
+}
+
+/*
+ * ECD-PSGD, Eq. (3): the sender extrapolates z_t = (1 - t/2) x_{t-1} + (t/2) x_t
+ * and sends C(z_t).  The coefficients are formed in double and rounded to fp32;
+ * t is also the random-number step.
+ */
+void orc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint64_t t, int bits,
+                      uint32_t bucket, uint64_t seed, float *scales, uint8_t *codes)
+{
+    const float a = (float)(1.0 - 0.5 * (double)t), b = (float)(0.5 * (double)t);
+    float *z = (float *)calloc(n ? n : 1, sizeof(float));
+    float *C = (float *)calloc(n ? n : 1, sizeof(float));
+    for (uint64_t i = 0; i < n; ++i) {
+        float p = a * x_prev[i];
+        float q = b * x[i];
+        z[i] = p + q;
+    }
+    quantize(z, n, bits, bucket, seed, t, scales, codes, C);
+    free(z);
+    free(C);
+}
+
+/*
+ * ECD-PSGD, Eq. (4): the receiver's estimate of the sender's model,
+ * x~_t = (1 - 2/t) x~_{t-1} + (2/t) C(z_t), coefficients in double rounded to fp32.
+ */
+void orc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                    uint32_t bucket, uint64_t t, float *x_tilde)
+{
+    const float c1 = (float)(1.0 - 2.0 / (double)t), c2 = (float)(2.0 / (double)t);
+    for (uint64_t i = 0; i < n; ++i) {
+        float p = c1 * x_tilde[i];
+        float q = c2 * dequantize(scales, codes, i, bits, bucket);
+        x_tilde[i] = p + q;
     }
 }

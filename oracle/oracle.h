@@ -90,4 +90,20 @@ void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
              int bits, uint32_t bucket, uint64_t seed, uint64_t step,
              float *scales, uint8_t *codes);
 
+/* DCD-PSGD step 3: x_hat <- x_hat + C(z) from codes and scales. */
+void orc_dcd_decode(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                    uint32_t bucket, float *x_hat);
+
+/* DCD-PSGD step 1: x_half = sum_j weights[j] * replicas[j] - lr * grad. */
+void orc_dcd_mix(int K, const float *const *replicas, const float *weights, const float *grad,
+                 float lr, float *x_half, uint64_t n);
+
+/* ECD-PSGD Eq. (3): codes and scales of C((1 - t/2) x_prev + (t/2) x). */
+void orc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint64_t t, int bits,
+                      uint32_t bucket, uint64_t seed, float *scales, uint8_t *codes);
+
+/* ECD-PSGD Eq. (4): x_tilde <- (1 - 2/t) x_tilde + (2/t) C(z). */
+void orc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int bits,
+                    uint32_t bucket, uint64_t t, float *x_tilde);
+
 #endif
