@@ -106,6 +106,73 @@ def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
                       f"{t_total:.1f} s on {threads} host threads"}
 
 
+def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log, reps: int = 5):
+    """Time the other calls of the path on the same workload, each alone
+    (after the step timing, outside `value`): DGC with Nesterov momentum and
+    with sampled selection, and the replica side of DCD-PSGD and ECD-PSGD.
+    Per call: ms, the method's algorithmic bytes and their fraction of HBM
+    peak, and the per-kernel split of one more call."""
+    import torch
+
+    n = plan.n_total
+    nb = (n + bucket - 1) // bucket
+    code_bytes = n // 2 + 4 * nb  # 4-bit codes and scales
+    U2 = torch.zeros(n, dtype=torch.float32, device=dev)
+    V2 = torch.zeros_like(U2)
+    L = X + 1e-4  # two neighbours' replicas, near the node's model
+    R_ = X - 1e-4
+    XHAT = X.clone()
+    XT = X.clone()
+    out = {}
+
+    def timed(name, fn, alg_bytes, extra=None):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(1 + r)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        B.gc_timing_enable("*")
+        fn(1 + reps)
+        torch.cuda.synchronize()
+        kern = {}
+        for kname in B.KERNELS:
+            kms, cnt = B.gc_timing_take(kname)
+            if cnt:
+                kern[kname] = round(kms * 1000.0, 2)
+        B.gc_timing_enable(None)
+        rec = {"ms": round(ms, 4), "alg_bytes": alg_bytes,
+               "alg_hbm_frac": round(alg_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+               "kernel_us": kern}
+        if extra:
+            rec.update(extra())
+        out[name] = rec
+        log(f"variant {name}: {ms:.3f} ms, {rec['alg_hbm_frac']:.3f} of HBM peak")
+
+    for label, opt in (("dgc_nesterov_exact", B.dgc_options(0.9, 1.0, 1, nesterov=True)),
+                       ("dgc_sampled_p100_over2", B.dgc_options(0.9, 1.0, 1, sampled=True, sample_period=100, over=2)),
+                       ("dgc_sampled_p1000_over2", B.dgc_options(0.9, 1.0, 1, sampled=True, sample_period=1000,
+                                                                 over=2))):
+        msg = B.Sparse.empty(plan, B.gc_dgc_message_cap(plan, opt), dev)
+        U2.zero_()
+        V2.zero_()
+
+        def run(t, opt=opt, msg=msg):
+            B.gc_dgc_step_ex(plan, G[t % len(G)], U2, V2, opt, msg, ws[B.GC_OP_DGC])
+
+        timed(label, run, 20 * n, lambda msg=msg: {"entries": msg.count(), "k_total": plan.total_k})
+    timed("dcd_decode_4bit", lambda t: B.gc_dcd_decode(scales, codes, XHAT, 4, bucket), 8 * n + code_bytes)
+    timed("dcd_mix_ring3", lambda t: B.gc_dcd_mix([X, L, R_], [0.5, 0.25, 0.25], G[t % len(G)], 0.1, XO),
+          20 * n)  # three replicas and the gradient read, x_half written
+    timed("ecd_compress_4bit", lambda t: B.gc_ecd_compress(X, XH[t % len(XH)], 2 + t, 4, bucket, 0x5EED,
+                                                           scales, codes), 8 * n + code_bytes)
+    timed("ecd_update_4bit", lambda t: B.gc_ecd_update(scales, codes, XT, 2 + t, 4, bucket), 8 * n + code_bytes)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +180,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--grads", type=int, default=2, help="distinct seeded gradients cycled over steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the DGC Nesterov / sampled and DCD replica / ECD calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (for counter calibration)")
     args = ap.parse_args(argv)
@@ -266,6 +335,9 @@ def main(argv=None):
                      "dgc_packed_bytes": int(dn.item()), "adacomp_packed_bytes": int(an.item())},
         "source_digest": digest,
     }
+    if not args.no_variants:
+        log("variants")
+        result["variants"] = measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, grads, x0)
