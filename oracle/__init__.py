@@ -75,6 +75,9 @@ def lib():
                                        ctypes.c_uint32, ctypes.c_uint64, P, P]
         L.orc_ecd_update.argtypes = [P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                                      ctypes.c_uint64, P]
+        L.orc_slimdp_core.argtypes = [P, ctypes.c_int, P, P, ctypes.c_float, P, P, P, P]
+        L.orc_slimdp_explore.argtypes = [P, ctypes.c_int, P, P, ctypes.c_uint64, ctypes.c_uint64,
+                                         P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -267,3 +270,38 @@ def ecd_update(scales, codes, x_tilde, t, bits=4, bucket=512):
     cd = np.ascontiguousarray(codes, dtype=np.uint8)
     lib().orc_ecd_update(_ptr(sc), _ptr(cd), xt.size, int(bits), int(bucket), int(t), _ptr(xt))
     return xt
+
+
+def mask_words(table) -> int:
+    """Words of a Slim-DP core bitmap: ceil(n_s / 32) per segment."""
+    t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+    return int(((t[:, 1] + 31) // 32).sum())
+
+
+def slimdp_core(table, w, g, c):
+    """Returns (core_idx, core_val (= S), seg_off, mask)."""
+    t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+    w = _f32(w)
+    g = _f32(g)
+    K = int(t[:, 3].sum())
+    idx = np.zeros(max(K, 1), np.uint32)
+    val = np.zeros(max(K, 1), np.float32)
+    off = np.zeros(len(t) + 1, np.uint32)
+    mask = np.zeros(max(mask_words(t), 1), np.uint32)
+    lib().orc_slimdp_core(_segs(t), len(t), _ptr(w), _ptr(g), float(c), _ptr(idx), _ptr(val),
+                          _ptr(off), _ptr(mask))
+    return idx[:K].copy(), val[:K].copy(), off, mask[:mask_words(t)].copy()
+
+
+def slimdp_explore(table, delta, mask, seed, step):
+    """Returns (idx, val (= delta at idx), seg_off)."""
+    t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+    d = _f32(delta)
+    mk = np.ascontiguousarray(mask, dtype=np.uint32)
+    K = int(t[:, 3].sum())
+    idx = np.zeros(max(K, 1), np.uint32)
+    val = np.zeros(max(K, 1), np.float32)
+    off = np.zeros(len(t) + 1, np.uint32)
+    lib().orc_slimdp_explore(_segs(t), len(t), _ptr(d), _ptr(mk), int(seed) & (2**64 - 1),
+                             int(step) & (2**64 - 1), _ptr(idx), _ptr(val), _ptr(off))
+    return idx[:K].copy(), val[:K].copy(), off

@@ -663,3 +663,97 @@ void orc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int b
         x_tilde[i] = p + q;
     }
 }
+
+/* ------------------------------------------------------------------ Slim-DP */
+/*
+ * Slim-DP (Sun et al.), §3: the communication set is a core of significant
+ * parameters plus a random explorer.
+ *  - Significance of parameter i combines the magnitude of the parameter and
+ *    of its gradient as a weighted sum with a positive coefficient c (the
+ *    equation itself is not on the page): S_i = |w_i| + c |g_i|;
+ *  - the core is the top-ranked parameters by S (here per tensor, k_s of
+ *    them, ties to the lower index); a bitmap marks it, one word-aligned run
+ *    of ceil(n_s/32) words per tensor, bit j%32 of word j/32 for entry j;
+ *  - the explorer is a uniformly random set of the parameters outside the
+ *    core, resampled every communication: the m_s non-core entries with the
+ *    largest Philox4x32-10 keys (key (seed lo, seed hi), counter (j/4, s,
+ *    step lo, step hi), word j%4, as r >> 1 | 1; core entries rank below).
+ */
+static void topk_by_key(const uint32_t *key, uint32_t n, uint32_t k, uint32_t *chosen)
+{
+    keyed *order = (keyed *)malloc(sizeof(keyed) * (size_t)(n ? n : 1));
+    for (uint32_t i = 0; i < n; ++i) {
+        order[i].key = key[i];
+        order[i].pos = i;
+    }
+    qsort(order, n, sizeof(keyed), by_key_desc_pos_asc);
+    for (uint32_t j = 0; j < k; ++j) chosen[j] = order[j].pos;
+    qsort(chosen, k, sizeof(uint32_t), u32_asc);
+    free(order);
+}
+
+void orc_slimdp_core(const orc_seg *segs, int nseg, const float *w, const float *g, float c,
+                     uint32_t *core_idx, float *core_val, uint32_t *seg_off, uint32_t *mask)
+{
+    uint32_t pos = 0;
+    uint64_t mbase = 0;
+    for (int s = 0; s < nseg; ++s) {
+        const uint64_t base = segs[s].offset;
+        const uint32_t n = segs[s].length, k = segs[s].k;
+        float *S = (float *)malloc(sizeof(float) * (size_t)n);
+        uint32_t *key = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n);
+        uint32_t *chosen = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)k);
+        for (uint32_t i = 0; i < n; ++i) {
+            float cg = c * fabsf(g[base + i]);
+            S[i] = fabsf(w[base + i]) + cg;
+            key[i] = abs_bits(S[i]);
+        }
+        topk_by_key(key, n, k, chosen);
+        uint32_t words = (n + 31) / 32;
+        memset(mask + mbase, 0, sizeof(uint32_t) * words);
+        seg_off[s] = pos;
+        for (uint32_t j = 0; j < k; ++j) {
+            core_idx[pos + j] = (uint32_t)(base + chosen[j]);
+            core_val[pos + j] = S[chosen[j]];
+            mask[mbase + chosen[j] / 32] |= 1u << (chosen[j] % 32);
+        }
+        pos += k;
+        mbase += words;
+        free(S);
+        free(key);
+        free(chosen);
+    }
+    seg_off[nseg] = pos;
+}
+
+void orc_slimdp_explore(const orc_seg *segs, int nseg, const float *delta, const uint32_t *mask,
+                        uint64_t seed, uint64_t step, uint32_t *idx, float *val, uint32_t *seg_off)
+{
+    const uint32_t pkey[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t pos = 0;
+    uint64_t mbase = 0;
+    for (int s = 0; s < nseg; ++s) {
+        const uint64_t base = segs[s].offset;
+        const uint32_t n = segs[s].length, m = segs[s].k;
+        uint32_t *key = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n);
+        uint32_t *chosen = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(m ? m : 1));
+        for (uint32_t j = 0; j < n; ++j) {
+            uint32_t ctr[4] = {j / 4, (uint32_t)s, (uint32_t)step, (uint32_t)(step >> 32)};
+            uint32_t r[4];
+            orc_philox4x32_10(ctr, pkey, r);
+            int in_core = (mask[mbase + j / 32] >> (j % 32)) & 1u;
+            key[j] = in_core ? 0u : ((r[j % 4] >> 1) | 1u);
+        }
+        topk_by_key(key, n, m, chosen);
+        seg_off[s] = pos;
+        for (uint32_t j = 0; j < m; ++j) {
+            idx[pos + j] = (uint32_t)(base + chosen[j]);
+            val[pos + j] = delta[base + chosen[j]];
+        }
+        pos += m;
+        mbase += (n + 31) / 32;
+        free(key);
+        free(chosen);
+    }
+    seg_off[nseg] = pos;
+}

@@ -106,4 +106,15 @@ void orc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint64_t 
 void orc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int bits,
                     uint32_t bucket, uint64_t t, float *x_tilde);
 
+/* Slim-DP core: per segment the k_s entries of largest S = |w| + c|g|
+ * (ties to the lower index), ascending; core_val = S.  mask receives one
+ * word-aligned run of ceil(n_s/32) words per segment marking the core. */
+void orc_slimdp_core(const orc_seg *segs, int nseg, const float *w, const float *g, float c,
+                     uint32_t *core_idx, float *core_val, uint32_t *seg_off, uint32_t *mask);
+
+/* Slim-DP explorer: per segment the k_s non-core entries with the largest
+ * Philox keys, ascending, with val = delta at them. */
+void orc_slimdp_explore(const orc_seg *segs, int nseg, const float *delta, const uint32_t *mask,
+                        uint64_t seed, uint64_t step, uint32_t *idx, float *val, uint32_t *seg_off);
+
 #endif
