@@ -86,6 +86,11 @@ _SIGS = {
                                        ctypes.c_uint32, ctypes.c_uint64, _P, _P, _P]),
     "gc_ecd_update": (ctypes.c_int, [_P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                                      ctypes.c_uint64, _P, _P]),
+    "gc_slimdp_mask_words": (ctypes.c_uint64, [_P]),
+    "gc_slimdp_core": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "gc_slimdp_explore": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_uint64, ctypes.c_uint64, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "gc_slimdp_core_values": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "gc_timing_enable": (ctypes.c_int, [ctypes.c_char_p]),
     "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
 }
@@ -94,7 +99,7 @@ KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dg
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd",
-           "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update")
+           "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update", "slimdp_values")
 
 
 def gc_timing_enable(kernels) -> None:
@@ -376,3 +381,31 @@ def gc_ecd_update(scales: torch.Tensor, codes: torch.Tensor, x_tilde, t: int, bi
     nb = _codes_check(n, bits, bucket, scales, codes, "gc_ecd_update")
     _check(load().gc_ecd_update(_f32(scales, nb, "scales"), _ptr(codes), n, int(bits), int(bucket), int(t),
                                 _f32(x_tilde, n, "x_tilde"), _stream(x_tilde)))
+
+
+def gc_slimdp_mask_words(plan: Plan) -> int:
+    return int(load().gc_slimdp_mask_words(plan.handle))
+
+
+def gc_slimdp_core(plan: Plan, w, g, c: float, core: Sparse, core_mask: torch.Tensor, ws: torch.Tensor):
+    n = plan.n_total
+    if core_mask.dtype != torch.int32 or core_mask.numel() < gc_slimdp_mask_words(plan):
+        raise ValueError("gc_slimdp_core: core_mask must be int32 (holding u32) of gc_slimdp_mask_words words")
+    msg = core.struct()
+    _check(load().gc_slimdp_core(plan.handle, _f32(w, n, "w"), _f32(g, n, "g"), float(c), ctypes.byref(msg),
+                                 _ptr(core_mask), _ptr(ws), ws.numel(), _stream(core_mask)))
+
+
+def gc_slimdp_explore(plan: Plan, core_plan: Plan, delta, core_mask: torch.Tensor, seed: int, step: int,
+                      out: Sparse, ws: torch.Tensor):
+    n = plan.n_total
+    msg = out.struct()
+    _check(load().gc_slimdp_explore(plan.handle, core_plan.handle, _f32(delta, n, "delta"), _ptr(core_mask),
+                                    int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), ctypes.byref(msg),
+                                    _ptr(ws), ws.numel(), _stream(delta)))
+
+
+def gc_slimdp_core_values(core_plan: Plan, core: Sparse, delta, values):
+    msg = core.struct()
+    _check(load().gc_slimdp_core_values(core_plan.handle, ctypes.byref(msg), _f32(delta, core_plan.n_total, "delta"),
+                                        _f32(values, core_plan.total_k, "values"), _stream(values)))

@@ -23,32 +23,6 @@ namespace gc {
 
 namespace {
 
-// Full 64-bit product of two u32 in one VALU op (v_mad_u64_u32 with a zero
-// addend); on gfx950 this is faster than the separate low and high multiplies.
-__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) {
-    uint64_t r, carry;
-    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "v"(b));
-    return r;
-}
-
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products, the
-// key advanced by the Weyl constants between rounds.
-__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
-    constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
-    constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        const uint64_t p0 = mul_wide(kM0, c.x);
-        const uint64_t p1 = mul_wide(kM1, c.z);
-        c = make_uint4(uint32_t(p1 >> 32) ^ c.y ^ k0, uint32_t(p1), uint32_t(p0 >> 32) ^ c.w ^ k1,
-                       uint32_t(p0));
-        k0 += kW0;
-        k1 += kW1;
-    }
-    return c;
-}
-
 // What the quantizer is applied to.  kDiff: z = xh - x, and xo = x + C(z) is
 // written.  kExtrap: z = fl(a x) + fl(b xh) (x = x_{t-1}, xh = x_t), nothing
 // but the codes and scales is written.

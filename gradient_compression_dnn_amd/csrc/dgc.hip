@@ -46,6 +46,7 @@
 // workgroup) lays the segments' variable-size outputs end to end.
 #include <algorithm>
 #include <cmath>
+#include <string>
 
 #include "gc_internal.hpp"
 
@@ -63,16 +64,33 @@ struct SegState {
     uint32_t base;  // first message slot of the segment
 };
 
+// What the selection kernels rank (the key is the magnitude bits of a value):
+//   kVanilla, kNesterov  DGC: V after the momentum-corrected update (U, V
+//                        updated in place; sent entries masked)
+//   kSignif              Slim-DP core: S = |w| + c |g| (read only)
+//   kExplore             Slim-DP explorer: a Philox key outside the core, 0
+//                        inside it (read only; the message carries delta)
+enum Mode { kVanilla = 0, kNesterov = 1, kSignif = 2, kExplore = 3 };
+
+struct Src {
+    const float *G;  // DGC: gradient; kSignif: g; kExplore: delta
+    float *U;        // DGC: momentum; kSignif: w (read only)
+    float *V;        // DGC: accumulator
+    float m;         // DGC: momentum; kSignif: c
+    uint32_t k0, k1, slo, shi;  // kExplore: Philox key (seed) and step
+    uint32_t *mask;  // kSignif: core bitmap out; kExplore: core bitmap in
+};
+
 // Momentum correction (§3.2; App. B and D).  Vanilla: U <- m U + G',
 // V <- V + U.  Nesterov: U <- m U + G', V <- V + (m U + G') with the updated U,
 // the Nesterov step direction accumulated in place of being applied.  One
 // rounding per operation, in this order.
-template <bool kNest>
+template <int kMode>
 __device__ __forceinline__ void momentum_update(float m, float gc, float &u, float &v) {
     float un = m * u;
     un = un + gc;
     u = un;
-    if (kNest) {
+    if (kMode == kNesterov) {
         float d = m * un;
         d = d + gc;
         v = v + d;
@@ -139,6 +157,27 @@ struct ChunkInfo {
 };
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return dev_f2u(v) & 0x7FFFFFFFu; }
+
+// Slim-DP significance (Slim-DP §3.2, a weighted sum of the magnitudes of
+// the parameter and of its gradient): fl(|w| + fl(c |g|)).
+__device__ __forceinline__ float significance(float w, float g, float c) {
+    const float cg = c * fabsf(g);
+    return fabsf(w) + cg;
+}
+
+// Slim-DP explorer values of the 4 entries [j0, j0 + 4) of segment s (j0 a
+// multiple of 4): the key r >> 1 | 1 of Philox4x32-10 word j % 4 (counter
+// (j / 4, s, step), key = seed) as float bits, 0 for core entries.  `words`
+// bounds the bitmap read (lanes past the segment end read its last word).
+__device__ __forceinline__ void explore_values(const Src &a, const SegDev &seg, uint32_t s, uint32_t j0,
+                                               float (&v)[4]) {
+    const uint4 r = philox4x32_10(make_uint4(j0 >> 2, s, a.slo, a.shi), a.k0, a.k1);
+    const uint32_t words = (seg.len + 31) / 32;
+    const uint32_t mw = a.mask[seg.mbase + min(j0 >> 5, words - 1)] >> (j0 & 31);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = dev_u2f(((mw >> q) & 1u) ? 0u : ((rw[q] >> 1) | 1u));
+}
 
 // Chunk geometry with the segment record cached across consecutive chunks
 // (a persistent workgroup's chunks mostly share a segment).
@@ -249,11 +288,8 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
 // Half a wave per chunk: in a sampled chunk, lane l < min(32, cnt) computes
 // V' of element sample_offset + l with the update's own arithmetic and
 // records its key (plain stores: no atomics).
-template <bool kNest>
-__global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const float *__restrict__ G,
-                                                            const float *__restrict__ U,
-                                                            const float *__restrict__ V, float m,
-                                                            DgcWs w) {
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, Src a, DgcWs w) {
     const uint32_t c = (blockIdx.x * kWaves + wave_id()) * 2u + (uint32_t(lane_id()) >> 5);
     const uint32_t l = lane_id() & 31;
     if (c >= P.ndchunk) return;
@@ -261,11 +297,23 @@ __global__ __launch_bounds__(kBlock) void dgc_sample_kernel(PlanDev P, const flo
     const uint32_t cnt = rec.y;
     const SegDev seg = P.seg[rec.z];
     if ((c - seg.dchunk0) % sample_stride(seg.dnchunk) != 0 || l >= min(kSamples, cnt)) return;
-    const uint64_t e = uint64_t(rec.x) + sample_offset(c, cnt) + l;
-    const float clip = w.st[rec.z].clip;
-    const float gc = clip * G[e];
-    float un = U[e], vn = V[e];
-    momentum_update<kNest>(m, gc, un, vn);
+    const uint32_t jc = sample_offset(c, cnt) + l;  // inside the chunk
+    const uint64_t e = uint64_t(rec.x) + jc;
+    float vn;
+    if (kMode == kSignif) {
+        vn = significance(a.U[e], a.G[e], a.m);
+    } else if (kMode == kExplore) {
+        const uint32_t j = (rec.w << kChunkLog2) + jc;
+        float v4[4];
+        explore_values(a, seg, rec.z, j & ~3u, v4);
+        vn = v4[j & 3];
+    } else {
+        const float clip = w.st[rec.z].clip;
+        const float gc = clip * a.G[e];
+        float un = a.U[e];
+        vn = a.V[e];
+        momentum_update<kMode>(a.m, gc, un, vn);
+    }
     w.skey[size_t(c) * kSamples + l] = mag_key(vn);
 }
 
@@ -281,11 +329,8 @@ __device__ __forceinline__ uint32_t sample_block_offset(uint32_t w, uint32_t per
     return 32u * ((w * 2654435769u) % period);  // Fibonacci hash of the window, mod 2^32
 }
 
-template <bool kNest>
-__global__ __launch_bounds__(kBlock) void dgc_ssample_kernel(PlanDev P, const float *__restrict__ G,
-                                                             const float *__restrict__ U,
-                                                             const float *__restrict__ V, float m,
-                                                             uint32_t period, DgcWs w) {
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void dgc_ssample_kernel(PlanDev P, Src a, uint32_t period, DgcWs w) {
     const uint32_t c = blockIdx.x * kWaves + wave_id();
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
@@ -303,9 +348,9 @@ __global__ __launch_bounds__(kBlock) void dgc_ssample_kernel(PlanDev P, const fl
         const uint64_t p = start + l;
         if (start < pos0 || start >= pos1 || p >= seg.len) continue;
         const uint64_t e = seg.off + p;
-        const float gc = clip * G[e];
-        float un = U[e], vn = V[e];
-        momentum_update<kNest>(m, gc, un, vn);
+        const float gc = clip * a.G[e];
+        float un = a.U[e], vn = a.V[e];
+        momentum_update<kMode>(a.m, gc, un, vn);
         w.sidx[seg.off + wi * 32 + l] = mag_key(vn);
     }
 }
@@ -430,10 +475,12 @@ __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
 // staged count of the (row, wave) pieces before its own, plus the ballot
 // ranks of lower lanes, plus its own earlier flags.  The piece counts go
 // through a double-buffered LDS table with one barrier per chunk.
-template <bool kNest>
-__global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const float *__restrict__ G,
-                                                            float *__restrict__ U,
-                                                            float *__restrict__ V, float m, DgcWs w) {
+//
+// The DGC modes read G, U and V and write U and V; kSignif reads g and w and
+// writes nothing dense; kExplore reads only the core bitmap.
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, DgcWs w) {
+    constexpr bool kDgc = kMode == kVanilla || kMode == kNesterov;
     uint32_t c0, c1;
     chunk_range(P.ndchunk, &c0, &c1);
     __shared__ uint32_t hist[kHist1];
@@ -443,18 +490,26 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
     float g[kRows][4], u[kRows][4], v[kRows][4];
     ChunkWalker walk;
     ChunkInfo ci = walk.at(P, c0);
-    BufRsrc rg = chunk_buf(G + ci.lo, ci.cnt), ru = chunk_buf(U + ci.lo, ci.cnt), rv = chunk_buf(V + ci.lo, ci.cnt);
+    BufRsrc rg, ru, rv;
+    auto fetch = [&](const ChunkInfo &k) {
+        if (kMode == kExplore) return;
+        rg = chunk_buf(a.G + k.lo, k.cnt);
+        ru = chunk_buf(a.U + k.lo, k.cnt);
+        if (kDgc) rv = chunk_buf(a.V + k.lo, k.cnt);
 #pragma unroll
-    for (int j = 0; j < kRows; ++j) {
-        load4(rg, row_elem(j), g[j]);
-        load4(ru, row_elem(j), u[j]);
-        load4(rv, row_elem(j), v[j]);
-    }
+        for (int j = 0; j < kRows; ++j) {
+            load4(rg, row_elem(j), g[j]);
+            load4(ru, row_elem(j), u[j]);
+            if (kDgc) load4(rv, row_elem(j), v[j]);
+        }
+    };
+    fetch(ci);
     __syncthreads();
     const int lane = lane_id(), wave = wave_id();
     for (uint32_t c = c0; c < c1; ++c) {
-        const float clip = w.st[ci.s].clip;
+        const float clip = kDgc ? w.st[ci.s].clip : 1.0f;
         const uint32_t Lkey = w.st[ci.s].Lkey;
+        const uint32_t pos = static_cast<uint32_t>(ci.lo - ci.seg.off);  // chunk start in the segment
         uint32_t flags[kRows], before[kRows];
 #pragma unroll
         for (int j = 0; j < kRows; ++j) {
@@ -462,10 +517,15 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
             flags[j] = 0;
             before[j] = 0;
             uint32_t piece_total = 0;
+            if (kMode == kExplore) explore_values(a, ci.seg, ci.s, pos + e0, v[j]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float gc = clip * g[j][q];
-                momentum_update<kNest>(m, gc, u[j][q], v[j][q]);
+                if (kDgc) {
+                    const float gc = clip * g[j][q];
+                    momentum_update<kMode>(a.m, gc, u[j][q], v[j][q]);
+                } else if (kMode == kSignif) {
+                    v[j][q] = significance(u[j][q], g[j][q], a.m);
+                }
                 const float vn = v[j][q];
                 const bool in = e0 + q < ci.cnt;
                 const uint32_t d = mag_key(vn) >> (kDigit2Bits + kDigit3Bits);
@@ -477,8 +537,10 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
                 piece_total += static_cast<uint32_t>(__popcll(bm));
             }
             if (lane == 0) piece[(c - c0) & 1][j * kWaves + wave] = piece_total;
-            store4(ru, e0, u[j]);
-            store4(rv, e0, v[j]);
+            if (kDgc) {
+                store4(ru, e0, u[j]);
+                store4(rv, e0, v[j]);
+            }
         }
         __syncthreads();
         {
@@ -511,15 +573,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, const flo
         const bool more = c + 1 < c1;
         if (more) {
             ci = walk.at(P, c + 1);
-            rg = chunk_buf(G + ci.lo, ci.cnt);
-            ru = chunk_buf(U + ci.lo, ci.cnt);
-            rv = chunk_buf(V + ci.lo, ci.cnt);
-#pragma unroll
-            for (int j = 0; j < kRows; ++j) {
-                load4(rg, row_elem(j), g[j]);
-                load4(ru, row_elem(j), u[j]);
-                load4(rv, row_elem(j), v[j]);
-            }
+            fetch(ci);
         }
         if (!more || ci.s != s_done) {
             __syncthreads();
@@ -636,8 +690,8 @@ __global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w) {
 // lanes below + within lane); no LDS, no workgroup barrier.
 constexpr int kWaveRows = kChunk / (4 * kWave);
 
-__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const float *__restrict__ V,
-                                                           DgcWs w) {
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, DgcWs w) {
     const uint32_t c = blockIdx.x * kWaves + wave_id();
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
@@ -660,10 +714,30 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, const floa
         }
         return;
     }
-    const BufRsrc rv = chunk_buf(V + lo, cnt);
+    // the ranked values again: V (DGC, already updated), or recomputed
     float v[kWaveRows][4];
+    if (kMode == kVanilla || kMode == kNesterov) {
+        const BufRsrc rv = chunk_buf(a.V + lo, cnt);
 #pragma unroll
-    for (int r = 0; r < kWaveRows; ++r) load4(rv, r * (4 * kWave) + 4u * lane, v[r]);
+        for (int r = 0; r < kWaveRows; ++r) load4(rv, r * (4 * kWave) + 4u * lane, v[r]);
+    } else if (kMode == kSignif) {
+        const BufRsrc rg = chunk_buf(a.G + lo, cnt), rw = chunk_buf(a.U + lo, cnt);
+        float gg[kWaveRows][4];
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r) {
+            load4(rg, r * (4 * kWave) + 4u * lane, gg[r]);
+            load4(rw, r * (4 * kWave) + 4u * lane, v[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[r][q] = significance(v[r][q], gg[r][q], a.m);
+    } else {
+        const SegDev seg = P.seg[s];
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r)
+            explore_values(a, seg, s, (rec.w << kChunkLog2) + r * (4 * kWave) + 4u * lane, v[r]);
+    }
     uint32_t run = 0;  // wave-uniform count of entries staged so far
 #pragma unroll
     for (int r = 0; r < kWaveRows; ++r) {
@@ -803,16 +877,29 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
 // ------------------------------------------------------------------ emit
 // One wave per chunk: staged entries in index order, 64 at a time; ties at T
 // are taken in index order up to the chunk's quota; ranks from ballots.
-__global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__restrict__ U,
-                                                          float *__restrict__ V, DgcWs w,
+// DGC masks U and V at the sent entries.  kSignif also writes the chunk's
+// words of the core bitmap (every word, zeros included: the chunk's 4096
+// entries start on a word boundary of the segment's run), assembled in LDS.
+// kExplore sends delta at the chosen entries.
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcWs w,
                                                           uint32_t *__restrict__ out_idx,
                                                           float *__restrict__ out_val) {
+    constexpr bool kDgc = kMode == kVanilla || kMode == kNesterov;
     const uint32_t c = blockIdx.x * kWaves + wave_id();
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
     const uint32_t lo = rec.x, s = rec.z;
     const uint32_t n = staged_count(w, c, rec.y);
-    if (n == 0) return;
+    __shared__ uint32_t cmask[kWaves][kChunk / 32];
+    uint32_t *cm = cmask[wave_id()];
+    if (kMode == kSignif) {
+        cm[lane_id()] = 0u;
+        cm[lane_id() + kWave] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    } else if (n == 0) {
+        return;
+    }
     const uint32_t T = w.st[s].T;
     const uint32_t take = w.ctake[c];
     const uint32_t base = w.cout[c];
@@ -833,12 +920,21 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, float *__re
         const uint32_t p = base + sel_run + lane_rank(selm);
         if (sel && p < limit) {
             out_idx[p] = id;
-            out_val[p] = val;
-            V[id] = 0.0f;
-            U[id] = 0.0f;
+            out_val[p] = kMode == kExplore ? a.G[id] : val;
+            if (kDgc) {
+                a.V[id] = 0.0f;
+                a.U[id] = 0.0f;
+            }
+            if (kMode == kSignif) atomicOr(&cm[(id - lo) >> 5], 1u << ((id - lo) & 31u));
         }
         eq_run += static_cast<uint32_t>(__popcll(eqm));
         sel_run += static_cast<uint32_t>(__popcll(selm));
+    }
+    if (kMode == kSignif) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        const uint32_t wbase = P.seg[s].mbase + (rec.w << (kChunkLog2 - 5));
+        const uint32_t nw = (rec.y + 31) / 32;
+        for (uint32_t l = lane_id(); l < nw; l += kWave) a.mask[wbase + l] = cm[l];
     }
 }
 
@@ -862,6 +958,51 @@ uint64_t dgc_capacity(const gc_plan *plan, int select, uint32_t over) {
     for (const SegDev &d : plan->seg) cap += std::min<uint64_t>(d.len, uint64_t(over) * d.k);
     return cap;
 }
+
+// Host checks shared by the selection calls: message, workspace, alignment.
+gc_status check_select_io(const char *fn, const gc_plan *plan, const gc_sparse *out, uint64_t cap,
+                          const void *ws, size_t ws_bytes) {
+    const std::string f(fn);
+    if (!out || !out->idx || !out->val || !out->seg_off)
+        return set_error(GC_EINVAL, f + ": out, out->idx, out->val, out->seg_off must be non-null");
+    if (out->cap < cap) return set_error(GC_ECAPACITY, f + ": out->cap below the message size");
+    if (!ws || ws_bytes < dgc_workspace_bytes(plan))
+        return set_error(GC_ECAPACITY, f + ": workspace smaller than gc_plan_workspace_bytes(GC_OP_DGC)");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return set_error(GC_EINVAL, f + ": workspace must be 256-byte aligned");
+    return GC_OK;
+}
+
+// The selection pipeline for one key source: (clip), prep, sample + bound
+// (exact) or ssample + squant (sampled), update, radix select, ordered emit.
+template <int kMode>
+void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const Src &src, bool clip, float thr,
+                   bool sampled, uint32_t period, uint32_t over, gc_sparse *out, hipStream_t stream) {
+    const unsigned segs = static_cast<unsigned>(plan->nseg);
+    const unsigned wave_grid = grid_1d(plan->ndchunk, kWaves);
+    if (clip)
+        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, src.G, w));
+    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
+    if constexpr (kMode == kVanilla || kMode == kNesterov) {
+        if (sampled) {
+            GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, period, w));
+            GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, period, w));
+        }
+    }
+    if (!sampled) {
+        GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<kMode><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, src, w));
+        GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
+    }
+    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode><<<persistent_grid(dgc_update_kernel<kMode>, plan->ndchunk), kBlock, 0, stream>>>(P, src, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
+    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
+    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
+    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
+    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+}
 }  // namespace
 
 extern "C" uint64_t gc_dgc_message_cap(const gc_plan *plan, const gc_dgc_options *opt) {
@@ -877,8 +1018,6 @@ extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *
     if (!plan) return set_error(GC_EINVAL, "gc_dgc_step: plan is null");
     if (!opt) return set_error(GC_EINVAL, "gc_dgc_step: options are null");
     if (!G || !U || !V) return set_error(GC_EINVAL, "gc_dgc_step: G, U and V must be non-null");
-    if (!out || !out->idx || !out->val || !out->seg_off)
-        return set_error(GC_EINVAL, "gc_dgc_step: out, out->idx, out->val, out->seg_off must be non-null");
     const float momentum = opt->momentum, thr_G = opt->thr_G;
     const int num_nodes = opt->num_nodes;
     if (!(momentum >= 0.0f && momentum < 1.0f))
@@ -895,54 +1034,21 @@ extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *
         return set_error(GC_EINVAL, "gc_dgc_step: sample_period must be >= 1");
     if (sampled && opt->over < 1) return set_error(GC_EINVAL, "gc_dgc_step: over must be >= 1");
     if (opt->reserved != 0) return set_error(GC_EINVAL, "gc_dgc_step: reserved must be 0");
-    if (out->cap < dgc_capacity(plan, opt->select, opt->over))
-        return set_error(GC_ECAPACITY, "gc_dgc_step: out->cap below gc_dgc_message_cap");
-    size_t need = dgc_workspace_bytes(plan);
-    if (!ws || ws_bytes < need)
-        return set_error(GC_ECAPACITY, "gc_dgc_step: workspace smaller than gc_plan_workspace_bytes");
-    if (reinterpret_cast<uintptr_t>(ws) % 256)
-        return set_error(GC_EINVAL, "gc_dgc_step: workspace must be 256-byte aligned");
+    gc_status st = check_select_io("gc_dgc_step", plan, out, dgc_capacity(plan, opt->select, opt->over), ws, ws_bytes);
+    if (st != GC_OK) return st;
     PlanDev P;
-    gc_status st = plan_device(plan, &P);
+    st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     DgcWs w = dgc_layout(plan, ws, nullptr);
     const bool clip = thr_G > 0.0f;
-    const bool nest = opt->momentum_kind == GC_MOMENTUM_NESTEROV;
     const float thr = clip ? static_cast<float>(static_cast<double>(thr_G) /
                                                 std::sqrt(static_cast<double>(num_nodes)))
                            : 0.0f;
-    const uint32_t over = sampled ? opt->over : 0u;
-    const unsigned segs = static_cast<unsigned>(plan->nseg);
-    const unsigned wave_grid = grid_1d(plan->ndchunk, kWaves);
-    if (clip)
-        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, G, w));
-    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
-    if (sampled) {
-        if (nest)
-            GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<true><<<wave_grid, kBlock, 0, stream>>>(P, G, U, V, momentum, opt->sample_period, w));
-        else
-            GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<false><<<wave_grid, kBlock, 0, stream>>>(P, G, U, V, momentum, opt->sample_period, w));
-        GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, opt->sample_period, w));
-    } else {
-        if (nest)
-            GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<true><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
-        else
-            GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<false><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
-        GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
-    }
-    if (nest)
-        GC_LAUNCH("dgc_update", stream, dgc_update_kernel<true><<<persistent_grid(dgc_update_kernel<true>, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
+    Src src{G, U, V, momentum, 0u, 0u, 0u, 0u, nullptr};
+    if (opt->momentum_kind == GC_MOMENTUM_NESTEROV)
+        launch_select<kNesterov>(plan, P, w, src, clip, thr, sampled, opt->sample_period, opt->over, out, stream);
     else
-        GC_LAUNCH("dgc_update", stream, dgc_update_kernel<false><<<persistent_grid(dgc_update_kernel<false>, plan->ndchunk), kBlock, 0, stream>>>(P, G, U, V, momentum, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, over));
-    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<<<wave_grid, kBlock, 0, stream>>>(P, V, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, over));
-    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, over));
-    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
-    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<<<wave_grid, kBlock, 0, stream>>>(P, U, V, w, out->idx, out->val));
+        launch_select<kVanilla>(plan, P, w, src, clip, thr, sampled, opt->sample_period, opt->over, out, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_dgc_step launch");
     return GC_OK;
@@ -958,4 +1064,79 @@ extern "C" gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, 
     o.momentum_kind = GC_MOMENTUM_VANILLA;
     o.select = GC_SELECT_EXACT;
     return gc_dgc_step_ex(plan, G, U, V, &o, out, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ Slim-DP
+extern "C" uint64_t gc_slimdp_mask_words(const gc_plan *plan) { return plan ? plan->mask_words : 0; }
+
+extern "C" gc_status gc_slimdp_core(const gc_plan *plan, const float *w_param, const float *g, float c,
+                                    gc_sparse *core, uint32_t *core_mask, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    clear_error();
+    if (!plan) return set_error(GC_EINVAL, "gc_slimdp_core: plan is null");
+    if (!w_param || !g || !core_mask) return set_error(GC_EINVAL, "gc_slimdp_core: w, g and core_mask must be non-null");
+    if (!(c > 0.0f) || std::isinf(c)) return set_error(GC_EINVAL, "gc_slimdp_core: c must be positive and finite");
+    gc_status st = check_select_io("gc_slimdp_core", plan, core, plan->total_k, ws, ws_bytes);
+    if (st != GC_OK) return st;
+    PlanDev P;
+    st = plan_device(plan, &P);
+    if (st != GC_OK) return st;
+    DgcWs w = dgc_layout(plan, ws, nullptr);
+    Src src{g, const_cast<float *>(w_param), nullptr, c, 0u, 0u, 0u, 0u, core_mask};
+    launch_select<kSignif>(plan, P, w, src, false, 0.0f, false, 0u, 0u, core, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_slimdp_core launch");
+    return GC_OK;
+}
+
+extern "C" gc_status gc_slimdp_explore(const gc_plan *plan, const gc_plan *core_plan, const float *delta,
+                                       const uint32_t *core_mask, uint64_t seed, uint64_t step, gc_sparse *out,
+                                       void *ws, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    if (!plan || !core_plan) return set_error(GC_EINVAL, "gc_slimdp_explore: plans must be non-null");
+    if (!delta || !core_mask) return set_error(GC_EINVAL, "gc_slimdp_explore: delta and core_mask must be non-null");
+    if (core_plan->nseg != plan->nseg || core_plan->n_total != plan->n_total)
+        return set_error(GC_EINVAL, "gc_slimdp_explore: plans must describe the same segments");
+    for (int s = 0; s < plan->nseg; ++s) {
+        const SegDev &a = plan->seg[s], &b = core_plan->seg[s];
+        if (a.off != b.off || a.len != b.len)
+            return set_error(GC_EINVAL, "gc_slimdp_explore: plans must describe the same segments");
+        if (uint64_t(a.k) + b.k > a.len)
+            return set_error(GC_EINVAL, "gc_slimdp_explore: core plus explorer exceeds a segment");
+    }
+    gc_status st = check_select_io("gc_slimdp_explore", plan, out, plan->total_k, ws, ws_bytes);
+    if (st != GC_OK) return st;
+    PlanDev P;
+    st = plan_device(plan, &P);
+    if (st != GC_OK) return st;
+    DgcWs w = dgc_layout(plan, ws, nullptr);
+    Src src{delta, nullptr, nullptr, 0.0f, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32),
+            static_cast<uint32_t>(step), static_cast<uint32_t>(step >> 32), const_cast<uint32_t *>(core_mask)};
+    launch_select<kExplore>(plan, P, w, src, false, 0.0f, false, 0u, 0u, out, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_slimdp_explore launch");
+    return GC_OK;
+}
+
+namespace {
+__global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t *__restrict__ idx, uint32_t count,
+                                                        const float *__restrict__ src, float *__restrict__ dst) {
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < count) dst[i] = src[idx[i]];
+}
+}  // namespace
+
+extern "C" gc_status gc_slimdp_core_values(const gc_plan *core_plan, const gc_sparse *core, const float *delta,
+                                           float *values, hipStream_t stream) {
+    clear_error();
+    if (!core_plan || !core || !core->idx || !delta || !values)
+        return set_error(GC_EINVAL, "gc_slimdp_core_values: arguments must be non-null");
+    if (core->cap < core_plan->total_k)
+        return set_error(GC_ECAPACITY, "gc_slimdp_core_values: core message smaller than the plan's total k");
+    const uint64_t K = core_plan->total_k;
+    GC_LAUNCH("slimdp_values", stream, gather_kernel<<<grid_1d(K, kBlock), kBlock, 0, stream>>>(
+        core->idx, static_cast<uint32_t>(K), delta, values));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_slimdp_core_values launch");
+    return GC_OK;
 }

@@ -47,7 +47,7 @@ struct SegDev {
     uint32_t kbase;      // first message slot of the segment in a DGC message
     uint32_t bgroup0;    // first 4096-bin group of the segment (AdaComp scale sum)
     uint32_t nbgroup;    // 4096-bin groups in the segment
-    uint32_t pad;
+    uint32_t mbase;      // first word of the segment's run in a selection bitmap
 };
 
 constexpr int kBinGroupLog2 = 12;  // bins per group of the scale's pairwise tree
@@ -84,6 +84,7 @@ struct gc_plan {
     uint32_t ndchunk = 0;
     uint32_t nachunk = 0;
     uint32_t nbgroup = 0;
+    uint64_t mask_words = 0;  // sum over segments of ceil(length / 32)
     std::vector<gc::SegDev> seg;
     std::vector<uint32_t> dchunk_seg;
     std::vector<uint32_t> achunk_seg;
@@ -335,6 +336,32 @@ __device__ __forceinline__ uint32_t block_compact4(const bool (&flag)[kRows][4],
     uint32_t t = tot;
     __syncthreads();
     return t;
+}
+
+// Full 64-bit product of two u32 in one VALU op (v_mad_u64_u32 with a zero
+// addend); on gfx950 this is faster than the separate low and high multiplies.
+__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) {
+    uint64_t r, carry;
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "v"(b));
+    return r;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products, the
+// key advanced by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+    constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = mul_wide(kM0, c.x);
+        const uint64_t p1 = mul_wide(kM1, c.z);
+        c = make_uint4(uint32_t(p1 >> 32) ^ c.y ^ k0, uint32_t(p1), uint32_t(p0 >> 32) ^ c.w ^ k1,
+                       uint32_t(p0));
+        k0 += kW0;
+        k1 += kW1;
+    }
+    return c;
 }
 
 // Perfect binary tree sum of one double per thread, leaves in thread order.

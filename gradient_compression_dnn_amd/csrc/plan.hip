@@ -189,7 +189,7 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     p->seg_start.resize(nseg);
     p->dchunk_seg.reserve(ndchunk);
     p->achunk_seg.reserve(nachunk);
-    uint32_t bin0 = 0, kbase = 0;
+    uint32_t bin0 = 0, kbase = 0, mbase = 0;
     for (int s = 0; s < nseg; ++s) {
         const gc_segment &g = segs[s];
         SegDev d{};
@@ -205,6 +205,8 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         d.anchunk = (g.length + d.achunk_len - 1) / d.achunk_len;
         d.bin0 = bin0;
         d.kbase = kbase;
+        d.mbase = mbase;
+        mbase += (g.length + 31) / 32;
         d.bgroup0 = static_cast<uint32_t>(p->bgroup_seg.size());
         d.nbgroup = (d.nbins + kBinGroup - 1) / kBinGroup;
         for (uint32_t g2 = 0; g2 < d.nbgroup; ++g2) p->bgroup_seg.push_back(static_cast<uint32_t>(s));
@@ -231,6 +233,7 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     p->ndchunk = static_cast<uint32_t>(p->dchunk_seg.size());
     p->nachunk = static_cast<uint32_t>(p->achunk_seg.size());
     p->nbgroup = static_cast<uint32_t>(p->bgroup_seg.size());
+    p->mask_words = mbase;
     *out = p;
     return GC_OK;
 }

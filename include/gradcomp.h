@@ -14,8 +14,9 @@
  *             parameter alpha of the compression operator, and ECD-PSGD's
  *             extrapolation and estimate (Eqs. 3 and 4).
  *   [SlimDP]  "Slim-DP: A Light Communication Data Parallelism for DNN",
- *             experimental setup (Quant-DP baseline: random quantization with
- *             buckets of 512).
+ *             §3 (core and explorer selection, significance, key caching)
+ *             and the experimental setup (Quant-DP baseline: random
+ *             quantization with buckets of 512).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -397,6 +398,46 @@ gc_status gc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint6
 gc_status gc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, int bits,
                         uint32_t bucket, uint64_t t, float *x_tilde, hipStream_t stream);
 
+/* ---------------------------------------------------------------- Slim-DP */
+/*
+ * Slim-DP's communication set ([SlimDP] §3: a core of significant parameters
+ * chosen by the server, plus an explorer of random parameters from outside
+ * the core chosen by each worker at every communication).
+ *
+ * Core:  S_i = fl32(|w_i| + fl32(c * |g_i|)), c > 0 (the page combines the
+ *   magnitudes of the parameter and of its gradient as a weighted sum with a
+ *   positive coefficient; its equation is not printed).  Per segment, the k_s
+ *   entries first in the order (S descending, index ascending) form the core
+ *   (k_s from `plan`, e.g. ceil(beta * n_s)).
+ *     core      : ascending idx, val = S_i; exactly sum(k_s) entries.
+ *     core_mask : gc_slimdp_mask_words(plan) u32 words out: per segment a run
+ *                 of ceil(n_s/32) words, bit j%32 of word j/32 set iff entry j
+ *                 of the segment is in the core.
+ * Explorer: per segment, the m_s non-core entries first in the order (key
+ *   descending, index ascending), key_j = r >> 1 | 1 with r = word j%4 of
+ *   Philox4x32-10(counter (j/4, s, lo(step), hi(step)), key (lo(seed),
+ *   hi(seed))) for entry j of segment s; core entries never qualify.  A
+ *   uniformly random set of m_s non-core entries, resampled with `step`.
+ *     plan      : the same segments as core_plan with k_s = m_s, and
+ *                 m_s + (core k_s) <= n_s.
+ *     out       : ascending idx, val = delta_i; exactly sum(m_s) entries.
+ * Core values: the core's keys are cached on both sides ([SlimDP] key caching
+ *   filter), so a push sends only values: values[j] = delta[core->idx[j]]
+ *   for j < gc_plan_total_k(core_plan).
+ * Workspaces: gc_plan_workspace_bytes(plan, GC_OP_DGC).
+ * Errors: GC_EINVAL (null, c not positive and finite, plans that differ in
+ *         segments, core + explorer above a segment), GC_ECAPACITY.
+ */
+uint64_t  gc_slimdp_mask_words(const gc_plan *plan);
+gc_status gc_slimdp_core(const gc_plan *plan, const float *w, const float *g, float c,
+                         gc_sparse *core, uint32_t *core_mask, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+gc_status gc_slimdp_explore(const gc_plan *plan, const gc_plan *core_plan, const float *delta,
+                            const uint32_t *core_mask, uint64_t seed, uint64_t step,
+                            gc_sparse *out, void *ws, size_t ws_bytes, hipStream_t stream);
+gc_status gc_slimdp_core_values(const gc_plan *core_plan, const gc_sparse *core,
+                                const float *delta, float *values, hipStream_t stream);
+
 /* ----------------------------------------------------------- measurement */
 /*
  * Kernel timing for measurement tools (off by default).  While enabled, each
@@ -409,7 +450,8 @@ gc_status gc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, i
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
  *             ada_apply, ada_fold, ada_emit, ada_residual,
  *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,
- *             decode, dcd, dcd_decode, dcd_mix, ecd_compress, ecd_update.
+ *             decode, dcd, dcd_decode, dcd_mix, ecd_compress, ecd_update,
+ *             slimdp_values (Slim-DP selection reuses the dgc_* names).
  * gc_timing_take waits for the recorded events of one kernel and returns the
  * summed duration in milliseconds and the number of launches, then forgets
  * them.  Host-thread safe; not for use while a stream is being captured.

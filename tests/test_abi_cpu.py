@@ -110,3 +110,11 @@ def test_dgc_ex_host_checks_and_message_cap():
     assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=2)) == 10 + 2 + 6
     assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=3)) == 15 + 3 + 7
     assert lib.gc_dgc_message_cap(None, None) == 0
+
+
+def test_slimdp_mask_words():
+    t = W.make_table([40, 5, 64], [1, 1, 1], [1, 1, 1])
+    p = B.Plan(t)
+    assert B.gc_slimdp_mask_words(p) == 2 + 1 + 2
+    assert B.load().gc_slimdp_mask_words(None) == 0
+    assert B.load().gc_slimdp_core(None, None, None, 1.0, None, None, None, 0, None) == B.GC_EINVAL
