@@ -170,6 +170,26 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
     timed("ecd_compress_4bit", lambda t: B.gc_ecd_compress(X, XH[t % len(XH)], 2 + t, 4, bucket, 0x5EED,
                                                            scales, codes), 8 * n + code_bytes)
     timed("ecd_update_4bit", lambda t: B.gc_ecd_update(scales, codes, XT, 2 + t, 4, bucket), 8 * n + code_bytes)
+
+    # Slim-DP at the page's VGG-16 setting (alpha 0.2, beta 0.1): a 10% core
+    # by significance and a 10% explorer, per tensor
+    import numpy as np
+    tc = np.array(plan.table, np.int64)
+    tc[:, 3] = np.ceil(tc[:, 1] * 0.1).astype(np.int64)
+    core_plan = B.Plan(tc, n)
+    exp_plan = B.Plan(tc, n)
+    mask = torch.zeros(B.gc_slimdp_mask_words(core_plan), dtype=torch.int32, device=dev)
+    core = B.Sparse.empty(core_plan, core_plan.total_k, dev)
+    expl = B.Sparse.empty(exp_plan, exp_plan.total_k, dev)
+    cvals = torch.zeros(core_plan.total_k, dtype=torch.float32, device=dev)
+    kc = core_plan.total_k
+    timed("slimdp_core_beta0.1", lambda t: B.gc_slimdp_core(core_plan, X, G[t % len(G)], 50.0, core, mask,
+                                                            ws[B.GC_OP_DGC]),
+          8 * n + n // 8 + 8 * kc)  # read w, g; write the bitmap and the core message
+    timed("slimdp_explore_0.1", lambda t: B.gc_slimdp_explore(exp_plan, core_plan, G[t % len(G)], mask, 0x5EED, t,
+                                                              expl, ws[B.GC_OP_DGC]),
+          n // 8 + 12 * exp_plan.total_k)  # read the bitmap and delta at the entries; write the message
+    timed("slimdp_core_values", lambda t: B.gc_slimdp_core_values(core_plan, core, G[t % len(G)], cvals), 12 * kc)
     return out
 
 

@@ -200,8 +200,9 @@ struct ChunkWalker {
     }
 };
 
-// Persistent dense kernels: workgroup b walks chunks [first, last), a
-// contiguous range, so consecutive chunks mostly share a segment.
+// Dense kernels: workgroup b walks chunks [first, last), a contiguous range
+// (one chunk when the grid has a workgroup per chunk), so consecutive chunks
+// mostly share a segment.
 __device__ __forceinline__ void chunk_range(uint32_t nchunk, uint32_t *first, uint32_t *last) {
     const uint32_t per = (nchunk + gridDim.x - 1) / gridDim.x;
     *first = blockIdx.x * per;
@@ -992,7 +993,9 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
         GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<kMode><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, src, w));
         GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
     }
-    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode><<<persistent_grid(dgc_update_kernel<kMode>, plan->ndchunk), kBlock, 0, stream>>>(P, src, w));
+    // one workgroup per chunk: with non-temporal streaming this measured 15%
+    // faster than an occupancy-sized persistent grid walking chunk ranges
+    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
     GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
