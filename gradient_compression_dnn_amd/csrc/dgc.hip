@@ -62,6 +62,7 @@ struct SegState {
     uint32_t all;   // sampled selection: every staged entry is sent
     uint32_t sent;  // entries the segment sends
     uint32_t base;  // first message slot of the segment
+    uint32_t qrank, qprefix;  // sampled selection: quantile search state
 };
 
 // What the selection kernels rank (the key is the magnitude bits of a value):
@@ -127,6 +128,7 @@ struct DgcWs {
     uint32_t *sidx;
     float *sval;
     uint32_t *skey;  // [ndchunk][kSamples] key of the sampled V'
+    uint32_t *qhist; // [nseg][kHist1] sample-quantile histogram (sampled selection)
 };
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
@@ -145,6 +147,7 @@ DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.sidx = c.take<uint32_t>(p->n_total);
     w.sval = c.take<float>(p->n_total);
     w.skey = c.take<uint32_t>(size_t(p->ndchunk) * kSamples);
+    w.qhist = c.take<uint32_t>(size_t(p->nseg) * kHist1);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -266,9 +269,11 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
 
 // ------------------------------------------------------------------ prep
 __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, int use_clip,
-                                                          float thr) {
+                                                          float thr, int zero_q) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
+    if (zero_q)
+        for (int i = threadIdx.x; i < kHist1; i += kBlock) w.qhist[size_t(s) * kHist1 + i] = 0u;
     uint4 *h4 = reinterpret_cast<uint4 *>(w.hist1 + size_t(s) * kHistRep * kHist1);
     for (int i = threadIdx.x; i < int(kHistRep * kHist1 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
     h4 = reinterpret_cast<uint4 *>(w.hist2 + size_t(s) * kHistRep * kHist2);
@@ -361,16 +366,27 @@ __global__ __launch_bounds__(kBlock) void dgc_ssample_kernel(PlanDev P, Src a, u
 // keys, r = ceil(S k / n) (u64 arithmetic), by radix select over the 11, 11
 // and 9-bit digits with an LDS histogram per digit (keys re-read from
 // global memory each level; they are L2-resident after the first).
+// Sampled entries S of a segment of `len` entries: every window but the last
+// holds a whole block.
+__host__ __device__ __forceinline__ uint32_t sample_count(uint32_t len, uint32_t period) {
+    const uint64_t win = 32ull * period;
+    const uint64_t nwin = (len + win - 1) / win;
+    const uint64_t wl = nwin - 1;
+    const uint64_t last_start = wl * win + 32u * ((static_cast<uint32_t>(wl) * 2654435769u) % period);
+    const uint64_t last_ns = last_start < len ? (len - last_start < 32 ? len - last_start : 32) : 0;
+    return static_cast<uint32_t>(wl * 32 + last_ns);
+}
+
+// r = ceil(S k / n), the estimate's rank among the samples.
+__device__ __forceinline__ uint32_t sample_rank(uint32_t S, const SegDev &seg) {
+    return static_cast<uint32_t>((uint64_t(S) * seg.k + seg.len - 1) / seg.len);
+}
+
 __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t period, DgcWs w) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
-    const uint64_t win = 32ull * period;
-    const uint64_t nwin = (seg.len + win - 1) / win;
-    const uint64_t wl = nwin - 1;
-    const uint64_t last_start = wl * win + sample_block_offset(static_cast<uint32_t>(wl), period);
-    const uint64_t last_ns = last_start < seg.len ? min<uint64_t>(32, seg.len - last_start) : 0;
-    const uint32_t S = static_cast<uint32_t>(wl * 32 + last_ns);
-    uint32_t rank = static_cast<uint32_t>((uint64_t(S) * seg.k + seg.len - 1) / seg.len);
+    const uint32_t S = sample_count(seg.len, period);
+    uint32_t rank = sample_rank(S, seg);
     const uint32_t *keys = w.sidx + seg.off;
     __shared__ uint32_t h[kHist1];
     uint32_t prefix = 0;
@@ -401,6 +417,67 @@ __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t 
         __syncthreads();
     }
     if (threadIdx.x == 0) w.st[s].Lkey = prefix;
+}
+
+// The same radix select spread over kQBlocks workgroups per segment, for
+// samples too many for one workgroup: per digit, a histogram kernel (each
+// workgroup an LDS histogram of its share of the keys that match the prefix,
+// flushed into the segment's qhist) and a find kernel (one workgroup per
+// segment: the digit, the rank left, qhist cleared for the next digit).
+constexpr uint32_t kQBlocks = 32;
+constexpr uint32_t kQuantOneBlock = 32768;  // most samples one workgroup handles alone
+
+template <int kLevel>
+__global__ __launch_bounds__(kBlock) void dgc_qhist_kernel(PlanDev P, uint32_t period, DgcWs w) {
+    const uint32_t s = blockIdx.x / kQBlocks, b = blockIdx.x % kQBlocks;
+    const SegDev seg = P.seg[s];
+    const uint32_t S = sample_count(seg.len, period);
+    const uint32_t per = (S + kQBlocks - 1) / kQBlocks;
+    const uint32_t j0 = b * per, j1 = min(S, j0 + per);
+    if (j0 >= j1) return;
+    constexpr int nb = kLevel == 2 ? kHist3 : kHist1;
+    constexpr int shift = kLevel == 0 ? kDigit2Bits + kDigit3Bits : kLevel == 1 ? kDigit3Bits : 0;
+    constexpr int pshift = kLevel == 1 ? kDigit2Bits + kDigit3Bits : kDigit3Bits;
+    const uint32_t prefix = kLevel > 0 ? w.st[s].qprefix : 0u;
+    __shared__ uint32_t h[nb];
+    for (int i = threadIdx.x; i < nb; i += kBlock) h[i] = 0u;
+    __syncthreads();
+    const uint32_t *keys = w.sidx + seg.off;
+    constexpr uint32_t kB = 8;
+    for (uint32_t i0 = j0; i0 < j1; i0 += kB * kBlock) {
+        uint32_t key[kB];
+#pragma unroll
+        for (uint32_t u = 0; u < kB; ++u) key[u] = keys[min(i0 + u * kBlock + threadIdx.x, j1 - 1)];
+#pragma unroll
+        for (uint32_t u = 0; u < kB; ++u) {
+            if (i0 + u * kBlock + threadIdx.x >= j1) continue;
+            if (kLevel > 0 && (key[u] >> pshift) != prefix) continue;
+            atomicAdd(&h[(key[u] >> shift) & uint32_t(nb - 1)], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t *g = w.qhist + size_t(s) * kHist1;
+    for (int i = threadIdx.x; i < nb; i += kBlock)
+        if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+template <int kLevel>
+__global__ __launch_bounds__(kBlock) void dgc_qfind_kernel(PlanDev P, uint32_t period, DgcWs w) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    uint32_t *g = w.qhist + size_t(s) * kHist1;
+    const uint32_t rank = kLevel == 0 ? sample_rank(sample_count(seg.len, period), seg) : w.st[s].qrank;
+    const uint32_t prefix = kLevel > 0 ? w.st[s].qprefix : 0u;
+    uint32_t above, d;
+    if (kLevel == 2) d = block_find_bucket<kHist3>(rank, [&](int b) { return g[b]; }, &above);
+    else d = block_find_bucket<kHist1>(rank, [&](int b) { return g[b]; }, &above);
+    for (int i = threadIdx.x; i < kHist1; i += kBlock) g[i] = 0u;  // clean for the next digit or call
+    if (threadIdx.x == 0) {
+        const uint32_t np = kLevel == 0 ? d : kLevel == 1 ? ((prefix << kDigit2Bits) | d) : ((prefix << kDigit3Bits) | d);
+        w.st[s].qrank = rank - above;
+        w.st[s].qprefix = np;
+        if (kLevel == 2) w.st[s].Lkey = np;
+    }
 }
 
 // ----------------------------------------------------------------- bound
@@ -982,11 +1059,26 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
     const unsigned wave_grid = grid_1d(plan->ndchunk, kWaves);
     if (clip)
         GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, src.G, w));
-    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr));
+    // sampled selection: one workgroup per segment finds the sample quantile
+    // unless a segment has more samples than kQuantOneBlock
+    bool multi_q = false;
+    if (sampled)
+        for (const SegDev &d : plan->seg) multi_q = multi_q || sample_count(d.len, period) > kQuantOneBlock;
+    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr, multi_q ? 1 : 0));
     if constexpr (kMode == kVanilla || kMode == kNesterov) {
         if (sampled) {
             GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, period, w));
-            GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, period, w));
+            if (multi_q) {
+                const unsigned qgrid = segs * kQBlocks;
+                GC_LAUNCH("dgc_squant", stream, dgc_qhist_kernel<0><<<qgrid, kBlock, 0, stream>>>(P, period, w));
+                GC_LAUNCH("dgc_squant", stream, dgc_qfind_kernel<0><<<segs, kBlock, 0, stream>>>(P, period, w));
+                GC_LAUNCH("dgc_squant", stream, dgc_qhist_kernel<1><<<qgrid, kBlock, 0, stream>>>(P, period, w));
+                GC_LAUNCH("dgc_squant", stream, dgc_qfind_kernel<1><<<segs, kBlock, 0, stream>>>(P, period, w));
+                GC_LAUNCH("dgc_squant", stream, dgc_qhist_kernel<2><<<qgrid, kBlock, 0, stream>>>(P, period, w));
+                GC_LAUNCH("dgc_squant", stream, dgc_qfind_kernel<2><<<segs, kBlock, 0, stream>>>(P, period, w));
+            } else {
+                GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, period, w));
+            }
         }
     }
     if (!sampled) {
