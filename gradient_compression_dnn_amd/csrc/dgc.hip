@@ -769,7 +769,7 @@ __global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w) {
 constexpr int kWaveRows = kChunk / (4 * kWave);
 
 template <int kMode>
-__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, DgcWs w) {
+__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, DgcWs w, int redo_only) {
     const uint32_t c = blockIdx.x * kWaves + wave_id();
     if (c >= P.ndchunk) return;
     const ChunkRec rec = P.dchunk_rec[c];
@@ -780,6 +780,7 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, Dgc
     uint32_t *h2 = w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2;
     const int lane = lane_id();
     if (!redo) {
+        if (redo_only) return;
         const uint32_t n = min(w.ccount[c], cnt);
         for (uint32_t i0 = 0; i0 < n; i0 += 4 * kWave) {
             uint32_t key[4];
@@ -847,6 +848,54 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, Dgc
         run += row_total;
     }
     if (lane == 0) w.ccount[c] = run;
+}
+
+// Digit-2 histogram of the boundary bucket for dense selections (Slim-DP's
+// core at 10% density puts millions of staged entries in the boundary
+// digit-1 bucket, where one global atomic per entry dominated): a workgroup
+// takes kStageSpan consecutive chunks, counts in LDS and flushes once per
+// segment it touched.  Re-staged segments are left to dgc_stage_kernel.
+constexpr uint32_t kStageSpan = 32;
+
+__global__ __launch_bounds__(kBlock) void dgc_stagew_kernel(PlanDev P, DgcWs w) {
+    const uint32_t c0 = blockIdx.x * kStageSpan, c1 = min(P.ndchunk, c0 + kStageSpan);
+    __shared__ uint32_t h[kHist2];
+    for (int i = threadIdx.x; i < kHist2; i += kBlock) h[i] = 0u;
+    __syncthreads();
+    uint32_t cur = P.dchunk_rec[c0].z;
+    auto flush = [&](uint32_t seg) {
+        __syncthreads();
+        uint32_t *h2 = w.hist2 + (size_t(seg) * kHistRep + blockIdx.x % kHistRep) * kHist2;
+        for (int i = threadIdx.x; i < kHist2; i += kBlock) {
+            const uint32_t v = h[i];
+            if (v) {
+                atomicAdd(&h2[i], v);
+                h[i] = 0u;
+            }
+        }
+        __syncthreads();
+    };
+    for (uint32_t c = c0; c < c1; ++c) {
+        const ChunkRec rec = P.dchunk_rec[c];
+        if (rec.z != cur) {
+            flush(cur);
+            cur = rec.z;
+        }
+        const SegState &st = w.st[rec.z];
+        if (st.all || st.redo) continue;
+        const uint32_t d1 = st.d1;
+        const uint32_t n = min(w.ccount[c], rec.y);
+        for (uint32_t i0 = 0; i0 < n; i0 += 4 * kBlock) {
+            uint32_t key[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) key[q] = mag_key(w.sval[rec.x + min(i0 + q * kBlock + threadIdx.x, n - 1)]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + q * kBlock + threadIdx.x < n && (key[q] >> (kDigit2Bits + kDigit3Bits)) == d1)
+                    atomicAdd(&h[(key[q] >> kDigit3Bits) & (kHist2 - 1)], 1u);
+        }
+    }
+    flush(cur);
 }
 
 // ------------------------------------------------- refine, count (waves)
@@ -969,7 +1018,7 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
     const ChunkRec rec = P.dchunk_rec[c];
     const uint32_t lo = rec.x, s = rec.z;
     const uint32_t n = staged_count(w, c, rec.y);
-    __shared__ uint32_t cmask[kWaves][kChunk / 32];
+    __shared__ uint32_t cmask[kWaves][kMode == kSignif ? kChunk / 32 : 1];
     uint32_t *cm = cmask[wave_id()];
     if (kMode == kSignif) {
         cm[lane_id()] = 0u;
@@ -1085,11 +1134,17 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
         GC_LAUNCH("dgc_sample", stream, dgc_sample_kernel<kMode><<<grid_1d(plan->ndchunk, 2 * kWaves), kBlock, 0, stream>>>(P, src, w));
         GC_LAUNCH("dgc_bound", stream, dgc_bound_kernel<<<segs, kBlock, 0, stream>>>(P, w));
     }
-    // one workgroup per chunk: with non-temporal streaming this measured 15%
+    // One workgroup per chunk: with non-temporal streaming this measured 15%
     // faster than an occupancy-sized persistent grid walking chunk ranges
+    // (the explorer, bound by its Philox keys, runs the same in either shape).
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
-    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w));
+    if (kMode == kSignif) {
+        GC_LAUNCH("dgc_stage", stream, dgc_stagew_kernel<<<grid_1d(plan->ndchunk, kStageSpan), kBlock, 0, stream>>>(P, w));
+        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, 1));
+    } else {
+        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, 0));
+    }
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
     GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
