@@ -193,6 +193,98 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
     return out
 
 
+def measure_configs(B, W, dev, log, reps: int = 10):
+    """The other workloads of the configuration list, each timed alone after
+    the step timing (not part of `value`): ms per step and dense fp32 GB/s.
+      fc1m        one AdaComp step (L_T = 50) and one DGC step (top 0.1%, no clip)
+      resnet50    DGC steps (momentum 0.9, clip 1.0, top 0.1% per tensor)
+      lstm_lm     AdaComp steps (L_T 500 / 50, residual carried)
+      resnet50x8  8 learners' DGC steps (N = 8) and the 8-message average"""
+    import torch
+
+    out = {}
+
+    def timed(name, fn, dense_bytes, alg_bytes):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(1 + r)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "dense_GBs": round(dense_bytes / (ms / 1000.0) / 1e9, 1),
+                     "alg_hbm_frac": round(alg_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"config {name}: {ms:.3f} ms")
+
+    def dev_grads(w, count=2):
+        return [torch.from_numpy(W.gradient(w, t)).to(dev) for t in range(count)]
+
+    # fc1m
+    w = W.make_config("fc1m")
+    n = w.n_total
+    plan = B.Plan(w.table, n)
+    g = dev_grads(w)
+    U, V, R = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
+    st = plan.adacomp_state(dev)
+    dm = B.Sparse.empty(plan, plan.total_k, dev)
+    am = B.Sparse.empty(plan, n, dev)
+    wsd, wsa = plan.workspace(B.GC_OP_DGC, dev), plan.workspace(B.GC_OP_ADACOMP, dev)
+    timed("fc1m_adacomp", lambda t: B.gc_adacomp_compress(plan, g[t % 2], R, 2.0, am, wsa, state=st), 4 * n, 12 * n)
+    timed("fc1m_dgc", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 0.0, 1, dm, wsd), 4 * n, 20 * n)
+    # the same two calls captured once in a HIP graph and replayed (the plan
+    # is already on the device, and the hot calls allocate nothing)
+    Gslot = g[0].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.gc_adacomp_compress(plan, Gslot, R, 2.0, am, wsa, state=st)
+        B.gc_dgc_step(plan, Gslot, U, V, 0.9, 0.0, 1, dm, wsd)
+    torch.cuda.synchronize()
+    timed("fc1m_adacomp_and_dgc_graph", lambda t: graph.replay(), 8 * n, 32 * n)
+    # resnet50
+    w = W.make_config("resnet50")
+    n = w.n_total
+    plan = B.Plan(w.table, n)
+    g = dev_grads(w)
+    U, V = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2))
+    dm = B.Sparse.empty(plan, plan.total_k, dev)
+    wsd = plan.workspace(B.GC_OP_DGC, dev)
+    timed("resnet50_dgc", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 1.0, 1, dm, wsd), 4 * n, 20 * n)
+    del g, U, V, wsd
+    # lstm_lm
+    w = W.make_config("lstm_lm")
+    n = w.n_total
+    plan = B.Plan(w.table, n)
+    g = dev_grads(w)
+    R = torch.zeros(n, dtype=torch.float32, device=dev)
+    st = plan.adacomp_state(dev)
+    am = B.Sparse.empty(plan, n, dev)
+    wsa = plan.workspace(B.GC_OP_ADACOMP, dev)
+    timed("lstm_lm_adacomp", lambda t: B.gc_adacomp_compress(plan, g[t % 2], R, 2.0, am, wsa, state=st), 4 * n, 12 * n)
+    del g, R, am, wsa
+    # resnet50x8: one plan per learner over its own 25.6M-element buffer
+    w = W.make_config("resnet50x8")
+    per = w.params["learner_len"]
+    single = W.make_config("resnet50")
+    plan = B.Plan(single.table, per)
+    gall = torch.from_numpy(W.gradient(w, 0)).to(dev)
+    G8 = [gall[j * per:(j + 1) * per] for j in range(8)]
+    U8 = torch.zeros(8 * per, dtype=torch.float32, device=dev)
+    V8 = torch.zeros_like(U8)
+    msgs = [B.Sparse.empty(plan, plan.total_k, dev) for _ in range(8)]
+    wsd, wsdec = plan.workspace(B.GC_OP_DGC, dev), plan.workspace(B.GC_OP_DECODE, dev)
+    avg = torch.zeros(per, dtype=torch.float32, device=dev)
+
+    def learners(t):
+        for j in range(8):
+            B.gc_dgc_step(plan, G8[j], U8[j * per:(j + 1) * per], V8[j * per:(j + 1) * per], 0.9, 1.0, 8, msgs[j], wsd)
+        B.gc_decompress_accumulate(plan, msgs, avg, B.GC_AVG, False, wsdec)
+
+    timed("resnet50x8_dgc_and_average", learners, 8 * 4 * per, 8 * 20 * per + 4 * per)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +450,7 @@ def main(argv=None):
     if not args.no_variants:
         log("variants")
         result["variants"] = measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log)
+        result["configs"] = measure_configs(B, W, dev, log)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, grads, x0)
