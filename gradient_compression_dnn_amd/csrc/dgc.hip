@@ -1,8 +1,12 @@
-// DGC step on gfx950: local clipping, momentum correction (vanilla or
-// Nesterov), top-k by radix select on |V| bit patterns (exact, or from a
-// sampled threshold with a hierarchical exact fallback), ordered compaction,
-// momentum factor masking.  "Deep Gradient Compression" (Lin et al.),
-// §3.1–§3.3, §5, §6, App. B, C, D.
+// Top-k selection on gfx950 for DGC and Slim-DP.
+//   DGC ("Deep Gradient Compression", Lin et al., §3.1-§3.3, §5, §6, App. B,
+//   C, D): local clipping, momentum correction (vanilla or Nesterov), top-k by
+//   radix select on |V| bit patterns (exact, or from a sampled threshold with
+//   a hierarchical exact fallback), ordered compaction, momentum factor
+//   masking.
+//   Slim-DP ("Slim-DP", §3): the core (top-k by significance) and the
+//   explorer (top-k of random keys outside the core) through the same
+//   kernels, with the key source chosen by a template mode.
 //
 // Launch sequence.  Chunk kernels run one workgroup (or one wave) per
 // 4096-element chunk of a segment; segment kernels one workgroup per segment.
@@ -12,25 +16,29 @@
 //   norm    (chunk, clip only) pairwise fp64 sum of G^2 over the chunk
 //   prep    (segment) clear the segment's histograms; finish the pairwise
 //           tree over the chunk sums and set the clip factor
-//   sample  (chunk) V' = V + (m U + c G) for 32 contiguous elements of the
-//           chunk; histogram of their digit 1 (key >> 20)
+//   sample  (chunk) the ranked value of 32 contiguous elements in up to 512
+//           chunks per segment, computed as the update will compute it
 //   bound   (segment) from the sample, a key Lkey that the k-th largest key
-//           almost surely reaches (the DGC paper estimates its threshold
-//           from a sample of the gradient, §3.1 / App. D)
-//   update  (chunk) U <- fl(fl(m U) + fl(c G)); V <- fl(V + U); LDS histogram
-//           of digit 1, flushed with global atomics; entries with key at or
-//           above Lkey staged in index order at the chunk's own offset
+//           almost surely reaches (the page estimates its threshold from a
+//           sample, §5)
+//   update  (chunk) U <- fl(fl(m U) + fl(c G)); V <- fl(V + U) (or the mode's
+//           value); LDS histogram of digit 1, flushed with global atomics;
+//           entries with key at or above Lkey staged in index order at the
+//           chunk's own offset
 //   select1 (segment) digit 1 of the k-th largest key, d1; if fewer than k
 //           entries were staged, the k-th largest key is below Lkey, the
 //           staging missed candidates and the segment is re-staged
 //   stage   (chunk) histogram digit 2 of the staged entries in the boundary
 //           bucket; for a re-staged segment, re-read V and stage digit 1 >= d1
+//           (Slim-DP's core uses stagew, 32 chunks per workgroup, for the
+//           histogram)
 //   select2 (segment) digit 2
 //   refine  (chunk) histogram digit 3 of staged entries in the boundary bucket
 //   select3 (segment) threshold key T, count above it, ties to send
 //   count   (chunk) staged keys > T and == T
 //   scan    (segment) message slot and tie quota of every chunk
-//   emit    (chunk) write (idx, V) in index order, then zero U and V there
+//   emit    (chunk) write (idx, value) in index order; DGC zeroes U and V
+//           there, Slim-DP's core writes its bitmap words
 // Staged entries below d1 are never counted or sent (their keys are below T),
 // so the looser staging changes no result.
 //
@@ -38,7 +46,9 @@
 //   ssample (chunk) V' at the sample positions (one 32-entry block per window
 //           of 32 P entries), keys stored at the segment's staging offset
 //   squant  (segment) the estimate: the r-th largest sample key,
-//           r = ceil(S k / n), by a three-digit LDS radix select
+//           r = ceil(S k / n), by a three-digit LDS radix select (or, for
+//           segments with more than 32,768 samples, qhist/qfind pairs with 32
+//           workgroups per segment)
 // and the update stages exactly the keys at or above the estimate.  select1
 // then sends all of them when they fit the budget min(n, over k) ("all"
 // segments skip stage, refine and the later selects), and otherwise takes
