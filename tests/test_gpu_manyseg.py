@@ -1,0 +1,98 @@
+"""GPU parity on plans with hundreds of segments (more than one 256-wide
+round in every per-segment scan: segment bases of sampled DGC, AdaComp
+offsets, pack tiles and layout, decode's segment walk), for every call that
+takes a plan, against the oracle bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, same_bits, say, sparse_from_host, to_dev, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def layout():
+    rng = np.random.default_rng(900)
+    t = W.random_table(rng, 700, max_len=3000, gaps=True)
+    return t, W.table_extent(t), rng
+
+
+def test_dgc_exact_sampled_nesterov(layout):
+    t, n, rng = layout
+    hp = HipPath(t, n)
+    U = W.random_values(rng, n, "laplace")
+    V = W.random_values(rng, n, "laplace")
+    for sampled, nest, period in ((False, False, 0), (True, True, 7), (True, False, 1)):
+        G = W.random_values(rng, n, "laplace")
+        tag = f"manyseg dgc sampled={sampled} nesterov={nest} P={period}"
+        say(tag)
+        Uo, Vo, idx, val, off, _ = oracle.dgc_ex(t, G, U, V, 0.9, 1e-3, 3, nesterov=nest, sampled=sampled,
+                                                 sample_period=max(period, 1), over=2)
+        opt = B.dgc_options(0.9, 1e-3, 3, nesterov=nest, sampled=sampled, sample_period=max(period, 1), over=2)
+        Ug, Vg, gidx, gval, goff = hp.dgc_ex(G, U, V, opt)
+        assert np.array_equal(goff, off) and np.array_equal(gidx, idx), tag
+        assert same_bits(gval, val) and same_bits(Ug, Uo) and same_bits(Vg, Vo), tag
+        U, V = Uo, Vo
+
+
+def test_adacomp_pack_decode(layout):
+    t, n, rng = layout
+    hp = HipPath(t, n)
+    R = W.random_values(rng, n, "normal")
+    msgs_h, msgs_d = [], []
+    for step in range(3):
+        dW = W.random_values(rng, n, "laplace")
+        say(f"manyseg adacomp step {step}")
+        Ro, idx, val, off, scale, _ = oracle.adacomp(t, dW, R, 2.0)
+        Rd, am = hp.adacomp(dW, R, 2.0, tensors=True)
+        gidx, gval, goff, gscale = am.host()
+        assert np.array_equal(goff, off) and np.array_equal(gidx, idx)
+        assert same_bits(gval, val) and same_bits(gscale[:len(t)], scale)
+        assert same_bits(Rd.cpu().numpy(), Ro), ulp_report(Rd.cpu().numpy(), Ro)
+        say(f"manyseg adacomp pack step {step}")
+        assert hp.pack(B.GC_KIND_ADACOMP, am) == oracle.pack(2, t, idx, val, off, scale)
+        R = Ro
+        msgs_h.append((idx, val))
+        msgs_d.append(am)
+    say("manyseg decode")
+    want = oracle.decode(t, n, msgs_h, mode=1)
+    got = hp.decode(msgs_d, B.GC_AVG)
+    assert same_bits(got, want), ulp_report(got, want)
+    # a DGC message through the packer on the same plan
+    G = W.random_values(rng, n, "normal")
+    z = np.zeros(n, np.float32)
+    _, _, didx, dval, doff, _ = oracle.dgc(t, G, z, z, 0.9)
+    _, _, dm = hp.dgc(G, z.copy(), z.copy(), 0.9, tensors=True)
+    say("manyseg dgc pack")
+    assert hp.pack(B.GC_KIND_DGC, dm) == oracle.pack(1, t, didx, dval, doff, np.zeros(len(t), np.float32))
+
+
+def test_slimdp(layout):
+    t, n, rng = layout
+    t = t[t[:, 1] >= 2]
+    n = W.table_extent(t)
+    tc = t.copy()
+    tc[:, 3] = np.maximum(1, t[:, 1] // 10)
+    te = tc.copy()
+    cp, ep = B.Plan(tc), B.Plan(te, W.table_extent(tc))
+    ws = cp.workspace(B.GC_OP_DGC, "cuda")
+    mask = torch.zeros(B.gc_slimdp_mask_words(cp), dtype=torch.int32, device="cuda")
+    w_, g_, d_ = (W.random_values(rng, n) for _ in range(3))
+    say("manyseg slimdp")
+    cidx, cval, coff, cmask = oracle.slimdp_core(tc, w_, g_, 2.0)
+    core = B.Sparse.empty(cp, cp.total_k, "cuda")
+    B.gc_slimdp_core(cp, to_dev(w_), to_dev(g_), 2.0, core, mask, ws)
+    torch.cuda.synchronize()
+    gi, gv, go, _ = core.host()
+    assert np.array_equal(gi, cidx) and same_bits(gv, cval) and np.array_equal(go, coff)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), cmask)
+    eidx, evals, eoff = oracle.slimdp_explore(te, d_, cmask, 5, 9)
+    out = B.Sparse.empty(ep, ep.total_k, "cuda")
+    B.gc_slimdp_explore(ep, cp, to_dev(d_), mask, 5, 9, out, ws)
+    torch.cuda.synchronize()
+    xi, xv, xo, _ = out.host()
+    assert np.array_equal(xi, eidx) and same_bits(xv, evals) and np.array_equal(xo, eoff)
