@@ -1190,8 +1190,8 @@ extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *
     if (opt->select != GC_SELECT_EXACT && opt->select != GC_SELECT_SAMPLED)
         return set_error(GC_EINVAL, "gc_dgc_step: select must be GC_SELECT_EXACT or GC_SELECT_SAMPLED");
     const bool sampled = opt->select == GC_SELECT_SAMPLED;
-    if (sampled && opt->sample_period < 1)
-        return set_error(GC_EINVAL, "gc_dgc_step: sample_period must be >= 1");
+    if (sampled && (opt->sample_period < 1 || opt->sample_period > GC_MAX_SAMPLE_PERIOD))
+        return set_error(GC_EINVAL, "gc_dgc_step: sample_period must be in [1, GC_MAX_SAMPLE_PERIOD]");
     if (sampled && opt->over < 1) return set_error(GC_EINVAL, "gc_dgc_step: over must be >= 1");
     if (opt->reserved != 0) return set_error(GC_EINVAL, "gc_dgc_step: reserved must be 0");
     gc_status st = check_select_io("gc_dgc_step", plan, out, dgc_capacity(plan, opt->select, opt->over), ws, ws_bytes);
@@ -1279,10 +1279,12 @@ extern "C" gc_status gc_slimdp_explore(const gc_plan *plan, const gc_plan *core_
 }
 
 namespace {
+// Indices at or past n are clamped, so a malformed message stays in bounds.
 __global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t *__restrict__ idx, uint32_t count,
-                                                        const float *__restrict__ src, float *__restrict__ dst) {
+                                                        const float *__restrict__ src, uint32_t n,
+                                                        float *__restrict__ dst) {
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (i < count) dst[i] = src[idx[i]];
+    if (i < count) dst[i] = src[min(idx[i], n - 1)];
 }
 }  // namespace
 
@@ -1295,7 +1297,7 @@ extern "C" gc_status gc_slimdp_core_values(const gc_plan *core_plan, const gc_sp
         return set_error(GC_ECAPACITY, "gc_slimdp_core_values: core message smaller than the plan's total k");
     const uint64_t K = core_plan->total_k;
     GC_LAUNCH("slimdp_values", stream, gather_kernel<<<grid_1d(K, kBlock), kBlock, 0, stream>>>(
-        core->idx, static_cast<uint32_t>(K), delta, values));
+        core->idx, static_cast<uint32_t>(K), delta, static_cast<uint32_t>(core_plan->n_total), values));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_slimdp_core_values launch");
     return GC_OK;

@@ -246,8 +246,10 @@ gc_status gc_dgc_step(const gc_plan *plan, const float *G, float *U, float *V,
  *     the segment's count.  The call's cost grows with S (small P is slow).
  *   out->cap >= gc_dgc_message_cap(plan, opt).
  * Errors: as gc_dgc_step; GC_EINVAL also for an unknown momentum_kind or
- *         select, sample_period or over < 1 in sampled mode, reserved != 0.
+ *         select, sample_period outside [1, GC_MAX_SAMPLE_PERIOD] or over < 1
+ *         in sampled mode, reserved != 0.
  */
+#define GC_MAX_SAMPLE_PERIOD  (1u << 26)
 #define GC_MOMENTUM_VANILLA   0
 #define GC_MOMENTUM_NESTEROV  1
 #define GC_SELECT_EXACT       0
@@ -258,7 +260,7 @@ typedef struct gc_dgc_options {
     int      num_nodes;      /* N >= 1                                       */
     int      momentum_kind;  /* GC_MOMENTUM_*                                */
     int      select;         /* GC_SELECT_*                                  */
-    uint32_t sample_period;  /* GC_SELECT_SAMPLED: P >= 1                    */
+    uint32_t sample_period;  /* GC_SELECT_SAMPLED: 1 <= P <= GC_MAX_SAMPLE_PERIOD */
     uint32_t over;           /* GC_SELECT_SAMPLED: budget factor >= 1        */
     uint32_t reserved;       /* must be 0                                    */
 } gc_dgc_options;
@@ -423,7 +425,8 @@ gc_status gc_ecd_update(const float *scales, const uint8_t *codes, uint64_t n, i
  *     out       : ascending idx, val = delta_i; exactly sum(m_s) entries.
  * Core values: the core's keys are cached on both sides ([SlimDP] key caching
  *   filter), so a push sends only values: values[j] = delta[core->idx[j]]
- *   for j < gc_plan_total_k(core_plan).
+ *   for j < gc_plan_total_k(core_plan) (core as gc_slimdp_core wrote it;
+ *   indices at or past n_total are clamped to the last element).
  * Workspaces: gc_plan_workspace_bytes(plan, GC_OP_DGC).
  * Errors: GC_EINVAL (null, c not positive and finite, plans that differ in
  *         segments, core + explorer above a segment), GC_ECAPACITY.

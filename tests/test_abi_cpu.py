@@ -118,3 +118,21 @@ def test_slimdp_mask_words():
     assert B.gc_slimdp_mask_words(p) == 2 + 1 + 2
     assert B.load().gc_slimdp_mask_words(None) == 0
     assert B.load().gc_slimdp_core(None, None, None, 1.0, None, None, None, 0, None) == B.GC_EINVAL
+
+
+def test_dgc_ex_rejects_options_on_the_host():
+    lib = B.load()
+    p = B.Plan(W.make_table([5000], [1], [5]))
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    cases = [
+        (B.dgc_options(0.9, sampled=True, sample_period=(1 << 26) + 1), "sample_period"),
+        (B.dgc_options(0.9, sampled=True, sample_period=0), "sample_period"),
+        (B.dgc_options(0.9, sampled=True, over=0), "over"),
+        (B.dgc_options(1.0), "momentum"),
+        (B.gc_dgc_options(0.9, 0.0, 1, 7, 0, 100, 2, 0), "momentum_kind"),
+        (B.gc_dgc_options(0.9, 0.0, 1, 0, 5, 100, 2, 0), "select"),
+        (B.gc_dgc_options(0.9, 0.0, 1, 0, 0, 100, 2, 1), "reserved"),
+    ]
+    for opt, word in cases:
+        st = lib.gc_dgc_step_ex(p.handle, fake, fake, fake, ctypes.byref(opt), None, None, 0, None)
+        assert st == B.GC_EINVAL and word in B.gc_last_error(), (word, B.gc_last_error())
