@@ -64,6 +64,9 @@ def lib():
         L.orc_dgc_ex.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P]
         L.orc_pack.restype = ctypes.c_uint64
         L.orc_pack.argtypes = [ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, ctypes.c_uint64]
+        L.orc_unpack.restype = ctypes.c_int
+        L.orc_unpack.argtypes = [ctypes.c_int, P, ctypes.c_int, P, ctypes.c_uint64, P, P, P, P,
+                                 ctypes.c_uint64]
         L.orc_decode.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                  ctypes.c_int, ctypes.c_int]
         L.orc_philox4x32_10.argtypes = [P, P, P]
@@ -191,6 +194,23 @@ def pack(kind, table, idx, val, seg_off, seg_scale=None, cap=None) -> bytes:
     if nbytes == 0:
         raise ValueError("capacity too small")
     return out[:nbytes].tobytes()
+
+
+def unpack(kind, table, data: bytes, cap=None):
+    """Read a packed stream back.  Returns (status, idx, val, seg_off, seg_scale);
+    status 0 for a stream that fits the plan."""
+    t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
+    buf = np.frombuffer(bytes(data), dtype=np.uint8).copy() if len(data) else np.zeros(1, np.uint8)
+    if cap is None:
+        cap = int(t[:, 1].sum()) if len(t) else 0
+    idx = np.zeros(max(cap, 1), np.uint32)
+    val = np.zeros(max(cap, 1), np.float32)
+    seg_off = np.zeros(len(t) + 1, np.uint32)
+    seg_scale = np.zeros(max(len(t), 1), np.float32)
+    st = lib().orc_unpack(int(kind), _segs(t), len(t), _ptr(buf), len(data), _ptr(idx), _ptr(val),
+                          _ptr(seg_off), _ptr(seg_scale), int(cap))
+    m = int(seg_off[-1]) if st == 0 else 0
+    return st, idx[:m].copy(), val[:m].copy(), seg_off, seg_scale[:len(t)]
 
 
 def decode(table, n_total, messages, mode=1, dense=None):

@@ -445,6 +445,72 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
     return (uint64_t)(w - out);
 }
 
+/* ------------------------------------------------------------------ unpack */
+/*
+ * The receiver's side of the DGC §3.1 encoder: the stream read back into a
+ * message.  A segment's entries come in code order; a code's run counts the
+ * unsent elements before its entry, an escape (DGC run 0xFFFF, AdaComp run
+ * 0x7FFF) skips that many elements and carries no entry.  AdaComp entries take
+ * +-scale by their sign bit.  Returns 0, or nonzero for a stream that does not
+ * fit the plan (bad header, block past the end, entry outside its segment,
+ * more entries than cap, a DGC count that disagrees with its header).
+ */
+static uint32_t get_u32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+int orc_unpack(int kind, const orc_seg *segs, int nseg, const uint8_t *buf, uint64_t nbytes,
+               uint32_t *idx, float *val, uint32_t *seg_off, float *seg_scale, uint64_t cap)
+{
+    if (nbytes < 16 || get_u32(buf) != ORC_MAGIC('G', 'C', 'P', '1') || get_u32(buf + 4) != (uint32_t)kind ||
+        get_u32(buf + 8) != (uint32_t)nseg)
+        return 1;
+    const uint32_t MAX = kind == 1 ? 65535u : 32767u;
+    const uint32_t bmagic = kind == 1 ? ORC_MAGIC('D', 'G', 'C', '1') : ORC_MAGIC('A', 'D', 'C', '1');
+    uint64_t at = 16, out = 0;
+    for (int s = 0; s < nseg; ++s) {
+        seg_off[s] = (uint32_t)out;
+        if (at + 16 > nbytes || get_u32(buf + at) != bmagic || get_u32(buf + at + 4) != segs[s].length)
+            return 2;
+        uint64_t E = get_u32(buf + at + 8);
+        uint32_t w3 = get_u32(buf + at + 12);
+        uint64_t size = 16 + 2 * E + 2 * (E % 2) + (kind == 1 ? 4 * E : 0);
+        if (at + size > nbytes) return 2;
+        float scale;
+        memcpy(&scale, &w3, sizeof scale);
+        seg_scale[s] = kind == 1 ? 0.0f : scale;
+        const uint8_t *runs = buf + at + 16;
+        const uint8_t *vals = runs + 2 * E + 2 * (E % 2);
+        uint64_t p = 0, count = 0;
+        for (uint64_t e = 0; e < E; ++e) {
+            uint32_t code = (uint32_t)runs[2 * e] | (uint32_t)runs[2 * e + 1] << 8;
+            uint32_t run = kind == 1 ? code : (code & 0x7FFFu);
+            if (run == MAX) {
+                p += MAX;
+                continue;
+            }
+            uint64_t rel = p + run;
+            if (rel >= segs[s].length) return 3;
+            if (out >= cap) return 4;
+            idx[out] = (uint32_t)(segs[s].offset + rel);
+            if (kind == 1) {
+                uint32_t u = get_u32(vals + 4 * e);
+                memcpy(&val[out], &u, sizeof u);
+            } else {
+                val[out] = (code & 0x8000u) ? -scale : scale;
+            }
+            ++out;
+            ++count;
+            p = rel + 1;
+        }
+        if (kind == 1 && count != w3) return 5;
+        at += size;
+    }
+    seg_off[nseg] = (uint32_t)out;
+    return at == nbytes ? 0 : 2;
+}
+
 /* ------------------------------------------------------------------ decode */
 /*
  * DGC App. A: the nodes' gradients are summed; AdaComp: the learners'

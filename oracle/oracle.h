@@ -75,6 +75,12 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
                   const uint32_t *seg_off, const float *seg_scale,
                   uint8_t *out, uint64_t cap);
 
+/* Read a packed stream back into a message (idx, val, seg_off[nseg+1],
+ * seg_scale[nseg]) of at most cap entries.  Returns 0, or nonzero for a
+ * stream that does not fit the plan. */
+int orc_unpack(int kind, const orc_seg *segs, int nseg, const uint8_t *buf, uint64_t nbytes,
+               uint32_t *idx, float *val, uint32_t *seg_off, float *seg_scale, uint64_t cap);
+
 /* Decompress-aggregate K messages (idx[k], val[k], count[k]) into dense.
  * mode 0 = sum, 1 = average; accumulate != 0 adds into dense. */
 void orc_decode(const orc_seg *segs, int nseg, int K,

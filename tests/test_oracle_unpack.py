@@ -1,0 +1,76 @@
+"""Pins of the oracle's unpacker (the stream read back into a message)
+against the hand-assembled streams, an independent reader written from the
+format's specification (tests/packfmt.py), and malformed streams."""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_dnn_amd import workloads as W
+from tests.packfmt import unpack as spec_unpack
+from tests.test_oracle_codec import _tbl
+
+
+def test_unpack_hand_streams(golden_dir):
+    with open(os.path.join(golden_dir, "pack_hand.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        t = _tbl(c["segments"])
+        st, idx, val, off, sc = oracle.unpack(c["kind"], t, bytes.fromhex(c["hex"]))
+        assert st == 0, c["name"]
+        assert idx.tolist() == c["idx"] and off.tolist() == c["seg_off"], c["name"]
+        if c["kind"] == 1:
+            assert val.tolist() == c["val"], c["name"]
+        else:
+            assert sc.tolist() == c["scale"], c["name"]
+            assert val.tolist() == [(-1.0 if v < 0 else 1.0) * c["scale"][s]
+                                    for s in range(len(t)) for v in c["val"][c["seg_off"][s]:c["seg_off"][s + 1]]]
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+@pytest.mark.parametrize("seed", range(4))
+def test_unpack_agrees_with_the_spec_reader(kind, seed):
+    rng = np.random.default_rng(50 + seed)
+    t = W.random_table(rng, 12, max_len=90000, gaps=True)
+    n = W.table_extent(t)
+    G = W.random_values(rng, n)
+    G[rng.random(n) < 0.9995] = 0  # long zero runs: escapes
+    if kind == 1:
+        z = np.zeros(n, np.float32)
+        _, _, idx, val, off, _ = oracle.dgc(t, G, z, z, 0.9)
+        sc = np.zeros(len(t), np.float32)
+    else:
+        _, idx, val, off, sc, _ = oracle.adacomp(t, G, np.zeros(n, np.float32))
+    buf = oracle.pack(kind, t, idx, val, off, sc)
+    st, uidx, uval, uoff, usc = oracle.unpack(kind, t, buf)
+    assert st == 0
+    _, segs = spec_unpack(buf, [int(o) for o in t[:, 0]])
+    ref = [e for entries, _ in segs for e in entries]
+    assert uidx.tolist() == [i for i, _ in ref]
+    assert np.array_equal(uval.view(np.uint32), np.array([v for _, v in ref], np.float32).view(np.uint32))
+    assert np.array_equal(uoff, np.cumsum([0] + [len(e) for e, _ in segs]))
+    # and the message itself comes back (AdaComp values are +-scale by sign)
+    assert np.array_equal(uidx, idx) and np.array_equal(uoff, off)
+    if kind == 1:
+        assert np.array_equal(uval.view(np.uint32), val.view(np.uint32))
+    else:
+        assert np.array_equal(usc, sc)
+
+
+def test_unpack_rejects_malformed_streams():
+    t = _tbl([[0, 10], [12, 5]])
+    good = oracle.pack(1, t, [2, 9, 13], [1.0, -2.0, 3.0], [0, 2, 3], np.zeros(2, np.float32))
+    assert oracle.unpack(1, t, good)[0] == 0
+    assert oracle.unpack(2, t, good)[0] != 0                 # wrong kind
+    assert oracle.unpack(1, t, good[:-4])[0] != 0            # truncated
+    assert oracle.unpack(1, t, good + b"\0\0\0\0")[0] != 0   # trailing bytes
+    bad = bytearray(good)
+    bad[16:20] = b"ADC1"                                      # block magic
+    assert oracle.unpack(1, t, bytes(bad))[0] != 0
+    bad = bytearray(good)
+    struct.pack_into("<H", bad, 32, 10)                      # run past the segment end
+    assert oracle.unpack(1, t, bytes(bad))[0] != 0
+    assert oracle.unpack(1, t, good, cap=2)[0] != 0          # more entries than cap
