@@ -106,7 +106,8 @@ def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
                       f"{t_total:.1f} s on {threads} host threads"}
 
 
-def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log, reps: int = 5):
+def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log, dmsg, amsg, dbuf, abuf,
+                     dn, an, reps: int = 5):
     """Time the other calls of the path on the same workload, each alone
     (after the step timing, outside `value`): DGC with Nesterov momentum and
     with sampled selection, and the replica side of DCD-PSGD and ECD-PSGD.
@@ -170,6 +171,19 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
     timed("ecd_compress_4bit", lambda t: B.gc_ecd_compress(X, XH[t % len(XH)], 2 + t, 4, bucket, 0x5EED,
                                                            scales, codes), 8 * n + code_bytes)
     timed("ecd_update_4bit", lambda t: B.gc_ecd_update(scales, codes, XT, 2 + t, 4, bucket), 8 * n + code_bytes)
+
+    # the receiver's side of the exchange: the step's packed streams read back
+    # into messages (the streams and messages come from the last timed step)
+    ustat = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsu = plan.workspace(B.GC_OP_UNPACK, dev)
+    for label, kind, buf, nb, src in (("unpack_dgc_stream", B.GC_KIND_DGC, dbuf, dn, dmsg),
+                                      ("unpack_adacomp_stream", B.GC_KIND_ADACOMP, abuf, an, amsg)):
+        nbytes = int(nb.item())
+        entries = src.count()
+        um = B.Sparse.empty(plan, max(entries, 1), dev)
+        timed(label, lambda t, kind=kind, buf=buf, nbytes=nbytes, um=um:
+              B.gc_unpack(plan, kind, buf, nbytes, um, ustat, wsu), nbytes + 8 * entries)
+        assert int(ustat.item()) == 0, "the step's own stream must unpack cleanly"
 
     # Slim-DP at the page's VGG-16 setting (alpha 0.2, beta 0.1): a 10% core
     # by significance and a 10% explorer, per tensor
@@ -449,7 +463,8 @@ def main(argv=None):
     }
     if not args.no_variants:
         log("variants")
-        result["variants"] = measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log)
+        result["variants"] = measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log,
+                                              dmsg, amsg, dbuf, abuf, dn, an)
         result["configs"] = measure_configs(B, W, dev, log)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

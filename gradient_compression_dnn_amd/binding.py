@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 GC_OK, GC_EINVAL, GC_ECAPACITY, GC_ERANGE, GC_EHIP, GC_ENOTSUP = 0, -1, -2, -3, -4, -5
-GC_OP_DGC, GC_OP_ADACOMP, GC_OP_PACK, GC_OP_DECODE = 1, 2, 3, 4
+GC_OP_DGC, GC_OP_ADACOMP, GC_OP_PACK, GC_OP_DECODE, GC_OP_UNPACK = 1, 2, 3, 4, 5
 GC_KIND_DGC, GC_KIND_ADACOMP = 1, 2
 GC_SUM, GC_AVG = 0, 1
 GC_MOMENTUM_VANILLA, GC_MOMENTUM_NESTEROV = 0, 1
@@ -76,6 +76,7 @@ _SIGS = {
     "gc_dgc_step_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gc_pack_bound": (ctypes.c_uint64, [_P, ctypes.c_int]),
     "gc_pack": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_uint64, _P, _P, ctypes.c_size_t, _P]),
+    "gc_unpack": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_uint64, _P, _P, _P, ctypes.c_size_t, _P]),
     "gc_decompress_accumulate": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
                                                 _P, ctypes.c_size_t, _P]),
     "gc_dcd_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
@@ -98,7 +99,8 @@ _SIGS = {
 KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
-           "pack_tiles", "pack_count", "pack_layout", "pack_write", "decode_index", "decode", "dcd",
+           "pack_tiles", "pack_count", "pack_layout", "pack_write", "unpack_walk", "unpack_count", "unpack_scan",
+           "unpack_write", "decode_index", "decode", "dcd",
            "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update", "slimdp_values")
 
 
@@ -321,6 +323,17 @@ def gc_pack(plan: Plan, kind: int, msg: Sparse, out: torch.Tensor, out_bytes: to
     m = msg.struct()
     _check(load().gc_pack(plan.handle, int(kind), ctypes.byref(m), _ptr(out), out.numel(),
                           _ptr(out_bytes), _ptr(ws), ws.numel(), _stream(out)))
+
+
+def gc_unpack(plan: Plan, kind: int, data: torch.Tensor, nbytes: int, out: Sparse, status: torch.Tensor,
+              ws: torch.Tensor):
+    """data: uint8 device tensor holding the stream's nbytes bytes; status:
+    an int32 device tensor (holding u32) that receives the stream's status."""
+    if data.dtype != torch.uint8 or data.numel() < nbytes or status.dtype != torch.int32:
+        raise ValueError("gc_unpack: data must be uint8 with nbytes bytes, status int32")
+    m = out.struct()
+    _check(load().gc_unpack(plan.handle, int(kind), _ptr(data), int(nbytes), ctypes.byref(m), _ptr(status),
+                            _ptr(ws), ws.numel(), _stream(data)))
 
 
 def gc_decompress_accumulate(plan: Plan, msgs, dense, mode: int, accumulate: bool,

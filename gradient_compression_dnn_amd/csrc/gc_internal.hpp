@@ -112,6 +112,7 @@ size_t dgc_workspace_bytes(const gc_plan *plan);
 size_t adacomp_workspace_bytes(const gc_plan *plan);
 size_t pack_workspace_bytes(const gc_plan *plan);
 size_t decode_workspace_bytes(const gc_plan *plan);
+size_t unpack_workspace_bytes(const gc_plan *plan);
 
 // --------------------------------------------------------------- workspace
 // Bump allocator over the caller's workspace; every region 256-byte aligned.

@@ -261,6 +261,7 @@ size_t gc_plan_workspace_bytes(const gc_plan *plan, int op) {
         case GC_OP_ADACOMP: return adacomp_workspace_bytes(plan);
         case GC_OP_PACK: return pack_workspace_bytes(plan);
         case GC_OP_DECODE: return decode_workspace_bytes(plan);
+        case GC_OP_UNPACK: return unpack_workspace_bytes(plan);
         default: return 0;
     }
 }

@@ -120,6 +120,7 @@ uint32_t  gc_topk_count(uint32_t n);
 #define GC_OP_ADACOMP  2
 #define GC_OP_PACK     3
 #define GC_OP_DECODE   4
+#define GC_OP_UNPACK   5
 /* Device workspace bytes a hot call with this plan needs (0 if none). */
 size_t gc_plan_workspace_bytes(const gc_plan *plan, int op);
 
@@ -298,6 +299,35 @@ gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
                   uint8_t *out, uint64_t out_cap, uint64_t *out_bytes,
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The receiver's inverse of gc_pack: a stream (as gc_pack wrote it, for this
+ * plan and kind) read back into a message for gc_decompress_accumulate.  Per
+ * segment, codes are read in order from position p = 0: a code whose run is
+ * MAX (DGC 0xFFFF; AdaComp 0x7FFF, sign bit ignored) advances p by MAX;
+ * any other code puts an entry at segment position p + run, with val = the
+ * code's f32 value (DGC) or +-scale_s by the sign bit (AdaComp), then sets
+ * p to that position + 1.
+ *   in       : device stream of in_bytes bytes (4-byte aligned, >= 16).
+ *   out      : idx/val (ascending per segment), seg_off[nseg+1] and, for
+ *              AdaComp, seg_scale[nseg].  Entries at or past out->cap are
+ *              not written (seg_off is clamped to cap).
+ *   status   : device u32, set to 0 for a stream that fits the plan, else a
+ *              bitmask: 1 bad stream header, 2 bad block header or size
+ *              (or trailing bytes), 4 an entry outside its segment (not
+ *              written), 8 more entries than out->cap, 16 a DGC block whose
+ *              entries disagree with its header count.  Whatever the stream,
+ *              every write stays inside the message and its segments.
+ *   ws       : gc_plan_workspace_bytes(plan, GC_OP_UNPACK) bytes.
+ * The block headers are followed from the stream start by one thread (each
+ * block's size depends on its entry count), so the call's latency grows with
+ * the number of segments.
+ * Errors: GC_EINVAL (bad kind, null pointers, misaligned or short stream),
+ *         GC_ECAPACITY (ws).
+ */
+gc_status gc_unpack(const gc_plan *plan, int kind, const uint8_t *in, uint64_t in_bytes,
+                    gc_sparse *out, uint32_t *status, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
 /* ---------------------------------------------------------------- decode */
 /*
  * Decompress-and-aggregate K messages into a dense update ([DGC] App. A: the
@@ -452,7 +482,8 @@ gc_status gc_slimdp_core_values(const gc_plan *core_plan, const gc_sparse *core,
  *             dgc_select, dgc_stage, dgc_refine, dgc_sbase, dgc_count,
  *             dgc_scan, dgc_emit, ada_max, ada_binsum, ada_scale, ada_offsets,
  *             ada_apply, ada_fold, ada_emit, ada_residual,
- *             pack_tiles, pack_count, pack_layout, pack_write, decode_index,
+ *             pack_tiles, pack_count, pack_layout, pack_write, unpack_walk,
+ *             unpack_count, unpack_scan, unpack_write, decode_index,
  *             decode, dcd, dcd_decode, dcd_mix, ecd_compress, ecd_update,
  *             slimdp_values (Slim-DP selection reuses the dgc_* names).
  * gc_timing_take waits for the recorded events of one kernel and returns the

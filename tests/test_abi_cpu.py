@@ -75,7 +75,7 @@ def test_plan_queries_and_workspace_on_workloads():
         t = w.table
         assert p.total_k == int(t[:, 3].sum())
         assert p.total_bins == int(((t[:, 1] + t[:, 2] - 1) // t[:, 2]).sum())
-        for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK, B.GC_OP_DECODE):
+        for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK, B.GC_OP_DECODE, B.GC_OP_UNPACK):
             assert p.workspace_bytes(op) > 0
         # staging needs 8 bytes per element at most, plus small tables
         assert p.workspace_bytes(B.GC_OP_DGC) < 9 * w.n_total + (64 << 20)

@@ -1,0 +1,142 @@
+"""GPU parity of gc_unpack (the receiver's inverse of gc_pack) against the
+oracle's unpacker, bit for bit: hand-assembled streams, GPU-packed streams
+with escapes on random layouts, the DeepSpeech layout's streams decoded into
+the same dense update as their messages, and malformed streams (status set,
+every write inside the message)."""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, same_bits, say, ulp_report
+from tests.test_oracle_codec import _tbl
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_unpack(plan, kind, data: bytes, cap, guard=64):
+    buf = torch.zeros(max(len(data), 4) + 4, dtype=torch.uint8, device="cuda")
+    if data:
+        buf[:len(data)] = torch.from_numpy(np.frombuffer(data, np.uint8).copy()).cuda()
+    out = B.Sparse.empty(plan, cap + guard, "cuda")
+    out.idx.fill_(-1)
+    out.val.fill_(-7.0)
+    out.cap = cap
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    B.gc_unpack(plan, kind, buf, len(data), out, status, plan.workspace(B.GC_OP_UNPACK, "cuda"))
+    torch.cuda.synchronize()
+    st = int(status.item()) & 0xFFFFFFFF
+    tail_ok = bool(torch.all(out.idx[cap:] == -1)) and bool(torch.all(out.val[cap:] == -7.0))
+    return st, out, tail_ok
+
+
+def host_msg(out, nseg):
+    off = out.seg_off.cpu().numpy().view(np.uint32)
+    m = int(off[-1])
+    return (out.idx[:m].cpu().numpy().view(np.uint32), out.val[:m].cpu().numpy(), off,
+            out.seg_scale[:nseg].cpu().numpy())
+
+
+def test_hand_streams(golden_dir):
+    with open(os.path.join(golden_dir, "pack_hand.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        t = _tbl(c["segments"])
+        plan = B.Plan(t)
+        say(f"unpack hand {c['name']}")
+        st, out, tail_ok = gpu_unpack(plan, c["kind"], bytes.fromhex(c["hex"]), 64)
+        ost, oidx, oval, ooff, osc = oracle.unpack(c["kind"], t, bytes.fromhex(c["hex"]))
+        assert st == 0 and ost == 0 and tail_ok
+        gi, gv, go, gs = host_msg(out, len(t))
+        assert np.array_equal(gi, oidx) and np.array_equal(go, ooff) and same_bits(gv, oval)
+        if c["kind"] == 2:
+            assert same_bits(gs, osc)
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+@pytest.mark.parametrize("seed", range(5))
+def test_roundtrip_of_gpu_streams(kind, seed):
+    rng = np.random.default_rng(600 + seed)
+    t = W.random_table(rng, int(rng.integers(1, 40)), max_len=200000, gaps=True)
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    G = W.random_values(rng, n, "laplace")
+    G[rng.random(n) < (0.9995 if seed % 2 else 0.5)] = 0  # long zero runs: escapes
+    z = np.zeros(n, np.float32)
+    if kind == 1:
+        _, _, msg = hp.dgc(G, z.copy(), z.copy(), 0.9, tensors=True)
+    else:
+        _, msg = hp.adacomp(G, z.copy(), tensors=True)
+    data = hp.pack(kind, msg)
+    idx, val, off, sc = msg.host()
+    say(f"unpack roundtrip kind={kind} seed={seed} nseg={len(t)} bytes={len(data)}")
+    st, out, tail_ok = gpu_unpack(hp.plan, kind, data, max(len(idx), 1))
+    ost, oidx, oval, ooff, osc = oracle.unpack(kind, t, data)
+    assert st == 0 and ost == 0 and tail_ok
+    gi, gv, go, gs = host_msg(out, len(t))
+    assert np.array_equal(gi, oidx) and np.array_equal(go, ooff) and same_bits(gv, oval)
+    assert np.array_equal(gi, idx) and np.array_equal(go, off)
+    if kind == 1:
+        assert same_bits(gv, val)
+    else:
+        assert same_bits(gs, sc[:len(t)]) and same_bits(gv, val)
+
+
+def test_malformed_streams_set_status_and_stay_in_bounds():
+    t = _tbl([[0, 10], [12, 5]])
+    plan = B.Plan(t)
+    good = oracle.pack(1, t, [2, 9, 13], [1.0, -2.0, 3.0], [0, 2, 3], np.zeros(2, np.float32))
+    st, out, tail_ok = gpu_unpack(plan, 1, good, 3)
+    assert st == 0 and tail_ok
+    cases = {"trailing": good + b"\0\0\0\0", "truncated": good[:-4]}
+    bad = bytearray(good)
+    bad[16:20] = b"ADC1"
+    cases["block magic"] = bytes(bad)
+    bad = bytearray(good)
+    struct.pack_into("<H", bad, 32, 10)
+    cases["run past the end"] = bytes(bad)
+    bad = bytearray(good)
+    struct.pack_into("<I", bad, 24, 1 << 30)  # absurd code count
+    cases["code count"] = bytes(bad)
+    for name, data in cases.items():
+        say(f"unpack malformed {name}")
+        st, out, tail_ok = gpu_unpack(plan, 1, data, 3)
+        assert st != 0 and tail_ok, name
+        assert oracle.unpack(1, t, data)[0] != 0, name
+        # the message's content is unspecified, but slots are either left
+        # alone or hold an index inside a segment, and seg_off stays in range
+        gi, _, go, _ = host_msg(out, len(t))
+        written = gi[gi != 0xFFFFFFFF].astype(np.int64)
+        assert np.all((written < 10) | ((written >= 12) & (written < 17))), name
+        assert np.all(np.diff(go.astype(np.int64)) >= 0) and go[-1] <= 3, name
+    st, out, tail_ok = gpu_unpack(plan, 1, good, 2)  # one entry over capacity
+    assert st & 8 and tail_ok
+
+
+def test_deepspeech_streams_decode_like_their_messages():
+    """Pack, unpack and decompress-average the DeepSpeech layout's DGC and
+    AdaComp messages: the dense updates equal those of the original messages."""
+    w = W.make_config("deepspeech")
+    t, n = w.table, w.n_total
+    hp = HipPath(t, n)
+    g = W.gradient(w, 0)
+    z = np.zeros(n, np.float32)
+    _, _, dm = hp.dgc(g, z.copy(), z.copy(), 0.9, 1.0, 1, tensors=True)
+    _, am = hp.adacomp(g, z.copy(), tensors=True)
+    for kind, msg in ((1, dm), (2, am)):
+        say(f"deepspeech unpack kind={kind}")
+        data = hp.pack(kind, msg)
+        st, out, tail_ok = gpu_unpack(hp.plan, kind, data, msg.count())
+        assert st == 0 and tail_ok
+        idx, val, off, sc = msg.host()
+        gi, gv, go, gs = host_msg(out, len(t))
+        assert np.array_equal(gi, idx) and np.array_equal(go, off) and same_bits(gv, val)
+        want = hp.decode([msg], B.GC_AVG)
+        got = hp.decode([out], B.GC_AVG)
+        assert same_bits(got, want), ulp_report(got, want)
