@@ -210,8 +210,9 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
 def measure_configs(B, W, dev, log, reps: int = 10):
     """The other workloads of the configuration list, each timed alone after
     the step timing (not part of `value`): ms per step and dense fp32 GB/s.
-      fc1m        one AdaComp step (L_T = 50) and one DGC step (top 0.1%, no clip)
-      resnet50    DGC steps (momentum 0.9, clip 1.0, top 0.1% per tensor)
+      fc1m        one AdaComp step (L_T = 50) and one DGC step (top 0.1%, no clip);
+                  the DGC step also cold (Infinity Cache evicted before each call)
+      resnet50    DGC steps (momentum 0.9, clip 1.0, top 0.1% per tensor), warm and cold
       lstm_lm     AdaComp steps (L_T 500 / 50, residual carried)
       resnet50x8  8 learners' DGC steps (N = 8) and the 8-message average"""
     import torch
@@ -232,6 +233,25 @@ def measure_configs(B, W, dev, log, reps: int = 10):
                      "alg_hbm_frac": round(alg_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"config {name}: {ms:.3f} ms")
 
+    scratch = torch.empty(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
+
+    def timed_cold(name, fn, dense_bytes, alg_bytes):
+        """Each call after writing 1 GiB of scratch, which evicts the 256 MB
+        Infinity Cache; only the call itself is inside the events."""
+        fn(0)
+        ms = 0.0
+        for r in range(reps):
+            scratch.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(1 + r)
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "dense_GBs": round(dense_bytes / (ms / 1000.0) / 1e9, 1),
+                     "alg_hbm_frac": round(alg_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"config {name}: {ms:.3f} ms")
+
     def dev_grads(w, count=2):
         return [torch.from_numpy(W.gradient(w, t)).to(dev) for t in range(count)]
 
@@ -247,6 +267,7 @@ def measure_configs(B, W, dev, log, reps: int = 10):
     wsd, wsa = plan.workspace(B.GC_OP_DGC, dev), plan.workspace(B.GC_OP_ADACOMP, dev)
     timed("fc1m_adacomp", lambda t: B.gc_adacomp_compress(plan, g[t % 2], R, 2.0, am, wsa, state=st), 4 * n, 12 * n)
     timed("fc1m_dgc", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 0.0, 1, dm, wsd), 4 * n, 20 * n)
+    timed_cold("fc1m_dgc_cold", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 0.0, 1, dm, wsd), 4 * n, 20 * n)
     # the same two calls captured once in a HIP graph and replayed (the plan
     # is already on the device, and the hot calls allocate nothing)
     Gslot = g[0].clone()
@@ -265,7 +286,9 @@ def measure_configs(B, W, dev, log, reps: int = 10):
     dm = B.Sparse.empty(plan, plan.total_k, dev)
     wsd = plan.workspace(B.GC_OP_DGC, dev)
     timed("resnet50_dgc", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 1.0, 1, dm, wsd), 4 * n, 20 * n)
-    del g, U, V, wsd
+    timed_cold("resnet50_dgc_cold", lambda t: B.gc_dgc_step(plan, g[t % 2], U, V, 0.9, 1.0, 1, dm, wsd), 4 * n,
+               20 * n)
+    del g, U, V, wsd, scratch
     # lstm_lm
     w = W.make_config("lstm_lm")
     n = w.n_total
