@@ -51,6 +51,17 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def stored_step_traffic(digest: str):
+    """HBM bytes of the whole step from committed counter runs, or None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_deepspeech.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return d.get("step_hbm_bytes") if d.get("source_digest") == digest else None
+
+
 def stored_traffic(kernel: str, digest: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
     the counters were taken on other sources."""
@@ -477,6 +488,10 @@ def main(argv=None):
                    "parallelism": "single GPU (one learner)"},
         "step_alg_bytes": step_bytes,
         "step_alg_hbm_frac": round(step_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        # the counters' bytes for the whole step (committed rocprofv3 runs of these sources), over this step time
+        "step_counter_hbm_bytes": stored_step_traffic(digest),
+        "step_counter_hbm_frac": (None if stored_step_traffic(digest) is None else
+                                  round(stored_step_traffic(digest) / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)),
         "roofline": roof,
         "kernel_us_per_step": breakdown,
         "kernel_alg_hbm_frac": kernel_frac,
