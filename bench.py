@@ -452,6 +452,15 @@ def main(argv=None):
         b.copy_(a)
         torch.cuda.synchronize()
 
+    # the DCD step's signal-to-noise measure (alpha of the DCD page):
+    # ||Z - C(Z)|| / ||Z|| with Z = x_half - x and C(Z) = x_out - x, for the
+    # breakdown step's inputs
+    t_last = args.warmup + 1 + args.steps
+    z = (XH[t_last % len(XH)].double() - X.double())
+    cz = XO.double() - X.double()
+    dcd_alpha = float(torch.linalg.vector_norm(z - cz) / torch.linalg.vector_norm(z))
+    del z, cz
+
     ada_entries = amsg.count()
     nbins = plan.total_bins
     alg = algorithmic_bytes(n, nbins, plan.total_k, ada_entries, bucket)
@@ -496,7 +505,11 @@ def main(argv=None):
         "kernel_us_per_step": breakdown,
         "kernel_alg_hbm_frac": kernel_frac,
         "messages": {"dgc_entries": plan.total_k, "adacomp_entries": ada_entries,
-                     "dgc_packed_bytes": int(dn.item()), "adacomp_packed_bytes": int(an.item())},
+                     "dgc_packed_bytes": int(dn.item()), "adacomp_packed_bytes": int(an.item()),
+                     "dgc_compression_ratio": round(4 * n / int(dn.item()), 1),
+                     "adacomp_compression_ratio": round(4 * n / int(an.item()), 1),
+                     "dcd_codes_and_scales_bytes": (n + 1) // 2 + 4 * ((n + bucket - 1) // bucket),
+                     "dcd_alpha_emp": round(dcd_alpha, 5)},
         "source_digest": digest,
     }
     if not args.no_variants:
