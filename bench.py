@@ -121,9 +121,10 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
                      dn, an, reps: int = 5):
     """Time the other calls of the path on the same workload, each alone
     (after the step timing, outside `value`): DGC with Nesterov momentum and
-    with sampled selection, and the replica side of DCD-PSGD and ECD-PSGD.
-    Per call: ms, the method's algorithmic bytes and their fraction of HBM
-    peak, and the per-kernel split of one more call."""
+    with sampled selection, the replica side of DCD-PSGD and ECD-PSGD, the
+    unpacking of the step's two streams, and Slim-DP's core, explorer and
+    values-only push.  Per call: ms, the method's algorithmic bytes and their
+    fraction of HBM peak, and the per-kernel split of one more call."""
     import torch
 
     n = plan.n_total
@@ -187,9 +188,9 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
     # into messages (the streams and messages come from the last timed step)
     ustat = torch.zeros(1, dtype=torch.int32, device=dev)
     wsu = plan.workspace(B.GC_OP_UNPACK, dev)
-    for label, kind, buf, nb, src in (("unpack_dgc_stream", B.GC_KIND_DGC, dbuf, dn, dmsg),
-                                      ("unpack_adacomp_stream", B.GC_KIND_ADACOMP, abuf, an, amsg)):
-        nbytes = int(nb.item())
+    for label, kind, buf, nbytes_dev, src in (("unpack_dgc_stream", B.GC_KIND_DGC, dbuf, dn, dmsg),
+                                              ("unpack_adacomp_stream", B.GC_KIND_ADACOMP, abuf, an, amsg)):
+        nbytes = int(nbytes_dev.item())
         entries = src.count()
         um = B.Sparse.empty(plan, max(entries, 1), dev)
         timed(label, lambda t, kind=kind, buf=buf, nbytes=nbytes, um=um:
