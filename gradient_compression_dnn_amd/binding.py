@@ -21,6 +21,7 @@ GC_MOMENTUM_VANILLA, GC_MOMENTUM_NESTEROV = 0, 1
 GC_SELECT_EXACT, GC_SELECT_SAMPLED = 0, 1
 GC_MAX_BIN_LEN = 4096
 GC_MAX_MESSAGES = 64
+GC_MAX_SEGMENT_LEN = 0xFFFC0000
 GC_MAX_REPLICAS = 16
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgradcomp.so")

@@ -129,6 +129,9 @@ struct WsCursor {
     }
 };
 
+// ceil(a / b) in 64 bits (lengths near 2^32 overflow u32 round-ups).
+__host__ __device__ constexpr uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
 inline unsigned grid_1d(uint64_t n, unsigned per_block) {
     return static_cast<unsigned>((n + per_block - 1) / per_block);
 }

@@ -32,7 +32,7 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
     PackWs w{};
     size_t tiles = 0;
-    for (const auto &s : p->seg) tiles += (s.len + kTile - 1) / kTile;
+    for (const auto &s : p->seg) tiles += ceil_div(s.len, kTile);
     w.max_tiles = tiles + 1;
     w.tile_base = c.take<uint32_t>(p->nseg + 1);
     w.tile_esc = c.take<uint32_t>(w.max_tiles + 1);

@@ -168,13 +168,15 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         if (g.bin_len < 1) return set_error(GC_EINVAL, at + "bin_len must be >= 1");
         if (g.bin_len > GC_MAX_BIN_LEN)
             return set_error(GC_ENOTSUP, at + "bin_len above GC_MAX_BIN_LEN");
+        if (g.length > GC_MAX_SEGMENT_LEN)
+            return set_error(GC_ENOTSUP, at + "length above GC_MAX_SEGMENT_LEN");
         if (g.k < 1 || g.k > g.length) return set_error(GC_EINVAL, at + "k must be in [1, length]");
         prev_end = g.offset + g.length;
         total_k += g.k;
-        total_bins += (g.length + g.bin_len - 1) / g.bin_len;
-        ndchunk += (g.length + kChunk - 1) / kChunk;
+        total_bins += ceil_div(g.length, g.bin_len);
+        ndchunk += ceil_div(g.length, kChunk);
         uint32_t per = (kChunk / g.bin_len) * g.bin_len;  // whole bins per AdaComp chunk
-        nachunk += (g.length + per - 1) / per;
+        nachunk += ceil_div(g.length, per);
     }
     if (ndchunk >= (uint64_t(1) << 31) || nachunk >= (uint64_t(1) << 31))
         return set_error(GC_ERANGE, "gc_plan_create: too many chunks");
@@ -197,16 +199,16 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         d.len = g.length;
         d.bin_len = g.bin_len;
         d.k = g.k;
-        d.nbins = (g.length + g.bin_len - 1) / g.bin_len;
+        d.nbins = static_cast<uint32_t>(ceil_div(g.length, g.bin_len));
         d.dchunk0 = static_cast<uint32_t>(p->dchunk_seg.size());
-        d.dnchunk = (g.length + kChunk - 1) / kChunk;
+        d.dnchunk = static_cast<uint32_t>(ceil_div(g.length, kChunk));
         d.achunk_len = (kChunk / g.bin_len) * g.bin_len;
         d.achunk0 = static_cast<uint32_t>(p->achunk_seg.size());
-        d.anchunk = (g.length + d.achunk_len - 1) / d.achunk_len;
+        d.anchunk = static_cast<uint32_t>(ceil_div(g.length, d.achunk_len));
         d.bin0 = bin0;
         d.kbase = kbase;
         d.mbase = mbase;
-        mbase += (g.length + 31) / 32;
+        mbase += static_cast<uint32_t>(ceil_div(g.length, 32));
         d.bgroup0 = static_cast<uint32_t>(p->bgroup_seg.size());
         d.nbgroup = (d.nbins + kBinGroup - 1) / kBinGroup;
         for (uint32_t g2 = 0; g2 < d.nbgroup; ++g2) p->bgroup_seg.push_back(static_cast<uint32_t>(s));

@@ -92,6 +92,10 @@ typedef struct gc_segment {
 
 #define GC_MAX_BIN_LEN   4096u
 #define GC_MAX_MESSAGES  64
+/* Longest segment, 2^32 - 2^18: a packed block of n_s elements holds up to
+ * n_s + n_s / 32767 + 1 codes (an AdaComp message that sends every element,
+ * plus its escapes), and that count travels as the block's u32 E. */
+#define GC_MAX_SEGMENT_LEN 0xFFFC0000u
 
 /* Opaque, immutable plan: validated segment table + device tables. */
 typedef struct gc_plan gc_plan;
@@ -102,7 +106,8 @@ typedef struct gc_plan gc_plan;
  *   [0, n_total); n_total must be < 2^32 (indices are u32).  Gaps between
  *   segments are allowed and are never read or written.
  * Returns GC_EINVAL (bad table), GC_ERANGE (n_total >= 2^32), GC_ENOTSUP
- * (bin_len > GC_MAX_BIN_LEN).  *out is set only on GC_OK.
+ * (bin_len > GC_MAX_BIN_LEN or length > GC_MAX_SEGMENT_LEN).  *out is set
+ * only on GC_OK.
  */
 gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total,
                          gc_plan **out);

@@ -60,6 +60,8 @@ def _create(rows, n_total):
     ([(0, 5, 1, 1, 7)], 10, B.GC_EINVAL),                    # reserved != 0
     ([(0, 5, 4097, 1, 0)], 10, B.GC_ENOTSUP),                # bin_len too large
     ([(0, 5, 1, 1, 0)], 1 << 32, B.GC_ERANGE),               # indices are u32
+    ([(0, B.GC_MAX_SEGMENT_LEN + 1, 1, 1, 0)], (1 << 32) - 1, B.GC_ENOTSUP),  # u32 code count
+    ([(0, 0xFFFFFFFF, 64, 1, 0)], (1 << 32) - 1, B.GC_ENOTSUP),
     ([(0, 5, 1, 5, 0), (7, 3, 2, 1, 0)], 10, B.GC_OK),       # gap allowed
 ])
 def test_plan_validation(rows, n_total, code):
@@ -85,6 +87,27 @@ def test_plan_queries_and_workspace_on_workloads():
         # the pack bound covers the format's closed form at k entries per segment
         E = t[:, 3]
         assert p.pack_bound(B.GC_KIND_DGC) >= 16 + int(np.sum(16 + 6 * E + 2 * (E % 2)))
+        del p
+
+
+def test_longest_segments_at_the_top_of_the_index_range():
+    # the longest segment ends at the last u32 index; counts that round up
+    # a length near 2^32 must not wrap
+    L = B.GC_MAX_SEGMENT_LEN
+    n_total = (1 << 32) - 1
+    for bin_len in (1, 50, 4096):
+        t = np.array([[7, 100, bin_len, 3], [n_total - L, L, bin_len, L]], dtype=np.int64)
+        p = B.Plan(t, n_total)
+        assert p.total_k == 3 + L
+        assert p.total_bins == -(-100 // bin_len) + -(-L // bin_len)
+        assert B.gc_slimdp_mask_words(p) == 4 + -(-L // 32)
+        assert p.workspace_bytes(B.GC_OP_DGC) >= 8 * n_total
+        # every DGC chunk has a few u32 counters in the workspace
+        assert p.workspace_bytes(B.GC_OP_DECODE) >= 4 * -(-L // 4096)
+        # an AdaComp message that sends every element: entries plus escapes
+        codes = L + L // 32767 + 1
+        assert codes < 1 << 32
+        assert p.pack_bound(B.GC_KIND_ADACOMP) >= 16 + 2 * 16 + 2 * codes
         del p
 
 

@@ -1,0 +1,232 @@
+"""The largest plans: n_total = 2^32 - 1 (indices are u32) with the segments
+at the very top of the index range, so every flat index, chunk record, slot
+and offset the kernels form lies just below 2^32.  The device buffers span
+the whole range (about 17 GB each); only the segments are touched.  The
+oracle runs on the same segments rebased to a small window, and indices are
+compared after adding the base back."""
+import gc as pygc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import same_bits, say, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+N_TOTAL = (1 << 32) - 1
+LENGTHS = [100_000, 4097, 65, 150_001]
+GAPS = [0, 3, 100_003, 7]
+
+
+def layouts():
+    local = W.make_table(LENGTHS, [50, 500, 7, 64], [W.topk_count(n) for n in LENGTHS], GAPS)
+    window = W.table_extent(local)
+    base = N_TOTAL - window  # the last segment ends exactly at N_TOTAL
+    top = local.copy()
+    top[:, 0] += base
+    return local, top, base, window
+
+
+def big(fill=0.0):
+    return torch.full((N_TOTAL,), fill, dtype=torch.float32, device="cuda")
+
+
+def put(buf, base, arr):
+    buf[base:base + len(arr)] = torch.from_numpy(arr).cuda()
+
+
+def get(buf, base, window):
+    return buf[base:base + window].cpu().numpy()
+
+
+@pytest.fixture(autouse=True)
+def release():
+    yield
+    pygc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_dgc_exact_and_sampled_at_the_top_of_the_range():
+    local, top, base, window = layouts()
+    plan = B.Plan(top, N_TOTAL)
+    rng = np.random.default_rng(77)
+    G, U, V = (W.random_values(rng, window, "laplace") for _ in range(3))
+    ws = plan.workspace(B.GC_OP_DGC, "cuda")
+    Gd, Ud, Vd = big(), big(), big()
+    for sampled in (False, True):
+        say(f"max-index dgc sampled={sampled}")
+        put(Gd, base, G)
+        put(Ud, base, U)
+        put(Vd, base, V)
+        opt = B.dgc_options(0.9, 1e-3, 2, sampled=sampled, sample_period=7, over=2)
+        msg = B.Sparse.empty(plan, B.gc_dgc_message_cap(plan, opt), "cuda")
+        B.gc_dgc_step_ex(plan, Gd, Ud, Vd, opt, msg, ws)
+        torch.cuda.synchronize()
+        Uo, Vo, idx, val, off, _ = oracle.dgc_ex(local, G, U, V, 0.9, 1e-3, 2, sampled=sampled,
+                                                 sample_period=7, over=2)
+        gi, gv, go, _ = msg.host()
+        assert np.array_equal(go, off)
+        assert np.array_equal(gi.astype(np.int64), idx.astype(np.int64) + base)
+        assert same_bits(gv, val)
+        assert same_bits(get(Ud, base, window), Uo) and same_bits(get(Vd, base, window), Vo)
+        # the packed stream and its unpacking
+        if not sampled:
+            say("max-index dgc pack and unpack")
+            cap = plan.pack_bound(B.GC_KIND_DGC)
+            buf = torch.zeros(cap, dtype=torch.uint8, device="cuda")
+            nb = torch.zeros(1, dtype=torch.int64, device="cuda")
+            B.gc_pack(plan, B.GC_KIND_DGC, msg, buf, nb, plan.workspace(B.GC_OP_PACK, "cuda"))
+            torch.cuda.synchronize()
+            data = buf[:int(nb.item())].cpu().numpy().tobytes()
+            assert data == oracle.pack(1, local, idx, val, off, np.zeros(len(local), np.float32))
+            um = B.Sparse.empty(plan, msg.count(), "cuda")
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            B.gc_unpack(plan, B.GC_KIND_DGC, buf, int(nb.item()), um, st, plan.workspace(B.GC_OP_UNPACK, "cuda"))
+            torch.cuda.synchronize()
+            ui, uv, uo, _ = um.host()
+            assert int(st.item()) == 0 and np.array_equal(ui, gi) and same_bits(uv, gv)
+            say("max-index decode")
+            dense = big(3.0)
+            B.gc_decompress_accumulate(plan, [msg], dense, B.GC_SUM, False, plan.workspace(B.GC_OP_DECODE, "cuda"))
+            torch.cuda.synchronize()
+            want = oracle.decode(local, window, [(idx, val)], mode=0)
+            got = get(dense, base, window)
+            inseg = np.zeros(window, bool)
+            for o, ln, _, _ in local:
+                inseg[o:o + ln] = True
+            assert same_bits(got[inseg], want[inseg]), ulp_report(got[inseg], want[inseg])
+            assert np.all(got[~inseg] == 3.0)  # gaps untouched
+            assert float(dense[0].item()) == 3.0
+            del dense
+
+
+def test_adacomp_at_the_top_of_the_range():
+    local, top, base, window = layouts()
+    plan = B.Plan(top, N_TOTAL)
+    rng = np.random.default_rng(78)
+    dW, R = (W.random_values(rng, window, "normal") for _ in range(2))
+    Rd, dWd = big(), big()
+    put(Rd, base, R)
+    put(dWd, base, dW)
+    st = plan.adacomp_state("cuda")
+    msg = B.Sparse.empty(plan, N_TOTAL, "cuda")
+    ws = plan.workspace(B.GC_OP_ADACOMP, "cuda")
+    say("max-index adacomp")
+    B.gc_adacomp_compress(plan, dWd, Rd, 2.0, msg, ws, state=st)
+    torch.cuda.synchronize()
+    Ro, idx, val, off, scale, _ = oracle.adacomp(local, dW, R, 2.0)
+    gi, gv, go, gs = msg.host()
+    assert np.array_equal(go, off) and np.array_equal(gi.astype(np.int64), idx.astype(np.int64) + base)
+    assert same_bits(gv, val) and same_bits(gs[:len(local)], scale)
+    exact = big()
+    B.gc_adacomp_residual(plan, Rd, st, exact)
+    torch.cuda.synchronize()
+    assert same_bits(get(exact, base, window), Ro)
+
+
+def test_dgc_on_the_longest_segment_by_its_properties():
+    """One segment of GC_MAX_SEGMENT_LEN elements ending at the last u32
+    index (about 1M chunks in one segment: the clipping tree, the histograms,
+    the chunk scans and the message all at their largest).  Too large for the
+    oracle, so the step is checked against what defines it: the clipping
+    factor from an exactly representable squared norm (G holds multiples of
+    2^-10 in [-3, 3] 2^-10, so every partial sum of squares is exact in fp64
+    whatever its order), the momentum arithmetic element by element in fp32,
+    masking at the sent entries, and the top-k order (every sent key above
+    every unsent key, ties at the threshold taken from the lowest indices).
+    The message is then packed, unpacked and decoded."""
+    L = B.GC_MAX_SEGMENT_LEN
+    base = N_TOTAL - L
+    k = W.topk_count(L)
+    plan = B.Plan(np.array([[base, L, 4096, k]], dtype=np.int64), N_TOTAL)
+    m, thr_G, nodes = 0.9, 10.0, 4
+    SL = 1 << 28
+    slices = [(a, min(a + SL, L)) for a in range(0, L, SL)]
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    Gd, Ud, Vd = big(), big(), big()
+    say("max-length segment: inputs")
+    for a, b in slices:
+        Gd[base + a:base + b] = torch.randint(-3, 4, (b - a,), generator=gen, device="cuda",
+                                              dtype=torch.int32).float() * 2.0 ** -10
+        Ud[base + a:base + b] = torch.randn(b - a, generator=gen, device="cuda") * 1e-3
+        Vd[base + a:base + b] = torch.randn(b - a, generator=gen, device="cuda") * 1e-3
+    U0, V0 = Ud[base:].clone(), Vd[base:].clone()
+    S = sum(float((Gd[base + a:base + b].double() ** 2).sum().item()) for a, b in slices)
+    thr = float(np.float32(thr_G / np.sqrt(nodes)))
+    c = float(np.float32(thr / np.sqrt(S))) if np.sqrt(S) > thr else 1.0
+    assert c < 1.0  # clipping is active
+
+    say("max-length segment: dgc step")
+    msg = B.Sparse.empty(plan, k, "cuda")
+    ws = plan.workspace(B.GC_OP_DGC, "cuda")
+    B.gc_dgc_step(plan, Gd, Ud, Vd, m, thr_G, nodes, msg, ws)
+    torch.cuda.synchronize()
+    del ws
+    pygc.collect()
+    torch.cuda.empty_cache()
+    off = msg.seg_off.cpu().numpy().view(np.uint32)
+    assert off[0] == 0 and off[1] == k
+    idx = msg.idx[:k].long() & 0xFFFFFFFF
+    assert bool((idx[1:] > idx[:-1]).all()) and int(idx[0]) >= base and int(idx[-1]) < N_TOTAL
+    rel = idx - base
+    sent = torch.zeros(L, dtype=torch.bool, device="cuda")
+    sent[rel] = True
+    vals = msg.val[:k]
+    key_sent = vals.view(torch.int32) & 0x7FFFFFFF
+    T = int(key_sent.min())
+    ties_sent_last = int(rel[key_sent == T].max())
+
+    say("max-length segment: element checks")
+    m32 = float(np.float32(m))
+    max_unsent, first_unsent_tie = -1, None
+    for a, b in slices:
+        g = Gd[base + a:base + b] * c
+        u = U0[a:b] * m32 + g
+        v = V0[a:b] + u
+        s = sent[a:b]
+        uo, vo = Ud[base + a:base + b], Vd[base + a:base + b]
+        ns = ~s
+        assert torch.equal(uo[ns].view(torch.int32), u[ns].view(torch.int32))
+        assert torch.equal(vo[ns].view(torch.int32), v[ns].view(torch.int32))
+        assert not bool(uo[s].view(torch.int32).any()) and not bool(vo[s].view(torch.int32).any())
+        kv = v.view(torch.int32) & 0x7FFFFFFF
+        ku = kv[ns]
+        if ku.numel():
+            max_unsent = max(max_unsent, int(ku.max()))
+        if first_unsent_tie is None:
+            at = torch.nonzero(ns & (kv == T))
+            if at.numel():
+                first_unsent_tie = a + int(at[0])
+        # the message carries V before masking
+        in_slice = (rel >= a) & (rel < b)
+        assert torch.equal(vals[in_slice].view(torch.int32), v[rel[in_slice] - a].view(torch.int32))
+        del g, u, v, kv, ku
+    assert max_unsent <= T
+    if first_unsent_tie is not None:
+        assert ties_sent_last < first_unsent_tie
+    del U0, V0, Ud, Vd, Gd, sent
+    pygc.collect()
+    torch.cuda.empty_cache()
+
+    say("max-length segment: pack, unpack, decode")
+    cap = plan.pack_bound(B.GC_KIND_DGC)
+    buf = torch.zeros(cap, dtype=torch.uint8, device="cuda")
+    nb = torch.zeros(1, dtype=torch.int64, device="cuda")
+    B.gc_pack(plan, B.GC_KIND_DGC, msg, buf, nb, plan.workspace(B.GC_OP_PACK, "cuda"))
+    um = B.Sparse.empty(plan, k, "cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.gc_unpack(plan, B.GC_KIND_DGC, buf, int(nb.item()), um, st, plan.workspace(B.GC_OP_UNPACK, "cuda"))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and um.count() == k
+    assert torch.equal(um.idx[:k], msg.idx[:k]) and torch.equal(um.val[:k].view(torch.int32), vals.view(torch.int32))
+    dense = big(3.0)
+    B.gc_decompress_accumulate(plan, [um], dense, B.GC_SUM, False, plan.workspace(B.GC_OP_DECODE, "cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(dense[idx].view(torch.int32), vals.view(torch.int32))
+    nz = sum(int(torch.count_nonzero(dense[base + a:base + b])) for a, b in slices)
+    assert nz == int(torch.count_nonzero(vals))
+    assert bool((dense[:base] == 3.0).all())  # before the segment: untouched
