@@ -92,9 +92,12 @@ constexpr uint32_t kSparseChunk = 32;  // up to this many entries: no LDS accumu
 
 // start[k][c] = first entry of message k at or after chunk c: entry j (0..n)
 // writes it for every chunk c with chunk(idx[j-1]) < c <= chunk(idx[j]),
-// taking chunk(idx[-1]) = -1 and chunk(idx[n]) = ndchunk.  Those intervals
-// cover 0..ndchunk whatever the order of the indices, so every start[k][c] is
-// written, with a value in [0, count_k].  The grid is
+// taking chunk(idx[-1]) = -1 and chunk(idx[n]) = ndchunk.  For ascending
+// indices those intervals tile 0..ndchunk, so every start[k][c] is written,
+// with a value in [0, count_k].  The cursor's clamping makes chunk() depend
+// on the walk for descending indices, which may leave a start unwritten; the
+// decode pass clamps what it reads to count_k, so that input still stays in
+// bounds.  The grid is
 // bounded and strides over the entries, since the host sizes it from the
 // capacity, not from the (device-resident) count.
 __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTable m, DecWs w) {
@@ -166,10 +169,13 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
     const int lane = lane_id();
     uint32_t a = 0, b = 0;
     if (lane < K) {
-        // the index pass wrote every start[lane][0..ndchunk] within [0, count]
+        // message lane's entries of the chunk, clamped to its count: for
+        // ascending indices the index pass wrote every start within it, and
+        // whatever it left for other input, no entry past the count is read
         const uint32_t *st = w.start + size_t(lane) * (P.ndchunk + 1);
-        a = st[c];
-        b = max(st[c + 1], a);
+        const uint32_t nk = msg_count(m, lane);
+        a = min(st[c], nk);
+        b = min(max(st[c + 1], a), nk);
     }
     const uint32_t total = wave_sum(b - a);  // identical in every wave
     float v[kRows][4];

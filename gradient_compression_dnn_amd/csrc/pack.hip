@@ -3,11 +3,17 @@
 // zero-run lengths; AdaComp messages carry only a sign per entry plus one
 // layer scale, so their 16-bit code holds the sign in bit 15.
 //
-// Entries of a segment are processed in tiles of 4096 (16 per thread).  A run longer than the code can hold is split with escapes; an
-// entry's slot in its block is its rank in the segment plus the escapes
-// emitted before it.  Escapes are rare (a gap of 32767+ unsent elements), so
-// the count pass adds per-segment totals with integer atomics, and the write
-// pass scans escape counts only in segments and tiles that have any.
+// Entries of a segment are processed in tiles of 4096.  A run longer than
+// the code can hold is split with escapes; an entry's slot in its block is
+// its rank in the segment plus the escapes emitted before it.  Escapes are
+// rare (a gap of 32767+ unsent elements), so the count pass adds per-segment
+// totals with integer atomics, and the write pass scans escape counts only
+// in segments and tiles that have any.  The count pass reads a tile in the
+// 4-wide lane layout of the dense kernels (one 16-byte load per lane and
+// row) and leaves a record of the tile (segment, entry range, segment
+// geometry), so that a write workgroup starts its data loads after a single
+// round trip; the write pass is lane-strided, so that each wave's 2-byte
+// code stores cover contiguous bytes.
 #include <algorithm>
 
 #include "gc_internal.hpp"
@@ -17,11 +23,13 @@ namespace gc {
 namespace {
 
 constexpr uint32_t kTile = 4096;
-constexpr uint32_t kPerThread = kTile / kBlock;
+constexpr int kTileRows = kTile / (4 * kBlock);
 
 struct PackWs {
-    uint32_t *tile_base;  // [nseg + 1] first tile of each segment
+    uint32_t *tile_base;  // [nseg + 1] first tile of each segment; [nseg] = tile count
     uint32_t *tile_esc;   // [max_tiles] escapes per tile
+    uint4 *tile_rec;      // [2 * max_tiles] per tile: {segment, first entry, entries, tile in segment},
+                          //   {segment offset, length, first entry of the segment, 0}
     uint32_t *seg_esc;    // [nseg] escapes per segment
     uint64_t *blk_off;    // [nseg] byte offset of each block
     uint32_t *seg_E;      // [nseg]
@@ -36,6 +44,7 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.max_tiles = tiles + 1;
     w.tile_base = c.take<uint32_t>(p->nseg + 1);
     w.tile_esc = c.take<uint32_t>(w.max_tiles + 1);
+    w.tile_rec = c.take<uint4>(2 * w.max_tiles);
     w.seg_esc = c.take<uint32_t>(p->nseg);
     w.blk_off = c.take<uint64_t>(p->nseg);
     w.seg_E = c.take<uint32_t>(p->nseg);
@@ -48,10 +57,11 @@ constexpr uint32_t magic(char a, char b, char c, char d) {
            uint32_t(uint8_t(d)) << 24;
 }
 
+// The segment of an entry, as the gap computation needs it.
 struct EntryCtx {
-    uint32_t s, first, end;  // segment and its entry range
-    uint64_t off;            // segment offset
-    uint32_t len;            // segment length
+    uint32_t first;  // first entry of the segment
+    uint32_t off;    // segment offset (below 2^32, as every index)
+    uint32_t len;    // segment length
 };
 
 // Entries of segment s, clamped so that a malformed message can never make
@@ -71,41 +81,47 @@ __device__ __forceinline__ uint32_t seg_max_entries(const SegDev &s, int kind) {
     return kind == GC_KIND_DGC ? s.k : s.len;
 }
 
-__device__ __forceinline__ EntryCtx entry_ctx(const PlanDev &P, const uint32_t *seg_off, int kind,
-                                              uint64_t cap, uint32_t s) {
-    EntryCtx x;
-    x.s = s;
-    x.first = seg_off[s];
-    x.end = x.first + seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap);
-    x.off = P.seg[s].off;
-    x.len = P.seg[s].len;
-    return x;
-}
-
 // Gap before entry j (unsent elements since the previous entry) from the
 // loaded indices cur = idx[j] and prv = idx[j - 1]; out-of-order or
 // out-of-segment indices count as gap 0.  Escapes before the entry are
 // floor(gap / MAX).
+// With rel = cur - off and p = prv - off (when prv >= off), the gap is
+// rel - p - 1 when p < rel < len; rel when j is the segment's first entry or
+// prv < off; 0 otherwise.  All in u32: no difference can wrap.
 __device__ __forceinline__ uint32_t entry_gap(const EntryCtx &x, uint32_t j, uint32_t cur, uint32_t prv) {
-    const uint64_t rel = cur >= x.off ? uint64_t(cur) - x.off : uint64_t(x.len);
-    const uint64_t prev_next = j > x.first ? (prv >= x.off ? uint64_t(prv) - x.off + 1 : 0) : 0;
-    return (rel < x.len && rel >= prev_next) ? static_cast<uint32_t>(rel - prev_next) : 0u;
+    if (cur < x.off) return 0u;
+    const uint32_t rel = cur - x.off;
+    if (rel >= x.len) return 0u;
+    if (j > x.first && prv >= x.off) {
+        const uint32_t p = prv - x.off;
+        return p < rel ? rel - p - 1 : 0u;
+    }
+    return rel;
 }
 
-// Loads idx[j] and idx[j - 1] for entries j = j0 + i * stride of one tile,
-// all issued before any is used: addresses are clamped into the segment's
-// entries (which the tile's existence makes non-empty), so no load sits
-// behind a branch.
-template <uint32_t N>
-__device__ __forceinline__ void load_ids(const uint32_t *__restrict__ idx, const EntryCtx &x, uint32_t j0,
-                                         uint32_t stride, uint32_t (&cur)[N], uint32_t (&prv)[N]) {
-    const uint32_t last = x.end > x.first ? x.end - 1 : x.first;
+// The tile's entries [j0, j0 + cnt) in the 4-wide layout: cur[r][q] =
+// idx[j0 + 1024 r + 4 t + q] (0 past cnt, from the buffer's range check)
+// and prv0[r] = the entry before the lane's first one of row r (clamped
+// into the tile when that entry is the segment's first, where it is unused,
+// or lies past the tile).  All loads are issued before any is used.
+__device__ __forceinline__ void load_tile(const uint32_t *__restrict__ a, uint32_t first, uint32_t j0,
+                                          uint32_t cnt, uint32_t (&cur)[kTileRows][4],
+                                          uint32_t (&prv0)[kTileRows]) {
+    const BufRsrc r = chunk_buf(reinterpret_cast<const float *>(a + j0), cnt);
 #pragma unroll
-    for (uint32_t i = 0; i < N; ++i) {
-        const uint32_t j = min(j0 + i * stride, last);
-        cur[i] = idx[j];
-        prv[i] = idx[j > x.first ? j - 1 : j];
+    for (int row = 0; row < kTileRows; ++row) {
+        float v[4];
+        load4(r, row_elem(row), v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[row][q] = dev_f2u(v[q]);
+        const uint32_t j = min(j0 + row_elem(row), j0 + cnt);
+        prv0[row] = a[j > first ? j - 1 : first];
     }
+}
+
+__device__ __forceinline__ uint32_t prev_of(const uint32_t (&cur)[kTileRows][4], const uint32_t (&prv0)[kTileRows],
+                                            int row, int q) {
+    return q == 0 ? prv0[row] : cur[row][q - 1];
 }
 
 // One workgroup: tile counts per segment -> tile_base.
@@ -130,7 +146,8 @@ __global__ __launch_bounds__(kBlock) void pack_tiles_kernel(PlanDev P, int kind,
 }
 
 // Segment of tile t: the last s with tile_base[s] <= t.  Workgroups copy the
-// table to LDS once when it fits, so the searches cost no global round trips.
+// table (and the tile count after it) to LDS once when it fits, so the
+// searches cost no global round trips.
 constexpr int kLdsSegs = 4096;
 
 struct TileTable {
@@ -139,13 +156,14 @@ struct TileTable {
     __device__ void init(const uint32_t *tile_base, int n, uint32_t *lds) {
         nseg = n;
         if (n <= kLdsSegs) {
-            for (int i = threadIdx.x; i < n; i += kBlock) lds[i] = tile_base[i];
+            for (int i = threadIdx.x; i <= n; i += kBlock) lds[i] = tile_base[i];
             __syncthreads();
             tb = lds;
         } else {
             tb = tile_base;
         }
     }
+    __device__ uint32_t count() const { return tb[nseg]; }
     __device__ uint32_t segment(uint32_t t) const {
         int lo = 0, hi = nseg - 1;
         while (lo < hi) {
@@ -161,28 +179,40 @@ __global__ __launch_bounds__(kBlock) void pack_count_kernel(PlanDev P, int kind,
                                                             const uint32_t *__restrict__ idx,
                                                             const uint32_t *__restrict__ seg_off,
                                                             uint64_t cap, uint32_t MAX, PackWs w) {
-    const uint32_t ntiles = w.tile_base[P.nseg];
-    if (blockIdx.x >= ntiles) return;
-    __shared__ uint32_t lds[kLdsSegs];
+    __shared__ uint32_t lds[kLdsSegs + 1];
     TileTable table;
     table.init(w.tile_base, P.nseg, lds);
+    const uint32_t ntiles = table.count();
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const EntryCtx x = entry_ctx(P, seg_off, kind, cap, table.segment(t));
-    const uint32_t j0 = x.first + (t - w.tile_base[x.s]) * kTile;
-    uint32_t cur[kPerThread], prv[kPerThread];
-    load_ids(idx, x, j0 + threadIdx.x, kBlock, cur, prv);
-    uint32_t esc = 0;
+        const uint32_t s = table.segment(t);
+        const uint32_t ts = t - table.tb[s];
+        const SegDev sg = P.seg[s];
+        EntryCtx x;
+        x.first = seg_off[s];
+        x.off = static_cast<uint32_t>(sg.off);
+        x.len = sg.len;
+        const uint32_t end = x.first + seg_entries(seg_off, s, seg_max_entries(sg, kind), cap);
+        const uint32_t j0 = x.first + ts * kTile;
+        const uint32_t cnt = min(end - j0, kTile);
+        uint32_t cur[kTileRows][4], prv0[kTileRows];
+        load_tile(idx, x.first, j0, cnt, cur, prv0);
+        uint32_t esc = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < kPerThread; ++i) {
-        const uint32_t j = j0 + i * kBlock + threadIdx.x;
-        if (j < x.end) esc += entry_gap(x, j, cur[i], prv[i]) / MAX;
-    }
-    uint32_t tot;
-    (void)block_exclusive_scan(esc, &tot);
-    if (threadIdx.x == 0) {
-        w.tile_esc[t] = tot;
-        if (tot) atomicAdd(&w.seg_esc[x.s], tot);
-    }
+        for (int row = 0; row < kTileRows; ++row)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t e = row_elem(row) + q;
+                if (e < cnt) esc += entry_gap(x, j0 + e, cur[row][q], prev_of(cur, prv0, row, q)) / MAX;
+            }
+        uint32_t tot;
+        (void)block_exclusive_scan(esc, &tot);
+        if (threadIdx.x == 0) {
+            w.tile_esc[t] = tot;
+            w.tile_rec[2 * size_t(t)] = make_uint4(s, j0, cnt, ts);
+            w.tile_rec[2 * size_t(t) + 1] =
+                make_uint4(x.off, x.len, x.first, 0u);
+            if (tot) atomicAdd(&w.seg_esc[s], tot);
+        }
     }
 }
 
@@ -235,99 +265,114 @@ __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind
     }
 }
 
-__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, uint64_t cap,
+// Write pass.  Entries are lane-strided here (entry i * 256 + t of the tile
+// in thread t), so that each 2-byte code store of a wave covers 128
+// contiguous bytes.  The loads of a tile are issued before its escape count
+// is known; a tile with escapes (rare) drops them and walks 16 contiguous
+// entries per thread in two light passes (escapes, then slots), reloading
+// what it needs, so that its registers do not add to the common path's.
+constexpr uint32_t kPerThread = kTile / kBlock;
+
+// A wave-uniform value moved to a scalar register (the tile geometry is read
+// with vector loads; every lane holds the same value).
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, size_t max_tiles,
                                                             const uint32_t *__restrict__ idx,
-                                                            const float *__restrict__ val,
-                                                            const uint32_t *__restrict__ seg_off,
-                                                            uint32_t MAX, uint8_t *__restrict__ out,
-                                                            PackWs w) {
-    const uint32_t ntiles = w.tile_base[P.nseg];
-    if (blockIdx.x >= ntiles) return;
+                                                            const float *__restrict__ val, uint32_t MAX,
+                                                            uint8_t *__restrict__ out, PackWs w) {
     const bool dgc = kind == GC_KIND_DGC;
-    __shared__ uint32_t lds[kLdsSegs];
-    TileTable table;
-    table.init(w.tile_base, P.nseg, lds);
-    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const EntryCtx x = entry_ctx(P, seg_off, kind, cap, table.segment(t));
-    const uint32_t tile0 = w.tile_base[x.s];
-    const uint32_t j0 = x.first + (t - tile0) * kTile;
-    const uint32_t E = w.seg_E[x.s];
-    uint8_t *blk = out + w.blk_off[x.s];
-    uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
-    float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
-    // escapes emitted before this tile in its segment
-    uint32_t esc_base = 0;
-    if (w.seg_esc[x.s] != 0) {
-        uint32_t part = 0;
-        for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
-        uint32_t all;
-        (void)block_exclusive_scan(part, &all);
-        esc_base = all;
-    }
-    if (w.tile_esc[t] == 0) {
-        // no escape in this tile: entry j goes to slot (j - first) + esc_base
+    for (uint32_t t = blockIdx.x; t < max_tiles; t += gridDim.x) {
+        // the tile count and the tile's record in one round trip (records
+        // past the count are never used)
+        const uint32_t ntiles = uni(w.tile_base[P.nseg]);
+        const uint4 ra = w.tile_rec[2 * size_t(t)], rb = w.tile_rec[2 * size_t(t) + 1];
+        if (t >= ntiles) break;
+        const uint32_t s = uni(ra.x), j0 = uni(ra.y), cnt = uni(ra.z);
+        EntryCtx x;
+        x.off = uni(rb.x);
+        x.len = uni(rb.y);
+        x.first = uni(rb.z);
+        const uint32_t tile0 = t - uni(ra.w);
+        // buffer resources over the tile (32-bit offsets; loads past the
+        // range return 0): entries, values, and the entries shifted back by
+        // one (from the entry before the tile unless the tile is the
+        // segment's first, where entry 0's predecessor is unused)
+        const uint32_t d = uni(j0 > x.first ? 1u : 0u);
+        const BufRsrc ri = chunk_buf(reinterpret_cast<const float *>(idx + j0), cnt);
+        const BufRsrc rp = chunk_buf(reinterpret_cast<const float *>(idx + j0 - d), cnt + d);
+        const BufRsrc rv = chunk_buf(val + j0, cnt);
         uint32_t cur[kPerThread], prv[kPerThread];
-        load_ids(idx, x, j0 + threadIdx.x, kBlock, cur, prv);
         float v[kPerThread];
-        const uint32_t last = x.end > x.first ? x.end - 1 : x.first;
-#pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) v[i] = val[min(j0 + i * kBlock + threadIdx.x, last)];
 #pragma unroll
         for (uint32_t i = 0; i < kPerThread; ++i) {
-            const uint32_t j = j0 + i * kBlock + threadIdx.x;
-            const uint32_t slot = (j - x.first) + esc_base;
-            if (j >= x.end || slot >= E) continue;  // slot >= E only for malformed messages
-            const uint32_t gap = entry_gap(x, j, cur[i], prv[i]);
+            const uint32_t e = i * kBlock + threadIdx.x;
+            const uint32_t ep = e + d > 0 ? e + d - 1 : 0u;
+            cur[i] = __builtin_amdgcn_raw_buffer_load_b32(ri, static_cast<int>(4 * e), 0, kBufNT);
+            prv[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, static_cast<int>(4 * ep), 0, kBufNT);
+            v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * e), 0, kBufNT));
+        }
+        const uint32_t E = w.seg_E[s];
+        const uint32_t tile_esc = w.tile_esc[t], seg_esc = w.seg_esc[s];
+        uint8_t *blk = out + w.blk_off[s];
+        uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
+        float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
+        // escapes emitted before this tile in its segment
+        uint32_t esc_base = 0;
+        if (seg_esc != 0) {
+            uint32_t part = 0;
+            for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
+            uint32_t all;
+            (void)block_exclusive_scan(part, &all);
+            esc_base = all;
+        }
+        auto put = [&](uint32_t slot, uint32_t gap, float value) {
             // the packed stream is not read again here: non-temporal stores
             if (dgc) {
                 __builtin_nontemporal_store(static_cast<uint16_t>(gap), runs + slot);
-                __builtin_nontemporal_store(v[i], vals + slot);
+                __builtin_nontemporal_store(value, vals + slot);
             } else {
-                const uint16_t sign = (dev_f2u(v[i]) >> 31) ? 0x8000u : 0u;
+                const uint16_t sign = (dev_f2u(value) >> 31) ? 0x8000u : 0u;
                 __builtin_nontemporal_store(static_cast<uint16_t>(sign | gap), runs + slot);
             }
-        }
-        continue;
-    }
-    // tile with escapes: thread-contiguous entries and an in-tile scan
-    uint32_t esc[kPerThread], gap[kPerThread];
-    {
-        uint32_t cur[kPerThread], prv[kPerThread];
-        load_ids(idx, x, j0 + threadIdx.x * kPerThread, 1u, cur, prv);
+        };
+        if (tile_esc == 0) {
+            // no escape in this tile: entry j goes to slot (j - first) + esc_base
 #pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            const uint32_t j = j0 + threadIdx.x * kPerThread + i;
-            gap[i] = j < x.end ? entry_gap(x, j, cur[i], prv[i]) : 0u;
-            esc[i] = gap[i] / MAX;
+            for (uint32_t i = 0; i < kPerThread; ++i) {
+                const uint32_t e = i * kBlock + threadIdx.x;
+                const uint32_t slot = (j0 + e - x.first) + esc_base;
+                if (e >= cnt || slot >= E) continue;  // slot >= E only for malformed messages
+                put(slot, entry_gap(x, j0 + e, cur[i], prv[i]), v[i]);
+            }
+            continue;
         }
-    }
-    uint32_t mine = 0;
-#pragma unroll
-    for (uint32_t i = 0; i < kPerThread; ++i) mine += esc[i];
-    uint32_t tot;
-    uint32_t before = esc_base + block_exclusive_scan(mine, &tot);
-#pragma unroll
-    for (uint32_t i = 0; i < kPerThread; ++i) {
-        const uint32_t j = j0 + threadIdx.x * kPerThread + i;
-        if (j >= x.end) continue;
-        uint32_t slot = (j - x.first) + before;
-        uint32_t g = gap[i];
-        for (uint32_t q = 0; q < esc[i] && slot < E; ++q) {
-            runs[slot] = static_cast<uint16_t>(MAX);
-            if (dgc) vals[slot] = 0.0f;
-            ++slot;
-            g -= MAX;
+        // tile with escapes: thread t takes entries [16 t, 16 t + 16) of the tile
+        const uint32_t e0 = threadIdx.x * kPerThread;
+        auto gap_at = [&](uint32_t e) {
+            const uint32_t j = j0 + e;
+            return entry_gap(x, j, idx[j], idx[j > x.first ? j - 1 : j]);
+        };
+        uint32_t mine = 0;
+#pragma unroll 1
+        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) mine += gap_at(e) / MAX;
+        uint32_t tot;
+        uint32_t before = esc_base + block_exclusive_scan(mine, &tot);
+#pragma unroll 1
+        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) {
+            uint32_t slot = (j0 + e - x.first) + before;
+            uint32_t g = gap_at(e);
+            const uint32_t esc = g / MAX;
+            for (uint32_t z = 0; z < esc && slot < E; ++z) {
+                runs[slot] = static_cast<uint16_t>(MAX);
+                if (dgc) vals[slot] = 0.0f;
+                ++slot;
+                g -= MAX;
+            }
+            before += esc;
+            if (slot >= E) continue;  // only for malformed messages
+            put(slot, g, val[j0 + e]);
         }
-        if (slot >= E) continue;  // only for malformed messages
-        if (dgc) {
-            runs[slot] = static_cast<uint16_t>(g);
-            vals[slot] = val[j];
-        } else {
-            const uint16_t sign = (dev_f2u(val[j]) >> 31) ? 0x8000u : 0u;
-            runs[slot] = static_cast<uint16_t>(sign | g);
-        }
-        before += esc[i];
-    }
     }
 }
 
@@ -391,7 +436,7 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
     GC_LAUNCH("pack_layout", stream, pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
                                                  out_bytes, w));
-    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->idx, in->val, in->seg_off, MAX,
+    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, w.max_tiles, in->idx, in->val, MAX,
                                                    out, w));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_pack launch");

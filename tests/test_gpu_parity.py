@@ -351,6 +351,59 @@ def test_decode_chunk_entry_counts(K):
             assert same_bits(got, want), ulp_report(got, want)
 
 
+def test_decode_malformed_messages_stay_in_bounds():
+    """Messages that break the decoder's contract: descending indices,
+    repeated ones, indices in gaps and past n, and a count beyond the
+    capacity.  The workspace starts filled with 0xFF, so any chunk start that
+    the index pass leaves unwritten reads as 2^32 - 1.  The call must complete
+    and touch no element outside the segments, whatever it leaves inside
+    them: each chunk's entry range is clamped to the message's count.  A
+    well-formed decode with the same workspace afterwards must equal the
+    oracle's."""
+    rng = np.random.default_rng(808)
+    t = W.make_table([9000, 4096 * 3 + 17, 300], [50, 50, 50], [9, 13, 1], [5, 1000, 7])
+    n = W.table_extent(t) + 500  # a gap after the last segment too
+    plan = B.Plan(t, n)
+    ws = plan.workspace(B.GC_OP_DECODE, "cuda")
+    ws.fill_(255)
+    inseg = np.zeros(n, bool)
+    for o, ln, _, _ in t:
+        inseg[o:o + ln] = True
+    valid = np.flatnonzero(inseg).astype(np.uint32)
+    gaps = np.flatnonzero(~inseg).astype(np.uint32)
+    desc = np.sort(rng.choice(valid, 3000, replace=False))[::-1].copy()
+    mixed = np.concatenate([rng.choice(valid, 2000), rng.choice(gaps, 300),
+                            np.array([n, n + 5, 0xFFFFFFFF, 0], np.uint32)])
+    rng.shuffle(mixed)
+    bad = []
+    for idx in (desc, mixed):
+        offs = np.linspace(0, idx.size, len(t) + 1).astype(np.uint32)
+        bad.append(sparse_from_host(plan, idx, W.random_values(rng, idx.size), offs))
+    # seg_off[nseg] far past the 64 entries the message holds
+    bad.append(sparse_from_host(plan, rng.choice(valid, 64).astype(np.uint32), W.random_values(rng, 64),
+                                [0, 10, 20, 1 << 30]))
+    for name, msgs in (("descending", bad[:1]), ("mixed", bad[1:2]), ("count past cap", bad[2:]),
+                       ("all three", bad)):
+        for acc in (False, True):
+            say(f"decode malformed {name} acc={acc}")
+            d = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+            B.gc_decompress_accumulate(plan, msgs, d, B.GC_SUM, acc, ws)
+            torch.cuda.synchronize()
+            got = d.cpu().numpy()
+            assert np.all(got[~inseg] == 7.0)
+            assert np.all(np.isfinite(got))
+    say("decode well-formed after malformed")
+    idx = np.sort(rng.choice(valid, 2500, replace=False)).astype(np.uint32)
+    val = W.random_values(rng, idx.size, "laplace")
+    offs = [int(np.searchsorted(idx, o)) for o, _, _, _ in t] + [idx.size]
+    good = sparse_from_host(plan, idx, val, offs)
+    d = torch.zeros(n, dtype=torch.float32, device="cuda")
+    B.gc_decompress_accumulate(plan, [good], d, B.GC_AVG, False, ws)
+    torch.cuda.synchronize()
+    want = oracle.decode(t, n, [(idx, val)], mode=B.GC_AVG)
+    assert same_bits(d.cpu().numpy(), want)
+
+
 # ---------------------------------------------------------------------- DCD
 @pytest.mark.parametrize("n", [1, 3, 4, 5, 511, 512, 513, 4096, 4097, 100_003])
 @pytest.mark.parametrize("bits_", [4, 8])
