@@ -77,8 +77,22 @@ def stored_traffic(kernel: str, digest: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
-    """The oracle, as it stands, over a bounded sample of the same workload."""
+    """The oracle, as it stands, over a bounded sample of the same workload;
+    then one step on a single thread over a smaller sample, and the library
+    on the first sample (same inputs and steps) compared bit for bit with
+    the oracle's last step."""
     import numpy as np
 
     import oracle
@@ -87,34 +101,131 @@ def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
     threads = len(os.sched_getaffinity(0))
     oracle.set_num_threads(threads)
     names = [nm for nm, _ in W.deepspeech_shapes()]
-    sel = [i for i, nm in enumerate(names) if nm.split(".")[0] in ("gru1", "gru2", "gru3", "gru4")]
-    sub = w.table[sel].copy()
-    lo, hi = int(sub[0, 0]), int(sub[-1, 0] + sub[-1, 1])
-    sub[:, 0] -= lo
+
+    def sample(layers):
+        sel = [i for i, nm in enumerate(names) if nm.split(".")[0] in layers]
+        sub = w.table[sel].copy()
+        lo, hi = int(sub[0, 0]), int(sub[-1, 0] + sub[-1, 1])
+        sub[:, 0] -= lo
+        return sub, lo, hi
+
+    def one_step(sub, lo, hi, t, U, V, R):
+        n = hi - lo
+        g = grads[t % len(grads)][lo:hi]
+        x = x0[lo:hi]
+        xh = W.dcd_half_step(x, g)
+        t0 = time.perf_counter()
+        U, V, idx, val, off, _ = oracle.dgc(sub, g, U, V, 0.9, 1.0, 1)
+        dbytes = oracle.pack(1, sub, idx, val, off)
+        R, ai, av, ao, asc, _ = oracle.adacomp(sub, g, R, 2.0)
+        abytes = oracle.pack(2, sub, ai, av, ao, asc)
+        dd = oracle.decode(sub, n, [(idx, val)], mode=1)
+        ad = oracle.decode(sub, n, [(ai, av)], mode=1)
+        xo, sc, cd = oracle.dcd(x, xh, 4, 512, 0x5EED, t)
+        dt = time.perf_counter() - t0
+        out = dict(U=U, V=V, R=R, dgc=(idx, val, off), dbytes=dbytes, ada=(ai, av, ao, asc), abytes=abytes,
+                   dd=dd, ad=ad, dcd=(xo, sc, cd))
+        return dt, out
+
+    sub, lo, hi = sample(("gru1", "gru2", "gru3", "gru4"))
     n = hi - lo
     U = np.zeros(n, np.float32)
     V = np.zeros(n, np.float32)
     R = np.zeros(n, np.float32)
-    x = x0[lo:hi].copy()
-    done, t_total = 0, 0.0
+    done, t_total, last = 0, 0.0, None
     while done < max_steps and (t_total < steps_min_s or done == 0):
-        g = grads[done % len(grads)][lo:hi]
-        xh = W.dcd_half_step(x, g)
-        t0 = time.perf_counter()
-        U, V, idx, val, off, _ = oracle.dgc(sub, g, U, V, 0.9, 1.0, 1)
-        oracle.pack(1, sub, idx, val, off)
-        R, ai, av, ao, asc, _ = oracle.adacomp(sub, g, R, 2.0)
-        oracle.pack(2, sub, ai, av, ao, asc)
-        oracle.decode(sub, n, [(idx, val)], mode=1)
-        oracle.decode(sub, n, [(ai, av)], mode=1)
-        oracle.dcd(x, xh, 4, 512, 0x5EED, done)
-        t_total += time.perf_counter() - t0
+        dt, last = one_step(sub, lo, hi, done, U, V, R)
+        U, V, R = last["U"], last["V"], last["R"]
+        t_total += dt
         done += 1
     gbs = 2 * 4 * n * done / t_total / 1e9
+
+    # one thread, one step over one GRU layer
+    sub1, lo1, hi1 = sample(("gru2",))
+    n1 = hi1 - lo1
+    oracle.set_num_threads(1)
+    z = np.zeros(n1, np.float32)
+    dt1, _ = one_step(sub1, lo1, hi1, 0, z, z.copy(), z.copy())
+    oracle.set_num_threads(threads)
+
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} full step(s) (DGC+pack, AdaComp+pack, 2 decodes, DCD) over the "
                       f"32 GRU tensors of layers 1-4 ({n:,} of {w.n_total:,} elements), "
-                      f"{t_total:.1f} s on {threads} host threads"}
+                      f"{t_total:.1f} s on {threads} host threads",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(2 * 4 * n1 / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"1 step over the 8 tensors of GRU layer 2 ({n1:,} elements), "
+                                        f"{dt1:.1f} s"},
+            "parity": library_parity(sub, lo, hi, grads, x0, done, last)}
+
+
+def library_parity(sub, lo, hi, grads, x0, steps, want):
+    """The library over the oracle baseline's sample, with the same inputs and
+    steps; the last step's outputs compared bit for bit with the oracle's."""
+    import numpy as np
+    import torch
+
+    from gradient_compression_dnn_amd import binding as B
+    from gradient_compression_dnn_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    n = hi - lo
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def same(t, a):
+        h = t.cpu().numpy() if torch.is_tensor(t) else t
+        return bool(np.array_equal(np.asarray(h).view(np.uint32), np.ascontiguousarray(a, np.float32).view(np.uint32)))
+
+    plan = B.Plan(sub, n)
+    ws = {op: plan.workspace(op, dev) for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK, B.GC_OP_DECODE)}
+    U, V, R = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
+    state = plan.adacomp_state(dev)
+    dmsg = B.Sparse.empty(plan, plan.total_k, dev)
+    amsg = B.Sparse.empty(plan, n, dev)
+    dbuf = torch.zeros(plan.pack_bound(B.GC_KIND_DGC), dtype=torch.uint8, device=dev)
+    abuf = torch.zeros(plan.pack_bound(B.GC_KIND_ADACOMP), dtype=torch.uint8, device=dev)
+    dn = torch.zeros(1, dtype=torch.int64, device=dev)
+    an = torch.zeros(1, dtype=torch.int64, device=dev)
+    dd, ad, xo = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
+    sc = torch.zeros((n + 511) // 512, dtype=torch.float32, device=dev)
+    cd = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=dev)
+    x = x0[lo:hi]
+    X = f32(x)
+    for t in range(steps):
+        gh = grads[t % len(grads)][lo:hi]
+        g, xh = f32(gh), f32(W.dcd_half_step(x, gh))
+        B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC])
+        B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK])
+        B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=state)
+        B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK])
+        B.gc_decompress_accumulate(plan, [dmsg], dd, B.GC_AVG, False, ws[B.GC_OP_DECODE])
+        B.gc_decompress_accumulate(plan, [amsg], ad, B.GC_AVG, False, ws[B.GC_OP_DECODE])
+        B.gc_dcd_compress(X, xh, xo, 4, 512, 0x5EED, t, sc, cd)
+    R_exact = torch.empty_like(R)
+    B.gc_adacomp_residual(plan, R, state, R_exact)
+    torch.cuda.synchronize()
+    di, dv, doff, _ = dmsg.host()
+    ai, av, aoff, asc = amsg.host()
+    wi, wv, woff = want["dgc"]
+    xi, xv, xoff, xsc = want["ada"]
+    wo, wsc, wcd = want["dcd"]
+    checks = {
+        "dgc_U_V": same(U, want["U"]) and same(V, want["V"]),
+        "dgc_message": (np.array_equal(di, wi) and same(dv, wv) and np.array_equal(doff, woff)),
+        "dgc_packed_bytes": dbuf[:int(dn.item())].cpu().numpy().tobytes() == want["dbytes"],
+        "adacomp_residual": same(R_exact, want["R"]),
+        "adacomp_message": (np.array_equal(ai, xi) and same(av, xv) and np.array_equal(aoff, xoff)
+                            and same(asc[:len(sub)], xsc)),
+        "adacomp_packed_bytes": abuf[:int(an.item())].cpu().numpy().tobytes() == want["abytes"],
+        "decoded": same(dd, want["dd"]) and same(ad, want["ad"]),
+        "dcd": same(xo, wo) and same(sc, wsc) and bool(np.array_equal(cd.cpu().numpy(), wcd)),
+    }
+    return {"bitwise_equal": all(checks.values()), "checks": checks, "steps": steps, "elements": n,
+            "what": "the library run on the oracle baseline's sample (same inputs and steps); "
+                    "the last step's states, messages, packed bytes, decoded updates and DCD outputs "
+                    "compared bit for bit"}
 
 
 def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log, dmsg, amsg, dbuf, abuf,
@@ -426,12 +537,17 @@ def main(argv=None):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} step(s)")
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     t_start.record()
     for t in range(args.steps):
         step(args.warmup + 1 + t)
+        if t + 1 < args.steps:
+            marks[t].record()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    bounds = [t_start] + marks + [t_end]
+    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
     dom_ms, dom_cnt = B.gc_timing_take(dominant)
     B.gc_timing_enable(None)
     ms_per_step = total_ms / args.steps
@@ -452,6 +568,23 @@ def main(argv=None):
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
+
+    # the measured streaming ceiling: a plain 1 GiB device-to-device copy, best of 5
+    ca = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
+    cb = torch.empty_like(ca)
+    cb.copy_(ca)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cb.copy_(ca)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    copy_gbs = 2 * ca.numel() * 4 / (best / 1000.0) / 1e9
+    del ca, cb
 
     # the DCD step's signal-to-noise measure (alpha of the DCD page):
     # ||Z - C(Z)|| / ||Z|| with Z = x_half - x and C(Z) = x_out - x, for the
@@ -488,7 +621,9 @@ def main(argv=None):
     result = {
         "metric": "GB/s of fp32 gradient compressed per step (+% HBM peak), DGC & AdaComp",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4), "step_ms_min": round(step_ms[0], 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "deepspeech: 121,893,373 fp32 gradient elements in 68 tensors "
                                "(5 conv + 7 bidirectional GRU, hidden 800 + FC), log-normal "
@@ -503,6 +638,8 @@ def main(argv=None):
         "step_counter_hbm_frac": (None if stored_step_traffic(digest) is None else
                                   round(stored_step_traffic(digest) / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)),
         "roofline": roof,
+        "copy_ceiling": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                         "what": "device-to-device copy of 1 GiB (1 GiB read + 1 GiB written), best of 5"},
         "kernel_us_per_step": breakdown,
         "kernel_alg_hbm_frac": kernel_frac,
         "messages": {"dgc_entries": plan.total_k, "adacomp_entries": ada_entries,
@@ -521,6 +658,7 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, grads, x0)
+        result["parity"] = result["cpu_baseline"].pop("parity")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
