@@ -70,6 +70,7 @@ _SIGS = {
     "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.c_float, _P, _P,
                                            ctypes.c_size_t, _P]),
     "gc_adacomp_state_bytes": (ctypes.c_size_t, [_P]),
+    "gc_adacomp_message_cap": (ctypes.c_uint64, [_P]),
     "gc_adacomp_residual": (ctypes.c_int, [_P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gc_dgc_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]),
@@ -276,6 +277,11 @@ def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws:
     _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _ptr(state),
                                       state.numel() if state is not None else 0, float(scale_factor),
                                       ctypes.byref(msg), _ptr(ws), ws.numel(), _stream(R)))
+
+
+def gc_adacomp_message_cap(plan: Plan) -> int:
+    """Slots an AdaComp message needs: the sum of the segment lengths."""
+    return int(load().gc_adacomp_message_cap(plan.handle))
 
 
 def gc_adacomp_state_bytes(plan: Plan) -> int:

@@ -463,6 +463,8 @@ size_t adacomp_workspace_bytes(const gc_plan *plan) {
 
 using namespace gc;
 
+extern "C" uint64_t gc_adacomp_message_cap(const gc_plan *plan) { return plan ? plan->seg_elems : 0; }
+
 extern "C" size_t gc_adacomp_state_bytes(const gc_plan *plan) {
     if (!plan) return 0;
     size_t b = 0;
@@ -481,8 +483,8 @@ extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, f
                          "gc_adacomp_compress: out and its idx, val, seg_off, seg_scale must be non-null");
     if (!(scale_factor >= 1.0f) || std::isinf(scale_factor))
         return set_error(GC_EINVAL, "gc_adacomp_compress: scale_factor must be finite and >= 1");
-    if (out->cap < plan->n_total)
-        return set_error(GC_ECAPACITY, "gc_adacomp_compress: out->cap must be >= n_total");
+    if (out->cap < plan->seg_elems)
+        return set_error(GC_ECAPACITY, "gc_adacomp_compress: out->cap below gc_adacomp_message_cap");
     size_t need = adacomp_workspace_bytes(plan);
     if (!ws || ws_bytes < need)
         return set_error(GC_ECAPACITY,

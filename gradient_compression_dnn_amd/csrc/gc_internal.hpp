@@ -85,6 +85,7 @@ struct gc_plan {
     uint32_t nachunk = 0;
     uint32_t nbgroup = 0;
     uint64_t mask_words = 0;  // sum over segments of ceil(length / 32)
+    uint64_t seg_elems = 0;   // sum over segments of the length
     std::vector<gc::SegDev> seg;
     std::vector<uint32_t> dchunk_seg;
     std::vector<uint32_t> achunk_seg;

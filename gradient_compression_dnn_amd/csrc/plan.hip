@@ -192,6 +192,7 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     p->dchunk_seg.reserve(ndchunk);
     p->achunk_seg.reserve(nachunk);
     uint32_t bin0 = 0, kbase = 0, mbase = 0;
+    uint64_t seg_elems = 0;
     for (int s = 0; s < nseg; ++s) {
         const gc_segment &g = segs[s];
         SegDev d{};
@@ -231,11 +232,13 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         }
         p->seg[s] = d;
         p->seg_start[s] = g.offset;
+        seg_elems += g.length;
     }
     p->ndchunk = static_cast<uint32_t>(p->dchunk_seg.size());
     p->nachunk = static_cast<uint32_t>(p->achunk_seg.size());
     p->nbgroup = static_cast<uint32_t>(p->bgroup_seg.size());
     p->mask_words = mbase;
+    p->seg_elems = seg_elems;
     *out = p;
     return GC_OK;
 }

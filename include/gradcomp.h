@@ -175,11 +175,13 @@ typedef struct gc_sparse {
  *     call applies before a1.  R and dW then cross HBM once per step instead
  *     of twice.  Messages are identical in both modes; gc_adacomp_residual()
  *     gives the exact residual of (R, state).
- *   dW  [n_total] in,  R [n_total] in/out,  out: cap >= n_total (worst case).
+ *   dW  [n_total] in,  R [n_total] in/out,
+ *   out : cap >= gc_adacomp_message_cap(plan), the sum of the segment
+ *         lengths (the worst case: every element sent).
  *   ws  : at least gc_plan_workspace_bytes(plan, GC_OP_ADACOMP) bytes.
  * Errors: GC_EINVAL (null pointer, scale_factor not finite or < 1, state
- *         not 256-byte aligned), GC_ECAPACITY (out->cap < n_total, ws or
- *         state too small).
+ *         not 256-byte aligned), GC_ECAPACITY (out->cap below
+ *         gc_adacomp_message_cap, ws or state too small).
  */
 gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, void *state,
                               size_t state_bytes, float scale_factor, gc_sparse *out,
@@ -188,6 +190,10 @@ gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, vo
 /* Bytes of one learner's deferred-residual state for this plan (0 if plan
  * is NULL). */
 size_t gc_adacomp_state_bytes(const gc_plan *plan);
+
+/* Slots an AdaComp message needs for this plan: the sum of the segment
+ * lengths (0 if plan is NULL).  Gaps between segments need none. */
+uint64_t gc_adacomp_message_cap(const gc_plan *plan);
 
 /* R_out[n_total] <- the exact residual held by (R, state): elements outside
  * every segment are copied, in-segment elements sent in the last deferred

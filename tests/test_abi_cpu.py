@@ -135,6 +135,23 @@ def test_dgc_ex_host_checks_and_message_cap():
     assert lib.gc_dgc_message_cap(None, None) == 0
 
 
+def test_adacomp_message_cap_is_the_sum_of_the_segment_lengths():
+    t = W.make_table([5000, 100, 7], [1, 1, 1], [5, 1, 3], [10, 2000, 3])
+    p = B.Plan(t, W.table_extent(t) + 50)
+    assert B.gc_adacomp_message_cap(p) == 5107
+    assert B.load().gc_adacomp_message_cap(None) == 0
+    # the host checks the capacity before anything touches a device (the
+    # pointers are never dereferenced on these paths)
+    lib, fake = B.load(), ctypes.c_void_p(256)
+
+    def call(cap):
+        msg = B.gc_sparse(fake, fake, fake, fake, cap)
+        return lib.gc_adacomp_compress(p.handle, fake, fake, None, 0, 2.0, ctypes.byref(msg), None, 0, None)
+
+    assert call(5106) == B.GC_ECAPACITY and "gc_adacomp_message_cap" in B.gc_last_error()
+    assert call(5107) == B.GC_ECAPACITY and "workspace" in B.gc_last_error()  # next check: no workspace
+
+
 def test_slimdp_mask_words():
     t = W.make_table([40, 5, 64], [1, 1, 1], [1, 1, 1])
     p = B.Plan(t)

@@ -113,7 +113,7 @@ def test_adacomp_at_the_top_of_the_range():
     put(Rd, base, R)
     put(dWd, base, dW)
     st = plan.adacomp_state("cuda")
-    msg = B.Sparse.empty(plan, N_TOTAL, "cuda")
+    msg = B.Sparse.empty(plan, B.gc_adacomp_message_cap(plan), "cuda")  # the segments' elements, not n
     ws = plan.workspace(B.GC_OP_ADACOMP, "cuda")
     say("max-index adacomp")
     B.gc_adacomp_compress(plan, dWd, Rd, 2.0, msg, ws, state=st)
