@@ -454,8 +454,6 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the DGC Nesterov / sampled and DCD replica / ECD calls")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 512 MiB device copy (for counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -563,14 +561,8 @@ def main(argv=None):
             breakdown[kname] = round(ms * 1000.0, 2)  # microseconds in one step
     B.gc_timing_enable(None)
 
-    if args.copy_calibration:
-        a = torch.empty(128 << 20, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    # the measured streaming ceiling: a plain 1 GiB device-to-device copy, best of 5
+    # the measured streaming ceiling: a plain 1 GiB device-to-device copy, best
+    # of 5 (also the reference that scales rocprofv3's byte counters)
     ca = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
     cb = torch.empty_like(ca)
     cb.copy_(ca)
