@@ -176,3 +176,36 @@ def test_dgc_ex_rejects_options_on_the_host():
     for opt, word in cases:
         st = lib.gc_dgc_step_ex(p.handle, fake, fake, fake, ctypes.byref(opt), None, None, 0, None)
         assert st == B.GC_EINVAL and word in B.gc_last_error(), (word, B.gc_last_error())
+
+
+def test_last_error_is_per_thread():
+    """Two host threads fail plan creation for different reasons at the same
+    time: each reads back its own message (the error state is thread-local),
+    and a success in one thread does not clear the other's."""
+    import threading
+
+    lib = B.load()
+    barrier = threading.Barrier(3)
+    seen = {}
+
+    def worker(name, rows, n_total, code):
+        arr = (B.gc_segment * len(rows))(*[B.gc_segment(*r) for r in rows])
+        for _ in range(200):
+            barrier.wait()
+            h = ctypes.c_void_p()
+            st = lib.gc_plan_create(arr, len(rows), n_total, ctypes.byref(h))
+            if st == B.GC_OK:
+                lib.gc_plan_destroy(h)
+            barrier.wait()
+            msg = lib.gc_last_error().decode()
+            if st != code or (code != B.GC_OK and name not in msg) or (code == B.GC_OK and msg):
+                seen.setdefault(name, []).append((st, msg))
+
+    t1 = threading.Thread(target=worker, args=("k must be", [(0, 10, 1, 11, 0)], 10, B.GC_EINVAL))
+    t2 = threading.Thread(target=worker, args=("n_total must be", [(0, 5, 1, 1, 0)], 1 << 32, B.GC_ERANGE))
+    t3 = threading.Thread(target=worker, args=("ok", [(0, 5, 1, 1, 0)], 10, B.GC_OK))
+    for t in (t1, t2, t3):
+        t.start()
+    for t in (t1, t2, t3):
+        t.join()
+    assert not seen, seen
