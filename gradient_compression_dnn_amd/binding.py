@@ -170,10 +170,27 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _f32(t: torch.Tensor, n: int, name: str):
-    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
-        raise ValueError(f"{name}: need a contiguous CUDA float32 tensor of >= {n} elements")
+# The C ABI trusts the sizes it is given; these checks make every pointer the
+# binding passes down a contiguous CUDA tensor of the right type holding at
+# least the elements the call may touch.
+def _dev(t, dtype, n: int, name: str):
+    if not torch.is_tensor(t) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name}: need a contiguous CUDA {str(dtype).replace('torch.', '')} tensor "
+                         f"of >= {n} elements")
     return _ptr(t)
+
+
+def _f32(t: torch.Tensor, n: int, name: str):
+    return _dev(t, torch.float32, n, name)
+
+
+def _ws(ws: torch.Tensor, name: str = "ws"):
+    """A workspace: uint8, so that its element count is its byte count."""
+    return _dev(ws, torch.uint8, 1, name), ws.numel()
+
+
+def _state(state):
+    return ctypes.c_void_p(0) if state is None else _dev(state, torch.uint8, 1, "state")
 
 
 # ---------------------------------------------------------------- plans
@@ -257,6 +274,15 @@ class Sparse:
         return gc_sparse(self.idx.data_ptr(), self.val.data_ptr(), self.seg_off.data_ptr(),
                          self.seg_scale.data_ptr(), self.cap)
 
+    def checked(self, plan: "Plan", name: str = "message") -> gc_sparse:
+        """The struct, after checking that the tensors hold cap entries and
+        the plan's per-segment arrays."""
+        _dev(self.idx, torch.int32, self.cap, f"{name}.idx")
+        _dev(self.val, torch.float32, self.cap, f"{name}.val")
+        _dev(self.seg_off, torch.int32, plan.nseg + 1, f"{name}.seg_off")
+        _dev(self.seg_scale, torch.float32, max(plan.nseg, 1), f"{name}.seg_scale")
+        return self.struct()
+
     def count(self) -> int:
         return int(self.seg_off[-1].item())
 
@@ -273,10 +299,10 @@ def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws:
     """state None: R is the exact residual.  state (Plan.adacomp_state()):
     deferred mode, the residual is (R, state)."""
     n = plan.n_total
-    msg = out.struct()
-    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _ptr(state),
+    msg = out.checked(plan, "out")
+    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _state(state),
                                       state.numel() if state is not None else 0, float(scale_factor),
-                                      ctypes.byref(msg), _ptr(ws), ws.numel(), _stream(R)))
+                                      ctypes.byref(msg), *_ws(ws), _stream(R)))
 
 
 def gc_adacomp_message_cap(plan: Plan) -> int:
@@ -290,7 +316,7 @@ def gc_adacomp_state_bytes(plan: Plan) -> int:
 
 def gc_adacomp_residual(plan: Plan, R, state: torch.Tensor | None, R_out):
     n = plan.n_total
-    _check(load().gc_adacomp_residual(plan.handle, _f32(R, n, "R"), _ptr(state),
+    _check(load().gc_adacomp_residual(plan.handle, _f32(R, n, "R"), _state(state),
                                       state.numel() if state is not None else 0,
                                       _f32(R_out, n, "R_out"), _stream(R_out)))
 
@@ -298,10 +324,10 @@ def gc_adacomp_residual(plan: Plan, R, state: torch.Tensor | None, R_out):
 def gc_dgc_step(plan: Plan, G, U, V, momentum: float, thr_G: float, num_nodes: int, out: Sparse,
                 ws: torch.Tensor):
     n = plan.n_total
-    msg = out.struct()
+    msg = out.checked(plan, "out")
     _check(load().gc_dgc_step(plan.handle, _f32(G, n, "G"), _f32(U, n, "U"), _f32(V, n, "V"),
                               float(momentum), float(thr_G), int(num_nodes), ctypes.byref(msg),
-                              _ptr(ws), ws.numel(), _stream(V)))
+                              *_ws(ws), _stream(V)))
 
 
 def dgc_options(momentum: float, thr_G: float = 0.0, num_nodes: int = 1, nesterov: bool = False,
@@ -318,18 +344,18 @@ def gc_dgc_message_cap(plan: Plan, opt: gc_dgc_options) -> int:
 
 def gc_dgc_step_ex(plan: Plan, G, U, V, opt: gc_dgc_options, out: Sparse, ws: torch.Tensor):
     n = plan.n_total
-    msg = out.struct()
+    msg = out.checked(plan, "out")
     _check(load().gc_dgc_step_ex(plan.handle, _f32(G, n, "G"), _f32(U, n, "U"), _f32(V, n, "V"),
-                                 ctypes.byref(opt), ctypes.byref(msg), _ptr(ws), ws.numel(), _stream(V)))
+                                 ctypes.byref(opt), ctypes.byref(msg), *_ws(ws), _stream(V)))
 
 
 def gc_pack(plan: Plan, kind: int, msg: Sparse, out: torch.Tensor, out_bytes: torch.Tensor,
             ws: torch.Tensor):
     if out.dtype != torch.uint8 or out_bytes.dtype != torch.int64:
         raise ValueError("gc_pack: out must be uint8 and out_bytes int64 (holding u64)")
-    m = msg.struct()
-    _check(load().gc_pack(plan.handle, int(kind), ctypes.byref(m), _ptr(out), out.numel(),
-                          _ptr(out_bytes), _ptr(ws), ws.numel(), _stream(out)))
+    m = msg.checked(plan, "msg")
+    _check(load().gc_pack(plan.handle, int(kind), ctypes.byref(m), _dev(out, torch.uint8, 1, "out"), out.numel(),
+                          _dev(out_bytes, torch.int64, 1, "out_bytes"), *_ws(ws), _stream(out)))
 
 
 def gc_unpack(plan: Plan, kind: int, data: torch.Tensor, nbytes: int, out: Sparse, status: torch.Tensor,
@@ -338,17 +364,17 @@ def gc_unpack(plan: Plan, kind: int, data: torch.Tensor, nbytes: int, out: Spars
     an int32 device tensor (holding u32) that receives the stream's status."""
     if data.dtype != torch.uint8 or data.numel() < nbytes or status.dtype != torch.int32:
         raise ValueError("gc_unpack: data must be uint8 with nbytes bytes, status int32")
-    m = out.struct()
-    _check(load().gc_unpack(plan.handle, int(kind), _ptr(data), int(nbytes), ctypes.byref(m), _ptr(status),
-                            _ptr(ws), ws.numel(), _stream(data)))
+    m = out.checked(plan, "out")
+    _check(load().gc_unpack(plan.handle, int(kind), _dev(data, torch.uint8, nbytes, "data"), int(nbytes), ctypes.byref(m), _dev(status, torch.int32, 1, "status"),
+                            *_ws(ws), _stream(data)))
 
 
 def gc_decompress_accumulate(plan: Plan, msgs, dense, mode: int, accumulate: bool,
                              ws: torch.Tensor):
     K = len(msgs)
-    arr = (gc_sparse * max(K, 1))(*[m.struct() for m in msgs])
+    arr = (gc_sparse * max(K, 1))(*[m.checked(plan, f"msgs[{i}]") for i, m in enumerate(msgs)])
     _check(load().gc_decompress_accumulate(plan.handle, arr, K, _f32(dense, plan.n_total, "dense"),
-                                           int(mode), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                           int(mode), int(bool(accumulate)), *_ws(ws),
                                            _stream(dense)))
 
 
@@ -360,7 +386,7 @@ def gc_dcd_compress(x, x_half, x_out, bits: int, bucket: int, seed: int, step: i
         raise ValueError("gc_dcd_compress: scales or codes too small")
     _check(load().gc_dcd_compress(_f32(x, n, "x"), _f32(x_half, n, "x_half"), _f32(x_out, n, "x_out"),
                                   n, int(bits), int(bucket), int(seed) & (2 ** 64 - 1),
-                                  int(step) & (2 ** 64 - 1), _f32(scales, nb, "scales"), _ptr(codes),
+                                  int(step) & (2 ** 64 - 1), _f32(scales, nb, "scales"), _dev(codes, torch.uint8, (n * bits + 7) // 8, "codes"),
                                   _stream(x_out)))
 
 
@@ -374,7 +400,7 @@ def _codes_check(n: int, bits: int, bucket: int, scales: torch.Tensor, codes: to
 def gc_dcd_decode(scales: torch.Tensor, codes: torch.Tensor, x_hat, bits: int, bucket: int):
     n = x_hat.numel()
     nb = _codes_check(n, bits, bucket, scales, codes, "gc_dcd_decode")
-    _check(load().gc_dcd_decode(_f32(scales, nb, "scales"), _ptr(codes), n, int(bits), int(bucket),
+    _check(load().gc_dcd_decode(_f32(scales, nb, "scales"), _dev(codes, torch.uint8, (n * bits + 7) // 8, "codes"), n, int(bits), int(bucket),
                                 _f32(x_hat, n, "x_hat"), _stream(x_hat)))
 
 
@@ -393,13 +419,13 @@ def gc_ecd_compress(x_prev, x, t: int, bits: int, bucket: int, seed: int, scales
     nb = _codes_check(n, bits, bucket, scales, codes, "gc_ecd_compress")
     _check(load().gc_ecd_compress(_f32(x_prev, n, "x_prev"), _f32(x, n, "x"), n, int(t), int(bits),
                                   int(bucket), int(seed) & (2 ** 64 - 1), _f32(scales, nb, "scales"),
-                                  _ptr(codes), _stream(x)))
+                                  _dev(codes, torch.uint8, (n * bits + 7) // 8, "codes"), _stream(x)))
 
 
 def gc_ecd_update(scales: torch.Tensor, codes: torch.Tensor, x_tilde, t: int, bits: int, bucket: int):
     n = x_tilde.numel()
     nb = _codes_check(n, bits, bucket, scales, codes, "gc_ecd_update")
-    _check(load().gc_ecd_update(_f32(scales, nb, "scales"), _ptr(codes), n, int(bits), int(bucket), int(t),
+    _check(load().gc_ecd_update(_f32(scales, nb, "scales"), _dev(codes, torch.uint8, (n * bits + 7) // 8, "codes"), n, int(bits), int(bucket), int(t),
                                 _f32(x_tilde, n, "x_tilde"), _stream(x_tilde)))
 
 
@@ -411,21 +437,21 @@ def gc_slimdp_core(plan: Plan, w, g, c: float, core: Sparse, core_mask: torch.Te
     n = plan.n_total
     if core_mask.dtype != torch.int32 or core_mask.numel() < gc_slimdp_mask_words(plan):
         raise ValueError("gc_slimdp_core: core_mask must be int32 (holding u32) of gc_slimdp_mask_words words")
-    msg = core.struct()
+    msg = core.checked(plan, "core")
     _check(load().gc_slimdp_core(plan.handle, _f32(w, n, "w"), _f32(g, n, "g"), float(c), ctypes.byref(msg),
-                                 _ptr(core_mask), _ptr(ws), ws.numel(), _stream(core_mask)))
+                                 _dev(core_mask, torch.int32, gc_slimdp_mask_words(plan), "core_mask"), *_ws(ws), _stream(core_mask)))
 
 
 def gc_slimdp_explore(plan: Plan, core_plan: Plan, delta, core_mask: torch.Tensor, seed: int, step: int,
                       out: Sparse, ws: torch.Tensor):
     n = plan.n_total
-    msg = out.struct()
-    _check(load().gc_slimdp_explore(plan.handle, core_plan.handle, _f32(delta, n, "delta"), _ptr(core_mask),
+    msg = out.checked(plan, "out")
+    _check(load().gc_slimdp_explore(plan.handle, core_plan.handle, _f32(delta, n, "delta"), _dev(core_mask, torch.int32, gc_slimdp_mask_words(plan), "core_mask"),
                                     int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), ctypes.byref(msg),
-                                    _ptr(ws), ws.numel(), _stream(delta)))
+                                    *_ws(ws), _stream(delta)))
 
 
 def gc_slimdp_core_values(core_plan: Plan, core: Sparse, delta, values):
-    msg = core.struct()
+    msg = core.checked(core_plan, "core")
     _check(load().gc_slimdp_core_values(core_plan.handle, ctypes.byref(msg), _f32(delta, core_plan.n_total, "delta"),
                                         _f32(values, core_plan.total_k, "values"), _stream(values)))

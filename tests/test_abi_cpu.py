@@ -209,3 +209,19 @@ def test_last_error_is_per_thread():
     for t in (t1, t2, t3):
         t.join()
     assert not seen, seen
+
+
+def test_binding_checks_tensors_before_calling_the_library():
+    """The binding passes only contiguous CUDA tensors of the right type and
+    size: host tensors are refused before anything reaches the C ABI."""
+    import torch
+
+    p = B.Plan(W.make_table([5000, 100], [1, 1], [5, 1]))
+    host = B.Sparse(torch.zeros(6, dtype=torch.int32), torch.zeros(6), torch.zeros(3, dtype=torch.int32),
+                    torch.zeros(2), 6)
+    with pytest.raises(ValueError, match="CUDA"):
+        host.checked(p)
+    x = torch.zeros(5100)
+    with pytest.raises(ValueError, match="need a contiguous CUDA"):
+        B.gc_dgc_step(p, x, x, x, 0.9, 0.0, 1, host, torch.zeros(16, dtype=torch.uint8))
+

@@ -461,5 +461,13 @@ def test_hot_call_errors_leave_buffers_untouched():
         B.gc_dcd_compress(x, x.clone(), x, 4, 500, 0, 0, torch.zeros(1, device="cuda"),
                           torch.zeros(64, dtype=torch.uint8, device="cuda"))
     assert e.value.status == B.GC_ENOTSUP
+    # the binding refuses what the library cannot check: a message whose
+    # tensors hold fewer entries than its cap, a workspace that is not bytes
+    short = B.Sparse(torch.zeros(4, dtype=torch.int32, device="cuda"), torch.zeros(4, device="cuda"),
+                     ok.seg_off, ok.seg_scale, hp.plan.total_k)
+    with pytest.raises(ValueError, match="out.idx"):
+        B.gc_dgc_step(hp.plan, G, U, V, 0.9, 0.0, 1, short, hp.workspace(B.GC_OP_DGC))
+    with pytest.raises(ValueError, match="ws: need a contiguous CUDA uint8"):
+        B.gc_dgc_step(hp.plan, G, U, V, 0.9, 0.0, 1, ok, torch.zeros(1 << 20, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(U, U0) and torch.equal(V, V0)
