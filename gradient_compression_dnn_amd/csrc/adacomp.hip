@@ -113,7 +113,13 @@ __device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const f
 }
 
 // Bin maxima of |G| over the chunk into the LDS array gm (zeroed by the
-// caller, then a barrier), as bit patterns, which order like the values.
+// caller, then a barrier), as bit patterns, which order like the values.  A
+// NaN (pattern above +Inf's) counts as 0: it never raises a bin's max.
+__device__ __forceinline__ uint32_t mag_bits(float v) {
+    const uint32_t m = dev_f2u(v) & 0x7FFFFFFFu;
+    return m > 0x7F800000u ? 0u : m;
+}
+
 __device__ __forceinline__ void chunk_bin_max(const AChunk &a, const float (&g)[kRows][4],
                                               const uint32_t (&bin)[kRows][4], uint32_t *gm) {
 #pragma unroll
@@ -121,7 +127,7 @@ __device__ __forceinline__ void chunk_bin_max(const AChunk &a, const float (&g)[
         const uint32_t e0 = row_elem(j);
         uint32_t mag[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mag[q] = e0 + q < a.cnt ? (dev_f2u(g[j][q]) & 0x7FFFFFFFu) : 0u;
+        for (int q = 0; q < 4; ++q) mag[q] = e0 + q < a.cnt ? mag_bits(g[j][q]) : 0u;
         const uint32_t b_first = __shfl(bin[j][0], 0, kWave);
         const uint32_t b_last = __shfl(bin[j][3], kWave - 1, kWave);
         const uint32_t row0 = e0 - 4u * lane_id();

@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint32_t a = dev_f2u(zv[j][u]) & 0x7FFFFFFFu;
+            if (a > 0x7F800000u) a = 0u;  // a NaN never counts toward the bucket max
             m = a > m ? a : m;
         }
         for (int d = 1; d < lanes_per_bucket; d <<= 1) {
@@ -107,9 +108,11 @@ __global__ __launch_bounds__(kBlock) void dcd_kernel(const float *x,  // may ali
         for (int u = 0; u < 4; ++u) {
             uint32_t level = 0;
             const float z = zv[j][u];
-            if (sb > 0.0f) {
-                float y = fabsf(z) * inv;
-                if (y > Lf) y = Lf;
+            float y = sb > 0.0f ? fabsf(z) * inv : 0.0f;
+            if (y > Lf) y = Lf;
+            // a NaN difference, and every difference in a bucket whose max is
+            // infinite (|z| * 0), quantizes to level 0
+            if (sb > 0.0f && y == y) {
                 const float l0 = floorf(y);
                 const float f = y - l0;
                 const float uu = static_cast<float>(words[u] >> 8) * 0x1p-24f;

@@ -79,7 +79,8 @@ static void adacomp_segment(const orc_seg *sg, const float *dW, float *R,
     /* residual + gradient */
     for (uint32_t i = 0; i < n; ++i) G[i] = R[base + i] + dW[base + i];
 
-    /* bin maxima; bins restart at the segment start, the last may be short */
+    /* bin maxima; bins restart at the segment start, the last may be short;
+     * a NaN never compares greater, so it does not count toward a maximum */
     for (uint32_t b = 0; b < nb; ++b) {
         float mx = 0.0f;
         uint32_t lo = b * L, hi = lo + L < n ? lo + L : n;
@@ -596,16 +597,18 @@ static void quantize(const float *z, uint64_t n, int bits, uint32_t bucket, uint
         float sb = 0.0f;
         for (uint64_t i = lo; i < hi; ++i) {
             float a = fabsf(z[i]);
-            if (a > sb) sb = a;
+            if (a > sb) sb = a; /* a NaN never counts toward the bucket max */
         }
         scales[b] = sb;
         float inv = sb > 0.0f ? Lf / sb : 0.0f;
         float stepq = sb > 0.0f ? sb / Lf : 0.0f;
         for (uint64_t i = lo; i < hi; ++i) {
             uint32_t level = 0;
-            if (sb > 0.0f) {
-                float y = fabsf(z[i]) * inv;
-                if (y > Lf) y = Lf;
+            float y = sb > 0.0f ? fabsf(z[i]) * inv : 0.0f;
+            if (y > Lf) y = Lf;
+            /* a NaN difference, and every difference in a bucket whose max is
+             * infinite (|z| * 0), quantizes to level 0 */
+            if (sb > 0.0f && !isnan(y)) {
                 float l0 = floorf(y);
                 float f = y - l0;
                 uint64_t q = i / 4;
