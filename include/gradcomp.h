@@ -38,8 +38,14 @@
  *    single correctly rounded IEEE operation in a fixed order (no FMA
  *    contraction), and every reduction that feeds a decision uses a fixed
  *    pairwise tree (see gc_dgc_step and gc_adacomp_compress).
- *  - Inputs must be finite.  NaN or Inf gives unspecified selections but never
- *    an out-of-bounds access.
+ *  - Non-finite inputs have defined results.  A NaN never counts toward a
+ *    maximum (an AdaComp bin's, a DCD bucket's), is never selected by
+ *    AdaComp (it stays in the residual) and quantizes to level 0 in DCD.
+ *    +-Inf are magnitudes above every finite one: an Inf is its bin's
+ *    maximum, and a DCD bucket whose maximum is Inf sends only level 0.  DGC
+ *    ranks by the magnitude bits, where a NaN ranks above +Inf.  Every other
+ *    step is the IEEE operation as written; NaNs that arithmetic makes carry
+ *    no guaranteed sign or payload.
  *  - Input, state and output buffers must not alias each other (except
  *    x_out == x in gc_dcd_compress).
  *  - Calls on different streams are independent as long as they use
