@@ -72,6 +72,8 @@ def lib():
         L.orc_philox4x32_10.argtypes = [P, P, P]
         L.orc_dcd.argtypes = [P, P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                               ctypes.c_uint64, ctypes.c_uint64, P, P]
+        L.orc_dcd_window.argtypes = [P, P, P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
+                                     ctypes.c_uint64, ctypes.c_uint64, P, P]
         L.orc_dcd_decode.argtypes = [P, P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32, P]
         L.orc_dcd_mix.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, P, ctypes.c_uint64]
         L.orc_ecd_compress.argtypes = [P, P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
@@ -248,6 +250,23 @@ def dcd(x, x_half, bits=4, bucket=512, seed=0, step=0):
     lib().orc_dcd(_ptr(x), _ptr(xh), _ptr(xo), n, int(bits), int(bucket), int(seed) & (2**64 - 1),
                   int(step) & (2**64 - 1), _ptr(scales), _ptr(codes))
     return xo, scales[:(n + bucket - 1) // bucket], codes[:(n * bits + 7) // 8]
+
+
+def dcd_window(x, x_half, base, bits=4, bucket=512, seed=0, step=0):
+    """dcd() for elements [base, base + len(x)) of a longer model (base a
+    multiple of bucket): buckets and Philox counters follow the model's
+    indices.  Returns (x_out, scales, codes) of the window."""
+    if base % bucket:
+        raise ValueError("base must be a multiple of bucket")
+    x = _f32(x)
+    xh = _f32(x_half)
+    m = x.size
+    xo = np.empty(m, np.float32)
+    scales = np.zeros(max((m + bucket - 1) // bucket, 1), np.float32)
+    codes = np.zeros(max((m * bits + 7) // 8, 1), np.uint8)
+    lib().orc_dcd_window(_ptr(x), _ptr(xh), _ptr(xo), m, int(base), int(bits), int(bucket),
+                         int(seed) & (2**64 - 1), int(step) & (2**64 - 1), _ptr(scales), _ptr(codes))
+    return xo, scales[:(m + bucket - 1) // bucket], codes[:(m * bits + 7) // 8]
 
 
 def dcd_decode(scales, codes, x_hat, bits=4, bucket=512):

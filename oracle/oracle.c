@@ -581,8 +581,11 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
  * bits: unbiased stochastic rounding to a uniform grid whose top level is the
  * bucket's max magnitude.  C_out[i] receives C(z)_i.
  */
-static void quantize(const float *z, uint64_t n, int bits, uint32_t bucket, uint64_t seed,
-                     uint64_t step, float *scales, uint8_t *codes, float *C_out)
+/* Random quantization of z[0..n), element i being element base + i of the
+ * model (base a multiple of the bucket): buckets and the Philox counter
+ * follow the model's indices. */
+static void quantize(const float *z, uint64_t n, uint64_t base, int bits, uint32_t bucket,
+                     uint64_t seed, uint64_t step, float *scales, uint8_t *codes, float *C_out)
 {
     const uint32_t L = (1u << (bits - 1)) - 1u;
     const float Lf = (float)L;
@@ -611,12 +614,12 @@ static void quantize(const float *z, uint64_t n, int bits, uint32_t bucket, uint
             if (sb > 0.0f && !isnan(y)) {
                 float l0 = floorf(y);
                 float f = y - l0;
-                uint64_t q = i / 4;
+                uint64_t q = (base + i) / 4;
                 uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)step,
                                    (uint32_t)(step >> 32)};
                 uint32_t r[4];
                 orc_philox4x32_10(ctr, key, r);
-                float u = (float)(r[i % 4] >> 8) * 0x1p-24f;
+                float u = (float)(r[(base + i) % 4] >> 8) * 0x1p-24f;
                 level = (uint32_t)l0 + (u < f ? 1u : 0u);
             }
             float C = 0.0f;
@@ -656,17 +659,24 @@ static float dequantize(const float *scales, const uint8_t *codes, uint64_t i, i
 /*
  * DCD-PSGD (Tang et al.) step 2: z = x_{t+1/2} - x_t, x_{t+1} = x_t + C(z).
  */
+void orc_dcd_window(const float *x, const float *x_half, float *x_out, uint64_t m, uint64_t base,
+                    int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+                    float *scales, uint8_t *codes)
+{
+    float *z = (float *)calloc(m ? m : 1, sizeof(float));
+    float *C = (float *)calloc(m ? m : 1, sizeof(float));
+    for (uint64_t i = 0; i < m; ++i) z[i] = x_half[i] - x[i];
+    quantize(z, m, base, bits, bucket, seed, step, scales, codes, C);
+    for (uint64_t i = 0; i < m; ++i) x_out[i] = x[i] + C[i];
+    free(z);
+    free(C);
+}
+
 void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
              int bits, uint32_t bucket, uint64_t seed, uint64_t step,
              float *scales, uint8_t *codes)
 {
-    float *z = (float *)calloc(n ? n : 1, sizeof(float));
-    float *C = (float *)calloc(n ? n : 1, sizeof(float));
-    for (uint64_t i = 0; i < n; ++i) z[i] = x_half[i] - x[i];
-    quantize(z, n, bits, bucket, seed, step, scales, codes, C);
-    for (uint64_t i = 0; i < n; ++i) x_out[i] = x[i] + C[i];
-    free(z);
-    free(C);
+    orc_dcd_window(x, x_half, x_out, n, 0, bits, bucket, seed, step, scales, codes);
 }
 
 /*
@@ -713,7 +723,7 @@ void orc_ecd_compress(const float *x_prev, const float *x, uint64_t n, uint64_t 
         float q = b * x[i];
         z[i] = p + q;
     }
-    quantize(z, n, bits, bucket, seed, t, scales, codes, C);
+    quantize(z, n, 0, bits, bucket, seed, t, scales, codes, C);
     free(z);
     free(C);
 }

@@ -95,6 +95,12 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
 void orc_dcd(const float *x, const float *x_half, float *x_out, uint64_t n,
              int bits, uint32_t bucket, uint64_t seed, uint64_t step,
              float *scales, uint8_t *codes);
+/* orc_dcd for the window [base, base + m) of a longer model: x, x_half,
+ * x_out, scales and codes hold the window's elements and buckets; base is a
+ * multiple of the bucket, and Philox counters use the model's indices. */
+void orc_dcd_window(const float *x, const float *x_half, float *x_out, uint64_t m, uint64_t base,
+                    int bits, uint32_t bucket, uint64_t seed, uint64_t step,
+                    float *scales, uint8_t *codes);
 
 /* DCD-PSGD step 3: x_hat <- x_hat + C(z) from codes and scales. */
 void orc_dcd_decode(const float *scales, const uint8_t *codes, uint64_t n, int bits,

@@ -230,3 +230,57 @@ def test_dgc_on_the_longest_segment_by_its_properties():
     nz = sum(int(torch.count_nonzero(dense[base + a:base + b])) for a, b in slices)
     assert nz == int(torch.count_nonzero(vals))
     assert bool((dense[:base] == 3.0).all())  # before the segment: untouched
+
+
+def test_dcd_decode_and_mix_at_the_largest_n():
+    """DCD over the largest n the calls accept (2^32 - 8192, indices and
+    Philox counters up to the top of the u32 range): windows at the start,
+    in the middle and at the very end against the oracle's window form; then
+    the replica decode of the same codes in place, and a two-replica mix,
+    on the same windows."""
+    n = (1 << 32) - 8192
+    bucket, m = 512, 8192
+    SL = 1 << 28
+    gen = torch.Generator(device="cuda").manual_seed(93)
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    xh = torch.empty_like(x)
+    say("max-n dcd: inputs")
+    for a in range(0, n, SL):
+        b = min(a + SL, n)
+        x[a:b] = torch.randn(b - a, generator=gen, device="cuda") * 0.05
+        xh[a:b] = x[a:b] - 0.1 * (torch.randn(b - a, generator=gen, device="cuda") * 1e-3)
+    bases = (0, 2_000_003 * bucket, n - m)
+    host = {base: (x[base:base + m].cpu().numpy(), xh[base:base + m].cpu().numpy()) for base in bases}
+    xo = torch.empty_like(x)
+    for bits_ in (4, 8):
+        say(f"max-n dcd compress bits={bits_}")
+        scales = torch.zeros(n // bucket, dtype=torch.float32, device="cuda")
+        codes = torch.zeros(n * bits_ // 8, dtype=torch.uint8, device="cuda")
+        B.gc_dcd_compress(x, xh, xo, bits_, bucket, 0x5EED, 3, scales, codes)
+        torch.cuda.synchronize()
+        want = {}
+        for base in bases:
+            hx, hh = host[base]
+            wo, ws, wc = oracle.dcd_window(hx, hh, base, bits_, bucket, seed=0x5EED, step=3)
+            want[base] = (ws, wc)
+            assert same_bits(xo[base:base + m].cpu().numpy(), wo)
+            assert same_bits(scales[base // bucket:(base + m) // bucket].cpu().numpy(), ws)
+            assert np.array_equal(codes[base * bits_ // 8:(base + m) * bits_ // 8].cpu().numpy(), wc)
+        say(f"max-n dcd decode bits={bits_}")
+        xr = xh.clone()  # a replica that receives the codes
+        B.gc_dcd_decode(scales, codes, xr, bits_, bucket)
+        torch.cuda.synchronize()
+        for base in bases:
+            ws, wc = want[base]
+            assert same_bits(xr[base:base + m].cpu().numpy(), oracle.dcd_decode(ws, wc, host[base][1], bits_, bucket))
+        del xr, scales, codes
+        pygc.collect()
+        torch.cuda.empty_cache()
+    say("max-n dcd mix")
+    out = torch.empty_like(x)
+    B.gc_dcd_mix([x, xh], [0.25, 0.75], xo, 0.1, out)
+    torch.cuda.synchronize()
+    for base in bases:
+        hx, hh = host[base]
+        got = out[base:base + m].cpu().numpy()
+        assert same_bits(got, oracle.dcd_mix([hx, hh], [0.25, 0.75], xo[base:base + m].cpu().numpy(), 0.1))

@@ -243,6 +243,40 @@ def test_dcd_uses_documented_counter_layout():
         assert codes[i] == (64 if u < 0.5 else 63)  # level 63 + (u < f); sign +
 
 
+def test_dcd_windows_tile_the_whole_call():
+    # windows at bucket-aligned bases, concatenated, equal the call over the
+    # whole buffer (buckets and counters follow the model's indices)
+    rng = np.random.default_rng(12)
+    n = 10_000
+    x = rng.normal(0, 0.05, n).astype(np.float32)
+    xh = (x - np.float32(0.1) * rng.normal(0, 1e-3, n).astype(np.float32)).astype(np.float32)
+    for bits in (4, 8):
+        xo, sc, cd = oracle.dcd(x, xh, bits, 512, seed=5, step=9)
+        parts = [oracle.dcd_window(x[a:b], xh[a:b], a, bits, 512, seed=5, step=9)
+                 for a, b in ((0, 2048), (2048, 6144), (6144, n))]
+        assert np.array_equal(np.concatenate([p[0] for p in parts]), xo)
+        assert np.array_equal(np.concatenate([p[1] for p in parts]), sc)
+        assert np.array_equal(np.concatenate([p[2] for p in parts]), cd)
+
+
+def test_dcd_window_counters_at_high_indices():
+    # element base + i draws word ((base + i) mod 4) of philox(counter =
+    # ((base + i)/4 lo, hi, step lo, step hi)), at the top of the u32 range
+    # and past it (the high counter word)
+    for base in ((1 << 32) - 8192, 1 << 34):
+        n = 16
+        x = np.zeros(n, np.float32)
+        xh = np.full(n, 0.5, np.float32)
+        xh[0] = 1.0
+        seed, step = 0xDEAD_BEEF_0BAD_F00D, 41
+        _, _, codes = oracle.dcd_window(x, xh, base, 8, 16, seed=seed, step=step)
+        key = [seed & 0xFFFFFFFF, seed >> 32]
+        for i in range(1, n):
+            q = (base + i) // 4
+            r = oracle.philox4x32_10([q & 0xFFFFFFFF, q >> 32, step, 0], key)[(base + i) % 4]
+            assert codes[i] == (64 if (int(r) >> 8) / 2 ** 24 < 0.5 else 63)
+
+
 def test_workload_sizes_match_pages():
     # DGC abstract: ResNet-50 gradients of 97 MB (MiB of fp32), DeepSpeech 488 MB
     r = W.make_config("resnet50")
