@@ -284,3 +284,48 @@ def test_dcd_decode_and_mix_at_the_largest_n():
         hx, hh = host[base]
         got = out[base:base + m].cpu().numpy()
         assert same_bits(got, oracle.dcd_mix([hx, hh], [0.25, 0.75], xo[base:base + m].cpu().numpy(), 0.1))
+
+
+def test_slimdp_at_the_top_of_the_range():
+    """Slim-DP's core (significance top-k, bitmap), explorer and values-only
+    push on segments at the top of the u32 index range, against the oracle on
+    the same segments rebased to a small window (the explorer's keys follow
+    segment-relative positions, so they do not move with the offset)."""
+    local, top, base, window = layouts()
+    tc, te = local.copy(), local.copy()
+    tc[:, 3] = np.maximum(1, tc[:, 1] // 10)
+    te[:, 3] = np.maximum(1, np.minimum(tc[:, 1] // 10, tc[:, 1] - tc[:, 3]))
+    ttc, tte = tc.copy(), te.copy()
+    ttc[:, 0] += base
+    tte[:, 0] += base
+    core_plan, exp_plan = B.Plan(ttc, N_TOTAL), B.Plan(tte, N_TOTAL)
+    rng = np.random.default_rng(79)
+    w, g, d = (W.random_values(rng, window, "laplace") for _ in range(3))
+    wd, gd, dd = big(), big(), big()
+    put(wd, base, w)
+    put(gd, base, g)
+    put(dd, base, d)
+    ws = core_plan.workspace(B.GC_OP_DGC, "cuda")
+    mask = torch.zeros(B.gc_slimdp_mask_words(core_plan), dtype=torch.int32, device="cuda")
+    say("max-index slimdp core")
+    core = B.Sparse.empty(core_plan, core_plan.total_k, "cuda")
+    B.gc_slimdp_core(core_plan, wd, gd, 1.5, core, mask, ws)
+    torch.cuda.synchronize()
+    cidx, cval, coff, cmask = oracle.slimdp_core(tc, w, g, 1.5)
+    gi, gv, go, _ = core.host()
+    assert np.array_equal(go, coff) and np.array_equal(gi.astype(np.int64), cidx.astype(np.int64) + base)
+    assert same_bits(gv, cval)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), cmask)
+    say("max-index slimdp explore")
+    out = B.Sparse.empty(exp_plan, exp_plan.total_k, "cuda")
+    B.gc_slimdp_explore(exp_plan, core_plan, dd, mask, 1234, 5, out, ws)
+    torch.cuda.synchronize()
+    eidx, evals, eoff = oracle.slimdp_explore(te, d, cmask, 1234, 5)
+    xi, xv, xo, _ = out.host()
+    assert np.array_equal(xo, eoff) and np.array_equal(xi.astype(np.int64), eidx.astype(np.int64) + base)
+    assert same_bits(xv, evals)
+    say("max-index slimdp core values")
+    vals = torch.zeros(core_plan.total_k, dtype=torch.float32, device="cuda")
+    B.gc_slimdp_core_values(core_plan, core, dd, vals)
+    torch.cuda.synchronize()
+    assert same_bits(vals.cpu().numpy(), d[cidx])
