@@ -73,42 +73,112 @@ __device__ __forceinline__ uint64_t block_bytes(uint64_t E, bool dgc) {
     return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0);
 }
 
-// One workgroup.  Thread 0 follows the headers (a chain of dependent loads);
-// then the workgroup lays out the tiles.
+// One block header read at `at` by one thread, with the checks of the
+// sequential walk: on a bad header the block counts as empty (E = 0) and st
+// gets kBadBlock; once st is set no header is read.  Returns the block's
+// bytes.
+__device__ __forceinline__ uint64_t walk_one(const PlanDev &P, bool dgc, uint32_t MAX, uint32_t bmagic,
+                                             const uint8_t *in, uint64_t nbytes, int s, uint64_t at, uint32_t &st,
+                                             UnpackWs &w, float *seg_scale) {
+    uint32_t E = 0, w3 = 0;
+    if (!st && at + 16 <= nbytes) {
+        const uint32_t *b = reinterpret_cast<const uint32_t *>(in + at);
+        const uint32_t m = b[0], n = b[1];
+        E = b[2];
+        w3 = b[3];
+        if (m != bmagic || n != P.seg[s].len || E > max_codes(n, MAX) || at + block_bytes(E, dgc) > nbytes) {
+            st |= kBadBlock;
+            E = 0;
+        }
+    } else if (!st) {
+        st |= kBadBlock;
+    }
+    w.blk_off[s] = at;
+    w.seg_E[s] = E;
+    w.seg_w3[s] = w3;
+    if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(w3);
+    return block_bytes(E, dgc);
+}
+
+// One workgroup; the headers are a chain (each block's size comes from its
+// own header), then the workgroup lays out the tiles.  AdaComp: thread 0
+// follows the chain.  DGC: a block normally holds exactly k_s codes (an
+// escape needs a gap of 65535 unsent elements), so wave 0 predicts the next
+// 64 headers' offsets from k, reads them at once, and keeps the prefix whose
+// headers are valid with E = k (what the sequential walk computes for them);
+// the first block that differs is read at its now known offset by the
+// sequential rule, and the next round predicts from there.
 __global__ __launch_bounds__(kBlock) void unpack_walk_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
                                                              uint64_t nbytes, UnpackWs w, float *seg_scale,
                                                              uint32_t *status) {
     const bool dgc = kind == GC_KIND_DGC;
     const uint32_t MAX = dgc ? 65535u : 32767u;
-    if (threadIdx.x == 0) {
+    const uint32_t bmagic = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
+    if (threadIdx.x < kWave) {
+        const int lane = lane_id();
         uint32_t st = 0;
         const uint32_t *h = reinterpret_cast<const uint32_t *>(in);
         if (nbytes < 16 || h[0] != magic('G', 'C', 'P', '1') || h[1] != uint32_t(kind) || h[2] != uint32_t(P.nseg))
             st |= kBadStream;
-        const uint32_t bmagic = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
         uint64_t at = 16;
-        for (int s = 0; s < P.nseg; ++s) {
-            uint32_t E = 0, w3 = 0;
-            if (!st && at + 16 <= nbytes) {
-                const uint32_t *b = reinterpret_cast<const uint32_t *>(in + at);
-                const uint32_t m = b[0], n = b[1];
-                E = b[2];
-                w3 = b[3];
-                if (m != bmagic || n != P.seg[s].len || E > max_codes(n, MAX) || at + block_bytes(E, dgc) > nbytes) {
-                    st |= kBadBlock;
-                    E = 0;
+        if (!dgc) {
+            if (lane == 0)
+                for (int s = 0; s < P.nseg; ++s) at += walk_one(P, dgc, MAX, bmagic, in, nbytes, s, at, st, w, seg_scale);
+        } else {
+            int s = 0;
+            while (s < P.nseg && !st) {
+                const int sl = s + lane;
+                const bool live = sl < P.nseg;
+                const uint32_t k = live ? P.seg[sl].k : 0u;
+                const uint32_t len = live ? P.seg[sl].len : 0u;
+                const uint64_t sz = live ? block_bytes(k, true) : 0;
+                uint64_t incl = sz;  // inclusive scan of the predicted sizes
+#pragma unroll
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const uint64_t y = __shfl_up(incl, d, kWave);
+                    if (lane >= d) incl += y;
                 }
-            } else if (!st) {
-                st |= kBadBlock;
+                const uint64_t my_at = at + incl - sz;
+                bool ok = false;
+                uint32_t w3 = 0;
+                if (live && my_at + 16 <= nbytes) {
+                    const uint32_t *b = reinterpret_cast<const uint32_t *>(in + my_at);
+                    w3 = b[3];
+                    ok = b[0] == bmagic && b[1] == len && b[2] == k && my_at + sz <= nbytes;
+                }
+                const uint64_t bad = __ballot(live && !ok);
+                const int nlive = P.nseg - s < kWave ? P.nseg - s : kWave;
+                const int f = bad ? __ffsll(static_cast<long long>(bad)) - 1 : nlive;  // confirmed blocks
+                if (lane < f) {
+                    w.blk_off[sl] = my_at;
+                    w.seg_E[sl] = k;
+                    w.seg_w3[sl] = w3;
+                    if (seg_scale) seg_scale[sl] = 0.0f;
+                }
+                if (f > 0) at = __shfl(my_at + sz, f - 1, kWave);
+                s += f;
+                if (f < nlive) {
+                    // block s differs from the prediction: the sequential rule
+                    uint64_t add = 0;
+                    if (lane == 0) add = walk_one(P, dgc, MAX, bmagic, in, nbytes, s, at, st, w, seg_scale);
+                    at += __shfl(add, 0, kWave);
+                    st = __shfl(st, 0, kWave);
+                    ++s;
+                }
             }
-            w.blk_off[s] = at;
-            w.seg_E[s] = E;
-            w.seg_w3[s] = w3;
-            if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(w3);
-            at += block_bytes(E, dgc);
+            // after a bad block the rest are read as empty, as in the sequential walk
+            for (int r = s + lane; r < P.nseg; r += kWave) {
+                w.blk_off[r] = at + 16ull * uint64_t(r - s);
+                w.seg_E[r] = 0;
+                w.seg_w3[r] = 0;
+                if (seg_scale) seg_scale[r] = 0.0f;
+            }
+            if (s < P.nseg) at += 16ull * uint64_t(P.nseg - s);
         }
-        if (!st && at != nbytes) st |= kBadBlock;
-        *status = st;
+        if (lane == 0) {
+            if (!st && at != nbytes) st |= kBadBlock;
+            *status = st;
+        }
     }
     __syncthreads();
     uint32_t run = 0;

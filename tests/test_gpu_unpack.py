@@ -140,3 +140,59 @@ def test_deepspeech_streams_decode_like_their_messages():
         want = hp.decode([msg], B.GC_AVG)
         got = hp.decode([out], B.GC_AVG)
         assert same_bits(got, want), ulp_report(got, want)
+
+
+def _block_offsets(data: bytes, nseg: int, dgc: bool):
+    """Offsets of the blocks of a well-formed stream (a host-side walk of the
+    documented layout)."""
+    at, offs = 16, []
+    for _ in range(nseg):
+        offs.append(at)
+        E = struct.unpack_from("<I", data, at + 8)[0]
+        at += 16 + 2 * E + 2 * (E & 1) + (4 * E if dgc else 0)
+    return offs
+
+
+def test_dgc_streams_with_many_segments():
+    """300 segments (the DGC header walk confirms up to 64 predicted blocks per
+    round): long sparse segments with escapes among ordinary ones, read back
+    exactly; then a bad block magic and a wrong code count past the first
+    round set the status and keep every write inside the message."""
+    rng = np.random.default_rng(333)
+    lengths = [int(rng.choice([int(rng.integers(1, 3000)), int(rng.integers(70_000, 400_000))])) for _ in range(300)]
+    ks = [max(1, n // int(rng.choice([10, 1000, 50_000]))) for n in lengths]
+    t = W.make_table(lengths, [1] * 300, ks, [int(rng.integers(0, 3)) for _ in lengths])
+    plan = B.Plan(t)
+    parts, offs, pos = [], [0], 0
+    for o, ln, _, k in t:
+        parts.append(np.sort(rng.choice(ln, int(k), replace=False)) + o)
+        pos += int(k)
+        offs.append(pos)
+    idx = np.concatenate(parts).astype(np.uint32)
+    val = W.random_values(rng, idx.size, "laplace")
+    data = oracle.pack(1, t, idx, val, offs)
+    escapes = sum(1 for o, ln, _, k in t if ln > 65535 and k < 5)
+    assert escapes > 0  # some blocks hold more codes than entries
+    say("unpack dgc 300 segments")
+    st, out, tail_ok = gpu_unpack(plan, 1, data, idx.size)
+    assert st == 0 and tail_ok
+    gi, gv, go, _ = host_msg(out, len(t))
+    assert np.array_equal(gi, idx) and np.array_equal(go, np.array(offs, np.uint32)) and same_bits(gv, val)
+    blocks = _block_offsets(data, len(t), True)
+    bad_magic = bytearray(data)
+    bad_magic[blocks[130]:blocks[130] + 4] = b"XXXX"
+    bad_count = bytearray(data)
+    E70 = struct.unpack_from("<I", data, blocks[70] + 8)[0]
+    struct.pack_into("<I", bad_count, blocks[70] + 8, E70 + 1)
+    for name, bad in (("block 130 magic", bytes(bad_magic)), ("block 70 count", bytes(bad_count))):
+        say(f"unpack dgc 300 segments, {name}")
+        st, out, tail_ok = gpu_unpack(plan, 1, bad, idx.size)
+        assert st != 0 and tail_ok, name
+        assert oracle.unpack(1, t, bad)[0] != 0, name
+        gi, _, go, _ = host_msg(out, len(t))
+        assert np.all(np.diff(go.astype(np.int64)) >= 0) and go[-1] <= idx.size, name
+        written = gi[gi != 0xFFFFFFFF].astype(np.int64)
+        inseg = np.zeros(int(t[-1, 0] + t[-1, 1]), bool)
+        for o, ln, _, _ in t:
+            inseg[o:o + ln] = True
+        assert np.all(inseg[written]), name
