@@ -6,8 +6,9 @@
 // messages are added in array order (bitwise deterministic without float
 // atomics):
 //   index   for every message and every 4096-element chunk, the first entry
-//           at or after the chunk (entries are ascending, so a chunk's entries
-//           are [start[c], start[c+1]))
+//           at or after the chunk, by bisection in its segment's entries
+//           (entries are ascending, so a chunk's entries are
+//           [start[c], start[c+1]))
 //   decode  one workgroup per chunk: for k = 0..K-1 scatter message k's
 //           entries of the chunk into an LDS accumulator (one owner per
 //           element within a message), barrier; then divide by K and write
@@ -43,106 +44,38 @@ DecWs dec_layout(const gc_plan *p, void *base, size_t *bytes) {
     return w;
 }
 
-// Walks ascending flat indices forward through the segments, keeping the
-// current segment's bounds in registers; the table of segment starts is read
-// from LDS when it fits.  Out-of-range or descending indices are clamped
-// into the plan (malformed input stays in bounds).
-constexpr int kLdsSegs = 4096;
-
-struct SegCursor {
-    const PlanDev *P;
-    const uint32_t *start;  // segment starts (LDS copy or plan table)
-    int s;
-    uint64_t off, next;
-    uint32_t dchunk0, dnchunk;
-    __device__ uint64_t seg_start(int i) const {
-        return start ? uint64_t(start[i]) : P->seg_start[i];
-    }
-    __device__ void load(int seg) {
-        s = seg;
-        const SegDev d = P->seg[s];
-        off = d.off;
-        dchunk0 = d.dchunk0;
-        dnchunk = d.dnchunk;
-        next = s + 1 < P->nseg ? seg_start(s + 1) : ~uint64_t(0);
-    }
-    __device__ void find(uint32_t i) {
-        int lo = 0, hi = P->nseg - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) / 2;
-            if (seg_start(mid) <= i) lo = mid;
-            else hi = mid - 1;
-        }
-        load(lo);
-    }
-    __device__ uint32_t chunk(uint32_t i) {
-        if (i >= next) {
-            int t = s;
-            while (t + 1 < P->nseg && seg_start(t + 1) <= i) ++t;
-            load(t);
-        }
-        uint64_t rel = i >= off ? (i - off) >> kChunkLog2 : 0;
-        if (rel >= dnchunk) rel = dnchunk - 1;
-        return dchunk0 + static_cast<uint32_t>(rel);
-    }
-};
-
-constexpr uint32_t kRun = 8;           // entries per thread in the index pass
 constexpr uint32_t kSparseChunk = 32;  // up to this many entries: no LDS accumulator
 
-// start[k][c] = first entry of message k at or after chunk c: entry j (0..n)
-// writes it for every chunk c with chunk(idx[j-1]) < c <= chunk(idx[j]),
-// taking chunk(idx[-1]) = -1 and chunk(idx[n]) = ndchunk.  For ascending
-// indices those intervals tile 0..ndchunk, so every start[k][c] is written,
-// with a value in [0, count_k].  The cursor's clamping makes chunk() depend
-// on the walk for descending indices, which may leave a start unwritten; the
-// decode pass clamps what it reads to count_k, so that input still stays in
-// bounds.  The grid is
-// bounded and strides over the entries, since the host sizes it from the
-// capacity, not from the (device-resident) count.
+// start[k][c] = first entry of message k at or after chunk c.  Chunk c lies
+// in segment s, whose entries are [seg_off[s], seg_off[s+1]) of the message,
+// ascending: start is the first of them at or after the chunk's first
+// element, a lower bound by bisection, and start[k][ndchunk] = count_k.  One
+// thread per chunk and message; the searches of a segment share their upper
+// levels in cache, and the pass reads a few lines per chunk instead of every
+// entry.  For a message that breaks the layout (descending indices, offsets
+// past the count) the starts are still in [0, count_k], clamped, and the
+// decode pass clamps each range it reads to count_k.
 __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTable m, DecWs w) {
     const int k = blockIdx.y;
+    const uint32_t c = blockIdx.x * kBlock + threadIdx.x;
+    if (c > P.ndchunk) return;
     const uint32_t n = msg_count(m, k);
-    const uint64_t stride = uint64_t(gridDim.x) * kBlock * kRun;
-    if (uint64_t(blockIdx.x) * kBlock * kRun > n) return;
-    __shared__ uint32_t starts[kLdsSegs];
-    const bool in_lds = P.nseg <= kLdsSegs;
-    if (in_lds) {
-        for (int i = threadIdx.x; i < P.nseg; i += kBlock) starts[i] = static_cast<uint32_t>(P.seg_start[i]);
-        __syncthreads();
-    }
-    const uint32_t *idx = m.idx[k];
     uint32_t *start = w.start + size_t(k) * (P.ndchunk + 1);
-    if (n == 0) {  // no entries (only workgroup 0 is left): every chunk starts at 0
-        for (uint32_t c = threadIdx.x; c <= P.ndchunk; c += kBlock) start[c] = 0u;
+    if (c == P.ndchunk) {
+        start[c] = n;
         return;
     }
-    SegCursor walk;
-    walk.P = &P;
-    walk.start = in_lds ? starts : nullptr;
-    // entries j = base + q * kBlock (q < kRun) per thread: coalesced loads of
-    // idx[j] and idx[j - 1], all issued before the walk; a thread's indices
-    // ascend, so one cursor walks forward through the segments
-    for (uint64_t base = uint64_t(blockIdx.x) * kBlock * kRun + threadIdx.x; base <= n; base += stride) {
-        uint32_t cur[kRun], prv[kRun];
-        const uint64_t last = n - 1;
-#pragma unroll
-        for (uint32_t q = 0; q < kRun; ++q) {
-            const uint64_t j = base + uint64_t(q) * kBlock;
-            const uint64_t jp = j > 0 ? j - 1 : 0;
-            cur[q] = idx[j < last ? j : last];
-            prv[q] = idx[jp < last ? jp : last];
-        }
-        walk.find(base > 0 ? prv[0] : cur[0]);
-#pragma unroll
-        for (uint32_t q = 0; q < kRun; ++q) {
-            const uint64_t j = base + uint64_t(q) * kBlock;
-            if (j > n) break;
-            const int64_t cp = j > 0 ? int64_t(walk.chunk(prv[q])) : -1;
-            const int64_t cj = j < n ? int64_t(walk.chunk(cur[q])) : int64_t(P.ndchunk);
-            for (int64_t c = cp + 1; c <= cj; ++c) start[c] = static_cast<uint32_t>(j);
-        }
+    const ChunkRec rec = P.dchunk_rec[c];
+    const uint32_t *seg_off = m.count[k] - P.nseg;
+    uint32_t lo = min(seg_off[rec.z], n), hi = min(seg_off[rec.z + 1], n);
+    if (hi < lo) hi = lo;
+    const uint32_t *idx = m.idx[k];
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (idx[mid] < rec.x) lo = mid + 1;
+        else hi = mid;
     }
+    start[c] = lo;
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
@@ -323,13 +256,8 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     gc_status st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     DecWs w = dec_layout(plan, ws, nullptr);
-    uint64_t max_entries = 0;
-    for (int k = 0; k < K; ++k) max_entries = std::max<uint64_t>(max_entries, msgs[k].cap);
-    // one pass: enough workgroups for the largest capacity (extra ones exit)
-    const uint64_t need_x = (max_entries + kBlock * kRun) / (kBlock * kRun) + 1;
-    const uint64_t cap_x = std::max<uint64_t>(64, uint64_t(16384) / uint64_t(K));
-    unsigned gx = static_cast<unsigned>(std::min(need_x, cap_x));
-    GC_LAUNCH("decode_index", stream, decode_index_kernel<<<dim3(gx, K), kBlock, 0, stream>>>(P, m, w));
+    GC_LAUNCH("decode_index", stream,
+              decode_index_kernel<<<dim3(grid_1d(uint64_t(plan->ndchunk) + 1, kBlock), K), kBlock, 0, stream>>>(P, m, w));
     GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
                                                         accumulate != 0));
     hipError_t e = hipGetLastError();
