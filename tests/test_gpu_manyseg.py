@@ -96,3 +96,44 @@ def test_slimdp(layout):
     torch.cuda.synchronize()
     xi, xv, xo, _ = out.host()
     assert np.array_equal(xi, eidx) and same_bits(xv, evals) and np.array_equal(xo, eoff)
+
+
+def test_more_segments_than_the_lds_tables_hold():
+    """5000 segments: past the 4096 segment-table entries that pack and unpack
+    keep in LDS, so their tile searches read the tables from global memory.
+    DGC and AdaComp messages, both packs and unpacks, and their decode."""
+    rng = np.random.default_rng(905)
+    t = W.random_table(rng, 5000, max_len=200, gaps=True)
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    G = W.random_values(rng, n, "laplace")
+    z = np.zeros(n, np.float32)
+    say(f"5000 segments, n={n}: dgc")
+    _, _, dm = hp.dgc(G, z.copy(), z.copy(), 0.9, 1e-3, 2, tensors=True)
+    _, _, didx, dval, doff, _ = oracle.dgc(t, G, z, z, 0.9, 1e-3, 2)
+    gi, gv, go, _ = dm.host()
+    assert np.array_equal(go, doff) and np.array_equal(gi, didx) and same_bits(gv, dval)
+    say("5000 segments: adacomp")
+    _, am = hp.adacomp(G, z.copy(), 2.0, tensors=True)
+    _, aidx, aval, aoff, asc, _ = oracle.adacomp(t, G, z, 2.0)
+    gi, gv, go, _ = am.host()
+    assert np.array_equal(go, aoff) and np.array_equal(gi, aidx) and same_bits(gv, aval)
+    for kind, msg, want in ((1, dm, oracle.pack(1, t, didx, dval, doff)),
+                            (2, am, oracle.pack(2, t, aidx, aval, aoff, asc))):
+        say(f"5000 segments: pack and unpack kind={kind}")
+        data = hp.pack(kind, msg)
+        assert data == want
+        buf = torch.zeros(len(data) + 4, dtype=torch.uint8, device="cuda")
+        buf[:len(data)] = torch.from_numpy(np.frombuffer(data, np.uint8).copy()).cuda()
+        out = B.Sparse.empty(hp.plan, msg.count(), "cuda")
+        st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        B.gc_unpack(hp.plan, kind, buf, len(data), out, st, hp.workspace(B.GC_OP_UNPACK))
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        ui, uv, uo, _ = out.host()
+        mi, mv, mo, _ = msg.host()
+        assert np.array_equal(ui, mi) and np.array_equal(uo, mo) and same_bits(uv, mv)
+    say("5000 segments: decode")
+    got = hp.decode([dm, am], B.GC_AVG)
+    want = oracle.decode(t, n, [(didx, dval), (aidx, aval)], mode=1)
+    assert same_bits(got, want), ulp_report(got, want)
