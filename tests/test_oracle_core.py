@@ -303,3 +303,31 @@ def test_dgc_clip_norm_bound_and_closed_form():
             assert clip[0] < 1
         elif norm < thr * (1 - 1e-12):
             assert clip[0] == 1.0
+
+
+def test_results_do_not_depend_on_the_thread_count():
+    """The oracle runs OpenMP only over independent units (segments, fixed
+    tree chunks, buckets), so one thread and all threads give the same bits."""
+    rng = np.random.default_rng(44)
+    t = W.random_table(rng, 40, max_len=30_000, gaps=True)
+    n = W.table_extent(t)
+    G, U, V, R = (W.random_values(rng, n, "laplace") for _ in range(4))
+    x = W.random_values(rng, n, "normal", 0.05)
+    xh = (x - np.float32(0.1) * G).astype(np.float32)
+    before = oracle.num_threads()
+
+    def run():
+        d = oracle.dgc(t, G, U, V, 0.9, 1e-3, 2)
+        a = oracle.adacomp(t, G, R, 2.0)
+        c = oracle.dcd(x, xh, 4, 512, seed=1, step=2)
+        dec = oracle.decode(t, n, [(d[2], d[3]), (a[1], a[2])], mode=1)
+        return [np.asarray(v).tobytes() for v in (*d, *a, *c, dec)]
+
+    try:
+        oracle.set_num_threads(1)
+        one = run()
+        oracle.set_num_threads(max(before, 4))
+        many = run()
+    finally:
+        oracle.set_num_threads(before)
+    assert one == many
