@@ -71,6 +71,7 @@ _SIGS = {
                                            ctypes.c_size_t, _P]),
     "gc_adacomp_state_bytes": (ctypes.c_size_t, [_P]),
     "gc_adacomp_message_cap": (ctypes.c_uint64, [_P]),
+    "gc_plan_upload": (ctypes.c_int, [_P]),
     "gc_adacomp_residual": (ctypes.c_int, [_P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gc_dgc_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]),
@@ -222,6 +223,10 @@ class Plan:
     @property
     def total_bins(self) -> int:
         return int(load().gc_plan_total_bins(self.handle))
+
+    def upload(self) -> None:
+        """Put the plan's tables on the current device (gc_plan_upload)."""
+        _check(load().gc_plan_upload(self.handle))
 
     def workspace_bytes(self, op: int) -> int:
         return int(load().gc_plan_workspace_bytes(self.handle, op))

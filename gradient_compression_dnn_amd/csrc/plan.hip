@@ -243,6 +243,13 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     return GC_OK;
 }
 
+gc_status gc_plan_upload(const gc_plan *plan) {
+    clear_error();
+    if (!plan) return set_error(GC_EINVAL, "gc_plan_upload: plan is null");
+    PlanDev P;
+    return plan_device(plan, &P);
+}
+
 void gc_plan_destroy(gc_plan *plan) {
     if (!plan) return;
     int cur = 0;

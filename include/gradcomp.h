@@ -118,6 +118,12 @@ typedef struct gc_plan gc_plan;
 gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total,
                          gc_plan **out);
 void      gc_plan_destroy(gc_plan *plan);
+/* Put the plan's tables on the current device now: one hipMalloc and one
+ * synchronous copy, once per plan and device (a hot call does the same on
+ * its first use there).  For callers that capture a plan's first calls in a
+ * HIP graph, or allocate nothing inside their hot loop.  Returns GC_OK once
+ * the tables are there, GC_EINVAL for a NULL plan, GC_EHIP on a HIP error. */
+gc_status gc_plan_upload(const gc_plan *plan);
 int       gc_plan_num_segments(const gc_plan *plan);
 uint64_t  gc_plan_num_elements(const gc_plan *plan);
 /* Sum over segments of k (the DGC message size). */

@@ -113,6 +113,7 @@ def test_longest_segments_at_the_top_of_the_index_range():
 
 def test_hot_calls_reject_null_plan_without_touching_a_device():
     lib = B.load()
+    assert lib.gc_plan_upload(None) == B.GC_EINVAL
     assert lib.gc_dgc_step(None, None, None, None, 0.9, 0.0, 1, None, None, 0, None) == B.GC_EINVAL
     assert lib.gc_adacomp_compress(None, None, None, None, 0, 2.0, None, None, 0, None) == B.GC_EINVAL
     assert lib.gc_adacomp_residual(None, None, None, 0, None, None) == B.GC_EINVAL

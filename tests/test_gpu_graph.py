@@ -73,3 +73,38 @@ def test_dgc_and_adacomp_steps_replay_like_eager():
         # unrelated eager work between replays
         torch.cuda.synchronize()
         _ = (grads[t] * 2).sum().item()
+
+
+def test_first_calls_of_an_uploaded_plan_capture():
+    """gc_plan_upload puts the tables on the device, so even a plan's first
+    DGC step can be captured (no allocation happens inside the capture); the
+    replays equal eager steps on a second plan of the same layout."""
+    w = W.make_config("fc1m")
+    n = w.n_total
+    dev = torch.device("cuda:0")
+    plan, twin = B.Plan(w.table, n), B.Plan(w.table, n)
+    plan.upload()
+    plan.upload()  # idempotent
+    grads = [torch.from_numpy(W.gradient(w, t)).to(dev) for t in range(3)]
+    G = torch.empty(n, dtype=torch.float32, device=dev)
+    U, V = torch.zeros(n, device=dev), torch.zeros(n, device=dev)
+    Ue, Ve = U.clone(), V.clone()
+    dm, dme = B.Sparse.empty(plan, plan.total_k, dev), B.Sparse.empty(twin, twin.total_k, dev)
+    ws, wse = plan.workspace(B.GC_OP_DGC, dev), twin.workspace(B.GC_OP_DGC, dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture of an uploaded plan's first call")
+    with torch.cuda.graph(graph):
+        B.gc_dgc_step(plan, G, U, V, 0.9, 1e-3, 2, dm, ws)
+    torch.cuda.synchronize()
+    for t in range(3):
+        G.copy_(grads[t])
+        graph.replay()
+        torch.cuda.synchronize()
+        B.gc_dgc_step(twin, grads[t], Ue, Ve, 0.9, 1e-3, 2, dme, wse)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(U), _bits(Ue)) and np.array_equal(_bits(V), _bits(Ve))
+        ai, av, ao, _ = dm.host()
+        bi, bv, bo, _ = dme.host()
+        assert np.array_equal(ai, bi) and np.array_equal(ao, bo) and np.array_equal(av.view(np.uint32), bv.view(np.uint32))
+
