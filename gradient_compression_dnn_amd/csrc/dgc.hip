@@ -192,8 +192,8 @@ __device__ __forceinline__ void explore_values(const Src &a, const SegDev &seg, 
     for (int q = 0; q < 4; ++q) v[q] = dev_u2f(((mw >> q) & 1u) ? 0u : ((rw[q] >> 1) | 1u));
 }
 
-// Chunk geometry with the segment record cached across consecutive chunks
-// (a persistent workgroup's chunks mostly share a segment).
+// Chunk geometry with the segment record cached while the chunks stay in one
+// segment.
 struct ChunkWalker {
     uint32_t s = 0;
     SegDev seg{};
@@ -228,10 +228,12 @@ __device__ __forceinline__ void chunk_range(uint32_t nchunk, uint32_t *first, ui
 // lane nodes go to LDS in index order; thread t then owns the 4 consecutive
 // level-2 nodes [4 t, 4 t + 4) (a 16-element subtree), and the 256 thread
 // sums are combined by block_tree_sum into the chunk's level-12 node.
+// The persistent grid strides over the chunks (workgroup b takes b, b + grid,
+// ...), so the resident workgroups read neighbouring chunks at any time; a
+// contiguous range per workgroup measured 4% slower.
 __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float *__restrict__ G,
                                                           DgcWs w) {
-    uint32_t c0, c1;
-    chunk_range(P.ndchunk, &c0, &c1);
+    const uint32_t c0 = blockIdx.x, c1 = P.ndchunk, step = gridDim.x;
     __shared__ double node[kChunk / 4];  // level-2 nodes of the chunk, in order
     float cur[kRows][4], nxt[kRows][4];
     ChunkWalker walk;
@@ -242,10 +244,10 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
 #pragma unroll
         for (int j = 0; j < kRows; ++j) load4(rg, row_elem(j), cur[j]);
     }
-    for (uint32_t c = c0; c < c1; ++c) {
+    for (uint32_t c = c0; c < c1; c += step) {
         ChunkInfo cn;
-        if (c + 1 < c1) {
-            cn = walk.at(P, c + 1);
+        if (c + step < c1) {
+            cn = walk.at(P, c + step);
             const BufRsrc rn = chunk_buf(G + cn.lo, cn.cnt);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) load4(rn, row_elem(j), nxt[j]);
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
         double t[1] = {t0 + t1};
         const double chunk_sum = block_tree_sum(t[0]);
         if (threadIdx.x == 0) w.partial[c] = chunk_sum;
-        if (c + 1 < c1) {
+        if (c + step < c1) {
             ci = cn;
 #pragma unroll
             for (int j = 0; j < kRows; ++j)
@@ -769,40 +771,85 @@ __global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w) {
     }
 }
 
+// ------------------------------------------- candidate kernels (waves)
+// stage, refine, count and emit give each wave CPW consecutive chunks.  A
+// chunk holds a few staged entries, so what these kernels cost is the chain
+// of dependent loads: chunk record, segment state, staged entries.  The wave
+// issues the loads of all its chunks at once (lane j holds chunk j's record
+// and state, and every lane its entry of each chunk's first 64), then takes
+// the chunks in turn.  Plans of at least kWideChunks chunks use kCpwWide:
+// with one wave per chunk they needed several rounds of resident waves, each
+// paying the whole chain.  Smaller plans keep one chunk per wave, since
+// fewer waves would leave the chip idle while each walks its chunks (the
+// 1M-element tensor measured 9% slower at 4 chunks per wave).
+constexpr uint32_t kCpwWide = 4;
+constexpr uint32_t kWideChunks = 16384;
+
+__device__ __forceinline__ uint32_t lane_val(uint32_t v, uint32_t j) { return __builtin_amdgcn_readlane(v, j); }
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <uint32_t CPW>
+__device__ __forceinline__ uint32_t wave_chunk0() { return (blockIdx.x * kWaves + wave_id()) * CPW; }
+
+// Lane j < CPW: record and staged count of chunk c0 + j (lanes past the
+// last chunk, and lanes >= CPW, hold a copy of a valid chunk's).
+struct WaveChunks {
+    ChunkRec rec;
+    uint32_t n;
+};
+
+template <uint32_t CPW>
+__device__ __forceinline__ WaveChunks wave_chunks(const PlanDev &P, const DgcWs &w, uint32_t c0) {
+    const uint32_t c = min(c0 + uint32_t(lane_id()) % CPW, P.ndchunk - 1);
+    WaveChunks wc;
+    wc.rec = P.dchunk_rec[c];
+    wc.n = min(w.ccount[c], wc.rec.y);
+    return wc;
+}
+
+// Staged entry `lane` (clamped) of chunk j of the wave, or 0 when it has none.
+__device__ __forceinline__ uint32_t first_key(const DgcWs &w, const WaveChunks &wc, uint32_t j) {
+    const uint32_t n = lane_val(wc.n, j);
+    return n ? mag_key(w.sval[lane_val(wc.rec.x, j) + min(uint32_t(lane_id()), n - 1)]) : 0u;
+}
+
+// Calls f(i, key) for the staged entries i < n of the chunk at lo (each lane
+// its own entries; entries past n are skipped): the first 64 from k0, the
+// rest four batches of loads at a time.
+template <typename F>
+__device__ __forceinline__ void for_staged_keys(const DgcWs &w, uint32_t lo, uint32_t n, uint32_t k0, F &&f) {
+    const uint32_t lane = lane_id();
+    if (lane < n) f(lane, k0);
+    for (uint32_t i0 = kWave; i0 < n; i0 += 4 * kWave) {
+        uint32_t key[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[q] = mag_key(w.sval[lo + min(i0 + q * kWave + lane, n - 1)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (i0 + q * kWave + lane < n) f(i0 + q * kWave + lane, key[q]);
+    }
+}
+
 // ----------------------------------------------------------------- stage
-// One wave per chunk.  Normally the update staged every candidate: the wave
-// histograms digit 2 of the staged entries whose digit 1 is d1.  In a
-// re-staged segment it re-reads V instead: lane l holds elements
-// [256 r + 4 l, +4) for rows r = 0..15, so 16 KB of V is in flight per wave
-// and the ordered compaction needs only ballots (rank = running count +
-// lanes below + within lane); no LDS, no workgroup barrier.
+// Normally the update staged every candidate: the wave histograms digit 2 of
+// the staged entries whose digit 1 is d1.  In a re-staged segment it re-reads
+// the chunk's values instead (stage_chunk_again).
 constexpr int kWaveRows = kChunk / (4 * kWave);
 
+// One wave re-stages chunk c: lane l holds elements [256 r + 4 l, +4) for
+// rows r = 0..15, so 16 KB of V is in flight per wave and the ordered
+// compaction needs only ballots (rank = running count + lanes below + within
+// lane); no LDS, no workgroup barrier.
 template <int kMode>
-__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, DgcWs w, int redo_only) {
-    const uint32_t c = blockIdx.x * kWaves + wave_id();
-    if (c >= P.ndchunk) return;
-    const ChunkRec rec = P.dchunk_rec[c];
+__device__ __forceinline__ void stage_chunk_again(const PlanDev &P, const Src &a, const DgcWs &w, uint32_t c,
+                                                  const ChunkRec &rec, uint32_t d1, uint32_t *h2) {
     const uint32_t lo = rec.x, cnt = rec.y, s = rec.z;
-    if (w.st[s].all) return;
-    const uint32_t d1 = w.st[s].d1;
-    const uint32_t redo = w.st[s].redo;
-    uint32_t *h2 = w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2;
     const int lane = lane_id();
-    if (!redo) {
-        if (redo_only) return;
-        const uint32_t n = min(w.ccount[c], cnt);
-        for (uint32_t i0 = 0; i0 < n; i0 += 4 * kWave) {
-            uint32_t key[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) key[q] = mag_key(w.sval[lo + min(i0 + q * kWave + lane, n - 1)]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (i0 + q * kWave + lane < n && (key[q] >> (kDigit2Bits + kDigit3Bits)) == d1)
-                    atomicAdd(&h2[(key[q] >> kDigit3Bits) & (kHist2 - 1)], 1u);
-        }
-        return;
-    }
     // the ranked values again: V (DGC, already updated), or recomputed
     float v[kWaveRows][4];
     if (kMode == kVanilla || kMode == kNesterov) {
@@ -860,6 +907,42 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, Dgc
     if (lane == 0) w.ccount[c] = run;
 }
 
+template <int kMode, uint32_t CPW>
+__global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, DgcWs w, int redo_only) {
+    const uint32_t c0 = wave_chunk0<CPW>();
+    if (c0 >= P.ndchunk) return;
+    const WaveChunks wc = wave_chunks<CPW>(P, w, c0);
+    const SegState &sl = w.st[wc.rec.z];
+    const uint32_t all_l = sl.all, redo_l = sl.redo, d1_l = sl.d1;
+    uint32_t k0[CPW];
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) k0[j] = redo_only ? 0u : first_key(w, wc, j);
+    auto hist2_of = [&](uint32_t c, uint32_t s) { return w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2; };
+    if (!redo_only) {
+#pragma unroll
+        for (uint32_t j = 0; j < CPW; ++j) {
+            const uint32_t c = c0 + j;
+            if (c >= P.ndchunk) break;
+            if (lane_val(all_l, j) || lane_val(redo_l, j)) continue;
+            const uint32_t d1 = lane_val(d1_l, j);
+            uint32_t *h2 = hist2_of(c, lane_val(wc.rec.z, j));
+            for_staged_keys(w, lane_val(wc.rec.x, j), lane_val(wc.n, j), k0[j], [&](uint32_t, uint32_t key) {
+                if ((key >> (kDigit2Bits + kDigit3Bits)) == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            });
+        }
+    }
+    // re-staged segments (the fallback): one chunk at a time
+#pragma unroll 1
+    for (uint32_t j = 0; j < CPW; ++j) {
+        const uint32_t c = c0 + j;
+        if (c >= P.ndchunk) break;
+        if (lane_val(all_l, j) || !lane_val(redo_l, j)) continue;
+        const ChunkRec rec = make_uint4(lane_val(wc.rec.x, j), lane_val(wc.rec.y, j), lane_val(wc.rec.z, j),
+                                        lane_val(wc.rec.w, j));
+        stage_chunk_again<kMode>(P, a, w, c, rec, lane_val(d1_l, j), hist2_of(c, rec.z));
+    }
+}
+
 // Digit-2 histogram of the boundary bucket for dense selections (Slim-DP's
 // core at 10% density puts millions of staged entries in the boundary
 // digit-1 bucket, where one global atomic per entry dominated): a workgroup
@@ -908,46 +991,54 @@ __global__ __launch_bounds__(kBlock) void dgc_stagew_kernel(PlanDev P, DgcWs w) 
     flush(cur);
 }
 
-// ------------------------------------------------- refine, count (waves)
-// The candidate kernels run one wave per chunk (four chunks per workgroup):
-// a chunk holds a few staged entries, read 64 at a time from clamped indices.
-__device__ __forceinline__ uint32_t staged_count(const DgcWs &w, uint32_t c, uint32_t cnt) {
-    return min(w.ccount[c], cnt);
-}
-
+// ------------------------------------------------------- refine, count
+template <uint32_t CPW>
 __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) {
-    const uint32_t c = blockIdx.x * kWaves + wave_id();
-    if (c >= P.ndchunk) return;
-    const ChunkRec rec = P.dchunk_rec[c];
-    const uint32_t lo = rec.x, s = rec.z;
-    const uint32_t n = staged_count(w, c, rec.y);
-    if (n == 0 || w.st[s].all) return;
-    const uint32_t prefix = (w.st[s].d1 << kDigit2Bits) | w.st[s].d2;
-    uint32_t *h3 = w.hist3 + size_t(s) * kHist3;
-    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
-        const uint32_t i = i0 + lane_id();
-        const uint32_t key = mag_key(w.sval[lo + min(i, n - 1)]);
-        if (i < n && (key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
+    const uint32_t c0 = wave_chunk0<CPW>();
+    if (c0 >= P.ndchunk) return;
+    const WaveChunks wc = wave_chunks<CPW>(P, w, c0);
+    const SegState &sl = w.st[wc.rec.z];
+    const uint32_t all_l = sl.all, prefix_l = (sl.d1 << kDigit2Bits) | sl.d2;
+    uint32_t k0[CPW];
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) k0[j] = first_key(w, wc, j);
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        if (c0 + j >= P.ndchunk) break;
+        const uint32_t n = lane_val(wc.n, j);
+        if (n == 0 || lane_val(all_l, j)) continue;
+        const uint32_t prefix = lane_val(prefix_l, j);
+        uint32_t *h3 = w.hist3 + size_t(lane_val(wc.rec.z, j)) * kHist3;
+        for_staged_keys(w, lane_val(wc.rec.x, j), n, k0[j], [&](uint32_t, uint32_t key) {
+            if ((key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
+        });
     }
 }
 
+template <uint32_t CPW>
 __global__ __launch_bounds__(kBlock) void dgc_count_kernel(PlanDev P, DgcWs w) {
-    const uint32_t c = blockIdx.x * kWaves + wave_id();
-    if (c >= P.ndchunk) return;
-    const ChunkRec rec = P.dchunk_rec[c];
-    const uint32_t lo = rec.x;
-    const uint32_t n = staged_count(w, c, rec.y);
-    const uint32_t T = w.st[rec.z].T;
-    uint32_t ngt = 0, neq = 0;
-    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
-        const uint32_t i = i0 + lane_id();
-        const uint32_t key = mag_key(w.sval[lo + min(i, n - 1)]);
-        ngt += static_cast<uint32_t>(__popcll(__ballot(i < n && key > T)));
-        neq += static_cast<uint32_t>(__popcll(__ballot(i < n && key == T)));
-    }
-    if (lane_id() == 0) {
-        w.cgt[c] = ngt;
-        w.ceq[c] = neq;
+    const uint32_t c0 = wave_chunk0<CPW>();
+    if (c0 >= P.ndchunk) return;
+    const WaveChunks wc = wave_chunks<CPW>(P, w, c0);
+    const uint32_t T_l = w.st[wc.rec.z].T;
+    uint32_t k0[CPW];
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) k0[j] = first_key(w, wc, j);
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        const uint32_t c = c0 + j;
+        if (c >= P.ndchunk) break;
+        const uint32_t T = lane_val(T_l, j);
+        uint32_t gt = 0, eq = 0;  // this lane's entries
+        for_staged_keys(w, lane_val(wc.rec.x, j), lane_val(wc.n, j), k0[j], [&](uint32_t, uint32_t key) {
+            gt += key > T ? 1u : 0u;
+            eq += key == T ? 1u : 0u;
+        });
+        const uint32_t ngt = wave_sum(gt), neq = wave_sum(eq);
+        if (lane_id() == 0) {
+            w.cgt[c] = ngt;
+            w.ceq[c] = neq;
+        }
     }
 }
 
@@ -1012,66 +1103,91 @@ __global__ __launch_bounds__(kBlock) void dgc_scan_kernel(PlanDev P, DgcWs w,
 }
 
 // ------------------------------------------------------------------ emit
-// One wave per chunk: staged entries in index order, 64 at a time; ties at T
-// are taken in index order up to the chunk's quota; ranks from ballots.
-// DGC masks U and V at the sent entries.  kSignif also writes the chunk's
-// words of the core bitmap (every word, zeros included: the chunk's 4096
-// entries start on a word boundary of the segment's run), assembled in LDS.
-// kExplore sends delta at the chosen entries.
-template <int kMode>
+// Each of the wave's chunks in turn: staged entries in index order, 64 at a
+// time; ties at T are taken in index order up to the chunk's quota; ranks
+// from ballots.  DGC masks U and V at the sent entries.  kSignif also writes
+// the chunk's words of the core bitmap (every word, zeros included: the
+// chunk's 4096 entries start on a word boundary of the segment's run),
+// assembled in LDS.  kExplore sends delta at the chosen entries.
+template <int kMode, uint32_t CPW>
 __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcWs w,
                                                           uint32_t *__restrict__ out_idx,
                                                           float *__restrict__ out_val) {
     constexpr bool kDgc = kMode == kVanilla || kMode == kNesterov;
-    const uint32_t c = blockIdx.x * kWaves + wave_id();
-    if (c >= P.ndchunk) return;
-    const ChunkRec rec = P.dchunk_rec[c];
-    const uint32_t lo = rec.x, s = rec.z;
-    const uint32_t n = staged_count(w, c, rec.y);
+    const uint32_t c0 = wave_chunk0<CPW>();
+    if (c0 >= P.ndchunk) return;
+    const int lane = lane_id();
+    const WaveChunks wc = wave_chunks<CPW>(P, w, c0);
+    const uint32_t cl = min(c0 + uint32_t(lane) % CPW, P.ndchunk - 1);
+    const SegState &sl = w.st[wc.rec.z];
+    const uint32_t T_l = sl.T, take_l = w.ctake[cl], base_l = w.cout[cl];
+    // a segment owns message slots [base, base + sent): never write past them
+    const uint32_t limit_l = sl.base + sl.sent;
+    uint32_t id0[CPW];
+    float v0[CPW];
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        const uint32_t n = lane_val(wc.n, j);
+        const uint32_t ic = lane_val(wc.rec.x, j) + (n ? min(uint32_t(lane), n - 1) : 0u);
+        id0[j] = n ? w.sidx[ic] : 0u;
+        v0[j] = n ? w.sval[ic] : 0.0f;
+    }
     __shared__ uint32_t cmask[kWaves][kMode == kSignif ? kChunk / 32 : 1];
     uint32_t *cm = cmask[wave_id()];
-    if (kMode == kSignif) {
-        cm[lane_id()] = 0u;
-        cm[lane_id() + kWave] = 0u;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    } else if (n == 0) {
-        return;
-    }
-    const uint32_t T = w.st[s].T;
-    const uint32_t take = w.ctake[c];
-    const uint32_t base = w.cout[c];
-    // a segment owns message slots [base, base + sent): never write past them
-    const uint32_t limit = w.st[s].base + w.st[s].sent;
-    uint32_t eq_run = 0, sel_run = 0;
-    for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
-        const uint32_t i = i0 + lane_id();
-        const uint32_t ic = lo + min(i, n - 1);
-        const uint32_t id = w.sidx[ic];
-        const float val = w.sval[ic];
-        const uint32_t key = mag_key(val);
-        const bool in = i < n;
-        const bool eq = in && key == T;
-        const uint64_t eqm = __ballot(eq);
-        const bool sel = (in && key > T) || (eq && eq_run + lane_rank(eqm) < take);
-        const uint64_t selm = __ballot(sel);
-        const uint32_t p = base + sel_run + lane_rank(selm);
-        if (sel && p < limit) {
-            out_idx[p] = id;
-            out_val[p] = kMode == kExplore ? a.G[id] : val;
-            if (kDgc) {
-                a.V[id] = 0.0f;
-                a.U[id] = 0.0f;
-            }
-            if (kMode == kSignif) atomicOr(&cm[(id - lo) >> 5], 1u << ((id - lo) & 31u));
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        if (c0 + j >= P.ndchunk) break;
+        const uint32_t n = lane_val(wc.n, j), lo = lane_val(wc.rec.x, j);
+        if (kMode == kSignif) {
+            cm[lane] = 0u;
+            cm[lane + kWave] = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        } else if (n == 0) {
+            continue;
         }
-        eq_run += static_cast<uint32_t>(__popcll(eqm));
-        sel_run += static_cast<uint32_t>(__popcll(selm));
-    }
-    if (kMode == kSignif) {
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        const uint32_t wbase = P.seg[s].mbase + (rec.w << (kChunkLog2 - 5));
-        const uint32_t nw = (rec.y + 31) / 32;
-        for (uint32_t l = lane_id(); l < nw; l += kWave) a.mask[wbase + l] = cm[l];
+        const uint32_t T = lane_val(T_l, j), take = lane_val(take_l, j), base = lane_val(base_l, j);
+        const uint32_t limit = lane_val(limit_l, j);
+        uint32_t eq_run = 0, sel_run = 0;
+        auto one = [&](uint32_t i, uint32_t id, float val) {
+            const uint32_t key = mag_key(val);
+            const bool in = i < n;
+            const bool eq = in && key == T;
+            const uint64_t eqm = __ballot(eq);
+            const bool sel = (in && key > T) || (eq && eq_run + lane_rank(eqm) < take);
+            const uint64_t selm = __ballot(sel);
+            const uint32_t p = base + sel_run + lane_rank(selm);
+            if (sel && p < limit) {
+                out_idx[p] = id;
+                out_val[p] = kMode == kExplore ? a.G[id] : val;
+                if (kDgc) {
+                    a.V[id] = 0.0f;
+                    a.U[id] = 0.0f;
+                }
+                if (kMode == kSignif) atomicOr(&cm[(id - lo) >> 5], 1u << ((id - lo) & 31u));
+            }
+            eq_run += static_cast<uint32_t>(__popcll(eqm));
+            sel_run += static_cast<uint32_t>(__popcll(selm));
+        };
+        if (n) one(lane, id0[j], v0[j]);
+        for (uint32_t i0 = kWave; i0 < n; i0 += 4 * kWave) {
+            uint32_t id[4];
+            float val[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t ic = lo + min(i0 + q * kWave + lane, n - 1);
+                id[q] = w.sidx[ic];
+                val[q] = w.sval[ic];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + q * kWave < n) one(i0 + q * kWave + lane, id[q], val[q]);
+        }
+        if (kMode == kSignif) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            const uint32_t wbase = P.seg[lane_val(wc.rec.z, j)].mbase + (lane_val(wc.rec.w, j) << (kChunkLog2 - 5));
+            const uint32_t nw = (lane_val(wc.rec.y, j) + 31) / 32;
+            for (uint32_t l = lane; l < nw; l += kWave) a.mask[wbase + l] = cm[l];
+        }
     }
 }
 
@@ -1107,6 +1223,29 @@ gc_status check_select_io(const char *fn, const gc_plan *plan, const gc_sparse *
         return set_error(GC_ECAPACITY, f + ": workspace smaller than gc_plan_workspace_bytes(GC_OP_DGC)");
     if (reinterpret_cast<uintptr_t>(ws) % 256) return set_error(GC_EINVAL, f + ": workspace must be 256-byte aligned");
     return GC_OK;
+}
+
+// The radix select levels and the candidate kernels after the update, at
+// CPW chunks per wave.
+template <int kMode, uint32_t CPW>
+void launch_candidates(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const Src &src, bool sampled,
+                       uint32_t over, gc_sparse *out, hipStream_t stream) {
+    const unsigned segs = static_cast<unsigned>(plan->nseg);
+    const unsigned cand_grid = grid_1d(plan->ndchunk, kWaves * CPW);
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
+    if (kMode == kSignif) {
+        GC_LAUNCH("dgc_stage", stream, dgc_stagew_kernel<<<grid_1d(plan->ndchunk, kStageSpan), kBlock, 0, stream>>>(P, w));
+        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, 1));
+    } else {
+        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, 0));
+    }
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
+    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
+    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
+    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
 }
 
 // The selection pipeline for one key source: (clip), prep, sample + bound
@@ -1148,20 +1287,10 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
     // faster than an occupancy-sized persistent grid walking chunk ranges
     // (the explorer, bound by its Philox keys, runs the same in either shape).
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
-    if (kMode == kSignif) {
-        GC_LAUNCH("dgc_stage", stream, dgc_stagew_kernel<<<grid_1d(plan->ndchunk, kStageSpan), kBlock, 0, stream>>>(P, w));
-        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, 1));
-    } else {
-        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, 0));
-    }
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
-    GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
-    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_count", stream, dgc_count_kernel<<<wave_grid, kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
-    GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+    if (plan->ndchunk >= kWideChunks)
+        launch_candidates<kMode, kCpwWide>(plan, P, w, src, sampled, over, out, stream);
+    else
+        launch_candidates<kMode, 1>(plan, P, w, src, sampled, over, out, stream);
 }
 }  // namespace
 

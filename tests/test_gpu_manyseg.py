@@ -1,7 +1,9 @@
 """GPU parity on plans with hundreds of segments (more than one 256-wide
 round in every per-segment scan: segment bases of sampled DGC, AdaComp
 offsets, pack tiles and layout, decode's segment walk), for every call that
-takes a plan, against the oracle bit for bit."""
+takes a plan, against the oracle bit for bit.  The 17,000-segment layout has
+more than 16,384 chunks, where the selection's candidate kernels give each
+wave four chunks, here mostly of different segments."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +16,11 @@ from tests.gpu_util import HipPath, same_bits, say, sparse_from_host, to_dev, ul
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def layout():
+@pytest.fixture(scope="module", params=[(700, 3000), (17000, 300)], ids=["700seg", "17000seg"])
+def layout(request):
+    nseg, max_len = request.param
     rng = np.random.default_rng(900)
-    t = W.random_table(rng, 700, max_len=3000, gaps=True)
+    t = W.random_table(rng, nseg, max_len=max_len, gaps=True)
     return t, W.table_extent(t), rng
 
 

@@ -107,15 +107,19 @@ def _dgc_sample_positions(t):
     return np.array(pos, np.int64)
 
 
+@pytest.mark.parametrize("wide", [False, True], ids=["3seg", "wide"])
 @pytest.mark.parametrize("layout", ["sampled_large", "sampled_large_ties"])
-def test_dgc_sample_bound_fallback(layout):
+def test_dgc_sample_bound_fallback(layout, wide):
     """Adversarial input for the sampled staging bound: the sampled elements
     hold the largest values, spread over many octaves, so the sample's upper
     quantile lies far above the true k-th largest value and the segment must
     be re-staged from V.  Results stay bit-exact against the oracle, and a
-    second segment with ordinary values is unaffected."""
+    second segment with ordinary values is unaffected.  The wide plan adds
+    16,400 one-chunk segments, past the 16,384 chunks from which the
+    candidate kernels give each wave four chunks."""
     rng = np.random.default_rng(91)
-    t = W.make_table([3000, 4096 * 16 + 123, 50000], [50, 50, 50], [3, 200, 50])
+    extra = 16400 if wide else 0
+    t = W.make_table([3000, 4096 * 16 + 123, 50000] + [64] * extra, [50] * (3 + extra), [3, 200, 50] + [1] * extra)
     n = W.table_extent(t)
     hp = HipPath(t, n)
     V = (rng.standard_normal(n) * 1e-20).astype(np.float32)
@@ -128,7 +132,7 @@ def test_dgc_sample_bound_fallback(layout):
     V[inseg] = (mags * np.where(rng.random(inseg.size) < 0.5, -1, 1)).astype(np.float32)
     z = np.zeros(n, np.float32)
     G = (rng.standard_normal(n) * 1e-30).astype(np.float32)
-    say(f"dgc sample fallback {layout}")
+    say(f"dgc sample fallback {layout} wide={wide}")
     U, Vo, idx, val, off, _ = oracle.dgc(t, G, z, V, 0.9, 0.0, 1)
     Ug, Vg, gidx, gval, goff = hp.dgc(G, z.copy(), V.copy(), 0.9, 0.0, 1)
     assert np.array_equal(goff, off) and np.array_equal(gidx, idx)
