@@ -384,53 +384,57 @@ __device__ __forceinline__ double block_tree_sum(double v) {
 }
 
 // Canonical pairwise sum of x[0..m) (zero-padded to a power of two) by one
-// workgroup.  load(i) returns term i as double for i < m.  Thread t sums an
-// aligned sub-block of B = max(1, M/kBlock) leaves sequentially with the
-// binary-counter stack (which forms exactly the perfect subtree), then the
-// 256 subtree sums are combined by block_tree_sum.  Sub-blocks past m are
-// +0.0 subtrees, and adding +0.0 to a non-negative value is exact, so the
-// result equals the tree over M leaves.
-constexpr int kTreeDepth = 26;  // sub-blocks of up to 2^25 leaves per thread
+// workgroup.  load(i) returns term i as double for i < m.  Thread t owns an
+// aligned sub-block of B = max(1, M/kBlock) leaves.  Below 8 leaves it adds
+// them as their perfect tree; otherwise it adds each run of 8 as a fixed
+// 8-leaf tree and combines those nodes in order with the binary-counter stack
+// (which forms exactly the perfect subtree over them).  The 256 subtree sums
+// are combined by block_tree_sum.  Sub-blocks past m are +0.0 subtrees, and
+// adding +0.0 to a non-negative value is exact, so the result equals the tree
+// over M leaves.  (A stack step per leaf cost 26 predicated adds each; per
+// 8-leaf node the 5,063-chunk clip tree finishes in a fraction of that.)
+constexpr int kTreeDepth = 23;  // levels of 8-leaf nodes: sub-blocks of up to 2^26 leaves per thread
 
 template <class Load>
 __device__ double block_pairwise_sum(uint64_t m, Load load) {
     uint64_t M = 1;
     while (M < m) M <<= 1;
-    uint64_t B = M > kBlock ? M / kBlock : 1;
-    uint64_t lo = static_cast<uint64_t>(threadIdx.x) * B;
-    double stack[kTreeDepth];
-    double carry = 0.0;
-    // leaves are loaded 8 at a time (clamped index, then selected) so that a
-    // batch is in flight together; m >= 1
-    constexpr uint64_t kBatch = 8;
-    for (uint64_t i0 = 0; i0 < B; i0 += kBatch) {
-        double leaf[kBatch];
+    const uint64_t B = M > kBlock ? M / kBlock : 1;
+    const uint64_t lo = static_cast<uint64_t>(threadIdx.x) * B;
+    // leaf g, +0.0 past the terms (the index is clamped, so the load is in
+    // bounds; m >= 1)
+    auto leaf = [&](uint64_t g) {
+        const double v = load(g < m ? g : m - 1);
+        return g < m ? v : 0.0;
+    };
+    double carry;
+    if (B < 8) {
+        double l[4];
 #pragma unroll
-        for (uint64_t u = 0; u < kBatch; ++u) {
-            const uint64_t g = lo + i0 + u;
-            const double v = load(g < m ? g : m - 1);
-            leaf[u] = g < m ? v : 0.0;
-        }
+        for (uint64_t u = 0; u < 4; ++u) l[u] = u < B ? leaf(lo + u) : 0.0;
+        carry = B == 1 ? l[0] : B == 2 ? l[0] + l[1] : (l[0] + l[1]) + (l[2] + l[3]);
+    } else {
+        double stack[kTreeDepth];
+        for (uint64_t i = 0; i < B / 8; ++i) {
+            double l[8];
 #pragma unroll
-        for (uint64_t u = 0; u < kBatch; ++u) {
-            const uint64_t i = i0 + u;
-            if (i >= B) break;
-            carry = leaf[u];
+            for (uint64_t u = 0; u < 8; ++u) l[u] = leaf(lo + 8 * i + u);
+            carry = ((l[0] + l[1]) + (l[2] + l[3])) + ((l[4] + l[5]) + (l[6] + l[7]));
             bool done = false;
 #pragma unroll
-            for (int l = 0; l < kTreeDepth; ++l) {
+            for (int lv = 0; lv < kTreeDepth; ++lv) {
                 if (!done) {
-                    if ((i >> l) & 1) {
-                        carry = stack[l] + carry;
+                    if ((i >> lv) & 1) {
+                        carry = stack[lv] + carry;
                     } else {
-                        stack[l] = carry;
+                        stack[lv] = carry;
                         done = true;
                     }
                 }
             }
         }
     }
-    // after B (a power of two) leaves the full subtree sum is the last carry
+    // after B/8 (a power of two) nodes the full subtree sum is the last carry
     return block_tree_sum(carry);
 }
 
