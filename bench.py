@@ -77,6 +77,23 @@ def stored_traffic(kernel: str, digest: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def stored_call_traffic(prefixes, digest: str):
+    """HBM bytes per step of the kernels whose names start with one of
+    `prefixes`, from committed rocprofv3 counter runs, or None if the counters
+    were taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_deepspeech.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != digest or not d.get("steps_in_run"):
+        return None
+    tot = sum(k["hbm_bytes_per_launch"] * k["launches"] for name, k in d.get("kernels", {}).items()
+              if name.startswith(prefixes))
+    return round(tot / d["steps_in_run"])
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -503,15 +520,24 @@ def main(argv=None):
     ws = {op: plan.workspace(op, dev) for op in (B.GC_OP_DGC, B.GC_OP_ADACOMP, B.GC_OP_PACK,
                                                  B.GC_OP_DECODE)}
 
-    def step(t):
+    CALLS = ("dgc", "dgc_pack", "adacomp", "adacomp_pack", "dgc_decode", "adacomp_decode", "dcd")
+
+    def step(t, marks=None):
+        """One step; with `marks` (len(CALLS) + 1 events) each call is bracketed."""
         g = G[t % len(G)]
-        B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC])
-        B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK])
-        B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=astate)
-        B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK])
-        B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE])
-        B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE])
-        B.gc_dcd_compress(X, XH[t % len(XH)], XO, 4, bucket, 0x5EED, t, scales, codes)
+        calls = (lambda: B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC]),
+                 lambda: B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK]),
+                 lambda: B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=astate),
+                 lambda: B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK]),
+                 lambda: B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
+                 lambda: B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
+                 lambda: B.gc_dcd_compress(X, XH[t % len(XH)], XO, 4, bucket, 0x5EED, t, scales, codes))
+        for i, call in enumerate(calls):
+            if marks:
+                marks[i].record()
+            call()
+        if marks:
+            marks[-1].record()
 
     # warm-up, then one instrumented step to find the dominant kernel
     log(f"warmup {args.warmup} step(s)")
@@ -561,6 +587,16 @@ def main(argv=None):
             breakdown[kname] = round(ms * 1000.0, 2)  # microseconds in one step
     B.gc_timing_enable(None)
 
+    # each call of the step alone: a few more steps with events between the
+    # calls (outside the timed region), averaged per call
+    call_ms = {c: 0.0 for c in CALLS}
+    for r in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
+        step(args.warmup + 2 + args.steps + r, ev)
+        torch.cuda.synchronize()
+        for i, c in enumerate(CALLS):
+            call_ms[c] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+
     # the measured streaming ceiling: a plain 1 GiB device-to-device copy, best
     # of 5 (also the reference that scales rocprofv3's byte counters)
     ca = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
@@ -605,6 +641,23 @@ def main(argv=None):
         if k in alg and us > 0:
             kernel_frac[k] = round(alg[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
+    # per method: the call's own time, the method's algorithmic bytes and the
+    # counters' bytes of its kernels (pack and decode: both calls together)
+    def method(ms, alg_bytes, prefixes):
+        ctr = stored_call_traffic(prefixes, digest)
+        frac = lambda b: None if b is None else round(b / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)
+        return {"ms": round(ms, 4), "alg_bytes": alg_bytes, "alg_hbm_frac": frac(alg_bytes),
+                "counter_bytes": ctr, "counter_hbm_frac": frac(ctr)}
+
+    methods = {
+        "dgc": method(call_ms["dgc"], alg["dgc_update"] + alg["dgc_emit"], ("dgc_",)),
+        "adacomp": method(call_ms["adacomp"], alg["ada_fold"] + alg["ada_emit"], ("ada_",)),
+        "pack_both": method(call_ms["dgc_pack"] + call_ms["adacomp_pack"],
+                            8 * (plan.total_k + ada_entries) + int(dn.item()) + int(an.item()), ("pack_",)),
+        "decode_both": method(call_ms["dgc_decode"] + call_ms["adacomp_decode"], 2 * alg["decode"], ("decode",)),
+        "dcd": method(call_ms["dcd"], alg["dcd"], ("dcd",)),
+    }
+
     value = 2 * 4 * n / (ms_per_step / 1000.0) / 1e9
     # the method's own bytes for the whole step: DGC 20 B/elt, AdaComp 12, DCD 12.5 + scales,
     # two dense decodes 4 each, plus the messages read and written
@@ -630,6 +683,7 @@ def main(argv=None):
         "step_counter_hbm_frac": (None if stored_step_traffic(digest) is None else
                                   round(stored_step_traffic(digest) / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)),
         "roofline": roof,
+        "methods": methods,
         "copy_ceiling": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "what": "device-to-device copy of 1 GiB (1 GiB read + 1 GiB written), best of 5"},
         "kernel_us_per_step": breakdown,
