@@ -16,7 +16,7 @@ import oracle
 from gradient_compression_dnn_amd import binding as B
 from gradient_compression_dnn_amd import workloads as W
 from tests.gpu_util import same_bits, say, to_dev
-from tests.test_gpu_parity import mixed_table
+from tests.test_gpu_parity import _dgc_sample_positions, mixed_table
 from tests.test_oracle_slimdp import _arr
 
 pytestmark = pytest.mark.gpu
@@ -138,3 +138,32 @@ def test_deepspeech_vgg_setting():
     xi, xv, xo, _ = sd.explore(d, 7, 3).host()
     assert np.array_equal(xi, eidx) and same_bits(xv, evals)
     assert abs(len(xi) + len(gi) - 0.2 * n) < 0.001 * n
+
+
+@pytest.mark.parametrize("wide", [False, True], ids=["3seg", "wide"])
+def test_core_sample_bound_fallback(wide):
+    """Adversarial significances for the sampled staging bound of the core
+    selection: the sampled elements of one tensor carry its largest |w|,
+    spread over many octaves, so the bound lies far above the true k-th
+    largest significance and the tensor is re-staged from w and g with the
+    significance recomputed.  Bit-exact against the oracle.  The wide plan
+    adds 16,400 one-chunk tensors, past the 16,384 chunks from which the
+    candidate kernels give each wave four chunks."""
+    rng = np.random.default_rng(93)
+    extra = 16400 if wide else 0
+    lens = [3000, 4096 * 16 + 123, 50000] + [64] * extra
+    t = W.make_table(lens, [50] * len(lens), [max(1, math.ceil(0.1 * x)) for x in lens])
+    n = W.table_extent(t)
+    w_ = (rng.standard_normal(n) * 1e-20).astype(np.float32)
+    g_ = (rng.standard_normal(n) * 1e-20).astype(np.float32)
+    pos = _dgc_sample_positions(t)
+    o1, l1 = int(t[1][0]), int(t[1][1])
+    inseg = pos[(pos >= o1) & (pos < o1 + l1)]
+    mags = (np.float32(2.0) ** (-(np.arange(inseg.size) / 4.0))).astype(np.float32)
+    w_[inseg] = (mags * np.where(rng.random(inseg.size) < 0.5, -1, 1)).astype(np.float32)
+    sd = SlimDP(t, t)
+    say(f"slimdp core sample fallback wide={wide}")
+    cidx, cval, coff, cmask = oracle.slimdp_core(t, w_, g_, 1.0)
+    gi, gv, go, _ = sd.core(w_, g_, 1.0).host()
+    assert np.array_equal(go, coff) and np.array_equal(gi, cidx) and same_bits(gv, cval)
+    assert np.array_equal(sd.mask_host(), cmask)
