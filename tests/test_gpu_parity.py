@@ -107,16 +107,17 @@ def _dgc_sample_positions(t):
     return np.array(pos, np.int64)
 
 
+@pytest.mark.parametrize("nesterov", [False, True], ids=["vanilla", "nesterov"])
 @pytest.mark.parametrize("wide", [False, True], ids=["3seg", "wide"])
 @pytest.mark.parametrize("layout", ["sampled_large", "sampled_large_ties"])
-def test_dgc_sample_bound_fallback(layout, wide):
+def test_dgc_sample_bound_fallback(layout, wide, nesterov):
     """Adversarial input for the sampled staging bound: the sampled elements
     hold the largest values, spread over many octaves, so the sample's upper
     quantile lies far above the true k-th largest value and the segment must
     be re-staged from V.  Results stay bit-exact against the oracle, and a
     second segment with ordinary values is unaffected.  The wide plan adds
     16,400 one-chunk segments, past the 16,384 chunks from which the
-    candidate kernels give each wave four chunks."""
+    candidate kernels give each wave four chunks.  Both momentum kinds."""
     rng = np.random.default_rng(91)
     extra = 16400 if wide else 0
     t = W.make_table([3000, 4096 * 16 + 123, 50000] + [64] * extra, [50] * (3 + extra), [3, 200, 50] + [1] * extra)
@@ -132,9 +133,10 @@ def test_dgc_sample_bound_fallback(layout, wide):
     V[inseg] = (mags * np.where(rng.random(inseg.size) < 0.5, -1, 1)).astype(np.float32)
     z = np.zeros(n, np.float32)
     G = (rng.standard_normal(n) * 1e-30).astype(np.float32)
-    say(f"dgc sample fallback {layout} wide={wide}")
-    U, Vo, idx, val, off, _ = oracle.dgc(t, G, z, V, 0.9, 0.0, 1)
-    Ug, Vg, gidx, gval, goff = hp.dgc(G, z.copy(), V.copy(), 0.9, 0.0, 1)
+    say(f"dgc sample fallback {layout} wide={wide} nesterov={nesterov}")
+    U, Vo, idx, val, off, _ = oracle.dgc_ex(t, G, z, V, 0.9, 0.0, 1, nesterov=nesterov)
+    opt = B.dgc_options(0.9, 0.0, 1, nesterov=nesterov)
+    Ug, Vg, gidx, gval, goff = hp.dgc_ex(G, z.copy(), V.copy(), opt)
     assert np.array_equal(goff, off) and np.array_equal(gidx, idx)
     assert same_bits(gval, val) and same_bits(Ug, U) and same_bits(Vg, Vo)
 
