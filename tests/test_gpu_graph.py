@@ -1,9 +1,10 @@
 """The hot calls under HIP graph capture: a DGC step (and an AdaComp step
-with its deferred residual) on the 1M-element FC layer is captured once and
-replayed several times, with eager work and synchronizations between the
-replays; every replay's message and state must equal an eager run of the
-same call on copies, bit for bit.  The plan is uploaded by a warm-up call
-before capture (the one allocation the library makes)."""
+with its deferred residual) on the 1M-element FC layer, and on a plan of
+17,000 random tensors, is captured once and replayed several times, with
+eager work and synchronizations between the replays; every replay's message
+and state must equal an eager run of the same call on copies, bit for bit.
+The plan is uploaded by a warm-up call before capture (the one allocation the
+library makes)."""
 import numpy as np
 import pytest
 import torch
@@ -19,12 +20,24 @@ def _bits(t):
     return t.detach().cpu().numpy().view(np.uint32)
 
 
-def test_dgc_and_adacomp_steps_replay_like_eager():
-    w = W.make_config("fc1m")
-    n = w.n_total
-    plan = B.Plan(w.table, n)
+def _workload(name):
+    """(table, n, four host gradients): the FC layer, or 17,000 random tensors
+    (more than 16,384 chunks: the DGC candidate kernels take four per wave)."""
+    if name == "fc1m":
+        w = W.make_config("fc1m")
+        return w.table, w.n_total, [W.gradient(w, t) for t in range(4)]
+    rng = np.random.default_rng(77)
+    t = W.random_table(rng, 17000, max_len=300, gaps=True)
+    n = W.table_extent(t)
+    return t, n, [W.random_values(rng, n, "laplace") for _ in range(4)]
+
+
+@pytest.mark.parametrize("name", ["fc1m", "wide"])
+def test_dgc_and_adacomp_steps_replay_like_eager(name):
+    table, n, host_grads = _workload(name)
+    plan = B.Plan(table, n)
     dev = torch.device("cuda:0")
-    grads = [torch.from_numpy(W.gradient(w, t)).to(dev) for t in range(4)]
+    grads = [torch.from_numpy(g).to(dev) for g in host_grads]
     G = torch.empty(n, dtype=torch.float32, device=dev)  # the graph's input slot
     U, V, R = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
     st = plan.adacomp_state(dev)
