@@ -614,6 +614,23 @@ def main(argv=None):
     copy_gbs = 2 * ca.numel() * 4 / (best / 1000.0) / 1e9
     del ca, cb
 
+    # the update's own access pattern with none of its selection work (three
+    # reads, two writes per element, the dense kernels' layout and hints) on
+    # the workload's size, best of 5: the streaming ceiling for dgc_update
+    # (inputs: a gradient and the DCD model pair; outputs: the decode buffers,
+    # rewritten by every step anyway)
+    B.gc_stream_probe(G[0], X, XH[0], ddense, adense)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.gc_stream_probe(G[0], X, XH[0], ddense, adense)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    stream_gbs = 20 * n / (best / 1000.0) / 1e9
+
     # the DCD step's signal-to-noise measure (alpha of the DCD page):
     # ||Z - C(Z)|| / ||Z|| with Z = x_half - x and C(Z) = x_out - x, for the
     # breakdown step's inputs
@@ -686,6 +703,12 @@ def main(argv=None):
         "methods": methods,
         "copy_ceiling": {"achieved": round(copy_gbs, 1), "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "what": "device-to-device copy of 1 GiB (1 GiB read + 1 GiB written), best of 5"},
+        "stream_ceiling": {"achieved": round(stream_gbs, 1), "unit": "GB/s", "frac": round(stream_gbs / HBM_PEAK_GBS, 4),
+                           "dominant_share": (None if roof is None or roof["kernel"] != "dgc_update"
+                                              else round(roof["achieved"] / stream_gbs, 4)),
+                           "what": "gc_stream_probe: 3 fp32 reads + 2 writes per element over the workload's n "
+                                   "in the dense kernels' layout and cache hints (dgc_update's traffic, no "
+                                   "selection work), best of 5"},
         "kernel_us_per_step": breakdown,
         "kernel_alg_hbm_frac": kernel_frac,
         "messages": {"dgc_entries": plan.total_k, "adacomp_entries": ada_entries,

@@ -97,6 +97,7 @@ _SIGS = {
     "gc_slimdp_core_values": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "gc_timing_enable": (ctypes.c_int, [ctypes.c_char_p]),
     "gc_timing_take": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
+    "gc_stream_probe": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_uint64, _P]),
 }
 
 KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
@@ -104,7 +105,7 @@ KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dg
            "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "unpack_walk", "unpack_count", "unpack_scan",
            "unpack_write", "decode_index", "decode", "dcd",
-           "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update", "slimdp_values")
+           "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update", "slimdp_values", "stream_probe")
 
 
 def gc_timing_enable(kernels) -> None:
@@ -117,6 +118,14 @@ def gc_timing_enable(kernels) -> None:
     else:
         arg = ",".join(kernels).encode()
     _check(load().gc_timing_enable(arg))
+
+
+def gc_stream_probe(a, b, c, d, e) -> None:
+    """The streaming reference: d = a + b, e = c + d over a.numel() fp32
+    elements (three reads, two writes per element)."""
+    n = a.numel()
+    _check(load().gc_stream_probe(_f32(a, n, "a"), _f32(b, n, "b"), _f32(c, n, "c"), _f32(d, n, "d"),
+                                  _f32(e, n, "e"), n, _stream(d)))
 
 
 def gc_timing_take(kernel: str):

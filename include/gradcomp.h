@@ -508,13 +508,31 @@ gc_status gc_slimdp_core_values(const gc_plan *core_plan, const gc_sparse *core,
  *             pack_tiles, pack_count, pack_layout, pack_write, unpack_walk,
  *             unpack_count, unpack_scan, unpack_write, decode_index,
  *             decode, dcd, dcd_decode, dcd_mix, ecd_compress, ecd_update,
- *             slimdp_values (Slim-DP selection reuses the dgc_* names).
+ *             slimdp_values, stream_probe (Slim-DP selection reuses the
+ *             dgc_* names).
  * gc_timing_take waits for the recorded events of one kernel and returns the
  * summed duration in milliseconds and the number of launches, then forgets
  * them.  Host-thread safe; not for use while a stream is being captured.
  */
 gc_status gc_timing_enable(const char *kernels);
 gc_status gc_timing_take(const char *kernel, double *total_ms, uint64_t *launches);
+
+/*
+ * A streaming reference for measurement tools, not part of any method:
+ * d[i] = a[i] + b[i] and e[i] = c[i] + d[i] (fp32) for i < n, that is three
+ * reads and two writes per element, the HBM traffic of the DGC update, in
+ * the same chunk tiling, lane layout and cache hints as the dense kernels
+ * and with none of their other work.  Timed beside dgc_update it gives the
+ * bandwidth that access pattern reaches on the device.
+ *   a, b, c : device, n floats each, read.   d, e : device, n floats each,
+ *             written; they must not overlap each other or the inputs.
+ *   n       : below 2^32; 0 enqueues nothing.
+ * All pointers 4-byte aligned.  Errors (GC_EINVAL null or misaligned
+ * pointer, GC_ERANGE n) are detected before anything is enqueued.
+ * Asynchronous on `stream`.
+ */
+gc_status gc_stream_probe(const float *a, const float *b, const float *c, float *d, float *e, uint64_t n,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -226,3 +226,13 @@ def test_binding_checks_tensors_before_calling_the_library():
     with pytest.raises(ValueError, match="need a contiguous CUDA"):
         B.gc_dgc_step(p, x, x, x, 0.9, 0.0, 1, host, torch.zeros(16, dtype=torch.uint8))
 
+
+
+def test_stream_probe_host_checks():
+    """The streaming reference rejects bad arguments before enqueuing anything."""
+    lib, fake = B.load(), ctypes.c_void_p(256)
+    assert lib.gc_stream_probe(None, fake, fake, fake, fake, 1, None) == B.GC_EINVAL
+    assert lib.gc_stream_probe(fake, fake, fake, fake, fake, 1 << 32, None) == B.GC_ERANGE
+    assert lib.gc_stream_probe(fake, fake, ctypes.c_void_p(258), fake, fake, 8, None) == B.GC_EINVAL
+    assert "aligned" in B.gc_last_error()
+    assert lib.gc_stream_probe(fake, fake, fake, fake, fake, 0, None) == B.GC_OK  # nothing enqueued

@@ -3,9 +3,12 @@ library, and its one JSON line checked field by field (the numbers must be
 consistent with one another; their size is what the benchmark measures)."""
 import json
 
+import numpy as np
 import pytest
+import torch
 
 import bench
+from gradient_compression_dnn_amd import binding as B
 from gradient_compression_dnn_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +48,11 @@ def test_bench_line_schema_and_consistency(capsys):
         assert r["source_digest"] == bench.source_digest()
         assert 0.9 * 20 * n < roof["traffic"] < 1.5 * 20 * n
 
+    sc = r["stream_ceiling"]
+    assert sc["unit"] == "GB/s" and sc["achieved"] > 0 and 0.0 < sc["frac"] < 1.0
+    assert sc["dominant_share"] == pytest.approx(roof["achieved"] / sc["achieved"], rel=1e-3)
+    assert 0.5 < sc["dominant_share"] < 1.3
+
     for name in ("dgc", "adacomp", "pack_both", "decode_both", "dcd"):
         m = r["methods"][name]
         assert m["ms"] > 0 and m["alg_bytes"] > 0
@@ -56,3 +64,20 @@ def test_bench_line_schema_and_consistency(capsys):
     assert msgs["dgc_entries"] == sum(W.topk_count(int(s[1])) for s in W.make_config("deepspeech").table)
     assert 0 < msgs["adacomp_entries"] <= n
     assert msgs["dgc_packed_bytes"] > 8 * msgs["dgc_entries"] // 2
+
+
+def test_stream_probe_arithmetic_and_bounds():
+    """The streaming reference computes d = a + b and e = c + d in fp32 and
+    writes nothing past n (ragged chunk tails included)."""
+    rng = np.random.default_rng(5)
+    for n in (1, 4095, 4096 * 3 + 7):
+        a, b, c = (rng.standard_normal(n).astype(np.float32) for _ in range(3))
+        d = torch.full((n + 64,), 7.0, device="cuda")
+        e = torch.full((n + 64,), 7.0, device="cuda")
+        B.gc_stream_probe(*(torch.from_numpy(x).cuda() for x in (a, b, c)), d[:n], e[:n])
+        torch.cuda.synchronize()
+        want_d = (a + b).astype(np.float32)
+        want_e = (c + want_d).astype(np.float32)
+        assert np.array_equal(d[:n].cpu().numpy().view(np.uint32), want_d.view(np.uint32))
+        assert np.array_equal(e[:n].cpu().numpy().view(np.uint32), want_e.view(np.uint32))
+        assert torch.all(d[n:] == 7.0) and torch.all(e[n:] == 7.0)
