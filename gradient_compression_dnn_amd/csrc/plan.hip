@@ -163,7 +163,9 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         if (g.length < 1) return set_error(GC_EINVAL, at + "length must be >= 1");
         if (g.offset < prev_end)
             return set_error(GC_EINVAL, at + "segments must be ascending and non-overlapping");
-        if (g.offset + g.length > n_total)
+        // compared without forming offset + length, which wraps for offsets
+        // near 2^64
+        if (g.offset >= n_total || g.length > n_total - g.offset)
             return set_error(GC_EINVAL, at + "segment extends past n_total");
         if (g.bin_len < 1) return set_error(GC_EINVAL, at + "bin_len must be >= 1");
         if (g.bin_len > GC_MAX_BIN_LEN)

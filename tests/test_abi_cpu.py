@@ -63,11 +63,24 @@ def _create(rows, n_total):
     ([(0, B.GC_MAX_SEGMENT_LEN + 1, 1, 1, 0)], (1 << 32) - 1, B.GC_ENOTSUP),  # u32 code count
     ([(0, 0xFFFFFFFF, 64, 1, 0)], (1 << 32) - 1, B.GC_ENOTSUP),
     ([(0, 5, 1, 5, 0), (7, 3, 2, 1, 0)], 10, B.GC_OK),       # gap allowed
+    # offsets near 2^64: offset + length wraps to a small value
+    ([((1 << 64) - 1, 1, 1, 1, 0)], 10, B.GC_EINVAL),
+    ([((1 << 64) - 1, 2, 1, 1, 0)], 10, B.GC_EINVAL),
+    ([(0, 5, 1, 1, 0), ((1 << 64) - 2, 3, 1, 1, 0)], 10, B.GC_EINVAL),
+    ([(10, 1, 1, 1, 0)], 10, B.GC_EINVAL),                   # starts at n_total
 ])
 def test_plan_validation(rows, n_total, code):
     assert _create(rows, n_total) == code
     if code != B.GC_OK:
         assert B.gc_last_error() != ""
+
+
+def test_plan_rejects_negative_offsets_from_the_binding():
+    # an int64 table offset of -1 reaches the library as 2^64 - 1
+    for off, n in ((-1, 1), (-1, 2), (-2, 3)):
+        with pytest.raises(B.GCError) as e:
+            B.Plan(np.array([[off, n, 1, 1]], dtype=np.int64), 10)
+        assert e.value.status == B.GC_EINVAL
 
 
 def test_plan_queries_and_workspace_on_workloads():
