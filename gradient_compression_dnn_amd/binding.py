@@ -82,6 +82,9 @@ _SIGS = {
     "gc_unpack": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_uint64, _P, _P, _P, ctypes.c_size_t, _P]),
     "gc_decompress_accumulate": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
                                                 _P, ctypes.c_size_t, _P]),
+    "gc_decompress_noalloc_max_chunks": (ctypes.c_uint64, [ctypes.c_int]),
+    "gc_decompress_accumulate_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int,
+                                                        _P]),
     "gc_dcd_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P]),
     "gc_dcd_decode": (ctypes.c_int, [_P, _P, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32, _P, _P]),
@@ -390,6 +393,19 @@ def gc_decompress_accumulate(plan: Plan, msgs, dense, mode: int, accumulate: boo
     _check(load().gc_decompress_accumulate(plan.handle, arr, K, _f32(dense, plan.n_total, "dense"),
                                            int(mode), int(bool(accumulate)), *_ws(ws),
                                            _stream(dense)))
+
+
+def gc_decompress_noalloc_max_chunks(K: int) -> int:
+    return int(load().gc_decompress_noalloc_max_chunks(int(K)))
+
+
+def gc_decompress_accumulate_noalloc(plan: Plan, msgs, dense, mode: int, accumulate: bool):
+    """gc_decompress_accumulate with the library's fixed device scratch in
+    place of a workspace; the plan must have been uploaded (Plan.upload)."""
+    K = len(msgs)
+    arr = (gc_sparse * max(K, 1))(*[m.checked(plan, f"msgs[{i}]") for i, m in enumerate(msgs)])
+    _check(load().gc_decompress_accumulate_noalloc(plan.handle, arr, K, _f32(dense, plan.n_total, "dense"),
+                                                   int(mode), int(bool(accumulate)), _stream(dense)))
 
 
 def gc_dcd_compress(x, x_half, x_out, bits: int, bucket: int, seed: int, step: int,

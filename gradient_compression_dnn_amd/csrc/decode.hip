@@ -13,6 +13,10 @@
 //           entries of the chunk into an LDS accumulator (one owner per
 //           element within a message), barrier; then divide by K and write
 #include <algorithm>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
 
 #include "gc_internal.hpp"
 
@@ -223,6 +227,75 @@ size_t decode_workspace_bytes(const gc_plan *plan) {
     return b;
 }
 
+namespace {
+
+// Host checks shared by both decode entry points; fills the message table.
+gc_status decode_args(const char *fn, const gc_plan *plan, const gc_sparse *msgs, int K, const float *dense,
+                      int mode, MsgTable *m) {
+    const std::string f(fn);
+    if (!plan) return set_error(GC_EINVAL, f + ": plan is null");
+    if (K < 1 || K > GC_MAX_MESSAGES) return set_error(GC_EINVAL, f + ": K must be in [1, GC_MAX_MESSAGES]");
+    if (!msgs || !dense) return set_error(GC_EINVAL, f + ": msgs and dense must be non-null");
+    if (mode != GC_SUM && mode != GC_AVG) return set_error(GC_EINVAL, f + ": mode must be GC_SUM or GC_AVG");
+    for (int k = 0; k < K; ++k) {
+        if (!msgs[k].idx || !msgs[k].val || !msgs[k].seg_off)
+            return set_error(GC_EINVAL, f + ": message pointers must be non-null");
+        m->idx[k] = msgs[k].idx;
+        m->val[k] = msgs[k].val;
+        m->count[k] = msgs[k].seg_off + plan->nseg;
+        m->cap[k] = std::min<uint64_t>(msgs[k].cap, 0xFFFFFFFFull);
+    }
+    return GC_OK;
+}
+
+gc_status decode_launch(const char *fn, const gc_plan *plan, const PlanDev &P, const MsgTable &m, int K,
+                        const DecWs &w, float *dense, int mode, int accumulate, hipStream_t stream) {
+    GC_LAUNCH("decode_index", stream,
+              decode_index_kernel<<<dim3(grid_1d(uint64_t(plan->ndchunk) + 1, kBlock), K), kBlock, 0, stream>>>(P, m, w));
+    GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
+                                                        accumulate != 0));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, fn);
+    return GC_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------- fixed scratch
+// gc_decompress_accumulate_noalloc keeps the index pass's start table in
+// this array instead of a caller workspace: K * (ndchunk + 1) u32, at most
+// kScratchBytes.  Every GPU the library runs on holds its own copy from the
+// code object's load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, once per
+// device, and is kept per device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, uint32_t *>> g_scratch_addr;  // (device, address of its copy)
+
+gc_status scratch_on_current_device(uint32_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_error(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const auto &pr : g_scratch_addr)
+        if (pr.first == dev) {
+            *out = pr.second;
+            return GC_OK;
+        }
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_error(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return set_error(GC_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_addr.emplace_back(dev, static_cast<uint32_t *>(ptr));
+    *out = static_cast<uint32_t *>(ptr);
+    return GC_OK;
+}
+}  // namespace
+
 }  // namespace gc
 
 using namespace gc;
@@ -231,21 +304,9 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
                                               float *dense, int mode, int accumulate, void *ws,
                                               size_t ws_bytes, hipStream_t stream) {
     clear_error();
-    if (!plan) return set_error(GC_EINVAL, "gc_decompress_accumulate: plan is null");
-    if (K < 1 || K > GC_MAX_MESSAGES)
-        return set_error(GC_EINVAL, "gc_decompress_accumulate: K must be in [1, GC_MAX_MESSAGES]");
-    if (!msgs || !dense) return set_error(GC_EINVAL, "gc_decompress_accumulate: msgs and dense must be non-null");
-    if (mode != GC_SUM && mode != GC_AVG)
-        return set_error(GC_EINVAL, "gc_decompress_accumulate: mode must be GC_SUM or GC_AVG");
     MsgTable m{};
-    for (int k = 0; k < K; ++k) {
-        if (!msgs[k].idx || !msgs[k].val || !msgs[k].seg_off)
-            return set_error(GC_EINVAL, "gc_decompress_accumulate: message pointers must be non-null");
-        m.idx[k] = msgs[k].idx;
-        m.val[k] = msgs[k].val;
-        m.count[k] = msgs[k].seg_off + plan->nseg;
-        m.cap[k] = std::min<uint64_t>(msgs[k].cap, 0xFFFFFFFFull);
-    }
+    gc_status st = decode_args("gc_decompress_accumulate", plan, msgs, K, dense, mode, &m);
+    if (st != GC_OK) return st;
     size_t need = decode_workspace_bytes(plan);
     if (!ws || ws_bytes < need)
         return set_error(GC_ECAPACITY,
@@ -253,14 +314,38 @@ extern "C" gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_spar
     if (reinterpret_cast<uintptr_t>(ws) % 256)
         return set_error(GC_EINVAL, "gc_decompress_accumulate: workspace must be 256-byte aligned");
     PlanDev P;
-    gc_status st = plan_device(plan, &P);
+    st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     DecWs w = dec_layout(plan, ws, nullptr);
-    GC_LAUNCH("decode_index", stream,
-              decode_index_kernel<<<dim3(grid_1d(uint64_t(plan->ndchunk) + 1, kBlock), K), kBlock, 0, stream>>>(P, m, w));
-    GC_LAUNCH("decode", stream, decode_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, m, K, w, dense, mode == GC_AVG,
-                                                        accumulate != 0));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_error(e, "gc_decompress_accumulate launch");
-    return GC_OK;
+    return decode_launch("gc_decompress_accumulate launch", plan, P, m, K, w, dense, mode, accumulate, stream);
+}
+
+extern "C" uint64_t gc_decompress_noalloc_max_chunks(int K) {
+    if (K < 1 || K > GC_MAX_MESSAGES) return 0;
+    return kScratchBytes / sizeof(uint32_t) / uint64_t(K) - 1;
+}
+
+extern "C" gc_status gc_decompress_accumulate_noalloc(const gc_plan *plan, const gc_sparse *msgs, int K,
+                                                      float *dense, int mode, int accumulate,
+                                                      hipStream_t stream) {
+    clear_error();
+    MsgTable m{};
+    gc_status st = decode_args("gc_decompress_accumulate_noalloc", plan, msgs, K, dense, mode, &m);
+    if (st != GC_OK) return st;
+    if (uint64_t(plan->ndchunk) > gc_decompress_noalloc_max_chunks(K))
+        return set_error(GC_ECAPACITY,
+                         "gc_decompress_accumulate_noalloc: K * (chunks + 1) start entries exceed the " +
+                             std::to_string(kScratchBytes >> 20) + " MiB fixed scratch (" +
+                             std::to_string(K) + " messages, " + std::to_string(plan->ndchunk) +
+                             " chunks); use gc_decompress_accumulate with a workspace");
+    PlanDev P;
+    st = plan_device_resident(plan, &P);
+    if (st != GC_OK) return st;
+    uint32_t *start = nullptr;
+    st = scratch_on_current_device(&start);
+    if (st != GC_OK) return st;
+    DecWs w{};
+    w.start = start;
+    return decode_launch("gc_decompress_accumulate_noalloc launch", plan, P, m, K, w, dense, mode, accumulate,
+                         stream);
 }

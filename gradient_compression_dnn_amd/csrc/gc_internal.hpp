@@ -107,6 +107,9 @@ void clear_error();
 
 // Device tables of a plan on the current device (uploads on first use).
 gc_status plan_device(const gc_plan *plan, PlanDev *out);
+// The same, for tables already on the current device (gc_plan_upload);
+// GC_EINVAL otherwise, without allocating.
+gc_status plan_device_resident(const gc_plan *plan, PlanDev *out);
 
 // Workspace bytes per operation (each op's translation unit lays out its own).
 size_t dgc_workspace_bytes(const gc_plan *plan);

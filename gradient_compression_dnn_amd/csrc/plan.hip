@@ -80,7 +80,7 @@ static BlobLayout blob_layout(const gc_plan *p) {
     return L;
 }
 
-gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
+static gc_status plan_tables(const gc_plan *cplan, PlanDev *out, bool upload) {
     gc_plan *plan = const_cast<gc_plan *>(cplan);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -91,6 +91,8 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
         std::lock_guard<std::mutex> lock(plan->mu);
         for (auto &pr : plan->dev_blob)
             if (pr.first == dev) blob = pr.second;
+        if (!blob && !upload)
+            return set_error(GC_EINVAL, "the plan's tables are not on the current device: call gc_plan_upload first");
         if (!blob) {
             e = hipMalloc(&blob, L.total);
             if (e != hipSuccess) return hip_error(e, "hipMalloc(plan tables)");
@@ -131,6 +133,10 @@ gc_status plan_device(const gc_plan *cplan, PlanDev *out) {
     out->n_total = plan->n_total;
     return GC_OK;
 }
+
+gc_status plan_device(const gc_plan *plan, PlanDev *out) { return plan_tables(plan, out, true); }
+
+gc_status plan_device_resident(const gc_plan *plan, PlanDev *out) { return plan_tables(plan, out, false); }
 
 }  // namespace gc
 

@@ -372,6 +372,31 @@ gc_status gc_decompress_accumulate(const gc_plan *plan, const gc_sparse *msgs,
                                    int accumulate, void *ws, size_t ws_bytes,
                                    hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation and results as gc_decompress_accumulate, with no workspace
+ * argument: the index pass's table (K * (chunks + 1) u32, where chunks is
+ * the plan's count of 4096-element tiles) lives in a fixed 8 MiB device
+ * array inside the library.  Each GPU holds its own copy until the process
+ * ends.  The call allocates nothing: it looks the array's address up once per
+ * device (hipGetSymbolAddress) and requires the plan's tables to be on the
+ * current device already (gc_plan_upload, outside the caller's hot loop).
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results; calls
+ * in one stream are ordered and safe.  Nothing in the array needs to start at
+ * any value: each call writes every entry it reads.
+ * gc_decompress_noalloc_max_chunks(K) is the largest plan chunk count the
+ * array holds for K messages (2,097,152 / K - 1; 0 for K out of range).
+ * Errors: as gc_decompress_accumulate, plus GC_ECAPACITY when the plan has
+ *         more chunks than that (checked on the host) and GC_EINVAL when the
+ *         plan was not uploaded to the current device.
+ */
+uint64_t  gc_decompress_noalloc_max_chunks(int K);
+gc_status gc_decompress_accumulate_noalloc(const gc_plan *plan, const gc_sparse *msgs,
+                                           int K, float *dense, int mode,
+                                           int accumulate, hipStream_t stream);
+
 /* ------------------------------------------------------------------- DCD */
 /*
  * Compressed model difference with random quantization ([DCD] DCD-PSGD step 2;

@@ -83,6 +83,19 @@ def test_plan_rejects_negative_offsets_from_the_binding():
         assert e.value.status == B.GC_EINVAL
 
 
+def test_noalloc_decode_capacity():
+    # 8 MiB of u32 start entries: K * (chunks + 1) <= 2^21
+    assert B.gc_decompress_noalloc_max_chunks(1) == (1 << 21) - 1
+    assert B.gc_decompress_noalloc_max_chunks(8) == (1 << 18) - 1
+    assert B.gc_decompress_noalloc_max_chunks(64) == (1 << 15) - 1
+    assert B.gc_decompress_noalloc_max_chunks(0) == 0
+    assert B.gc_decompress_noalloc_max_chunks(65) == 0
+    # the DeepSpeech layout (29,760 chunks) fits 64 messages
+    w = W.make_config("deepspeech")
+    assert B.Plan(w.table, w.n_total).total_k > 0
+    assert sum(-(-int(n) // 4096) for n in w.table[:, 1]) <= B.gc_decompress_noalloc_max_chunks(64)
+
+
 def test_plan_queries_and_workspace_on_workloads():
     for name in ("fc1m", "resnet50", "deepspeech"):
         w = W.make_config(name)
