@@ -26,18 +26,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 
-# Algorithmic bytes per launch of each kernel at this workload: what the
-# method itself must move (reads + writes of dense data, plus message bytes
-# where the kernel's job is the message).
+# Algorithmic bytes of each kernel in one step, summed over its launches in
+# the step: what the method itself must move (reads + writes of dense data,
+# plus message bytes where the kernel's job is the message).  Returns
+# {kernel: (bytes per step, launches per step)}.
 def algorithmic_bytes(n: int, nbins: int, k_total: int, ada_entries: int, bucket: int = 512):
     return {
-        "dgc_update": 20 * n,                 # read G, U, V; write U, V
-        "dgc_norm": 4 * n,                    # read G
-        "ada_fold": 12 * n,                   # read R, dW; write R (deferred residual: one pass)
-        "ada_emit": 8 * ada_entries,          # message
-        "dcd": 12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket),  # x, x_half, x_out, codes, scales
-        "decode": 4 * n + 4 * (k_total + ada_entries),  # dense write; the two messages, per launch
-        "dgc_emit": 8 * k_total + 8 * k_total,  # message out + masking writes
+        "dgc_update": (20 * n, 1),                 # read G, U, V; write U, V
+        "dgc_norm": (4 * n, 1),                    # read G
+        "ada_fold": (12 * n, 1),                   # read R, dW; write R (deferred residual: one pass)
+        "ada_emit": (8 * ada_entries, 1),          # message
+        "dcd": (12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket), 1),  # x, x_half, x_out, codes, scales
+        # two launches: each writes the dense update and reads its message
+        "decode": (8 * n + 8 * (k_total + ada_entries), 2),
+        "dgc_emit": (8 * k_total + 8 * k_total, 1),  # message out + masking writes
     }
 
 
@@ -105,11 +107,12 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
+def cpu_baseline(w, grad_host, x0, steps_min_s: float = 10.0, max_steps: int = 24):
     """The oracle, as it stands, over a bounded sample of the same workload;
     then one step on a single thread over a smaller sample, and the library
     on the first sample (same inputs and steps) compared bit for bit with
-    the oracle's last step."""
+    the oracle's last step.  grad_host(t, lo, hi) is elements [lo, hi) of
+    step t's gradient on the host (the same bits the library is given)."""
     import numpy as np
 
     import oracle
@@ -128,7 +131,7 @@ def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
 
     def one_step(sub, lo, hi, t, U, V, R):
         n = hi - lo
-        g = grads[t % len(grads)][lo:hi]
+        g = grad_host(t, lo, hi)
         x = x0[lo:hi]
         xh = W.dcd_half_step(x, g)
         t0 = time.perf_counter()
@@ -173,10 +176,10 @@ def cpu_baseline(w, grads, x0, steps_min_s: float = 10.0, max_steps: int = 24):
             "single_thread": {"value": round(2 * 4 * n1 / dt1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"1 step over the 8 tensors of GRU layer 2 ({n1:,} elements), "
                                         f"{dt1:.1f} s"},
-            "parity": library_parity(sub, lo, hi, grads, x0, done, last)}
+            "parity": library_parity(sub, lo, hi, grad_host, x0, done, last)}
 
 
-def library_parity(sub, lo, hi, grads, x0, steps, want):
+def library_parity(sub, lo, hi, grad_host, x0, steps, want):
     """The library over the oracle baseline's sample, with the same inputs and
     steps; the last step's outputs compared bit for bit with the oracle's."""
     import numpy as np
@@ -211,7 +214,7 @@ def library_parity(sub, lo, hi, grads, x0, steps, want):
     x = x0[lo:hi]
     X = f32(x)
     for t in range(steps):
-        gh = grads[t % len(grads)][lo:hi]
+        gh = grad_host(t, lo, hi)
         g, xh = f32(gh), f32(W.dcd_half_step(x, gh))
         B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC])
         B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK])
@@ -467,7 +470,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--grads", type=int, default=2, help="distinct seeded gradients cycled over steps")
+    ap.add_argument("--max-grads", type=int, default=64,
+                    help="most distinct seeded gradients held on the device (each step of the run "
+                         "draws its own while the run has at most this many steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the DGC Nesterov / sampled and DCD replica / ECD calls")
@@ -494,13 +499,20 @@ def main(argv=None):
     w = W.make_config("deepspeech")
     n = w.n_total
     plan = B.Plan(w.table, n)
-    log(f"workload deepspeech: {w.nseg} tensors, {n:,} elements; generating {args.grads} gradients")
-    grads = [W.gradient(w, t) for t in range(args.grads)]
+    # every step of the run (warm-up, instrumented, timed, breakdown, per-call)
+    # gets its own gradient, seed 5000 + t, drawn on the device before any
+    # step; past --max-grads steps the pool is cycled
+    run_steps = args.warmup + 2 * args.steps + 2
+    ng = max(1, min(run_steps, args.max_grads))
+    log(f"workload deepspeech: {w.nseg} tensors, {n:,} elements; drawing {ng} gradients on the device")
     x0 = W.dcd_model(w)
-
-    G = [torch.from_numpy(g).to(dev) for g in grads]
+    G = [W.gradient_device(w, t, dev) for t in range(ng)]
     X = torch.from_numpy(x0).to(dev)
     XH = [X - 0.1 * g for g in G]  # synthetic x_{t+1/2}, prepared outside the timed region
+    torch.cuda.synchronize()
+
+    def grad_host(t, lo, hi):
+        return G[t % ng][lo:hi].cpu().numpy()
     U = torch.zeros(n, dtype=torch.float32, device=dev)
     V = torch.zeros_like(U)
     R = torch.zeros_like(U)
@@ -587,6 +599,15 @@ def main(argv=None):
             breakdown[kname] = round(ms * 1000.0, 2)  # microseconds in one step
     B.gc_timing_enable(None)
 
+    # the DCD step's signal-to-noise measure (alpha of the DCD page):
+    # ||Z - C(Z)|| / ||Z|| with Z = x_half - x and C(Z) = x_out - x, taken
+    # here, while XO still holds the breakdown step's output for its XH
+    t_last = args.warmup + 1 + args.steps
+    z = (XH[t_last % len(XH)].double() - X.double())
+    cz = XO.double() - X.double()
+    dcd_alpha = float(torch.linalg.vector_norm(z - cz) / torch.linalg.vector_norm(z))
+    del z, cz
+
     # each call of the step alone: a few more steps with events between the
     # calls (outside the timed region), averaged per call
     call_ms = {c: 0.0 for c in CALLS}
@@ -631,15 +652,6 @@ def main(argv=None):
         best = ms if best is None else min(best, ms)
     stream_gbs = 20 * n / (best / 1000.0) / 1e9
 
-    # the DCD step's signal-to-noise measure (alpha of the DCD page):
-    # ||Z - C(Z)|| / ||Z|| with Z = x_half - x and C(Z) = x_out - x, for the
-    # breakdown step's inputs
-    t_last = args.warmup + 1 + args.steps
-    z = (XH[t_last % len(XH)].double() - X.double())
-    cz = XO.double() - X.double()
-    dcd_alpha = float(torch.linalg.vector_norm(z - cz) / torch.linalg.vector_norm(z))
-    del z, cz
-
     ada_entries = amsg.count()
     nbins = plan.total_bins
     alg = algorithmic_bytes(n, nbins, plan.total_k, ada_entries, bucket)
@@ -647,16 +659,19 @@ def main(argv=None):
     digest = source_digest()
     roof = None
     if dominant in alg:
-        ach = alg[dominant] / dom_avg_s / 1e9
+        per_launch = alg[dominant][0] // alg[dominant][1]
+        ach = per_launch / dom_avg_s / 1e9
         traffic = stored_traffic(dominant, digest)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "avg_us": round(dom_avg_s * 1e6, 2), "launches": dom_cnt,
-                "algorithmic_bytes_per_launch": alg[dominant]}
+                "algorithmic_bytes_per_launch": per_launch}
+    # each kernel's bytes over all its launches in the step, over its time in
+    # the step (breakdown sums the launches too)
     kernel_frac = {}
     for k, us in breakdown.items():
         if k in alg and us > 0:
-            kernel_frac[k] = round(alg[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            kernel_frac[k] = round(alg[k][0] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     # per method: the call's own time, the method's algorithmic bytes and the
     # counters' bytes of its kernels (pack and decode: both calls together)
@@ -667,19 +682,19 @@ def main(argv=None):
                 "counter_bytes": ctr, "counter_hbm_frac": frac(ctr)}
 
     methods = {
-        "dgc": method(call_ms["dgc"], alg["dgc_update"] + alg["dgc_emit"], ("dgc_",)),
-        "adacomp": method(call_ms["adacomp"], alg["ada_fold"] + alg["ada_emit"], ("ada_",)),
+        "dgc": method(call_ms["dgc"], alg["dgc_update"][0] + alg["dgc_emit"][0], ("dgc_",)),
+        "adacomp": method(call_ms["adacomp"], alg["ada_fold"][0] + alg["ada_emit"][0], ("ada_",)),
         "pack_both": method(call_ms["dgc_pack"] + call_ms["adacomp_pack"],
                             8 * (plan.total_k + ada_entries) + int(dn.item()) + int(an.item()), ("pack_",)),
-        "decode_both": method(call_ms["dgc_decode"] + call_ms["adacomp_decode"], 2 * alg["decode"], ("decode",)),
-        "dcd": method(call_ms["dcd"], alg["dcd"], ("dcd",)),
+        "decode_both": method(call_ms["dgc_decode"] + call_ms["adacomp_decode"], alg["decode"][0], ("decode",)),
+        "dcd": method(call_ms["dcd"], alg["dcd"][0], ("dcd",)),
     }
 
     value = 2 * 4 * n / (ms_per_step / 1000.0) / 1e9
     # the method's own bytes for the whole step: DGC 20 B/elt, AdaComp 12, DCD 12.5 + scales,
     # two dense decodes 4 each, plus the messages read and written
-    step_bytes = (alg["dgc_update"] + 12 * n + alg["dcd"] + 2 * alg["decode"]
-                  + alg["dgc_emit"] + 8 * ada_entries + int(dn.item()) + int(an.item()))
+    step_bytes = (alg["dgc_update"][0] + 12 * n + alg["dcd"][0] + alg["decode"][0]
+                  + alg["dgc_emit"][0] + 8 * ada_entries + int(dn.item()) + int(an.item()))
     result = {
         "metric": "GB/s of fp32 gradient compressed per step (+% HBM peak), DGC & AdaComp",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -692,6 +707,9 @@ def main(argv=None):
                                "per-tensor scales",
                    "step": "DGC(m=0.9, clip 1.0, top 0.1%, masking)+pack, AdaComp(L_T=500, x2)+pack, "
                            "2x decompress-average (K=1), DCD 4-bit bucket 512",
+                   "gradients": (f"a fresh seeded gradient per step (seed 5000 + t), {ng} drawn on the device "
+                                 f"before the run" + ("" if ng >= run_steps else
+                                                     f", cycled past {ng} of the run's {run_steps} steps")),
                    "parallelism": "single GPU (one learner)"},
         "step_alg_bytes": step_bytes,
         "step_alg_hbm_frac": round(step_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
@@ -726,7 +744,7 @@ def main(argv=None):
         result["configs"] = measure_configs(B, W, dev, log)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, grads, x0)
+        result["cpu_baseline"] = cpu_baseline(w, grad_host, x0)
         result["parity"] = result["cpu_baseline"].pop("parity")
     else:
         result["cpu_baseline"] = None

@@ -49,7 +49,8 @@ class gc_dgc_options(ctypes.Structure):
     _fields_ = [("momentum", ctypes.c_float), ("thr_G", ctypes.c_float),
                 ("num_nodes", ctypes.c_int), ("momentum_kind", ctypes.c_int),
                 ("select", ctypes.c_int), ("sample_period", ctypes.c_uint32),
-                ("over", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("over", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("density_num", ctypes.c_uint32), ("density_den", ctypes.c_uint32)]
 
 
 _lib = None
@@ -103,7 +104,7 @@ _SIGS = {
     "gc_stream_probe": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_uint64, _P]),
 }
 
-KERNELS = ("dgc_norm", "dgc_prep", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
+KERNELS = ("dgc_norm", "dgc_prep", "dgc_prepare", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "unpack_walk", "unpack_count", "unpack_scan",
@@ -348,11 +349,15 @@ def gc_dgc_step(plan: Plan, G, U, V, momentum: float, thr_G: float, num_nodes: i
 
 
 def dgc_options(momentum: float, thr_G: float = 0.0, num_nodes: int = 1, nesterov: bool = False,
-                sampled: bool = False, sample_period: int = 100, over: int = 2) -> gc_dgc_options:
+                sampled: bool = False, sample_period: int = 100, over: int = 2,
+                density: tuple[int, int] | None = None) -> gc_dgc_options:
+    """density=(num, den): this call keeps ceil(n_s num / den) entries per
+    segment instead of the plan's k (warm-up)."""
+    num, den = density if density is not None else (0, 0)
     return gc_dgc_options(float(momentum), float(thr_G), int(num_nodes),
                           GC_MOMENTUM_NESTEROV if nesterov else GC_MOMENTUM_VANILLA,
                           GC_SELECT_SAMPLED if sampled else GC_SELECT_EXACT,
-                          int(sample_period), int(over), 0)
+                          int(sample_period), int(over), 0, int(num), int(den))
 
 
 def gc_dgc_message_cap(plan: Plan, opt: gc_dgc_options) -> int:

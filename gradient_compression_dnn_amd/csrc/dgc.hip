@@ -73,6 +73,7 @@ struct SegState {
     uint32_t sent;  // entries the segment sends
     uint32_t base;  // first message slot of the segment
     uint32_t qrank, qprefix;  // sampled selection: quantile search state
+    uint32_t fshift;          // exact path: fine bins above Lkey are 2^fshift keys wide
 };
 
 // What the selection kernels rank (the key is the magnitude bits of a value):
@@ -130,6 +131,11 @@ __device__ __forceinline__ uint32_t sample_stride(uint32_t dnchunk) {
 constexpr uint32_t kHistRep = 16;
 static_assert(kHist1 == kHist2, "the sample bound reuses one LDS histogram for digits 1 and 2");
 
+// Exact path (DGC, exact selection): the staged keys are binned in
+// kFineBins bins of 2^fshift keys above the staging bound Lkey (the last bin
+// takes every key above the range).
+constexpr uint32_t kFineBins = kHist1;
+
 struct DgcWs {
     uint32_t *hist1, *hist2, *hist3;
     SegState *st;
@@ -139,7 +145,23 @@ struct DgcWs {
     float *sval;
     uint32_t *skey;  // [ndchunk][kSamples] key of the sampled V'
     uint32_t *qhist; // [nseg][kHist1] sample-quantile histogram (sampled selection)
+    // exact path
+    uint4 *crec;     // [ndchunk] emit record: first slot, end slot, T, staged count | quota << 16
+    uint32_t *cpack; // [ndchunk] per-chunk counts (two u16) for segments past the LDS tables
+    // the call's top-k count per segment: ceil(n_s * knum / kden) in [1, n_s],
+    // or the plan's k when kden is 0
+    uint32_t knum, kden;
 };
+
+// k_s of a segment for this call (warm-up densities are set per call).
+__host__ __device__ __forceinline__ uint32_t seg_topk(uint32_t len, uint32_t plan_k, uint32_t knum, uint32_t kden) {
+    if (kden == 0) return plan_k;
+    const uint64_t k = (uint64_t(len) * knum + kden - 1) / kden;
+    return k < 1 ? 1u : (k > len ? len : static_cast<uint32_t>(k));
+}
+__device__ __forceinline__ uint32_t seg_k(const SegDev &seg, const DgcWs &w) {
+    return seg_topk(seg.len, seg.k, w.knum, w.kden);
+}
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     WsCursor c(base);
@@ -154,10 +176,15 @@ DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.ceq = c.take<uint32_t>(p->ndchunk);
     w.cout = c.take<uint32_t>(p->ndchunk);
     w.ctake = c.take<uint32_t>(p->ndchunk);
-    w.sidx = c.take<uint32_t>(p->n_total);
-    w.sval = c.take<float>(p->n_total);
+    // staging: at a chunk's first element (the candidate kernels), or in the
+    // chunk's own 4096-entry slot (the exact path), whichever is larger
+    const size_t nstage = std::max<size_t>(p->n_total, size_t(p->ndchunk) << kChunkLog2);
+    w.sidx = c.take<uint32_t>(nstage);
+    w.sval = c.take<float>(nstage);
     w.skey = c.take<uint32_t>(size_t(p->ndchunk) * kSamples);
     w.qhist = c.take<uint32_t>(size_t(p->nseg) * kHist1);
+    w.crec = c.take<uint4>(p->ndchunk);
+    w.cpack = c.take<uint32_t>(p->ndchunk);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -510,7 +537,7 @@ __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
     const uint32_t last_cnt = min(seg.len - last * uint32_t(kChunk), uint32_t(kChunk));
     const uint32_t last_ns = min(kSamples, last_cnt);
     const uint32_t total = (nsc - 1) * kSamples + last_ns;
-    const double E = double(total) * double(seg.k) / double(seg.len);
+    const double E = double(total) * double(seg_k(seg, w)) / double(seg.len);
     const double target = E + 4.0 * sqrt(E) + 16.0;
     if (!(target < double(total))) {  // uniform: too few samples, stage everything
         if (threadIdx.x == 0) w.st[s].Lkey = 0u;
@@ -568,7 +595,13 @@ __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
 //
 // The DGC modes read G, U and V and write U and V; kSignif reads g and w and
 // writes nothing dense; kExplore reads only the core bitmap.
-template <int kMode>
+//
+// kFine (the exact path): no histogram; the staged entries go to the chunk's
+// own 4096-entry slot (c * 4096, 16-byte aligned) instead of its first
+// element.  (The exact path's select histograms the staged keys itself:
+// counting them here raised the kernel to 130 VGPRs, three waves per SIMD,
+// and cost it 5% of its bandwidth.)
+template <int kMode, bool kFine = false>
 __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, DgcWs w) {
     constexpr bool kDgc = kMode == kVanilla || kMode == kNesterov;
     uint32_t c0, c1;
@@ -618,9 +651,9 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                 }
                 const float vn = v[j][q];
                 const bool in = e0 + q < ci.cnt;
-                const uint32_t d = mag_key(vn) >> (kDigit2Bits + kDigit3Bits);
-                if (in) atomicAdd(&hist[d], 1u);
-                const bool f = in && mag_key(vn) >= Lkey;
+                const uint32_t key = mag_key(vn);
+                const bool f = in && key >= Lkey;
+                if (!kFine && in) atomicAdd(&hist[key >> (kDigit2Bits + kDigit3Bits)], 1u);
                 flags[j] |= uint32_t(f) << q;
                 const uint64_t bm = __ballot(f);
                 before[j] += lane_rank(bm);
@@ -644,10 +677,11 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                     run += pc[j * kWaves + ww];
                 }
             if (threadIdx.x == 0) w.ccount[c] = run;
+            const uint32_t slot0 = kFine ? (c << kChunkLog2) : static_cast<uint32_t>(ci.lo);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) {
                 if (!flags[j]) continue;
-                uint32_t slot = static_cast<uint32_t>(ci.lo) + base[j] + before[j];
+                uint32_t slot = slot0 + base[j] + before[j];
                 const uint32_t e0 = static_cast<uint32_t>(ci.lo) + row_elem(j);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -665,7 +699,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
             ci = walk.at(P, c + 1);
             fetch(ci);
         }
-        if (!more || ci.s != s_done) {
+        if (!kFine && (!more || ci.s != s_done)) {
             __syncthreads();
             uint32_t *h1 = w.hist1 + (size_t(s_done) * kHistRep + blockIdx.x % kHistRep) * kHist1;
             for (int i = threadIdx.x; i < kHist1; i += kBlock) {
@@ -700,7 +734,8 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
     uint32_t above;
     if (kLevel == 1) {
         const uint32_t *h = w.hist1 + size_t(s) * kHistRep * kHist1;
-        uint32_t d = block_find_bucket<kHist1>(seg.k, [&](int b) { return replica_sum<kHist1>(h, b); }, &above);
+        const uint32_t ks = seg_k(seg, w);
+        uint32_t d = block_find_bucket<kHist1>(ks, [&](int b) { return replica_sum<kHist1>(h, b); }, &above);
         // entries the update staged in the segment (all keys >= Lkey)
         uint32_t staged = 0;
         for (uint32_t i0 = 0; i0 < seg.dnchunk; i0 += 8 * kBlock) {
@@ -719,10 +754,10 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
             w.st[s].above1 = above;
             w.st[s].redo = 0u;
             w.st[s].all = 0u;
-            w.st[s].sent = seg.k;
+            w.st[s].sent = ks;
             w.st[s].base = seg.kbase;
             if (over == 0) {
-                w.st[s].redo = staged_total < seg.k ? 1u : 0u;
+                w.st[s].redo = staged_total < ks ? 1u : 0u;
             } else {
                 const uint64_t budget = min<uint64_t>(seg.len, uint64_t(over) * seg.k);
                 if (staged_total <= budget) {
@@ -737,7 +772,7 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
     } else if (kLevel == 2) {
         if (st.all) return;
         const uint32_t *h = w.hist2 + size_t(s) * kHistRep * kHist2;
-        uint32_t d = block_find_bucket<kHist2>(seg.k - st.above1, [&](int b) { return replica_sum<kHist2>(h, b); },
+        uint32_t d = block_find_bucket<kHist2>(seg_k(seg, w) - st.above1, [&](int b) { return replica_sum<kHist2>(h, b); },
                                                &above);
         if (threadIdx.x == 0) {
             w.st[s].d2 = d;
@@ -746,12 +781,13 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
     } else {
         if (st.all) return;
         const uint32_t *h = w.hist3 + size_t(s) * kHist3;
-        uint32_t d = block_find_bucket<kHist3>(seg.k - st.above2, [&](int b) { return h[b]; }, &above);
+        const uint32_t ks = seg_k(seg, w);
+        uint32_t d = block_find_bucket<kHist3>(ks - st.above2, [&](int b) { return h[b]; }, &above);
         if (threadIdx.x == 0) {
             uint32_t gt = st.above2 + above;
             w.st[s].T = (((st.d1 << kDigit2Bits) | st.d2) << kDigit3Bits) | d;
             w.st[s].gt = gt;
-            w.st[s].need_eq = seg.k - gt;
+            w.st[s].need_eq = ks - gt;
         }
     }
 }
@@ -1192,6 +1228,563 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
     }
 }
 
+// ================================================================ exact path
+// Exact DGC selection (vanilla and Nesterov) in four launches after the clip
+// norm, for plans where every tensor of more than one chunk keeps at most
+// 1/512 of its entries:
+//   prepare (segment) the clip factor; V' at a sample of up to 16,384
+//           entries; the staging bound Lkey and the width 2^fshift of the
+//           fine bins above it (the bins reach the largest sampled key)
+//   update  (chunk)   dgc_update_kernel<kMode, true>: U, V and the staging of
+//           every key >= Lkey in the chunk's own slot
+//   select  (segment) a histogram of the staged keys by fine bin gives T's
+//           bin; a second pass takes that bin's keys to LDS (T) and each
+//           chunk's keys above and in the bin; then each chunk's message
+//           slots and tie quota, in index order
+//   emit    (chunk)   the chunk's entries in index order, U and V masked
+// Rare cases stay exact on slower branches of select: T's bin holding more
+// keys than LDS, or T above the fine bins (three radix passes over the
+// staged keys), and fewer than k staged entries (the sample bound was too
+// high: three radix passes over V, then the segment is staged again).
+constexpr int kSelBlock = 1024;
+constexpr uint32_t kSampleMax = 16384;  // sampled entries per tensor at most
+constexpr uint32_t kPrepPer = kSampleMax / kSelBlock;
+constexpr uint32_t kSelKeys = 8192;     // LDS list of the keys in T's fine bin
+constexpr uint32_t kQuadRun = 10;       // chunks per quad of lanes in a round of a per-chunk pass
+constexpr uint32_t kWalkChunks = kSelBlock / 4 * kQuadRun;  // chunks per round of a per-chunk pass
+constexpr uint32_t kSelScanRun = 5;                         // chunks per thread in a round of the ordered scan
+constexpr uint32_t kSelChunks = kSelBlock * kSelScanRun;   // chunks per round of the ordered scan, and
+                                                            // of per-chunk values kept in LDS
+constexpr uint32_t kThreadN = 128;      // staged entries one thread counts; more: a wave
+constexpr uint32_t kFastDensity = 512;  // exact path when k_s * 512 <= n_s (or one chunk)
+
+// Sample of a tensor for the exact path: one chunk, all of it; up to 512
+// chunks, a block of sc = min(4096, (16384 / chunks) rounded down to 32)
+// contiguous entries per chunk; more chunks, 32 entries of every stride-th
+// chunk.  Full chunks start their block at min(128 ((13 c) mod 32),
+// 4096 - sc) (c the plan-wide chunk number), a partial last chunk at 0.
+struct SampleShape {
+    uint32_t stride, nsc, sc, total, last_cnt;
+};
+__device__ __forceinline__ SampleShape sample_shape(const SegDev &seg) {
+    SampleShape z;
+    if (seg.dnchunk == 1) {
+        z.stride = 1;
+        z.nsc = 1;
+        z.sc = seg.len;
+    } else if (seg.dnchunk <= kSampleChunks) {
+        z.stride = 1;
+        z.nsc = seg.dnchunk;
+        z.sc = min(uint32_t(kChunk), (kSampleMax / seg.dnchunk) & ~(kSamples - 1));
+    } else {
+        z.stride = sample_stride(seg.dnchunk);
+        z.nsc = (seg.dnchunk + z.stride - 1) / z.stride;
+        z.sc = kSamples;
+    }
+    z.last_cnt = min(seg.len - (z.nsc - 1) * z.stride * uint32_t(kChunk), uint32_t(kChunk));
+    z.total = (z.nsc - 1) * z.sc + min(z.sc, z.last_cnt);
+    return z;
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kSelBlock) void dgc_prepare_kernel(PlanDev P, Src a, DgcWs w, int use_clip,
+                                                                 float thr) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    const uint32_t k = seg_k(seg, w);
+    // the sample's G, U, V first (in flight during the clip factor's tree);
+    // sample q = sc j + l is entry l of sampled chunk j, thread t takes
+    // q = t, t + 1024, ...
+    const SampleShape z = sample_shape(seg);
+    float gs[kPrepPer], us[kPrepPer], vs[kPrepPer];
+    uint32_t valid = 0;
+#pragma unroll
+    for (uint32_t u = 0; u < kPrepPer; ++u) {
+        const uint32_t q = u * kSelBlock + threadIdx.x;
+        gs[u] = us[u] = vs[u] = 0.0f;
+        if (q < z.total) {
+            const uint32_t j = q / z.sc, l = q - j * z.sc;
+            const uint32_t cnt = j + 1 < z.nsc ? uint32_t(kChunk) : z.last_cnt;
+            const uint32_t off = cnt == uint32_t(kChunk)
+                                     ? min(sample_offset(seg.dchunk0 + j * z.stride, cnt), uint32_t(kChunk) - z.sc)
+                                     : 0u;
+            const uint64_t e = seg.off + (uint64_t(j * z.stride) << kChunkLog2) + off + l;
+            gs[u] = a.G[e];
+            us[u] = a.U[e];
+            vs[u] = a.V[e];
+            valid |= 1u << u;
+        }
+    }
+    float cl = 1.0f;
+    if (use_clip) {
+        const double *part = w.partial + seg.dchunk0;
+        const double S = block_pairwise_sum<kSelBlock>(seg.dnchunk, [&](uint64_t g) { return part[g]; });
+        const double norm = sqrt(S);
+        if (norm > static_cast<double>(thr)) cl = static_cast<float>(static_cast<double>(thr) / norm);
+    }
+    uint32_t key[kPrepPer], kmax = 0;
+#pragma unroll
+    for (uint32_t u = 0; u < kPrepPer; ++u) {
+        const float gc = cl * gs[u];
+        float un = us[u], vn = vs[u];
+        momentum_update<kMode>(a.m, gc, un, vn);
+        key[u] = mag_key(vn);
+        if ((valid >> u) & 1u) kmax = max(kmax, key[u]);
+    }
+    __shared__ uint32_t h[kHist1];
+    __shared__ uint32_t wmax[kSelBlock / kWave];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    if (lane_id() == 0) wmax[wave_id()] = kmax;
+    __syncthreads();
+    uint32_t Hkey = 0;
+    for (int i = 0; i < kSelBlock / kWave; ++i) Hkey = max(Hkey, wmax[i]);
+    // Lkey: the (E + 4 sqrt(E) + 16)-th largest sample key rounded down to its
+    // 22-bit prefix, with E = total k / n the expected sampled top-k entries
+    // (0, stage everything, when the sample is too small for that)
+    const double E = double(z.total) * double(k) / double(seg.len);
+    const double target = E + 4.0 * sqrt(E) + 16.0;
+    uint32_t Lkey = 0;
+    if (target < double(z.total)) {
+        uint32_t rank = static_cast<uint32_t>(target), prefix = 0;
+        for (int level = 0; level < 2; ++level) {
+            for (int i = threadIdx.x; i < kHist1; i += kSelBlock) h[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (uint32_t u = 0; u < kPrepPer; ++u) {
+                if (!((valid >> u) & 1u)) continue;
+                const uint32_t d1 = key[u] >> (kDigit2Bits + kDigit3Bits);
+                if (level == 0) atomicAdd(&h[d1], 1u);
+                else if (d1 == prefix) atomicAdd(&h[(key[u] >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            }
+            __syncthreads();
+            uint32_t above;
+            const uint32_t d = block_find_bucket<kHist1, kSelBlock>(rank, [&](int b) { return h[b]; }, &above);
+            rank -= above;
+            prefix = level == 0 ? d : ((prefix << kDigit2Bits) | d);
+            __syncthreads();
+        }
+        Lkey = prefix << kDigit3Bits;
+    }
+    if (threadIdx.x == 0) {
+        uint32_t fs = 0;
+        if (Hkey > Lkey)
+            while (((Hkey - Lkey) >> fs) > kFineBins - 2) ++fs;
+        SegState &st = w.st[s];
+        st.clip = cl;
+        st.Lkey = Lkey;
+        st.fshift = fs;
+        st.sent = k;
+        st.base = seg.kbase;
+        st.redo = 0u;
+        st.all = 0u;
+    }
+}
+
+// Per-chunk values over the staged keys of a segment's chunks [r0, r1):
+// settle(i, n, &v) may give chunk i's value without its keys; otherwise
+// v = sum of count(key) over its staged keys (two u16 counts in a u32, so
+// count may also record keys elsewhere); then store(i, v).  Four lanes (a
+// quad) share a chunk, so one wave load covers 16 chunks' first 16 keys in 16
+// lines (a chunk's staged keys start its 16 KB slot): quad Q takes the chunks
+// [r0 + Q per, +per), per <= kQuadRun, loads all their counts, then 16 keys
+// of every one of them per round of loads (a chunk holds some 13 at the 0.1%
+// density of the pages).  A chunk of more than kThreadN staged entries goes
+// to a list whose chunks are counted one per wave, 1024 keys per round.
+template <class Settle, class Count, class Store>
+__device__ __forceinline__ void sel_walk_round(const SegDev &seg, const DgcWs &w, uint32_t r0, uint32_t r1,
+                                               Settle settle, Count count, Store store, uint32_t *big,
+                                               uint32_t *nbig) {
+    if (threadIdx.x == 0) *nbig = 0u;
+    __syncthreads();
+    const uint32_t quad = threadIdx.x >> 2, ql = threadIdx.x & 3u;
+    const uint32_t per = (r1 - r0 + kSelBlock / 4 - 1) / (kSelBlock / 4);  // <= kQuadRun
+    const uint32_t t0 = r0 + quad * per;
+    uint32_t n[kQuadRun], v[kQuadRun];
+    uint32_t need = 0;  // bit b: chunk t0 + b is counted by the quad
+#pragma unroll
+    for (uint32_t b = 0; b < kQuadRun; ++b) {
+        const uint32_t i = t0 + b;
+        const bool act = b < per && i < r1;
+        n[b] = act ? min(w.ccount[seg.dchunk0 + i], min(uint32_t(kChunk), seg.len - (i << kChunkLog2))) : 0u;
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < kQuadRun; ++b) {
+        const uint32_t i = t0 + b;
+        v[b] = 0u;
+        if (b < per && i < r1 && !settle(i, n[b], &v[b])) {
+            if (n[b] > kThreadN) {
+                if (ql == 0) big[atomicAdd(nbig, 1u)] = i;
+            } else {
+                need |= 1u << b;
+            }
+        }
+    }
+    auto add4 = [&](uint32_t &acc, const uint4 &q, uint32_t e, uint32_t nn) {
+        if (e < nn) acc += count(q.x & 0x7FFFFFFFu);
+        if (e + 1 < nn) acc += count(q.y & 0x7FFFFFFFu);
+        if (e + 2 < nn) acc += count(q.z & 0x7FFFFFFFu);
+        if (e + 3 < nn) acc += count(q.w & 0x7FFFFFFFu);
+    };
+    uint32_t nmax = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < kQuadRun; ++b) nmax = max(nmax, ((need >> b) & 1u) ? n[b] : 0u);
+    for (uint32_t q0 = 0; q0 < nmax; q0 += 16) {
+        uint4 x[kQuadRun];
+#pragma unroll
+        for (uint32_t b = 0; b < kQuadRun; ++b) {
+            const bool ld = ((need >> b) & 1u) && q0 < n[b];
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                w.sval + (size_t(seg.dchunk0 + (ld ? t0 + b : 0u)) << kChunkLog2));
+            x[b] = ld ? src[(q0 >> 2) + ql] : make_uint4(0u, 0u, 0u, 0u);  // inside the chunk's 4096-entry slot
+        }
+#pragma unroll
+        for (uint32_t b = 0; b < kQuadRun; ++b)
+            if ((need >> b) & 1u) add4(v[b], x[b], q0 + 4 * ql, n[b]);
+    }
+    // the quad's four partial counts of each chunk
+#pragma unroll
+    for (uint32_t b = 0; b < kQuadRun; ++b) {
+        if ((need >> b) & 1u) {
+            v[b] += __shfl_xor(v[b], 1);
+            v[b] += __shfl_xor(v[b], 2);
+        }
+    }
+    // (the shuffles above run in every lane of a quad alike: need, n and per
+    // are the quad's)
+#pragma unroll
+    for (uint32_t b = 0; b < kQuadRun; ++b)
+        if (ql == 0 && b < per && t0 + b < r1) store(t0 + b, v[b]);
+    __syncthreads();
+    const uint32_t nb = *nbig;
+    const int lane = lane_id();
+    for (uint32_t bi = wave_id(); bi < nb; bi += kSelBlock / kWave) {
+        const uint32_t i = big[bi];
+        const uint32_t nn = min(w.ccount[seg.dchunk0 + i], min(uint32_t(kChunk), seg.len - (i << kChunkLog2)));
+        const uint4 *src = reinterpret_cast<const uint4 *>(w.sval + (size_t(seg.dchunk0 + i) << kChunkLog2));
+        uint32_t acc = 0;
+        for (uint32_t q0 = 0; q0 < nn; q0 += 4 * 4 * kWave) {
+            uint4 y[4];
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) y[u] = src[min((q0 >> 2) + u * kWave + lane, uint32_t(kChunk / 4 - 1))];
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) add4(acc, y[u], q0 + 4 * (u * kWave + lane), nn);
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) store(i, acc);
+    }
+    __syncthreads();
+}
+
+template <class Settle, class Count, class Store>
+__device__ __forceinline__ void sel_walk(const SegDev &seg, const DgcWs &w, uint32_t r0, uint32_t r1,
+                                         Settle settle, Count count, Store store, uint32_t *big, uint32_t *nbig) {
+    for (uint32_t q0 = r0; q0 < r1; q0 += kWalkChunks)
+        sel_walk_round(seg, w, q0, min(r1, q0 + kWalkChunks), settle, count, store, big, nbig);
+}
+
+// The rank-th largest key (1 <= rank <= keys visited) among the keys that
+// each(f) visits (f(key) for every key, from whichever threads), by three
+// LDS histogram passes over the 11, 11 and 9-bit digits.  *gt receives the
+// number of keys above it.
+template <class Each>
+__device__ __forceinline__ uint32_t sel_radix(uint32_t rank, Each each, uint32_t *h, uint32_t *gt) {
+    uint32_t prefix = 0, above_all = 0;
+    for (int level = 0; level < 3; ++level) {
+        const int nb = level == 2 ? kHist3 : kHist1;
+        const int shift = level == 0 ? kDigit2Bits + kDigit3Bits : level == 1 ? kDigit3Bits : 0;
+        const int pshift = level == 1 ? kDigit2Bits + kDigit3Bits : kDigit3Bits;
+        for (int i = threadIdx.x; i < nb; i += kSelBlock) h[i] = 0u;
+        __syncthreads();
+        each([&](uint32_t key) {
+            if (level == 0 || (key >> pshift) == prefix) atomicAdd(&h[(key >> shift) & uint32_t(nb - 1)], 1u);
+        });
+        __syncthreads();
+        uint32_t above, d;
+        if (level == 2) d = block_find_bucket<kHist3, kSelBlock>(rank, [&](int b) { return h[b]; }, &above);
+        else d = block_find_bucket<kHist1, kSelBlock>(rank, [&](int b) { return h[b]; }, &above);
+        rank -= above;
+        above_all += above;
+        prefix = level == 0 ? d : level == 1 ? ((prefix << kDigit2Bits) | d) : ((prefix << kDigit3Bits) | d);
+        __syncthreads();
+    }
+    *gt = above_all;
+    return prefix;
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a, DgcWs w,
+                                                                 uint32_t *__restrict__ seg_off) {
+    const uint32_t s = blockIdx.x;
+    const SegDev seg = P.seg[s];
+    const uint32_t k = w.st[s].sent, Lkey = w.st[s].Lkey, fs = w.st[s].fshift, base = w.st[s].base;
+    const uint32_t nch = seg.dnchunk, c0 = seg.dchunk0;
+    __shared__ uint32_t h[kFineBins];
+    __shared__ uint32_t list[kSelKeys];
+    __shared__ uint32_t cpk[kSelChunks];
+    __shared__ uint32_t big[kWalkChunks];
+    __shared__ uint32_t sh_n, sh_nbig;
+    // per-chunk values: LDS when one round covers the segment, else the workspace
+    const bool one_round = nch <= kSelChunks;
+    auto pk_store = [&](uint32_t i, uint32_t v) {
+        if (one_round) cpk[i] = v;
+        else w.cpack[c0 + i] = v;
+    };
+    auto pk_load = [&](uint32_t i) { return one_round ? cpk[i] : w.cpack[c0 + i]; };
+    auto chunk_len = [&](uint32_t i) { return min(uint32_t(kChunk), seg.len - (i << kChunkLog2)); };
+    auto bin_of = [&](uint32_t key) { return min((key - Lkey) >> fs, kFineBins - 1); };
+    auto never = [](uint32_t, uint32_t, uint32_t *) { return false; };
+    auto each_staged = [&](auto f) {
+        sel_walk(
+            seg, w, 0, nch, never,
+            [&](uint32_t key) {
+                f(key);
+                return 0u;
+            },
+            [](uint32_t, uint32_t) {}, big, &sh_nbig);
+    };
+
+    uint32_t my = 0;
+    for (uint32_t i = threadIdx.x; i < nch; i += kSelBlock) my += min(w.ccount[c0 + i], chunk_len(i));
+    uint32_t staged;
+    (void)block_exclusive_scan<uint32_t, kSelBlock>(my, &staged);
+    uint32_t T, gt;
+    bool have_pk = false;  // cpk holds each chunk's keys above T's bin (low) and in it (high)
+    bool all_eq = false;   // every staged key equals T
+    if (staged < k) {
+        // the sample bound was above the k-th key: select over V itself, then
+        // stage every chunk's entries with key >= T again
+        auto each_v = [&](auto f) {
+            for (uint32_t i = 0; i < nch; ++i) {
+                const uint32_t cnt = chunk_len(i);
+                const BufRsrc rv = chunk_buf(a.V + seg.off + (uint64_t(i) << kChunkLog2), cnt);
+                float v[4];
+                load4(rv, 4u * threadIdx.x, v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (4u * threadIdx.x + q < cnt) f(mag_key(v[q]));
+            }
+        };
+        T = sel_radix(k, each_v, h, &gt);
+        for (uint32_t i = 0; i < nch; ++i) {
+            const uint32_t cnt = chunk_len(i);
+            const uint64_t lo = seg.off + (uint64_t(i) << kChunkLog2);
+            const BufRsrc rv = chunk_buf(a.V + lo, cnt);
+            float v[4];
+            load4(rv, 4u * threadIdx.x, v);
+            bool f[4];
+            uint32_t nf = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f[q] = 4u * threadIdx.x + q < cnt && mag_key(v[q]) >= T;
+                nf += f[q] ? 1u : 0u;
+            }
+            uint32_t tot;
+            uint32_t slot = block_exclusive_scan<uint32_t, kSelBlock>(nf, &tot);
+            const size_t sbase = size_t(c0 + i) << kChunkLog2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (f[q]) {
+                    w.sidx[sbase + slot] = static_cast<uint32_t>(lo) + 4u * threadIdx.x + q;
+                    w.sval[sbase + slot] = v[q];
+                    ++slot;
+                }
+            if (threadIdx.x == 0) w.ccount[c0 + i] = tot;
+        }
+        __syncthreads();
+    } else {
+        // the staged keys by fine bin
+        for (int i = threadIdx.x; i < int(kFineBins); i += kSelBlock) h[i] = 0u;
+        __syncthreads();
+        sel_walk(
+            seg, w, 0, nch, never,
+            [&](uint32_t key) {
+                atomicAdd(&h[bin_of(key)], 1u);
+                return 0u;
+            },
+            [](uint32_t, uint32_t) {}, big, &sh_nbig);
+        uint32_t above;
+        const uint32_t bstar = block_find_bucket<kFineBins, kSelBlock>(k, [&](int b) { return h[b]; }, &above);
+        const uint32_t cnt_b = h[bstar];
+        __syncthreads();
+        if (bstar == kFineBins - 1 || (fs > 0 && cnt_b > kSelKeys)) {
+            // T above the fine bins, or its bin too full for LDS
+            T = sel_radix(k, each_staged, h, &gt);
+        } else if (fs == 0 && cnt_b == staged) {
+            T = Lkey + bstar;  // one key per bin, and every staged key in T's
+            gt = 0;
+            all_eq = true;
+        } else {
+            // each chunk's keys above and in T's bin, and (bins wider than
+            // one key) that bin's keys into LDS
+            if (threadIdx.x == 0) sh_n = 0u;
+            __syncthreads();
+            auto count = [&](uint32_t key) {
+                const uint32_t b = bin_of(key);
+                if (b > bstar) return 1u;
+                if (b < bstar) return 0u;
+                if (fs > 0) {
+                    const uint32_t at = atomicAdd(&sh_n, 1u);
+                    if (at < kSelKeys) list[at] = key;
+                }
+                return 1u << 16;
+            };
+            sel_walk(seg, w, 0, nch, never, count, [&](uint32_t i, uint32_t v) { pk_store(i, v); }, big, &sh_nbig);
+            have_pk = one_round;
+            if (fs == 0) {
+                T = Lkey + bstar;
+                gt = above;
+            } else {
+                const uint32_t m = min(sh_n, kSelKeys);
+                uint32_t gt_in;
+                T = sel_radix(k - above, [&](auto f) {
+                    for (uint32_t i = threadIdx.x; i < m; i += kSelBlock) f(list[i]);
+                }, h, &gt_in);
+                gt = above + gt_in;
+            }
+        }
+    }
+    const uint32_t need_eq = k - gt;
+    // each chunk's keys above and at T (low and high u16), then the ordered
+    // scan: ties go to the lowest indices, so a chunk's quota is what the
+    // ties of the chunks before it leave
+    auto settle2 = [&](uint32_t i, uint32_t n, uint32_t *v) {
+        if (n == 0) {
+            *v = 0u;
+            return true;
+        }
+        if (all_eq) {
+            *v = n << 16;
+            return true;
+        }
+        if (have_pk) {
+            const uint32_t pk = pk_load(i);
+            // nothing in T's bin (its keys above the bin are above T), or a
+            // bin of one key (its keys equal T)
+            if ((pk >> 16) == 0 || fs == 0) {
+                *v = pk;
+                return true;
+            }
+        }
+        return false;
+    };
+    auto count2 = [&](uint32_t key) { return (key > T ? 1u : 0u) | (key == T ? 1u << 16 : 0u); };
+    uint32_t eq_before = 0, sel_before = 0;
+    for (uint32_t r0 = 0; r0 < nch; r0 += kSelChunks) {
+        const uint32_t r1 = min(nch, r0 + kSelChunks);
+        sel_walk(seg, w, r0, r1, settle2, count2, [&](uint32_t i, uint32_t v) { pk_store(i, v); }, big, &sh_nbig);
+        // the round's chunks in order: thread t takes [r0 + t per, +per)
+        const uint32_t per = (r1 - r0 + kSelBlock - 1) / kSelBlock;
+        const uint32_t t0 = r0 + threadIdx.x * per;
+        uint32_t pk[kSelScanRun], nn[kSelScanRun];
+        uint32_t eq_sum = 0, gt_sum = 0;
+#pragma unroll
+        for (uint32_t b = 0; b < kSelScanRun; ++b) {
+            const uint32_t i = t0 + b;
+            const bool act = b < per && i < r1;
+            pk[b] = act ? pk_load(i) : 0u;
+            nn[b] = act ? min(w.ccount[c0 + i], chunk_len(i)) : 0u;
+            eq_sum += pk[b] >> 16;
+            gt_sum += pk[b] & 0xFFFFu;
+        }
+        uint32_t eq_tot;
+        const uint32_t eq_pre = eq_before + block_exclusive_scan<uint32_t, kSelBlock>(eq_sum, &eq_tot);
+        const uint32_t take_run = need_eq > eq_pre ? min(need_eq - eq_pre, eq_sum) : 0u;
+        uint32_t sel_tot;
+        const uint32_t sel_pre = sel_before + block_exclusive_scan<uint32_t, kSelBlock>(gt_sum + take_run, &sel_tot);
+        uint32_t eq_run = eq_pre, sel_run = sel_pre;
+#pragma unroll
+        for (uint32_t b = 0; b < kSelScanRun; ++b) {
+            const uint32_t i = t0 + b;
+            if (b < per && i < r1) {
+                const uint32_t e = pk[b] >> 16, g = pk[b] & 0xFFFFu;
+                const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e) : 0u;
+                w.crec[c0 + i] = make_uint4(base + sel_run, base + sel_run + g + take, T, nn[b] | (take << 16));
+                eq_run += e;
+                sel_run += g + take;
+            }
+        }
+        eq_before += eq_tot;
+        sel_before += sel_tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        w.st[s].T = T;
+        w.st[s].gt = gt;
+        w.st[s].need_eq = need_eq;
+        seg_off[s] = base;
+        if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = base + k;
+    }
+}
+
+// Each of the wave's chunks in turn (records and first entries of all CPW
+// chunks loaded together): staged entries in index order, 64 at a time;
+// entries above T are sent, ties at T up to the chunk's quota in index order;
+// slots from ballots, never past the chunk's last slot; U and V masked at the
+// sent entries.  Record: first slot, end slot, T, staged count | quota << 16.
+template <int kMode, uint32_t CPW>
+__global__ __launch_bounds__(kBlock) void dgc_xemit_kernel(PlanDev P, Src a, DgcWs w,
+                                                           uint32_t *__restrict__ out_idx,
+                                                           float *__restrict__ out_val) {
+    const uint32_t c0 = wave_chunk0<CPW>();
+    if (c0 >= P.ndchunk) return;
+    const int lane = lane_id();
+    const uint4 rec = w.crec[min(c0 + uint32_t(lane) % CPW, P.ndchunk - 1)];
+    uint32_t id0[CPW];
+    float v0[CPW];
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        const bool any = lane_val(rec.y, j) != lane_val(rec.x, j);
+        const uint32_t n = any ? min(lane_val(rec.w, j) & 0xFFFFu, uint32_t(kChunk)) : 0u;
+        const size_t ic = (size_t(c0 + j) << kChunkLog2) + (n ? min(uint32_t(lane), n - 1) : 0u);
+        id0[j] = n ? w.sidx[ic] : 0u;
+        v0[j] = n ? w.sval[ic] : 0.0f;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < CPW; ++j) {
+        if (c0 + j >= P.ndchunk) break;
+        const uint32_t base = lane_val(rec.x, j), limit = lane_val(rec.y, j);
+        if (limit == base) continue;  // nothing to send
+        const uint32_t n = min(lane_val(rec.w, j) & 0xFFFFu, uint32_t(kChunk));
+        const uint32_t take = lane_val(rec.w, j) >> 16, T = lane_val(rec.z, j);
+        const size_t lo = size_t(c0 + j) << kChunkLog2;
+        uint32_t eq_run = 0, sel_run = 0;
+        auto one = [&](uint32_t i, uint32_t id, float val) {
+            const uint32_t key = mag_key(val);
+            const bool in = i < n;
+            const bool eq = in && key == T;
+            const uint64_t eqm = __ballot(eq);
+            const bool sel = (in && key > T) || (eq && eq_run + lane_rank(eqm) < take);
+            const uint64_t selm = __ballot(sel);
+            const uint32_t p = base + sel_run + lane_rank(selm);
+            if (sel && p < limit) {
+                out_idx[p] = id;
+                out_val[p] = val;
+                a.V[id] = 0.0f;
+                a.U[id] = 0.0f;
+            }
+            eq_run += static_cast<uint32_t>(__popcll(eqm));
+            sel_run += static_cast<uint32_t>(__popcll(selm));
+        };
+        one(lane, id0[j], v0[j]);
+        for (uint32_t i0 = kWave; i0 < n; i0 += 4 * kWave) {
+            uint32_t id[4];
+            float val[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const size_t ic = lo + min(i0 + q * kWave + lane, n - 1);
+                id[q] = w.sidx[ic];
+                val[q] = w.sval[ic];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + q * kWave < n) one(i0 + q * kWave + lane, id[q], val[q]);
+        }
+    }
+}
+
 }  // namespace
 
 size_t dgc_workspace_bytes(const gc_plan *plan) {
@@ -1204,10 +1797,29 @@ size_t dgc_workspace_bytes(const gc_plan *plan) {
 
 using namespace gc;
 
+namespace gc {
+// Whether exact DGC selection takes the four-launch path for these
+// densities: every tensor of more than one chunk keeps at most 1/512 of its
+// entries (denser selections stage more entries than one workgroup per
+// tensor counts quickly, and take the candidate kernels).
+bool dgc_exact_fast(const gc_plan *plan, uint32_t knum, uint32_t kden) {
+    for (const SegDev &d : plan->seg) {
+        if (d.len <= uint32_t(kChunk)) continue;
+        if (uint64_t(seg_topk(d.len, d.k, knum, kden)) * kFastDensity > d.len) return false;
+    }
+    return true;
+}
+}  // namespace gc
+
 namespace {
 // Entries a message of this plan and selection holds at most.
-uint64_t dgc_capacity(const gc_plan *plan, int select, uint32_t over) {
-    if (select != GC_SELECT_SAMPLED) return plan->total_k;
+uint64_t dgc_capacity(const gc_plan *plan, int select, uint32_t over, uint32_t knum = 0, uint32_t kden = 0) {
+    if (select != GC_SELECT_SAMPLED) {
+        if (kden == 0) return plan->total_k;
+        uint64_t cap = 0;
+        for (const SegDev &d : plan->seg) cap += seg_topk(d.len, d.k, knum, kden);
+        return cap;
+    }
     uint64_t cap = 0;
     for (const SegDev &d : plan->seg) cap += std::min<uint64_t>(d.len, uint64_t(over) * d.k);
     return cap;
@@ -1243,10 +1855,27 @@ void launch_candidates(const gc_plan *plan, const PlanDev &P, const DgcWs &w, co
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
     GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
-    if (sampled) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    if (sampled || w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_count", stream, dgc_count_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
     GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+}
+
+// Exact DGC selection in four launches after the clip norm.
+template <int kMode>
+void launch_exact(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const Src &src, bool clip, float thr,
+                  gc_sparse *out, hipStream_t stream) {
+    const unsigned segs = static_cast<unsigned>(plan->nseg);
+    if (clip)
+        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, src.G, w));
+    GC_LAUNCH("dgc_prepare", stream, dgc_prepare_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, clip ? 1 : 0, thr));
+    if (w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode, true><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
+    GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off));
+    if (plan->ndchunk >= kWideChunks)
+        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+    else
+        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, 1><<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
 }
 
 // The selection pipeline for one key source: (clip), prep, sample + bound
@@ -1297,8 +1926,9 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
 
 extern "C" uint64_t gc_dgc_message_cap(const gc_plan *plan, const gc_dgc_options *opt) {
     if (!plan) return 0;
-    if (!opt || opt->select != GC_SELECT_SAMPLED) return plan->total_k;
-    return dgc_capacity(plan, GC_SELECT_SAMPLED, opt->over);
+    if (!opt) return plan->total_k;
+    if (opt->select == GC_SELECT_SAMPLED) return dgc_capacity(plan, GC_SELECT_SAMPLED, opt->over);
+    return dgc_capacity(plan, GC_SELECT_EXACT, 0, opt->density_num, opt->density_den);
 }
 
 extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V,
@@ -1324,18 +1954,32 @@ extern "C" gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *
         return set_error(GC_EINVAL, "gc_dgc_step: sample_period must be in [1, GC_MAX_SAMPLE_PERIOD]");
     if (sampled && opt->over < 1) return set_error(GC_EINVAL, "gc_dgc_step: over must be >= 1");
     if (opt->reserved != 0) return set_error(GC_EINVAL, "gc_dgc_step: reserved must be 0");
-    gc_status st = check_select_io("gc_dgc_step", plan, out, dgc_capacity(plan, opt->select, opt->over), ws, ws_bytes);
+    const uint32_t knum = opt->density_num, kden = opt->density_den;
+    if (kden != 0 && (knum < 1 || knum > kden))
+        return set_error(GC_EINVAL, "gc_dgc_step: density_num must be in [1, density_den] when density_den > 0");
+    if (kden != 0 && sampled)
+        return set_error(GC_ENOTSUP, "gc_dgc_step: a per-call density needs GC_SELECT_EXACT");
+    gc_status st = check_select_io("gc_dgc_step", plan, out, dgc_capacity(plan, opt->select, opt->over, knum, kden),
+                                   ws, ws_bytes);
     if (st != GC_OK) return st;
     PlanDev P;
     st = plan_device(plan, &P);
     if (st != GC_OK) return st;
     DgcWs w = dgc_layout(plan, ws, nullptr);
+    w.knum = knum;
+    w.kden = kden;
     const bool clip = thr_G > 0.0f;
     const float thr = clip ? static_cast<float>(static_cast<double>(thr_G) /
                                                 std::sqrt(static_cast<double>(num_nodes)))
                            : 0.0f;
     Src src{G, U, V, momentum, 0u, 0u, 0u, 0u, nullptr};
-    if (opt->momentum_kind == GC_MOMENTUM_NESTEROV)
+    const bool nesterov = opt->momentum_kind == GC_MOMENTUM_NESTEROV;
+    const bool fast = !sampled && (kden == 0 ? plan->dgc_fast : dgc_exact_fast(plan, knum, kden));
+    if (fast && nesterov)
+        launch_exact<kNesterov>(plan, P, w, src, clip, thr, out, stream);
+    else if (fast)
+        launch_exact<kVanilla>(plan, P, w, src, clip, thr, out, stream);
+    else if (nesterov)
         launch_select<kNesterov>(plan, P, w, src, clip, thr, sampled, opt->sample_period, opt->over, out, stream);
     else
         launch_select<kVanilla>(plan, P, w, src, clip, thr, sampled, opt->sample_period, opt->over, out, stream);

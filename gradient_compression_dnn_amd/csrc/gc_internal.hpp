@@ -86,6 +86,7 @@ struct gc_plan {
     uint32_t nbgroup = 0;
     uint64_t mask_words = 0;  // sum over segments of ceil(length / 32)
     uint64_t seg_elems = 0;   // sum over segments of the length
+    bool dgc_fast = false;    // exact DGC at the plan's k takes the four-launch path
     std::vector<gc::SegDev> seg;
     std::vector<uint32_t> dchunk_seg;
     std::vector<uint32_t> achunk_seg;
@@ -110,6 +111,10 @@ gc_status plan_device(const gc_plan *plan, PlanDev *out);
 // The same, for tables already on the current device (gc_plan_upload);
 // GC_EINVAL otherwise, without allocating.
 gc_status plan_device_resident(const gc_plan *plan, PlanDev *out);
+
+// Whether exact DGC selection at these densities takes the four-launch path
+// (knum = kden = 0: the plan's own k).
+bool dgc_exact_fast(const gc_plan *plan, uint32_t knum, uint32_t kden);
 
 // Workspace bytes per operation (each op's translation unit lays out its own).
 size_t dgc_workspace_bytes(const gc_plan *plan);
@@ -192,11 +197,12 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// Exclusive scan of one value per thread, in thread order, over the
-// workgroup.  Returns the exclusive prefix; *total receives the sum.
-template <class T>
+// Exclusive scan of one value per thread, in thread order, over a workgroup
+// of BS threads.  Returns the exclusive prefix; *total receives the sum.
+template <class T, int BS = kBlock>
 __device__ __forceinline__ T block_exclusive_scan(T v, T *total) {
-    __shared__ T wsum[kWaves];
+    constexpr int NW = BS / kWave;
+    __shared__ T wsum[NW];
     T x = v;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -207,7 +213,7 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *total) {
     __syncthreads();
     T before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         T s = wsum[w];
         if (w < wave_id()) before += s;
         all += s;
@@ -372,37 +378,47 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-// Perfect binary tree sum of one double per thread, leaves in thread order.
-// Butterfly adds are bit-identical on both lanes because IEEE addition is
-// commutative, so every lane ends with the wave's subtree sum.
+// Perfect binary tree sum of one double per thread of a BS-thread
+// workgroup, leaves in thread order.  Butterfly adds are bit-identical on
+// both lanes because IEEE addition is commutative, so every lane ends with
+// the wave's subtree sum; the wave sums are then added as a perfect tree.
+template <int BS = kBlock>
 __device__ __forceinline__ double block_tree_sum(double v) {
-    __shared__ double ws[kWaves];
+    constexpr int NW = BS / kWave;
+    static_assert((NW & (NW - 1)) == 0, "power-of-two wave count");
+    __shared__ double ws[NW];
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) v = v + __shfl_xor(v, d, kWave);
     if (lane_id() == 0) ws[wave_id()] = v;
     __syncthreads();
-    double r = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    double t[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t[w] = ws[w];
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1)
+#pragma unroll
+        for (int w = 0; w < half; ++w) t[w] = t[2 * w] + t[2 * w + 1];
     __syncthreads();
-    return r;
+    return t[0];
 }
 
 // Canonical pairwise sum of x[0..m) (zero-padded to a power of two) by one
-// workgroup.  load(i) returns term i as double for i < m.  Thread t owns an
-// aligned sub-block of B = max(1, M/kBlock) leaves.  Below 8 leaves it adds
+// workgroup of BS threads.  load(i) returns term i as double for i < m.
+// Thread t owns an aligned sub-block of B = max(1, M/BS) leaves.  Below 8 leaves it adds
 // them as their perfect tree; otherwise it adds each run of 8 as a fixed
 // 8-leaf tree and combines those nodes in order with the binary-counter stack
-// (which forms exactly the perfect subtree over them).  The 256 subtree sums
+// (which forms exactly the perfect subtree over them).  The BS subtree sums
 // are combined by block_tree_sum.  Sub-blocks past m are +0.0 subtrees, and
 // adding +0.0 to a non-negative value is exact, so the result equals the tree
 // over M leaves.  (A stack step per leaf cost 26 predicated adds each; per
 // 8-leaf node the 5,063-chunk clip tree finishes in a fraction of that.)
 constexpr int kTreeDepth = 23;  // levels of 8-leaf nodes: sub-blocks of up to 2^26 leaves per thread
 
-template <class Load>
+template <int BS = kBlock, class Load>
 __device__ double block_pairwise_sum(uint64_t m, Load load) {
     uint64_t M = 1;
     while (M < m) M <<= 1;
-    const uint64_t B = M > kBlock ? M / kBlock : 1;
+    const uint64_t B = M > uint64_t(BS) ? M / BS : 1;
     const uint64_t lo = static_cast<uint64_t>(threadIdx.x) * B;
     // leaf g, +0.0 past the terms (the index is clamped, so the load is in
     // bounds; m >= 1)
@@ -438,16 +454,17 @@ __device__ double block_pairwise_sum(uint64_t m, Load load) {
         }
     }
     // after B/8 (a power of two) nodes the full subtree sum is the last carry
-    return block_tree_sum(carry);
+    return block_tree_sum<BS>(carry);
 }
 
 // Given NB bucket counts (read through `count(b)`), and 1 <= k <= total, find
 // the bucket d holding the k-th largest element: sum_{b>d} < k <= sum_{b>=d}.
-// Returns d and writes sum_{b>d} to *above.  Called by the whole workgroup.
-template <int NB, class Count>
+// Returns d and writes sum_{b>d} to *above.  Called by the whole workgroup
+// of BS threads.
+template <int NB, int BS = kBlock, class Count>
 __device__ uint32_t block_find_bucket(uint32_t k, Count count, uint32_t *above) {
-    constexpr int per = NB / kBlock;
-    static_assert(per >= 1 && NB % kBlock == 0, "bucket count");
+    constexpr int per = NB >= BS ? NB / BS : 1;
+    static_assert(NB >= BS ? NB % BS == 0 : true, "bucket count");
     __shared__ uint32_t res_d, res_above;
     if (threadIdx.x == 0) {
         res_d = 0;
@@ -455,14 +472,16 @@ __device__ uint32_t block_find_bucket(uint32_t k, Count count, uint32_t *above) 
     }
     uint32_t c[per];
     uint32_t tsum = 0;
-    // thread t owns buckets NB-1-t*per down to NB-(t+1)*per (descending)
+    // thread t owns buckets NB-1-t*per down to NB-(t+1)*per (descending);
+    // threads past the buckets own none
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-        c[i] = count(NB - 1 - threadIdx.x * per - i);
+        const int b = NB - 1 - int(threadIdx.x) * per - i;
+        c[i] = b >= 0 ? count(b) : 0u;
         tsum += c[i];
     }
     uint32_t total;
-    uint32_t pre = block_exclusive_scan(tsum, &total);
+    uint32_t pre = block_exclusive_scan<uint32_t, BS>(tsum, &total);
     if (pre < k && pre + tsum >= k) {
         uint32_t cum = pre;
 #pragma unroll

@@ -247,6 +247,7 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
     p->nbgroup = static_cast<uint32_t>(p->bgroup_seg.size());
     p->mask_words = mbase;
     p->seg_elems = seg_elems;
+    p->dgc_fast = dgc_exact_fast(p, 0, 0);
     *out = p;
     return GC_OK;
 }

@@ -14,7 +14,12 @@ trained weights are not used; values are seeded random draws):
              of hidden 800 and an FC layer: 68 tensors, 121,893,373
 
 Every array is drawn in float64 with NumPy's PCG64 generator and cast once
-to float32, so every consumer sees identical bits.
+to float32, so every consumer sees identical bits.  gradient_device() draws
+the same distributions on a GPU with torch's seeded generator (float64, cast
+once to float32), for runs that need a fresh full-size gradient per step:
+NumPy takes about 11 s per DeepSpeech-scale gradient on one host core.  Its
+values differ from gradient()'s; a consumer copies them to the host when the
+oracle needs them.
 
 A segment table is an int64 array of rows (offset, length, bin_len, k);
 k is the 0.1%-density count ceil(length / 1000) unless a config says otherwise.
@@ -191,6 +196,50 @@ def gradient(w: Workload, step: int = 0, learner: int = 0) -> np.ndarray:
         for s, (off, n, _, _) in enumerate(w.table):
             g[off:off + n] *= sigma[s]
         return g.astype(np.float32)
+    raise KeyError(w.name)
+
+
+def gradient_device(w: Workload, step: int = 0, device="cuda"):
+    """A seeded fp32 gradient drawn on `device` (torch tensor): the same
+    recipe and seeds as gradient() (fc1m 1 + step, resnet50 2000 + step,
+    lstm_lm 3000 + step, deepspeech 5000 + step), with torch's generator for
+    the per-element draws and NumPy's PCG64 for the few per-tensor and
+    per-row ones (DeepSpeech's layer scales, the LSTM's heavy rows)."""
+    import torch
+
+    def gen(seed):
+        return torch.Generator(device=device).manual_seed(seed)
+
+    f64 = dict(dtype=torch.float64, device=device)
+    if w.name == "fc1m":
+        return (torch.randn(w.n_total, generator=gen(1 + step), **f64) * 1e-3).float()
+    if w.name == "resnet50":
+        u = torch.rand(w.n_total, generator=gen(2000 + step), **f64) - 0.5
+        g = -1e-3 * torch.sign(u) * torch.log1p(-2.0 * u.abs())  # Laplace(0, 1e-3) by inversion
+        for s, (off, n, _, _) in enumerate(w.table):
+            g[off:off + n] *= float(w.fan_in[s]) ** -0.5
+        return g.float()
+    if w.name == "lstm_lm":
+        gg = gen(3000 + step)
+        rng = _rng(3000 + step)
+        g = torch.randn(w.n_total, generator=gg, **f64) * 1e-3
+        for s, (off, n, _, _) in enumerate(w.table):
+            if not w.two_d[s]:
+                continue
+            rows = int(w.rows[s])
+            cols = int(n) // rows
+            heavy = torch.from_numpy(np.nonzero(rng.random(rows) < 0.02)[0]).to(device)
+            z = torch.randn(heavy.numel(), cols, generator=gg, **f64)
+            chi2 = torch.randn(3, heavy.numel(), cols, generator=gg, **f64).square().sum(0)
+            block = g[off:off + n].view(rows, cols)
+            block[heavy] = 1e-3 * z * torch.sqrt(3.0 / chi2)  # Student-t, nu = 3
+        return g.float()
+    if w.name == "deepspeech":
+        sigma = 1e-3 * np.exp(_rng(5000 + step).normal(0.0, 1.0, w.nseg))
+        g = torch.randn(w.n_total, generator=gen(5000 + step), **f64)
+        for s, (off, n, _, _) in enumerate(w.table):
+            g[off:off + n] *= float(sigma[s])
+        return g.float()
     raise KeyError(w.name)
 
 

@@ -287,6 +287,10 @@ typedef struct gc_dgc_options {
     uint32_t sample_period;  /* GC_SELECT_SAMPLED: 1 <= P <= GC_MAX_SAMPLE_PERIOD */
     uint32_t over;           /* GC_SELECT_SAMPLED: budget factor >= 1        */
     uint32_t reserved;       /* must be 0                                    */
+    uint32_t density_num;    /* per-call density (warm-up): with             */
+    uint32_t density_den;    /* density_den > 0, k_s = clamp(ceil(n_s *     */
+                             /* density_num / density_den), 1, n_s) in place */
+                             /* of the plan's k; 0 < num <= den; exact only  */
 } gc_dgc_options;
 
 /* Entries a message needs for these options: sum of k_s (exact), or sum of

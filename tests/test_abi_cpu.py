@@ -160,6 +160,10 @@ def test_dgc_ex_host_checks_and_message_cap():
     assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=2)) == 10 + 2 + 6
     assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, sampled=True, over=3)) == 15 + 3 + 7
     assert lib.gc_dgc_message_cap(None, None) == 0
+    # a per-call density: ceil(n_s num / den), at least 1, at most n_s
+    assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, density=(1, 4))) == 1250 + 25 + 2
+    assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, density=(1, 256))) == 20 + 1 + 1
+    assert B.gc_dgc_message_cap(p, B.dgc_options(0.9, density=(3, 3))) == 5000 + 100 + 7
 
 
 def test_adacomp_message_cap_is_the_sum_of_the_segment_lengths():
@@ -196,6 +200,8 @@ def test_dgc_ex_rejects_options_on_the_host():
         (B.dgc_options(0.9, sampled=True, sample_period=0), "sample_period"),
         (B.dgc_options(0.9, sampled=True, over=0), "over"),
         (B.dgc_options(1.0), "momentum"),
+        (B.dgc_options(0.9, density=(0, 4)), "density_num"),
+        (B.dgc_options(0.9, density=(5, 4)), "density_num"),
         (B.gc_dgc_options(0.9, 0.0, 1, 7, 0, 100, 2, 0), "momentum_kind"),
         (B.gc_dgc_options(0.9, 0.0, 1, 0, 5, 100, 2, 0), "select"),
         (B.gc_dgc_options(0.9, 0.0, 1, 0, 0, 100, 2, 1), "reserved"),
@@ -203,6 +209,10 @@ def test_dgc_ex_rejects_options_on_the_host():
     for opt, word in cases:
         st = lib.gc_dgc_step_ex(p.handle, fake, fake, fake, ctypes.byref(opt), None, None, 0, None)
         assert st == B.GC_EINVAL and word in B.gc_last_error(), (word, B.gc_last_error())
+    # a per-call density is for exact selection only
+    opt = B.dgc_options(0.9, sampled=True, density=(1, 4))
+    st = lib.gc_dgc_step_ex(p.handle, fake, fake, fake, ctypes.byref(opt), None, None, 0, None)
+    assert st == B.GC_ENOTSUP and "density" in B.gc_last_error()
 
 
 def test_last_error_is_per_thread():

@@ -22,13 +22,15 @@ def test_world_size_above_one_is_refused(monkeypatch, capsys):
 def test_algorithmic_bytes_per_unit():
     n, nbins, k, ada, bucket = 1_000_000, 2_000, 1_000, 150_000, 512
     a = bench.algorithmic_bytes(n, nbins, k, ada, bucket)
-    assert a["dgc_update"] == 20 * n          # read G, U, V; write U, V
-    assert a["dgc_norm"] == 4 * n             # read G
-    assert a["ada_fold"] == 12 * n            # read R, dW; write R
-    assert a["ada_emit"] == 8 * ada           # idx and val per entry
-    assert a["dcd"] == 12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket)  # 12.5 B/elt + scales
-    assert a["decode"] == 4 * n + 4 * (k + ada)
-    assert a["dgc_emit"] == 16 * k            # message and masking writes
+    # (bytes per step over all launches, launches per step)
+    assert a["dgc_update"] == (20 * n, 1)          # read G, U, V; write U, V
+    assert a["dgc_norm"] == (4 * n, 1)             # read G
+    assert a["ada_fold"] == (12 * n, 1)            # read R, dW; write R
+    assert a["ada_emit"] == (8 * ada, 1)           # idx and val per entry
+    assert a["dcd"] == (12 * n + n // 2 + 4 * ((n + bucket - 1) // bucket), 1)  # 12.5 B/elt + scales
+    # two decodes, each writing the dense update and reading its message (idx + val)
+    assert a["decode"] == (2 * 4 * n + 8 * (k + ada), 2)
+    assert a["dgc_emit"] == (16 * k, 1)            # message and masking writes
 
 
 def test_source_digest_is_stable_and_covers_the_sources():

@@ -62,6 +62,14 @@ def test_bench_line_schema_and_consistency(capsys):
 
     msgs = r["messages"]
     assert msgs["dgc_entries"] == sum(W.topk_count(int(s[1])) for s in W.make_config("deepspeech").table)
+    # per-kernel fractions: the bytes of all the kernel's launches in a step
+    # over its time in the step (two decodes, each its own message)
+    kf, kus = r["kernel_alg_hbm_frac"], r["kernel_us_per_step"]
+    dec = 2 * 4 * n + 8 * (msgs["dgc_entries"] + msgs["adacomp_entries"])
+    assert kf["decode"] == pytest.approx(dec / (kus["decode"] * 1e-6) / 1e9 / 8000.0, rel=2e-3)
+    assert kf["dgc_update"] == pytest.approx(20 * n / (kus["dgc_update"] * 1e-6) / 1e9 / 8000.0, rel=2e-3)
+    # each step of the run draws its own gradient
+    assert "fresh seeded gradient per step" in r["config"]["gradients"]
     assert 0 < msgs["adacomp_entries"] <= n
     assert msgs["dgc_packed_bytes"] > 8 * msgs["dgc_entries"] // 2
 

@@ -1,0 +1,198 @@
+"""GPU parity of exact DGC selection on plans that take the four-launch path
+(every tensor of more than one 4096-element chunk keeps at most 1/512 of its
+entries; the 0.1% density of the pages qualifies).  Every output is compared
+with the oracle bit for bit: indices, values, segment offsets, U and V.
+
+Besides ordinary multi-step runs, inputs are built to reach each branch of
+the selection: fine bins of one key, with every staged key equal to T or
+not (plateaus at one or two adjacent floats); T above the fine bins (the top
+entries away from the sampled positions); T's bin holding more keys than the
+workgroup's list (a long tie run under a much larger sampled maximum); fewer
+than k entries staged (the sampled positions hold the largest values, so the
+segment is selected again over V); one-chunk tensors, sampled whole; and a
+tensor of more than 5120 chunks (per-chunk passes in rounds)."""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, same_bits, say, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = (1, 2, 63, 64, 65, 4095, 4096, 4097, 8192, 12289, 50000, 131072 + 77)
+
+
+def fast_table(rng, nseg, big=True):
+    """Segments at the pages' 0.1% density, k = ceil(n / 1000)."""
+    lengths = []
+    for i in range(nseg):
+        if big and i == 0:
+            lengths.append(int(rng.integers(300_000, 900_000)))
+        elif rng.random() < 0.5:
+            lengths.append(int(rng.choice(LENGTHS)))
+        else:
+            lengths.append(int(rng.integers(1, 60000)))
+    gaps = [int(rng.integers(0, 7)) for _ in range(nseg)]
+    return W.make_table(lengths, [50] * nseg, None, gaps)
+
+
+def check(t, G, U, V, m, thr, N, nesterov=False, hp=None, steps=1, rng=None, kind=None):
+    hp = hp or HipPath(t, W.table_extent(t))
+    opt = B.dgc_options(m, thr, N, nesterov=nesterov)
+    Ug, Vg = U.copy(), V.copy()
+    for step in range(steps):
+        if step:
+            G = W.random_values(rng, len(G), kind)
+        U, V, idx, val, off, _ = oracle.dgc_ex(t, G, U, V, m, thr, N, nesterov=nesterov)
+        Ug, Vg, gidx, gval, goff = hp.dgc_ex(G, Ug, Vg, opt)
+        assert np.array_equal(goff, off), "segment offsets"
+        assert np.array_equal(gidx, idx), "selected indices"
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Ug, U), ulp_report(Ug, U)
+        assert same_bits(Vg, V), ulp_report(Vg, V)
+    return hp
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
+def test_exact_path_multistep(seed, kind):
+    rng = np.random.default_rng(8100 + seed)
+    t = fast_table(rng, int(rng.integers(1, 12)))
+    n = W.table_extent(t)
+    U = W.random_values(rng, n, kind)
+    V = W.random_values(rng, n, kind)
+    G = W.random_values(rng, n, kind)
+    clip = [(0.0, 1), (1e-3 if kind != "denormal" else 1e-41, 1 + seed % 4), (1.0, 8)][seed % 3]
+    nesterov = seed % 2 == 1
+    say(f"exact multistep seed={seed} kind={kind} nseg={len(t)} n={n} clip={clip} nesterov={nesterov}")
+    check(t, G, U, V, 0.9, clip[0], clip[1], nesterov=nesterov, steps=3, rng=rng, kind=kind)
+
+
+def _sample_positions(t):
+    """Positions the exact path samples: a one-chunk tensor whole; a tensor
+    of up to 512 chunks, sc = min(4096, (16384 // chunks) rounded down to 32)
+    contiguous entries per chunk, from min(128 ((13 c) mod 32), 4096 - sc) in
+    a full chunk (c numbered over the plan) and from 0 in a partial one; a
+    longer tensor, 32 entries of every ceil(chunks / 512)-th chunk."""
+    pos, c = [], 0
+    for o, ln, _, _ in t:
+        nch = -(-ln // 4096)
+        if nch == 1:
+            pos.extend(range(o, o + ln))
+            c += 1
+            continue
+        if nch <= 512:
+            stride, sc = 1, min(4096, (16384 // nch) & ~31)
+        else:
+            stride, sc = -(-nch // 512), 32
+        for j in range(0, nch, stride):
+            c0 = j * 4096
+            cnt = min(4096, ln - c0)
+            off = min(128 * ((13 * (c + j)) % 32), 4096 - sc) if cnt == 4096 else 0
+            pos.extend(range(o + c0 + off, o + c0 + off + min(sc, cnt)))
+        c += nch
+    return np.array(pos, np.int64)
+
+
+@pytest.mark.parametrize("nesterov", [False, True], ids=["vanilla", "nesterov"])
+def test_exact_restage_when_the_sample_bound_is_too_high(nesterov):
+    """The sampled entries of the middle tensor hold its largest values, over
+    many octaves, and k exceeds the few that reach the bound: fewer than k
+    entries are staged, and the tensor is selected again over V."""
+    rng = np.random.default_rng(8201)
+    t = W.make_table([3000, 4096 * 40 + 123, 50000], [50] * 3, [3, 160, 50])
+    n = W.table_extent(t)
+    V = (rng.standard_normal(n) * 1e-20).astype(np.float32)
+    pos = _sample_positions(t)
+    o1, l1 = int(t[1][0]), int(t[1][1])
+    inseg = pos[(pos >= o1) & (pos < o1 + l1)]
+    mags = np.float32(2.0) ** (-(np.arange(inseg.size) / 8.0)).astype(np.float32)
+    V[inseg] = (mags * np.where(rng.random(inseg.size) < 0.5, -1, 1)).astype(np.float32)
+    # a tie run across the k-th sampled value
+    V[inseg[100:220]] = V[inseg[100]]
+    z = np.zeros(n, np.float32)
+    G = (rng.standard_normal(n) * 1e-30).astype(np.float32)
+    say(f"exact restage nesterov={nesterov}")
+    check(t, G, z, V, 0.9, 0.0, 1, nesterov=nesterov)
+
+
+def test_exact_threshold_above_the_fine_bins():
+    """The k largest entries sit away from every sampled position, far above
+    the sampled maximum: T falls in the last fine bin."""
+    rng = np.random.default_rng(8202)
+    t = W.make_table([4096 * 30, 7000], [50, 50])
+    n = W.table_extent(t)
+    V = rng.standard_normal(n).astype(np.float32)
+    pos = set(_sample_positions(t).tolist())
+    free = np.array([i for i in range(t[0][1]) if i not in pos])
+    big = rng.choice(free, 400, replace=False)
+    V[big] = (rng.uniform(1e3, 1e4, big.size) * np.where(rng.random(big.size) < 0.5, -1, 1)).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    say("exact T above the fine bins")
+    check(t, z, z, V, 0.9, 0.0, 1)
+
+
+def test_exact_tie_run_larger_than_the_bin_list():
+    """1% of a 2M-entry tensor equals 1.0 and a few sampled entries are near
+    100, so the fine bins are wide and T's bin (at 1.0) holds some 20,000
+    keys; the lowest-index ties fill the quota."""
+    rng = np.random.default_rng(8203)
+    t = W.make_table([2_000_000, 5000], [50, 50])
+    n = W.table_extent(t)
+    V = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    ties = rng.choice(2_000_000, 20_000, replace=False)
+    V[ties] = np.float32(1.0)
+    pos = _sample_positions(t)
+    # fewer than the bound's rank (48 of ~15,600 samples), so the bound stays at 1.0
+    V[pos[:20]] = (np.float32(100.0) - np.arange(20, dtype=np.float32)).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    say("exact tie run past the bin list")
+    check(t, z, z, V, 0.9, 0.0, 1)
+
+
+def test_exact_few_distinct_magnitudes_and_one_chunk_tensors():
+    """Values on a coarse grid in large tensors (the staged keys all equal
+    the largest value), and one-chunk tensors sampled whole."""
+    rng = np.random.default_rng(8204)
+    t = W.make_table([4096 * 20 + 5, 3000, 4096, 700, 2, 1, 90000, 4095], [50] * 8)
+    n = W.table_extent(t)
+    V = (rng.integers(-40, 41, n) * np.float32(0.25)).astype(np.float32)
+    G = (rng.integers(-3, 4, n) * np.float32(0.125)).astype(np.float32)
+    U = np.zeros(n, np.float32)
+    say("exact coarse grid")
+    check(t, G, U, V, 0.5, 0.0, 1, steps=3, rng=rng, kind="ties")
+
+
+def test_exact_plateau_one_key_per_fine_bin():
+    """2% of each large tensor sits exactly at 5.0 (above everything else):
+    the sampled bound and maximum meet at that key, the fine bins are one key
+    wide, and T is read off the histogram; the quota takes the lowest-index
+    ties."""
+    rng = np.random.default_rng(8206)
+    t = W.make_table([4096 * 50 + 17, 700_000, 3333, 300_000], [50] * 4)
+    n = W.table_extent(t)
+    V = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    V[rng.random(n) < 0.02] = np.float32(5.0)
+    # the last tensor's plateau holds two adjacent floats: one-key bins, but
+    # not every staged key equals T
+    o3 = int(t[3][0])
+    hi = np.nextafter(np.float32(5.0), np.float32(np.inf))
+    V[o3:][(V[o3:] == np.float32(5.0)) & (rng.random(n - o3) < 0.5)] = hi
+    z = np.zeros(n, np.float32)
+    say("exact plateau")
+    check(t, z, z, V, 0.9, 0.0, 1)
+
+
+def test_exact_tensor_of_more_than_one_round_of_chunks():
+    """One tensor of 8300 chunks (34M entries): the per-chunk passes of the
+    selection run in two rounds of 5120 chunks."""
+    rng = np.random.default_rng(8205)
+    t = W.make_table([4096 * 8300 - 1000, 333], [50, 50])
+    n = W.table_extent(t)
+    G = W.random_values(rng, n, "laplace")
+    V = W.random_values(rng, n, "normal")
+    U = W.random_values(rng, n, "normal")
+    say("exact 8300-chunk tensor")
+    check(t, G, U, V, 0.9, 1.0, 2)

@@ -1,0 +1,116 @@
+"""GPU parity over the configurations' full step counts, at full size, with
+the state carried across steps and a fresh seeded gradient per step (drawn on
+the device, copied to the host for the oracle):
+  ResNet-50: 10 DGC steps (momentum 0.9, clip 1.0, top 0.1% per tensor);
+  LSTM LM: 20 AdaComp steps (L_T 500 / 50), both residual modes;
+  ResNet-50 warm-up: densities 1/4, 1/16, 1/64, 1/256, then the plan's 0.1%,
+  set per call, with U and V carried (the DGC page's exponentially
+  increasing sparsity, read as 75%, 93.75%, 98.4375%, 99.6%, 99.9%).
+Every step's message and state are compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, dev, same_bits, say, ulp_report
+
+pytestmark = pytest.mark.gpu
+
+
+def test_resnet50_ten_dgc_steps():
+    w = W.make_config("resnet50")
+    n = w.n_total
+    hp = HipPath(w.table, n)
+    U = np.zeros(n, np.float32)
+    V = U.copy()
+    Ud = torch.zeros(n, dtype=torch.float32, device=dev())
+    Vd = torch.zeros_like(Ud)
+    out = B.Sparse.empty(hp.plan, hp.plan.total_k, dev())
+    ws = hp.workspace(B.GC_OP_DGC)
+    for step in range(10):
+        g = W.gradient_device(w, step, dev())
+        say(f"resnet50 dgc step {step}: hip")
+        B.gc_dgc_step(hp.plan, g, Ud, Vd, 0.9, 1.0, 1, out, ws)
+        torch.cuda.synchronize()
+        say(f"resnet50 dgc step {step}: oracle")
+        U, V, idx, val, off, _ = oracle.dgc(w.table, g.cpu().numpy(), U, V, 0.9, 1.0, 1)
+        gi, gv, go, _ = out.host()
+        assert np.array_equal(go, off) and np.array_equal(gi, idx), f"step {step}"
+        assert same_bits(gv, val), ulp_report(gv, val)
+    assert same_bits(Ud.cpu().numpy(), U), ulp_report(Ud.cpu().numpy(), U)
+    assert same_bits(Vd.cpu().numpy(), V), ulp_report(Vd.cpu().numpy(), V)
+
+
+def test_lstm_twenty_adacomp_steps_both_residual_modes():
+    w = W.make_config("lstm_lm")
+    n = w.n_total
+    hp = HipPath(w.table, n)
+    R = np.zeros(n, np.float32)
+    Re = torch.zeros(n, dtype=torch.float32, device=dev())   # exact residual
+    Rd = torch.zeros_like(Re)                                # deferred residual
+    state = hp.plan.adacomp_state(dev())
+    ws = hp.workspace(B.GC_OP_ADACOMP)
+    oe = B.Sparse.empty(hp.plan, n, dev())
+    od = B.Sparse.empty(hp.plan, n, dev())
+    for step in range(20):
+        g = W.gradient_device(w, step, dev())
+        say(f"lstm adacomp step {step}: hip (both modes)")
+        B.gc_adacomp_compress(hp.plan, g, Re, 2.0, oe, ws)
+        B.gc_adacomp_compress(hp.plan, g, Rd, 2.0, od, ws, state=state)
+        torch.cuda.synchronize()
+        say(f"lstm adacomp step {step}: oracle")
+        R, idx, val, off, scale, _ = oracle.adacomp(w.table, g.cpu().numpy(), R, 2.0)
+        for label, o in (("exact", oe), ("deferred", od)):
+            gi, gv, go, gs = o.host()
+            assert np.array_equal(go, off) and np.array_equal(gi, idx), f"{label} step {step}"
+            assert same_bits(gv, val), ulp_report(gv, val)
+            assert same_bits(gs[:len(w.table)], scale), ulp_report(gs[:len(w.table)], scale)
+    assert same_bits(Re.cpu().numpy(), R), ulp_report(Re.cpu().numpy(), R)
+    exact = torch.empty_like(Rd)
+    B.gc_adacomp_residual(hp.plan, Rd, state, exact)
+    torch.cuda.synchronize()
+    assert same_bits(exact.cpu().numpy(), R), ulp_report(exact.cpu().numpy(), R)
+
+
+# the warm-up densities (numerator, denominator) per step; None: the plan's k
+WARMUP = [(1, 4), (1, 16), (1, 64), (1, 256), None, None]
+
+
+def stage_table(table, density):
+    """The segment table with k_s = ceil(n_s * num / den), at least 1."""
+    t = np.array(table, np.int64)
+    if density is not None:
+        num, den = density
+        t[:, 3] = np.maximum(1, (t[:, 1] * num + den - 1) // den)
+    return t
+
+
+@pytest.mark.parametrize("nesterov", [False, True], ids=["vanilla", "nesterov"])
+def test_resnet50_warmup_density_schedule(nesterov):
+    w = W.make_config("resnet50")
+    n = w.n_total
+    hp = HipPath(w.table, n)
+    U = np.zeros(n, np.float32)
+    V = U.copy()
+    Ud = torch.zeros(n, dtype=torch.float32, device=dev())
+    Vd = torch.zeros_like(Ud)
+    ws = hp.workspace(B.GC_OP_DGC)
+    for step, density in enumerate(WARMUP):
+        opt = B.dgc_options(0.9, 1.0, 1, nesterov=nesterov, density=density)
+        t = stage_table(w.table, density)
+        cap = B.gc_dgc_message_cap(hp.plan, opt)
+        assert cap == int(t[:, 3].sum())
+        out = B.Sparse.empty(hp.plan, cap, dev())
+        g = W.gradient_device(w, 100 + step, dev())
+        say(f"resnet50 warm-up step {step} density={density} nesterov={nesterov}: hip")
+        B.gc_dgc_step_ex(hp.plan, g, Ud, Vd, opt, out, ws)
+        torch.cuda.synchronize()
+        say(f"resnet50 warm-up step {step}: oracle")
+        U, V, idx, val, off, _ = oracle.dgc_ex(t, g.cpu().numpy(), U, V, 0.9, 1.0, 1, nesterov=nesterov)
+        gi, gv, go, _ = out.host()
+        assert np.array_equal(go, off) and np.array_equal(gi, idx), f"step {step}"
+        assert same_bits(gv, val), ulp_report(gv, val)
+        assert same_bits(Ud.cpu().numpy(), U), ulp_report(Ud.cpu().numpy(), U)
+        assert same_bits(Vd.cpu().numpy(), V), ulp_report(Vd.cpu().numpy(), V)
