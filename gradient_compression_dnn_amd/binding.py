@@ -104,7 +104,7 @@ _SIGS = {
     "gc_stream_probe": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_uint64, _P]),
 }
 
-KERNELS = ("dgc_norm", "dgc_prep", "dgc_prepare", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update",
+KERNELS = ("dgc_norm", "dgc_prep", "dgc_prepare", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update", "dgc_collect",
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
            "pack_tiles", "pack_count", "pack_layout", "pack_write", "unpack_walk", "unpack_count", "unpack_scan",

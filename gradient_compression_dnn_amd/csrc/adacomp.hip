@@ -128,14 +128,12 @@ __device__ __forceinline__ void chunk_bin_max(const AChunk &a, const float (&g)[
         uint32_t mag[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) mag[q] = e0 + q < a.cnt ? mag_bits(g[j][q]) : 0u;
-        const uint32_t b_first = __shfl(bin[j][0], 0, kWave);
-        const uint32_t b_last = __shfl(bin[j][3], kWave - 1, kWave);
+        const uint32_t b_first = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin[j][0]), 0));
+        const uint32_t b_last = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin[j][3]), kWave - 1));
         const uint32_t row0 = e0 - 4u * lane_id();
         if (b_first == b_last) {
             // the wave's 256 elements of this row share one bin
-            uint32_t m = max(max(mag[0], mag[1]), max(mag[2], mag[3]));
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, d, kWave)));
+            const uint32_t m = wave_max_all(max(max(mag[0], mag[1]), max(mag[2], mag[3])));
             if (lane_id() == 0 && row0 < a.cnt) atomicMax(&gm[b_first], m);
         } else {
             // runs of equal bins inside the lane, one LDS max per run

@@ -82,11 +82,7 @@ __global__ __launch_bounds__(kBlock) void decode_index_kernel(PlanDev P, MsgTabl
     start[c] = lo;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_total(v); }
 
 // One workgroup per output chunk.  Lane k (< K) of every wave loads message
 // k's entry range for the chunk, so every wave sees the same entry total and
@@ -126,13 +122,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
         // single round trip; then every thread walks them in that order and
         // adds those that fall on its own elements
         const uint32_t cntk = b - a;
-        uint32_t pre = cntk;  // inclusive scan over the message lanes
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t o = __shfl_up(pre, d, kWave);
-            if (lane >= d) pre += o;
-        }
-        pre -= cntk;
+        uint32_t pre = wave_inclusive_scan(cntk) - cntk;  // exclusive scan over the message lanes
         // message q holds chunk entries [pre_q, pre_q + cnt_q); every lane
         // takes part in the shuffles, then lanes below the total load
         int k = 0;

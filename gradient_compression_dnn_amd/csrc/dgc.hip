@@ -135,6 +135,10 @@ static_assert(kHist1 == kHist2, "the sample bound reuses one LDS histogram for d
 // kFineBins bins of 2^fshift keys above the staging bound Lkey (the last bin
 // takes every key above the range).
 constexpr uint32_t kFineBins = kHist1;
+// Its fine histogram of the staged keys (the update adds each key) is kept
+// in the segment's digit-1 area; the keys in T's fine bin are gathered into
+// an LDS list of at most kXListCap keys.
+constexpr uint32_t kXListCap = 8192;
 
 struct DgcWs {
     uint32_t *hist1, *hist2, *hist3;
@@ -161,6 +165,10 @@ __host__ __device__ __forceinline__ uint32_t seg_topk(uint32_t len, uint32_t pla
 }
 __device__ __forceinline__ uint32_t seg_k(const SegDev &seg, const DgcWs &w) {
     return seg_topk(seg.len, seg.k, w.knum, w.kden);
+}
+// The exact path's fine histogram of segment s.
+__device__ __forceinline__ uint32_t *xtables(const DgcWs &w, uint32_t s) {
+    return w.hist1 + size_t(s) * kHistRep * kHist1;
 }
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
@@ -596,11 +604,12 @@ __global__ __launch_bounds__(kBlock) void dgc_bound_kernel(PlanDev P, DgcWs w) {
 // The DGC modes read G, U and V and write U and V; kSignif reads g and w and
 // writes nothing dense; kExplore reads only the core bitmap.
 //
-// kFine (the exact path): no histogram; the staged entries go to the chunk's
-// own 4096-entry slot (c * 4096, 16-byte aligned) instead of its first
-// element.  (The exact path's select histograms the staged keys itself:
-// counting them here raised the kernel to 130 VGPRs, three waves per SIMD,
-// and cost it 5% of its bandwidth.)
+// kFine (the exact path): no digit-1 histogram; the staged entries go to the
+// chunk's own 4096-entry slot (c * 4096, 16-byte aligned) instead of its
+// first element, and each staged key is added to the segment's fine
+// histogram by a global atomic (a few dozen per chunk at the pages' 0.1%
+// density).  (An LDS histogram flushed per segment raised the kernel to 130
+// VGPRs, three waves per SIMD, and cost it 5% of its bandwidth.)
 template <int kMode, bool kFine = false>
 __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, DgcWs w) {
     constexpr bool kDgc = kMode == kVanilla || kMode == kNesterov;
@@ -632,6 +641,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
     for (uint32_t c = c0; c < c1; ++c) {
         const float clip = kDgc ? w.st[ci.s].clip : 1.0f;
         const uint32_t Lkey = w.st[ci.s].Lkey;
+        const uint32_t fs = kFine ? w.st[ci.s].fshift : 0u;
         const uint32_t pos = static_cast<uint32_t>(ci.lo - ci.seg.off);  // chunk start in the segment
         uint32_t flags[kRows], before[kRows];
 #pragma unroll
@@ -689,6 +699,8 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                         w.sidx[slot] = e0 + q;
                         w.sval[slot] = v[j][q];
                         ++slot;
+                        if (kFine)
+                            atomicAdd(xtables(w, ci.s) + min((mag_key(v[j][q]) - Lkey) >> fs, kFineBins - 1), 1u);
                     }
                 }
             }
@@ -824,11 +836,7 @@ constexpr uint32_t kWideChunks = 16384;
 
 __device__ __forceinline__ uint32_t lane_val(uint32_t v, uint32_t j) { return __builtin_amdgcn_readlane(v, j); }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) { return wave_total(x); }
 
 template <uint32_t CPW>
 __device__ __forceinline__ uint32_t wave_chunk0() { return (blockIdx.x * kWaves + wave_id()) * CPW; }
@@ -1229,27 +1237,29 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
 }
 
 // ================================================================ exact path
-// Exact DGC selection (vanilla and Nesterov) in four launches after the clip
+// Exact DGC selection (vanilla and Nesterov) in five launches after the clip
 // norm, for plans where every tensor of more than one chunk keeps at most
 // 1/512 of its entries:
 //   prepare (segment) the clip factor; V' at a sample of up to 16,384
 //           entries; the staging bound Lkey and the width 2^fshift of the
 //           fine bins above it (the bins reach the largest sampled key)
-//   update  (chunk)   dgc_update_kernel<kMode, true>: U, V and the staging of
-//           every key >= Lkey in the chunk's own slot
-//   select  (segment) a histogram of the staged keys by fine bin gives T's
-//           bin; a second pass takes that bin's keys to LDS (T) and each
-//           chunk's keys above and in the bin; then each chunk's message
-//           slots and tie quota, in index order
+//   update  (chunk)   dgc_update_kernel<kMode, true>: U, V, the staging of
+//           every key >= Lkey in the chunk's own slot, and the segment's
+//           histogram of the staged keys by fine bin
+//   collect (chunk)   T's bin off the histogram; each chunk's keys above and
+//           in the bin, and the bin's keys to the segment's list
+//   select  (segment) T from the list (three LDS radix passes); then each
+//           chunk's message slots and tie quota, in index order
 //   emit    (chunk)   the chunk's entries in index order, U and V masked
 // Rare cases stay exact on slower branches of select: T's bin holding more
-// keys than LDS, or T above the fine bins (three radix passes over the
+// keys than the list, or T above the fine bins (three radix passes over the
 // staged keys), and fewer than k staged entries (the sample bound was too
-// high: three radix passes over V, then the segment is staged again).
+// high: three radix passes over V, then the segment is staged again); those
+// and segments past one round of the ordered scan with bins wider than one
+// key count the chunks' keys at T again.
 constexpr int kSelBlock = 1024;
 constexpr uint32_t kSampleMax = 16384;  // sampled entries per tensor at most
 constexpr uint32_t kPrepPer = kSampleMax / kSelBlock;
-constexpr uint32_t kSelKeys = 8192;     // LDS list of the keys in T's fine bin
 constexpr uint32_t kQuadRun = 10;       // chunks per quad of lanes in a round of a per-chunk pass
 constexpr uint32_t kWalkChunks = kSelBlock / 4 * kQuadRun;  // chunks per round of a per-chunk pass
 constexpr uint32_t kSelScanRun = 5;                         // chunks per thread in a round of the ordered scan
@@ -1257,6 +1267,8 @@ constexpr uint32_t kSelChunks = kSelBlock * kSelScanRun;   // chunks per round o
                                                             // of per-chunk values kept in LDS
 constexpr uint32_t kThreadN = 128;      // staged entries one thread counts; more: a wave
 constexpr uint32_t kFastDensity = 512;  // exact path when k_s * 512 <= n_s (or one chunk)
+constexpr uint32_t kGatherBig = kXListCap / kSamples;  // chunks with more than kSamples keys in T's bin, at most
+static_assert(2 * kGatherBig <= kWalkChunks, "select's gather keeps those chunks in the walk's LDS list");
 
 // Sample of a tensor for the exact path: one chunk, all of it; up to 512
 // chunks, a block of sc = min(4096, (16384 / chunks) rounded down to 32)
@@ -1292,6 +1304,9 @@ __global__ __launch_bounds__(kSelBlock) void dgc_prepare_kernel(PlanDev P, Src a
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     const uint32_t k = seg_k(seg, w);
+    // the update adds every staged key to the fine histogram
+    uint32_t *xt = xtables(w, s);
+    for (int i = threadIdx.x; i < int(kFineBins); i += kSelBlock) xt[i] = 0u;
     // the sample's G, U, V first (in flight during the clip factor's tree);
     // sample q = sc j + l is entry l of sampled chunk j, thread t takes
     // q = t, t + 1024, ...
@@ -1333,9 +1348,7 @@ __global__ __launch_bounds__(kSelBlock) void dgc_prepare_kernel(PlanDev P, Src a
     }
     __shared__ uint32_t h[kHist1];
     __shared__ uint32_t wmax[kSelBlock / kWave];
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    kmax = wave_max_all(kmax);
     if (lane_id() == 0) wmax[wave_id()] = kmax;
     __syncthreads();
     uint32_t Hkey = 0;
@@ -1471,8 +1484,7 @@ __device__ __forceinline__ void sel_walk_round(const SegDev &seg, const DgcWs &w
 #pragma unroll
             for (uint32_t u = 0; u < 4; ++u) add4(acc, y[u], q0 + 4 * (u * kWave + lane), nn);
         }
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        acc = wave_total(acc);
         if (lane == 0) store(i, acc);
     }
     __syncthreads();
@@ -1514,18 +1526,209 @@ __device__ __forceinline__ uint32_t sel_radix(uint32_t rank, Each each, uint32_t
     return prefix;
 }
 
+// T's fine bin b* of a segment, found by one wave from the fine histogram:
+// fewer than k staged keys lie in the bins above b*, at least k in b* and
+// above.  ok: the selection takes select's fast branch (at least k staged
+// keys, b* below the last bin, and a bin of one key or at most kXListCap
+// keys).
+struct FineBin {
+    uint32_t bstar, above, in;
+    bool ok;
+};
+__device__ __forceinline__ FineBin wave_fine_bin(const uint32_t *hist, uint32_t k, uint32_t fs) {
+    const uint32_t lane = lane_id();
+    // lane l holds bins [b0, b0 + 32) with b0 = 2016 - 32 l: lane 0 the highest
+    const uint32_t b0 = kFineBins - 32u * (lane + 1u);
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + b0);
+    uint32_t hv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 q = h4[i];
+        hv[4 * i] = q.x;
+        hv[4 * i + 1] = q.y;
+        hv[4 * i + 2] = q.z;
+        hv[4 * i + 3] = q.w;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += hv[i];
+    const uint32_t incl = wave_inclusive_scan(sum);  // keys in lanes 0..l
+    FineBin r{0u, 0u, 0u, false};
+    const uint64_t reach = __ballot(incl >= k);
+    if (reach == 0) return r;  // fewer than k staged keys
+    const int L = __ffsll(static_cast<unsigned long long>(reach)) - 1;
+    uint32_t acc = incl - sum, bb = 0, ab = 0, cb = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+        if (!found && acc + hv[i] >= k) {
+            found = true;
+            bb = b0 + i;
+            ab = acc;
+            cb = hv[i];
+        }
+        acc += hv[i];
+    }
+    r.bstar = lane_val(bb, L);
+    r.above = lane_val(ab, L);
+    r.in = lane_val(cb, L);
+    r.ok = r.bstar != kFineBins - 1 && (fs == 0 || r.in <= kXListCap);
+    return r;
+}
+
+// Chip-wide, kXCollectChunks chunks per workgroup (a quarter per wave): each
+// chunk's staged keys above T's fine bin (low u16) and in it (high u16) go to
+// cpack, and (bins wider than one key) its first kSamples keys in the bin, in
+// staging order, to its row of skey (select gathers the rows; a chunk with
+// more in the bin is read again there).  Segments whose selection takes a
+// slower branch of select are skipped.  T's bin is found once per workgroup
+// when its chunks share a segment (256 threads, 8 bins each), else per wave
+// and segment.  Each wave reads the first 64 staged keys of its chunks with
+// their records, before T's bin is known (a chunk's 4096-entry slot is always
+// there to read; keys past the staged count are ignored).  (Appending the
+// bin's keys to one list per segment through a shared counter, and finding
+// the bin in every wave from the whole histogram, took 20 us on the
+// DeepSpeech sizes.)
+constexpr uint32_t kXCollectChunks = 32;
+constexpr uint32_t kXCollectCpw = kXCollectChunks / kWaves;
+__global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w) {
+    const uint32_t cb0 = blockIdx.x * kXCollectChunks;
+    const uint32_t s_first = P.dchunk_seg[cb0];
+    const uint32_t s_last = P.dchunk_seg[min(cb0 + kXCollectChunks, P.ndchunk) - 1];
+    const uint32_t lane = lane_id();
+    const uint32_t c0 = cb0 + wave_id() * kXCollectCpw;
+    const uint32_t cl = min(c0 + lane % kXCollectCpw, P.ndchunk - 1);
+    const uint32_t my_seg = P.dchunk_seg[cl];
+    const uint32_t my_n = min(w.ccount[cl], P.dchunk_rec[cl].y);
+    uint32_t key0[kXCollectCpw];
+#pragma unroll
+    for (uint32_t j = 0; j < kXCollectCpw; ++j)
+        key0[j] = mag_key(w.sval[(size_t(min(c0 + j, P.ndchunk - 1)) << kChunkLog2) + lane]);
+    uint32_t cur = ~0u, Lkey = 0, fs = 0;
+    FineBin fb{};
+    if (s_first == s_last) {
+        // thread t holds bins [2040 - 8 t, 2048 - 8 t): thread 0 the highest
+        __shared__ FineBin sh_fb;
+        const SegDev seg = P.seg[s_first];
+        const uint32_t k = seg_k(seg, w);
+        const uint32_t b0 = kFineBins - 8u * (threadIdx.x + 1u);
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(xtables(w, s_first) + b0);
+        const uint4 qa = h4[0], qb = h4[1];
+        const uint32_t hv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        uint32_t tsum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tsum += hv[i];
+        if (threadIdx.x == 0) sh_fb = FineBin{0u, 0u, 0u, false};
+        uint32_t total;
+        const uint32_t pre = block_exclusive_scan<uint32_t, kBlock>(tsum, &total);
+        if (total >= k && pre < k && pre + tsum >= k) {
+            uint32_t acc = pre;
+            bool found = false;
+#pragma unroll
+            for (int i = 7; i >= 0; --i) {
+                if (!found && acc + hv[i] >= k) {
+                    found = true;
+                    const uint32_t bs = b0 + i;
+                    sh_fb = FineBin{bs, acc, hv[i], bs != kFineBins - 1 && (w.st[s_first].fshift == 0 || hv[i] <= kXListCap)};
+                }
+                acc += hv[i];
+            }
+        }
+        __syncthreads();
+        fb = sh_fb;
+        cur = s_first;
+        Lkey = w.st[s_first].Lkey;
+        fs = w.st[s_first].fshift;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kXCollectCpw; ++j) {
+        const uint32_t c = c0 + j;
+        if (c >= P.ndchunk) break;
+        const uint32_t s = lane_val(my_seg, j);
+        if (s != cur) {
+            cur = s;
+            const SegDev seg = P.seg[s];
+            Lkey = w.st[s].Lkey;
+            fs = w.st[s].fshift;
+            fb = wave_fine_bin(xtables(w, s), seg_k(seg, w), fs);
+        }
+        if (!fb.ok) continue;
+        const uint32_t n = lane_val(my_n, j);
+        uint32_t gt = 0, in = 0;
+        for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+            const uint32_t i = i0 + lane;
+            const uint32_t key = i0 == 0 ? key0[j] : mag_key(w.sval[(size_t(c) << kChunkLog2) + min(i, uint32_t(kChunk) - 1)]);
+            const uint32_t b = min((key - Lkey) >> fs, kFineBins - 1);
+            const bool valid = i < n;
+            const bool inb = valid && b == fb.bstar;
+            const uint64_t gtm = __ballot(valid && b > fb.bstar);
+            const uint64_t inm = __ballot(inb);
+            const uint32_t at = in + lane_rank(inm);
+            if (fs > 0 && inb && at < kSamples) w.skey[size_t(c) * kSamples + at] = key;
+            gt += static_cast<uint32_t>(__popcll(gtm));
+            in += static_cast<uint32_t>(__popcll(inm));
+        }
+        if (lane == 0) w.cpack[c] = gt | (in << 16);
+    }
+}
+
+// The rank-th largest (1 <= rank <= m) of the m <= kWaveSel keys list[0, m),
+// all in [lo, lo + 2^fs), by one wave: the fs bits of key - lo from the
+// highest, each set when at least rank keys match the prefix with it set
+// (else rank drops by that count).  *gt_out: the keys above the result.
+constexpr uint32_t kWaveSel = 512;
+__device__ __forceinline__ uint32_t wave_select(const uint32_t *list, uint32_t m, uint32_t lo, uint32_t fs,
+                                                uint32_t rank, uint32_t *gt_out) {
+    constexpr uint32_t kPer = kWaveSel / kWave;
+    const uint32_t lane = lane_id();
+    uint32_t x[kPer];  // key - lo (< 2^31), or ~0u past the list
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) {
+        const uint32_t i = q * kWave + lane;
+        x[q] = i < m ? list[i] - lo : ~0u;
+    }
+    uint32_t prefix = 0;
+    for (int bit = int(fs) - 1; bit >= 0; --bit) {
+        const uint32_t want = (prefix >> bit) | 1u;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < kPer; ++q) cnt += static_cast<uint32_t>(__popcll(__ballot((x[q] >> bit) == want)));
+        if (cnt >= rank) prefix |= 1u << bit;
+        else rank -= cnt;
+    }
+    uint32_t g = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) g += static_cast<uint32_t>(__popcll(__ballot(x[q] != ~0u && x[q] > prefix)));
+    *gt_out = g;
+    return lo + prefix;
+}
+
+// One workgroup per segment.  The common case (at least k staged keys, T's
+// fine bin below the last and holding at most kXListCap keys, the segment's
+// chunks in one round of kSelChunks): thread t's chunks [t per, +per) have
+// their staged counts and collect words loaded with two histogram bins; one
+// scan gives T's bin and each thread's first place in the list of the bin's
+// keys; T is taken from the list (one wave when it is short); the keys at and
+// above T in the bin go back to their chunks (LDS atomics); the per-chunk
+// words wait in LDS (cpk, cnn) meanwhile; one more scan of
+// the counts above and at T gives every chunk's first slot and tie quota:
+// the quota of thread t's chunks is what the ties of the chunks before them
+// leave, and the ties taken before them are min(need_eq, ties before them).
 template <int kMode>
 __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a, DgcWs w,
                                                                  uint32_t *__restrict__ seg_off) {
+    static_assert(kFineBins == 2 * kSelBlock, "two histogram bins per thread");
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     const uint32_t k = w.st[s].sent, Lkey = w.st[s].Lkey, fs = w.st[s].fshift, base = w.st[s].base;
     const uint32_t nch = seg.dnchunk, c0 = seg.dchunk0;
     __shared__ uint32_t h[kFineBins];
-    __shared__ uint32_t list[kSelKeys];
+    __shared__ uint32_t list[kXListCap];
+    __shared__ uint32_t lch[kXListCap];
     __shared__ uint32_t cpk[kSelChunks];
+    __shared__ uint32_t cnn[kSelChunks];  // one-round segments: staged count of each chunk
     __shared__ uint32_t big[kWalkChunks];
-    __shared__ uint32_t sh_n, sh_nbig;
+    __shared__ uint32_t sh_nbig, sh_bstar, sh_above, sh_cnt, sh_T, sh_gtin;
     // per-chunk values: LDS when one round covers the segment, else the workspace
     const bool one_round = nch <= kSelChunks;
     auto pk_store = [&](uint32_t i, uint32_t v) {
@@ -1545,13 +1748,88 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
             },
             [](uint32_t, uint32_t) {}, big, &sh_nbig);
     };
+    // the keys in T's bin of thread t's chunks [t0, t0 + per) (collect words
+    // pkr) to the LDS list from place `at`: a chunk's skey row, or a wave per
+    // chunk with more than kSamples of them (fewer than kGatherBig chunks)
+    auto gather = [&](const uint32_t (&pkr)[kSelScanRun], uint32_t t0, uint32_t at, uint32_t bstar) {
+        if (threadIdx.x == 0) sh_nbig = 0u;
+        __syncthreads();
+#pragma unroll
+        for (uint32_t b = 0; b < kSelScanRun; ++b) {
+            const uint32_t e = pkr[b] >> 16, i = t0 + b;
+            if (e > kSamples) {
+                const uint32_t bi = atomicAdd(&sh_nbig, 1u);
+                if (bi < kGatherBig) {
+                    big[bi] = i;
+                    big[kGatherBig + bi] = at;
+                }
+            } else {
+                const uint32_t *row = w.skey + size_t(c0 + i) * kSamples;
+                for (uint32_t q = 0; q < e; ++q)
+                    if (at + q < kXListCap) {
+                        list[at + q] = row[q];
+                        lch[at + q] = i;
+                    }
+            }
+            at += e;
+        }
+        __syncthreads();
+        const uint32_t nb = min(sh_nbig, kGatherBig);
+        const uint32_t lane = lane_id();
+        for (uint32_t bi = wave_id(); bi < nb; bi += kSelBlock / kWave) {
+            const uint32_t i = big[bi];
+            uint32_t pos = big[kGatherBig + bi];
+            const uint32_t n = min(w.ccount[c0 + i], chunk_len(i));
+            for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+                const uint32_t j = i0 + lane;
+                const uint32_t key = j < n ? mag_key(w.sval[(size_t(c0 + i) << kChunkLog2) + j]) : 0u;
+                const bool inb = j < n && bin_of(key) == bstar;
+                const uint64_t mk = __ballot(inb);
+                const uint32_t q = pos + lane_rank(mk);
+                if (inb && q < kXListCap) {
+                    list[q] = key;
+                    lch[q] = i;
+                }
+                pos += static_cast<uint32_t>(__popcll(mk));
+            }
+        }
+        __syncthreads();
+    };
 
-    uint32_t my = 0;
-    for (uint32_t i = threadIdx.x; i < nch; i += kSelBlock) my += min(w.ccount[c0 + i], chunk_len(i));
-    uint32_t staged;
-    (void)block_exclusive_scan<uint32_t, kSelBlock>(my, &staged);
+    // one round of loads: a one-round segment's staged counts and collect
+    // words of thread t's chunks (to cnn and cpk), and bins 2047 - 2t and
+    // 2046 - 2t
+    const uint32_t per1 = one_round ? (nch + kSelBlock - 1) / kSelBlock : 0u;
+    const uint32_t t1 = threadIdx.x * per1;
+    uint32_t in_sum = 0;
+    {
+        uint32_t nn[kSelScanRun], pk[kSelScanRun];
+#pragma unroll
+        for (uint32_t b = 0; b < kSelScanRun; ++b) {
+            const uint32_t i = t1 + b;
+            const bool act = b < per1 && i < nch;
+            nn[b] = act ? min(w.ccount[c0 + i], chunk_len(i)) : 0u;
+            pk[b] = act ? w.cpack[c0 + i] : 0u;
+        }
+#pragma unroll
+        for (uint32_t b = 0; b < kSelScanRun; ++b) {
+            const uint32_t i = t1 + b;
+            if (b < per1 && i < nch) {
+                cnn[i] = nn[b];
+                cpk[i] = pk[b];
+            }
+            in_sum += pk[b] >> 16;
+        }
+    }
+    const uint2 hp = reinterpret_cast<const uint2 *>(xtables(w, s))[kFineBins / 2 - 1 - threadIdx.x];
+    const uint32_t hsum = hp.x + hp.y;
+    uint64_t tot64;
+    const uint64_t pre64 =
+        block_exclusive_scan<uint64_t, kSelBlock>(uint64_t(hsum) | (uint64_t(in_sum) << 32), &tot64);
+    const uint32_t staged = static_cast<uint32_t>(tot64);  // every staged key is in the histogram once
     uint32_t T, gt;
-    bool have_pk = false;  // cpk holds each chunk's keys above T's bin (low) and in it (high)
+    bool have_pk = false;  // pk_load(i): chunk i's keys above T's bin (low) and in it (high)
+    bool pk_done = false;  // cpk: each chunk's keys above T (low) and at T (high), one round
     bool all_eq = false;   // every staged key equals T
     if (staged < k) {
         // the sample bound was above the k-th key: select over V itself, then
@@ -1595,120 +1873,190 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
         }
         __syncthreads();
     } else {
-        // the staged keys by fine bin
-        for (int i = threadIdx.x; i < int(kFineBins); i += kSelBlock) h[i] = 0u;
+        // T's fine bin: thread t holds bins 2047 - 2t (first) and 2046 - 2t
+        const uint32_t hpre = static_cast<uint32_t>(pre64);
+        if (hpre < k && hpre + hsum >= k) {
+            const bool hi = hpre + hp.y >= k;
+            sh_bstar = kFineBins - 1 - 2 * threadIdx.x - (hi ? 0u : 1u);
+            sh_above = hi ? hpre : hpre + hp.y;
+            sh_cnt = hi ? hp.y : hp.x;
+        }
         __syncthreads();
-        sel_walk(
-            seg, w, 0, nch, never,
-            [&](uint32_t key) {
-                atomicAdd(&h[bin_of(key)], 1u);
-                return 0u;
-            },
-            [](uint32_t, uint32_t) {}, big, &sh_nbig);
-        uint32_t above;
-        const uint32_t bstar = block_find_bucket<kFineBins, kSelBlock>(k, [&](int b) { return h[b]; }, &above);
-        const uint32_t cnt_b = h[bstar];
-        __syncthreads();
-        if (bstar == kFineBins - 1 || (fs > 0 && cnt_b > kSelKeys)) {
-            // T above the fine bins, or its bin too full for LDS
+        const uint32_t bstar = sh_bstar, above = sh_above, cnt_b = sh_cnt;
+        if (bstar == kFineBins - 1 || (fs > 0 && cnt_b > kXListCap)) {
+            // T above the fine bins, or its bin too full for the list
             T = sel_radix(k, each_staged, h, &gt);
         } else if (fs == 0 && cnt_b == staged) {
             T = Lkey + bstar;  // one key per bin, and every staged key in T's
             gt = 0;
             all_eq = true;
+            if (one_round) {
+#pragma unroll
+                for (uint32_t b = 0; b < kSelScanRun; ++b)
+                    if (b < per1 && t1 + b < nch) cpk[t1 + b] = cnn[t1 + b] << 16;
+                pk_done = true;
+            }
+        } else if (fs == 0) {
+            // a bin of one key: the collect words count the keys above T and at T
+            T = Lkey + bstar;
+            gt = above;
+            have_pk = true;
+            pk_done = one_round;
         } else {
-            // each chunk's keys above and in T's bin, and (bins wider than
-            // one key) that bin's keys into LDS
-            if (threadIdx.x == 0) sh_n = 0u;
-            __syncthreads();
-            auto count = [&](uint32_t key) {
-                const uint32_t b = bin_of(key);
-                if (b > bstar) return 1u;
-                if (b < bstar) return 0u;
-                if (fs > 0) {
-                    const uint32_t at = atomicAdd(&sh_n, 1u);
-                    if (at < kSelKeys) list[at] = key;
+            // the collect kernel left each chunk's keys above T's bin (low
+            // u16) and in it (high u16) in cpack, and up to kSamples of the
+            // bin's keys in its skey row
+            have_pk = true;
+            uint32_t m;
+            if (one_round) {
+                m = min(static_cast<uint32_t>(tot64 >> 32), kXListCap);
+                uint32_t pk[kSelScanRun];
+#pragma unroll
+                for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                    const bool act = b < per1 && t1 + b < nch;
+                    pk[b] = act ? cpk[t1 + b] : 0u;
+                    if (act) cpk[t1 + b] = pk[b] & 0xFFFFu;
                 }
-                return 1u << 16;
-            };
-            sel_walk(seg, w, 0, nch, never, count, [&](uint32_t i, uint32_t v) { pk_store(i, v); }, big, &sh_nbig);
-            have_pk = one_round;
-            if (fs == 0) {
-                T = Lkey + bstar;
-                gt = above;
+                gather(pk, t1, static_cast<uint32_t>(pre64 >> 32), bstar);
             } else {
-                const uint32_t m = min(sh_n, kSelKeys);
-                uint32_t gt_in;
+                m = 0;
+                for (uint32_t r0 = 0; r0 < nch; r0 += kSelChunks) {
+                    const uint32_t r1 = min(nch, r0 + kSelChunks);
+                    const uint32_t per = (r1 - r0 + kSelBlock - 1) / kSelBlock;
+                    const uint32_t t0 = r0 + threadIdx.x * per;
+                    uint32_t pkr[kSelScanRun], sum = 0;
+#pragma unroll
+                    for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                        const uint32_t i = t0 + b;
+                        pkr[b] = b < per && i < r1 ? w.cpack[c0 + i] : 0u;
+                        sum += pkr[b] >> 16;
+                    }
+                    uint32_t tot;
+                    const uint32_t at = m + block_exclusive_scan<uint32_t, kSelBlock>(sum, &tot);
+                    gather(pkr, t0, at, bstar);
+                    m += tot;
+                }
+                m = min(m, kXListCap);
+            }
+            uint32_t gt_in;
+            if (m <= kWaveSel) {
+                if (wave_id() == 0) {
+                    uint32_t g;
+                    const uint32_t t = wave_select(list, m, Lkey + (bstar << fs), fs, k - above, &g);
+                    if (lane_id() == 0) {
+                        sh_T = t;
+                        sh_gtin = g;
+                    }
+                }
+                __syncthreads();
+                T = sh_T;
+                gt_in = sh_gtin;
+            } else {
                 T = sel_radix(k - above, [&](auto f) {
                     for (uint32_t i = threadIdx.x; i < m; i += kSelBlock) f(list[i]);
                 }, h, &gt_in);
-                gt = above + gt_in;
+            }
+            gt = above + gt_in;
+            if (one_round) {
+                // the bin's keys above and at T, back to their chunks
+                for (uint32_t i = threadIdx.x; i < m; i += kSelBlock) {
+                    const uint32_t key = list[i];
+                    if (key > T) atomicAdd(&cpk[lch[i]], 1u);
+                    else if (key == T) atomicAdd(&cpk[lch[i]], 1u << 16);
+                }
+                __syncthreads();
+                pk_done = true;
             }
         }
     }
     const uint32_t need_eq = k - gt;
-    // each chunk's keys above and at T (low and high u16), then the ordered
-    // scan: ties go to the lowest indices, so a chunk's quota is what the
-    // ties of the chunks before it leave
-    auto settle2 = [&](uint32_t i, uint32_t n, uint32_t *v) {
-        if (n == 0) {
-            *v = 0u;
-            return true;
-        }
-        if (all_eq) {
-            *v = n << 16;
-            return true;
-        }
-        if (have_pk) {
-            const uint32_t pk = pk_load(i);
-            // nothing in T's bin (its keys above the bin are above T), or a
-            // bin of one key (its keys equal T)
-            if ((pk >> 16) == 0 || fs == 0) {
-                *v = pk;
-                return true;
-            }
-        }
-        return false;
-    };
-    auto count2 = [&](uint32_t key) { return (key > T ? 1u : 0u) | (key == T ? 1u << 16 : 0u); };
-    uint32_t eq_before = 0, sel_before = 0;
-    for (uint32_t r0 = 0; r0 < nch; r0 += kSelChunks) {
-        const uint32_t r1 = min(nch, r0 + kSelChunks);
-        sel_walk(seg, w, r0, r1, settle2, count2, [&](uint32_t i, uint32_t v) { pk_store(i, v); }, big, &sh_nbig);
-        // the round's chunks in order: thread t takes [r0 + t per, +per)
-        const uint32_t per = (r1 - r0 + kSelBlock - 1) / kSelBlock;
-        const uint32_t t0 = r0 + threadIdx.x * per;
-        uint32_t pk[kSelScanRun], nn[kSelScanRun];
-        uint32_t eq_sum = 0, gt_sum = 0;
+    if (pk_done) {
+        // the ordered scan of a one-round segment from cpk and cnn
+        uint32_t pk[kSelScanRun], eq_sum = 0, gt_sum = 0;
 #pragma unroll
         for (uint32_t b = 0; b < kSelScanRun; ++b) {
-            const uint32_t i = t0 + b;
-            const bool act = b < per && i < r1;
-            pk[b] = act ? pk_load(i) : 0u;
-            nn[b] = act ? min(w.ccount[c0 + i], chunk_len(i)) : 0u;
+            pk[b] = b < per1 && t1 + b < nch ? cpk[t1 + b] : 0u;
             eq_sum += pk[b] >> 16;
             gt_sum += pk[b] & 0xFFFFu;
         }
-        uint32_t eq_tot;
-        const uint32_t eq_pre = eq_before + block_exclusive_scan<uint32_t, kSelBlock>(eq_sum, &eq_tot);
-        const uint32_t take_run = need_eq > eq_pre ? min(need_eq - eq_pre, eq_sum) : 0u;
-        uint32_t sel_tot;
-        const uint32_t sel_pre = sel_before + block_exclusive_scan<uint32_t, kSelBlock>(gt_sum + take_run, &sel_tot);
-        uint32_t eq_run = eq_pre, sel_run = sel_pre;
+        uint64_t tot2;
+        const uint64_t pre2 = block_exclusive_scan<uint64_t, kSelBlock>(uint64_t(gt_sum) | (uint64_t(eq_sum) << 32), &tot2);
+        uint32_t eq_run = static_cast<uint32_t>(pre2 >> 32);
+        uint32_t sel_run = static_cast<uint32_t>(pre2) + min(need_eq, eq_run);
 #pragma unroll
         for (uint32_t b = 0; b < kSelScanRun; ++b) {
-            const uint32_t i = t0 + b;
-            if (b < per && i < r1) {
+            const uint32_t i = t1 + b;
+            if (b < per1 && i < nch) {
                 const uint32_t e = pk[b] >> 16, g = pk[b] & 0xFFFFu;
                 const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e) : 0u;
-                w.crec[c0 + i] = make_uint4(base + sel_run, base + sel_run + g + take, T, nn[b] | (take << 16));
+                w.crec[c0 + i] = make_uint4(base + sel_run, base + sel_run + g + take, T, cnn[i] | (take << 16));
                 eq_run += e;
                 sel_run += g + take;
             }
         }
-        eq_before += eq_tot;
-        sel_before += sel_tot;
-        __syncthreads();
+    } else {
+        // each chunk's keys above and at T (low and high u16), then the
+        // ordered scan in rounds
+        auto settle2 = [&](uint32_t i, uint32_t n, uint32_t *v) {
+            if (n == 0) {
+                *v = 0u;
+                return true;
+            }
+            if (all_eq) {
+                *v = n << 16;
+                return true;
+            }
+            if (have_pk) {
+                const uint32_t p = pk_load(i);
+                // nothing in T's bin (its keys above the bin are above T), or
+                // a bin of one key (its keys equal T)
+                if ((p >> 16) == 0 || fs == 0) {
+                    *v = p;
+                    return true;
+                }
+            }
+            return false;
+        };
+        auto count2 = [&](uint32_t key) { return (key > T ? 1u : 0u) | (key == T ? 1u << 16 : 0u); };
+        uint32_t eq_before = 0, sel_before = 0;
+        for (uint32_t r0 = 0; r0 < nch; r0 += kSelChunks) {
+            const uint32_t r1 = min(nch, r0 + kSelChunks);
+            sel_walk(seg, w, r0, r1, settle2, count2, [&](uint32_t i, uint32_t v) { pk_store(i, v); }, big, &sh_nbig);
+            // the round's chunks in order: thread t takes [r0 + t per, +per)
+            const uint32_t per = (r1 - r0 + kSelBlock - 1) / kSelBlock;
+            const uint32_t t0 = r0 + threadIdx.x * per;
+            uint32_t pkr[kSelScanRun], nr[kSelScanRun];
+            uint32_t eq_sum = 0, gt_sum = 0;
+#pragma unroll
+            for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                const uint32_t i = t0 + b;
+                const bool act = b < per && i < r1;
+                pkr[b] = act ? pk_load(i) : 0u;
+                nr[b] = act ? min(w.ccount[c0 + i], chunk_len(i)) : 0u;
+                eq_sum += pkr[b] >> 16;
+                gt_sum += pkr[b] & 0xFFFFu;
+            }
+            uint64_t tot2;
+            const uint64_t pre2 =
+                block_exclusive_scan<uint64_t, kSelBlock>(uint64_t(gt_sum) | (uint64_t(eq_sum) << 32), &tot2);
+            uint32_t eq_run = eq_before + static_cast<uint32_t>(pre2 >> 32);
+            uint32_t sel_run = sel_before + static_cast<uint32_t>(pre2) + min(need_eq, eq_run) - min(need_eq, eq_before);
+#pragma unroll
+            for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                const uint32_t i = t0 + b;
+                if (b < per && i < r1) {
+                    const uint32_t e = pkr[b] >> 16, g = pkr[b] & 0xFFFFu;
+                    const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e) : 0u;
+                    w.crec[c0 + i] = make_uint4(base + sel_run, base + sel_run + g + take, T, nr[b] | (take << 16));
+                    eq_run += e;
+                    sel_run += g + take;
+                }
+            }
+            const uint32_t eq_all = eq_before + static_cast<uint32_t>(tot2 >> 32);
+            sel_before += static_cast<uint32_t>(tot2) + min(need_eq, eq_all) - min(need_eq, eq_before);
+            eq_before = eq_all;
+            __syncthreads();
+        }
     }
     if (threadIdx.x == 0) {
         w.st[s].T = T;
@@ -1871,6 +2219,7 @@ void launch_exact(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const S
     GC_LAUNCH("dgc_prepare", stream, dgc_prepare_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, clip ? 1 : 0, thr));
     if (w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode, true><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
+    GC_LAUNCH("dgc_collect", stream, dgc_xcollect_kernel<<<grid_1d(plan->ndchunk, kXCollectChunks), kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off));
     if (plan->ndchunk >= kWideChunks)
         GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));

@@ -197,18 +197,70 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
+// Wave-wide integer scans and reductions by DPP moves (CDNA data-parallel
+// primitives): row_shr 1, 2, 4 and 8 inside each 16-lane row, then
+// row_bcast 15 and row_bcast 31 carry the row totals into the rows above.  A
+// lane whose source lies outside its row, or a row the broadcast skips,
+// reads 0, the identity of + and of an unsigned max.  Every lane of the wave
+// must be active.  (A wave scan by ds_bpermute shuffles measured about 8x
+// slower: six dependent LDS round trips.)
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += dpp_u32<kDppRowShr1>(x);
+    x += dpp_u32<kDppRowShr2>(x);
+    x += dpp_u32<kDppRowShr4>(x);
+    x += dpp_u32<kDppRowShr8>(x);
+    x += dpp_u32<kDppRowBcast15, 0xA>(x);
+    x += dpp_u32<kDppRowBcast31, 0xC>(x);
+    return x;
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ void dpp_add_u64(uint32_t &lo, uint32_t &hi) {
+    const uint32_t l = dpp_u32<kCtrl, kRowMask>(lo), h = dpp_u32<kCtrl, kRowMask>(hi);
+    const uint32_t n = lo + l;
+    hi = hi + h + (n < lo ? 1u : 0u);
+    lo = n;
+}
+__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t x) {
+    uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+    dpp_add_u64<kDppRowShr1>(lo, hi);
+    dpp_add_u64<kDppRowShr2>(lo, hi);
+    dpp_add_u64<kDppRowShr4>(lo, hi);
+    dpp_add_u64<kDppRowShr8>(lo, hi);
+    dpp_add_u64<kDppRowBcast15, 0xA>(lo, hi);
+    dpp_add_u64<kDppRowBcast31, 0xC>(lo, hi);
+    return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t x) {
+    x = max(x, dpp_u32<kDppRowShr1>(x));
+    x = max(x, dpp_u32<kDppRowShr2>(x));
+    x = max(x, dpp_u32<kDppRowShr4>(x));
+    x = max(x, dpp_u32<kDppRowShr8>(x));
+    x = max(x, dpp_u32<kDppRowBcast15, 0xA>(x));
+    x = max(x, dpp_u32<kDppRowBcast31, 0xC>(x));
+    return x;
+}
+// The wave's sum and maximum, in every lane.
+__device__ __forceinline__ uint32_t wave_total(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_scan(x)), kWave - 1));
+}
+__device__ __forceinline__ uint32_t wave_max_all(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_max(x)), kWave - 1));
+}
+
 // Exclusive scan of one value per thread, in thread order, over a workgroup
-// of BS threads.  Returns the exclusive prefix; *total receives the sum.
+// of BS threads (T: uint32_t or uint64_t).  Returns the exclusive prefix;
+// *total receives the sum.
 template <class T, int BS = kBlock>
 __device__ __forceinline__ T block_exclusive_scan(T v, T *total) {
     constexpr int NW = BS / kWave;
     __shared__ T wsum[NW];
-    T x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T y = __shfl_up(x, d, kWave);
-        if (lane_id() >= d) x += y;
-    }
+    const T x = wave_inclusive_scan(v);
     if (lane_id() == kWave - 1) wsum[wave_id()] = x;
     __syncthreads();
     T before = 0, all = 0;
@@ -241,12 +293,7 @@ __device__ __forceinline__ uint32_t block_compact(const bool (&flag)[EPT], uint3
     if (threadIdx.x < kWave) {
         // one wave scans the EPT*kWaves (<= 64) counters in (j, wave) order
         uint32_t v = threadIdx.x < EPT * kWaves ? cnt[threadIdx.x] : 0u;
-        uint32_t x = v;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            uint32_t y = __shfl_up(x, d, kWave);
-            if (lane_id() >= d) x += y;
-        }
+        const uint32_t x = wave_inclusive_scan(v);
         if (threadIdx.x < EPT * kWaves) cnt[threadIdx.x] = x - v;
         if (threadIdx.x == kWave - 1) tot = x;
     }
@@ -333,12 +380,7 @@ __device__ __forceinline__ uint32_t block_compact4(const bool (&flag)[kRows][4],
     __syncthreads();
     if (threadIdx.x < kWave) {
         uint32_t v = threadIdx.x < kRows * kWaves ? cnt[threadIdx.x] : 0u;
-        uint32_t x = v;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            uint32_t y = __shfl_up(x, d, kWave);
-            if (lane_id() >= d) x += y;
-        }
+        const uint32_t x = wave_inclusive_scan(v);
         if (threadIdx.x < kRows * kWaves) cnt[threadIdx.x] = x - v;
         if (threadIdx.x == kWave - 1) tot = x;
     }

@@ -324,24 +324,14 @@ __device__ __forceinline__ void block_row_scan(const uint32_t (&v)[kUPer], uint3
     uint32_t incl[kUPer];
 #pragma unroll
     for (uint32_t i = 0; i < kUPer; ++i) {
-        uint32_t x = v[i];
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d, kWave);
-            if (lane_id() >= d) x += y;
-        }
+        const uint32_t x = wave_inclusive_scan(v[i]);
         incl[i] = x;
         if (lane_id() == kWave - 1) tot[i * kWaves + wave_id()] = x;
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
         const uint32_t t = threadIdx.x < kUPer * kWaves ? tot[threadIdx.x] : 0u;
-        uint32_t x = t;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d, kWave);
-            if (lane_id() >= d) x += y;
-        }
+        const uint32_t x = wave_inclusive_scan(t);
         if (threadIdx.x < kUPer * kWaves) tot[threadIdx.x] = x - t;
     }
     __syncthreads();
