@@ -258,60 +258,40 @@ __device__ __forceinline__ void chunk_range(uint32_t nchunk, uint32_t *first, ui
 }
 
 // ------------------------------------------------------------------ norm
-// Lane l of wave w holds elements [1024 j + 256 w + 4 l, +4) of row j: its
-// (x0^2 + x1^2) + (x2^2 + x3^2) is a level-2 node of the pairwise tree.  The
-// lane nodes go to LDS in index order; thread t then owns the 4 consecutive
-// level-2 nodes [4 t, 4 t + 4) (a 16-element subtree), and the 256 thread
-// sums are combined by block_tree_sum into the chunk's level-12 node.
-// The persistent grid strides over the chunks (workgroup b takes b, b + grid,
-// ...), so the resident workgroups read neighbouring chunks at any time; a
-// contiguous range per workgroup measured 4% slower.
+// One workgroup per chunk.  Lane l of wave w holds elements
+// [1024 j + 256 w + 4 l, +4) of row j: its (x0^2 + x1^2) + (x2^2 + x3^2) is a
+// level-2 node of the pairwise tree.  The lane nodes go to LDS in index
+// order; thread t then owns the 4 consecutive level-2 nodes [4 t, 4 t + 4)
+// (a 16-element subtree), and the 256 thread sums are combined by
+// block_tree_sum into the chunk's level-12 node.  (A persistent grid striding
+// over the chunks, each workgroup loading its next chunk during the tree,
+// measured 1-2 us slower on the DeepSpeech sizes: the resident workgroups
+// already keep enough loads in flight.)
 __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float *__restrict__ G,
                                                           DgcWs w) {
-    const uint32_t c0 = blockIdx.x, c1 = P.ndchunk, step = gridDim.x;
+    const uint32_t c = blockIdx.x;
     __shared__ double node[kChunk / 4];  // level-2 nodes of the chunk, in order
-    float cur[kRows][4], nxt[kRows][4];
-    ChunkWalker walk;
-    ChunkInfo ci;
-    if (c0 < c1) {
-        ci = walk.at(P, c0);
-        const BufRsrc rg = chunk_buf(G + ci.lo, ci.cnt);
+    float x[kRows][4];
+    const ChunkRec rec = P.dchunk_rec[c];
+    const BufRsrc rg = chunk_buf(G + rec.x, rec.y);
 #pragma unroll
-        for (int j = 0; j < kRows; ++j) load4(rg, row_elem(j), cur[j]);
+    for (int j = 0; j < kRows; ++j) load4(rg, row_elem(j), x[j]);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+        double a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double d = static_cast<double>(x[j][q]);
+            a[q] = d * d;
+        }
+        node[j * kBlock + threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
     }
-    for (uint32_t c = c0; c < c1; c += step) {
-        ChunkInfo cn;
-        if (c + step < c1) {
-            cn = walk.at(P, c + step);
-            const BufRsrc rn = chunk_buf(G + cn.lo, cn.cnt);
-#pragma unroll
-            for (int j = 0; j < kRows; ++j) load4(rn, row_elem(j), nxt[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < kRows; ++j) {
-            double a[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                double x = static_cast<double>(cur[j][q]);
-                a[q] = x * x;
-            }
-            node[j * kBlock + threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
-        }
-        __syncthreads();
-        // four consecutive level-2 nodes: the 16-element level-4 node of thread t
-        const double t0 = node[4 * threadIdx.x] + node[4 * threadIdx.x + 1];
-        const double t1 = node[4 * threadIdx.x + 2] + node[4 * threadIdx.x + 3];
-        double t[1] = {t0 + t1};
-        const double chunk_sum = block_tree_sum(t[0]);
-        if (threadIdx.x == 0) w.partial[c] = chunk_sum;
-        if (c + step < c1) {
-            ci = cn;
-#pragma unroll
-            for (int j = 0; j < kRows; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) cur[j][q] = nxt[j][q];
-        }
-    }
+    __syncthreads();
+    // four consecutive level-2 nodes: the 16-element level-4 node of thread t
+    const double t0 = node[4 * threadIdx.x] + node[4 * threadIdx.x + 1];
+    const double t1 = node[4 * threadIdx.x + 2] + node[4 * threadIdx.x + 3];
+    const double chunk_sum = block_tree_sum(t0 + t1);
+    if (threadIdx.x == 0) w.partial[c] = chunk_sum;
 }
 
 // ------------------------------------------------------------------ prep
@@ -1526,133 +1506,73 @@ __device__ __forceinline__ uint32_t sel_radix(uint32_t rank, Each each, uint32_t
     return prefix;
 }
 
-// T's fine bin b* of a segment, found by one wave from the fine histogram:
-// fewer than k staged keys lie in the bins above b*, at least k in b* and
-// above.  ok: the selection takes select's fast branch (at least k staged
-// keys, b* below the last bin, and a bin of one key or at most kXListCap
-// keys).
+// One workgroup per collect block (up to kXBlockChunks chunks of one
+// segment, a quarter per wave): T's fine bin b* is found once from the
+// segment's histogram (256 threads, 8 bins each: fewer than k staged keys in
+// the bins above b*, at least k in b* and above); then each chunk's staged
+// keys above b* (low u16) and in it (high u16) go to cpack, and (bins wider
+// than one key) its first kSamples keys in the bin, in staging order, to its
+// row of skey (select gathers the rows; a chunk with more in the bin is read
+// again there).  Segments whose selection takes a slower branch of select
+// (fewer than k staged keys, b* the last bin, or more keys in b* than the
+// list holds) are skipped.  Each wave reads the first 64 staged keys of its
+// chunks with their counts, before b* is known (a chunk's 4096-entry slot is
+// always there to read; keys past the staged count are ignored).  (Appending
+// the bin's keys to one list per segment through a shared counter, or
+// finding the bin per wave from the whole histogram, took 20 us on the
+// DeepSpeech sizes.)
+constexpr uint32_t kXCollectCpw = kXBlockChunks / kWaves;
 struct FineBin {
     uint32_t bstar, above, in;
     bool ok;
 };
-__device__ __forceinline__ FineBin wave_fine_bin(const uint32_t *hist, uint32_t k, uint32_t fs) {
-    const uint32_t lane = lane_id();
-    // lane l holds bins [b0, b0 + 32) with b0 = 2016 - 32 l: lane 0 the highest
-    const uint32_t b0 = kFineBins - 32u * (lane + 1u);
-    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + b0);
-    uint32_t hv[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint4 q = h4[i];
-        hv[4 * i] = q.x;
-        hv[4 * i + 1] = q.y;
-        hv[4 * i + 2] = q.z;
-        hv[4 * i + 3] = q.w;
-    }
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += hv[i];
-    const uint32_t incl = wave_inclusive_scan(sum);  // keys in lanes 0..l
-    FineBin r{0u, 0u, 0u, false};
-    const uint64_t reach = __ballot(incl >= k);
-    if (reach == 0) return r;  // fewer than k staged keys
-    const int L = __ffsll(static_cast<unsigned long long>(reach)) - 1;
-    uint32_t acc = incl - sum, bb = 0, ab = 0, cb = 0;
-    bool found = false;
-#pragma unroll
-    for (int i = 31; i >= 0; --i) {
-        if (!found && acc + hv[i] >= k) {
-            found = true;
-            bb = b0 + i;
-            ab = acc;
-            cb = hv[i];
-        }
-        acc += hv[i];
-    }
-    r.bstar = lane_val(bb, L);
-    r.above = lane_val(ab, L);
-    r.in = lane_val(cb, L);
-    r.ok = r.bstar != kFineBins - 1 && (fs == 0 || r.in <= kXListCap);
-    return r;
-}
-
-// Chip-wide, kXCollectChunks chunks per workgroup (a quarter per wave): each
-// chunk's staged keys above T's fine bin (low u16) and in it (high u16) go to
-// cpack, and (bins wider than one key) its first kSamples keys in the bin, in
-// staging order, to its row of skey (select gathers the rows; a chunk with
-// more in the bin is read again there).  Segments whose selection takes a
-// slower branch of select are skipped.  T's bin is found once per workgroup
-// when its chunks share a segment (256 threads, 8 bins each), else per wave
-// and segment.  Each wave reads the first 64 staged keys of its chunks with
-// their records, before T's bin is known (a chunk's 4096-entry slot is always
-// there to read; keys past the staged count are ignored).  (Appending the
-// bin's keys to one list per segment through a shared counter, and finding
-// the bin in every wave from the whole histogram, took 20 us on the
-// DeepSpeech sizes.)
-constexpr uint32_t kXCollectChunks = 32;
-constexpr uint32_t kXCollectCpw = kXCollectChunks / kWaves;
 __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w) {
-    const uint32_t cb0 = blockIdx.x * kXCollectChunks;
-    const uint32_t s_first = P.dchunk_seg[cb0];
-    const uint32_t s_last = P.dchunk_seg[min(cb0 + kXCollectChunks, P.ndchunk) - 1];
+    const uint2 blk = P.xblock[blockIdx.x];
+    const uint32_t s = blk.x;
+    const SegDev seg = P.seg[s];
+    const uint32_t cend = seg.dchunk0 + seg.dnchunk;  // the segment's chunks end here
     const uint32_t lane = lane_id();
-    const uint32_t c0 = cb0 + wave_id() * kXCollectCpw;
-    const uint32_t cl = min(c0 + lane % kXCollectCpw, P.ndchunk - 1);
-    const uint32_t my_seg = P.dchunk_seg[cl];
+    const uint32_t c0 = blk.y + wave_id() * kXCollectCpw;
+    const uint32_t cl = min(c0 + lane % kXCollectCpw, cend - 1);
     const uint32_t my_n = min(w.ccount[cl], P.dchunk_rec[cl].y);
     uint32_t key0[kXCollectCpw];
 #pragma unroll
     for (uint32_t j = 0; j < kXCollectCpw; ++j)
-        key0[j] = mag_key(w.sval[(size_t(min(c0 + j, P.ndchunk - 1)) << kChunkLog2) + lane]);
-    uint32_t cur = ~0u, Lkey = 0, fs = 0;
-    FineBin fb{};
-    if (s_first == s_last) {
-        // thread t holds bins [2040 - 8 t, 2048 - 8 t): thread 0 the highest
-        __shared__ FineBin sh_fb;
-        const SegDev seg = P.seg[s_first];
-        const uint32_t k = seg_k(seg, w);
-        const uint32_t b0 = kFineBins - 8u * (threadIdx.x + 1u);
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(xtables(w, s_first) + b0);
-        const uint4 qa = h4[0], qb = h4[1];
-        const uint32_t hv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        uint32_t tsum = 0;
+        key0[j] = mag_key(w.sval[(size_t(min(c0 + j, cend - 1)) << kChunkLog2) + lane]);
+    const uint32_t k = seg_k(seg, w);
+    const uint32_t Lkey = w.st[s].Lkey, fs = w.st[s].fshift;
+    // thread t holds bins [2040 - 8 t, 2048 - 8 t): thread 0 the highest
+    __shared__ FineBin sh_fb;
+    const uint32_t b0 = kFineBins - 8u * (threadIdx.x + 1u);
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(xtables(w, s) + b0);
+    const uint4 qa = h4[0], qb = h4[1];
+    const uint32_t hv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    uint32_t tsum = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tsum += hv[i];
-        if (threadIdx.x == 0) sh_fb = FineBin{0u, 0u, 0u, false};
-        uint32_t total;
-        const uint32_t pre = block_exclusive_scan<uint32_t, kBlock>(tsum, &total);
-        if (total >= k && pre < k && pre + tsum >= k) {
-            uint32_t acc = pre;
-            bool found = false;
+    for (int i = 0; i < 8; ++i) tsum += hv[i];
+    if (threadIdx.x == 0) sh_fb = FineBin{0u, 0u, 0u, false};
+    uint32_t total;
+    const uint32_t pre = block_exclusive_scan<uint32_t, kBlock>(tsum, &total);
+    if (total >= k && pre < k && pre + tsum >= k) {
+        uint32_t acc = pre;
+        bool found = false;
 #pragma unroll
-            for (int i = 7; i >= 0; --i) {
-                if (!found && acc + hv[i] >= k) {
-                    found = true;
-                    const uint32_t bs = b0 + i;
-                    sh_fb = FineBin{bs, acc, hv[i], bs != kFineBins - 1 && (w.st[s_first].fshift == 0 || hv[i] <= kXListCap)};
-                }
-                acc += hv[i];
+        for (int i = 7; i >= 0; --i) {
+            if (!found && acc + hv[i] >= k) {
+                found = true;
+                const uint32_t bs = b0 + i;
+                sh_fb = FineBin{bs, acc, hv[i], bs != kFineBins - 1 && (fs == 0 || hv[i] <= kXListCap)};
             }
+            acc += hv[i];
         }
-        __syncthreads();
-        fb = sh_fb;
-        cur = s_first;
-        Lkey = w.st[s_first].Lkey;
-        fs = w.st[s_first].fshift;
     }
+    __syncthreads();
+    const FineBin fb = sh_fb;
+    if (!fb.ok) return;
 #pragma unroll
     for (uint32_t j = 0; j < kXCollectCpw; ++j) {
         const uint32_t c = c0 + j;
-        if (c >= P.ndchunk) break;
-        const uint32_t s = lane_val(my_seg, j);
-        if (s != cur) {
-            cur = s;
-            const SegDev seg = P.seg[s];
-            Lkey = w.st[s].Lkey;
-            fs = w.st[s].fshift;
-            fb = wave_fine_bin(xtables(w, s), seg_k(seg, w), fs);
-        }
-        if (!fb.ok) continue;
+        if (c >= cend) break;
         const uint32_t n = lane_val(my_n, j);
         uint32_t gt = 0, in = 0;
         for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
@@ -1983,17 +1903,24 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
         const uint64_t pre2 = block_exclusive_scan<uint64_t, kSelBlock>(uint64_t(gt_sum) | (uint64_t(eq_sum) << 32), &tot2);
         uint32_t eq_run = static_cast<uint32_t>(pre2 >> 32);
         uint32_t sel_run = static_cast<uint32_t>(pre2) + min(need_eq, eq_run);
+        // each chunk's first slot to cpk and staged count | quota << 16 to
+        // cnn; then the records in chunk order, a chunk's end slot being the
+        // next one's first (k after the last: the chunks send gt + need_eq)
 #pragma unroll
         for (uint32_t b = 0; b < kSelScanRun; ++b) {
             const uint32_t i = t1 + b;
             if (b < per1 && i < nch) {
                 const uint32_t e = pk[b] >> 16, g = pk[b] & 0xFFFFu;
                 const uint32_t take = need_eq > eq_run ? min(need_eq - eq_run, e) : 0u;
-                w.crec[c0 + i] = make_uint4(base + sel_run, base + sel_run + g + take, T, cnn[i] | (take << 16));
+                cpk[i] = sel_run;
+                cnn[i] |= take << 16;
                 eq_run += e;
                 sel_run += g + take;
             }
         }
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nch; i += kSelBlock)
+            w.crec[c0 + i] = make_uint4(base + cpk[i], base + (i + 1 < nch ? cpk[i + 1] : k), T, cnn[i]);
     } else {
         // each chunk's keys above and at T (low and high u16), then the
         // ordered scan in rounds
@@ -2215,11 +2142,11 @@ void launch_exact(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const S
                   gc_sparse *out, hipStream_t stream) {
     const unsigned segs = static_cast<unsigned>(plan->nseg);
     if (clip)
-        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, src.G, w));
+        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, src.G, w));
     GC_LAUNCH("dgc_prepare", stream, dgc_prepare_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, clip ? 1 : 0, thr));
     if (w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode, true><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
-    GC_LAUNCH("dgc_collect", stream, dgc_xcollect_kernel<<<grid_1d(plan->ndchunk, kXCollectChunks), kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_collect", stream, dgc_xcollect_kernel<<<static_cast<unsigned>(plan->xblock.size()), kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off));
     if (plan->ndchunk >= kWideChunks)
         GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
@@ -2235,7 +2162,7 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
     const unsigned segs = static_cast<unsigned>(plan->nseg);
     const unsigned wave_grid = grid_1d(plan->ndchunk, kWaves);
     if (clip)
-        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<persistent_grid(dgc_norm_kernel, plan->ndchunk), kBlock, 0, stream>>>(P, src.G, w));
+        GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, src.G, w));
     // sampled selection: one workgroup per segment finds the sample quantile
     // unless a segment has more samples than kQuantOneBlock
     bool multi_q = false;

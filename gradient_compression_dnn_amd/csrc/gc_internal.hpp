@@ -50,6 +50,10 @@ struct SegDev {
     uint32_t mbase;      // first word of the segment's run in a selection bitmap
 };
 
+// Exact DGC: the collect kernel's workgroups each take up to kXBlockChunks
+// chunks of one segment.
+constexpr uint32_t kXBlockChunks = 32;
+
 constexpr int kBinGroupLog2 = 12;  // bins per group of the scale's pairwise tree
 constexpr uint32_t kBinGroup = 1u << kBinGroupLog2;
 
@@ -67,10 +71,12 @@ struct PlanDev {
     const uint32_t *achunk_seg; // [nachunk]
     const uint64_t *seg_start;  // [nseg] offsets, for searching an index
     const uint32_t *bgroup_seg; // [nbgroup] segment of each bin group
+    const uint2 *xblock;        // [nxblock] exact DGC collect blocks: segment, first DGC chunk
     int nseg;
     uint32_t ndchunk;
     uint32_t nachunk;
     uint32_t nbgroup;
+    uint32_t nxblock;
     uint64_t n_total;
 };
 
@@ -92,6 +98,7 @@ struct gc_plan {
     std::vector<uint32_t> achunk_seg;
     std::vector<uint64_t> seg_start;
     std::vector<uint32_t> bgroup_seg;
+    std::vector<uint2> xblock;  // exact DGC collect blocks (kXBlockChunks chunks of one segment at most)
     std::vector<gc::ChunkRec> dchunk_rec;
     std::vector<gc::ChunkRec> achunk_rec;
     // device copies, one per device, uploaded on first use
@@ -143,20 +150,6 @@ __host__ __device__ constexpr uint64_t ceil_div(uint64_t a, uint64_t b) { return
 
 inline unsigned grid_1d(uint64_t n, unsigned per_block) {
     return static_cast<unsigned>((n + per_block - 1) / per_block);
-}
-
-// Upper bound on the workgroups of a persistent pass (256 CUs x 8 resident
-// 256-thread workgroups at full occupancy).
-constexpr unsigned kPersistentBlocks = 256 * 8;
-
-// Workgroups of a persistent pass of `kernel` (256 threads, no dynamic LDS):
-// as many as are resident at once on the current device, given the kernel's
-// registers and LDS, so that every workgroup starts in the first round;
-// never more than the work items, never fewer than 1.
-unsigned resident_grid(const void *kernel, uint64_t items);
-template <class K>
-unsigned persistent_grid(K *kernel, uint64_t items) {
-    return resident_grid(reinterpret_cast<const void *>(kernel), items);
 }
 
 // Kernel timing (see gc_timing_enable): returns an event to record before

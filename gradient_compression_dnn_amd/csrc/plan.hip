@@ -25,39 +25,9 @@ gc_status hip_error(hipError_t e, const char *what) {
 
 void clear_error() { g_last_error.clear(); }
 
-unsigned resident_grid(const void *kernel, uint64_t items) {
-    struct Entry {
-        const void *kernel;
-        int device;
-        unsigned blocks;
-    };
-    static std::mutex mu;
-    static std::vector<Entry> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-    unsigned blocks = 0;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        for (const Entry &e : cache)
-            if (e.kernel == kernel && e.device == dev) blocks = e.blocks;
-    }
-    if (blocks == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus < 1)
-            cus = 256;
-        blocks = std::min<unsigned>(kPersistentBlocks, unsigned(per_cu) * unsigned(cus));
-        std::lock_guard<std::mutex> lock(mu);
-        cache.push_back({kernel, dev, blocks});
-    }
-    return static_cast<unsigned>(items < blocks ? (items ? items : 1) : blocks);
-}
-
 // Layout of the per-device table blob.
 struct BlobLayout {
-    size_t seg, dchunk, achunk, start, bgroup, drec, arec, total;
+    size_t seg, dchunk, achunk, start, bgroup, xblock, drec, arec, total;
 };
 
 static BlobLayout blob_layout(const gc_plan *p) {
@@ -74,6 +44,7 @@ static BlobLayout blob_layout(const gc_plan *p) {
     L.achunk = take(sizeof(uint32_t) * p->achunk_seg.size());
     L.start = take(sizeof(uint64_t) * p->seg_start.size());
     L.bgroup = take(sizeof(uint32_t) * p->bgroup_seg.size());
+    L.xblock = take(sizeof(uint2) * p->xblock.size());
     L.drec = take(sizeof(ChunkRec) * p->dchunk_rec.size());
     L.arec = take(sizeof(ChunkRec) * p->achunk_rec.size());
     L.total = std::max<size_t>(o, 256);
@@ -106,6 +77,7 @@ static gc_status plan_tables(const gc_plan *cplan, PlanDev *out, bool upload) {
                         sizeof(uint64_t) * plan->seg_start.size());
             std::memcpy(host.data() + L.bgroup, plan->bgroup_seg.data(),
                         sizeof(uint32_t) * plan->bgroup_seg.size());
+            std::memcpy(host.data() + L.xblock, plan->xblock.data(), sizeof(uint2) * plan->xblock.size());
             std::memcpy(host.data() + L.drec, plan->dchunk_rec.data(),
                         sizeof(ChunkRec) * plan->dchunk_rec.size());
             std::memcpy(host.data() + L.arec, plan->achunk_rec.data(),
@@ -124,10 +96,12 @@ static gc_status plan_tables(const gc_plan *cplan, PlanDev *out, bool upload) {
     out->achunk_seg = reinterpret_cast<const uint32_t *>(b + L.achunk);
     out->seg_start = reinterpret_cast<const uint64_t *>(b + L.start);
     out->bgroup_seg = reinterpret_cast<const uint32_t *>(b + L.bgroup);
+    out->xblock = reinterpret_cast<const uint2 *>(b + L.xblock);
     out->dchunk_rec = reinterpret_cast<const ChunkRec *>(b + L.drec);
     out->achunk_rec = reinterpret_cast<const ChunkRec *>(b + L.arec);
     out->nseg = plan->nseg;
     out->nbgroup = plan->nbgroup;
+    out->nxblock = static_cast<uint32_t>(plan->xblock.size());
     out->ndchunk = plan->ndchunk;
     out->nachunk = plan->nachunk;
     out->n_total = plan->n_total;
@@ -223,6 +197,8 @@ gc_status gc_plan_create(const gc_segment *segs, int nseg, uint64_t n_total, gc_
         for (uint32_t g2 = 0; g2 < d.nbgroup; ++g2) p->bgroup_seg.push_back(static_cast<uint32_t>(s));
         bin0 += d.nbins;
         kbase += g.k;
+        for (uint32_t c = 0; c < d.dnchunk; c += kXBlockChunks)
+            p->xblock.push_back(make_uint2(static_cast<uint32_t>(s), d.dchunk0 + c));
         for (uint32_t c = 0; c < d.dnchunk; ++c) {
             p->dchunk_seg.push_back(static_cast<uint32_t>(s));
             const uint32_t first = c * uint32_t(kChunk);
