@@ -52,9 +52,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")  # another build of oracle.c (the sanitizer check's)
+        if not path:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            path = _LIB
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L.orc_psum64.restype = ctypes.c_double
         L.orc_psum64.argtypes = [P, ctypes.c_uint64]
