@@ -62,6 +62,7 @@ def lib():
         L.orc_psum64.restype = ctypes.c_double
         L.orc_psum64.argtypes = [P, ctypes.c_uint64]
         L.orc_adacomp.argtypes = [P, ctypes.c_int, P, P, ctypes.c_float, P, P, P, P, P]
+        L.orc_adacomp_rule.argtypes = [P, ctypes.c_int, P, P, ctypes.c_float, ctypes.c_int, P, P, P, P, P]
         L.orc_dgc.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_float, ctypes.c_float,
                               ctypes.c_int, P, P, P, P]
         L.orc_dgc_ex.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P]
@@ -123,7 +124,13 @@ def psum64(x) -> float:
     return lib().orc_psum64(_ptr(x), x.size)
 
 
-def adacomp(table, dW, R, scale_factor=2.0):
+# AdaComp threshold readings (oracle.c): the factor on the accumulated
+# residual (the default), or on the new gradient with the bin max always sent
+RULE_RESIDUAL = 0
+RULE_GRADIENT = 1
+
+
+def adacomp(table, dW, R, scale_factor=2.0, rule=RULE_RESIDUAL):
     """One AdaComp step.  Returns (R_new, idx, val, seg_off, seg_scale, gmax)."""
     t = np.asarray(table, dtype=np.int64).reshape(-1, 4)
     dW = _f32(dW)
@@ -135,8 +142,8 @@ def adacomp(table, dW, R, scale_factor=2.0):
     seg_off = np.zeros(len(t) + 1, np.uint32)
     seg_scale = np.zeros(max(len(t), 1), np.float32)
     gmax = np.zeros(max(nbins, 1), np.float32)
-    lib().orc_adacomp(_segs(t), len(t), _ptr(dW), _ptr(R), float(scale_factor), _ptr(idx),
-                      _ptr(val), _ptr(seg_off), _ptr(seg_scale), _ptr(gmax))
+    lib().orc_adacomp_rule(_segs(t), len(t), _ptr(dW), _ptr(R), float(scale_factor), int(rule), _ptr(idx),
+                           _ptr(val), _ptr(seg_off), _ptr(seg_scale), _ptr(gmax))
     m = int(seg_off[-1])
     return R, idx[:m].copy(), val[:m].copy(), seg_off, seg_scale[:len(t)], gmax[:nbins]
 

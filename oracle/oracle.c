@@ -65,8 +65,21 @@ double orc_psum64(const double *x, uint64_t m)
  *  - what is not sent stays in the residual (residual gradient compression,
  *    Abstract); layers are treated independently.
  */
+/*
+ * Two readings of the adaptive threshold (the pages do not fix which one is
+ * meant; neither is pinned by them):
+ *  rule 0 (the default): the scale factor s multiplies the accumulated
+ *    residual G = R + dW; entry i is sent when g_max(bin) > 0 and
+ *    fl(s |G_i|) >= g_max(bin);
+ *  rule 1: the factor weighs the new gradient instead, H = R + s dW, formed
+ *    from G as H_i = fl(G_i + fl((s - 1) dW_i)) (for s = 2, fl(G_i + dW_i));
+ *    entry i is sent when g_max(bin) > 0 and |H_i| >= g_max(bin), and every
+ *    entry with |G_i| = g_max(bin) is sent as well (the bin's max always is).
+ * Everything else (bin maxima of |G|, the layer scale, sign times scale, the
+ * residual G - q) is the same under both.
+ */
 static void adacomp_segment(const orc_seg *sg, const float *dW, float *R,
-                            float s, uint32_t *idx, float *val,
+                            float s, int rule, uint32_t *idx, float *val,
                             uint32_t *count, float *scale_out, float *gmax_out)
 {
     const uint64_t base = sg->offset;
@@ -98,11 +111,19 @@ static void adacomp_segment(const orc_seg *sg, const float *dW, float *R,
 
     /* selection, quantization, new residual */
     uint32_t c = 0;
+    const float s1 = s - 1.0f;
     for (uint32_t i = 0; i < n; ++i) {
         float g = G[i];
         float gm = gmax[i / L];
-        float t = s * fabsf(g);
-        if (gm > 0.0f && t >= gm) {
+        int send;
+        if (rule == 0) {
+            float t = s * fabsf(g);
+            send = gm > 0.0f && t >= gm;
+        } else {
+            float h = g + s1 * dW[base + i];
+            send = gm > 0.0f && (fabsf(h) >= gm || fabsf(g) >= gm);
+        }
+        if (send) {
             float q = copysignf(scale, g);
             R[base + i] = g - q;
             idx[c] = (uint32_t)(base + i);
@@ -124,6 +145,13 @@ void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
                  float scale_factor, uint32_t *out_idx, float *out_val,
                  uint32_t *seg_off, float *seg_scale, float *gmax_out)
 {
+    orc_adacomp_rule(segs, nseg, dW, R, scale_factor, 0, out_idx, out_val, seg_off, seg_scale, gmax_out);
+}
+
+void orc_adacomp_rule(const orc_seg *segs, int nseg, const float *dW, float *R,
+                      float scale_factor, int rule, uint32_t *out_idx, float *out_val,
+                      uint32_t *seg_off, float *seg_scale, float *gmax_out)
+{
     /* segment s may emit up to n_s entries; stage each at its own offset */
     uint64_t *stage_at = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nseg + 1));
     uint64_t *bin_at = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nseg + 1));
@@ -140,7 +168,7 @@ void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (int s = 0; s < nseg; ++s)
-        adacomp_segment(&segs[s], dW, R, scale_factor, sidx + stage_at[s],
+        adacomp_segment(&segs[s], dW, R, scale_factor, rule, sidx + stage_at[s],
                         sval + stage_at[s], &cnt[s], &seg_scale[s],
                         gmax_out ? gmax_out + bin_at[s] : NULL);
 

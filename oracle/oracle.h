@@ -41,6 +41,11 @@ double orc_psum64(const double *x, uint64_t m);
 void orc_adacomp(const orc_seg *segs, int nseg, const float *dW, float *R,
                  float scale_factor, uint32_t *out_idx, float *out_val,
                  uint32_t *seg_off, float *seg_scale, float *gmax_out);
+/* The same with the threshold rule chosen: 0 as orc_adacomp, 1 the factor on
+ * the new gradient with the bin max always sent (see oracle.c). */
+void orc_adacomp_rule(const orc_seg *segs, int nseg, const float *dW, float *R,
+                      float scale_factor, int rule, uint32_t *out_idx, float *out_val,
+                      uint32_t *seg_off, float *seg_scale, float *gmax_out);
 
 /* DGC options.  nesterov: 0 vanilla momentum (Alg. 3), 1 Nesterov (Alg. 4).
  * sampled: 0 exact top-k; 1 threshold estimated from a sample of one
