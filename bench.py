@@ -350,6 +350,46 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
     return out
 
 
+def adacomp_rule_messages(B, W, dev, log, steps: int = 10):
+    """Both readings of AdaComp's adaptive threshold (the factor on the
+    accumulated residual, the default; or on the new gradient, with the bin
+    max always sent) on the DeepSpeech and LSTM LM workloads: `steps` steps
+    from a zero residual with a fresh seeded gradient each (deferred
+    residual), then the last step's message packed.  Reports the fraction of
+    the n elements sent and the compression ratio 4 n / packed bytes.  Run
+    outside the timed region."""
+    import torch
+
+    res = {"steps": steps,
+           "page_context": "the AdaComp page reports ~200x end to end for fully connected and recurrent "
+                           "layers and ~40x for convolutional layers (trained models, not these "
+                           "synthetic gradients)"}
+    for name in ("deepspeech", "lstm_lm"):
+        w = W.make_config(name)
+        n = w.n_total
+        plan = B.Plan(w.table, n)
+        wsa, wsp = plan.workspace(B.GC_OP_ADACOMP, dev), plan.workspace(B.GC_OP_PACK, dev)
+        msg = B.Sparse.empty(plan, n, dev)
+        buf = torch.zeros(plan.pack_bound(B.GC_KIND_ADACOMP), dtype=torch.uint8, device=dev)
+        nbytes = torch.zeros(1, dtype=torch.int64, device=dev)
+        per = {}
+        for label, rule in (("residual", B.GC_ADACOMP_RULE_RESIDUAL), ("gradient", B.GC_ADACOMP_RULE_GRADIENT)):
+            R = torch.zeros(n, dtype=torch.float32, device=dev)
+            st = plan.adacomp_state(dev)
+            for t in range(steps):
+                g = W.gradient_device(w, t, dev)
+                B.gc_adacomp_compress(plan, g, R, 2.0, msg, wsa, state=st, rule=rule)
+            B.gc_pack(plan, B.GC_KIND_ADACOMP, msg, buf, nbytes, wsp)
+            torch.cuda.synchronize()
+            sent, nb = msg.count(), int(nbytes.item())
+            per[label] = {"entries": sent, "entries_frac": round(sent / n, 5), "packed_bytes": nb,
+                          "compression_ratio": round(4 * n / nb, 1)}
+            log(f"adacomp {name} rule {label}: {100.0 * sent / n:.2f}% sent, {4 * n / nb:.1f}x")
+        res[name] = per
+        del R, st, msg, buf
+    return res
+
+
 def measure_configs(B, W, dev, log, reps: int = 10):
     """The other workloads of the configuration list, each timed alone after
     the step timing (not part of `value`): ms per step and dense fp32 GB/s.
@@ -742,6 +782,7 @@ def main(argv=None):
         result["variants"] = measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, log,
                                               dmsg, amsg, dbuf, abuf, dn, an)
         result["configs"] = measure_configs(B, W, dev, log)
+        result["messages"]["adacomp_rules"] = adacomp_rule_messages(B, W, dev, log)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, grad_host, x0)

@@ -19,6 +19,7 @@ GC_KIND_DGC, GC_KIND_ADACOMP = 1, 2
 GC_SUM, GC_AVG = 0, 1
 GC_MOMENTUM_VANILLA, GC_MOMENTUM_NESTEROV = 0, 1
 GC_SELECT_EXACT, GC_SELECT_SAMPLED = 0, 1
+GC_ADACOMP_RULE_RESIDUAL, GC_ADACOMP_RULE_GRADIENT = 0, 1
 GC_MAX_BIN_LEN = 4096
 GC_MAX_MESSAGES = 64
 GC_MAX_SEGMENT_LEN = 0xFFFC0000
@@ -53,6 +54,11 @@ class gc_dgc_options(ctypes.Structure):
                 ("density_num", ctypes.c_uint32), ("density_den", ctypes.c_uint32)]
 
 
+class gc_adacomp_options(ctypes.Structure):
+    _fields_ = [("scale_factor", ctypes.c_float), ("rule", ctypes.c_int),
+                ("reserved", ctypes.c_uint32 * 2)]
+
+
 _lib = None
 
 # every symbol the header declares, with (restype, argtypes)
@@ -70,6 +76,8 @@ _SIGS = {
     "gc_plan_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int]),
     "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.c_float, _P, _P,
                                            ctypes.c_size_t, _P]),
+    "gc_adacomp_compress_ex": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
     "gc_adacomp_state_bytes": (ctypes.c_size_t, [_P]),
     "gc_adacomp_message_cap": (ctypes.c_uint64, [_P]),
     "gc_plan_upload": (ctypes.c_int, [_P]),
@@ -313,14 +321,20 @@ class Sparse:
 
 # -------------------------------------------------------------- hot calls
 def gc_adacomp_compress(plan: Plan, dW, R, scale_factor: float, out: Sparse, ws: torch.Tensor,
-                        state: torch.Tensor | None = None):
+                        state: torch.Tensor | None = None, rule: int | None = None):
     """state None: R is the exact residual.  state (Plan.adacomp_state()):
-    deferred mode, the residual is (R, state)."""
+    deferred mode, the residual is (R, state).  rule None:
+    gc_adacomp_compress (the default reading); else gc_adacomp_compress_ex
+    with that GC_ADACOMP_RULE_*."""
     n = plan.n_total
     msg = out.checked(plan, "out")
-    _check(load().gc_adacomp_compress(plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _state(state),
-                                      state.numel() if state is not None else 0, float(scale_factor),
-                                      ctypes.byref(msg), *_ws(ws), _stream(R)))
+    args = (plan.handle, _f32(dW, n, "dW"), _f32(R, n, "R"), _state(state),
+            state.numel() if state is not None else 0)
+    if rule is None:
+        _check(load().gc_adacomp_compress(*args, float(scale_factor), ctypes.byref(msg), *_ws(ws), _stream(R)))
+    else:
+        opt = gc_adacomp_options(float(scale_factor), int(rule))
+        _check(load().gc_adacomp_compress_ex(*args, ctypes.byref(opt), ctypes.byref(msg), *_ws(ws), _stream(R)))
 
 
 def gc_adacomp_message_cap(plan: Plan) -> int:

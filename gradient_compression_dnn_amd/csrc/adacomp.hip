@@ -95,9 +95,20 @@ __device__ __forceinline__ uint32_t div_small(uint32_t e, uint32_t L, float invL
     return q;
 }
 
-// G = R + dW for the chunk in the 4-wide layout, with each element's bin.
-__device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const float *dW, float invL,
-                                        float (&g)[kRows][4], uint32_t (&bin)[kRows][4]) {
+// The two readings of the adaptive threshold (the page's "Proposed method"
+// gives a scale factor s, empirically 2, without fixing what it multiplies):
+//   kRuleResidual (default): sent when g_max(bin) > 0 and fl(s |G|) >= g_max;
+//   kRuleGradient: the factor weighs the new gradient, H = fl(G + fl((s - 1)
+//     dW)) (for s = 2, fl(G + dW)); sent when g_max(bin) > 0 and |H| >= g_max,
+//     and every entry with |G| = g_max is sent too.
+constexpr int kRuleResidual = GC_ADACOMP_RULE_RESIDUAL;
+constexpr int kRuleGradient = GC_ADACOMP_RULE_GRADIENT;
+
+// G = R + dW for the chunk in the 4-wide layout, with each element's bin;
+// under kRuleGradient also H = G + (s - 1) dW (s1 = s - 1).
+template <int kRule>
+__device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const float *dW, float invL, float s1,
+                                        float (&g)[kRows][4], float (&h)[kRows][4], uint32_t (&bin)[kRows][4]) {
     const BufRsrc rr = chunk_buf(R + a.lo, a.cnt), rd = chunk_buf(dW + a.lo, a.cnt);
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
@@ -107,6 +118,7 @@ __device__ __forceinline__ void chunk_G(const AChunk &a, const float *R, const f
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             g[j][q] = r[q] + d[q];
+            if (kRule == kRuleGradient) h[j][q] = g[j][q] + s1 * d[q];
             bin[j][q] = div_small(row_elem(j) + q, a.L, invL);
         }
     }
@@ -155,16 +167,24 @@ __device__ __forceinline__ void chunk_bin_max(const AChunk &a, const float (&g)[
     }
 }
 
-// Selection against the bin maxima: element (row j, q) is sent when its
-// bin's max is positive and fl(sf |G|) reaches it.
-__device__ __forceinline__ bool selected(const AChunk &a, uint32_t e, float gq, uint32_t b, float sf,
+// Whether an entry (G, H) is sent against its bin's max gmx, by the rule.
+template <int kRule>
+__device__ __forceinline__ bool send_rule(float gq, float hq, float gmx, float sf) {
+    if (kRule == kRuleGradient) return gmx > 0.0f && (fabsf(hq) >= gmx || fabsf(gq) >= gmx);
+    const float t = sf * fabsf(gq);
+    return gmx > 0.0f && t >= gmx;
+}
+
+// Selection against the bin maxima (LDS bit patterns) of element e.
+template <int kRule>
+__device__ __forceinline__ bool selected(const AChunk &a, uint32_t e, float gq, float hq, uint32_t b, float sf,
                                          const uint32_t *gm) {
     const bool in = e < a.cnt;
     const float gmx = dev_u2f(gm[in ? b : 0u]);
-    const float t = sf * fabsf(gq);
-    return in && gmx > 0.0f && t >= gmx;
+    return in && send_rule<kRule>(gq, hq, gmx, sf);
 }
 
+template <int kRule>
 __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float *__restrict__ dW,
                                                          const float *__restrict__ R, float sf,
                                                          AdaWs w) {
@@ -175,9 +195,9 @@ __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float 
     const uint32_t nb = (a.cnt + L - 1) / L;
     __shared__ uint32_t gm[kChunk];
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = 0u;
-    float g[kRows][4];
+    float g[kRows][4], h[kRows][4];
     uint32_t bin[kRows][4];
-    chunk_G(a, R, dW, invL, g, bin);
+    chunk_G<kRule>(a, R, dW, invL, sf - 1.0f, g, h, bin);
     __syncthreads();
     chunk_bin_max(a, g, bin, gm);
     __syncthreads();
@@ -185,7 +205,8 @@ __global__ __launch_bounds__(kBlock) void ada_max_kernel(PlanDev P, const float 
 #pragma unroll
     for (int j = 0; j < kRows; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mine += selected(a, row_elem(j) + q, g[j][q], bin[j][q], sf, gm) ? 1u : 0u;
+        for (int q = 0; q < 4; ++q)
+            mine += selected<kRule>(a, row_elem(j) + q, g[j][q], h[j][q], bin[j][q], sf, gm) ? 1u : 0u;
     uint32_t total;
     (void)block_exclusive_scan(mine, &total);
     float *gout = w.gmax + a.bin_first;
@@ -270,6 +291,7 @@ __global__ __launch_bounds__(kBlock) void ada_offsets_kernel(int nseg, AdaWs w,
     if (threadIdx.x == 0) seg_off[nseg] = run;
 }
 
+template <int kRule>
 __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const float *__restrict__ dW,
                                                            float *__restrict__ R, float sf, AdaWs w,
                                                            const uint32_t *__restrict__ seg_off,
@@ -284,9 +306,9 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
     __shared__ float gm[kChunk];
     const float *gin = w.gmax + a.bin_first;
     for (uint32_t b = threadIdx.x; b < nb; b += kBlock) gm[b] = gin[b];
-    float g[kRows][4];
+    float g[kRows][4], h[kRows][4];
     uint32_t bin[kRows][4];
-    chunk_G(a, R, dW, invL, g, bin);
+    chunk_G<kRule>(a, R, dW, invL, sf - 1.0f, g, h, bin);
     const float scale = seg_scale[a.s];
     const uint32_t base = seg_off[a.s] + w.cpre[c];
     const uint32_t count = w.ccount[c];  // slots reserved for this chunk by ada_max
@@ -302,8 +324,7 @@ __global__ __launch_bounds__(kBlock) void ada_apply_kernel(PlanDev P, const floa
         for (int q = 0; q < 4; ++q) {
             const bool in = e0 + q < a.cnt;
             const float gmx = gm[in ? bin[j][q] : 0u];
-            const float t = sf * fabsf(g[j][q]);
-            flag[j][q] = in && gmx > 0.0f && t >= gmx;
+            flag[j][q] = in && send_rule<kRule>(g[j][q], h[j][q], gmx, sf);
             const float qv = copysignf(scale, g[j][q]);
             r[q] = flag[j][q] ? g[j][q] - qv : g[j][q];
         }
@@ -340,6 +361,7 @@ __device__ __forceinline__ float pending(float r, uint32_t held, int bit, float 
     return ((held >> bit) & 1u) ? r - copysignf(pscale, r) : r;
 }
 
+template <int kRule>
 __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float *__restrict__ dW,
                                                           float *__restrict__ R, float sf, AdaWs w,
                                                           AdaState S) {
@@ -354,7 +376,8 @@ __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float
     const size_t word = size_t(c) * kBlock + threadIdx.x;
     const uint32_t held = S.sel[word];
     const float pscale = S.scale[a.s];
-    float g[kRows][4];
+    const float s1 = sf - 1.0f;
+    float g[kRows][4], h[kRows][4];
     uint32_t bin[kRows][4];
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
@@ -364,6 +387,7 @@ __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             g[j][q] = pending(r[q], held, 4 * j + q, pscale) + d[q];
+            if (kRule == kRuleGradient) h[j][q] = g[j][q] + s1 * d[q];
             bin[j][q] = div_small(row_elem(j) + q, L, invL);
         }
     }
@@ -377,7 +401,7 @@ __global__ __launch_bounds__(kBlock) void ada_fold_kernel(PlanDev P, const float
     for (int j = 0; j < kRows; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const bool f = selected(a, row_elem(j) + q, g[j][q], bin[j][q], sf, gm);
+            const bool f = selected<kRule>(a, row_elem(j) + q, g[j][q], h[j][q], bin[j][q], sf, gm);
             bits |= uint32_t(f) << (4 * j + q);
             signs |= (dev_f2u(g[j][q]) >> 31) << (4 * j + q);
             mine += f ? 1u : 0u;
@@ -476,52 +500,78 @@ extern "C" size_t gc_adacomp_state_bytes(const gc_plan *plan) {
     return b;
 }
 
-extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, void *state,
-                                         size_t state_bytes, float scale_factor, gc_sparse *out,
-                                         void *ws, size_t ws_bytes, hipStream_t stream) {
-    clear_error();
-    if (!plan) return set_error(GC_EINVAL, "gc_adacomp_compress: plan is null");
-    if (!dW || !R) return set_error(GC_EINVAL, "gc_adacomp_compress: dW and R must be non-null");
-    if (!out || !out->idx || !out->val || !out->seg_off || !out->seg_scale)
-        return set_error(GC_EINVAL,
-                         "gc_adacomp_compress: out and its idx, val, seg_off, seg_scale must be non-null");
-    if (!(scale_factor >= 1.0f) || std::isinf(scale_factor))
-        return set_error(GC_EINVAL, "gc_adacomp_compress: scale_factor must be finite and >= 1");
-    if (out->cap < plan->seg_elems)
-        return set_error(GC_ECAPACITY, "gc_adacomp_compress: out->cap below gc_adacomp_message_cap");
-    size_t need = adacomp_workspace_bytes(plan);
-    if (!ws || ws_bytes < need)
-        return set_error(GC_ECAPACITY,
-                         "gc_adacomp_compress: workspace smaller than gc_plan_workspace_bytes");
-    if (reinterpret_cast<uintptr_t>(ws) % 256)
-        return set_error(GC_EINVAL, "gc_adacomp_compress: workspace must be 256-byte aligned");
-    if (state && state_bytes < gc_adacomp_state_bytes(plan))
-        return set_error(GC_ECAPACITY, "gc_adacomp_compress: state smaller than gc_adacomp_state_bytes");
-    if (state && reinterpret_cast<uintptr_t>(state) % 256)
-        return set_error(GC_EINVAL, "gc_adacomp_compress: state must be 256-byte aligned");
-    PlanDev P;
-    gc_status st = plan_device(plan, &P);
-    if (st != GC_OK) return st;
-    AdaWs w = ada_layout(plan, ws, nullptr);
+template <int kRule>
+static void adacomp_launch(const gc_plan *plan, const PlanDev &P, AdaWs w, const float *dW, float *R, void *state,
+                    float sf, gc_sparse *out, hipStream_t stream) {
     if (state) {
         const AdaState S = ada_state_layout(plan, state, nullptr);
-        GC_LAUNCH("ada_fold", stream, ada_fold_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w, S));
+        GC_LAUNCH("ada_fold", stream, ada_fold_kernel<kRule><<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, sf, w, S));
         GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
         GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale, S.scale));
         GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
         GC_LAUNCH("ada_emit", stream, ada_emit_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
             P, w, S, out->seg_off, out->seg_scale, out->idx, out->val));
     } else {
-        GC_LAUNCH("ada_max", stream, ada_max_kernel<<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, scale_factor, w));
+        GC_LAUNCH("ada_max", stream, ada_max_kernel<kRule><<<plan->nachunk, kBlock, 0, stream>>>(P, dW, R, sf, w));
         GC_LAUNCH("ada_binsum", stream, ada_binsum_kernel<<<plan->nbgroup, kBlock, 0, stream>>>(P, w));
         GC_LAUNCH("ada_scale", stream, ada_scale_kernel<<<plan->nseg, kBlock, 0, stream>>>(P, w, out->seg_scale, nullptr));
         GC_LAUNCH("ada_offsets", stream, ada_offsets_kernel<<<1, kBlock, 0, stream>>>(plan->nseg, w, out->seg_off));
-        GC_LAUNCH("ada_apply", stream, ada_apply_kernel<<<plan->nachunk, kBlock, 0, stream>>>(
-            P, dW, R, scale_factor, w, out->seg_off, out->seg_scale, out->idx, out->val));
+        GC_LAUNCH("ada_apply", stream, ada_apply_kernel<kRule><<<plan->nachunk, kBlock, 0, stream>>>(
+            P, dW, R, sf, w, out->seg_off, out->seg_scale, out->idx, out->val));
     }
+}
+
+static gc_status adacomp_compress(const char *fn, const gc_plan *plan, const float *dW, float *R, void *state,
+                           size_t state_bytes, float scale_factor, int rule, gc_sparse *out, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    const std::string f(fn);
+    if (!plan) return set_error(GC_EINVAL, f + ": plan is null");
+    if (!dW || !R) return set_error(GC_EINVAL, f + ": dW and R must be non-null");
+    if (!out || !out->idx || !out->val || !out->seg_off || !out->seg_scale)
+        return set_error(GC_EINVAL, f + ": out and its idx, val, seg_off, seg_scale must be non-null");
+    if (!(scale_factor >= 1.0f) || std::isinf(scale_factor))
+        return set_error(GC_EINVAL, f + ": scale_factor must be finite and >= 1");
+    if (rule != GC_ADACOMP_RULE_RESIDUAL && rule != GC_ADACOMP_RULE_GRADIENT)
+        return set_error(GC_EINVAL, f + ": rule must be GC_ADACOMP_RULE_RESIDUAL or GC_ADACOMP_RULE_GRADIENT");
+    if (out->cap < plan->seg_elems)
+        return set_error(GC_ECAPACITY, f + ": out->cap below gc_adacomp_message_cap");
+    size_t need = adacomp_workspace_bytes(plan);
+    if (!ws || ws_bytes < need) return set_error(GC_ECAPACITY, f + ": workspace smaller than gc_plan_workspace_bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return set_error(GC_EINVAL, f + ": workspace must be 256-byte aligned");
+    if (state && state_bytes < gc_adacomp_state_bytes(plan))
+        return set_error(GC_ECAPACITY, f + ": state smaller than gc_adacomp_state_bytes");
+    if (state && reinterpret_cast<uintptr_t>(state) % 256)
+        return set_error(GC_EINVAL, f + ": state must be 256-byte aligned");
+    PlanDev P;
+    gc_status st = plan_device(plan, &P);
+    if (st != GC_OK) return st;
+    AdaWs w = ada_layout(plan, ws, nullptr);
+    if (rule == GC_ADACOMP_RULE_GRADIENT)
+        adacomp_launch<kRuleGradient>(plan, P, w, dW, R, state, scale_factor, out, stream);
+    else
+        adacomp_launch<kRuleResidual>(plan, P, w, dW, R, state, scale_factor, out, stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_error(e, "gc_adacomp_compress launch");
+    if (e != hipSuccess) return hip_error(e, (f + " launch").c_str());
     return GC_OK;
+}
+
+extern "C" gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, void *state,
+                                         size_t state_bytes, float scale_factor, gc_sparse *out,
+                                         void *ws, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    return adacomp_compress("gc_adacomp_compress", plan, dW, R, state, state_bytes, scale_factor,
+                            GC_ADACOMP_RULE_RESIDUAL, out, ws, ws_bytes, stream);
+}
+
+extern "C" gc_status gc_adacomp_compress_ex(const gc_plan *plan, const float *dW, float *R, void *state,
+                                            size_t state_bytes, const gc_adacomp_options *opt,
+                                            gc_sparse *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    if (!opt) return set_error(GC_EINVAL, "gc_adacomp_compress_ex: opt is null");
+    if (opt->reserved[0] || opt->reserved[1])
+        return set_error(GC_EINVAL, "gc_adacomp_compress_ex: reserved fields must be 0");
+    return adacomp_compress("gc_adacomp_compress_ex", plan, dW, R, state, state_bytes, opt->scale_factor,
+                            opt->rule, out, ws, ws_bytes, stream);
 }
 
 extern "C" gc_status gc_adacomp_residual(const gc_plan *plan, const float *R, const void *state,

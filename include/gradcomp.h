@@ -199,6 +199,37 @@ gc_status gc_adacomp_compress(const gc_plan *plan, const float *dW, float *R, vo
                               size_t state_bytes, float scale_factor, gc_sparse *out,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The same step with the reading of the adaptive threshold chosen.  The
+ * AdaComp page ("Proposed method") builds the threshold from a scale factor
+ * (empirically 2x) that picks entries near the bin's max, without fixing what
+ * the factor multiplies; both readings are offered, and neither is pinned by
+ * the page:
+ *   GC_ADACOMP_RULE_RESIDUAL (gc_adacomp_compress): step a3 above;
+ *   GC_ADACOMP_RULE_GRADIENT: the factor weighs the new gradient instead,
+ *     a3' H_i = fl32(G_i + fl32((scale_factor - 1) * dW_i))
+ *              (for the factor 2, fl32(G_i + dW_i), i.e. R + 2 dW rounded
+ *               from G)
+ *         sel_i <=> g_max(b) > 0 and (|H_i| >= g_max(b) or |G_i| = g_max(b))
+ *         (every entry at the bin's max is sent, as under the default).
+ *   Steps a1, a2, a4-a6 and both residual modes are unchanged; an entry with
+ *   G_i = +-0 that H sends gets copysign(scale_s, G_i).
+ * opt: scale_factor finite and >= 1; rule one of the two; reserved zero.
+ * Arguments, layouts and the other errors as gc_adacomp_compress.
+ * Errors: GC_EINVAL also for a null opt, an unknown rule or nonzero
+ *         reserved fields.
+ */
+#define GC_ADACOMP_RULE_RESIDUAL 0
+#define GC_ADACOMP_RULE_GRADIENT 1
+typedef struct gc_adacomp_options {
+    float    scale_factor;  /* >= 1; 2.0 in the pages  */
+    int      rule;          /* GC_ADACOMP_RULE_*       */
+    uint32_t reserved[2];   /* must be 0               */
+} gc_adacomp_options;
+gc_status gc_adacomp_compress_ex(const gc_plan *plan, const float *dW, float *R, void *state,
+                                 size_t state_bytes, const gc_adacomp_options *opt, gc_sparse *out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of one learner's deferred-residual state for this plan (0 if plan
  * is NULL). */
 size_t gc_adacomp_state_bytes(const gc_plan *plan);

@@ -73,15 +73,16 @@ class HipPath:
         idx, val, off, _ = out.host()
         return Ud.cpu().numpy(), Vd.cpu().numpy(), idx, val, off
 
-    def adacomp(self, dW, R, scale_factor=2.0, tensors=False, state=None):
+    def adacomp(self, dW, R, scale_factor=2.0, tensors=False, state=None, rule=None):
         """One AdaComp call; with `state` (a deferred-residual state tensor) the
         returned R is the exact residual, materialized by gc_adacomp_residual,
-        while the device R keeps the deferred form."""
+        while the device R keeps the deferred form.  rule: a GC_ADACOMP_RULE_*
+        for gc_adacomp_compress_ex, None for gc_adacomp_compress."""
         dWd = dW if torch.is_tensor(dW) else to_dev(dW)
         Rd = R if torch.is_tensor(R) else to_dev(R)
         out = B.Sparse.empty(self.plan, self.n, dev())
         B.gc_adacomp_compress(self.plan, dWd, Rd, scale_factor, out, self.workspace(B.GC_OP_ADACOMP),
-                              state=state)
+                              state=state, rule=rule)
         torch.cuda.synchronize()
         if state is not None and not tensors:
             exact = torch.empty_like(Rd)
