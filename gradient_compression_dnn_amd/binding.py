@@ -76,6 +76,7 @@ _SIGS = {
     "gc_plan_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int]),
     "gc_adacomp_compress": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, ctypes.c_float, _P, _P,
                                            ctypes.c_size_t, _P]),
+    "gc_dgc_pack_bound": (ctypes.c_uint64, [_P, _P]),
     "gc_adacomp_compress_ex": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
     "gc_adacomp_state_bytes": (ctypes.c_size_t, [_P]),
@@ -376,6 +377,10 @@ def dgc_options(momentum: float, thr_G: float = 0.0, num_nodes: int = 1, nestero
 
 def gc_dgc_message_cap(plan: Plan, opt: gc_dgc_options) -> int:
     return int(load().gc_dgc_message_cap(plan.handle, ctypes.byref(opt)))
+
+
+def gc_dgc_pack_bound(plan: Plan, opt: gc_dgc_options | None) -> int:
+    return int(load().gc_dgc_pack_bound(plan.handle, ctypes.byref(opt) if opt is not None else None))
 
 
 def gc_dgc_step_ex(plan: Plan, G, U, V, opt: gc_dgc_options, out: Sparse, ws: torch.Tensor):

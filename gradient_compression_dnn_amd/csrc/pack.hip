@@ -33,6 +33,7 @@ struct PackWs {
     uint32_t *seg_esc;    // [nseg] escapes per segment
     uint64_t *blk_off;    // [nseg] byte offset of each block
     uint32_t *seg_E;      // [nseg]
+    uint32_t *overflow;   // [1] set by the layout pass when the stream exceeds out_cap
     size_t max_tiles;
 };
 
@@ -48,6 +49,7 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.seg_esc = c.take<uint32_t>(p->nseg);
     w.blk_off = c.take<uint64_t>(p->nseg);
     w.seg_E = c.take<uint32_t>(p->nseg);
+    w.overflow = c.take<uint32_t>(1);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -65,8 +67,8 @@ struct EntryCtx {
 };
 
 // Entries of segment s, clamped so that a malformed message can never make
-// the packer read past the message or write past gc_pack_bound: at most
-// max_entries (k for DGC, the length for AdaComp) and never past cap.
+// the packer read past the message: at most max_entries (the segment's
+// length) and never past cap.
 __device__ __forceinline__ uint32_t seg_entries(const uint32_t *seg_off, int s, uint32_t max_entries,
                                                 uint64_t cap) {
     uint32_t a = seg_off[s], b = seg_off[s + 1];
@@ -77,9 +79,10 @@ __device__ __forceinline__ uint32_t seg_entries(const uint32_t *seg_off, int s, 
     return static_cast<uint32_t>(n);
 }
 
-__device__ __forceinline__ uint32_t seg_max_entries(const SegDev &s, int kind) {
-    return kind == GC_KIND_DGC ? s.k : s.len;
-}
+// A DGC message may hold more than the plan's k per segment (a per-call
+// density, or the sampled selection's budget), an AdaComp one up to every
+// element: either kind is bounded by the segment's length.
+__device__ __forceinline__ uint32_t seg_max_entries(const SegDev &s, int) { return s.len; }
 
 // Gap before entry j (unsent elements since the previous entry) from the
 // loaded indices cur = idx[j] and prv = idx[j - 1]; out-of-order or
@@ -223,25 +226,26 @@ __global__ __launch_bounds__(kBlock) void pack_count_kernel(PlanDev P, int kind,
     }
 }
 
-// One workgroup: size every block from its entries and escapes, write the
-// stream header, block headers and pads, and the stream length.
+// One workgroup: size every block from its entries and escapes; when the
+// stream fits out_cap, write the stream header, block headers and pads;
+// always the stream length, and the overflow flag the write pass reads.
 __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind, uint64_t cap, uint32_t MAX,
                                                              const uint32_t *__restrict__ seg_off,
                                                              const float *__restrict__ seg_scale,
-                                                             uint8_t *__restrict__ out,
+                                                             uint8_t *__restrict__ out, uint64_t out_cap,
                                                              uint64_t *__restrict__ out_bytes, PackWs w) {
     uint64_t byte_run = 16;
     const bool dgc = kind == GC_KIND_DGC;
     for (int r = 0; r < P.nseg; r += kBlock) {
         int s = r + threadIdx.x;
         uint64_t sz = 0;
-        uint32_t E = 0, cnt = 0;
+        uint32_t E = 0;
         if (s < P.nseg) {
             const SegDev sg = P.seg[s];
             const uint32_t maxe = seg_max_entries(sg, kind);
-            cnt = seg_entries(seg_off, s, maxe, cap);
+            const uint32_t cnt = seg_entries(seg_off, s, maxe, cap);
             uint32_t esc = w.seg_esc[s];
-            // never more slots than gc_pack_bound reserves for the segment
+            // never more codes than a segment of this length can need
             uint64_t cap_e = uint64_t(maxe) + sg.len / MAX + 1;
             uint64_t e64 = uint64_t(cnt) + esc;
             E = static_cast<uint32_t>(e64 < cap_e ? e64 : cap_e);
@@ -250,25 +254,35 @@ __global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind
         uint64_t tot;
         uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
         if (s < P.nseg) {
-            uint64_t at = byte_run + pre;
-            w.blk_off[s] = at;
+            w.blk_off[s] = byte_run + pre;
             w.seg_E[s] = E;
+        }
+        byte_run += tot;
+    }
+    const bool fits = byte_run <= out_cap;
+    __syncthreads();
+    if (fits) {
+        for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
+            const uint64_t at = w.blk_off[s];
+            const uint32_t E = w.seg_E[s];
             uint32_t *h = reinterpret_cast<uint32_t *>(out + at);
             h[0] = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
             h[1] = P.seg[s].len;
             h[2] = E;
-            h[3] = dgc ? cnt : dev_f2u(seg_scale[s]);
+            h[3] = dgc ? seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap) : dev_f2u(seg_scale[s]);
             if (E & 1u) *reinterpret_cast<uint16_t *>(out + at + 16 + 2ull * E) = 0;
         }
-        byte_run += tot;
     }
     if (threadIdx.x == 0) {
-        uint32_t *h = reinterpret_cast<uint32_t *>(out);
-        h[0] = magic('G', 'C', 'P', '1');
-        h[1] = static_cast<uint32_t>(kind);
-        h[2] = static_cast<uint32_t>(P.nseg);
-        h[3] = 0u;
+        if (fits) {
+            uint32_t *h = reinterpret_cast<uint32_t *>(out);
+            h[0] = magic('G', 'C', 'P', '1');
+            h[1] = static_cast<uint32_t>(kind);
+            h[2] = static_cast<uint32_t>(P.nseg);
+            h[3] = 0u;
+        }
         *out_bytes = byte_run;
+        *w.overflow = fits ? 0u : 1u;
     }
 }
 
@@ -289,6 +303,7 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
                                                             const float *__restrict__ val, uint32_t MAX,
                                                             uint8_t *__restrict__ out, PackWs w) {
     const bool dgc = kind == GC_KIND_DGC;
+    if (*w.overflow) return;  // the stream does not fit out_cap: nothing is written
     for (uint32_t t = blockIdx.x; t < max_tiles; t += gridDim.x) {
         // the tile count and the tile's record in one round trip (records
         // past the count are never used)
@@ -395,16 +410,30 @@ size_t pack_workspace_bytes(const gc_plan *plan) {
 
 using namespace gc;
 
-extern "C" uint64_t gc_pack_bound(const gc_plan *plan, int kind) {
-    if (!plan || (kind != GC_KIND_DGC && kind != GC_KIND_ADACOMP)) return 0;
+// Stream bytes at most for messages of at most entries(s) entries per segment.
+template <class F>
+static uint64_t pack_bound_for(const gc_plan *plan, int kind, F entries) {
     const uint64_t MAX = kind == GC_KIND_DGC ? 65535 : 32767;
     const uint64_t per = kind == GC_KIND_DGC ? 6 : 2;
     uint64_t b = 16;
-    for (const auto &s : plan->seg) {
-        uint64_t entries = kind == GC_KIND_DGC ? s.k : s.len;
-        b += 16 + 2 + per * (entries + s.len / MAX + 1);
-    }
+    for (const auto &s : plan->seg) b += 16 + 2 + per * (entries(s) + s.len / MAX + 1);
     return b;
+}
+
+extern "C" uint64_t gc_pack_bound(const gc_plan *plan, int kind) {
+    if (!plan || (kind != GC_KIND_DGC && kind != GC_KIND_ADACOMP)) return 0;
+    return pack_bound_for(plan, kind, [&](const SegDev &s) -> uint64_t { return kind == GC_KIND_DGC ? s.k : s.len; });
+}
+
+extern "C" uint64_t gc_dgc_pack_bound(const gc_plan *plan, const gc_dgc_options *opt) {
+    if (!plan) return 0;
+    if (!opt) return gc_pack_bound(plan, GC_KIND_DGC);
+    return pack_bound_for(plan, GC_KIND_DGC, [&](const SegDev &s) -> uint64_t {
+        if (opt->select == GC_SELECT_SAMPLED) return std::min<uint64_t>(s.len, uint64_t(opt->over) * s.k);
+        if (opt->density_den == 0) return s.k;
+        const uint64_t k = (uint64_t(s.len) * opt->density_num + opt->density_den - 1) / opt->density_den;
+        return std::max<uint64_t>(1, std::min<uint64_t>(k, s.len));
+    });
 }
 
 extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in, uint8_t *out,
@@ -442,7 +471,7 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     GC_LAUNCH("pack_tiles", stream, pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w));
     GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
     GC_LAUNCH("pack_layout", stream, pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
-                                                 out_bytes, w));
+                                                 out_cap, out_bytes, w));
     GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, w.max_tiles, in->idx, in->val, MAX,
                                                    out, w));
     hipError_t e = hipGetLastError();

@@ -336,7 +336,7 @@ gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V
  * Byte-exact run-length encoding of a message ([DGC] §3.1: 32-bit values and
  * 16-bit zero-run lengths).  Little-endian; every block 4-byte aligned.
  *   stream header : u32 'GCP1', u32 kind, u32 nseg, u32 0
- *   DGC block     : u32 'DGC1', u32 n_s, u32 E, u32 k_s,
+ *   DGC block     : u32 'DGC1', u32 n_s, u32 E, u32 entries of the segment,
  *                   u16 run[E] (+ one u16 0 if E is odd), f32 val[E]
  *   AdaComp block : u32 'ADC1', u32 n_s, u32 E, f32 scale_s,
  *                   u16 code[E] (+ one u16 0 if E is odd);
@@ -345,14 +345,26 @@ gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V
  * (from the segment start for the first).  A run >= MAX is split: emit an
  * escape (run MAX; DGC value +0.0f), subtract MAX, repeat.  MAX is 65535 for
  * DGC and 32767 for AdaComp; E counts entries plus escapes.
- *   in       : a message produced for this plan (device counts are read).
- *   out      : device byte buffer of out_cap >= gc_pack_bound(plan, kind).
- *   out_bytes: device u64, receives the stream length.
+ *   in       : a message produced for this plan (device counts are read;
+ *              a segment's entries are taken up to its length).
+ *   out      : device byte buffer of out_cap >= gc_pack_bound(plan, kind),
+ *              which holds any AdaComp message and any DGC message of the
+ *              plan's k per segment.  A DGC message with more entries per
+ *              segment (a per-call density, or the sampled selection's
+ *              budget) may need up to gc_dgc_pack_bound(plan, opt) bytes.
+ *   out_bytes: device u64, receives the stream length.  When it exceeds
+ *              out_cap the stream did not fit: nothing was written to out,
+ *              and *out_bytes is the size to pack it into.
  * Errors: GC_EINVAL (bad kind / null), GC_ECAPACITY (out_cap or ws too small).
  */
 #define GC_KIND_DGC      1
 #define GC_KIND_ADACOMP  2
 uint64_t  gc_pack_bound(const gc_plan *plan, int kind);
+/* Stream bytes a DGC message of these selection options needs at most: the
+ * bound above with k_s replaced by the call's entries per segment (a
+ * per-call density's ceil(n_s num / den), or min(n_s, over k_s) sampled).
+ * opt NULL: gc_pack_bound(plan, GC_KIND_DGC).  0 if plan is NULL. */
+uint64_t  gc_dgc_pack_bound(const gc_plan *plan, const gc_dgc_options *opt);
 gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
                   uint8_t *out, uint64_t out_cap, uint64_t *out_bytes,
                   void *ws, size_t ws_bytes, hipStream_t stream);
