@@ -6,14 +6,22 @@
 // Entries of a segment are processed in tiles of 4096.  A run longer than
 // the code can hold is split with escapes; an entry's slot in its block is
 // its rank in the segment plus the escapes emitted before it.  Escapes are
-// rare (a gap of 32767+ unsent elements), so the count pass adds per-segment
-// totals with integer atomics, and the write pass scans escape counts only
-// in segments and tiles that have any.  The count pass reads a tile in the
-// 4-wide lane layout of the dense kernels (one 16-byte load per lane and
-// row) and leaves a record of the tile (segment, entry range, segment
-// geometry), so that a write workgroup starts its data loads after a single
-// round trip; the write pass is lane-strided, so that each wave's 2-byte
-// code stores cover contiguous bytes.
+// rare (a gap of 32767 or 65535 unsent elements), so the stream is laid out
+// first as if there were none, and written in one pass over the entries,
+// which also counts each tile's escapes:
+//   plan     one workgroup: entries, tiles and block offsets with no escapes;
+//            stream and block headers; the stream length
+//   write    one workgroup per tile: codes (and DGC values) at their slots
+//            when the tile has no escape; each tile's escape count, and a
+//            flag when any tile has one
+//   relayout one workgroup, only when flagged: blocks resized with their
+//            escapes, headers and length written again
+//   rewrite  one workgroup per tile, only when flagged: every tile written
+//            with the escapes before it
+// (A separate count pass reading every index before the write measured 51 us
+// of 127 for the two packs of a DeepSpeech step.)  Messages are read in the
+// lane-strided layout (entry i * 256 + t of the tile in thread t), so that
+// each wave's 2-byte code stores cover contiguous bytes.
 #include <algorithm>
 
 #include "gc_internal.hpp"
@@ -23,17 +31,13 @@ namespace gc {
 namespace {
 
 constexpr uint32_t kTile = 4096;
-constexpr int kTileRows = kTile / (4 * kBlock);
 
 struct PackWs {
-    uint32_t *tile_base;  // [nseg + 1] first tile of each segment; [nseg] = tile count
-    uint32_t *tile_esc;   // [max_tiles] escapes per tile
-    uint4 *tile_rec;      // [2 * max_tiles] per tile: {segment, first entry, entries, tile in segment},
-                          //   {segment offset, length, first entry of the segment, 0}
-    uint32_t *seg_esc;    // [nseg] escapes per segment
+    uint4 *srec;          // [nseg] {first entry, entries, E, first tile}
     uint64_t *blk_off;    // [nseg] byte offset of each block
-    uint32_t *seg_E;      // [nseg]
-    uint32_t *overflow;   // [1] set by the layout pass when the stream exceeds out_cap
+    uint32_t *tile_seg;   // [max_tiles] segment of each tile
+    uint32_t *tile_esc;   // [max_tiles] escapes per tile (write pass)
+    uint32_t *flags;      // [0] tiles, [1] the stream exceeds out_cap, [2] some tile has an escape
     size_t max_tiles;
 };
 
@@ -43,13 +47,11 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     size_t tiles = 0;
     for (const auto &s : p->seg) tiles += ceil_div(s.len, kTile);
     w.max_tiles = tiles + 1;
-    w.tile_base = c.take<uint32_t>(p->nseg + 1);
-    w.tile_esc = c.take<uint32_t>(w.max_tiles + 1);
-    w.tile_rec = c.take<uint4>(2 * w.max_tiles);
-    w.seg_esc = c.take<uint32_t>(p->nseg);
+    w.srec = c.take<uint4>(p->nseg);
     w.blk_off = c.take<uint64_t>(p->nseg);
-    w.seg_E = c.take<uint32_t>(p->nseg);
-    w.overflow = c.take<uint32_t>(1);
+    w.tile_seg = c.take<uint32_t>(w.max_tiles);
+    w.tile_esc = c.take<uint32_t>(w.max_tiles);
+    w.flags = c.take<uint32_t>(4);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -108,214 +110,174 @@ __device__ __forceinline__ uint32_t entry_gap(const EntryCtx &x, uint32_t j, uin
 // a 20% slower write pass).
 constexpr int kKeep = 0;
 
-// The tile's entries [j0, j0 + cnt) in the 4-wide layout: cur[r][q] =
-// idx[j0 + 1024 r + 4 t + q] (0 past cnt, from the buffer's range check)
-// and prv0[r] = the entry before the lane's first one of row r (clamped
-// into the tile when that entry is the segment's first, where it is unused,
-// or lies past the tile).  All loads are issued before any is used.
-__device__ __forceinline__ void load_tile(const uint32_t *__restrict__ a, uint32_t first, uint32_t j0,
-                                          uint32_t cnt, uint32_t (&cur)[kTileRows][4],
-                                          uint32_t (&prv0)[kTileRows]) {
-    const BufRsrc r = chunk_buf(reinterpret_cast<const float *>(a + j0), cnt);
-#pragma unroll
-    for (int row = 0; row < kTileRows; ++row) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(row_elem(row) * 4u), 0, kKeep);
-        cur[row][0] = v.x;
-        cur[row][1] = v.y;
-        cur[row][2] = v.z;
-        cur[row][3] = v.w;
-        const uint32_t j = min(j0 + row_elem(row), j0 + cnt);
-        prv0[row] = a[j > first ? j - 1 : first];
-    }
+__device__ __forceinline__ uint64_t block_bytes(uint64_t E, bool dgc) {
+    return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0);
 }
 
-__device__ __forceinline__ uint32_t prev_of(const uint32_t (&cur)[kTileRows][4], const uint32_t (&prv0)[kTileRows],
-                                            int row, int q) {
-    return q == 0 ? prv0[row] : cur[row][q - 1];
+// Headers of block s (at `at`, E codes, cnt entries) and its pad.
+__device__ __forceinline__ void write_block_header(uint8_t *out, uint64_t at, bool dgc, uint32_t len, uint32_t E,
+                                                   uint32_t cnt, float scale) {
+    uint32_t *h = reinterpret_cast<uint32_t *>(out + at);
+    h[0] = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
+    h[1] = len;
+    h[2] = E;
+    h[3] = dgc ? cnt : dev_f2u(scale);
+    if (E & 1u) *reinterpret_cast<uint16_t *>(out + at + 16 + 2ull * E) = 0;
 }
 
-// One workgroup: tile counts per segment -> tile_base.
-__global__ __launch_bounds__(kBlock) void pack_tiles_kernel(PlanDev P, int kind,
-                                                            const uint32_t *__restrict__ seg_off,
-                                                            uint64_t cap, PackWs w) {
-    const int nseg = P.nseg;
-    uint32_t run = 0;
-    for (int r = 0; r < nseg; r += kBlock) {
-        int s = r + threadIdx.x;
-        uint32_t v = 0;
-        if (s < nseg) v = (seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap) + kTile - 1) / kTile;
-        uint32_t tot;
-        uint32_t pre = block_exclusive_scan(v, &tot);
-        if (s < nseg) {
-            w.tile_base[s] = run + pre;
-            w.seg_esc[s] = 0u;
-        }
-        run += tot;
-    }
-    if (threadIdx.x == 0) w.tile_base[nseg] = run;
+__device__ __forceinline__ void write_stream_header(uint8_t *out, int kind, int nseg) {
+    uint32_t *h = reinterpret_cast<uint32_t *>(out);
+    h[0] = magic('G', 'C', 'P', '1');
+    h[1] = static_cast<uint32_t>(kind);
+    h[2] = static_cast<uint32_t>(nseg);
+    h[3] = 0u;
 }
 
-// Segment of tile t: the last s with tile_base[s] <= t.  Workgroups copy the
-// table (and the tile count after it) to LDS once when it fits, so the
-// searches cost no global round trips.
-constexpr int kLdsSegs = 4096;
-
-struct TileTable {
-    const uint32_t *tb;
-    int nseg;
-    __device__ void init(const uint32_t *tile_base, int n, uint32_t *lds) {
-        nseg = n;
-        if (n <= kLdsSegs) {
-            for (int i = threadIdx.x; i <= n; i += kBlock) lds[i] = tile_base[i];
-            __syncthreads();
-            tb = lds;
-        } else {
-            tb = tile_base;
-        }
-    }
-    __device__ uint32_t count() const { return tb[nseg]; }
-    __device__ uint32_t segment(uint32_t t) const {
-        int lo = 0, hi = nseg - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) / 2;
-            if (tb[mid] <= t) lo = mid;
-            else hi = mid - 1;
-        }
-        return static_cast<uint32_t>(lo);
-    }
-};
-
-__global__ __launch_bounds__(kBlock) void pack_count_kernel(PlanDev P, int kind,
-                                                            const uint32_t *__restrict__ idx,
-                                                            const uint32_t *__restrict__ seg_off,
-                                                            uint64_t cap, uint32_t MAX, PackWs w) {
-    __shared__ uint32_t lds[kLdsSegs + 1];
-    TileTable table;
-    table.init(w.tile_base, P.nseg, lds);
-    const uint32_t ntiles = table.count();
-    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t s = table.segment(t);
-        const uint32_t ts = t - table.tb[s];
-        const SegDev sg = P.seg[s];
-        EntryCtx x;
-        x.first = seg_off[s];
-        x.off = static_cast<uint32_t>(sg.off);
-        x.len = sg.len;
-        const uint32_t end = x.first + seg_entries(seg_off, s, seg_max_entries(sg, kind), cap);
-        const uint32_t j0 = x.first + ts * kTile;
-        const uint32_t cnt = min(end - j0, kTile);
-        uint32_t cur[kTileRows][4], prv0[kTileRows];
-        load_tile(idx, x.first, j0, cnt, cur, prv0);
-        uint32_t esc = 0;
-#pragma unroll
-        for (int row = 0; row < kTileRows; ++row)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t e = row_elem(row) + q;
-                if (e < cnt) esc += entry_gap(x, j0 + e, cur[row][q], prev_of(cur, prv0, row, q)) / MAX;
-            }
-        uint32_t tot;
-        (void)block_exclusive_scan(esc, &tot);
-        if (threadIdx.x == 0) {
-            w.tile_esc[t] = tot;
-            w.tile_rec[2 * size_t(t)] = make_uint4(s, j0, cnt, ts);
-            w.tile_rec[2 * size_t(t) + 1] =
-                make_uint4(x.off, x.len, x.first, 0u);
-            if (tot) atomicAdd(&w.seg_esc[s], tot);
-        }
-    }
-}
-
-// One workgroup: size every block from its entries and escapes; when the
-// stream fits out_cap, write the stream header, block headers and pads;
-// always the stream length, and the overflow flag the write pass reads.
-__global__ __launch_bounds__(kBlock) void pack_layout_kernel(PlanDev P, int kind, uint64_t cap, uint32_t MAX,
-                                                             const uint32_t *__restrict__ seg_off,
-                                                             const float *__restrict__ seg_scale,
-                                                             uint8_t *__restrict__ out, uint64_t out_cap,
-                                                             uint64_t *__restrict__ out_bytes, PackWs w) {
-    uint64_t byte_run = 16;
+// Plan pass, one workgroup: per segment its entries (clamped as above), its
+// tiles and, with E = entries, its block's offset; the tile -> segment table;
+// when the stream fits out_cap, every header; always the stream length and
+// the flags the later passes read.
+__global__ __launch_bounds__(kBlock) void pack_plan_kernel(PlanDev P, int kind, uint64_t cap,
+                                                           const uint32_t *__restrict__ seg_off,
+                                                           const float *__restrict__ seg_scale,
+                                                           uint8_t *__restrict__ out, uint64_t out_cap,
+                                                           uint64_t *__restrict__ out_bytes, PackWs w) {
     const bool dgc = kind == GC_KIND_DGC;
+    __shared__ uint32_t tstart[kBlock + 1];
+    uint64_t byte_run = 16;
+    uint32_t tile_run = 0;
     for (int r = 0; r < P.nseg; r += kBlock) {
-        int s = r + threadIdx.x;
-        uint64_t sz = 0;
-        uint32_t E = 0;
+        const int s = r + int(threadIdx.x);
+        uint32_t cnt = 0, first = 0;
         if (s < P.nseg) {
-            const SegDev sg = P.seg[s];
-            const uint32_t maxe = seg_max_entries(sg, kind);
-            const uint32_t cnt = seg_entries(seg_off, s, maxe, cap);
-            uint32_t esc = w.seg_esc[s];
-            // never more codes than a segment of this length can need
-            uint64_t cap_e = uint64_t(maxe) + sg.len / MAX + 1;
-            uint64_t e64 = uint64_t(cnt) + esc;
-            E = static_cast<uint32_t>(e64 < cap_e ? e64 : cap_e);
-            sz = 16 + 2ull * E + 2ull * (E & 1u) + (dgc ? 4ull * E : 0ull);
+            cnt = seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap);
+            first = seg_off[s];
         }
-        uint64_t tot;
-        uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
+        const uint32_t nt = (cnt + kTile - 1) / kTile;
+        uint64_t btot;
+        uint32_t ttot;
+        const uint64_t bpre = block_exclusive_scan<uint64_t>(block_bytes(cnt, dgc) * (s < P.nseg), &btot);
+        const uint32_t tpre = block_exclusive_scan<uint32_t>(nt, &ttot);
         if (s < P.nseg) {
-            w.blk_off[s] = byte_run + pre;
-            w.seg_E[s] = E;
+            w.srec[s] = make_uint4(first, cnt, cnt, tile_run + tpre);
+            w.blk_off[s] = byte_run + bpre;
         }
-        byte_run += tot;
+        // the tile -> segment table of these segments' ttot tiles: thread t
+        // fills an equal share, from the segment of its first tile on
+        tstart[threadIdx.x] = tpre;
+        if (threadIdx.x == 0) tstart[kBlock] = ttot;
+        __syncthreads();
+        const uint32_t per = (ttot + kBlock - 1) / kBlock;
+        const uint32_t q0 = threadIdx.x * per, q1 = min(q0 + per, ttot);
+        if (q0 < q1) {
+            int lo = 0, hi = kBlock - 1;  // the last segment starting at or before q0
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (tstart[mid] <= q0) lo = mid;
+                else hi = mid - 1;
+            }
+            for (uint32_t q = q0; q < q1; ++q) {
+                while (tstart[lo + 1] <= q) ++lo;
+                w.tile_seg[tile_run + q] = static_cast<uint32_t>(r + lo);
+            }
+        }
+        __syncthreads();
+        byte_run += btot;
+        tile_run += ttot;
     }
     const bool fits = byte_run <= out_cap;
-    __syncthreads();
     if (fits) {
         for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
-            const uint64_t at = w.blk_off[s];
-            const uint32_t E = w.seg_E[s];
-            uint32_t *h = reinterpret_cast<uint32_t *>(out + at);
-            h[0] = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
-            h[1] = P.seg[s].len;
-            h[2] = E;
-            h[3] = dgc ? seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap) : dev_f2u(seg_scale[s]);
-            if (E & 1u) *reinterpret_cast<uint16_t *>(out + at + 16 + 2ull * E) = 0;
+            const uint32_t cnt = seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap);
+            // the block offset again, from this thread's own write above
+            write_block_header(out, w.blk_off[s], dgc, P.seg[s].len, cnt, cnt, dgc ? 0.0f : seg_scale[s]);
         }
     }
     if (threadIdx.x == 0) {
-        if (fits) {
-            uint32_t *h = reinterpret_cast<uint32_t *>(out);
-            h[0] = magic('G', 'C', 'P', '1');
-            h[1] = static_cast<uint32_t>(kind);
-            h[2] = static_cast<uint32_t>(P.nseg);
-            h[3] = 0u;
-        }
+        if (fits) write_stream_header(out, kind, P.nseg);
         *out_bytes = byte_run;
-        *w.overflow = fits ? 0u : 1u;
+        w.flags[0] = tile_run;
+        w.flags[1] = fits ? 0u : 1u;
+        w.flags[2] = 0u;
     }
 }
 
-// Write pass.  Entries are lane-strided here (entry i * 256 + t of the tile
-// in thread t), so that each 2-byte code store of a wave covers 128
-// contiguous bytes.  The loads of a tile are issued before its escape count
-// is known; a tile with escapes (rare) drops them and walks 16 contiguous
-// entries per thread in two light passes (escapes, then slots), reloading
-// what it needs, so that its registers do not add to the common path's.
-constexpr uint32_t kPerThread = kTile / kBlock;
+// Relayout, by one workgroup, when some tile has escapes: each segment's
+// escapes (the sum over its tiles), blocks resized, headers, stream length
+// and overflow written again.
+__device__ void pack_relayout(const PlanDev &P, int kind, uint32_t MAX, const float *__restrict__ seg_scale,
+                              uint8_t *__restrict__ out, uint64_t out_cap, uint64_t *__restrict__ out_bytes,
+                              const PackWs &w) {
+    const bool dgc = kind == GC_KIND_DGC;
+    const uint32_t ntiles = w.flags[0];
+    uint64_t byte_run = 16;
+    for (int r = 0; r < P.nseg; r += kBlock) {
+        const int s = r + int(threadIdx.x);
+        uint64_t sz = 0;
+        if (s < P.nseg) {
+            const uint4 sr = w.srec[s];
+            const uint32_t t1 = s + 1 < P.nseg ? w.srec[s + 1].w : ntiles;
+            uint64_t esc = 0;
+            for (uint32_t u = sr.w; u < t1; ++u) esc += w.tile_esc[u];
+            // never more codes than a segment of this length can need
+            const uint64_t cap_e = uint64_t(P.seg[s].len) + P.seg[s].len / MAX + 1;
+            const uint64_t e64 = uint64_t(sr.y) + esc;
+            const uint32_t E = static_cast<uint32_t>(e64 < cap_e ? e64 : cap_e);
+            w.srec[s].z = E;
+            sz = block_bytes(E, dgc);
+        }
+        uint64_t tot;
+        const uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
+        if (s < P.nseg) w.blk_off[s] = byte_run + pre;
+        byte_run += tot;
+    }
+    const bool fits = byte_run <= out_cap;
+    if (fits)
+        for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
+            const uint4 sr = w.srec[s];
+            write_block_header(out, w.blk_off[s], dgc, P.seg[s].len, sr.z, sr.y, dgc ? 0.0f : seg_scale[s]);
+        }
+    if (threadIdx.x == 0) {
+        *out_bytes = byte_run;
+        w.flags[1] = fits ? 0u : 1u;
+    }
+}
 
 // A wave-uniform value moved to a scalar register (the tile geometry is read
 // with vector loads; every lane holds the same value).
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, size_t max_tiles,
-                                                            const uint32_t *__restrict__ idx,
+constexpr uint32_t kPerThread = kTile / kBlock;
+
+// Write pass (kRedo false) and rewrite pass (kRedo true).  A tile's loads
+// are issued after one round trip for its segment record.  The write pass
+// writes a tile only when it has no escape, with slot = rank in the
+// segment; it records the tile's escapes and flags the stream when there
+// are any.  The rewrite pass (run only when flagged, after the relayout)
+// writes every tile: one without escapes at rank + the escapes before it; a
+// tile with escapes walks 16 contiguous entries per thread in two light
+// passes (escapes, then slots), reloading what it needs, so that its
+// registers do not add to the common path's.
+template <bool kRedo>
+__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, const uint32_t *__restrict__ idx,
                                                             const float *__restrict__ val, uint32_t MAX,
                                                             uint8_t *__restrict__ out, PackWs w) {
     const bool dgc = kind == GC_KIND_DGC;
-    if (*w.overflow) return;  // the stream does not fit out_cap: nothing is written
-    for (uint32_t t = blockIdx.x; t < max_tiles; t += gridDim.x) {
-        // the tile count and the tile's record in one round trip (records
-        // past the count are never used)
-        const uint32_t ntiles = uni(w.tile_base[P.nseg]);
-        const uint4 ra = w.tile_rec[2 * size_t(t)], rb = w.tile_rec[2 * size_t(t) + 1];
-        if (t >= ntiles) break;
-        const uint32_t s = uni(ra.x), j0 = uni(ra.y), cnt = uni(ra.z);
+    if (w.flags[1]) return;  // the stream does not fit out_cap: nothing is written
+    if (kRedo && !w.flags[2]) return;
+    const uint32_t ntiles = uni(w.flags[0]);
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint32_t s = uni(w.tile_seg[t]);
+        const uint4 sr = w.srec[s];
+        const SegDev sg = P.seg[s];
+        const uint64_t boff = w.blk_off[s];
         EntryCtx x;
-        x.off = uni(rb.x);
-        x.len = uni(rb.y);
-        x.first = uni(rb.z);
-        const uint32_t tile0 = t - uni(ra.w);
+        x.first = uni(sr.x);
+        x.off = static_cast<uint32_t>(sg.off);
+        x.len = sg.len;
+        const uint32_t E = uni(sr.z), tile0 = uni(sr.w);
+        const uint32_t j0 = x.first + (t - tile0) * kTile;
+        const uint32_t cnt = uni(min(sr.y - (t - tile0) * kTile, kTile));
         // buffer resources over the tile (32-bit offsets; loads past the
         // range return 0): entries, values, and the entries shifted back by
         // one (from the entry before the tile unless the tile is the
@@ -334,20 +296,9 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
             prv[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, static_cast<int>(4 * ep), 0, kKeep);
             v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * e), 0, kKeep));
         }
-        const uint32_t E = w.seg_E[s];
-        const uint32_t tile_esc = w.tile_esc[t], seg_esc = w.seg_esc[s];
-        uint8_t *blk = out + w.blk_off[s];
+        uint8_t *blk = out + boff;
         uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
         float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
-        // escapes emitted before this tile in its segment
-        uint32_t esc_base = 0;
-        if (seg_esc != 0) {
-            uint32_t part = 0;
-            for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
-            uint32_t all;
-            (void)block_exclusive_scan(part, &all);
-            esc_base = all;
-        }
         auto put = [&](uint32_t slot, uint32_t gap, float value) {
             // the packed stream is not read again here: non-temporal stores
             if (dgc) {
@@ -358,14 +309,40 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
                 __builtin_nontemporal_store(static_cast<uint16_t>(sign | gap), runs + slot);
             }
         };
-        if (tile_esc == 0) {
-            // no escape in this tile: entry j goes to slot (j - first) + esc_base
+        uint32_t gap[kPerThread], mine = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < kPerThread; ++i) {
+            const uint32_t e = i * kBlock + threadIdx.x;
+            gap[i] = e < cnt ? entry_gap(x, j0 + e, cur[i], prv[i]) : 0u;
+            mine += gap[i] / MAX;
+        }
+        if (!kRedo) {
+            uint32_t tile_esc;
+            (void)block_exclusive_scan(mine, &tile_esc);
+            if (threadIdx.x == 0) {
+                w.tile_esc[t] = tile_esc;
+                if (tile_esc) atomicOr(&w.flags[2], 1u);
+            }
+            if (tile_esc) continue;  // written by the rewrite pass
+#pragma unroll
+            for (uint32_t i = 0; i < kPerThread; ++i) {
+                const uint32_t e = i * kBlock + threadIdx.x;
+                const uint32_t slot = j0 + e - x.first;
+                if (e < cnt && slot < E) put(slot, gap[i], v[i]);  // slot >= E only for malformed messages
+            }
+            continue;
+        }
+        // rewrite: the escapes of the segment's tiles before this one
+        uint32_t part = 0;
+        for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
+        uint32_t esc_base;
+        (void)block_exclusive_scan(part, &esc_base);
+        if (w.tile_esc[t] == 0) {
 #pragma unroll
             for (uint32_t i = 0; i < kPerThread; ++i) {
                 const uint32_t e = i * kBlock + threadIdx.x;
                 const uint32_t slot = (j0 + e - x.first) + esc_base;
-                if (e >= cnt || slot >= E) continue;  // slot >= E only for malformed messages
-                put(slot, entry_gap(x, j0 + e, cur[i], prv[i]), v[i]);
+                if (e < cnt && slot < E) put(slot, gap[i], v[i]);
             }
             continue;
         }
@@ -375,11 +352,11 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
             const uint32_t j = j0 + e;
             return entry_gap(x, j, idx[j], idx[j > x.first ? j - 1 : j]);
         };
-        uint32_t mine = 0;
+        uint32_t own = 0;
 #pragma unroll 1
-        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) mine += gap_at(e) / MAX;
+        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) own += gap_at(e) / MAX;
         uint32_t tot;
-        uint32_t before = esc_base + block_exclusive_scan(mine, &tot);
+        uint32_t before = esc_base + block_exclusive_scan(own, &tot);
 #pragma unroll 1
         for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) {
             uint32_t slot = (j0 + e - x.first) + before;
@@ -396,6 +373,17 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
             put(slot, g, val[j0 + e]);
         }
     }
+}
+
+// Relayout pass, one workgroup, only when some tile has escapes.  (Having
+// the last write workgroup do it instead cost each of them a device-scope
+// fence and an atomic on one counter: the write pass ran 10x slower.)
+__global__ __launch_bounds__(kBlock) void pack_relayout_kernel(PlanDev P, int kind, uint32_t MAX,
+                                                               const float *__restrict__ seg_scale,
+                                                               uint8_t *__restrict__ out, uint64_t out_cap,
+                                                               uint64_t *__restrict__ out_bytes, PackWs w) {
+    if (w.flags[1] || !w.flags[2]) return;
+    pack_relayout(P, kind, MAX, seg_scale, out, out_cap, out_bytes, w);
 }
 
 }  // namespace
@@ -468,12 +456,12 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     // count exit at once
     constexpr size_t kTileGrid = 8192;
     const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kTileGrid));
-    GC_LAUNCH("pack_tiles", stream, pack_tiles_kernel<<<1, kBlock, 0, stream>>>(P, kind, in->seg_off, cap, w));
-    GC_LAUNCH("pack_count", stream, pack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->seg_off, cap, MAX, w));
-    GC_LAUNCH("pack_layout", stream, pack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, MAX, in->seg_off, in->seg_scale, out,
-                                                 out_cap, out_bytes, w));
-    GC_LAUNCH("pack_write", stream, pack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, w.max_tiles, in->idx, in->val, MAX,
-                                                   out, w));
+    GC_LAUNCH("pack_plan", stream, pack_plan_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale, out,
+                                                                             out_cap, out_bytes, w));
+    GC_LAUNCH("pack_write", stream, pack_write_kernel<false><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
+    GC_LAUNCH("pack_relayout", stream, pack_relayout_kernel<<<1, kBlock, 0, stream>>>(P, kind, MAX, in->seg_scale, out, out_cap,
+                                                                                     out_bytes, w));
+    GC_LAUNCH("pack_rewrite", stream, pack_write_kernel<true><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_pack launch");
     return GC_OK;

@@ -353,8 +353,10 @@ gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V
  *              segment (a per-call density, or the sampled selection's
  *              budget) may need up to gc_dgc_pack_bound(plan, opt) bytes.
  *   out_bytes: device u64, receives the stream length.  When it exceeds
- *              out_cap the stream did not fit: nothing was written to out,
- *              and *out_bytes is the size to pack it into.
+ *              out_cap the stream did not fit: out does not hold it (no
+ *              byte past out_cap is written), and the message needs a
+ *              buffer of at least *out_bytes bytes (the sizes above always
+ *              suffice).
  * Errors: GC_EINVAL (bad kind / null), GC_ECAPACITY (out_cap or ws too small).
  */
 #define GC_KIND_DGC      1
