@@ -119,6 +119,10 @@ gc_status plan_device(const gc_plan *plan, PlanDev *out);
 // GC_EINVAL otherwise, without allocating.
 gc_status plan_device_resident(const gc_plan *plan, PlanDev *out);
 
+// Workgroups of kBlock threads of `kernel` that the current device holds at
+// once (its occupancy times the compute units), cached per device and kernel.
+unsigned resident_blocks(const void *kernel);
+
 // Whether exact DGC selection at these densities takes the four-launch path
 // (knum = kden = 0: the plan's own k).
 bool dgc_exact_fast(const gc_plan *plan, uint32_t knum, uint32_t kden);
@@ -199,6 +203,7 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
 // slower: six dependent LDS round trips.)
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+constexpr int kDppWaveShr1 = 0x138;  // lane l reads lane l - 1 across the whole wave
 template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, kRowMask, 0xF, false));

@@ -8,16 +8,24 @@
 // its rank in the segment plus the escapes emitted before it.  Escapes are
 // rare (a gap of 32767 or 65535 unsent elements), so the stream is laid out
 // first as if there were none, and written in one pass over the entries,
-// which also counts each tile's escapes:
+// which also counts each tile's escapes.  Plans of at most 512 segments take
+// two passes:
+//   main     every workgroup lays the stream out (escape-free) from the
+//            message's segment counts in LDS; workgroup 0 writes the headers
+//            and the length; every tile records its escapes and, when it has
+//            none, writes its codes (and DGC values) at their slots
+//   fix      returns unless some tile has escapes; otherwise lays the stream
+//            out again with each segment's escapes and writes every tile
+//            with the escapes before it
+// Plans of more segments (a layout per workgroup would cost each of them a
+// pass over every segment) take four:
 //   plan     one workgroup: entries, tiles and block offsets with no escapes;
 //            stream and block headers; the stream length
-//   write    one workgroup per tile: codes (and DGC values) at their slots
-//            when the tile has no escape; each tile's escape count, and a
-//            flag when any tile has one
+//   write    one workgroup per tile, as in main, from the plan's tables; a
+//            flag when any tile has an escape
 //   relayout one workgroup, only when flagged: blocks resized with their
 //            escapes, headers and length written again
-//   rewrite  one workgroup per tile, only when flagged: every tile written
-//            with the escapes before it
+//   rewrite  one workgroup per tile, only when flagged, as in fix
 // (A separate count pass reading every index before the write measured 51 us
 // of 127 for the two packs of a DeepSpeech step.)  Messages are read in the
 // lane-strided layout (entry i * 256 + t of the tile in thread t), so that
@@ -37,6 +45,7 @@ struct PackWs {
     uint64_t *blk_off;    // [nseg] byte offset of each block
     uint32_t *tile_seg;   // [max_tiles] segment of each tile
     uint32_t *tile_esc;   // [max_tiles] escapes per tile (write pass)
+    uint8_t *tile_any;    // [max_tiles] 1 when the tile has escapes (write pass)
     uint32_t *flags;      // [0] tiles, [1] the stream exceeds out_cap, [2] some tile has an escape
     size_t max_tiles;
 };
@@ -51,6 +60,7 @@ PackWs pack_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.blk_off = c.take<uint64_t>(p->nseg);
     w.tile_seg = c.take<uint32_t>(w.max_tiles);
     w.tile_esc = c.take<uint32_t>(w.max_tiles);
+    w.tile_any = c.take<uint8_t>(w.max_tiles);
     w.flags = c.take<uint32_t>(4);
     if (bytes) *bytes = c.used + 256;
     return w;
@@ -249,15 +259,185 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_re
 
 constexpr uint32_t kPerThread = kTile / kBlock;
 
-// Write pass (kRedo false) and rewrite pass (kRedo true).  A tile's loads
-// are issued after one round trip for its segment record.  The write pass
-// writes a tile only when it has no escape, with slot = rank in the
-// segment; it records the tile's escapes and flags the stream when there
-// are any.  The rewrite pass (run only when flagged, after the relayout)
-// writes every tile: one without escapes at rank + the escapes before it; a
-// tile with escapes walks 16 contiguous entries per thread in two light
-// passes (escapes, then slots), reloading what it needs, so that its
-// registers do not add to the common path's.
+// Sum over the workgroup of one value per thread, in every thread.
+__device__ __forceinline__ uint32_t block_total(uint32_t v) {
+    __shared__ uint32_t wsum[kWaves];
+    const uint32_t x = wave_total(v);
+    if (lane_id() == 0) wsum[wave_id()] = x;
+    __syncthreads();
+    uint32_t all = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) all += wsum[i];
+    return all;
+}
+
+// Tile t of segment s: entries [j0, j0 + cnt) of the message, the segment's
+// tiles starting at tile0, its block of E codes at byte boff.
+struct TileGeom {
+    EntryCtx x;
+    uint32_t E, j0, cnt, tile0;
+    uint64_t boff;
+};
+
+// The tile's loads in the lane-strided layout (entry i * kBlock + t of the
+// tile in thread t) and each entry's gap.  An entry's predecessor is the one
+// in the lane before (a wave shift); lane 0 loads its own, from the entry
+// before the tile unless the tile is the segment's first (where entry 0's
+// predecessor is unused).  Buffer resources cover the tile: loads past it
+// return 0.
+__device__ __forceinline__ void tile_load(const TileGeom &g, const uint32_t *__restrict__ idx,
+                                          const float *__restrict__ val, uint32_t (&gap)[kPerThread],
+                                          float (&v)[kPerThread]) {
+    const uint32_t d = uni(g.j0 > g.x.first ? 1u : 0u);
+    const BufRsrc ri = chunk_buf(reinterpret_cast<const float *>(idx + g.j0), g.cnt);
+    const BufRsrc rp = chunk_buf(reinterpret_cast<const float *>(idx + g.j0 - d), g.cnt + d);
+    const BufRsrc rv = chunk_buf(val + g.j0, g.cnt);
+    uint32_t cur[kPerThread], p0[kPerThread];
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t e = i * kBlock + threadIdx.x;
+        cur[i] = __builtin_amdgcn_raw_buffer_load_b32(ri, static_cast<int>(4 * e), 0, kKeep);
+        v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * e), 0, kKeep));
+        p0[i] = 0u;
+    }
+    if (lane_id() == 0) {
+#pragma unroll
+        for (uint32_t i = 0; i < kPerThread; ++i) {
+            const uint32_t e = i * kBlock + threadIdx.x;
+            const uint32_t ep = e + d > 0 ? e + d - 1 : 0u;
+            p0[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, static_cast<int>(4 * ep), 0, kKeep);
+        }
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t e = i * kBlock + threadIdx.x;
+        // lane l takes lane l - 1's entry; lane 0 keeps its loaded one
+        const uint32_t prv = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(static_cast<int>(p0[i]), static_cast<int>(cur[i]), kDppWaveShr1, 0xF, 0xF, false));
+        gap[i] = e < g.cnt ? entry_gap(g.x, g.j0 + e, cur[i], prv) : 0u;
+    }
+}
+
+// One code (and DGC value) at its slot of the block.  The packed stream is
+// not read again here: non-temporal stores.
+__device__ __forceinline__ void put_code(bool dgc, uint16_t *runs, float *vals, uint32_t slot, uint32_t gap,
+                                         float value) {
+    if (dgc) {
+        __builtin_nontemporal_store(static_cast<uint16_t>(gap), runs + slot);
+        __builtin_nontemporal_store(value, vals + slot);
+    } else {
+        const uint16_t sign = (dev_f2u(value) >> 31) ? 0x8000u : 0u;
+        __builtin_nontemporal_store(static_cast<uint16_t>(sign | gap), runs + slot);
+    }
+}
+
+__device__ __forceinline__ uint16_t *block_runs(uint8_t *out, const TileGeom &g) {
+    return reinterpret_cast<uint16_t *>(out + g.boff + 16);
+}
+__device__ __forceinline__ float *block_vals(uint8_t *out, const TileGeom &g) {
+    return reinterpret_cast<float *>(out + g.boff + 16 + 2ull * g.E + 2ull * (g.E & 1u));
+}
+
+// First pass over a tile: its escapes to tile_esc[t]; a tile without any is
+// written at slot = rank in the segment.  Returns the tile's escapes.
+__device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bool dgc,
+                                               const uint32_t *__restrict__ idx, const float *__restrict__ val,
+                                               uint32_t MAX, uint8_t *__restrict__ out, const PackWs &w) {
+    uint32_t gap[kPerThread];
+    float v[kPerThread];
+    tile_load(g, idx, val, gap, v);
+    uint32_t mine = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) mine += gap[i] / MAX;
+    const uint32_t esc = block_total(mine);
+    if (threadIdx.x == 0) {
+        w.tile_esc[t] = esc;
+        w.tile_any[t] = esc ? 1u : 0u;
+    }
+    if (esc) return esc;  // written by the rewrite pass
+    uint16_t *runs = block_runs(out, g);
+    float *vals = block_vals(out, g);
+#pragma unroll
+    for (uint32_t i = 0; i < kPerThread; ++i) {
+        const uint32_t e = i * kBlock + threadIdx.x;
+        const uint32_t slot = g.j0 + e - g.x.first;
+        if (e < g.cnt && slot < g.E) put_code(dgc, runs, vals, slot, gap[i], v[i]);  // slot >= E only for malformed messages
+    }
+    return 0;
+}
+
+// Rewrite pass over a tile, after the relayout: a tile without escapes at
+// rank + the escapes of the segment's earlier tiles; a tile with escapes
+// walks 16 contiguous entries per thread in two light passes (escapes, then
+// slots), reloading what it needs, so that its registers do not add to the
+// common path's.
+__device__ __forceinline__ void tile_rewrite(const TileGeom &g, uint32_t t, bool dgc,
+                                             const uint32_t *__restrict__ idx, const float *__restrict__ val,
+                                             uint32_t MAX, uint8_t *__restrict__ out, const PackWs &w) {
+    uint32_t part = 0;
+#pragma unroll 4
+    for (uint32_t u = g.tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
+    const uint32_t esc_base = block_total(part);
+    uint16_t *runs = block_runs(out, g);
+    float *vals = block_vals(out, g);
+    if (uni(w.tile_esc[t]) == 0) {
+        uint32_t gap[kPerThread];
+        float v[kPerThread];
+        tile_load(g, idx, val, gap, v);
+#pragma unroll
+        for (uint32_t i = 0; i < kPerThread; ++i) {
+            const uint32_t e = i * kBlock + threadIdx.x;
+            const uint32_t slot = (g.j0 + e - g.x.first) + esc_base;
+            if (e < g.cnt && slot < g.E) put_code(dgc, runs, vals, slot, gap[i], v[i]);
+        }
+        return;
+    }
+    const uint32_t e0 = threadIdx.x * kPerThread;
+    auto gap_at = [&](uint32_t e) {
+        const uint32_t j = g.j0 + e;
+        return entry_gap(g.x, j, idx[j], idx[j > g.x.first ? j - 1 : j]);
+    };
+    uint32_t own = 0;
+#pragma unroll 1
+    for (uint32_t e = e0; e < min(e0 + kPerThread, g.cnt); ++e) own += gap_at(e) / MAX;
+    uint32_t tot;
+    uint32_t before = esc_base + block_exclusive_scan(own, &tot);
+#pragma unroll 1
+    for (uint32_t e = e0; e < min(e0 + kPerThread, g.cnt); ++e) {
+        uint32_t slot = (g.j0 + e - g.x.first) + before;
+        uint32_t gp = gap_at(e);
+        const uint32_t esc = gp / MAX;
+        for (uint32_t z = 0; z < esc && slot < g.E; ++z) {
+            runs[slot] = static_cast<uint16_t>(MAX);
+            if (dgc) vals[slot] = 0.0f;
+            ++slot;
+            gp -= MAX;
+        }
+        before += esc;
+        if (slot >= g.E) continue;  // only for malformed messages
+        put_code(dgc, runs, vals, slot, gp, val[g.j0 + e]);
+    }
+}
+
+// ------------------------------------------------- plans of many segments
+// Geometry of tile t from the plan pass's tables.
+__device__ __forceinline__ TileGeom table_tile(const PlanDev &P, const PackWs &w, uint32_t t) {
+    const uint32_t s = uni(w.tile_seg[t]);
+    const uint4 sr = w.srec[s];
+    const SegDev sg = P.seg[s];
+    TileGeom g;
+    g.x.first = uni(sr.x);
+    g.x.off = static_cast<uint32_t>(sg.off);
+    g.x.len = sg.len;
+    g.E = uni(sr.z);
+    g.tile0 = uni(sr.w);
+    g.j0 = g.x.first + (t - g.tile0) * kTile;
+    g.cnt = uni(min(sr.y - (t - g.tile0) * kTile, kTile));
+    g.boff = w.blk_off[s];
+    return g;
+}
+
+// Write pass (kRedo false) and rewrite pass (kRedo true) after the plan pass.
 template <bool kRedo>
 __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, const uint32_t *__restrict__ idx,
                                                             const float *__restrict__ val, uint32_t MAX,
@@ -267,111 +447,13 @@ __global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind,
     if (kRedo && !w.flags[2]) return;
     const uint32_t ntiles = uni(w.flags[0]);
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t s = uni(w.tile_seg[t]);
-        const uint4 sr = w.srec[s];
-        const SegDev sg = P.seg[s];
-        const uint64_t boff = w.blk_off[s];
-        EntryCtx x;
-        x.first = uni(sr.x);
-        x.off = static_cast<uint32_t>(sg.off);
-        x.len = sg.len;
-        const uint32_t E = uni(sr.z), tile0 = uni(sr.w);
-        const uint32_t j0 = x.first + (t - tile0) * kTile;
-        const uint32_t cnt = uni(min(sr.y - (t - tile0) * kTile, kTile));
-        // buffer resources over the tile (32-bit offsets; loads past the
-        // range return 0): entries, values, and the entries shifted back by
-        // one (from the entry before the tile unless the tile is the
-        // segment's first, where entry 0's predecessor is unused)
-        const uint32_t d = uni(j0 > x.first ? 1u : 0u);
-        const BufRsrc ri = chunk_buf(reinterpret_cast<const float *>(idx + j0), cnt);
-        const BufRsrc rp = chunk_buf(reinterpret_cast<const float *>(idx + j0 - d), cnt + d);
-        const BufRsrc rv = chunk_buf(val + j0, cnt);
-        uint32_t cur[kPerThread], prv[kPerThread];
-        float v[kPerThread];
-#pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            const uint32_t e = i * kBlock + threadIdx.x;
-            const uint32_t ep = e + d > 0 ? e + d - 1 : 0u;
-            cur[i] = __builtin_amdgcn_raw_buffer_load_b32(ri, static_cast<int>(4 * e), 0, kKeep);
-            prv[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, static_cast<int>(4 * ep), 0, kKeep);
-            v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * e), 0, kKeep));
+        const TileGeom g = table_tile(P, w, t);
+        if (kRedo) {
+            tile_rewrite(g, t, dgc, idx, val, MAX, out, w);
+        } else if (tile_write(g, t, dgc, idx, val, MAX, out, w) && threadIdx.x == 0) {
+            atomicOr(&w.flags[2], 1u);
         }
-        uint8_t *blk = out + boff;
-        uint16_t *runs = reinterpret_cast<uint16_t *>(blk + 16);
-        float *vals = reinterpret_cast<float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
-        auto put = [&](uint32_t slot, uint32_t gap, float value) {
-            // the packed stream is not read again here: non-temporal stores
-            if (dgc) {
-                __builtin_nontemporal_store(static_cast<uint16_t>(gap), runs + slot);
-                __builtin_nontemporal_store(value, vals + slot);
-            } else {
-                const uint16_t sign = (dev_f2u(value) >> 31) ? 0x8000u : 0u;
-                __builtin_nontemporal_store(static_cast<uint16_t>(sign | gap), runs + slot);
-            }
-        };
-        uint32_t gap[kPerThread], mine = 0;
-#pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            const uint32_t e = i * kBlock + threadIdx.x;
-            gap[i] = e < cnt ? entry_gap(x, j0 + e, cur[i], prv[i]) : 0u;
-            mine += gap[i] / MAX;
-        }
-        if (!kRedo) {
-            uint32_t tile_esc;
-            (void)block_exclusive_scan(mine, &tile_esc);
-            if (threadIdx.x == 0) {
-                w.tile_esc[t] = tile_esc;
-                if (tile_esc) atomicOr(&w.flags[2], 1u);
-            }
-            if (tile_esc) continue;  // written by the rewrite pass
-#pragma unroll
-            for (uint32_t i = 0; i < kPerThread; ++i) {
-                const uint32_t e = i * kBlock + threadIdx.x;
-                const uint32_t slot = j0 + e - x.first;
-                if (e < cnt && slot < E) put(slot, gap[i], v[i]);  // slot >= E only for malformed messages
-            }
-            continue;
-        }
-        // rewrite: the escapes of the segment's tiles before this one
-        uint32_t part = 0;
-        for (uint32_t u = tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
-        uint32_t esc_base;
-        (void)block_exclusive_scan(part, &esc_base);
-        if (w.tile_esc[t] == 0) {
-#pragma unroll
-            for (uint32_t i = 0; i < kPerThread; ++i) {
-                const uint32_t e = i * kBlock + threadIdx.x;
-                const uint32_t slot = (j0 + e - x.first) + esc_base;
-                if (e < cnt && slot < E) put(slot, gap[i], v[i]);
-            }
-            continue;
-        }
-        // tile with escapes: thread t takes entries [16 t, 16 t + 16) of the tile
-        const uint32_t e0 = threadIdx.x * kPerThread;
-        auto gap_at = [&](uint32_t e) {
-            const uint32_t j = j0 + e;
-            return entry_gap(x, j, idx[j], idx[j > x.first ? j - 1 : j]);
-        };
-        uint32_t own = 0;
-#pragma unroll 1
-        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) own += gap_at(e) / MAX;
-        uint32_t tot;
-        uint32_t before = esc_base + block_exclusive_scan(own, &tot);
-#pragma unroll 1
-        for (uint32_t e = e0; e < min(e0 + kPerThread, cnt); ++e) {
-            uint32_t slot = (j0 + e - x.first) + before;
-            uint32_t g = gap_at(e);
-            const uint32_t esc = g / MAX;
-            for (uint32_t z = 0; z < esc && slot < E; ++z) {
-                runs[slot] = static_cast<uint16_t>(MAX);
-                if (dgc) vals[slot] = 0.0f;
-                ++slot;
-                g -= MAX;
-            }
-            before += esc;
-            if (slot >= E) continue;  // only for malformed messages
-            put(slot, g, val[j0 + e]);
-        }
+        __syncthreads();
     }
 }
 
@@ -384,6 +466,200 @@ __global__ __launch_bounds__(kBlock) void pack_relayout_kernel(PlanDev P, int ki
                                                                uint64_t *__restrict__ out_bytes, PackWs w) {
     if (w.flags[1] || !w.flags[2]) return;
     pack_relayout(P, kind, MAX, seg_scale, out, out_cap, out_bytes, w);
+}
+
+// ------------------------------------------------- plans of few segments
+// Every workgroup lays the stream out itself (escape-free) from the message
+// counts, in LDS, so that no plan pass runs before the write.
+constexpr int kFuseSegs = 512;
+
+struct FuseLds {
+    uint32_t first[kFuseSegs], cnt[kFuseSegs], off[kFuseSegs], len[kFuseSegs];
+    uint32_t tile0[kFuseSegs + 1];
+    uint64_t boff[kFuseSegs];
+    uint32_t cur;  // segment of the current tile
+};
+
+// Per segment its first entry, entries (clamped as in the plan pass),
+// offset, length, first tile and block offset; returns the stream length,
+// and the tile count in *ntiles.
+__device__ uint64_t fused_layout(const PlanDev &P, bool dgc, uint64_t cap, const uint32_t *__restrict__ seg_off,
+                                 FuseLds &L, uint32_t *ntiles) {
+    uint64_t byte_run = 16;
+    uint32_t tile_run = 0;
+    for (int r = 0; r < P.nseg; r += kBlock) {
+        const int s = r + int(threadIdx.x);
+        uint32_t cnt = 0;
+        if (s < P.nseg) {
+            const uint32_t len = P.seg[s].len;
+            cnt = seg_entries(seg_off, s, len, cap);
+            L.first[s] = seg_off[s];
+            L.cnt[s] = cnt;
+            L.off[s] = static_cast<uint32_t>(P.seg[s].off);
+            L.len[s] = len;
+        }
+        uint64_t btot;
+        uint32_t ttot;
+        const uint64_t bpre = block_exclusive_scan<uint64_t>(block_bytes(cnt, dgc) * (s < P.nseg), &btot);
+        const uint32_t tpre = block_exclusive_scan<uint32_t>((cnt + kTile - 1) / kTile, &ttot);
+        if (s < P.nseg) {
+            L.tile0[s] = tile_run + tpre;
+            L.boff[s] = byte_run + bpre;
+        }
+        byte_run += btot;
+        tile_run += ttot;
+    }
+    if (threadIdx.x == 0) L.tile0[P.nseg] = tile_run;
+    __syncthreads();
+    *ntiles = tile_run;
+    return byte_run;
+}
+
+// Geometry of tile t: the segment whose tile range holds it (exactly one).
+__device__ __forceinline__ TileGeom fused_tile(const PlanDev &P, FuseLds &L, uint32_t t, const uint32_t *E) {
+    for (int s = threadIdx.x; s < P.nseg; s += kBlock)
+        if (L.tile0[s] <= t && t < L.tile0[s + 1]) L.cur = static_cast<uint32_t>(s);
+    __syncthreads();
+    const uint32_t s = uni(L.cur);
+    TileGeom g;
+    g.x.first = uni(L.first[s]);
+    g.x.off = uni(L.off[s]);
+    g.x.len = uni(L.len[s]);
+    g.E = uni(E ? E[s] : L.cnt[s]);
+    g.tile0 = uni(L.tile0[s]);
+    g.j0 = g.x.first + (t - g.tile0) * kTile;
+    g.cnt = uni(min(L.cnt[s] - (t - g.tile0) * kTile, kTile));
+    g.boff = L.boff[s];
+    return g;
+}
+
+// Main pass: layout, then every tile as in the write pass.  Workgroup 0
+// writes the headers, the stream length, the tile count (flags[0]) and
+// whether the stream does not fit (flags[1]); every tile writes its escape
+// count, so nothing has to be cleared before the pass.
+__global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, int kind, uint64_t cap,
+                                                           const uint32_t *__restrict__ seg_off,
+                                                           const float *__restrict__ seg_scale,
+                                                           const uint32_t *__restrict__ idx,
+                                                           const float *__restrict__ val, uint32_t MAX,
+                                                           uint8_t *__restrict__ out, uint64_t out_cap,
+                                                           uint64_t *__restrict__ out_bytes, PackWs w) {
+    const bool dgc = kind == GC_KIND_DGC;
+    __shared__ FuseLds L;
+    uint32_t ntiles;
+    const uint64_t bytes = fused_layout(P, dgc, cap, seg_off, L, &ntiles);
+    const bool fits = bytes <= out_cap;
+    if (blockIdx.x == 0) {
+        if (fits)
+            for (int s = threadIdx.x; s < P.nseg; s += kBlock)
+                write_block_header(out, L.boff[s], dgc, L.len[s], L.cnt[s], L.cnt[s], dgc ? 0.0f : seg_scale[s]);
+        if (threadIdx.x == 0) {
+            if (fits) write_stream_header(out, kind, P.nseg);
+            *out_bytes = bytes;
+            w.flags[0] = ntiles;
+            w.flags[1] = fits ? 0u : 1u;
+        }
+    }
+    if (!fits) return;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const TileGeom g = fused_tile(P, L, t, nullptr);
+        (void)tile_write(g, t, dgc, idx, val, MAX, out, w);
+        __syncthreads();
+    }
+}
+
+// Fix pass: returns unless some tile has escapes (each workgroup reads the
+// tile counts).  Otherwise every workgroup lays the stream out again with
+// each segment's escapes (the relayout of the plan path), workgroup 0
+// rewrites the headers and the length, and the tiles are written again.
+__global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, int kind, uint64_t cap,
+                                                          const uint32_t *__restrict__ seg_off,
+                                                          const float *__restrict__ seg_scale,
+                                                          const uint32_t *__restrict__ idx,
+                                                          const float *__restrict__ val, uint32_t MAX,
+                                                          uint8_t *__restrict__ out, uint64_t out_cap,
+                                                          uint64_t *__restrict__ out_bytes, PackWs w) {
+    const bool dgc = kind == GC_KIND_DGC;
+    // the tiles' escape bytes (sixteen per load, over the workspace's whole
+    // table) in the same round of loads as the tile count; bytes past the
+    // count are not this call's
+    const uint32_t ntiles = uni(w.flags[0]);
+    const uint32_t nofit = w.flags[1];
+    const uint4 *ta = reinterpret_cast<const uint4 *>(w.tile_any);  // 256-byte aligned region
+    const uint32_t n16 = static_cast<uint32_t>((w.max_tiles + 15) / 16);
+    uint32_t any = 0;
+    for (uint32_t q0 = threadIdx.x; q0 < n16; q0 += 8 * kBlock) {
+        uint4 x[8];
+#pragma unroll
+        for (uint32_t q = 0; q < 8; ++q) {
+            const uint32_t i = q0 + q * kBlock;
+            x[q] = i < n16 ? ta[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 8; ++q) {
+            const uint32_t b = 16 * (q0 + q * kBlock);
+            const uint32_t word[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                const uint32_t b0 = b + 4 * k;  // bytes [b0, b0 + 4) of the table
+                const uint32_t keep = b0 + 4 <= ntiles ? 0xFFFFFFFFu
+                                      : b0 >= ntiles   ? 0u
+                                                       : (1u << (8 * (ntiles - b0))) - 1u;
+                any |= word[k] & keep;
+            }
+        }
+    }
+    if (nofit) return;
+    if (!__syncthreads_or(any != 0u)) return;
+    __shared__ FuseLds L;
+    __shared__ uint32_t esc[kFuseSegs];
+    uint32_t nt2;
+    (void)fused_layout(P, dgc, cap, seg_off, L, &nt2);  // the main pass's layout: nt2 == ntiles
+    for (int s = threadIdx.x; s < P.nseg; s += kBlock) esc[s] = 0u;
+    __syncthreads();
+    for (uint32_t t = threadIdx.x; t < ntiles; t += kBlock) {
+        const uint32_t e = w.tile_esc[t];
+        if (!e) continue;
+        int lo = 0, hi = P.nseg - 1;  // the last segment whose tiles start at or before t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (L.tile0[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        atomicAdd(&esc[lo], e);
+    }
+    __syncthreads();
+    uint64_t byte_run = 16;
+    for (int r = 0; r < P.nseg; r += kBlock) {
+        const int s = r + int(threadIdx.x);
+        uint64_t sz = 0;
+        if (s < P.nseg) {
+            // never more codes than a segment of this length can need
+            const uint64_t cap_e = uint64_t(L.len[s]) + L.len[s] / MAX + 1;
+            const uint64_t e64 = uint64_t(L.cnt[s]) + esc[s];
+            const uint32_t E = static_cast<uint32_t>(e64 < cap_e ? e64 : cap_e);
+            esc[s] = E;  // from here on: the block's codes
+            sz = block_bytes(E, dgc);
+        }
+        uint64_t tot;
+        const uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
+        if (s < P.nseg) L.boff[s] = byte_run + pre;
+        byte_run += tot;
+    }
+    __syncthreads();
+    const bool fits = byte_run <= out_cap;
+    if (blockIdx.x == 0) {
+        if (fits)
+            for (int s = threadIdx.x; s < P.nseg; s += kBlock)
+                write_block_header(out, L.boff[s], dgc, L.len[s], esc[s], L.cnt[s], dgc ? 0.0f : seg_scale[s]);
+        if (threadIdx.x == 0) *out_bytes = byte_run;
+    }
+    if (!fits) return;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const TileGeom g = fused_tile(P, L, t, esc);
+        tile_rewrite(g, t, dgc, idx, val, MAX, out, w);
+        __syncthreads();
+    }
 }
 
 }  // namespace
@@ -450,18 +726,41 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     PackWs w = pack_layout(plan, ws, nullptr);
     const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
     const uint64_t cap = in->cap;
-    // one tile per workgroup up to kTileGrid tiles (each tile is a chain of
+    // One tile per workgroup up to kTileGrid tiles (each tile is a chain of
     // dependent loads, so tiles run side by side rather than in sequence);
-    // the grid follows the capacity, and workgroups past the actual tile
-    // count exit at once
+    // workgroups past the actual tile count exit at once.  A DGC message
+    // normally holds the plan's k per segment: its grid follows those tiles
+    // (with room for denser messages, whose extra tiles the workgroups loop
+    // over), not the capacity.
     constexpr size_t kTileGrid = 8192;
-    const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kTileGrid));
-    GC_LAUNCH("pack_plan", stream, pack_plan_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale, out,
-                                                                             out_cap, out_bytes, w));
-    GC_LAUNCH("pack_write", stream, pack_write_kernel<false><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
-    GC_LAUNCH("pack_relayout", stream, pack_relayout_kernel<<<1, kBlock, 0, stream>>>(P, kind, MAX, in->seg_scale, out, out_cap,
+    size_t want = w.max_tiles;
+    if (kind == GC_KIND_DGC) {
+        size_t ktiles = 0;
+        for (const auto &s : plan->seg) ktiles += ceil_div(s.k, kTile);
+        want = std::max<size_t>(2 * ktiles, 256);
+    }
+    unsigned grid = static_cast<unsigned>(std::min({w.max_tiles, want, kTileGrid}));
+    if (plan->nseg <= kFuseSegs) {
+        // the main pass keeps its workgroups resident: each lays the stream
+        // out once, then loops over tiles
+        grid = std::min(grid, resident_blocks(reinterpret_cast<const void *>(pack_main_kernel)));
+        // few segments: every workgroup lays the stream out itself; the fix
+        // pass only reads the tile counts unless a tile has escapes
+        const unsigned fgrid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, 256));
+        GC_LAUNCH("pack_main", stream, pack_main_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale,
+                                                                                     in->idx, in->val, MAX, out, out_cap,
                                                                                      out_bytes, w));
-    GC_LAUNCH("pack_rewrite", stream, pack_write_kernel<true><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
+        GC_LAUNCH("pack_fix", stream, pack_fix_kernel<<<fgrid, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale,
+                                                                                       in->idx, in->val, MAX, out, out_cap,
+                                                                                       out_bytes, w));
+    } else {
+        GC_LAUNCH("pack_plan", stream, pack_plan_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale, out,
+                                                                                 out_cap, out_bytes, w));
+        GC_LAUNCH("pack_write", stream, pack_write_kernel<false><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
+        GC_LAUNCH("pack_relayout", stream, pack_relayout_kernel<<<1, kBlock, 0, stream>>>(P, kind, MAX, in->seg_scale, out, out_cap,
+                                                                                         out_bytes, w));
+        GC_LAUNCH("pack_rewrite", stream, pack_write_kernel<true><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_pack launch");
     return GC_OK;

@@ -51,6 +51,31 @@ static BlobLayout blob_layout(const gc_plan *p) {
     return L;
 }
 
+unsigned resident_blocks(const void *kernel) {
+    static std::mutex mu;
+    static std::vector<std::pair<std::pair<int, const void *>, unsigned>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1024;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &c : cache)
+        if (c.first.first == dev && c.first.second == kernel) return c.second;
+    int per = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kBlock, 0) != hipSuccess || per < 1) {
+        (void)hipGetLastError();
+        per = 1;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        cus = 1;
+    }
+    const unsigned v = static_cast<unsigned>(per) * static_cast<unsigned>(cus);
+    cache.push_back({{dev, kernel}, v});
+    return v;
+}
+
 static gc_status plan_tables(const gc_plan *cplan, PlanDev *out, bool upload) {
     gc_plan *plan = const_cast<gc_plan *>(cplan);
     int dev = 0;
