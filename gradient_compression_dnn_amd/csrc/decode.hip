@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(PlanDev P, MsgTable m, i
     } else if (total != 0) {
         for (int e = threadIdx.x; e < kChunk; e += kBlock) acc[e] = 0.0f;
         __syncthreads();
-        constexpr uint32_t kBatch = 4;  // entries per thread with loads in flight together
+        // entries per thread with loads in flight together: 2048 per round
+        // covers the ~1100 entries a chunk holds at AdaComp's density in one
+        // round trip
+        constexpr uint32_t kBatch = 8;
         for (int k = 0; k < K; ++k) {
             const uint32_t ak = __shfl(a, k, kWave), bk = __shfl(b, k, kWave);
             const uint32_t *idx = m.idx[k];
