@@ -116,7 +116,7 @@ _SIGS = {
 KERNELS = ("dgc_norm", "dgc_prep", "dgc_prepare", "dgc_sample", "dgc_bound", "dgc_ssample", "dgc_squant", "dgc_update", "dgc_collect",
            "dgc_select", "dgc_stage", "dgc_refine", "dgc_sbase", "dgc_count", "dgc_scan", "dgc_emit", "ada_max", "ada_binsum", "ada_scale", "ada_offsets", "ada_apply",
            "ada_fold", "ada_emit", "ada_residual",
-           "pack_plan", "pack_write", "pack_relayout", "pack_rewrite", "pack_main", "pack_fix", "unpack_walk", "unpack_count", "unpack_scan",
+           "pack_plan", "pack_write", "pack_relayout", "pack_rewrite", "pack_main", "pack_fix", "unpack_layout",
            "unpack_write", "decode_index", "decode", "dcd",
            "dcd_decode", "dcd_mix", "ecd_compress", "ecd_update", "slimdp_values", "stream_probe")
 

@@ -120,8 +120,22 @@ __device__ __forceinline__ uint32_t entry_gap(const EntryCtx &x, uint32_t j, uin
 // a 20% slower write pass).
 constexpr int kKeep = 0;
 
+constexpr uint32_t kCkpt = 4096;  // codes between a block's checkpoints
+
 __device__ __forceinline__ uint64_t block_bytes(uint64_t E, bool dgc) {
-    return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0);
+    return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0) + 8 * ((E + kCkpt - 1) / kCkpt);
+}
+
+// The first block's offset: stream header and block table before it.
+__device__ __forceinline__ uint64_t blocks_start(int nseg) { return 16 + 16 * uint64_t(nseg); }
+
+// Table entry s: the block's offset, codes and entries.
+__device__ __forceinline__ void write_table_entry(uint8_t *out, int s, uint64_t at, uint32_t E, uint32_t cnt) {
+    uint32_t *t = reinterpret_cast<uint32_t *>(out + 16 + 16 * uint64_t(s));
+    t[0] = static_cast<uint32_t>(at);
+    t[1] = static_cast<uint32_t>(at >> 32);
+    t[2] = E;
+    t[3] = cnt;
 }
 
 // Headers of block s (at `at`, E codes, cnt entries) and its pad.
@@ -137,7 +151,7 @@ __device__ __forceinline__ void write_block_header(uint8_t *out, uint64_t at, bo
 
 __device__ __forceinline__ void write_stream_header(uint8_t *out, int kind, int nseg) {
     uint32_t *h = reinterpret_cast<uint32_t *>(out);
-    h[0] = magic('G', 'C', 'P', '1');
+    h[0] = magic('G', 'C', 'P', '2');
     h[1] = static_cast<uint32_t>(kind);
     h[2] = static_cast<uint32_t>(nseg);
     h[3] = 0u;
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void pack_plan_kernel(PlanDev P, int kind, 
                                                            uint64_t *__restrict__ out_bytes, PackWs w) {
     const bool dgc = kind == GC_KIND_DGC;
     __shared__ uint32_t tstart[kBlock + 1];
-    uint64_t byte_run = 16;
+    uint64_t byte_run = blocks_start(P.nseg);
     uint32_t tile_run = 0;
     for (int r = 0; r < P.nseg; r += kBlock) {
         const int s = r + int(threadIdx.x);
@@ -201,6 +215,7 @@ __global__ __launch_bounds__(kBlock) void pack_plan_kernel(PlanDev P, int kind, 
             const uint32_t cnt = seg_entries(seg_off, s, seg_max_entries(P.seg[s], kind), cap);
             // the block offset again, from this thread's own write above
             write_block_header(out, w.blk_off[s], dgc, P.seg[s].len, cnt, cnt, dgc ? 0.0f : seg_scale[s]);
+            write_table_entry(out, s, w.blk_off[s], cnt, cnt);
         }
     }
     if (threadIdx.x == 0) {
@@ -220,7 +235,7 @@ __device__ void pack_relayout(const PlanDev &P, int kind, uint32_t MAX, const fl
                               const PackWs &w) {
     const bool dgc = kind == GC_KIND_DGC;
     const uint32_t ntiles = w.flags[0];
-    uint64_t byte_run = 16;
+    uint64_t byte_run = blocks_start(P.nseg);
     for (int r = 0; r < P.nseg; r += kBlock) {
         const int s = r + int(threadIdx.x);
         uint64_t sz = 0;
@@ -246,6 +261,7 @@ __device__ void pack_relayout(const PlanDev &P, int kind, uint32_t MAX, const fl
         for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
             const uint4 sr = w.srec[s];
             write_block_header(out, w.blk_off[s], dgc, P.seg[s].len, sr.z, sr.y, dgc ? 0.0f : seg_scale[s]);
+            write_table_entry(out, s, w.blk_off[s], sr.z, sr.y);
         }
     if (threadIdx.x == 0) {
         *out_bytes = byte_run;
@@ -287,7 +303,7 @@ struct TileGeom {
 // return 0.
 __device__ __forceinline__ void tile_load(const TileGeom &g, const uint32_t *__restrict__ idx,
                                           const float *__restrict__ val, uint32_t (&gap)[kPerThread],
-                                          float (&v)[kPerThread]) {
+                                          float (&v)[kPerThread], uint32_t &cur0) {
     const uint32_t d = uni(g.j0 > g.x.first ? 1u : 0u);
     const BufRsrc ri = chunk_buf(reinterpret_cast<const float *>(idx + g.j0), g.cnt);
     const BufRsrc rp = chunk_buf(reinterpret_cast<const float *>(idx + g.j0 - d), g.cnt + d);
@@ -316,6 +332,7 @@ __device__ __forceinline__ void tile_load(const TileGeom &g, const uint32_t *__r
             __builtin_amdgcn_update_dpp(static_cast<int>(p0[i]), static_cast<int>(cur[i]), kDppWaveShr1, 0xF, 0xF, false));
         gap[i] = e < g.cnt ? entry_gap(g.x, g.j0 + e, cur[i], prv) : 0u;
     }
+    cur0 = cur[0];
 }
 
 // One code (and DGC value) at its slot of the block.  The packed stream is
@@ -337,15 +354,23 @@ __device__ __forceinline__ uint16_t *block_runs(uint8_t *out, const TileGeom &g)
 __device__ __forceinline__ float *block_vals(uint8_t *out, const TileGeom &g) {
     return reinterpret_cast<float *>(out + g.boff + 16 + 2ull * g.E + 2ull * (g.E & 1u));
 }
+// The block's checkpoints: (entries, reader position) before code kCkpt c.
+__device__ __forceinline__ uint32_t *block_ckpt(uint8_t *out, const TileGeom &g, bool dgc) {
+    return reinterpret_cast<uint32_t *>(out + g.boff + 16 + 2ull * g.E + 2ull * (g.E & 1u) + (dgc ? 4ull * g.E : 0));
+}
+__device__ __forceinline__ void put_ckpt(uint32_t *ck, uint32_t code, uint32_t entries, uint32_t pos) {
+    ck[2 * (code / kCkpt)] = entries;
+    ck[2 * (code / kCkpt) + 1] = pos;
+}
 
 // First pass over a tile: its escapes to tile_esc[t]; a tile without any is
 // written at slot = rank in the segment.  Returns the tile's escapes.
 __device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bool dgc,
                                                const uint32_t *__restrict__ idx, const float *__restrict__ val,
                                                uint32_t MAX, uint8_t *__restrict__ out, const PackWs &w) {
-    uint32_t gap[kPerThread];
+    uint32_t gap[kPerThread], cur0;
     float v[kPerThread];
-    tile_load(g, idx, val, gap, v);
+    tile_load(g, idx, val, gap, v, cur0);
     uint32_t mine = 0;
 #pragma unroll
     for (uint32_t i = 0; i < kPerThread; ++i) mine += gap[i] / MAX;
@@ -363,6 +388,11 @@ __device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bo
         const uint32_t slot = g.j0 + e - g.x.first;
         if (e < g.cnt && slot < g.E) put_code(dgc, runs, vals, slot, gap[i], v[i]);  // slot >= E only for malformed messages
     }
+    // without escapes code c of the block is entry c: the tile's first entry
+    // starts checkpoint t - tile0, with the reader standing at its position
+    // minus its run
+    if (threadIdx.x == 0 && g.j0 - g.x.first < g.E)
+        put_ckpt(block_ckpt(out, g, dgc), g.j0 - g.x.first, g.j0 - g.x.first, (cur0 - g.x.off) - gap[0]);
     return 0;
 }
 
@@ -380,15 +410,22 @@ __device__ __forceinline__ void tile_rewrite(const TileGeom &g, uint32_t t, bool
     const uint32_t esc_base = block_total(part);
     uint16_t *runs = block_runs(out, g);
     float *vals = block_vals(out, g);
+    uint32_t *ck = block_ckpt(out, g, dgc);
     if (uni(w.tile_esc[t]) == 0) {
-        uint32_t gap[kPerThread];
+        uint32_t gap[kPerThread], cur0;
         float v[kPerThread];
-        tile_load(g, idx, val, gap, v);
+        tile_load(g, idx, val, gap, v, cur0);
 #pragma unroll
         for (uint32_t i = 0; i < kPerThread; ++i) {
             const uint32_t e = i * kBlock + threadIdx.x;
             const uint32_t slot = (g.j0 + e - g.x.first) + esc_base;
-            if (e < g.cnt && slot < g.E) put_code(dgc, runs, vals, slot, gap[i], v[i]);
+            if (e < g.cnt && slot < g.E) {
+                put_code(dgc, runs, vals, slot, gap[i], v[i]);
+                // an entry of a tile without escapes: the code before it is
+                // the previous entry's, so the reader stands at its position
+                // minus its run
+                if (slot % kCkpt == 0) put_ckpt(ck, slot, g.j0 + e - g.x.first, (idx[g.j0 + e] - g.x.off) - gap[i]);
+            }
         }
         return;
     }
@@ -407,14 +444,19 @@ __device__ __forceinline__ void tile_rewrite(const TileGeom &g, uint32_t t, bool
         uint32_t slot = (g.j0 + e - g.x.first) + before;
         uint32_t gp = gap_at(e);
         const uint32_t esc = gp / MAX;
+        const uint32_t rank = g.j0 + e - g.x.first;     // entries before this one in the segment
+        uint32_t pos = (idx[g.j0 + e] - g.x.off) - gp;  // the reader's position before its first code
         for (uint32_t z = 0; z < esc && slot < g.E; ++z) {
+            if (slot % kCkpt == 0) put_ckpt(ck, slot, rank, pos);
             runs[slot] = static_cast<uint16_t>(MAX);
             if (dgc) vals[slot] = 0.0f;
             ++slot;
             gp -= MAX;
+            pos += MAX;
         }
         before += esc;
         if (slot >= g.E) continue;  // only for malformed messages
+        if (slot % kCkpt == 0) put_ckpt(ck, slot, rank, pos);
         put_code(dgc, runs, vals, slot, gp, val[g.j0 + e]);
     }
 }
@@ -485,7 +527,7 @@ struct FuseLds {
 // and the tile count in *ntiles.
 __device__ uint64_t fused_layout(const PlanDev &P, bool dgc, uint64_t cap, const uint32_t *__restrict__ seg_off,
                                  FuseLds &L, uint32_t *ntiles) {
-    uint64_t byte_run = 16;
+    uint64_t byte_run = blocks_start(P.nseg);
     uint32_t tile_run = 0;
     for (int r = 0; r < P.nseg; r += kBlock) {
         const int s = r + int(threadIdx.x);
@@ -551,8 +593,10 @@ __global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, int kind, 
     const bool fits = bytes <= out_cap;
     if (blockIdx.x == 0) {
         if (fits)
-            for (int s = threadIdx.x; s < P.nseg; s += kBlock)
+            for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
                 write_block_header(out, L.boff[s], dgc, L.len[s], L.cnt[s], L.cnt[s], dgc ? 0.0f : seg_scale[s]);
+                write_table_entry(out, s, L.boff[s], L.cnt[s], L.cnt[s]);
+            }
         if (threadIdx.x == 0) {
             if (fits) write_stream_header(out, kind, P.nseg);
             *out_bytes = bytes;
@@ -629,7 +673,7 @@ __global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, int kind, u
         atomicAdd(&esc[lo], e);
     }
     __syncthreads();
-    uint64_t byte_run = 16;
+    uint64_t byte_run = blocks_start(P.nseg);
     for (int r = 0; r < P.nseg; r += kBlock) {
         const int s = r + int(threadIdx.x);
         uint64_t sz = 0;
@@ -650,8 +694,10 @@ __global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, int kind, u
     const bool fits = byte_run <= out_cap;
     if (blockIdx.x == 0) {
         if (fits)
-            for (int s = threadIdx.x; s < P.nseg; s += kBlock)
+            for (int s = threadIdx.x; s < P.nseg; s += kBlock) {
                 write_block_header(out, L.boff[s], dgc, L.len[s], esc[s], L.cnt[s], dgc ? 0.0f : seg_scale[s]);
+                write_table_entry(out, s, L.boff[s], esc[s], L.cnt[s]);
+            }
         if (threadIdx.x == 0) *out_bytes = byte_run;
     }
     if (!fits) return;
@@ -680,7 +726,10 @@ static uint64_t pack_bound_for(const gc_plan *plan, int kind, F entries) {
     const uint64_t MAX = kind == GC_KIND_DGC ? 65535 : 32767;
     const uint64_t per = kind == GC_KIND_DGC ? 6 : 2;
     uint64_t b = 16;
-    for (const auto &s : plan->seg) b += 16 + 2 + per * (entries(s) + s.len / MAX + 1);
+    for (const auto &s : plan->seg) {
+        const uint64_t codes = entries(s) + s.len / MAX + 1;  // at most
+        b += 16 + 16 + 2 + per * codes + 8 * ceil_div(codes, kCkpt);  // table entry, header, pad, codes, checkpoints
+    }
     return b;
 }
 

@@ -3,18 +3,19 @@
 // values with 16-bit zero-run lengths (AdaComp codes carry a sign bit and one
 // layer scale instead).
 //
-// A segment's codes are read in tiles of 4096.  An element position is the
-// sum of the steps before the code plus its run (a step is run + 1 for an
-// entry and MAX for an escape); an entry's slot is the count of entries
-// before it.  Both sums are prefix scans, so the path is
-//   walk  (one workgroup) follow the block headers from the stream start
-//         (each block's size depends on its entry count), check them against
-//         the plan, and lay out the tiles
-//   count (tile) entries and summed steps per tile
-//   scan  (one workgroup) entry slots (over all tiles) and step prefixes
-//   write (tile) block scans of steps and entries; idx, val
+// The stream's block table gives every block's offset, codes and entries, and
+// each block carries a checkpoint (entries read, reader position) before
+// every 4096th code, so the blocks and their tiles of 4096 codes are read
+// independently:
+//   layout (one workgroup) check the stream header, the table and every
+//          block header against the plan and against one another; segment
+//          offsets of the message, tiles, scales
+//   write  (tile) codes from the tile's checkpoint: block scans of steps and
+//          entries give every entry's position and slot; the tile's end must
+//          meet the next checkpoint (or the block's entry count); idx, val
 // Anything that does not fit the plan sets a bit in *status and is not
-// written; the message stays within its capacity and its segments.
+// written; the message stays within its capacity and its segments.  A stream
+// whose layout is wrong anywhere is read as empty.
 #include <algorithm>
 
 #include "gc_internal.hpp"
@@ -23,21 +24,18 @@ namespace gc {
 
 namespace {
 
-constexpr uint32_t kUTile = 4096;
+constexpr uint32_t kUTile = 4096;            // codes per tile, and between checkpoints
 constexpr uint32_t kUPer = kUTile / kBlock;  // codes per thread in a tile
 
 // status bits
 constexpr uint32_t kBadStream = 1u, kBadBlock = 2u, kBadEntry = 4u, kOverCap = 8u, kBadCount = 16u;
 
 struct UnpackWs {
-    uint64_t *blk_off;    // [nseg] byte offset of each block
-    uint32_t *seg_E;      // [nseg] codes of each block (0 for a bad block)
-    uint32_t *seg_w3;     // [nseg] the header's last word (DGC count, AdaComp scale bits)
-    uint32_t *tile_base;  // [nseg + 1]
-    uint32_t *tile_cnt;   // [max_tiles] entries per tile
-    uint32_t *tile_steps; // [max_tiles] summed steps per tile
-    uint32_t *tile_out;   // [max_tiles + 1] first slot of each tile
-    uint64_t *tile_gpos;  // [max_tiles + 1] steps before each tile, over all tiles
+    uint64_t *blk_off;     // [nseg] byte offset of each block
+    uint32_t *seg_E;       // [nseg] codes of each block (0 when the stream is bad)
+    uint32_t *seg_cnt;     // [nseg] entries of each block (0 when the stream is bad)
+    uint32_t *tile_base;   // [nseg + 1] first tile of each block
+    uint32_t *slot_base;   // [nseg + 1] first message slot of each block (before clamping to cap)
     size_t max_tiles;
 };
 
@@ -54,12 +52,9 @@ UnpackWs unpack_layout(const gc_plan *p, void *base, size_t *bytes) {
     w.max_tiles = tiles + 1;
     w.blk_off = c.take<uint64_t>(p->nseg);
     w.seg_E = c.take<uint32_t>(p->nseg);
-    w.seg_w3 = c.take<uint32_t>(p->nseg);
+    w.seg_cnt = c.take<uint32_t>(p->nseg);
     w.tile_base = c.take<uint32_t>(p->nseg + 1);
-    w.tile_cnt = c.take<uint32_t>(w.max_tiles);
-    w.tile_steps = c.take<uint32_t>(w.max_tiles);
-    w.tile_out = c.take<uint32_t>(w.max_tiles + 1);
-    w.tile_gpos = c.take<uint64_t>(w.max_tiles + 1);
+    w.slot_base = c.take<uint32_t>(p->nseg + 1);
     if (bytes) *bytes = c.used + 256;
     return w;
 }
@@ -70,127 +65,114 @@ constexpr uint32_t magic(char a, char b, char c, char d) {
 }
 
 __device__ __forceinline__ uint64_t block_bytes(uint64_t E, bool dgc) {
-    return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0);
+    return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0) + 8 * ((E + kUTile - 1) / kUTile);
 }
 
-// One block header read at `at` by one thread, with the checks of the
-// sequential walk: on a bad header the block counts as empty (E = 0) and st
-// gets kBadBlock; once st is set no header is read.  Returns the block's
-// bytes.
-__device__ __forceinline__ uint64_t walk_one(const PlanDev &P, bool dgc, uint32_t MAX, uint32_t bmagic,
-                                             const uint8_t *in, uint64_t nbytes, int s, uint64_t at, uint32_t &st,
-                                             UnpackWs &w, float *seg_scale) {
-    uint32_t E = 0, w3 = 0;
-    if (!st && at + 16 <= nbytes) {
-        const uint32_t *b = reinterpret_cast<const uint32_t *>(in + at);
-        const uint32_t m = b[0], n = b[1];
-        E = b[2];
-        w3 = b[3];
-        if (m != bmagic || n != P.seg[s].len || E > max_codes(n, MAX) || at + block_bytes(E, dgc) > nbytes) {
-            st |= kBadBlock;
-            E = 0;
-        }
-    } else if (!st) {
-        st |= kBadBlock;
+__device__ __forceinline__ uint64_t ld_u64(const uint8_t *p) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+    return uint64_t(q[0]) | uint64_t(q[1]) << 32;
+}
+
+// Block s as the table and its header give it: table entry (offset, E, cnt)
+// and whether the block fits the plan and the stream on its own (its header
+// inside the stream, magic, length, codes and count agree with the table, its
+// bytes inside the stream).  w3 is the header's last word.
+struct BlockView {
+    uint64_t off;
+    uint32_t E, cnt, w3;
+    bool ok;
+};
+__device__ __forceinline__ BlockView view_block(const PlanDev &P, bool dgc, uint32_t MAX, uint32_t bmagic,
+                                                const uint8_t *in, uint64_t nbytes, int s) {
+    BlockView b{};
+    const uint8_t *t = in + 16 + 16 * uint64_t(s);
+    b.off = ld_u64(t);
+    b.E = reinterpret_cast<const uint32_t *>(t)[2];
+    b.cnt = reinterpret_cast<const uint32_t *>(t)[3];
+    const uint32_t len = P.seg[s].len;
+    b.ok = b.off % 4 == 0 && b.off <= nbytes && nbytes - b.off >= 16 && b.E <= max_codes(len, MAX) && b.cnt <= b.E &&
+           block_bytes(b.E, dgc) <= nbytes - b.off;
+    if (b.ok) {
+        const uint32_t *h = reinterpret_cast<const uint32_t *>(in + b.off);
+        b.w3 = h[3];
+        b.ok = h[0] == bmagic && h[1] == len && h[2] == b.E && (!dgc || h[3] == b.cnt);
     }
-    w.blk_off[s] = at;
-    w.seg_E[s] = E;
-    w.seg_w3[s] = w3;
-    if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(w3);
-    return block_bytes(E, dgc);
+    return b;
 }
 
-// One workgroup; the headers are a chain (each block's size comes from its
-// own header), then the workgroup lays out the tiles.  AdaComp: thread 0
-// follows the chain.  DGC: a block normally holds exactly k_s codes (an
-// escape needs a gap of 65535 unsent elements), so wave 0 predicts the next
-// 64 headers' offsets from k, reads them at once, and keeps the prefix whose
-// headers are valid with E = k (what the sequential walk computes for them);
-// the first block that differs is read at its now known offset by the
-// sequential rule, and the next round predicts from there.
-__global__ __launch_bounds__(kBlock) void unpack_walk_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
-                                                             uint64_t nbytes, UnpackWs w, float *seg_scale,
-                                                             uint32_t *status) {
+// One workgroup.  Pass 1 checks every block and that each lies where the
+// blocks before it end; pass 2 lays out the tiles and slots (every block
+// empty when anything failed) and writes the message's segment offsets and
+// scales.
+__global__ __launch_bounds__(kBlock) void unpack_layout_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
+                                                               uint64_t nbytes, uint64_t cap, UnpackWs w,
+                                                               uint32_t *__restrict__ seg_off, float *seg_scale,
+                                                               uint32_t *status) {
     const bool dgc = kind == GC_KIND_DGC;
     const uint32_t MAX = dgc ? 65535u : 32767u;
     const uint32_t bmagic = dgc ? magic('D', 'G', 'C', '1') : magic('A', 'D', 'C', '1');
-    if (threadIdx.x < kWave) {
-        const int lane = lane_id();
-        uint32_t st = 0;
+    const uint64_t head = 16 + 16 * uint64_t(P.nseg);
+    uint32_t st = 0;
+    {
         const uint32_t *h = reinterpret_cast<const uint32_t *>(in);
-        if (nbytes < 16 || h[0] != magic('G', 'C', 'P', '1') || h[1] != uint32_t(kind) || h[2] != uint32_t(P.nseg))
-            st |= kBadStream;
-        uint64_t at = 16;
-        if (!dgc) {
-            if (lane == 0)
-                for (int s = 0; s < P.nseg; ++s) at += walk_one(P, dgc, MAX, bmagic, in, nbytes, s, at, st, w, seg_scale);
-        } else {
-            int s = 0;
-            while (s < P.nseg && !st) {
-                const int sl = s + lane;
-                const bool live = sl < P.nseg;
-                const uint32_t k = live ? P.seg[sl].k : 0u;
-                const uint32_t len = live ? P.seg[sl].len : 0u;
-                const uint64_t sz = live ? block_bytes(k, true) : 0;
-                uint64_t incl = sz;  // inclusive scan of the predicted sizes
-#pragma unroll
-                for (int d = 1; d < kWave; d <<= 1) {
-                    const uint64_t y = __shfl_up(incl, d, kWave);
-                    if (lane >= d) incl += y;
-                }
-                const uint64_t my_at = at + incl - sz;
-                bool ok = false;
-                uint32_t w3 = 0;
-                if (live && my_at + 16 <= nbytes) {
-                    const uint32_t *b = reinterpret_cast<const uint32_t *>(in + my_at);
-                    w3 = b[3];
-                    ok = b[0] == bmagic && b[1] == len && b[2] == k && my_at + sz <= nbytes;
-                }
-                const uint64_t bad = __ballot(live && !ok);
-                const int nlive = P.nseg - s < kWave ? P.nseg - s : kWave;
-                const int f = bad ? __ffsll(static_cast<long long>(bad)) - 1 : nlive;  // confirmed blocks
-                if (lane < f) {
-                    w.blk_off[sl] = my_at;
-                    w.seg_E[sl] = k;
-                    w.seg_w3[sl] = w3;
-                    if (seg_scale) seg_scale[sl] = 0.0f;
-                }
-                if (f > 0) at = __shfl(my_at + sz, f - 1, kWave);
-                s += f;
-                if (f < nlive) {
-                    // block s differs from the prediction: the sequential rule
-                    uint64_t add = 0;
-                    if (lane == 0) add = walk_one(P, dgc, MAX, bmagic, in, nbytes, s, at, st, w, seg_scale);
-                    at += __shfl(add, 0, kWave);
-                    st = __shfl(st, 0, kWave);
-                    ++s;
-                }
-            }
-            // after a bad block the rest are read as empty, as in the sequential walk
-            for (int r = s + lane; r < P.nseg; r += kWave) {
-                w.blk_off[r] = at + 16ull * uint64_t(r - s);
-                w.seg_E[r] = 0;
-                w.seg_w3[r] = 0;
-                if (seg_scale) seg_scale[r] = 0.0f;
-            }
-            if (s < P.nseg) at += 16ull * uint64_t(P.nseg - s);
-        }
-        if (lane == 0) {
-            if (!st && at != nbytes) st |= kBadBlock;
-            *status = st;
-        }
+        if (nbytes < head || h[0] != magic('G', 'C', 'P', '2') || h[1] != uint32_t(kind) ||
+            h[2] != uint32_t(P.nseg) || h[3] != 0u)
+            st = kBadStream;
     }
-    __syncthreads();
-    uint32_t run = 0;
+    // pass 1
+    uint64_t at = head;
+    uint32_t bad = 0;
+    if (!st) {
+        for (int r = 0; r < P.nseg; r += kBlock) {
+            const int s = r + int(threadIdx.x);
+            uint64_t sz = 0;
+            bool ok = true;
+            uint64_t off = 0;
+            if (s < P.nseg) {
+                const BlockView b = view_block(P, dgc, MAX, bmagic, in, nbytes, s);
+                ok = b.ok;
+                off = b.off;
+                sz = ok ? block_bytes(b.E, dgc) : 0;  // a bad block's size is unknown: the stream fails anyway
+            }
+            uint64_t tot;
+            const uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
+            if (s < P.nseg && (!ok || off != at + pre)) bad = 1u;
+            at += tot;
+        }
+        if (__syncthreads_or(bad != 0u) || at != nbytes) st = kBadBlock;
+    }
+    // pass 2
+    uint32_t tile_run = 0;
+    uint64_t slot_run = 0;
     for (int r = 0; r < P.nseg; r += kBlock) {
         const int s = r + int(threadIdx.x);
-        const uint32_t v = s < P.nseg ? (w.seg_E[s] + kUTile - 1) / kUTile : 0u;
-        uint32_t tot;
-        const uint32_t pre = block_exclusive_scan(v, &tot);
-        if (s < P.nseg) w.tile_base[s] = run + pre;
-        run += tot;
+        BlockView b{};
+        if (s < P.nseg && !st) b = view_block(P, dgc, MAX, bmagic, in, nbytes, s);
+        const uint32_t E = st ? 0u : b.E, cnt = st ? 0u : b.cnt;
+        uint32_t ttot;
+        uint64_t ctot;
+        const uint32_t tpre = block_exclusive_scan<uint32_t>((E + kUTile - 1) / kUTile, &ttot);
+        const uint64_t cpre = block_exclusive_scan<uint64_t>(cnt, &ctot);
+        if (s < P.nseg) {
+            w.blk_off[s] = st ? 0 : b.off;
+            w.seg_E[s] = E;
+            w.seg_cnt[s] = cnt;
+            w.tile_base[s] = tile_run + tpre;
+            const uint64_t sb = slot_run + cpre;
+            w.slot_base[s] = static_cast<uint32_t>(min<uint64_t>(sb, 0xFFFFFFFFull));
+            seg_off[s] = static_cast<uint32_t>(min<uint64_t>(sb, cap));
+            if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(b.w3);
+        }
+        tile_run += ttot;
+        slot_run += ctot;
     }
-    if (threadIdx.x == 0) w.tile_base[P.nseg] = run;
+    if (threadIdx.x == 0) {
+        w.tile_base[P.nseg] = tile_run;
+        w.slot_base[P.nseg] = static_cast<uint32_t>(min<uint64_t>(slot_run, 0xFFFFFFFFull));
+        seg_off[P.nseg] = static_cast<uint32_t>(min<uint64_t>(slot_run, cap));
+        if (slot_run > cap) st |= kOverCap;
+        *status = st;
+    }
 }
 
 // Segment of tile t (the last s with tile_base[s] <= t), from an LDS copy of
@@ -220,107 +202,12 @@ struct TileOf {
     }
 };
 
-__device__ __forceinline__ const uint16_t *block_runs(const uint8_t *in, const UnpackWs &w, uint32_t s) {
-    return reinterpret_cast<const uint16_t *>(in + w.blk_off[s] + 16);
-}
-
-__global__ __launch_bounds__(kBlock) void unpack_count_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
-                                                              UnpackWs w) {
-    const uint32_t ntiles = w.tile_base[P.nseg];
-    if (blockIdx.x >= ntiles) return;
-    const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
-    const uint32_t rmask = kind == GC_KIND_DGC ? 0xFFFFu : 0x7FFFu;
-    __shared__ uint32_t lds[kLdsSegs];
-    TileOf table;
-    table.init(w.tile_base, P.nseg, lds);
-    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t s = table.segment(t);
-        const uint32_t E = w.seg_E[s];
-        const uint32_t j0 = (t - w.tile_base[s]) * kUTile;
-        const uint16_t *runs = block_runs(in, w, s);
-        uint32_t code[kUPer];
-#pragma unroll
-        for (uint32_t i = 0; i < kUPer; ++i) code[i] = runs[min(j0 + i * kBlock + threadIdx.x, E - 1)];
-        uint32_t cnt = 0, steps = 0;
-#pragma unroll
-        for (uint32_t i = 0; i < kUPer; ++i) {
-            if (j0 + i * kBlock + threadIdx.x >= E) continue;
-            const uint32_t r = code[i] & rmask;
-            const bool esc = r == MAX;
-            cnt += esc ? 0u : 1u;
-            steps += esc ? MAX : r + 1;
-        }
-        uint32_t tc, ts;
-        (void)block_exclusive_scan(cnt, &tc);
-        (void)block_exclusive_scan(steps, &ts);
-        if (threadIdx.x == 0) {
-            w.tile_cnt[t] = tc;
-            w.tile_steps[t] = ts;
-        }
-    }
-}
-
-// One workgroup: slots and step prefixes over all tiles, segment offsets, the
-// capacity and the DGC header counts.
-constexpr uint32_t kScanRun = 16;
-
-__global__ __launch_bounds__(kBlock) void unpack_scan_kernel(PlanDev P, int kind, UnpackWs w, uint64_t cap,
-                                                             uint32_t *__restrict__ seg_off, uint32_t *status) {
-    const uint32_t ntiles = w.tile_base[P.nseg];
-    uint32_t out_run = 0;
-    uint64_t pos_run = 0;
-    for (uint32_t r0 = 0; r0 < ntiles; r0 += kBlock * kScanRun) {
-        const uint32_t t0 = r0 + threadIdx.x * kScanRun;
-        uint32_t c[kScanRun], st[kScanRun];
-        uint32_t csum = 0;
-        uint64_t ssum = 0;
-#pragma unroll
-        for (uint32_t u = 0; u < kScanRun; ++u) {
-            const bool in = t0 + u < ntiles;
-            c[u] = in ? w.tile_cnt[t0 + u] : 0u;
-            st[u] = in ? w.tile_steps[t0 + u] : 0u;
-            csum += c[u];
-            ssum += st[u];
-        }
-        uint32_t ctot;
-        uint64_t stot;
-        uint32_t cpre = out_run + block_exclusive_scan(csum, &ctot);
-        uint64_t spre = pos_run + block_exclusive_scan<uint64_t>(ssum, &stot);
-#pragma unroll
-        for (uint32_t u = 0; u < kScanRun; ++u) {
-            if (t0 + u >= ntiles) break;
-            w.tile_out[t0 + u] = cpre;
-            w.tile_gpos[t0 + u] = spre;
-            cpre += c[u];
-            spre += st[u];
-        }
-        out_run += ctot;
-        pos_run += stot;
-    }
-    if (threadIdx.x == 0) {
-        w.tile_out[ntiles] = out_run;
-        w.tile_gpos[ntiles] = pos_run;
-    }
-    __syncthreads();
-    uint32_t bad = 0;
-    for (int s = threadIdx.x; s <= P.nseg; s += kBlock) {
-        const uint32_t o = w.tile_out[w.tile_base[s]];
-        seg_off[s] = static_cast<uint32_t>(min<uint64_t>(o, cap));
-        if (s < P.nseg && kind == GC_KIND_DGC) {
-            const uint32_t cnt = w.tile_out[w.tile_base[s + 1]] - o;
-            if (w.seg_E[s] && cnt != w.seg_w3[s]) bad |= kBadCount;
-        }
-    }
-    if (out_run > cap) bad |= kOverCap;
-    if (bad) atomicOr(status, bad);
-}
-
 // Exclusive prefix of one value per element in the tile's order, element
 // (row i, thread t) being code i * kBlock + t: a wave scan per row, then one
-// wave scans the kUPer * kWaves (row, wave) totals.
-__device__ __forceinline__ void block_row_scan(const uint32_t (&v)[kUPer], uint32_t (&ex)[kUPer]) {
+// wave scans the kUPer * kWaves (row, wave) totals.  Returns the tile's total.
+__device__ __forceinline__ uint32_t block_row_scan(const uint32_t (&v)[kUPer], uint32_t (&ex)[kUPer]) {
     static_assert(kUPer * kWaves <= kWave, "one wave scans the row totals");
-    __shared__ uint32_t tot[kUPer * kWaves];
+    __shared__ uint32_t tot[kUPer * kWaves + 1];
     uint32_t incl[kUPer];
 #pragma unroll
     for (uint32_t i = 0; i < kUPer; ++i) {
@@ -333,18 +220,22 @@ __device__ __forceinline__ void block_row_scan(const uint32_t (&v)[kUPer], uint3
         const uint32_t t = threadIdx.x < kUPer * kWaves ? tot[threadIdx.x] : 0u;
         const uint32_t x = wave_inclusive_scan(t);
         if (threadIdx.x < kUPer * kWaves) tot[threadIdx.x] = x - t;
+        if (threadIdx.x == kWave - 1) tot[kUPer * kWaves] = x;
     }
     __syncthreads();
 #pragma unroll
     for (uint32_t i = 0; i < kUPer; ++i) ex[i] = tot[i * kWaves + wave_id()] + incl[i] - v[i];
+    const uint32_t all = tot[kUPer * kWaves];
     __syncthreads();
+    return all;
 }
 
 // Code i * kBlock + t of the tile is thread t's i-th: loads and the entries'
 // stores are coalesced along a row; the row-order scans give every code its
-// position and slot.
+// position and slot from the tile's checkpoint.
 __global__ __launch_bounds__(kBlock) void unpack_write_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
                                                               UnpackWs w, uint64_t cap,
+                                                              const float *__restrict__ seg_scale,
                                                               uint32_t *__restrict__ out_idx,
                                                               float *__restrict__ out_val, uint32_t *status) {
     const uint32_t ntiles = w.tile_base[P.nseg];
@@ -358,11 +249,19 @@ __global__ __launch_bounds__(kBlock) void unpack_write_kernel(PlanDev P, int kin
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const uint32_t s = table.segment(t);
         const SegDev seg = P.seg[s];
-        const uint32_t E = w.seg_E[s];
-        const uint32_t j0 = (t - w.tile_base[s]) * kUTile;
-        const uint16_t *runs = block_runs(in, w, s);
-        const float *vals = reinterpret_cast<const float *>(in + w.blk_off[s] + 16 + 2ull * E + 2ull * (E & 1u));
-        const float scale = dev_u2f(w.seg_w3[s]);
+        const uint32_t E = w.seg_E[s], cnt = w.seg_cnt[s];
+        const uint32_t c = t - w.tile_base[s];
+        const uint32_t j0 = c * kUTile;
+        const uint32_t nck = (E + kUTile - 1) / kUTile;
+        const uint8_t *blk = in + w.blk_off[s];
+        const uint16_t *runs = reinterpret_cast<const uint16_t *>(blk + 16);
+        const float *vals = reinterpret_cast<const float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
+        const uint32_t *ck = reinterpret_cast<const uint32_t *>(blk + 16 + 2ull * E + 2ull * (E & 1u) + (dgc ? 4ull * E : 0));
+        const float scale = dgc ? 0.0f : seg_scale[s];
+        // the tile's start and, unless it is the block's last, the next tile's
+        const uint32_t e0 = ck[2 * c], p0 = ck[2 * c + 1];
+        const bool last = c + 1 >= nck;
+        const uint32_t e1 = last ? cnt : ck[2 * c + 2], p1 = last ? 0u : ck[2 * c + 3];
         uint32_t code[kUPer], steps[kUPer], ent[kUPer];
 #pragma unroll
         for (uint32_t i = 0; i < kUPer; ++i) code[i] = runs[min(j0 + i * kBlock + threadIdx.x, E - 1)];
@@ -379,19 +278,21 @@ __global__ __launch_bounds__(kBlock) void unpack_write_kernel(PlanDev P, int kin
             steps[i] = !in_tile ? 0u : (r == MAX ? MAX : r + 1);
         }
         uint32_t spre[kUPer], epre[kUPer];
-        block_row_scan(steps, spre);
-        block_row_scan(ent, epre);
-        const uint64_t pos0 = w.tile_gpos[t] - w.tile_gpos[w.tile_base[s]];
-        const uint32_t slot0 = w.tile_out[t];
+        const uint32_t stot = block_row_scan(steps, spre);
+        const uint32_t etot = block_row_scan(ent, epre);
         uint32_t bad = 0;
+        // the tile must end where the next checkpoint (or the block's count) says
+        if (uint64_t(e0) + etot != e1 || (!last && uint64_t(p0) + stot != p1)) bad |= kBadCount;
+        // slots of this block's entries stay inside its range of the message
+        const uint64_t slot_end = min<uint64_t>(uint64_t(w.slot_base[s]) + cnt, cap);
 #pragma unroll
         for (uint32_t i = 0; i < kUPer; ++i) {
             if (!ent[i]) continue;
-            const uint64_t rel = pos0 + spre[i] + (code[i] & rmask);
-            const uint32_t slot = slot0 + epre[i];
+            const uint64_t rel = uint64_t(p0) + spre[i] + (code[i] & rmask);
+            const uint64_t slot = uint64_t(w.slot_base[s]) + e0 + epre[i];
             if (rel >= seg.len) {
                 bad |= kBadEntry;
-            } else if (slot < cap) {
+            } else if (slot < slot_end) {
                 __builtin_nontemporal_store(static_cast<uint32_t>(seg.off + rel), out_idx + slot);
                 __builtin_nontemporal_store(dgc ? v[i] : ((code[i] & 0x8000u) ? -scale : scale), out_val + slot);
             }
@@ -433,10 +334,10 @@ extern "C" gc_status gc_unpack(const gc_plan *plan, int kind, const uint8_t *in,
     UnpackWs w = unpack_layout(plan, ws, nullptr);
     constexpr size_t kTileGrid = 8192;
     const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kTileGrid));
-    GC_LAUNCH("unpack_walk", stream, unpack_walk_kernel<<<1, kBlock, 0, stream>>>(P, kind, in, in_bytes, w, out->seg_scale, status));
-    GC_LAUNCH("unpack_count", stream, unpack_count_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in, w));
-    GC_LAUNCH("unpack_scan", stream, unpack_scan_kernel<<<1, kBlock, 0, stream>>>(P, kind, w, out->cap, out->seg_off, status));
-    GC_LAUNCH("unpack_write", stream, unpack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in, w, out->cap, out->idx,
+    GC_LAUNCH("unpack_layout", stream, unpack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, in, in_bytes, out->cap, w,
+                                                                                     out->seg_off, out->seg_scale, status));
+    GC_LAUNCH("unpack_write", stream, unpack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in, w, out->cap,
+                                                                                       out->seg_scale, out->idx,
                                                                                        out->val, status));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_unpack launch");

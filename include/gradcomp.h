@@ -335,12 +335,21 @@ gc_status gc_dgc_step_ex(const gc_plan *plan, const float *G, float *U, float *V
 /*
  * Byte-exact run-length encoding of a message ([DGC] §3.1: 32-bit values and
  * 16-bit zero-run lengths).  Little-endian; every block 4-byte aligned.
- *   stream header : u32 'GCP1', u32 kind, u32 nseg, u32 0
+ *   stream header : u32 'GCP2', u32 kind, u32 nseg, u32 0
+ *   block table   : per segment u64 offset of its block from the stream
+ *                   start, u32 E, u32 entries of the segment
+ *   then the blocks in segment order, the first at 16 + 16 nseg:
  *   DGC block     : u32 'DGC1', u32 n_s, u32 E, u32 entries of the segment,
- *                   u16 run[E] (+ one u16 0 if E is odd), f32 val[E]
+ *                   u16 run[E] (+ one u16 0 if E is odd), f32 val[E],
+ *                   checkpoints
  *   AdaComp block : u32 'ADC1', u32 n_s, u32 E, f32 scale_s,
- *                   u16 code[E] (+ one u16 0 if E is odd);
+ *                   u16 code[E] (+ one u16 0 if E is odd), checkpoints;
  *                   code = sign << 15 | run  (sign 1 = negative)
+ *   checkpoints   : for c = 0 .. ceil(E / 4096) - 1, u32 entries and u32
+ *                   reader position p (as gc_unpack defines it) before code
+ *                   4096 c
+ * The table and the checkpoints let a receiver read blocks and tiles of
+ * 4096 codes independently.
  * A run counts the unsent elements since the previous entry of the segment
  * (from the segment start for the first).  A run >= MAX is split: emit an
  * escape (run MAX; DGC value +0.0f), subtract MAX, repeat.  MAX is 65535 for
@@ -384,15 +393,19 @@ gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
  *              AdaComp, seg_scale[nseg].  Entries at or past out->cap are
  *              not written (seg_off is clamped to cap).
  *   status   : device u32, set to 0 for a stream that fits the plan, else a
- *              bitmask: 1 bad stream header, 2 bad block header or size
- *              (or trailing bytes), 4 an entry outside its segment (not
- *              written), 8 more entries than out->cap, 16 a DGC block whose
- *              entries disagree with its header count.  Whatever the stream,
- *              every write stays inside the message and its segments.
+ *              bitmask: 1 bad stream header (or too short for its table),
+ *              2 a block table entry or block header that disagrees with the
+ *              plan, the stream's bytes or the blocks before it (or
+ *              trailing bytes): the whole stream is then read as empty,
+ *              4 an entry outside its segment (not written), 8 more entries
+ *              than out->cap, 16 a tile whose entries or positions disagree
+ *              with the next checkpoint or the block's entry count.
+ *              Whatever the stream, every write stays inside the message,
+ *              inside the range seg_off gives its segment, and inside the
+ *              segment's elements.
  *   ws       : gc_plan_workspace_bytes(plan, GC_OP_UNPACK) bytes.
- * The block headers are followed from the stream start by one thread (each
- * block's size depends on its entry count), so the call's latency grows with
- * the number of segments.
+ * One workgroup checks the table and headers; then every tile of 4096 codes
+ * is read from its checkpoint, independently of the others.
  * Errors: GC_EINVAL (bad kind, null pointers, misaligned or short stream),
  *         GC_ECAPACITY (ws).
  */

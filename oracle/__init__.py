@@ -198,8 +198,10 @@ def pack(kind, table, idx, val, seg_off, seg_scale=None, cap=None) -> bytes:
     if cap is None:
         MAX = 65535 if kind == 1 else 32767
         per = 6 if kind == 1 else 2
-        cap = 16 + sum(16 + 2 + per * (int(seg_off[s + 1] - seg_off[s]) + int(t[s, 1]) // MAX + 1)
-                       for s in range(len(t)))
+        cap = 16
+        for s in range(len(t)):
+            codes = int(seg_off[s + 1] - seg_off[s]) + int(t[s, 1]) // MAX + 1  # at most
+            cap += 16 + 16 + 2 + per * codes + 8 * ((codes + 4095) // 4096)
     out = np.zeros(int(cap), np.uint8)
     nbytes = lib().orc_pack(int(kind), _segs(t), len(t), _ptr(idx), _ptr(val), _ptr(seg_off),
                             _ptr(sc), _ptr(out), int(cap))

@@ -377,7 +377,10 @@ void orc_dgc(const orc_seg *segs, int nseg, const float *G, float *U, float *V,
 /* -------------------------------------------------------------------- pack */
 /*
  * DGC §3.1: the encoder stores 32-bit values and 16-bit zero-run lengths.
- * Layout (little-endian, 4-byte aligned blocks) as documented with gc_pack.
+ * Layout (little-endian, 4-byte aligned blocks) as documented with gc_pack:
+ * stream header, a table with each block's offset, codes and entries, then
+ * the blocks in segment order, each with a checkpoint (entries and reader
+ * position before the code) at every 4096th code.
  */
 static void put_u32(uint8_t *p, uint32_t v)
 {
@@ -385,6 +388,12 @@ static void put_u32(uint8_t *p, uint32_t v)
     p[1] = (uint8_t)(v >> 8);
     p[2] = (uint8_t)(v >> 16);
     p[3] = (uint8_t)(v >> 24);
+}
+
+static void put_u64(uint8_t *p, uint64_t v)
+{
+    put_u32(p, (uint32_t)v);
+    put_u32(p + 4, (uint32_t)(v >> 32));
 }
 
 static void put_u16(uint8_t *p, uint16_t v)
@@ -402,6 +411,25 @@ static void put_f32(uint8_t *p, float f)
 
 #define ORC_MAGIC(a, b, c, d) \
     ((uint32_t)(a) | (uint32_t)(b) << 8 | (uint32_t)(c) << 16 | (uint32_t)(d) << 24)
+#define ORC_CKPT 4096u /* codes between checkpoints */
+
+/* Bytes of a block of E codes. */
+static uint64_t block_size(int kind, uint64_t E)
+{
+    return 16 + 2 * E + 2 * (E % 2) + (kind == 1 ? 4 * E : 0) + 8 * ((E + ORC_CKPT - 1) / ORC_CKPT);
+}
+
+/* Codes (entries plus escapes) of segment s's entries. */
+static uint64_t seg_codes(const orc_seg *sg, const uint32_t *idx, uint32_t j0, uint32_t j1, uint32_t MAX)
+{
+    uint64_t E = 0, p = 0;
+    for (uint32_t j = j0; j < j1; ++j) {
+        uint64_t rel = idx[j] - sg->offset;
+        E += (rel - p) / MAX + 1;
+        p = rel + 1;
+    }
+    return E;
+}
 
 uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
                   const uint32_t *idx, const float *val,
@@ -410,34 +438,24 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
 {
     const uint32_t MAX = kind == 1 ? 65535u : 32767u;
     /* first pass: the stream length */
-    uint64_t total = 16;
-    for (int s = 0; s < nseg; ++s) {
-        uint64_t E = 0, p = 0;
-        for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
-            uint64_t rel = idx[j] - segs[s].offset;
-            uint64_t gap = rel - p;
-            E += gap / MAX + 1;
-            p = rel + 1;
-        }
-        total += 16 + 2 * E + 2 * (E % 2) + (kind == 1 ? 4 * E : 0);
-    }
+    uint64_t total = 16 + 16 * (uint64_t)nseg;
+    for (int s = 0; s < nseg; ++s)
+        total += block_size(kind, seg_codes(&segs[s], idx, seg_off[s], seg_off[s + 1], MAX));
     if (total > cap) return 0;
 
-    uint8_t *w = out;
-    put_u32(w, ORC_MAGIC('G', 'C', 'P', '1'));
-    put_u32(w + 4, (uint32_t)kind);
-    put_u32(w + 8, (uint32_t)nseg);
-    put_u32(w + 12, 0);
-    w += 16;
+    put_u32(out, ORC_MAGIC('G', 'C', 'P', '2'));
+    put_u32(out + 4, (uint32_t)kind);
+    put_u32(out + 8, (uint32_t)nseg);
+    put_u32(out + 12, 0);
+    uint64_t at = 16 + 16 * (uint64_t)nseg;
     for (int s = 0; s < nseg; ++s) {
-        /* count entries + escapes again for the header */
-        uint64_t E = 0, p = 0;
-        for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
-            uint64_t rel = idx[j] - segs[s].offset;
-            E += (rel - p) / MAX + 1;
-            p = rel + 1;
-        }
-        uint32_t cnt = seg_off[s + 1] - seg_off[s];
+        const uint64_t E = seg_codes(&segs[s], idx, seg_off[s], seg_off[s + 1], MAX);
+        const uint32_t cnt = seg_off[s + 1] - seg_off[s];
+        uint8_t *tab = out + 16 + 16 * (uint64_t)s;
+        put_u64(tab, at);
+        put_u32(tab + 8, (uint32_t)E);
+        put_u32(tab + 12, cnt);
+        uint8_t *w = out + at;
         put_u32(w, kind == 1 ? ORC_MAGIC('D', 'G', 'C', '1') : ORC_MAGIC('A', 'D', 'C', '1'));
         put_u32(w + 4, segs[s].length);
         put_u32(w + 8, (uint32_t)E);
@@ -447,16 +465,28 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
             put_f32(w + 12, seg_scale[s]);
         uint8_t *runs = w + 16;
         uint8_t *vals = runs + 2 * E + 2 * (E % 2);
-        uint64_t e = 0;
-        p = 0;
+        uint8_t *ckpt = vals + (kind == 1 ? 4 * E : 0);
+        /* e: codes written; pr: the reader's position before the next code;
+           done: entries written */
+        uint64_t e = 0, pr = 0;
+        uint32_t done = 0;
         for (uint32_t j = seg_off[s]; j < seg_off[s + 1]; ++j) {
             uint64_t rel = idx[j] - segs[s].offset;
-            uint64_t gap = rel - p;
+            uint64_t gap = rel - pr;
             while (gap >= MAX) { /* escape: skip MAX positions, carry nothing */
+                if (e % ORC_CKPT == 0) {
+                    put_u32(ckpt + 8 * (e / ORC_CKPT), done);
+                    put_u32(ckpt + 8 * (e / ORC_CKPT) + 4, (uint32_t)pr);
+                }
                 put_u16(runs + 2 * e, (uint16_t)MAX);
                 if (kind == 1) put_f32(vals + 4 * e, 0.0f);
                 ++e;
+                pr += MAX;
                 gap -= MAX;
+            }
+            if (e % ORC_CKPT == 0) {
+                put_u32(ckpt + 8 * (e / ORC_CKPT), done);
+                put_u32(ckpt + 8 * (e / ORC_CKPT) + 4, (uint32_t)pr);
             }
             if (kind == 1) {
                 put_u16(runs + 2 * e, (uint16_t)gap);
@@ -466,12 +496,13 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
                 put_u16(runs + 2 * e, (uint16_t)(sign | gap));
             }
             ++e;
-            p = rel + 1;
+            ++done;
+            pr = rel + 1;
         }
         if (E % 2) put_u16(runs + 2 * E, 0);
-        w = vals + (kind == 1 ? 4 * E : 0);
+        at += block_size(kind, E);
     }
-    return (uint64_t)(w - out);
+    return at;
 }
 
 /* ------------------------------------------------------------------ unpack */
@@ -481,38 +512,54 @@ uint64_t orc_pack(int kind, const orc_seg *segs, int nseg,
  * unsent elements before its entry, an escape (DGC run 0xFFFF, AdaComp run
  * 0x7FFF) skips that many elements and carries no entry.  AdaComp entries take
  * +-scale by their sign bit.  Returns 0, or nonzero for a stream that does not
- * fit the plan (bad header, block past the end, entry outside its segment,
- * more entries than cap, a DGC count that disagrees with its header).
+ * fit the plan: 1 bad stream header, or a table entry that is not where the
+ * blocks lie; 2 bad block header or size, or trailing bytes; 3 an entry outside
+ * its segment; 4 more entries than cap; 5 entries or positions that disagree
+ * with the table, the DGC header count or a checkpoint.
  */
 static uint32_t get_u32(const uint8_t *p)
 {
     return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
 }
 
+static uint64_t get_u64(const uint8_t *p)
+{
+    return (uint64_t)get_u32(p) | (uint64_t)get_u32(p + 4) << 32;
+}
+
 int orc_unpack(int kind, const orc_seg *segs, int nseg, const uint8_t *buf, uint64_t nbytes,
                uint32_t *idx, float *val, uint32_t *seg_off, float *seg_scale, uint64_t cap)
 {
-    if (nbytes < 16 || get_u32(buf) != ORC_MAGIC('G', 'C', 'P', '1') || get_u32(buf + 4) != (uint32_t)kind ||
-        get_u32(buf + 8) != (uint32_t)nseg)
+    const uint64_t head = 16 + 16 * (uint64_t)nseg;
+    if (nbytes < head || get_u32(buf) != ORC_MAGIC('G', 'C', 'P', '2') || get_u32(buf + 4) != (uint32_t)kind ||
+        get_u32(buf + 8) != (uint32_t)nseg || get_u32(buf + 12) != 0)
         return 1;
     const uint32_t MAX = kind == 1 ? 65535u : 32767u;
     const uint32_t bmagic = kind == 1 ? ORC_MAGIC('D', 'G', 'C', '1') : ORC_MAGIC('A', 'D', 'C', '1');
-    uint64_t at = 16, out = 0;
+    uint64_t at = head, out = 0;
     for (int s = 0; s < nseg; ++s) {
         seg_off[s] = (uint32_t)out;
+        const uint8_t *tab = buf + 16 + 16 * (uint64_t)s;
+        if (get_u64(tab) != at) return 1;
         if (at + 16 > nbytes || get_u32(buf + at) != bmagic || get_u32(buf + at + 4) != segs[s].length)
             return 2;
         uint64_t E = get_u32(buf + at + 8);
         uint32_t w3 = get_u32(buf + at + 12);
-        uint64_t size = 16 + 2 * E + 2 * (E % 2) + (kind == 1 ? 4 * E : 0);
+        if (get_u32(tab + 8) != E) return 2;
+        const uint32_t cnt = get_u32(tab + 12);
+        uint64_t size = block_size(kind, E);
         if (at + size > nbytes) return 2;
         float scale;
         memcpy(&scale, &w3, sizeof scale);
         seg_scale[s] = kind == 1 ? 0.0f : scale;
         const uint8_t *runs = buf + at + 16;
         const uint8_t *vals = runs + 2 * E + 2 * (E % 2);
+        const uint8_t *ckpt = vals + (kind == 1 ? 4 * E : 0);
         uint64_t p = 0, count = 0;
         for (uint64_t e = 0; e < E; ++e) {
+            if (e % ORC_CKPT == 0 &&
+                (get_u32(ckpt + 8 * (e / ORC_CKPT)) != count || get_u32(ckpt + 8 * (e / ORC_CKPT) + 4) != p))
+                return 5;
             uint32_t code = (uint32_t)runs[2 * e] | (uint32_t)runs[2 * e + 1] << 8;
             uint32_t run = kind == 1 ? code : (code & 0x7FFFu);
             if (run == MAX) {
@@ -533,7 +580,7 @@ int orc_unpack(int kind, const orc_seg *segs, int nseg, const uint8_t *buf, uint
             ++count;
             p = rel + 1;
         }
-        if (kind == 1 && count != w3) return 5;
+        if (count != cnt || (kind == 1 && count != w3)) return 5;
         at += size;
     }
     seg_off[nseg] = (uint32_t)out;

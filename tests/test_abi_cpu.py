@@ -112,7 +112,7 @@ def test_plan_queries_and_workspace_on_workloads():
         assert p.adacomp_state_bytes < w.n_total // 8 + (4 << 20)
         # the pack bound covers the format's closed form at k entries per segment
         E = t[:, 3]
-        assert p.pack_bound(B.GC_KIND_DGC) >= 16 + int(np.sum(16 + 6 * E + 2 * (E % 2)))
+        assert p.pack_bound(B.GC_KIND_DGC) >= 16 + int(np.sum(16 + 16 + 6 * E + 2 * (E % 2) + 8 * -(-E // 4096)))
         del p
 
 
@@ -133,7 +133,7 @@ def test_longest_segments_at_the_top_of_the_index_range():
         # an AdaComp message that sends every element: entries plus escapes
         codes = L + L // 32767 + 1
         assert codes < 1 << 32
-        assert p.pack_bound(B.GC_KIND_ADACOMP) >= 16 + 2 * 16 + 2 * codes
+        assert p.pack_bound(B.GC_KIND_ADACOMP) >= 16 + 2 * (16 + 16) + 2 * codes + 8 * -(-codes // 4096)
         del p
 
 

@@ -140,8 +140,8 @@ int main(void) {
     for (int j = 0; j < K0; ++j) CHECK(hidx[j] == 1000 - K0 + j && hval[j] == (float)(1000 - K0 + j + 1));
     for (int j = 0; j < K1; ++j) CHECK(hidx[K0 + j] == 3000 - K1 + j && hval[K0 + j] == (float)(3000 - K1 + j + 1));
     CHECK(hV[999] == 0.0f && hV[995] == 996.0f);  /* masked where sent, V = G elsewhere */
-    /* stream header + 2 blocks of 16 B + k codes (2 B runs, even-padded) + k values */
-    CHECK(hn == 16 + (16 + 2 * K0 + 4 * K0) + (16 + 2 * K1 + 4 * K1));
+    /* stream header, block table, two blocks of K codes and one checkpoint each */
+    CHECK(hn == 16 + 2 * 16 + (16 + 2 * K0 + 4 * K0 + 8) + (16 + 2 * K1 + 4 * K1 + 8));
     CHECK(host[999] == 1000.0f && host[998] == 999.0f && host[995] == 0.0f && host[1200] == 0.0f);
     gc_plan_destroy(p);
     printf("ok\n");

@@ -16,6 +16,7 @@ from gradient_compression_dnn_amd import binding as B
 from gradient_compression_dnn_amd import workloads as W
 from tests.gpu_util import HipPath, same_bits, say, ulp_report
 from tests.test_oracle_codec import _tbl
+from tests.test_oracle_unpack import MALFORMED
 
 pytestmark = pytest.mark.gpu
 
@@ -95,15 +96,13 @@ def test_malformed_streams_set_status_and_stay_in_bounds():
     st, out, tail_ok = gpu_unpack(plan, 1, good, 3)
     assert st == 0 and tail_ok
     cases = {"trailing": good + b"\0\0\0\0", "truncated": good[:-4]}
-    bad = bytearray(good)
-    bad[16:20] = b"ADC1"
-    cases["block magic"] = bytes(bad)
-    bad = bytearray(good)
-    struct.pack_into("<H", bad, 32, 10)
-    cases["run past the end"] = bytes(bad)
-    bad = bytearray(good)
-    struct.pack_into("<I", bad, 24, 1 << 30)  # absurd code count
-    cases["code count"] = bytes(bad)
+    for name, at, fmt, v, _ in MALFORMED:
+        bad = bytearray(good)
+        if fmt == "magic":
+            bad[at:at + 4] = v
+        else:
+            struct.pack_into(fmt, bad, at, v)
+        cases[name] = bytes(bad)
     for name, data in cases.items():
         say(f"unpack malformed {name}")
         st, out, tail_ok = gpu_unpack(plan, 1, data, 3)
@@ -144,20 +143,21 @@ def test_deepspeech_streams_decode_like_their_messages():
 
 def _block_offsets(data: bytes, nseg: int, dgc: bool):
     """Offsets of the blocks of a well-formed stream (a host-side walk of the
-    documented layout)."""
-    at, offs = 16, []
-    for _ in range(nseg):
+    documented layout, checked against the stream's block table)."""
+    at, offs = 16 + 16 * nseg, []
+    for s in range(nseg):
         offs.append(at)
+        assert struct.unpack_from("<Q", data, 16 + 16 * s)[0] == at
         E = struct.unpack_from("<I", data, at + 8)[0]
-        at += 16 + 2 * E + 2 * (E & 1) + (4 * E if dgc else 0)
+        at += 16 + 2 * E + 2 * (E & 1) + (4 * E if dgc else 0) + 8 * -(-E // 4096)
     return offs
 
 
 def test_dgc_streams_with_many_segments():
-    """300 segments (the DGC header walk confirms up to 64 predicted blocks per
-    round): long sparse segments with escapes among ordinary ones, read back
-    exactly; then a bad block magic and a wrong code count past the first
-    round set the status and keep every write inside the message."""
+    """300 segments (more than one round of the layout pass's 256 threads):
+    long sparse segments with escapes among ordinary ones, read back exactly;
+    then a bad block magic, a wrong code count and a wrong checkpoint past the
+    first round set the status and keep every write inside the message."""
     rng = np.random.default_rng(333)
     lengths = [int(rng.choice([int(rng.integers(1, 3000)), int(rng.integers(70_000, 400_000))])) for _ in range(300)]
     ks = [max(1, n // int(rng.choice([10, 1000, 50_000]))) for n in lengths]
@@ -184,7 +184,14 @@ def test_dgc_streams_with_many_segments():
     bad_count = bytearray(data)
     E70 = struct.unpack_from("<I", data, blocks[70] + 8)[0]
     struct.pack_into("<I", bad_count, blocks[70] + 8, E70 + 1)
-    for name, bad in (("block 130 magic", bytes(bad_magic)), ("block 70 count", bytes(bad_count))):
+    # a block of more than one tile: its second checkpoint's position
+    big = next(s for s in range(len(t)) if struct.unpack_from("<I", data, blocks[s] + 8)[0] > 4096)
+    Eb = struct.unpack_from("<I", data, blocks[big] + 8)[0]
+    ck = blocks[big] + 16 + 2 * Eb + 2 * (Eb & 1) + 4 * Eb
+    bad_ckpt = bytearray(data)
+    struct.pack_into("<I", bad_ckpt, ck + 12, struct.unpack_from("<I", data, ck + 12)[0] + 1)
+    for name, bad in (("block 130 magic", bytes(bad_magic)), ("block 70 count", bytes(bad_count)),
+                      (f"block {big} checkpoint", bytes(bad_ckpt))):
         say(f"unpack dgc 300 segments, {name}")
         st, out, tail_ok = gpu_unpack(plan, 1, bad, idx.size)
         assert st != 0 and tail_ok, name

@@ -33,14 +33,42 @@ def test_pack_hand_streams(golden_dir):
         assert got.hex() == c["hex"], c["name"]
 
 
+def test_pack_checkpoints(golden_dir):
+    """Checkpoints past the first: hand-derived entries and reader positions
+    before code 4096, also where that code is an escape."""
+    g = load(golden_dir, "pack_hand.json")
+    for c in g["checkpoint_cases"]:
+        t = _tbl(c["segments"])
+        if c["kind"] == 2:
+            idx = np.arange(0, 10000, 2)
+            sc = [c["scale"]]
+        else:
+            idx = np.concatenate([np.arange(4096), [74096]])
+            sc = [0.0]
+        val = np.full(len(idx), c["value"], np.float32)
+        buf = oracle.pack(c["kind"], t, idx, val, [0, len(idx)], sc)
+        assert len(buf) == c["expect_bytes"], c["name"]
+        off, E, cnt = struct.unpack_from("<QII", buf, 16)
+        assert off == 32 and E == c["expect_E"] and cnt == len(idx), c["name"]
+        codes = off + 16
+        ck = codes + 2 * E + 2 * (E % 2) + (4 * E if c["kind"] == 1 else 0)
+        got = [list(struct.unpack_from("<II", buf, ck + 8 * i)) for i in range(-(-E // 4096))]
+        assert got == c["expect_checkpoints"], c["name"]
+        if c["kind"] == 1:
+            assert struct.unpack_from("<H", buf, codes + 2 * 4096)[0] == c["expect_code_4096"]
+            assert struct.unpack_from("<H", buf, codes + 2 * 4097)[0] == c["expect_code_4097"]
+        st, uidx, _, _, _ = oracle.unpack(c["kind"], t, buf)
+        assert st == 0 and np.array_equal(uidx, idx)
+
+
 def _closed_form_size(kind, t, idx, off):
     MAX = 65535 if kind == 1 else 32767
-    total = 16
+    total = 16 + 16 * len(t)  # stream header and block table
     for s, (o, n, _, _) in enumerate(t):
         rel = idx[off[s]:off[s + 1]].astype(np.int64) - o
         gaps = np.diff(np.concatenate([[-1], rel])) - 1
         E = len(rel) + int(np.sum(gaps // MAX))
-        total += 16 + 2 * E + 2 * (E % 2) + (4 * E if kind == 1 else 0)
+        total += 16 + 2 * E + 2 * (E % 2) + (4 * E if kind == 1 else 0) + 8 * -(-E // 4096)
     return total
 
 
@@ -78,7 +106,7 @@ def test_pack_size_of_deepspeech_layout_at_top_0p1_percent():
     # closed form with one entry per thousand elements and no escapes lands near it.
     w = W.make_config("deepspeech")
     E = w.table[:, 3]
-    size = 16 + int(np.sum(16 + 6 * E + 2 * (E % 2)))
+    size = 16 + int(np.sum(16 + 16 + 6 * E + 2 * (E % 2) + 8 * -(-E // 4096)))
     assert 0.70e6 < size < 0.76e6
 
 

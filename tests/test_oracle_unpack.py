@@ -64,13 +64,32 @@ def test_unpack_rejects_malformed_streams():
     t = _tbl([[0, 10], [12, 5]])
     good = oracle.pack(1, t, [2, 9, 13], [1.0, -2.0, 3.0], [0, 2, 3], np.zeros(2, np.float32))
     assert oracle.unpack(1, t, good)[0] == 0
+    # stream header 16 bytes, table 2 x 16; block 0 at 48: header, runs at 64
+    # (2 codes), values at 68, its one checkpoint at 76; block 1 at 84
+    assert struct.unpack_from("<Q", good, 16)[0] == 48 and struct.unpack_from("<Q", good, 32)[0] == 84
     assert oracle.unpack(2, t, good)[0] != 0                 # wrong kind
     assert oracle.unpack(1, t, good[:-4])[0] != 0            # truncated
     assert oracle.unpack(1, t, good + b"\0\0\0\0")[0] != 0   # trailing bytes
-    bad = bytearray(good)
-    bad[16:20] = b"ADC1"                                      # block magic
-    assert oracle.unpack(1, t, bytes(bad))[0] != 0
-    bad = bytearray(good)
-    struct.pack_into("<H", bad, 32, 10)                      # run past the segment end
-    assert oracle.unpack(1, t, bytes(bad))[0] != 0
-    assert oracle.unpack(1, t, good, cap=2)[0] != 0          # more entries than cap
+    for name, at, fmt, v, want in MALFORMED:
+        bad = bytearray(good)
+        if fmt == "magic":
+            bad[at:at + 4] = v
+        else:
+            struct.pack_into(fmt, bad, at, v)
+        assert oracle.unpack(1, t, bytes(bad))[0] == want, name
+    assert oracle.unpack(1, t, good, cap=2)[0] == 4          # more entries than cap
+
+
+# (name, byte offset, struct format, value, the oracle's status) for the
+# two-segment DGC stream above
+MALFORMED = [
+    ("block magic", 48, "magic", b"ADC1", 2),
+    ("run past the segment end", 64, "<H", 10, 3),
+    ("table offset", 16, "<Q", 52, 1),
+    ("table codes", 24, "<I", 3, 2),
+    ("table entries", 28, "<I", 1, 5),
+    ("checkpoint position", 80, "<I", 1, 5),
+    ("checkpoint entries", 76, "<I", 1, 5),
+    ("header code count", 56, "<I", 1 << 30, 2),
+    ("header entry count", 60, "<I", 3, 5),
+]
