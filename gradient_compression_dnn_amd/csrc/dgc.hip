@@ -751,7 +751,7 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
             if (over == 0) {
                 w.st[s].redo = staged_total < ks ? 1u : 0u;
             } else {
-                const uint64_t budget = min<uint64_t>(seg.len, uint64_t(over) * seg.k);
+                const uint64_t budget = umin64(seg.len, uint64_t(over) * seg.k);
                 if (staged_total <= budget) {
                     w.st[s].all = 1u;
                     w.st[s].sent = staged_total;

@@ -149,6 +149,10 @@ struct WsCursor {
     }
 };
 
+// Minimum of two u64 by comparison (the device min<uint64_t> overload goes
+// through double).
+__host__ __device__ constexpr uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
 // ceil(a / b) in 64 bits (lengths near 2^32 overflow u32 round-ups).
 __host__ __device__ constexpr uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 

@@ -68,6 +68,12 @@ __device__ __forceinline__ uint64_t block_bytes(uint64_t E, bool dgc) {
     return 16 + 2 * E + 2 * (E & 1u) + (dgc ? 4 * E : 0) + 8 * ((E + kUTile - 1) / kUTile);
 }
 
+// A wave-uniform value moved to scalar registers.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+    return uint64_t(uni(static_cast<uint32_t>(v))) | uint64_t(uni(static_cast<uint32_t>(v >> 32))) << 32;
+}
+
 __device__ __forceinline__ uint64_t ld_u64(const uint8_t *p) {
     const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
     return uint64_t(q[0]) | uint64_t(q[1]) << 32;
@@ -100,10 +106,10 @@ __device__ __forceinline__ BlockView view_block(const PlanDev &P, bool dgc, uint
     return b;
 }
 
-// One workgroup.  Pass 1 checks every block and that each lies where the
-// blocks before it end; pass 2 lays out the tiles and slots (every block
-// empty when anything failed) and writes the message's segment offsets and
-// scales.
+// One workgroup.  One pass checks every block, that each lies where the
+// blocks before it end, and lays out the tiles and slots as the table gives
+// them; when anything failed, a second pass lays out every block as empty.
+// Then the message's segment offsets (clamped to cap) and scales.
 __global__ __launch_bounds__(kBlock) void unpack_layout_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
                                                                uint64_t nbytes, uint64_t cap, UnpackWs w,
                                                                uint32_t *__restrict__ seg_off, float *seg_scale,
@@ -119,60 +125,50 @@ __global__ __launch_bounds__(kBlock) void unpack_layout_kernel(PlanDev P, int ki
             h[2] != uint32_t(P.nseg) || h[3] != 0u)
             st = kBadStream;
     }
-    // pass 1
-    uint64_t at = head;
-    uint32_t bad = 0;
-    if (!st) {
+    uint32_t over = 0;  // kOverCap, kept apart from st: st alone decides the second pass
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1 && !st) break;  // the layout of the first pass stands (st is the same in every thread)
+        uint64_t at = head, slot_run = 0;
+        uint32_t tile_run = 0, bad = 0;
         for (int r = 0; r < P.nseg; r += kBlock) {
             const int s = r + int(threadIdx.x);
-            uint64_t sz = 0;
-            bool ok = true;
-            uint64_t off = 0;
-            if (s < P.nseg) {
-                const BlockView b = view_block(P, dgc, MAX, bmagic, in, nbytes, s);
-                ok = b.ok;
-                off = b.off;
-                sz = ok ? block_bytes(b.E, dgc) : 0;  // a bad block's size is unknown: the stream fails anyway
+            BlockView b{};
+            if (s < P.nseg && !st) {
+                b = view_block(P, dgc, MAX, bmagic, in, nbytes, s);
+                if (!b.ok) {
+                    bad = 1u;
+                    b.E = b.cnt = 0;  // a bad block's size is unknown: the stream fails anyway
+                }
             }
-            uint64_t tot;
-            const uint64_t pre = block_exclusive_scan<uint64_t>(sz, &tot);
-            if (s < P.nseg && (!ok || off != at + pre)) bad = 1u;
-            at += tot;
+            uint64_t btot, ctot;
+            uint32_t ttot;
+            const uint64_t bpre = block_exclusive_scan<uint64_t>(st ? 0 : block_bytes(b.E, dgc) * (s < P.nseg), &btot);
+            const uint64_t cpre = block_exclusive_scan<uint64_t>(b.cnt, &ctot);
+            const uint32_t tpre = block_exclusive_scan<uint32_t>((b.E + kUTile - 1) / kUTile, &ttot);
+            if (s < P.nseg) {
+                if (!st && b.off != at + bpre) bad = 1u;
+                w.blk_off[s] = b.off;
+                w.seg_E[s] = b.E;
+                w.seg_cnt[s] = b.cnt;
+                w.tile_base[s] = tile_run + tpre;
+                const uint64_t sb = slot_run + cpre;
+                w.slot_base[s] = static_cast<uint32_t>(umin64(sb, 0xFFFFFFFFull));
+                seg_off[s] = static_cast<uint32_t>(umin64(sb, cap));
+                if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(b.w3);
+            }
+            at += btot;
+            slot_run += ctot;
+            tile_run += ttot;
         }
-        if (__syncthreads_or(bad != 0u) || at != nbytes) st = kBadBlock;
-    }
-    // pass 2
-    uint32_t tile_run = 0;
-    uint64_t slot_run = 0;
-    for (int r = 0; r < P.nseg; r += kBlock) {
-        const int s = r + int(threadIdx.x);
-        BlockView b{};
-        if (s < P.nseg && !st) b = view_block(P, dgc, MAX, bmagic, in, nbytes, s);
-        const uint32_t E = st ? 0u : b.E, cnt = st ? 0u : b.cnt;
-        uint32_t ttot;
-        uint64_t ctot;
-        const uint32_t tpre = block_exclusive_scan<uint32_t>((E + kUTile - 1) / kUTile, &ttot);
-        const uint64_t cpre = block_exclusive_scan<uint64_t>(cnt, &ctot);
-        if (s < P.nseg) {
-            w.blk_off[s] = st ? 0 : b.off;
-            w.seg_E[s] = E;
-            w.seg_cnt[s] = cnt;
-            w.tile_base[s] = tile_run + tpre;
-            const uint64_t sb = slot_run + cpre;
-            w.slot_base[s] = static_cast<uint32_t>(min<uint64_t>(sb, 0xFFFFFFFFull));
-            seg_off[s] = static_cast<uint32_t>(min<uint64_t>(sb, cap));
-            if (seg_scale) seg_scale[s] = dgc || st ? 0.0f : dev_u2f(b.w3);
+        if (!st && (__syncthreads_or(bad != 0u) || at != nbytes)) st = kBadBlock;
+        over = !st && slot_run > cap ? kOverCap : 0u;
+        if (threadIdx.x == 0) {
+            w.tile_base[P.nseg] = tile_run;
+            w.slot_base[P.nseg] = static_cast<uint32_t>(umin64(slot_run, 0xFFFFFFFFull));
+            seg_off[P.nseg] = static_cast<uint32_t>(umin64(slot_run, cap));
         }
-        tile_run += ttot;
-        slot_run += ctot;
     }
-    if (threadIdx.x == 0) {
-        w.tile_base[P.nseg] = tile_run;
-        w.slot_base[P.nseg] = static_cast<uint32_t>(min<uint64_t>(slot_run, 0xFFFFFFFFull));
-        seg_off[P.nseg] = static_cast<uint32_t>(min<uint64_t>(slot_run, cap));
-        if (slot_run > cap) st |= kOverCap;
-        *status = st;
-    }
+    if (threadIdx.x == 0) *status = st | over;
 }
 
 // Segment of tile t (the last s with tile_base[s] <= t), from an LDS copy of
@@ -202,102 +198,140 @@ struct TileOf {
     }
 };
 
-// Exclusive prefix of one value per element in the tile's order, element
-// (row i, thread t) being code i * kBlock + t: a wave scan per row, then one
-// wave scans the kUPer * kWaves (row, wave) totals.  Returns the tile's total.
-__device__ __forceinline__ uint32_t block_row_scan(const uint32_t (&v)[kUPer], uint32_t (&ex)[kUPer]) {
-    static_assert(kUPer * kWaves <= kWave, "one wave scans the row totals");
-    __shared__ uint32_t tot[kUPer * kWaves + 1];
-    uint32_t incl[kUPer];
-#pragma unroll
-    for (uint32_t i = 0; i < kUPer; ++i) {
-        const uint32_t x = wave_inclusive_scan(v[i]);
-        incl[i] = x;
-        if (lane_id() == kWave - 1) tot[i * kWaves + wave_id()] = x;
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        const uint32_t t = threadIdx.x < kUPer * kWaves ? tot[threadIdx.x] : 0u;
-        const uint32_t x = wave_inclusive_scan(t);
-        if (threadIdx.x < kUPer * kWaves) tot[threadIdx.x] = x - t;
-        if (threadIdx.x == kWave - 1) tot[kUPer * kWaves] = x;
-    }
-    __syncthreads();
-#pragma unroll
-    for (uint32_t i = 0; i < kUPer; ++i) ex[i] = tot[i * kWaves + wave_id()] + incl[i] - v[i];
-    const uint32_t all = tot[kUPer * kWaves];
-    __syncthreads();
-    return all;
-}
-
 // Code i * kBlock + t of the tile is thread t's i-th: loads and the entries'
-// stores are coalesced along a row; the row-order scans give every code its
-// position and slot from the tile's checkpoint.
-__global__ __launch_bounds__(kBlock) void unpack_write_kernel(PlanDev P, int kind, const uint8_t *__restrict__ in,
+// stores are coalesced along a row.  One pass of row-order scans gives every
+// code the steps and entries before it in the tile (one wave scan per row of
+// both packed in a u32, then one wave scans the kUPer * kWaves (row, wave)
+// totals of each), and so its position and slot from the tile's checkpoint.
+// The steps and entry flags are derived from the codes where needed rather
+// than kept, so that a thread holds two values per code (one more for DGC's
+// values).
+template <bool kDgc>
+__global__ __launch_bounds__(kBlock) void unpack_write_kernel(PlanDev P, const uint8_t *__restrict__ in,
                                                               UnpackWs w, uint64_t cap,
                                                               const float *__restrict__ seg_scale,
                                                               uint32_t *__restrict__ out_idx,
                                                               float *__restrict__ out_val, uint32_t *status) {
+    static_assert(kUPer * kWaves <= kWave, "one wave scans the row totals");
     const uint32_t ntiles = w.tile_base[P.nseg];
     if (blockIdx.x >= ntiles) return;
-    const bool dgc = kind == GC_KIND_DGC;
-    const uint32_t MAX = dgc ? 65535u : 32767u;
-    const uint32_t rmask = dgc ? 0xFFFFu : 0x7FFFu;
+    constexpr uint32_t MAX = kDgc ? 65535u : 32767u;
+    constexpr uint32_t rmask = kDgc ? 0xFFFFu : 0x7FFFu;
     __shared__ uint32_t lds[kLdsSegs];
+    __shared__ uint32_t tot_s[kUPer * kWaves + 1], tot_e[kUPer * kWaves + 1];
     TileOf table;
     table.init(w.tile_base, P.nseg, lds);
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t s = table.segment(t);
-        const SegDev seg = P.seg[s];
-        const uint32_t E = w.seg_E[s], cnt = w.seg_cnt[s];
-        const uint32_t c = t - w.tile_base[s];
+        // every value of the tile's geometry is the workgroup's: scalar registers
+        const uint32_t s = uni(table.segment(t));
+        const uint32_t seg_len = uni(P.seg[s].len);
+        const uint64_t seg_off0 = uni64(P.seg[s].off);
+        const uint32_t E = uni(w.seg_E[s]), cnt = uni(w.seg_cnt[s]);
+        const uint32_t c = t - uni(w.tile_base[s]);
         const uint32_t j0 = c * kUTile;
         const uint32_t nck = (E + kUTile - 1) / kUTile;
-        const uint8_t *blk = in + w.blk_off[s];
+        const uint32_t sbase = uni(w.slot_base[s]);
+        const uint8_t *blk = in + uni64(w.blk_off[s]);
         const uint16_t *runs = reinterpret_cast<const uint16_t *>(blk + 16);
         const float *vals = reinterpret_cast<const float *>(blk + 16 + 2ull * E + 2ull * (E & 1u));
-        const uint32_t *ck = reinterpret_cast<const uint32_t *>(blk + 16 + 2ull * E + 2ull * (E & 1u) + (dgc ? 4ull * E : 0));
-        const float scale = dgc ? 0.0f : seg_scale[s];
+        const uint32_t *ck = reinterpret_cast<const uint32_t *>(blk + 16 + 2ull * E + 2ull * (E & 1u) + (kDgc ? 4ull * E : 0));
+        const float scale = kDgc ? 0.0f : dev_u2f(uni(dev_f2u(seg_scale[s])));
         // the tile's start and, unless it is the block's last, the next tile's
-        const uint32_t e0 = ck[2 * c], p0 = ck[2 * c + 1];
+        const uint32_t e0 = uni(ck[2 * c]), p0 = uni(ck[2 * c + 1]);
         const bool last = c + 1 >= nck;
-        const uint32_t e1 = last ? cnt : ck[2 * c + 2], p1 = last ? 0u : ck[2 * c + 3];
-        uint32_t code[kUPer], steps[kUPer], ent[kUPer];
+        const uint32_t e1 = last ? cnt : uni(ck[2 * c + 2]), p1 = last ? 0u : uni(ck[2 * c + 3]);
+        // buffer resources over the tile's codes and values: loads past the
+        // block's last code return 0 (and are never used)
+        const uint32_t ntile = min(E - j0, kUTile);
+        const BufRsrc rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(runs + j0), static_cast<short>(0),
+                                                             static_cast<int>(2 * ntile), kBufWord3);
+        uint32_t code[kUPer];
+        float v[kDgc ? kUPer : 1];
 #pragma unroll
-        for (uint32_t i = 0; i < kUPer; ++i) code[i] = runs[min(j0 + i * kBlock + threadIdx.x, E - 1)];
-        float v[kUPer] = {};
-        if (dgc) {  // an AdaComp block has no value array: never read past its codes
+        for (uint32_t i = 0; i < kUPer; ++i)
+            code[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, static_cast<int>(2 * threadIdx.x),
+                                                           static_cast<int>(2 * i * kBlock), 0);
+        if (kDgc) {  // an AdaComp block has no value array
+            const BufRsrc rv = chunk_buf(vals + j0, ntile);
 #pragma unroll
-            for (uint32_t i = 0; i < kUPer; ++i) v[i] = vals[min(j0 + i * kBlock + threadIdx.x, E - 1)];
+            for (uint32_t i = 0; i < kUPer; ++i)
+                v[kDgc ? i : 0] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * threadIdx.x),
+                                                                                static_cast<int>(4 * i * kBlock), 0));
         }
+        auto in_tile = [&](uint32_t i) { return j0 + i * kBlock + threadIdx.x < E; };
+        auto step_of = [&](uint32_t i) {
+            const uint32_t r = code[i] & rmask;
+            return !in_tile(i) ? 0u : (r == MAX ? MAX : r + 1);
+        };
+        auto ent_of = [&](uint32_t i) { return in_tile(i) && (code[i] & rmask) != MAX ? 1u : 0u; };
+        // a row of one wave holds at most 64 entries (8 bits) and 64 * 65535
+        // steps (22 bits): one scan of (steps << 8 | entries) gives both
+        uint32_t pre[kUPer], rowtot[kUPer];
 #pragma unroll
         for (uint32_t i = 0; i < kUPer; ++i) {
-            const bool in_tile = j0 + i * kBlock + threadIdx.x < E;
-            const uint32_t r = code[i] & rmask;
-            ent[i] = in_tile && r != MAX ? 1u : 0u;
-            steps[i] = !in_tile ? 0u : (r == MAX ? MAX : r + 1);
+            const uint32_t x = step_of(i) << 8 | ent_of(i);
+            const uint32_t xi = wave_inclusive_scan(x);
+            pre[i] = xi - x;
+            rowtot[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(xi), kWave - 1));
         }
-        uint32_t spre[kUPer], epre[kUPer];
-        const uint32_t stot = block_row_scan(steps, spre);
-        const uint32_t etot = block_row_scan(ent, epre);
+        if (lane_id() < kUPer) {  // lane i writes row i's totals (the wave's own)
+            uint32_t x = 0;
+#pragma unroll
+            for (uint32_t i = 0; i < kUPer; ++i) x = lane_id() == int(i) ? rowtot[i] : x;
+            tot_s[lane_id() * kWaves + wave_id()] = x >> 8;
+            tot_e[lane_id() * kWaves + wave_id()] = x & 0xFFu;
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const uint32_t ts = threadIdx.x < kUPer * kWaves ? tot_s[threadIdx.x] : 0u;
+            const uint32_t te = threadIdx.x < kUPer * kWaves ? tot_e[threadIdx.x] : 0u;
+            const uint32_t xs = wave_inclusive_scan(ts), xe = wave_inclusive_scan(te);
+            if (threadIdx.x < kUPer * kWaves) {
+                tot_s[threadIdx.x] = xs - ts;
+                tot_e[threadIdx.x] = xe - te;
+            }
+            if (threadIdx.x == kWave - 1) {
+                tot_s[kUPer * kWaves] = xs;
+                tot_e[kUPer * kWaves] = xe;
+            }
+        }
+        __syncthreads();
+        const uint32_t stot = tot_s[kUPer * kWaves], etot = tot_e[kUPer * kWaves];
         uint32_t bad = 0;
         // the tile must end where the next checkpoint (or the block's count) says
         if (uint64_t(e0) + etot != e1 || (!last && uint64_t(p0) + stot != p1)) bad |= kBadCount;
-        // slots of this block's entries stay inside its range of the message
-        const uint64_t slot_end = min<uint64_t>(uint64_t(w.slot_base[s]) + cnt, cap);
+        // the tile's entries go to slots first_slot + (entries before them in
+        // the tile), kept inside the block's range of the message and the
+        // capacity by the range of the stores' buffer resources (stores past
+        // it are dropped)
+        const uint64_t first_slot = uint64_t(sbase) + e0;
+        const uint64_t slot_end = umin64(uint64_t(sbase) + cnt, cap);
+        const uint32_t room = first_slot < slot_end ? static_cast<uint32_t>(umin64(slot_end - first_slot, kUTile)) : 0u;
+        const BufRsrc oi = chunk_buf(reinterpret_cast<const float *>(out_idx + (room ? first_slot : 0)), room);
+        const BufRsrc ov = chunk_buf(out_val + (room ? first_slot : 0), room);
+        // positions in 32 bits: p0 + (steps before the code in the tile, below
+        // 2^28) + run wraps only for a checkpoint near 2^32, which then fails
+        // the segment-length test like any position past the segment
+        uint32_t far = 0;
 #pragma unroll
         for (uint32_t i = 0; i < kUPer; ++i) {
-            if (!ent[i]) continue;
-            const uint64_t rel = uint64_t(p0) + spre[i] + (code[i] & rmask);
-            const uint64_t slot = uint64_t(w.slot_base[s]) + e0 + epre[i];
-            if (rel >= seg.len) {
-                bad |= kBadEntry;
-            } else if (slot < slot_end) {
-                __builtin_nontemporal_store(static_cast<uint32_t>(seg.off + rel), out_idx + slot);
-                __builtin_nontemporal_store(dgc ? v[i] : ((code[i] & 0x8000u) ? -scale : scale), out_val + slot);
-            }
+            const uint32_t row = i * kWaves + wave_id();
+            const uint32_t ts = tot_s[row], te = tot_e[row];
+            const uint32_t d = ts + (pre[i] >> 8) + (code[i] & rmask);
+            const uint32_t rel = p0 + d;
+            const bool en = ent_of(i) != 0u;
+            const bool out = rel < d || rel >= seg_len;  // wrapped, or past the segment
+            far |= en && out ? 1u : 0u;
+            // a code that is no entry, or an entry outside its segment, is
+            // stored past the resources' range: dropped
+            const uint32_t o = en && !out ? 4 * (te + (pre[i] & 0xFFu)) : 0x7FFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(seg_off0) + rel, oi, static_cast<int>(o), 0, kBufNT);
+            const float x = kDgc ? v[kDgc ? i : 0] : ((code[i] & 0x8000u) ? -scale : scale);
+            __builtin_amdgcn_raw_buffer_store_b32(dev_f2u(x), ov, static_cast<int>(o), 0, kBufNT);
         }
+        if (far) bad |= kBadEntry;
         if (bad) atomicOr(status, bad);
+        __syncthreads();  // tot_s / tot_e are rewritten by the next tile
     }
 }
 
@@ -336,9 +370,12 @@ extern "C" gc_status gc_unpack(const gc_plan *plan, int kind, const uint8_t *in,
     const unsigned grid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, kTileGrid));
     GC_LAUNCH("unpack_layout", stream, unpack_layout_kernel<<<1, kBlock, 0, stream>>>(P, kind, in, in_bytes, out->cap, w,
                                                                                      out->seg_off, out->seg_scale, status));
-    GC_LAUNCH("unpack_write", stream, unpack_write_kernel<<<grid, kBlock, 0, stream>>>(P, kind, in, w, out->cap,
-                                                                                       out->seg_scale, out->idx,
-                                                                                       out->val, status));
+    if (kind == GC_KIND_DGC)
+        GC_LAUNCH("unpack_write", stream, unpack_write_kernel<true><<<grid, kBlock, 0, stream>>>(P, in, w, out->cap, out->seg_scale,
+                                                                                                 out->idx, out->val, status));
+    else
+        GC_LAUNCH("unpack_write", stream, unpack_write_kernel<false><<<grid, kBlock, 0, stream>>>(P, in, w, out->cap, out->seg_scale,
+                                                                                                  out->idx, out->val, status));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_error(e, "gc_unpack launch");
     return GC_OK;
