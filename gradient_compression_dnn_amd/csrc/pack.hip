@@ -309,20 +309,18 @@ __device__ __forceinline__ void tile_load(const TileGeom &g, const uint32_t *__r
     const BufRsrc rp = chunk_buf(reinterpret_cast<const float *>(idx + g.j0 - d), g.cnt + d);
     const BufRsrc rv = chunk_buf(val + g.j0, g.cnt);
     uint32_t cur[kPerThread], p0[kPerThread];
+    // lane 0 loads its predecessor (entry e - 1, at e + d - 1 in rp); the
+    // other lanes, and the tile's first entry when it has none, load past the
+    // resource's range (no memory access, 0) and take it from the lane before
+    const bool lane0 = lane_id() == 0;
 #pragma unroll
     for (uint32_t i = 0; i < kPerThread; ++i) {
         const uint32_t e = i * kBlock + threadIdx.x;
-        cur[i] = __builtin_amdgcn_raw_buffer_load_b32(ri, static_cast<int>(4 * e), 0, kKeep);
-        v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, static_cast<int>(4 * e), 0, kKeep));
-        p0[i] = 0u;
-    }
-    if (lane_id() == 0) {
-#pragma unroll
-        for (uint32_t i = 0; i < kPerThread; ++i) {
-            const uint32_t e = i * kBlock + threadIdx.x;
-            const uint32_t ep = e + d > 0 ? e + d - 1 : 0u;
-            p0[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, static_cast<int>(4 * ep), 0, kKeep);
-        }
+        const int vo = static_cast<int>(4 * threadIdx.x), so = static_cast<int>(4 * i * kBlock);
+        cur[i] = __builtin_amdgcn_raw_buffer_load_b32(ri, vo, so, kKeep);
+        v[i] = dev_u2f(__builtin_amdgcn_raw_buffer_load_b32(rv, vo, so, kKeep));
+        const int po = lane0 && e + d > 0 ? static_cast<int>(4 * (e + d - 1)) : 0x7FFFFFF0;
+        p0[i] = __builtin_amdgcn_raw_buffer_load_b32(rp, po, 0, kKeep);
     }
 #pragma unroll
     for (uint32_t i = 0; i < kPerThread; ++i) {
@@ -365,9 +363,12 @@ __device__ __forceinline__ void put_ckpt(uint32_t *ck, uint32_t code, uint32_t e
 
 // First pass over a tile: its escapes to tile_esc[t]; a tile without any is
 // written at slot = rank in the segment.  Returns the tile's escapes.
-__device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bool dgc,
-                                               const uint32_t *__restrict__ idx, const float *__restrict__ val,
-                                               uint32_t MAX, uint8_t *__restrict__ out, const PackWs &w) {
+template <bool kDgc>
+__device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, const uint32_t *__restrict__ idx,
+                                               const float *__restrict__ val, uint8_t *__restrict__ out,
+                                               const PackWs &w) {
+    constexpr bool dgc = kDgc;
+    constexpr uint32_t MAX = kDgc ? 65535u : 32767u;
     uint32_t gap[kPerThread], cur0;
     float v[kPerThread];
     tile_load(g, idx, val, gap, v, cur0);
@@ -380,13 +381,23 @@ __device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bo
         w.tile_any[t] = esc ? 1u : 0u;
     }
     if (esc) return esc;  // written by the rewrite pass
-    uint16_t *runs = block_runs(out, g);
-    float *vals = block_vals(out, g);
+    // buffer resources over the tile's codes and values in the block (slots
+    // j0 - first .. + cnt, inside the block's E): stores past them are dropped
+    const uint32_t slot0 = g.j0 - g.x.first;
+    const uint32_t room = slot0 < g.E ? min(g.cnt, g.E - slot0) : 0u;  // below cnt only for malformed messages
+    const BufRsrc rr = __builtin_amdgcn_make_buffer_rsrc(block_runs(out, g) + slot0, static_cast<short>(0),
+                                                         static_cast<int>(2 * room), kBufWord3);
+    const BufRsrc rv = chunk_buf(block_vals(out, g) + slot0, dgc ? room : 0u);
 #pragma unroll
     for (uint32_t i = 0; i < kPerThread; ++i) {
-        const uint32_t e = i * kBlock + threadIdx.x;
-        const uint32_t slot = g.j0 + e - g.x.first;
-        if (e < g.cnt && slot < g.E) put_code(dgc, runs, vals, slot, gap[i], v[i]);  // slot >= E only for malformed messages
+        const int vo = static_cast<int>(threadIdx.x), so = static_cast<int>(i * kBlock);
+        if (dgc) {
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(gap[i]), rr, 2 * vo, 2 * so, kBufNT);
+            __builtin_amdgcn_raw_buffer_store_b32(dev_f2u(v[i]), rv, 4 * vo, 4 * so, kBufNT);
+        } else {
+            const uint16_t sign = (dev_f2u(v[i]) >> 31) ? 0x8000u : 0u;
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(sign | gap[i]), rr, 2 * vo, 2 * so, kBufNT);
+        }
     }
     // without escapes code c of the block is entry c: the tile's first entry
     // starts checkpoint t - tile0, with the reader standing at its position
@@ -401,9 +412,12 @@ __device__ __forceinline__ uint32_t tile_write(const TileGeom &g, uint32_t t, bo
 // walks 16 contiguous entries per thread in two light passes (escapes, then
 // slots), reloading what it needs, so that its registers do not add to the
 // common path's.
-__device__ __forceinline__ void tile_rewrite(const TileGeom &g, uint32_t t, bool dgc,
-                                             const uint32_t *__restrict__ idx, const float *__restrict__ val,
-                                             uint32_t MAX, uint8_t *__restrict__ out, const PackWs &w) {
+template <bool kDgc>
+__device__ __forceinline__ void tile_rewrite(const TileGeom &g, uint32_t t, const uint32_t *__restrict__ idx,
+                                             const float *__restrict__ val, uint8_t *__restrict__ out,
+                                             const PackWs &w) {
+    constexpr bool dgc = kDgc;
+    constexpr uint32_t MAX = kDgc ? 65535u : 32767u;
     uint32_t part = 0;
 #pragma unroll 4
     for (uint32_t u = g.tile0 + threadIdx.x; u < t; u += kBlock) part += w.tile_esc[u];
@@ -480,19 +494,18 @@ __device__ __forceinline__ TileGeom table_tile(const PlanDev &P, const PackWs &w
 }
 
 // Write pass (kRedo false) and rewrite pass (kRedo true) after the plan pass.
-template <bool kRedo>
-__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, int kind, const uint32_t *__restrict__ idx,
-                                                            const float *__restrict__ val, uint32_t MAX,
-                                                            uint8_t *__restrict__ out, PackWs w) {
-    const bool dgc = kind == GC_KIND_DGC;
+template <bool kRedo, bool kDgc>
+__global__ __launch_bounds__(kBlock) void pack_write_kernel(PlanDev P, const uint32_t *__restrict__ idx,
+                                                            const float *__restrict__ val, uint8_t *__restrict__ out,
+                                                            PackWs w) {
     if (w.flags[1]) return;  // the stream does not fit out_cap: nothing is written
     if (kRedo && !w.flags[2]) return;
     const uint32_t ntiles = uni(w.flags[0]);
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const TileGeom g = table_tile(P, w, t);
         if (kRedo) {
-            tile_rewrite(g, t, dgc, idx, val, MAX, out, w);
-        } else if (tile_write(g, t, dgc, idx, val, MAX, out, w) && threadIdx.x == 0) {
+            tile_rewrite<kDgc>(g, t, idx, val, out, w);
+        } else if (tile_write<kDgc>(g, t, idx, val, out, w) && threadIdx.x == 0) {
             atomicOr(&w.flags[2], 1u);
         }
         __syncthreads();
@@ -579,14 +592,15 @@ __device__ __forceinline__ TileGeom fused_tile(const PlanDev &P, FuseLds &L, uin
 // writes the headers, the stream length, the tile count (flags[0]) and
 // whether the stream does not fit (flags[1]); every tile writes its escape
 // count, so nothing has to be cleared before the pass.
-__global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, int kind, uint64_t cap,
-                                                           const uint32_t *__restrict__ seg_off,
+template <bool kDgc>
+__global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, uint64_t cap, const uint32_t *__restrict__ seg_off,
                                                            const float *__restrict__ seg_scale,
                                                            const uint32_t *__restrict__ idx,
-                                                           const float *__restrict__ val, uint32_t MAX,
-                                                           uint8_t *__restrict__ out, uint64_t out_cap,
-                                                           uint64_t *__restrict__ out_bytes, PackWs w) {
-    const bool dgc = kind == GC_KIND_DGC;
+                                                           const float *__restrict__ val, uint8_t *__restrict__ out,
+                                                           uint64_t out_cap, uint64_t *__restrict__ out_bytes,
+                                                           PackWs w) {
+    constexpr bool dgc = kDgc;
+    constexpr int kind = kDgc ? GC_KIND_DGC : GC_KIND_ADACOMP;
     __shared__ FuseLds L;
     uint32_t ntiles;
     const uint64_t bytes = fused_layout(P, dgc, cap, seg_off, L, &ntiles);
@@ -607,7 +621,7 @@ __global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, int kind, 
     if (!fits) return;
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const TileGeom g = fused_tile(P, L, t, nullptr);
-        (void)tile_write(g, t, dgc, idx, val, MAX, out, w);
+        (void)tile_write<kDgc>(g, t, idx, val, out, w);
         __syncthreads();
     }
 }
@@ -616,14 +630,15 @@ __global__ __launch_bounds__(kBlock) void pack_main_kernel(PlanDev P, int kind, 
 // tile counts).  Otherwise every workgroup lays the stream out again with
 // each segment's escapes (the relayout of the plan path), workgroup 0
 // rewrites the headers and the length, and the tiles are written again.
-__global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, int kind, uint64_t cap,
-                                                          const uint32_t *__restrict__ seg_off,
+template <bool kDgc>
+__global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, uint64_t cap, const uint32_t *__restrict__ seg_off,
                                                           const float *__restrict__ seg_scale,
                                                           const uint32_t *__restrict__ idx,
-                                                          const float *__restrict__ val, uint32_t MAX,
-                                                          uint8_t *__restrict__ out, uint64_t out_cap,
-                                                          uint64_t *__restrict__ out_bytes, PackWs w) {
-    const bool dgc = kind == GC_KIND_DGC;
+                                                          const float *__restrict__ val, uint8_t *__restrict__ out,
+                                                          uint64_t out_cap, uint64_t *__restrict__ out_bytes,
+                                                          PackWs w) {
+    constexpr bool dgc = kDgc;
+    constexpr uint32_t MAX = kDgc ? 65535u : 32767u;
     // the tiles' escape bytes (sixteen per load, over the workspace's whole
     // table) in the same round of loads as the tile count; bytes past the
     // count are not this call's
@@ -703,7 +718,7 @@ __global__ __launch_bounds__(kBlock) void pack_fix_kernel(PlanDev P, int kind, u
     if (!fits) return;
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const TileGeom g = fused_tile(P, L, t, esc);
-        tile_rewrite(g, t, dgc, idx, val, MAX, out, w);
+        tile_rewrite<kDgc>(g, t, idx, val, out, w);
         __syncthreads();
     }
 }
@@ -749,6 +764,38 @@ extern "C" uint64_t gc_dgc_pack_bound(const gc_plan *plan, const gc_dgc_options 
     });
 }
 
+template <bool kDgc>
+static gc_status pack_launch(const gc_plan *plan, const PlanDev &P, const gc_sparse *in, uint8_t *out,
+                             uint64_t out_cap, uint64_t *out_bytes, const PackWs &w, uint32_t MAX, unsigned grid,
+                             hipStream_t stream) {
+    constexpr int kind = kDgc ? GC_KIND_DGC : GC_KIND_ADACOMP;
+    const uint64_t cap = in->cap;
+    if (plan->nseg <= kFuseSegs) {
+        // few segments: every workgroup lays the stream out itself; the fix
+        // pass only reads the tile counts unless a tile has escapes.  The
+        // main pass keeps its workgroups resident: each lays the stream out
+        // once, then loops over tiles.
+        grid = std::min(grid, resident_blocks(reinterpret_cast<const void *>(pack_main_kernel<kDgc>)));
+        const unsigned fgrid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, 256));
+        GC_LAUNCH("pack_main", stream, pack_main_kernel<kDgc><<<grid, kBlock, 0, stream>>>(P, cap, in->seg_off, in->seg_scale,
+                                                                                           in->idx, in->val, out, out_cap,
+                                                                                           out_bytes, w));
+        GC_LAUNCH("pack_fix", stream, pack_fix_kernel<kDgc><<<fgrid, kBlock, 0, stream>>>(P, cap, in->seg_off, in->seg_scale,
+                                                                                          in->idx, in->val, out, out_cap,
+                                                                                          out_bytes, w));
+    } else {
+        GC_LAUNCH("pack_plan", stream, pack_plan_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale, out,
+                                                                                 out_cap, out_bytes, w));
+        GC_LAUNCH("pack_write", stream, pack_write_kernel<false, kDgc><<<grid, kBlock, 0, stream>>>(P, in->idx, in->val, out, w));
+        GC_LAUNCH("pack_relayout", stream, pack_relayout_kernel<<<1, kBlock, 0, stream>>>(P, kind, MAX, in->seg_scale, out, out_cap,
+                                                                                         out_bytes, w));
+        GC_LAUNCH("pack_rewrite", stream, pack_write_kernel<true, kDgc><<<grid, kBlock, 0, stream>>>(P, in->idx, in->val, out, w));
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_error(e, "gc_pack launch");
+    return GC_OK;
+}
+
 extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in, uint8_t *out,
                              uint64_t out_cap, uint64_t *out_bytes, void *ws, size_t ws_bytes,
                              hipStream_t stream) {
@@ -774,7 +821,6 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
     if (st != GC_OK) return st;
     PackWs w = pack_layout(plan, ws, nullptr);
     const uint32_t MAX = kind == GC_KIND_DGC ? 65535u : 32767u;
-    const uint64_t cap = in->cap;
     // One tile per workgroup up to kTileGrid tiles (each tile is a chain of
     // dependent loads, so tiles run side by side rather than in sequence);
     // workgroups past the actual tile count exit at once.  A DGC message
@@ -788,29 +834,8 @@ extern "C" gc_status gc_pack(const gc_plan *plan, int kind, const gc_sparse *in,
         for (const auto &s : plan->seg) ktiles += ceil_div(s.k, kTile);
         want = std::max<size_t>(2 * ktiles, 256);
     }
-    unsigned grid = static_cast<unsigned>(std::min({w.max_tiles, want, kTileGrid}));
-    if (plan->nseg <= kFuseSegs) {
-        // the main pass keeps its workgroups resident: each lays the stream
-        // out once, then loops over tiles
-        grid = std::min(grid, resident_blocks(reinterpret_cast<const void *>(pack_main_kernel)));
-        // few segments: every workgroup lays the stream out itself; the fix
-        // pass only reads the tile counts unless a tile has escapes
-        const unsigned fgrid = static_cast<unsigned>(std::min<size_t>(w.max_tiles, 256));
-        GC_LAUNCH("pack_main", stream, pack_main_kernel<<<grid, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale,
-                                                                                     in->idx, in->val, MAX, out, out_cap,
-                                                                                     out_bytes, w));
-        GC_LAUNCH("pack_fix", stream, pack_fix_kernel<<<fgrid, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale,
-                                                                                       in->idx, in->val, MAX, out, out_cap,
-                                                                                       out_bytes, w));
-    } else {
-        GC_LAUNCH("pack_plan", stream, pack_plan_kernel<<<1, kBlock, 0, stream>>>(P, kind, cap, in->seg_off, in->seg_scale, out,
-                                                                                 out_cap, out_bytes, w));
-        GC_LAUNCH("pack_write", stream, pack_write_kernel<false><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
-        GC_LAUNCH("pack_relayout", stream, pack_relayout_kernel<<<1, kBlock, 0, stream>>>(P, kind, MAX, in->seg_scale, out, out_cap,
-                                                                                         out_bytes, w));
-        GC_LAUNCH("pack_rewrite", stream, pack_write_kernel<true><<<grid, kBlock, 0, stream>>>(P, kind, in->idx, in->val, MAX, out, w));
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_error(e, "gc_pack launch");
-    return GC_OK;
+    const unsigned grid = static_cast<unsigned>(std::min({w.max_tiles, want, kTileGrid}));
+    if (kind == GC_KIND_DGC) return pack_launch<true>(plan, P, in, out, out_cap, out_bytes, w, MAX, grid, stream);
+    return pack_launch<false>(plan, P, in, out, out_cap, out_bytes, w, MAX, grid, stream);
 }
+
