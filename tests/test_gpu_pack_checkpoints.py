@@ -1,0 +1,94 @@
+"""GPU packing of streams whose blocks hold more than one tile of 4096
+codes: the hand-derived checkpoint cases (a second checkpoint; a checkpoint
+that falls on an escape, which the fix pass writes), and a long DGC segment
+whose escapes fall at many places among 70 tiles.  The bytes equal the
+oracle's, and the GPU reader gives back the message."""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_compression_dnn_amd import binding as B
+from gradient_compression_dnn_amd import workloads as W
+from tests.gpu_util import HipPath, dev, same_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def message(plan, idx, val, seg_off, scale):
+    n = len(idx)
+    return B.Sparse(torch.from_numpy(np.asarray(idx, np.uint32).view(np.int32).copy()).to(dev()),
+                    torch.from_numpy(np.asarray(val, np.float32).copy()).to(dev()),
+                    torch.from_numpy(np.asarray(seg_off, np.uint32).view(np.int32).copy()).to(dev()),
+                    torch.from_numpy(np.asarray(scale, np.float32).copy()).to(dev()), n)
+
+
+def unpack_back(plan, kind, data, cap):
+    buf = torch.from_numpy(np.frombuffer(data, np.uint8).copy()).to(dev())
+    out = B.Sparse.empty(plan, cap, dev())
+    st = torch.full((1,), -1, dtype=torch.int32, device=dev())
+    B.gc_unpack(plan, kind, buf, len(data), out, st, plan.workspace(B.GC_OP_UNPACK, dev()))
+    torch.cuda.synchronize()
+    return int(st.item()), out.host()
+
+
+def check(t, kind, idx, val, seg_off, scale, what):
+    hp = HipPath(t)
+    msg = message(hp.plan, idx, val, seg_off, scale)
+    say(f"pack checkpoints: {what}")
+    data = hp.pack(kind, msg)
+    want = oracle.pack(kind, t, idx, val, seg_off, scale)
+    assert len(data) == len(want) and data == want, what
+    st, (gi, gv, go, gs) = unpack_back(hp.plan, kind, data, len(idx))
+    assert st == 0, what
+    assert np.array_equal(gi, np.asarray(idx, np.uint32)) and np.array_equal(go, np.asarray(seg_off, np.uint32))
+    if kind == 1:
+        assert same_bits(gv, np.asarray(val, np.float32))
+    return data
+
+
+def test_hand_checkpoint_cases(golden_dir):
+    with open(os.path.join(golden_dir, "pack_hand.json")) as f:
+        cases = json.load(f)["checkpoint_cases"]
+    for c in cases:
+        (off, n), = c["segments"]
+        if c["kind"] == 2:
+            idx = np.arange(0, 10000, 2)
+            scale = [c["scale"]]
+        else:
+            idx = np.concatenate([np.arange(4096), [74096]])
+            scale = [0.0]
+        t = W.make_table([n], [1], [len(idx)], [off])
+        val = np.full(len(idx), c["value"], np.float32)
+        data = check(t, c["kind"], idx, val, [0, len(idx)], scale, c["name"])
+        assert len(data) == c["expect_bytes"]
+        E = struct.unpack_from("<I", data, 24)[0]
+        ck = 32 + 16 + 2 * E + 2 * (E % 2) + (4 * E if c["kind"] == 1 else 0)
+        got = [list(struct.unpack_from("<II", data, ck + 8 * i)) for i in range(-(-E // 4096))]
+        assert got == c["expect_checkpoints"], c["name"]
+
+
+def test_escapes_among_many_tiles():
+    # one DGC segment of 12M elements: 70 runs of 4096 + r entries, each run
+    # 70,000 elements after the previous one (one escape before each run),
+    # so escapes fall at many offsets inside the 4096-code tiles; and an
+    # AdaComp segment with the same layout (MAX 32767: two escapes per gap)
+    rng = np.random.default_rng(77)
+    n = 12_000_000
+    parts, at = [], 5
+    for _ in range(70):
+        run = 4096 + int(rng.integers(-2000, 2000))
+        parts.append(at + np.arange(run))
+        at += run + 70_000
+    idx = np.concatenate(parts)
+    assert idx[-1] < n
+    val = W.random_values(rng, idx.size, "laplace")
+    t = W.make_table([n], [1], [idx.size], [0])
+    check(t, 1, idx, val, [0, idx.size], [0.0], "DGC, escapes among 70 tiles")
+    scale = np.float32(0.375)
+    check(t, 2, idx, np.where(val < 0, -scale, scale).astype(np.float32), [0, idx.size], [scale],
+          "AdaComp, escapes among 70 tiles")
