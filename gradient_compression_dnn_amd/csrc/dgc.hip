@@ -8,11 +8,16 @@
 //   explorer (top-k of random keys outside the core) through the same
 //   kernels, with the key source chosen by a template mode.
 //
-// Launch sequence.  Chunk kernels run one workgroup (or one wave) per
-// 4096-element chunk of a segment; segment kernels one workgroup per segment.
-// Chunk kernels hand results to segment kernels through global memory at
-// kernel boundaries only (no cross-workgroup fences, which on gfx950 write
-// back the XCD's L2).
+// Two launch sequences.  Exact selection at the pages' densities (every
+// tensor of more than one chunk keeps at most 1/512 of its entries) takes
+// the exact path described further down: norm, prepare, update, collect,
+// select, emit.  Denser exact selections (warm-up, Slim-DP's core) and the
+// sampled threshold take the candidate kernels below.  Chunk kernels run
+// one workgroup (or one wave) per 4096-element chunk of a segment; segment
+// kernels one workgroup per segment.  Chunk kernels hand results to segment
+// kernels through global memory at kernel boundaries only (no cross-
+// workgroup fences, which on gfx950 write back the XCD's L2).  The
+// candidate sequence:
 //   norm    (chunk, clip only) pairwise fp64 sum of G^2 over the chunk
 //   prep    (segment) clear the segment's histograms; finish the pairwise
 //           tree over the chunk sums and set the clip factor
