@@ -92,3 +92,25 @@ def test_escapes_among_many_tiles():
     scale = np.float32(0.375)
     check(t, 2, idx, np.where(val < 0, -scale, scale).astype(np.float32), [0, idx.size], [scale],
           "AdaComp, escapes among 70 tiles")
+
+
+@pytest.mark.parametrize("nseg", [512, 513])
+def test_both_pack_paths_at_the_segment_boundary(nseg):
+    # up to 512 segments every workgroup lays the stream out itself; past it a
+    # plan pass does: both must write the oracle's bytes, escapes included
+    rng = np.random.default_rng(500 + nseg)
+    lengths = [int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(70_000, 140_000))])) for _ in range(nseg)]
+    t = W.make_table(lengths, [50] * nseg, [max(1, n // 700) for n in lengths], [int(rng.integers(0, 3)) for _ in lengths])
+    hp = HipPath(t)
+    parts, offs, pos = [], [0], 0
+    for o, ln, _, k in t:
+        parts.append(np.sort(rng.choice(ln, int(k), replace=False)) + o)
+        pos += int(k)
+        offs.append(pos)
+    idx = np.concatenate(parts).astype(np.uint32)
+    val = W.random_values(rng, idx.size, "laplace")
+    check(t, 1, idx, val, offs, np.zeros(nseg, np.float32), f"DGC, {nseg} segments")
+    scale = np.abs(W.random_values(rng, nseg, "normal")) + np.float32(0.5)
+    seg_of = np.repeat(np.arange(nseg), np.diff(offs))
+    aval = np.where(val < 0, -scale[seg_of], scale[seg_of]).astype(np.float32)
+    check(t, 2, idx, aval, offs, scale.astype(np.float32), f"AdaComp, {nseg} segments")
