@@ -114,3 +114,57 @@ def test_both_pack_paths_at_the_segment_boundary(nseg):
     seg_of = np.repeat(np.arange(nseg), np.diff(offs))
     aval = np.where(val < 0, -scale[seg_of], scale[seg_of]).astype(np.float32)
     check(t, 2, idx, aval, offs, scale.astype(np.float32), f"AdaComp, {nseg} segments")
+
+
+@pytest.mark.parametrize("nseg", [3, 600])
+def test_malformed_messages_stay_in_bounds(nseg):
+    """Messages that break gc_pack's contract (offsets that go back, a
+    segment holding more entries than its length, descending indices,
+    indices outside their segment, a count past the capacity): the call
+    completes, writes nothing past out_cap, and reports a length the format
+    allows for entries clamped to their segments."""
+    rng = np.random.default_rng(900 + nseg)
+    lengths = [int(rng.integers(50, 3000)) for _ in range(nseg)]
+    lengths[0] = 200_000
+    t = W.make_table(lengths, [1] * nseg, [max(1, n // 10) for n in lengths])
+    hp = HipPath(t)
+    n = W.table_extent(t)
+    offs = [0]
+    for o, ln, _, k in t:
+        offs.append(offs[-1] + int(k))
+    # the message has room for 8,192 more entries than the offsets use, so
+    # that a segment can claim more entries than its length
+    idx = np.concatenate([np.sort(rng.choice(ln, int(k), replace=False)) + o for o, ln, _, k in t]
+                         + [rng.integers(0, n, 8192)]).astype(np.uint32)
+    cap = idx.size
+    val = W.random_values(rng, cap, "laplace")
+    cases = {}
+    o = np.array(offs, np.uint32)
+    back = o.copy(); back[2] = back[1] - 3 if back[1] >= 3 else 0          # segment 1 ends before it starts
+    cases["offsets go back"] = (idx, back)
+    over = o.copy(); over[2:] = over[2:] + 2 * lengths[1]                   # segment 1 holds past its length
+    assert over[2] - over[1] > lengths[1]
+    cases["more than the length"] = (idx, over)
+    desc = idx.copy(); desc[o[0]:o[1]] = desc[o[0]:o[1]][::-1]             # descending in segment 0
+    cases["descending"] = (desc, o)
+    outside = idx.copy(); outside[o[1]:o[2]] = n + 5                      # past every segment
+    cases["outside the segments"] = (outside, o)
+    past = o.copy(); past[-1] = cap + 10_000                               # count past the capacity
+    cases["count past the capacity"] = (idx, past)
+    room = 4096
+    for name, (ci, co) in cases.items():
+        for kind in (1, 2):
+            say(f"pack malformed ({nseg} segments): {name}, kind {kind}")
+            msg = message(hp.plan, ci, val if kind == 1 else np.sign(val).astype(np.float32), co,
+                          np.ones(nseg, np.float32))
+            bound = hp.plan.pack_bound(kind) if kind == 2 else B.gc_dgc_pack_bound(hp.plan, B.dgc_options(0.9, density=(1, 1)))
+            buf = torch.full((bound + room,), 0xA5, dtype=torch.uint8, device=dev())
+            nb = torch.zeros(1, dtype=torch.int64, device=dev())
+            B.gc_pack(hp.plan, kind, msg, buf[:bound], nb, hp.workspace(B.GC_OP_PACK))
+            torch.cuda.synchronize()
+            data = buf.cpu().numpy()
+            assert np.all(data[bound:] == 0xA5), f"{name}: wrote past out_cap"
+            nbytes = int(nb.item())
+            assert 16 + 16 * nseg <= nbytes, name
+            if nbytes <= bound:
+                assert data[:4].tobytes() == b"GCP2", name
