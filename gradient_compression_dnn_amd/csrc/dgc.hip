@@ -672,17 +672,21 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                     run += pc[j * kWaves + ww];
                 }
             if (threadIdx.x == 0) w.ccount[c] = run;
-            const uint32_t slot0 = kFine ? (c << kChunkLog2) : static_cast<uint32_t>(ci.lo);
+            // the staging area: the chunk's first element, or its own slot
+            // (64-bit: a plan may hold more than 2^20 chunks)
+            const size_t slot0 = kFine ? (size_t(c) << kChunkLog2) : size_t(ci.lo);
+            uint32_t *const sidx = w.sidx + slot0;
+            float *const sval = w.sval + slot0;
 #pragma unroll
             for (int j = 0; j < kRows; ++j) {
                 if (!flags[j]) continue;
-                uint32_t slot = slot0 + base[j] + before[j];
+                uint32_t slot = base[j] + before[j];
                 const uint32_t e0 = static_cast<uint32_t>(ci.lo) + row_elem(j);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if ((flags[j] >> q) & 1u) {
-                        w.sidx[slot] = e0 + q;
-                        w.sval[slot] = v[j][q];
+                        sidx[slot] = e0 + q;
+                        sval[slot] = v[j][q];
                         ++slot;
                         if (kFine)
                             atomicAdd(xtables(w, ci.s) + min((mag_key(v[j][q]) - Lkey) >> fs, kFineBins - 1), 1u);

@@ -232,6 +232,78 @@ def test_dgc_on_the_longest_segment_by_its_properties():
     assert bool((dense[:base] == 3.0).all())  # before the segment: untouched
 
 
+def test_dgc_past_two_to_the_twenty_chunks():
+    """A plan of more than 2^20 chunks: one segment of GC_MAX_SEGMENT_LEN
+    (2^20 - 64 chunks) and then 200 one-chunk segments, so the later chunks'
+    staging slots (chunk number times 4096) pass 2^32 entries.  The small
+    segments are compared with the oracle (rebased), and the long segment's
+    message with V' computed at its indices (no clipping: V' = V + (m U + G)
+    with each operation rounded once)."""
+    L0 = B.GC_MAX_SEGMENT_LEN
+    k0 = W.topk_count(L0)
+    n_small = 200
+    lengths = [1000 + i for i in range(n_small)]
+    local = W.make_table(lengths, [50] * n_small, [W.topk_count(n, 3) for n in lengths],
+                         [0] + [13] * (n_small - 1))
+    window = W.table_extent(local)
+    base = L0 + 5
+    assert base + window <= N_TOTAL
+    top = local.copy()
+    top[:, 0] += base
+    table = np.vstack([np.array([[0, L0, 4096, k0]], dtype=np.int64), top])
+    plan = B.Plan(table, N_TOTAL)
+    assert (L0 + 4095) // 4096 + n_small > 1 << 20
+    rng = np.random.default_rng(5)
+    G, U, V = (W.random_values(rng, window, "laplace") for _ in range(3))
+    m = 0.9
+    Gd, Ud, Vd = big(), big(), big()
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    SL = 1 << 28
+    for a in range(0, L0, SL):
+        b = min(a + SL, L0)
+        Gd[a:b] = torch.randn(b - a, generator=gen, device="cuda") * 1e-3
+        Ud[a:b] = torch.randn(b - a, generator=gen, device="cuda") * 1e-3
+        Vd[a:b] = torch.randn(b - a, generator=gen, device="cuda") * 1e-3
+    ws = plan.workspace(B.GC_OP_DGC, "cuda")
+    for sampled in (False, True):
+        say(f"past 2^20 chunks: dgc sampled={sampled}")
+        put(Gd, base, G)
+        put(Ud, base, U)
+        put(Vd, base, V)
+        opt = B.dgc_options(m, 0.0, 1, sampled=sampled, sample_period=7, over=2)
+        cap = B.gc_dgc_message_cap(plan, opt)
+        msg = B.Sparse.empty(plan, cap, "cuda")
+        g_before, u_before, v_before = Gd[:L0], Ud[:L0].clone(), Vd[:L0].clone()
+        B.gc_dgc_step_ex(plan, Gd, Ud, Vd, opt, msg, ws)
+        torch.cuda.synchronize()
+        Uo, Vo, idx, val, off, _ = oracle.dgc_ex(local, G, U, V, m, 0.0, 1, sampled=sampled,
+                                                 sample_period=7, over=2)
+        go = msg.seg_off.cpu().numpy().view(np.uint32)
+        n0 = int(go[1])
+        # the small segments
+        assert np.array_equal(go[1:].astype(np.int64) - n0, off.astype(np.int64))
+        gi = (msg.idx[n0:n0 + int(off[-1])].cpu().numpy().view(np.uint32)).astype(np.int64)
+        gv = msg.val[n0:n0 + int(off[-1])].cpu().numpy()
+        assert np.array_equal(gi, idx.astype(np.int64) + base)
+        assert same_bits(gv, val)
+        assert same_bits(get(Ud, base, window), Uo) and same_bits(get(Vd, base, window), Vo)
+        # the long segment: its own entries, ascending, carrying V' before masking
+        if not sampled:
+            assert n0 == k0
+        i0 = msg.idx[:n0].long() & 0xFFFFFFFF
+        assert bool((i0[1:] > i0[:-1]).all()) and int(i0[-1]) < L0
+        m32 = float(np.float32(m))
+        want = v_before[i0] + (u_before[i0] * m32 + g_before[i0])
+        assert torch.equal(msg.val[:n0].view(torch.int32), want.view(torch.int32))
+        assert not bool(Ud[i0].view(torch.int32).any()) and not bool(Vd[i0].view(torch.int32).any())
+        # restore the long segment's state for the next selection
+        Ud[:L0] = u_before
+        Vd[:L0] = v_before
+        del u_before, v_before, msg
+        pygc.collect()
+        torch.cuda.empty_cache()
+
+
 def test_dcd_decode_and_mix_at_the_largest_n():
     """DCD over the largest n the calls accept (2^32 - 8192, indices and
     Philox counters up to the top of the u32 range): windows at the start,
