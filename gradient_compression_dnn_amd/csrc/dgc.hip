@@ -211,6 +211,38 @@ struct ChunkInfo {
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return dev_f2u(v) & 0x7FFFFFFFu; }
 
+// Global histogram increments aggregated over a wave.  add() is called by
+// the whole wave (full exec mask) with a wave-uniform histogram: the lanes
+// that add to one bin become one count, and counts to the same bin of the
+// same histogram accumulate over calls until another bin comes or flush()
+// (lane 0 issues the atomic).  Keys that crowd into one bin (a tensor of
+// zeros, a constant tensor) then cost one atomic per run of calls instead of
+// one per key: one global address takes about one atomic per 10 ns, so a
+// 20M-element tensor of zeros took 235 ms with an atomic per key.
+struct WaveHist {
+    uint32_t *h = nullptr;
+    uint32_t bin = 0, cnt = 0;
+    __device__ __forceinline__ void flush() {
+        if (cnt != 0 && lane_id() == 0) atomicAdd(h + bin, cnt);
+        cnt = 0;
+    }
+    __device__ __forceinline__ void add(uint32_t *hist, bool f, uint32_t b) {
+        uint64_t todo = __ballot(f);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), leader));
+            const uint64_t same = __ballot(f && b == lb) & todo;
+            if (hist != h || lb != bin) {
+                flush();
+                h = hist;
+                bin = lb;
+            }
+            cnt += static_cast<uint32_t>(__popcll(same));
+            todo &= ~same;
+        }
+    }
+};
+
 // Slim-DP significance (Slim-DP §3.2, a weighted sum of the magnitudes of
 // the parameter and of its gradient): fl(|w| + fl(c |g|)).
 __device__ __forceinline__ float significance(float w, float g, float c) {
@@ -623,6 +655,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
     fetch(ci);
     __syncthreads();
     const int lane = lane_id(), wave = wave_id();
+    WaveHist fine;  // the exact path's fine histogram
     for (uint32_t c = c0; c < c1; ++c) {
         const float clip = kDgc ? w.st[ci.s].clip : 1.0f;
         const uint32_t Lkey = w.st[ci.s].Lkey;
@@ -677,20 +710,25 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
             const size_t slot0 = kFine ? (size_t(c) << kChunkLog2) : size_t(ci.lo);
             uint32_t *const sidx = w.sidx + slot0;
             float *const sval = w.sval + slot0;
+            uint32_t *const xt = xtables(w, ci.s);
 #pragma unroll
             for (int j = 0; j < kRows; ++j) {
-                if (!flags[j]) continue;
-                uint32_t slot = base[j] + before[j];
-                const uint32_t e0 = static_cast<uint32_t>(ci.lo) + row_elem(j);
+                if (flags[j]) {
+                    uint32_t slot = base[j] + before[j];
+                    const uint32_t e0 = static_cast<uint32_t>(ci.lo) + row_elem(j);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if ((flags[j] >> q) & 1u) {
-                        sidx[slot] = e0 + q;
-                        sval[slot] = v[j][q];
-                        ++slot;
-                        if (kFine)
-                            atomicAdd(xtables(w, ci.s) + min((mag_key(v[j][q]) - Lkey) >> fs, kFineBins - 1), 1u);
+                    for (int q = 0; q < 4; ++q) {
+                        if ((flags[j] >> q) & 1u) {
+                            sidx[slot] = e0 + q;
+                            sval[slot] = v[j][q];
+                            ++slot;
+                        }
                     }
+                }
+                if (kFine) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        fine.add(xt, (flags[j] >> q) & 1u, min((mag_key(v[j][q]) - Lkey) >> fs, kFineBins - 1));
                 }
             }
         }
@@ -711,6 +749,30 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                 }
             }
             __syncthreads();
+        }
+    }
+    if (kFine) {
+        // the waves' last counts, combined in the workgroup (in a tensor of
+        // zeros every wave ends on the same bin)
+        __shared__ uint32_t *fh[kWaves];
+        __shared__ uint32_t fbin[kWaves], fcnt[kWaves];
+        if (lane == 0) {
+            fh[wave] = fine.h;
+            fbin[wave] = fine.bin;
+            fcnt[wave] = fine.cnt;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 0; i < kWaves; ++i) {
+                if (fcnt[i] == 0) continue;
+                uint32_t n = fcnt[i];
+                for (int j = i + 1; j < kWaves; ++j)
+                    if (fcnt[j] != 0 && fh[j] == fh[i] && fbin[j] == fbin[i]) {
+                        n += fcnt[j];
+                        fcnt[j] = 0;
+                    }
+                atomicAdd(fh[i] + fbin[i], n);
+            }
         }
     }
 }
@@ -869,6 +931,21 @@ __device__ __forceinline__ void for_staged_keys(const DgcWs &w, uint32_t lo, uin
     }
 }
 
+// The same walk with the whole wave in every call: f(valid, key), valid
+// false for the lanes past n (for WaveHist, whose ballots need every lane).
+template <typename F>
+__device__ __forceinline__ void for_staged_keys_wave(const DgcWs &w, uint32_t lo, uint32_t n, uint32_t k0, F &&f) {
+    const uint32_t lane = lane_id();
+    f(lane < n, k0);
+    for (uint32_t i0 = kWave; i0 < n; i0 += 4 * kWave) {
+        uint32_t key[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[q] = mag_key(w.sval[lo + min(i0 + q * kWave + lane, n - 1)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f(i0 + q * kWave + lane < n, key[q]);
+    }
+}
+
 // ----------------------------------------------------------------- stage
 // Normally the update staged every candidate: the wave histograms digit 2 of
 // the staged entries whose digit 1 is d1.  In a re-staged segment it re-reads
@@ -909,6 +986,7 @@ __device__ __forceinline__ void stage_chunk_again(const PlanDev &P, const Src &a
             explore_values(a, seg, s, (rec.w << kChunkLog2) + r * (4 * kWave) + 4u * lane, v[r]);
     }
     uint32_t run = 0;  // wave-uniform count of entries staged so far
+    WaveHist wh;
 #pragma unroll
     for (int r = 0; r < kWaveRows; ++r) {
         const uint32_t e0 = r * (4 * kWave) + 4u * lane;
@@ -920,7 +998,7 @@ __device__ __forceinline__ void stage_chunk_again(const PlanDev &P, const Src &a
             const uint32_t key = mag_key(v[r][q]);
             const uint32_t dig1 = key >> (kDigit2Bits + kDigit3Bits);
             flag[q] = in && dig1 >= d1;
-            if (in && dig1 == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            wh.add(h2, in && dig1 == d1, (key >> kDigit3Bits) & (kHist2 - 1));
             const uint64_t m = __ballot(flag[q]);
             before += lane_rank(m);
             row_total += static_cast<uint32_t>(__popcll(m));
@@ -938,6 +1016,7 @@ __device__ __forceinline__ void stage_chunk_again(const PlanDev &P, const Src &a
         }
         run += row_total;
     }
+    wh.flush();
     if (lane == 0) w.ccount[c] = run;
 }
 
@@ -953,6 +1032,7 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, Dgc
     for (uint32_t j = 0; j < CPW; ++j) k0[j] = redo_only ? 0u : first_key(w, wc, j);
     auto hist2_of = [&](uint32_t c, uint32_t s) { return w.hist2 + (size_t(s) * kHistRep + c % kHistRep) * kHist2; };
     if (!redo_only) {
+        WaveHist wh;
 #pragma unroll
         for (uint32_t j = 0; j < CPW; ++j) {
             const uint32_t c = c0 + j;
@@ -960,10 +1040,11 @@ __global__ __launch_bounds__(kBlock) void dgc_stage_kernel(PlanDev P, Src a, Dgc
             if (lane_val(all_l, j) || lane_val(redo_l, j)) continue;
             const uint32_t d1 = lane_val(d1_l, j);
             uint32_t *h2 = hist2_of(c, lane_val(wc.rec.z, j));
-            for_staged_keys(w, lane_val(wc.rec.x, j), lane_val(wc.n, j), k0[j], [&](uint32_t, uint32_t key) {
-                if ((key >> (kDigit2Bits + kDigit3Bits)) == d1) atomicAdd(&h2[(key >> kDigit3Bits) & (kHist2 - 1)], 1u);
+            for_staged_keys_wave(w, lane_val(wc.rec.x, j), lane_val(wc.n, j), k0[j], [&](bool valid, uint32_t key) {
+                wh.add(h2, valid && (key >> (kDigit2Bits + kDigit3Bits)) == d1, (key >> kDigit3Bits) & (kHist2 - 1));
             });
         }
+        wh.flush();
     }
     // re-staged segments (the fallback): one chunk at a time
 #pragma unroll 1
@@ -1036,6 +1117,7 @@ __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) 
     uint32_t k0[CPW];
 #pragma unroll
     for (uint32_t j = 0; j < CPW; ++j) k0[j] = first_key(w, wc, j);
+    WaveHist wh;
 #pragma unroll
     for (uint32_t j = 0; j < CPW; ++j) {
         if (c0 + j >= P.ndchunk) break;
@@ -1043,10 +1125,11 @@ __global__ __launch_bounds__(kBlock) void dgc_refine_kernel(PlanDev P, DgcWs w) 
         if (n == 0 || lane_val(all_l, j)) continue;
         const uint32_t prefix = lane_val(prefix_l, j);
         uint32_t *h3 = w.hist3 + size_t(lane_val(wc.rec.z, j)) * kHist3;
-        for_staged_keys(w, lane_val(wc.rec.x, j), n, k0[j], [&](uint32_t, uint32_t key) {
-            if ((key >> kDigit3Bits) == prefix) atomicAdd(&h3[key & (kHist3 - 1)], 1u);
+        for_staged_keys_wave(w, lane_val(wc.rec.x, j), n, k0[j], [&](bool valid, uint32_t key) {
+            wh.add(h3, valid && (key >> kDigit3Bits) == prefix, key & (kHist3 - 1));
         });
     }
+    wh.flush();
 }
 
 template <uint32_t CPW>
@@ -1524,7 +1607,8 @@ __device__ __forceinline__ uint32_t sel_radix(uint32_t rank, Each each, uint32_t
 // row of skey (select gathers the rows; a chunk with more in the bin is read
 // again there).  Segments whose selection takes a slower branch of select
 // (fewer than k staged keys, b* the last bin, or more keys in b* than the
-// list holds) are skipped.  Each wave reads the first 64 staged keys of its
+// list holds) are skipped, and so are those where every staged key equals T
+// (bins of one key, all of them in b*).  Each wave reads the first 64 staged keys of its
 // chunks with their counts, before b* is known (a chunk's 4096-entry slot is
 // always there to read; keys past the staged count are ignored).  (Appending
 // the bin's keys to one list per segment through a shared counter, or
@@ -1577,7 +1661,9 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
     }
     __syncthreads();
     const FineBin fb = sh_fb;
-    if (!fb.ok) return;
+    // nothing to collect: T's bin unusable here, or (bins of one key) every
+    // staged key in T's bin, where select takes each chunk's staged count
+    if (!fb.ok || (fs == 0 && fb.in == total)) return;
 #pragma unroll
     for (uint32_t j = 0; j < kXCollectCpw; ++j) {
         const uint32_t c = c0 + j;
