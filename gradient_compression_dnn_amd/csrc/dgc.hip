@@ -79,6 +79,7 @@ struct SegState {
     uint32_t base;  // first message slot of the segment
     uint32_t qrank, qprefix;  // sampled selection: quantile search state
     uint32_t fshift;          // exact path: fine bins above Lkey are 2^fshift keys wide
+    uint32_t hkey;            // sampled selection on the exact path: the largest sample key
 };
 
 // What the selection kernels rank (the key is the magnitude bits of a value):
@@ -136,9 +137,10 @@ __device__ __forceinline__ uint32_t sample_stride(uint32_t dnchunk) {
 constexpr uint32_t kHistRep = 16;
 static_assert(kHist1 == kHist2, "the sample bound reuses one LDS histogram for digits 1 and 2");
 
-// Exact path (DGC, exact selection): the staged keys are binned in
-// kFineBins bins of 2^fshift keys above the staging bound Lkey (the last bin
-// takes every key above the range).
+// Exact path (DGC, exact selection, and sampled selection on its kernels):
+// the staged keys are binned in kFineBins bins above the staging bound Lkey,
+// Lkey alone in the first and 2^fshift keys in each of the others (the last
+// bin takes every key above the range).
 constexpr uint32_t kFineBins = kHist1;
 // Its fine histogram of the staged keys (the update adds each key) is kept
 // in the segment's digit-1 area; the keys in T's fine bin are gathered into
@@ -174,6 +176,26 @@ __device__ __forceinline__ uint32_t seg_k(const SegDev &seg, const DgcWs &w) {
 // The exact path's fine histogram of segment s.
 __device__ __forceinline__ uint32_t *xtables(const DgcWs &w, uint32_t s) {
     return w.hist1 + size_t(s) * kHistRep * kHist1;
+}
+// Fine bins of the staged keys (all >= Lkey): bin 0 holds Lkey itself, bin
+// b >= 1 the 2^fs keys from Lkey + 1 + (b - 1) 2^fs, and the last bin every
+// key above the range.  Lkey has a bin of its own because keys crowd there
+// (a tensor of zeros has Lkey = 0): T in bin 0 is then known without
+// listing the bin's keys, however wide the other bins are.
+__device__ __forceinline__ uint32_t fine_bin(uint32_t key, uint32_t Lkey, uint32_t fs) {
+    return key == Lkey ? 0u : min(((key - Lkey - 1u) >> fs) + 1u, kFineBins - 1);
+}
+// The smallest key of fine bin b (b below the last).
+__device__ __forceinline__ uint32_t fine_lo(uint32_t b, uint32_t Lkey, uint32_t fs) {
+    return b == 0 ? Lkey : Lkey + 1u + ((b - 1u) << fs);
+}
+// Width 2^fs of the fine bins: the narrowest that brings Hkey into a bin
+// below the last.
+__device__ __forceinline__ uint32_t fine_shift(uint32_t Lkey, uint32_t Hkey) {
+    uint32_t fs = 0;
+    if (Hkey > Lkey)
+        while (((Hkey - Lkey - 1u) >> fs) > kFineBins - 3) ++fs;
+    return fs;
 }
 
 DgcWs dgc_layout(const gc_plan *p, void *base, size_t *bytes) {
@@ -332,18 +354,25 @@ __global__ __launch_bounds__(kBlock) void dgc_norm_kernel(PlanDev P, const float
 }
 
 // ------------------------------------------------------------------ prep
+// fine (sampled selection on the exact path): only the fine histogram is
+// cleared, and the segment state the exact path's prepare sets is set here.
 __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, int use_clip,
-                                                          float thr, int zero_q) {
+                                                          float thr, int zero_q, int fine) {
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
     if (zero_q)
         for (int i = threadIdx.x; i < kHist1; i += kBlock) w.qhist[size_t(s) * kHist1 + i] = 0u;
-    uint4 *h4 = reinterpret_cast<uint4 *>(w.hist1 + size_t(s) * kHistRep * kHist1);
-    for (int i = threadIdx.x; i < int(kHistRep * kHist1 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-    h4 = reinterpret_cast<uint4 *>(w.hist2 + size_t(s) * kHistRep * kHist2);
-    for (int i = threadIdx.x; i < int(kHistRep * kHist2 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t *h = w.hist3 + size_t(s) * kHist3;
-    for (int i = threadIdx.x; i < kHist3; i += kBlock) h[i] = 0u;
+    if (fine) {
+        uint4 *x4 = reinterpret_cast<uint4 *>(xtables(w, s));
+        for (int i = threadIdx.x; i < int(kFineBins / 4); i += kBlock) x4[i] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        uint4 *h4 = reinterpret_cast<uint4 *>(w.hist1 + size_t(s) * kHistRep * kHist1);
+        for (int i = threadIdx.x; i < int(kHistRep * kHist1 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+        h4 = reinterpret_cast<uint4 *>(w.hist2 + size_t(s) * kHistRep * kHist2);
+        for (int i = threadIdx.x; i < int(kHistRep * kHist2 / 4); i += kBlock) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t *h = w.hist3 + size_t(s) * kHist3;
+        for (int i = threadIdx.x; i < kHist3; i += kBlock) h[i] = 0u;
+    }
     float cl = 1.0f;
     if (use_clip) {
         const double *part = w.partial + seg.dchunk0;
@@ -351,7 +380,16 @@ __global__ __launch_bounds__(kBlock) void dgc_prep_kernel(PlanDev P, DgcWs w, in
         double norm = sqrt(S);
         if (norm > static_cast<double>(thr)) cl = static_cast<float>(static_cast<double>(thr) / norm);
     }
-    if (threadIdx.x == 0) w.st[s].clip = cl;
+    if (threadIdx.x == 0) {
+        w.st[s].clip = cl;
+        w.st[s].hkey = 0u;  // the sample's largest key, by atomicMax over the qhist workgroups
+        if (fine) {
+            w.st[s].sent = seg.k;
+            w.st[s].base = seg.kbase;
+            w.st[s].redo = 0u;
+            w.st[s].all = 0u;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- sample
@@ -453,7 +491,8 @@ __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t 
     uint32_t rank = sample_rank(S, seg);
     const uint32_t *keys = w.sidx + seg.off;
     __shared__ uint32_t h[kHist1];
-    uint32_t prefix = 0;
+    __shared__ uint32_t wmax[kWaves];
+    uint32_t prefix = 0, kmax = 0;
     for (int level = 0; level < 3; ++level) {
         const int nb = level == 2 ? kHist3 : kHist1;
         const int shift = level == 0 ? kDigit2Bits + kDigit3Bits : level == 1 ? kDigit3Bits : 0;
@@ -468,6 +507,7 @@ __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t 
 #pragma unroll
             for (uint32_t u = 0; u < kB; ++u) {
                 if (j0 + u * kBlock + threadIdx.x >= S) continue;
+                if (level == 0) kmax = max(kmax, key[u]);
                 if (level > 0 && (key[u] >> pshift) != prefix) continue;
                 atomicAdd(&h[(key[u] >> shift) & uint32_t(nb - 1)], 1u);
             }
@@ -480,7 +520,16 @@ __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t 
         prefix = level == 0 ? d : level == 1 ? ((prefix << kDigit2Bits) | d) : ((prefix << kDigit3Bits) | d);
         __syncthreads();
     }
-    if (threadIdx.x == 0) w.st[s].Lkey = prefix;
+    kmax = wave_max_all(kmax);
+    if (lane_id() == 0) wmax[wave_id()] = kmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t hk = 0;
+        for (int i = 0; i < kWaves; ++i) hk = max(hk, wmax[i]);
+        w.st[s].Lkey = prefix;
+        w.st[s].hkey = hk;
+        w.st[s].fshift = fine_shift(prefix, hk);
+    }
 }
 
 // The same radix select spread over kQBlocks workgroups per segment, for
@@ -508,6 +557,7 @@ __global__ __launch_bounds__(kBlock) void dgc_qhist_kernel(PlanDev P, uint32_t p
     __syncthreads();
     const uint32_t *keys = w.sidx + seg.off;
     constexpr uint32_t kB = 8;
+    uint32_t kmax = 0;
     for (uint32_t i0 = j0; i0 < j1; i0 += kB * kBlock) {
         uint32_t key[kB];
 #pragma unroll
@@ -515,8 +565,21 @@ __global__ __launch_bounds__(kBlock) void dgc_qhist_kernel(PlanDev P, uint32_t p
 #pragma unroll
         for (uint32_t u = 0; u < kB; ++u) {
             if (i0 + u * kBlock + threadIdx.x >= j1) continue;
+            if (kLevel == 0) kmax = max(kmax, key[u]);
             if (kLevel > 0 && (key[u] >> pshift) != prefix) continue;
             atomicAdd(&h[(key[u] >> shift) & uint32_t(nb - 1)], 1u);
+        }
+    }
+    if (kLevel == 0) {
+        // the largest sample key (hkey is cleared by prep)
+        __shared__ uint32_t wmax[kWaves];
+        kmax = wave_max_all(kmax);
+        if (lane_id() == 0) wmax[wave_id()] = kmax;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t hk = 0;
+            for (int i = 0; i < kWaves; ++i) hk = max(hk, wmax[i]);
+            atomicMax(&w.st[s].hkey, hk);
         }
     }
     __syncthreads();
@@ -540,7 +603,10 @@ __global__ __launch_bounds__(kBlock) void dgc_qfind_kernel(PlanDev P, uint32_t p
         const uint32_t np = kLevel == 0 ? d : kLevel == 1 ? ((prefix << kDigit2Bits) | d) : ((prefix << kDigit3Bits) | d);
         w.st[s].qrank = rank - above;
         w.st[s].qprefix = np;
-        if (kLevel == 2) w.st[s].Lkey = np;
+        if (kLevel == 2) {
+            w.st[s].Lkey = np;
+            w.st[s].fshift = fine_shift(np, w.st[s].hkey);
+        }
     }
 }
 
@@ -728,7 +794,7 @@ __global__ __launch_bounds__(kBlock) void dgc_update_kernel(PlanDev P, Src a, Dg
                 if (kFine) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        fine.add(xt, (flags[j] >> q) & 1u, min((mag_key(v[j][q]) - Lkey) >> fs, kFineBins - 1));
+                        fine.add(xt, (flags[j] >> q) & 1u, fine_bin(mag_key(v[j][q]), Lkey, fs));
                 }
             }
         }
@@ -857,17 +923,22 @@ __global__ __launch_bounds__(kBlock) void dgc_select_kernel(PlanDev P, DgcWs w, 
 
 // ----------------------------------------------------------------- sbase
 // Sampled selection: segments send variable counts, laid end to end in
-// segment order.
-__global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w) {
+// segment order.  With seg_off (sampled selection on the exact path, where
+// the counts are settled by select) the message's offsets are written too.
+__global__ __launch_bounds__(kBlock) void dgc_sbase_kernel(PlanDev P, DgcWs w, uint32_t *__restrict__ seg_off) {
     uint32_t run = 0;
     for (int s0 = 0; s0 < P.nseg; s0 += kBlock) {
         const int s = s0 + int(threadIdx.x);
         const uint32_t v = s < P.nseg ? w.st[s].sent : 0u;
         uint32_t tot;
         const uint32_t pre = block_exclusive_scan(v, &tot);
-        if (s < P.nseg) w.st[s].base = run + pre;
+        if (s < P.nseg) {
+            w.st[s].base = run + pre;
+            if (seg_off) seg_off[s] = run + pre;
+        }
         run += tot;
     }
+    if (seg_off && threadIdx.x == 0) seg_off[P.nseg] = run;
 }
 
 // ------------------------------------------- candidate kernels (waves)
@@ -1453,13 +1524,10 @@ __global__ __launch_bounds__(kSelBlock) void dgc_prepare_kernel(PlanDev P, Src a
         Lkey = prefix << kDigit3Bits;
     }
     if (threadIdx.x == 0) {
-        uint32_t fs = 0;
-        if (Hkey > Lkey)
-            while (((Hkey - Lkey) >> fs) > kFineBins - 2) ++fs;
         SegState &st = w.st[s];
         st.clip = cl;
         st.Lkey = Lkey;
-        st.fshift = fs;
+        st.fshift = fine_shift(Lkey, Hkey);
         st.sent = k;
         st.base = seg.kbase;
         st.redo = 0u;
@@ -1654,7 +1722,7 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
             if (!found && acc + hv[i] >= k) {
                 found = true;
                 const uint32_t bs = b0 + i;
-                sh_fb = FineBin{bs, acc, hv[i], bs != kFineBins - 1 && (fs == 0 || hv[i] <= kXListCap)};
+                sh_fb = FineBin{bs, acc, hv[i], bs != kFineBins - 1 && (fs == 0 || bs == 0 || hv[i] <= kXListCap)};
             }
             acc += hv[i];
         }
@@ -1663,7 +1731,8 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
     const FineBin fb = sh_fb;
     // nothing to collect: T's bin unusable here, or (bins of one key) every
     // staged key in T's bin, where select takes each chunk's staged count
-    if (!fb.ok || (fs == 0 && fb.in == total)) return;
+    const bool one_key = fs == 0 || fb.bstar == 0;  // T's bin holds one key
+    if (!fb.ok || (one_key && fb.in == total)) return;
 #pragma unroll
     for (uint32_t j = 0; j < kXCollectCpw; ++j) {
         const uint32_t c = c0 + j;
@@ -1673,13 +1742,13 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
         for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
             const uint32_t i = i0 + lane;
             const uint32_t key = i0 == 0 ? key0[j] : mag_key(w.sval[(size_t(c) << kChunkLog2) + min(i, uint32_t(kChunk) - 1)]);
-            const uint32_t b = min((key - Lkey) >> fs, kFineBins - 1);
+            const uint32_t b = fine_bin(key, Lkey, fs);
             const bool valid = i < n;
             const bool inb = valid && b == fb.bstar;
             const uint64_t gtm = __ballot(valid && b > fb.bstar);
             const uint64_t inm = __ballot(inb);
             const uint32_t at = in + lane_rank(inm);
-            if (fs > 0 && inb && at < kSamples) w.skey[size_t(c) * kSamples + at] = key;
+            if (!one_key && inb && at < kSamples) w.skey[size_t(c) * kSamples + at] = key;
             gt += static_cast<uint32_t>(__popcll(gtm));
             in += static_cast<uint32_t>(__popcll(inm));
         }
@@ -1718,7 +1787,12 @@ __device__ __forceinline__ uint32_t wave_select(const uint32_t *list, uint32_t m
     return lo + prefix;
 }
 
-// One workgroup per segment.  The common case (at least k staged keys, T's
+// One workgroup per segment.  kSampled (sampled selection): the staged keys
+// are those at or above the sample's estimate; when they fit the budget
+// min(n, over k) they are all sent (each chunk's slots from the staged counts
+// alone), otherwise the exact top-k among them is taken as below.  Slots are
+// then relative to the segment, whose base sbase lays out afterwards.
+// The common case (at least k staged keys, T's
 // fine bin below the last and holding at most kXListCap keys, the segment's
 // chunks in one round of kSelChunks): thread t's chunks [t per, +per) have
 // their staged counts and collect words loaded with two histogram bins; one
@@ -1729,13 +1803,14 @@ __device__ __forceinline__ uint32_t wave_select(const uint32_t *list, uint32_t m
 // the counts above and at T gives every chunk's first slot and tie quota:
 // the quota of thread t's chunks is what the ties of the chunks before them
 // leave, and the ties taken before them are min(need_eq, ties before them).
-template <int kMode>
+template <int kMode, bool kSampled>
 __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a, DgcWs w,
-                                                                 uint32_t *__restrict__ seg_off) {
+                                                                 uint32_t *__restrict__ seg_off, uint32_t over) {
     static_assert(kFineBins == 2 * kSelBlock, "two histogram bins per thread");
     const uint32_t s = blockIdx.x;
     const SegDev seg = P.seg[s];
-    const uint32_t k = w.st[s].sent, Lkey = w.st[s].Lkey, fs = w.st[s].fshift, base = w.st[s].base;
+    const uint32_t k = w.st[s].sent, Lkey = w.st[s].Lkey, fs = w.st[s].fshift;
+    const uint32_t base = kSampled ? 0u : w.st[s].base;
     const uint32_t nch = seg.dnchunk, c0 = seg.dchunk0;
     __shared__ uint32_t h[kFineBins];
     __shared__ uint32_t list[kXListCap];
@@ -1752,7 +1827,7 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
     };
     auto pk_load = [&](uint32_t i) { return one_round ? cpk[i] : w.cpack[c0 + i]; };
     auto chunk_len = [&](uint32_t i) { return min(uint32_t(kChunk), seg.len - (i << kChunkLog2)); };
-    auto bin_of = [&](uint32_t key) { return min((key - Lkey) >> fs, kFineBins - 1); };
+    auto bin_of = [&](uint32_t key) { return fine_bin(key, Lkey, fs); };
     auto never = [](uint32_t, uint32_t, uint32_t *) { return false; };
     auto each_staged = [&](auto f) {
         sel_walk(
@@ -1846,7 +1921,38 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
     bool have_pk = false;  // pk_load(i): chunk i's keys above T's bin (low) and in it (high)
     bool pk_done = false;  // cpk: each chunk's keys above T (low) and at T (high), one round
     bool all_eq = false;   // every staged key equals T
-    if (staged < k) {
+    // sampled selection: every staged entry is sent
+    const bool send_all = kSampled && uint64_t(staged) <= umin64(seg.len, uint64_t(over) * k);
+    if (send_all) {
+        // T = Lkey with every chunk's ties in its quota: the emit sends all
+        // staged keys, each chunk's at the slots after the chunks before it
+        uint32_t run = 0;
+        for (uint32_t r0 = 0; r0 < nch; r0 += kSelChunks) {
+            const uint32_t r1 = min(nch, r0 + kSelChunks);
+            const uint32_t per = (r1 - r0 + kSelBlock - 1) / kSelBlock;
+            const uint32_t t0 = r0 + threadIdx.x * per;
+            uint32_t nr[kSelScanRun], sum = 0;
+#pragma unroll
+            for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                const uint32_t i = t0 + b;
+                nr[b] = b < per && i < r1 ? min(w.ccount[c0 + i], chunk_len(i)) : 0u;
+                sum += nr[b];
+            }
+            uint32_t tot;
+            uint32_t at = run + block_exclusive_scan<uint32_t, kSelBlock>(sum, &tot);
+#pragma unroll
+            for (uint32_t b = 0; b < kSelScanRun; ++b) {
+                const uint32_t i = t0 + b;
+                if (b < per && i < r1) {
+                    w.crec[c0 + i] = make_uint4(at, at + nr[b], Lkey, nr[b] | (nr[b] << 16));
+                    at += nr[b];
+                }
+            }
+            run += tot;
+        }
+        T = Lkey;
+        gt = 0;
+    } else if (staged < k) {
         // the sample bound was above the k-th key: select over V itself, then
         // stage every chunk's entries with key >= T again
         auto each_v = [&](auto f) {
@@ -1898,11 +2004,12 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
         }
         __syncthreads();
         const uint32_t bstar = sh_bstar, above = sh_above, cnt_b = sh_cnt;
-        if (bstar == kFineBins - 1 || (fs > 0 && cnt_b > kXListCap)) {
+        const bool one_key = fs == 0 || bstar == 0;  // T's fine bin holds one key
+        if (bstar == kFineBins - 1 || (!one_key && cnt_b > kXListCap)) {
             // T above the fine bins, or its bin too full for the list
             T = sel_radix(k, each_staged, h, &gt);
-        } else if (fs == 0 && cnt_b == staged) {
-            T = Lkey + bstar;  // one key per bin, and every staged key in T's
+        } else if (one_key && cnt_b == staged) {
+            T = Lkey + bstar;  // a bin of one key (fs = 0, or Lkey's own), and every staged key in it
             gt = 0;
             all_eq = true;
             if (one_round) {
@@ -1911,7 +2018,7 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
                     if (b < per1 && t1 + b < nch) cpk[t1 + b] = cnn[t1 + b] << 16;
                 pk_done = true;
             }
-        } else if (fs == 0) {
+        } else if (one_key) {
             // a bin of one key: the collect words count the keys above T and at T
             T = Lkey + bstar;
             gt = above;
@@ -1957,7 +2064,7 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
             if (m <= kWaveSel) {
                 if (wave_id() == 0) {
                     uint32_t g;
-                    const uint32_t t = wave_select(list, m, Lkey + (bstar << fs), fs, k - above, &g);
+                    const uint32_t t = wave_select(list, m, fine_lo(bstar, Lkey, fs), fs, k - above, &g);  // bstar >= 1
                     if (lane_id() == 0) {
                         sh_T = t;
                         sh_gtin = g;
@@ -1984,8 +2091,10 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
             }
         }
     }
-    const uint32_t need_eq = k - gt;
-    if (pk_done) {
+    const uint32_t need_eq = send_all ? 0xFFFFFFFFu : k - gt;
+    if (send_all) {
+        // the records are written
+    } else if (pk_done) {
         // the ordered scan of a one-round segment from cpk and cnn
         uint32_t pk[kSelScanRun], eq_sum = 0, gt_sum = 0;
 #pragma unroll
@@ -2031,8 +2140,10 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
             if (have_pk) {
                 const uint32_t p = pk_load(i);
                 // nothing in T's bin (its keys above the bin are above T), or
-                // a bin of one key (its keys equal T)
-                if ((p >> 16) == 0 || fs == 0) {
+                // a bin of one key (its keys equal T): bins of one key, or T
+                // in Lkey's own bin (a test on values already held: a flag
+                // kept for it made the kernel spill 37 registers)
+                if ((p >> 16) == 0 || fs == 0 || T == Lkey) {
                     *v = p;
                     return true;
                 }
@@ -2084,8 +2195,13 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
         w.st[s].T = T;
         w.st[s].gt = gt;
         w.st[s].need_eq = need_eq;
-        seg_off[s] = base;
-        if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = base + k;
+        if (kSampled) {
+            w.st[s].all = send_all ? 1u : 0u;
+            w.st[s].sent = send_all ? staged : k;
+        } else {
+            seg_off[s] = base;
+            if (s == uint32_t(P.nseg - 1)) seg_off[P.nseg] = base + k;
+        }
     }
 }
 
@@ -2094,14 +2210,21 @@ __global__ __launch_bounds__(kSelBlock) void dgc_xselect_kernel(PlanDev P, Src a
 // entries above T are sent, ties at T up to the chunk's quota in index order;
 // slots from ballots, never past the chunk's last slot; U and V masked at the
 // sent entries.  Record: first slot, end slot, T, staged count | quota << 16.
-template <int kMode, uint32_t CPW>
+// kSampled: the slots are relative to the segment's base (set by sbase).
+template <int kMode, uint32_t CPW, bool kSampled>
 __global__ __launch_bounds__(kBlock) void dgc_xemit_kernel(PlanDev P, Src a, DgcWs w,
                                                            uint32_t *__restrict__ out_idx,
                                                            float *__restrict__ out_val) {
     const uint32_t c0 = wave_chunk0<CPW>();
     if (c0 >= P.ndchunk) return;
     const int lane = lane_id();
-    const uint4 rec = w.crec[min(c0 + uint32_t(lane) % CPW, P.ndchunk - 1)];
+    const uint32_t cl = min(c0 + uint32_t(lane) % CPW, P.ndchunk - 1);
+    uint4 rec = w.crec[cl];
+    if (kSampled) {
+        const uint32_t sb = w.st[P.dchunk_rec[cl].z].base;
+        rec.x += sb;
+        rec.y += sb;
+    }
     uint32_t id0[CPW];
     float v0[CPW];
 #pragma unroll
@@ -2225,7 +2348,7 @@ void launch_candidates(const gc_plan *plan, const PlanDev &P, const DgcWs &w, co
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
     GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
-    if (sampled || w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    if (sampled || w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w, nullptr));
     GC_LAUNCH("dgc_count", stream, dgc_count_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_scan", stream, dgc_scan_kernel<<<segs, kBlock, 0, stream>>>(P, w, out->seg_off));
     GC_LAUNCH("dgc_emit", stream, dgc_emit_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
@@ -2239,18 +2362,22 @@ void launch_exact(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const S
     if (clip)
         GC_LAUNCH("dgc_norm", stream, dgc_norm_kernel<<<plan->ndchunk, kBlock, 0, stream>>>(P, src.G, w));
     GC_LAUNCH("dgc_prepare", stream, dgc_prepare_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, clip ? 1 : 0, thr));
-    if (w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w));
+    if (w.kden) GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w, nullptr));
     GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode, true><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
     GC_LAUNCH("dgc_collect", stream, dgc_xcollect_kernel<<<static_cast<unsigned>(plan->xblock.size()), kBlock, 0, stream>>>(P, w));
-    GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off));
+    GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode, false><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off, 0u));
     if (plan->ndchunk >= kWideChunks)
-        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide, false><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
     else
-        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, 1><<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+        GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, 1, false><<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
 }
 
 // The selection pipeline for one key source: (clip), prep, sample + bound
 // (exact) or ssample + squant (sampled), update, radix select, ordered emit.
+// Sampled DGC selection on plans of the exact path's densities goes on from
+// the estimate with the exact path's kernels instead: the update stages the
+// keys at or above it, collect and select settle each segment (all of them
+// sent, or the exact top-k among them), sbase lays the segments out, emit.
 template <int kMode>
 void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const Src &src, bool clip, float thr,
                    bool sampled, uint32_t period, uint32_t over, gc_sparse *out, hipStream_t stream) {
@@ -2263,7 +2390,9 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
     bool multi_q = false;
     if (sampled)
         for (const SegDev &d : plan->seg) multi_q = multi_q || sample_count(d.len, period) > kQuantOneBlock;
-    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr, multi_q ? 1 : 0));
+    const bool fine = sampled && plan->dgc_fast;
+    GC_LAUNCH("dgc_prep", stream, dgc_prep_kernel<<<segs, kBlock, 0, stream>>>(P, w, clip ? 1 : 0, thr, multi_q ? 1 : 0,
+                                                                               fine ? 1 : 0));
     if constexpr (kMode == kVanilla || kMode == kNesterov) {
         if (sampled) {
             GC_LAUNCH("dgc_ssample", stream, dgc_ssample_kernel<kMode><<<wave_grid, kBlock, 0, stream>>>(P, src, period, w));
@@ -2278,6 +2407,17 @@ void launch_select(const gc_plan *plan, const PlanDev &P, const DgcWs &w, const 
             } else {
                 GC_LAUNCH("dgc_squant", stream, dgc_squant_kernel<<<segs, kBlock, 0, stream>>>(P, period, w));
             }
+        }
+        if (fine) {
+            GC_LAUNCH("dgc_update", stream, dgc_update_kernel<kMode, true><<<plan->ndchunk, kBlock, 0, stream>>>(P, src, w));
+            GC_LAUNCH("dgc_collect", stream, dgc_xcollect_kernel<<<static_cast<unsigned>(plan->xblock.size()), kBlock, 0, stream>>>(P, w));
+            GC_LAUNCH("dgc_select", stream, dgc_xselect_kernel<kMode, true><<<segs, kSelBlock, 0, stream>>>(P, src, w, out->seg_off, over));
+            GC_LAUNCH("dgc_sbase", stream, dgc_sbase_kernel<<<1, kBlock, 0, stream>>>(P, w, out->seg_off));
+            if (plan->ndchunk >= kWideChunks)
+                GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, kCpwWide, true><<<grid_1d(plan->ndchunk, kWaves * kCpwWide), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+            else
+                GC_LAUNCH("dgc_emit", stream, dgc_xemit_kernel<kMode, 1, true><<<grid_1d(plan->ndchunk, kWaves), kBlock, 0, stream>>>(P, src, w, out->idx, out->val));
+            return;
         }
     }
     if (!sampled) {
