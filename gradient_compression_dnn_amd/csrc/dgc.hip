@@ -479,6 +479,15 @@ __host__ __device__ __forceinline__ uint32_t sample_count(uint32_t len, uint32_t
     return static_cast<uint32_t>(wl * 32 + last_ns);
 }
 
+// The top of the fine bins for sampled selection: the largest sample key, or
+// when the estimate is that key itself (a sample of a few dozen keys gives
+// r = 1) the largest finite key, since nothing is known above.  When the
+// staged keys pass the budget, T then lies in a bin of at most 2^20 keys
+// (an eighth of a binade) instead of above the bins.
+__device__ __forceinline__ uint32_t sample_top(uint32_t est, uint32_t hkey) {
+    return hkey > est ? hkey : 0x7F800000u;
+}
+
 // r = ceil(S k / n), the estimate's rank among the samples.
 __device__ __forceinline__ uint32_t sample_rank(uint32_t S, const SegDev &seg) {
     return static_cast<uint32_t>((uint64_t(S) * seg.k + seg.len - 1) / seg.len);
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(kBlock) void dgc_squant_kernel(PlanDev P, uint32_t 
         for (int i = 0; i < kWaves; ++i) hk = max(hk, wmax[i]);
         w.st[s].Lkey = prefix;
         w.st[s].hkey = hk;
-        w.st[s].fshift = fine_shift(prefix, hk);
+        w.st[s].fshift = fine_shift(prefix, sample_top(prefix, hk));
     }
 }
 
@@ -605,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void dgc_qfind_kernel(PlanDev P, uint32_t p
         w.st[s].qprefix = np;
         if (kLevel == 2) {
             w.st[s].Lkey = np;
-            w.st[s].fshift = fine_shift(np, w.st[s].hkey);
+            w.st[s].fshift = fine_shift(np, sample_top(np, w.st[s].hkey));
         }
     }
 }
