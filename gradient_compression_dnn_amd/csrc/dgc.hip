@@ -1748,9 +1748,7 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
         if (c >= cend) break;
         const uint32_t n = lane_val(my_n, j);
         uint32_t gt = 0, in = 0;
-        for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
-            const uint32_t i = i0 + lane;
-            const uint32_t key = i0 == 0 ? key0[j] : mag_key(w.sval[(size_t(c) << kChunkLog2) + min(i, uint32_t(kChunk) - 1)]);
+        auto count = [&](uint32_t i, uint32_t key) {
             const uint32_t b = fine_bin(key, Lkey, fs);
             const bool valid = i < n;
             const bool inb = valid && b == fb.bstar;
@@ -1760,6 +1758,18 @@ __global__ __launch_bounds__(kBlock) void dgc_xcollect_kernel(PlanDev P, DgcWs w
             if (!one_key && inb && at < kSamples) w.skey[size_t(c) * kSamples + at] = key;
             gt += static_cast<uint32_t>(__popcll(gtm));
             in += static_cast<uint32_t>(__popcll(inm));
+        };
+        count(lane, key0[j]);
+        // a chunk of many staged keys (a tensor of near-zeros stages every
+        // entry): the rest four batches of loads at a time
+        const uint32_t *sv = reinterpret_cast<const uint32_t *>(w.sval) + (size_t(c) << kChunkLog2);
+        for (uint32_t i0 = kWave; i0 < n; i0 += 4 * kWave) {
+            uint32_t key[4];
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) key[q] = sv[min(i0 + q * kWave + lane, uint32_t(kChunk) - 1)] & 0x7FFFFFFFu;
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+                if (i0 + q * kWave < n) count(i0 + q * kWave + lane, key[q]);
         }
         if (lane == 0) w.cpack[c] = gt | (in << 16);
     }
