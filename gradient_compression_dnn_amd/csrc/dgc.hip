@@ -8,11 +8,13 @@
 //   explorer (top-k of random keys outside the core) through the same
 //   kernels, with the key source chosen by a template mode.
 //
-// Two launch sequences.  Exact selection at the pages' densities (every
-// tensor of more than one chunk keeps at most 1/512 of its entries) takes
-// the exact path described further down: norm, prepare, update, collect,
-// select, emit.  Denser exact selections (warm-up, Slim-DP's core) and the
-// sampled threshold take the candidate kernels below.  Chunk kernels run
+// Two launch sequences.  Selection at the pages' densities (every tensor of
+// more than one chunk keeps at most 1/512 of its entries) takes the exact
+// path described further down: norm, prepare, update, collect, select,
+// emit (the sampled threshold replaces prepare by its sample and quantile
+// and adds sbase).  Denser selections (warm-up, Slim-DP's core and
+// explorer, the sampled threshold on such plans) take the candidate kernels
+// below.  Chunk kernels run
 // one workgroup (or one wave) per 4096-element chunk of a segment; segment
 // kernels one workgroup per segment.  Chunk kernels hand results to segment
 // kernels through global memory at kernel boundaries only (no cross-
@@ -54,10 +56,12 @@
 //           r = ceil(S k / n), by a three-digit LDS radix select (or, for
 //           segments with more than 32,768 samples, qhist/qfind pairs with 32
 //           workgroups per segment)
-// and the update stages exactly the keys at or above the estimate.  select1
-// then sends all of them when they fit the budget min(n, over k) ("all"
-// segments skip stage, refine and the later selects), and otherwise takes
-// the exact top-k among them through the normal path.  sbase (one
+// and the update stages exactly the keys at or above the estimate.  The
+// segment then sends all of them when they fit the budget min(n, over k),
+// and otherwise the exact top-k among them: on the exact path's kernels
+// (collect and select as for exact selection, select settling each
+// segment's count), or with the candidate kernels (select1 marks "all"
+// segments, which skip stage, refine and the later selects).  sbase (one
 // workgroup) lays the segments' variable-size outputs end to end.
 #include <algorithm>
 #include <cmath>
