@@ -259,3 +259,34 @@ def test_tensors_of_zeros_and_nearly_zeros(sampled):
     ordinary = _step_ms(hp, Gn, Un, Vn, opt)
     say(f"  crowded {crowded:.3f} ms, ordinary {ordinary:.3f} ms")
     assert crowded < 10 * ordinary + 1.0
+
+
+@pytest.mark.parametrize("period,over", [(1, 1), (1, 3), (7, 2), (100, 2), (1000, 1)])
+@pytest.mark.parametrize("kind", ["normal", "laplace", "ties", "zeros", "denormal"])
+def test_sampled_threshold_on_the_exact_path(period, over, kind):
+    """Sampled selection on tables at the pages' density, which take the
+    exact path's kernels after the estimate (the random tables of the sampled
+    tests elsewhere are mostly denser and take the candidate kernels): three
+    steps with the state carried, alternating momentum kinds, clipping on the
+    last, bit-exact against the oracle."""
+    rng = np.random.default_rng(700 + period + 10 * over)
+    t = fast_table(rng, int(rng.integers(2, 12)))
+    hp = HipPath(t, W.table_extent(t))
+    n = W.table_extent(t)
+    U = W.random_values(rng, n, kind)
+    V = W.random_values(rng, n, kind)
+    Ug, Vg = U.copy(), V.copy()
+    for step in range(3):
+        G = W.random_values(rng, n, kind)
+        nest = step % 2 == 1
+        thr = 1e-3 if step == 2 else 0.0
+        say(f"sampled on the exact path P={period} over={over} kind={kind} n={n} step={step}")
+        U, V, idx, val, off, _ = oracle.dgc_ex(t, G, U, V, 0.9, thr, 2, nesterov=nest, sampled=True,
+                                               sample_period=period, over=over)
+        opt = B.dgc_options(0.9, thr, 2, nesterov=nest, sampled=True, sample_period=period, over=over)
+        Ug, Vg, gidx, gval, goff = hp.dgc_ex(G, Ug, Vg, opt)
+        assert np.array_equal(goff, off), "segment offsets"
+        assert np.array_equal(gidx, idx), "selected indices"
+        assert same_bits(gval, val), ulp_report(gval, val)
+        assert same_bits(Ug, U), ulp_report(Ug, U)
+        assert same_bits(Vg, V), ulp_report(Vg, V)
