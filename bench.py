@@ -542,7 +542,8 @@ def main(argv=None):
     # every step of the run (warm-up, instrumented, timed, breakdown, per-call)
     # gets its own gradient, seed 5000 + t, drawn on the device before any
     # step; past --max-grads steps the pool is cycled
-    run_steps = args.warmup + 2 * args.steps + 2
+    call_reps = max(3, min(args.steps, 10))  # back-to-back repeats of each call timed alone
+    run_steps = args.warmup + args.steps + 2 + call_reps
     ng = max(1, min(run_steps, args.max_grads))
     log(f"workload deepspeech: {w.nseg} tensors, {n:,} elements; drawing {ng} gradients on the device")
     x0 = W.dcd_model(w)
@@ -574,17 +575,20 @@ def main(argv=None):
 
     CALLS = ("dgc", "dgc_pack", "adacomp", "adacomp_pack", "dgc_decode", "adacomp_decode", "dcd")
 
+    def step_calls(t):
+        """The step's calls, in order, for step t."""
+        g = G[t % len(G)]
+        return (lambda: B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC]),
+                lambda: B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK]),
+                lambda: B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=astate),
+                lambda: B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK]),
+                lambda: B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
+                lambda: B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
+                lambda: B.gc_dcd_compress(X, XH[t % len(XH)], XO, 4, bucket, 0x5EED, t, scales, codes))
+
     def step(t, marks=None):
         """One step; with `marks` (len(CALLS) + 1 events) each call is bracketed."""
-        g = G[t % len(G)]
-        calls = (lambda: B.gc_dgc_step(plan, g, U, V, 0.9, 1.0, 1, dmsg, ws[B.GC_OP_DGC]),
-                 lambda: B.gc_pack(plan, B.GC_KIND_DGC, dmsg, dbuf, dn, ws[B.GC_OP_PACK]),
-                 lambda: B.gc_adacomp_compress(plan, g, R, 2.0, amsg, ws[B.GC_OP_ADACOMP], state=astate),
-                 lambda: B.gc_pack(plan, B.GC_KIND_ADACOMP, amsg, abuf, an, ws[B.GC_OP_PACK]),
-                 lambda: B.gc_decompress_accumulate(plan, [dmsg], ddense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
-                 lambda: B.gc_decompress_accumulate(plan, [amsg], adense, B.GC_AVG, False, ws[B.GC_OP_DECODE]),
-                 lambda: B.gc_dcd_compress(X, XH[t % len(XH)], XO, 4, bucket, 0x5EED, t, scales, codes))
-        for i, call in enumerate(calls):
+        for i, call in enumerate(step_calls(t)):
             if marks:
                 marks[i].record()
             call()
@@ -648,15 +652,22 @@ def main(argv=None):
     dcd_alpha = float(torch.linalg.vector_norm(z - cz) / torch.linalg.vector_norm(z))
     del z, cz
 
-    # each call of the step alone: a few more steps with events between the
-    # calls (outside the timed region), averaged per call
-    call_ms = {c: 0.0 for c in CALLS}
-    for r in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
-        step(args.warmup + 2 + args.steps + r, ev)
+    # each call of the step alone (outside the timed region): the call
+    # repeated back to back over the steps that follow, with events only
+    # around the batch, so that no event marker (several microseconds each)
+    # falls between two calls; the compressions take a fresh gradient (and
+    # DCD a fresh step) each time, packs and decodes the last message
+    call_ms = {}
+    t_calls = args.warmup + 2 + args.steps
+    reps = call_reps
+    for i, c in enumerate(CALLS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            step_calls(t_calls + r)[i]()
+        e1.record()
         torch.cuda.synchronize()
-        for i, c in enumerate(CALLS):
-            call_ms[c] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+        call_ms[c] = e0.elapsed_time(e1) / reps
 
     # the measured streaming ceiling: a plain 1 GiB device-to-device copy, best
     # of 5 (also the reference that scales rocprofv3's byte counters)
@@ -699,7 +710,8 @@ def main(argv=None):
     digest = source_digest()
     roof = None
     if dominant in alg:
-        per_launch = alg[dominant][0] // alg[dominant][1]
+        # launches per step from the instrumented step
+        per_launch = alg[dominant][0] // per_kernel[dominant][1]
         ach = per_launch / dom_avg_s / 1e9
         traffic = stored_traffic(dominant, digest)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
