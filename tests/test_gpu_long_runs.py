@@ -5,7 +5,9 @@ the device, copied to the host for the oracle):
   LSTM LM: 20 AdaComp steps (L_T 500 / 50), both residual modes;
   ResNet-50 warm-up: densities 1/4, 1/16, 1/64, 1/256, then the plan's 0.1%,
   set per call, with U and V carried (the DGC page's exponentially
-  increasing sparsity, read as 75%, 93.75%, 98.4375%, 99.6%, 99.9%).
+  increasing sparsity, read as 75%, 93.75%, 98.4375%, 99.6%, 99.9%);
+  DeepSpeech: 10 steps alternating DGC and AdaComp (deferred residual), with
+  the 4-bit compressed difference applied to one model buffer every step.
 Every step's message and state are compared bit for bit."""
 import numpy as np
 import pytest
@@ -114,3 +116,64 @@ def test_resnet50_warmup_density_schedule(nesterov):
         assert same_bits(gv, val), ulp_report(gv, val)
         assert same_bits(Ud.cpu().numpy(), U), ulp_report(Ud.cpu().numpy(), U)
         assert same_bits(Vd.cpu().numpy(), V), ulp_report(Vd.cpu().numpy(), V)
+
+
+def test_deepspeech_ten_steps_alternating_dgc_adacomp_with_dcd():
+    """The DeepSpeech-scale configuration at its stated length: 10 steps on
+    the 121,893,373-entry layout, a fresh gradient per step (seed 5000 + t);
+    even steps DGC (momentum 0.9, clip 1.0, top 0.1%, U and V carried), odd
+    steps AdaComp (L_T 500, factor 2, the deferred residual carried), and
+    every step the compressed difference (4-bit, buckets of 512) of
+    x_{t+1/2} - x_t applied in place to the same model buffer."""
+    w = W.make_config("deepspeech")
+    t, n = w.table, w.n_total
+    hp = HipPath(t, n)
+    U = np.zeros(n, np.float32)
+    V = U.copy()
+    R = U.copy()
+    Ud = torch.zeros(n, dtype=torch.float32, device=dev())
+    Vd = torch.zeros_like(Ud)
+    Rd = torch.zeros_like(Ud)
+    state = hp.plan.adacomp_state(dev())
+    dmsg = B.Sparse.empty(hp.plan, hp.plan.total_k, dev())
+    amsg = B.Sparse.empty(hp.plan, n, dev())
+    x = W.dcd_model(w)
+    xd = torch.from_numpy(x.copy()).to(dev())
+    nb = (n + 511) // 512
+    scales = torch.zeros(nb, dtype=torch.float32, device=dev())
+    codes = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=dev())
+    for step in range(10):
+        g = W.gradient_device(w, step, dev())
+        gh = g.cpu().numpy()
+        if step % 2 == 0:
+            say(f"deepspeech step {step} dgc: hip")
+            B.gc_dgc_step(hp.plan, g, Ud, Vd, 0.9, 1.0, 1, dmsg, hp.workspace(B.GC_OP_DGC))
+            torch.cuda.synchronize()
+            say(f"deepspeech step {step} dgc: oracle")
+            U, V, idx, val, off, _ = oracle.dgc(t, gh, U, V, 0.9, 1.0, 1)
+            gi, gv, go, _ = dmsg.host()
+            assert np.array_equal(go, off) and np.array_equal(gi, idx), f"dgc step {step}"
+            assert same_bits(gv, val), ulp_report(gv, val)
+        else:
+            say(f"deepspeech step {step} adacomp: hip")
+            B.gc_adacomp_compress(hp.plan, g, Rd, 2.0, amsg, hp.workspace(B.GC_OP_ADACOMP), state=state)
+            torch.cuda.synchronize()
+            say(f"deepspeech step {step} adacomp: oracle")
+            R, idx, val, off, scale, _ = oracle.adacomp(t, gh, R, 2.0)
+            gi, gv, go, gs = amsg.host()
+            assert np.array_equal(go, off) and np.array_equal(gi, idx), f"adacomp step {step}"
+            assert same_bits(gv, val), ulp_report(gv, val)
+            assert same_bits(gs[:len(t)], scale), ulp_report(gs[:len(t)], scale)
+        say(f"deepspeech step {step} dcd")
+        xh = W.dcd_half_step(x, gh)
+        B.gc_dcd_compress(xd, torch.from_numpy(xh).to(dev()), xd, 4, 512, 0x5EED, step, scales, codes)
+        torch.cuda.synchronize()
+        x, sc, cd = oracle.dcd(x, xh, 4, 512, 0x5EED, step)
+        assert same_bits(scales.cpu().numpy(), sc) and np.array_equal(codes.cpu().numpy(), cd), f"dcd step {step}"
+    assert same_bits(Ud.cpu().numpy(), U), ulp_report(Ud.cpu().numpy(), U)
+    assert same_bits(Vd.cpu().numpy(), V), ulp_report(Vd.cpu().numpy(), V)
+    exact = torch.empty_like(Rd)
+    B.gc_adacomp_residual(hp.plan, Rd, state, exact)
+    torch.cuda.synchronize()
+    assert same_bits(exact.cpu().numpy(), R), ulp_report(exact.cpu().numpy(), R)
+    assert same_bits(xd.cpu().numpy(), x), ulp_report(xd.cpu().numpy(), x)
