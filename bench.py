@@ -308,6 +308,21 @@ def measure_variants(B, plan, w, G, X, XH, XO, scales, codes, ws, bucket, dev, l
             B.gc_dgc_step_ex(plan, G[t % len(G)], U2, V2, opt, msg, ws[B.GC_OP_DGC])
 
         timed(label, run, 20 * n, lambda msg=msg: {"entries": msg.count(), "k_total": plan.total_k})
+    # the warm-up densities of the DGC page (sparsity 75%, 93.75%, 98.4375%,
+    # 99.6%), each call's k set per call; the message and the masking writes
+    # (16 B per entry) count with the update's 20 B per element
+    for num, den in ((1, 4), (1, 16), (1, 64), (1, 256)):
+        opt = B.dgc_options(0.9, 1.0, 1, density=(num, den))
+        cap = B.gc_dgc_message_cap(plan, opt)
+        msg = B.Sparse.empty(plan, cap, dev)
+        U2.zero_()
+        V2.zero_()
+
+        def run(t, opt=opt, msg=msg):
+            B.gc_dgc_step_ex(plan, G[t % len(G)], U2, V2, opt, msg, ws[B.GC_OP_DGC])
+
+        timed(f"dgc_warmup_density_{num}_{den}", run, 20 * n + 16 * cap,
+              lambda msg=msg: {"entries": msg.count()})
     timed("dcd_decode_4bit", lambda t: B.gc_dcd_decode(scales, codes, XHAT, 4, bucket), 8 * n + code_bytes)
     timed("dcd_mix_ring3", lambda t: B.gc_dcd_mix([X, L, R_], [0.5, 0.25, 0.25], G[t % len(G)], 0.1, XO),
           20 * n)  # three replicas and the gradient read, x_half written
