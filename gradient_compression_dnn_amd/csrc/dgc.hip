@@ -1053,6 +1053,10 @@ __device__ __forceinline__ void for_staged_keys_wave(const DgcWs &w, uint32_t lo
 // the staged entries whose digit 1 is d1.  In a re-staged segment it re-reads
 // the chunk's values instead (stage_chunk_again).
 constexpr int kWaveRows = kChunk / (4 * kWave);
+// A chunk of the candidate path that sends at least this many entries masks
+// U and V by rewriting the chunk (64 KB of traffic) instead of two scattered
+// 4-byte writes per entry (each a partial line, some 128 B of traffic).
+constexpr uint32_t kDenseMask = 512;
 
 // One wave re-stages chunk c: lane l holds elements [256 r + 4 l, +4) for
 // rows r = 0..15, so 16 KB of V is in flight per wave and the ordered
@@ -1353,6 +1357,7 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
     const uint32_t cl = min(c0 + uint32_t(lane) % CPW, P.ndchunk - 1);
     const SegState &sl = w.st[wc.rec.z];
     const uint32_t T_l = sl.T, take_l = w.ctake[cl], base_l = w.cout[cl];
+    const uint32_t gt_l = kDgc ? w.cgt[cl] : 0u;
     // a segment owns message slots [base, base + sent): never write past them
     const uint32_t limit_l = sl.base + sl.sent;
     uint32_t id0[CPW];
@@ -1364,13 +1369,19 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
         id0[j] = n ? w.sidx[ic] : 0u;
         v0[j] = n ? w.sval[ic] : 0.0f;
     }
-    __shared__ uint32_t cmask[kWaves][kMode == kSignif ? kChunk / 32 : 1];
+    // a bitmap of the chunk's sent entries: Slim-DP's core writes it out; DGC
+    // uses it to mask a chunk that sends many entries (below)
+    __shared__ uint32_t cmask[kWaves][kMode == kSignif || kDgc ? kChunk / 32 : 1];
     uint32_t *cm = cmask[wave_id()];
 #pragma unroll
     for (uint32_t j = 0; j < CPW; ++j) {
         if (c0 + j >= P.ndchunk) break;
         const uint32_t n = lane_val(wc.n, j), lo = lane_val(wc.rec.x, j);
-        if (kMode == kSignif) {
+        // DGC masking of a chunk that sends at least kDenseMask entries (the
+        // warm-up's first densities): the bitmap, then the chunk's U and V
+        // rewritten whole, instead of two scattered 4-byte writes per entry
+        const bool dense = kDgc && lane_val(gt_l, j) + lane_val(take_l, j) >= kDenseMask;
+        if (kMode == kSignif || dense) {
             cm[lane] = 0u;
             cm[lane + kWave] = 0u;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -1391,11 +1402,11 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
             if (sel && p < limit) {
                 out_idx[p] = id;
                 out_val[p] = kMode == kExplore ? a.G[id] : val;
-                if (kDgc) {
+                if (kDgc && !dense) {
                     a.V[id] = 0.0f;
                     a.U[id] = 0.0f;
                 }
-                if (kMode == kSignif) atomicOr(&cm[(id - lo) >> 5], 1u << ((id - lo) & 31u));
+                if (kMode == kSignif || dense) atomicOr(&cm[(id - lo) >> 5], 1u << ((id - lo) & 31u));
             }
             eq_run += static_cast<uint32_t>(__popcll(eqm));
             sel_run += static_cast<uint32_t>(__popcll(selm));
@@ -1419,6 +1430,37 @@ __global__ __launch_bounds__(kBlock) void dgc_emit_kernel(PlanDev P, Src a, DgcW
             const uint32_t wbase = P.seg[lane_val(wc.rec.z, j)].mbase + (lane_val(wc.rec.w, j) << (kChunkLog2 - 5));
             const uint32_t nw = (lane_val(wc.rec.y, j) + 31) / 32;
             for (uint32_t l = lane; l < nw; l += kWave) a.mask[wbase + l] = cm[l];
+        }
+        if (dense) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            // lane l holds elements [256 r + 4 l, +4) of rows r; four rows of U
+            // and V in flight at a time
+            const uint32_t cnt = lane_val(wc.rec.y, j);
+            const BufRsrc ru = chunk_buf(a.U + lo, cnt), rv = chunk_buf(a.V + lo, cnt);
+#pragma unroll
+            for (int r0 = 0; r0 < kWaveRows; r0 += 4) {
+                float u[4][4], v[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t e0 = (r0 + r) * (4 * kWave) + 4u * lane;
+                    load4(ru, e0, u[r]);
+                    load4(rv, e0, v[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t e0 = (r0 + r) * (4 * kWave) + 4u * lane;
+                    const uint32_t bits = cm[e0 >> 5] >> (e0 & 31u);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if ((bits >> q) & 1u) {
+                            u[r][q] = 0.0f;
+                            v[r][q] = 0.0f;
+                        }
+                    }
+                    store4(ru, e0, u[r]);
+                    store4(rv, e0, v[r]);
+                }
+            }
         }
     }
 }
