@@ -2434,12 +2434,10 @@ void launch_candidates(const gc_plan *plan, const PlanDev &P, const DgcWs &w, co
     const unsigned segs = static_cast<unsigned>(plan->nseg);
     const unsigned cand_grid = grid_1d(plan->ndchunk, kWaves * CPW);
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<1><<<segs, kBlock, 0, stream>>>(P, w, sampled ? over : 0u));
-    if (kMode == kSignif) {
-        GC_LAUNCH("dgc_stage", stream, dgc_stagew_kernel<<<grid_1d(plan->ndchunk, kStageSpan), kBlock, 0, stream>>>(P, w));
-        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, 1));
-    } else {
-        GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, 0));
-    }
+    // the boundary bucket's digit-2 histogram in LDS per span of chunks, then
+    // the re-staged segments
+    GC_LAUNCH("dgc_stage", stream, dgc_stagew_kernel<<<grid_1d(plan->ndchunk, kStageSpan), kBlock, 0, stream>>>(P, w));
+    GC_LAUNCH("dgc_stage", stream, dgc_stage_kernel<kMode, CPW><<<cand_grid, kBlock, 0, stream>>>(P, src, w, 1));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<2><<<segs, kBlock, 0, stream>>>(P, w, 0u));
     GC_LAUNCH("dgc_refine", stream, dgc_refine_kernel<CPW><<<cand_grid, kBlock, 0, stream>>>(P, w));
     GC_LAUNCH("dgc_select", stream, dgc_select_kernel<3><<<segs, kBlock, 0, stream>>>(P, w, 0u));
