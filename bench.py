@@ -412,7 +412,8 @@ def measure_configs(B, W, dev, log, reps: int = 10):
                   the DGC step also cold (Infinity Cache evicted before each call)
       resnet50    DGC steps (momentum 0.9, clip 1.0, top 0.1% per tensor), warm and cold
       lstm_lm     AdaComp steps (L_T 500 / 50, residual carried)
-      resnet50x8  8 learners' DGC steps (N = 8) and the 8-message average"""
+      resnet50x8  8 learners' DGC steps (N = 8) and the 8-message average; the
+                  8 learners' DGC steps as one call over a 1,288-tensor plan"""
     import torch
 
     out = {}
@@ -517,6 +518,15 @@ def measure_configs(B, W, dev, log, reps: int = 10):
         B.gc_decompress_accumulate(plan, msgs, avg, B.GC_AVG, False, wsdec)
 
     timed("resnet50x8_dgc_and_average", learners, 8 * 4 * per, 8 * 20 * per + 4 * per)
+    # the same eight learners' DGC steps as one call: one plan over the eight
+    # buffers (1,288 tensors), so the selection's launches serve all of them
+    plan8 = B.Plan(w.table, w.n_total)
+    msg8 = B.Sparse.empty(plan8, plan8.total_k, dev)
+    wsd8 = plan8.workspace(B.GC_OP_DGC, dev)
+    U8.zero_()
+    V8.zero_()
+    timed("resnet50x8_dgc_one_call", lambda t: B.gc_dgc_step(plan8, gall, U8, V8, 0.9, 1.0, 8, msg8, wsd8),
+          8 * 4 * per, 8 * 20 * per)
     return out
 
 
