@@ -125,3 +125,31 @@ def test_deepspeech_sampled_and_nesterov():
              "deepspeech sampled P=100")
     run_both(hp, w.table, g, z, z, z.copy(), z.copy(), 0.9, 1.0, 1, True, False, 0, 0,
              "deepspeech nesterov exact")
+
+
+@pytest.mark.parametrize("per_chunk", [511, 512, 513], ids=["511", "512", "513"])
+def test_dense_chunk_masking_threshold(per_chunk):
+    """Dense selections mask U and V per chunk either by scattered writes or,
+    for a chunk that sends at least 512 entries, by rewriting the chunk: each
+    chunk here sends exactly `per_chunk` large entries (the ragged last chunk
+    of the second tensor 600), so both ways run side by side; three steps
+    carry the masked state, bit for bit against the oracle."""
+    rng = np.random.default_rng(per_chunk)
+    lens = [4 * 4096, 3 * 4096 + 1000]
+    sends = [[per_chunk] * 4, [per_chunk] * 3 + [600]]
+    ks = [sum(s) for s in sends]
+    t = W.make_table(lens, [500, 500], ks, [0, 7])
+    n = W.table_extent(t)
+    hp = HipPath(t, n)
+    U = np.zeros(n, np.float32)
+    V = U.copy()
+    Ug, Vg = U.copy(), V.copy()
+    for step in range(3):
+        G = rng.uniform(-1.0, 1.0, n).astype(np.float32)
+        for (off, ln, _, _), sc in zip(t, sends):
+            for c, cnt in enumerate(sc):
+                lo = off + 4096 * c
+                pos = lo + rng.choice(min(4096, ln - 4096 * c), cnt, replace=False)
+                G[pos] = np.float32(100.0 + step) * np.sign(G[pos] + 0.5)
+        U, V, Ug, Vg, _ = run_both(hp, t, G, U, V, Ug, Vg, 0.9, 0.0, 1, False, False, 100, 2,
+                                   f"dense masking per_chunk={per_chunk} step={step}")
